@@ -1,0 +1,140 @@
+"""Quantizers of the oracle (test infrastructure only).
+
+Every step is written in the order its definition gives, in IEEE fp32 where
+the definition produces an fp32 quantity (a scale, a scaled value) and in
+exact arithmetic elsewhere.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .numerics import bf16_bits_to_f32, f32_to_bf16_bits, mean_abs_f32, mean_abs_rows_f32
+
+Q_MAX = 127  # 2**(b-1) - 1 for b = 8 ([VG] 'Symmetric quantization', Fig. 17)
+
+
+def absmax_scale(alpha: np.ndarray) -> np.ndarray:
+    """s = q_max / alpha in fp32, alpha = max|x| of the group.
+
+    [VG] 'Symmetric quantization' (absmax, Fig. 16-17): the scale is the
+    multiplier q_max / alpha.  [OVR] section 3.1 step 2 writes the reciprocal
+    (alpha / 127, then divides); the stored value here is the multiplier.
+    An all-zero group (alpha = 0) gets s = 1 so its codes are 0 (the pages do
+    not cover it)."""
+    alpha = np.asarray(alpha, dtype=np.float32)
+    with np.errstate(divide="ignore"):
+        s = np.float32(Q_MAX) / alpha
+    return np.where(alpha == np.float32(0), np.float32(1), s).astype(np.float32)
+
+
+def quantize_with_scale(x: np.ndarray, s) -> np.ndarray:
+    """x_q = clip(round(s * x), -q_max, q_max) with one fp32 multiply and
+    round-half-to-even ([VG] 'Symmetric quantization', Fig. 17-18)."""
+    x = np.asarray(x, dtype=np.float32)
+    t = (x * np.asarray(s, dtype=np.float32)).astype(np.float32)
+    q = np.clip(np.rint(t), -Q_MAX, Q_MAX)
+    return q.astype(np.int8)
+
+
+def quantize_absmax(x: np.ndarray, per_row: bool):
+    """Symmetric absmax int8 quantization.
+
+    per_row=True: one scale per row (per output channel for weights, per token
+    for activations -- [OVR] section 2.3 granularity; [SEP] section 6.2 keeps a
+    scale per row).  per_row=False: one scale for the whole tensor.
+    Returns (codes int8, same shape as x; s fp32 [rows] or [1])."""
+    x = np.asarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x2 = x[None, :]
+    else:
+        x2 = x
+    if per_row:
+        alpha = np.max(np.abs(x2), axis=1) if x2.shape[1] else np.zeros(x2.shape[0], np.float32)
+        s = absmax_scale(alpha)
+        q = quantize_with_scale(x2, s[:, None])
+    else:
+        alpha = np.max(np.abs(x2)) if x2.size else np.float32(0)
+        s = absmax_scale(np.array([alpha], dtype=np.float32))
+        q = quantize_with_scale(x2, s[0])
+    return q.reshape(x.shape), s.astype(np.float32)
+
+
+def dequantize(q: np.ndarray, s) -> np.ndarray:
+    """x_hat = x_q / s in fp64 ([VG] 'Symmetric quantization', Fig. 19)."""
+    return np.asarray(q, dtype=np.float64) / np.asarray(s, dtype=np.float64)
+
+
+def ternary_absmean(w: np.ndarray):
+    """BitNet b1.58 absmean quantization to {-1, 0, +1} for the whole tensor.
+
+    [VG] 'BitNet b1.58' (Fig. 60): gamma is the mean absolute weight; each
+    weight is divided by gamma, rounded and clipped to [-1, 1].  gamma is the
+    correctly rounded fp32 of the exact mean; W / gamma is one fp32 division;
+    rounding is half-to-even.  gamma = 0 (all-zero tensor) gives all-zero codes.
+    Returns (codes int8, gamma fp32)."""
+    w = np.asarray(w, dtype=np.float32)
+    gamma = mean_abs_f32(w) if w.size else np.float32(0)
+    if gamma == 0:
+        return np.zeros(w.shape, np.int8), np.float32(0)
+    with np.errstate(over="ignore"):
+        t = (w / gamma).astype(np.float32)
+    q = np.clip(np.rint(t), -1, 1).astype(np.int8)
+    return q, np.float32(gamma)
+
+
+def sign_residual_split(w: np.ndarray):
+    """Separated quantization of a weight matrix into a sign backbone and an
+    int8 residual, per output row.
+
+    [SEP] section 2.1: W ~ alpha * sign(W) + W_res with W_res = W - alpha*sign(W),
+    and the residual is itself quantized to 8 bits with a scale of its own
+    ([SEP] section 6.3).  sign maps negatives to -1 and non-negatives (incl.
+    -0.0) to +1 ([VG] 'BitNet, weight quantization', Fig. 55); alpha of a row is
+    its mean |W| (the least-squares optimum of ||W - alpha*sign(W)||^2) as a
+    correctly rounded fp32; R = fl32(W - alpha*sign); (Rq, s_r) = per-row
+    absmax int8 of R.
+    Returns (sign int8 +-1, alpha fp32 [n], rq int8 [n][k], s_r fp32 [n])."""
+    w = np.asarray(w, dtype=np.float32)
+    if w.ndim != 2:
+        raise ValueError("2-D weight expected")
+    sign = np.where(w >= np.float32(0), 1, -1).astype(np.int8)
+    alpha = mean_abs_rows_f32(w) if w.shape[1] else np.zeros(w.shape[0], np.float32)
+    backbone = (alpha[:, None] * sign.astype(np.float32)).astype(np.float32)
+    r = (w - backbone).astype(np.float32)
+    rq, s_r = quantize_absmax(r, per_row=True)
+    return sign, alpha, rq, s_r
+
+
+def outlier_split_quantize(x_bf16_bits: np.ndarray, idx: np.ndarray):
+    """Activation outlier-channel split with per-token int8 quantization.
+
+    [SEP] section 2.2: the few channels whose activations are tens of times
+    larger are taken out and kept in high precision (here bf16, gathered
+    into X_out[m][j] = X[m][idx[j]]); the remaining channels are quantized to
+    int8.  The per-token absmax covers only the non-outlier channels and the
+    outlier columns of Xq are 0.
+    Returns (xq int8 [m][k], s_x fp32 [m], x_out bf16 bits [m][n_out])."""
+    xb = np.asarray(x_bf16_bits, dtype=np.uint16)
+    x = bf16_bits_to_f32(xb)
+    m, k = x.shape
+    idx = np.asarray(idx, dtype=np.int64)
+    is_out = np.zeros(k, dtype=bool)
+    is_out[idx] = True
+    keep = ~is_out
+    if keep.any():
+        alpha = np.max(np.abs(x[:, keep]), axis=1)
+    else:
+        alpha = np.zeros(m, np.float32)
+    s = absmax_scale(alpha)
+    xq = quantize_with_scale(x, s[:, None])
+    xq[:, is_out] = 0
+    x_out = np.ascontiguousarray(xb[:, idx])
+    return xq, s, x_out
+
+
+def gather_outlier_weights(w: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """W_out[n][j] = bf16(W[n][idx[j]]): the high-precision weights that the
+    outlier channels multiply ([SEP] section 2.2, high-precision path).
+    Returns bf16 bit patterns [n][n_out]."""
+    w = np.asarray(w, dtype=np.float32)
+    return f32_to_bf16_bits(np.ascontiguousarray(w[:, np.asarray(idx, dtype=np.int64)]))
