@@ -1,0 +1,255 @@
+/*
+ * qgemv.h -- C ABI of the MI355X (gfx950) quantized-GEMV library.
+ *
+ * Symmetric absmax / absmean quantization of LLM weights and activations to
+ * int8, ternary (1.58-bit, packed 2 bits per weight) and "1-bit sign backbone
+ * + int8 residual", the packed batch-1 matrix-vector products that decode
+ * runs on them, and a W8A8 prefill GEMM with an activation outlier-channel
+ * split.
+ *
+ * Sources cited below (by short tag):
+ *   [SEP]  "1-bit quantization is not magic": blog on separated
+ *          quantization, m.lqnn.cn/news/241359.
+ *   [VG]   "A Visual Guide to LLM Quantization" (Chinese translation),
+ *          puppylpg.github.io.
+ *   [OVR]  LLM quantization overview, 2048ai.net/68d1f9e38867235e13877cac.html.
+ *   [T158] "1.58 bits vs FP8: what ternary weights actually buy",
+ *          feinterview.poetries.top.
+ *
+ * Conventions (every entry point)
+ *   - Pointers are DEVICE pointers unless a parameter says "host".  The caller
+ *     allocates and owns every buffer, including workspaces (sized by the
+ *     *_workspace_bytes queries).  The library never allocates, never frees
+ *     and never synchronizes.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     work is enqueued asynchronously on it; results are valid once the
+ *     stream has reached that point.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error nothing is launched and an error code is returned.  QG_ERR_HIP
+ *     reports a launch failure (hipGetLastError after the launch).
+ *   - Matrices are row-major with contiguous rows.  Base pointers that are
+ *     streamed must be 16-byte aligned (QG_ERR_ALIGN otherwise).
+ *   - Inputs are finite (non-finite inputs are a precondition violation; the
+ *     kernels stay in bounds but the codes are unspecified).
+ *   - Scales are the quantization MULTIPLIER s = 127 / max|x| ([VG]
+ *     'Symmetric quantization', Fig. 17), except the ternary gamma and the
+ *     sign-backbone alpha, which are dequantization steps (mean |W|).
+ *   - Calls are stateless and may be issued from several host threads.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t qg_status;
+#define QG_OK            0
+#define QG_ERR_NULLPTR   1  /* a required pointer is NULL */
+#define QG_ERR_SHAPE     2  /* a size is out of range or not a required multiple */
+#define QG_ERR_ALIGN     3  /* a streamed pointer is not 16-byte aligned */
+#define QG_ERR_ARG       4  /* unsupported format / mode / dtype, or bad index list */
+#define QG_ERR_WORKSPACE 5  /* workspace missing or too small */
+#define QG_ERR_HIP       6  /* the HIP runtime reported an error at launch */
+
+/* element types */
+#define QG_F32  0
+#define QG_BF16 1
+
+/* quantization granularity */
+#define QG_PER_TENSOR 0
+#define QG_PER_ROW    1
+
+/* weight formats of qg_weight.fmt */
+#define QG_WFMT_INT8       0  /* int8 codes [n][k], per-row scale s_w[n]            */
+#define QG_WFMT_TERNARY2   1  /* 2-bit packed ternary [n][k/4], per-tensor gamma    */
+#define QG_WFMT_SIGN1_RES8 2  /* 1-bit sign [n][k/8] + alpha[n], int8 residual      */
+                              /* [n][k] + its own per-row scale s_r[n]              */
+
+/* activation modes of qg_qgemv */
+#define QG_ACT_INT8  0  /* x is quantized per tensor (absmax int8) inside the call */
+#define QG_ACT_FLOAT 1  /* x is used as given (bf16), fp32 accumulation            */
+
+/* limits */
+#define QG_MAX_OUTLIERS 256     /* n_out of the outlier split                     */
+#define QG_QGEMV_MAX_K  32768   /* k of qg_qgemv (the activation vector is staged on chip) */
+
+/* Human-readable text for a status code (static storage). */
+const char* qg_status_str(qg_status s);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int32_t qg_abi_version(void);
+
+/*
+ * Symmetric absmax int8 quantization ([VG] 'Symmetric quantization', absmax,
+ * Fig. 16-18; [OVR] section 3.1 steps 1-3; granularity per [OVR] section 2.3).
+ *   alpha = max|x| over the group (a row, or the whole tensor);
+ *   s = fl32(127 / alpha)  (IEEE fp32 division; s = 1 when alpha = 0);
+ *   q = clip(round_half_even(fl32(x * s)), -127, 127).
+ * x      : [rows][cols] of type xt (QG_F32 or QG_BF16), 16-B aligned.
+ * q      : [rows][cols] int8 (out), 16-B aligned.
+ * s      : [rows] (QG_PER_ROW) or [1] (QG_PER_TENSOR) fp32 (out).
+ * ws     : workspace of qg_quantize_absmax_workspace_bytes() bytes (may be
+ *          NULL when that is 0).
+ * cols % 8 == 0; rows >= 1; cols >= 8.
+ */
+size_t qg_quantize_absmax_workspace_bytes(int64_t rows, int64_t cols, int32_t gran);
+qg_status qg_quantize_absmax(const void* x, int32_t xt, int64_t rows, int64_t cols,
+                             int32_t gran, int8_t* q, float* s,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Activation outlier-channel split with per-token int8 quantization
+ * ([SEP] section 2.2: a few channels tens of times larger are taken out and
+ * kept in high precision; the rest go to int8; the channel list is found once
+ * and cached).  For each row m:
+ *   s[m]  = fl32(127 / max_{k not in idx} |x[m][k]|)  (1 when that max is 0);
+ *   q[m][k] = clip(rne(fl32(x[m][k] * s[m])), -127, 127) for k not in idx,
+ *             0 for k in idx;
+ *   x_out[m][j] = x[m][idx[j]]  (bf16, copied bit for bit).
+ * x      : [rows][cols] bf16, 16-B aligned.
+ * idx    : HOST array of n_out int32, strictly increasing, in [0, cols)
+ *          (QG_ERR_ARG otherwise); n_out in [0, QG_MAX_OUTLIERS]; may be NULL
+ *          when n_out = 0.
+ * q      : [rows][cols] int8 (out), 16-B aligned.  s: [rows] fp32 (out).
+ * x_out  : [rows][n_out] bf16 (out); may be NULL when n_out = 0.
+ * cols % 8 == 0; cols <= 262144.
+ */
+qg_status qg_quantize_absmax_split(const void* x, int64_t rows, int64_t cols,
+                                   const int32_t* idx, int32_t n_out,
+                                   int8_t* q, float* s, void* x_out, void* stream);
+
+/*
+ * Gather the outlier channels' weights in high precision:
+ * w_out[n][j] = bf16_rne(w[n][idx[j]]) ([SEP] section 2.2, high-precision path).
+ * w      : [n][k] fp32.   idx: HOST array as in qg_quantize_absmax_split.
+ * w_out  : [n][n_out] bf16 (out).
+ */
+qg_status qg_gather_columns_bf16(const float* w, int64_t n, int64_t k,
+                                 const int32_t* idx, int32_t n_out,
+                                 void* w_out, void* stream);
+
+/*
+ * Ternary (BitNet b1.58) absmean quantization of a whole tensor ([VG]
+ * 'BitNet b1.58', Fig. 58-60; [OVR] section 5.1):
+ *   gamma = the fp32 nearest (ties to even) to the exact mean of |w|
+ *           (computed exactly, independent of summation order);
+ *   q = clip(rne(fl32(w / gamma)), -1, 1)  (all 0 when gamma = 0).
+ * w      : [n][k] fp32, 16-B aligned.
+ * q      : [n][k] int8 codes in {-1, 0, 1} (out), 16-B aligned.
+ * gamma  : [1] fp32 (out).
+ * ws     : qg_ternary_workspace_bytes() bytes, 8-B aligned.
+ * n * k % 4 == 0; n * k < 2^39.
+ */
+size_t qg_ternary_workspace_bytes(int64_t n, int64_t k);
+qg_status qg_quantize_ternary(const float* w, int64_t n, int64_t k, int8_t* q,
+                              float* gamma, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Separated quantization: 1-bit sign backbone + int8 residual, per output row
+ * ([SEP] section 2.1: W ~ alpha*sign(W) + W_res, W_res = W - alpha*sign(W),
+ * residual re-quantized to 8 bits; section 6.3: the residual keeps a scale of
+ * its own; sign of a non-negative weight is +1 per [VG] 'BitNet', Fig. 55):
+ *   sign[n][k] = +1 if w >= 0 (including -0.0), else -1;
+ *   alpha[n]   = fp32 nearest to the exact mean of |w[n][:]|;
+ *   R          = fl32(w - alpha[n] * sign);
+ *   s_r[n]     = fl32(127 / max|R[n][:]|) (1 when 0);
+ *   rq[n][k]   = clip(rne(fl32(R * s_r[n])), -127, 127).
+ * w: [n][k] fp32; sign, rq: [n][k] int8 (out); alpha, s_r: [n] fp32 (out).
+ * All 16-B aligned; k % 8 == 0; k < 2^31.
+ */
+qg_status qg_split_sign_residual(const float* w, int64_t n, int64_t k,
+                                 int8_t* sign, float* alpha, int8_t* rq, float* s_r,
+                                 void* stream);
+
+/*
+ * Bit packing of low-bit codes (the storage format behind [SEP] section 3.2's
+ * 0.125 byte per sign weight and [VG] 'BitNet b1.58''s log2(3) bits):
+ *   bits = 2: field = q + 1 in {0, 1, 2} (q in {-1, 0, 1}), 4 per byte;
+ *   bits = 1: field = 1 for q = +1, 0 for q = -1, 8 per byte.
+ * Code k of a row is stored in byte k / (8/bits) at bit offset
+ * bits * (k % (8/bits)), least significant field first; rows contiguous.
+ * codes : [n][k] int8.   packed: [n][k*bits/8] uint8 (out).
+ * k % (8 / bits) == 0.  Codes outside the allowed set give unspecified
+ * (in-bounds) bytes.
+ */
+qg_status qg_pack(const int8_t* codes, int64_t n, int64_t k, int32_t bits,
+                  uint8_t* packed, void* stream);
+/* Inverse of qg_pack (field 3 of a 2-bit code decodes to +2). */
+qg_status qg_unpack(const uint8_t* packed, int64_t n, int64_t k, int32_t bits,
+                    int8_t* codes, void* stream);
+
+/*
+ * A quantized weight matrix, described on the host (the struct lives in host
+ * memory; its pointers are device pointers, all 16-B aligned).
+ *   QG_WFMT_INT8      : codes = int8 [n][k];           scale = s_w[n]
+ *   QG_WFMT_TERNARY2  : codes = packed 2-bit [n][k/4]; scale = &gamma (1 fp32)
+ *   QG_WFMT_SIGN1_RES8: codes = packed 1-bit [n][k/8]; resid = int8 [n][k];
+ *                       scale = alpha[n]; scale2 = s_r[n]
+ */
+typedef struct qg_weight {
+    int32_t fmt;
+    int32_t reserved;
+    int64_t n, k;
+    const void* codes;
+    const int8_t* resid;
+    const float* scale;
+    const float* scale2;
+} qg_weight;
+
+/*
+ * Batch-1 quantized matrix-vector product for decode ([SEP] section 3.1 and
+ * [T158]: at batch 1 the time goes into reading the weights once per token;
+ * [VG] 'GGUF' block-wise in-kernel dequantization: codes are decoded in
+ * registers and used at once, never expanded in memory).
+ *
+ *   fmt INT8, amode QG_ACT_INT8 (W8A8, [VG] 'Why quantize activations'):
+ *       xq, s_x = per-tensor absmax int8 of x (as qg_quantize_absmax);
+ *       acc[n] = sum_k codes[n][k] * xq[k] (int32, exact);
+ *       y[n] = acc[n] / (s_w[n] * s_x).
+ *   fmt INT8, amode QG_ACT_FLOAT (weight-only W8A16):
+ *       y[n] = (sum_k codes[n][k] * x[k]) / s_w[n], fp32 accumulation.
+ *   fmt TERNARY2, amode QG_ACT_INT8 ([VG] 'BitNet b1.58' Fig. 58-59: +1 adds,
+ *       0 skips, -1 subtracts the int8 activation):
+ *       acc[n] = sum_k t[n][k] * xq[k] (int32, exact); y[n] = acc[n] * gamma / s_x.
+ *   fmt SIGN1_RES8, amode QG_ACT_FLOAT ([SEP] sections 2.3 and 3.3: backbone
+ *       and residual products in one fused kernel, results added):
+ *       y[n] = alpha[n] * sum_k sign[n][k] x[k] + (sum_k rq[n][k] x[k]) / s_r[n],
+ *       fp32 accumulation.
+ * x       : [k] of type xt (QG_F32 or QG_BF16; SIGN1_RES8 needs QG_BF16).
+ * y       : [n] of type yt (QG_F32 or QG_BF16; bf16 is rounded to nearest even).
+ * acc_out : [n] int32 raw accumulators (integer modes only); may be NULL.
+ * k % 128 == 0, 128 <= k <= QG_QGEMV_MAX_K, n >= 1.
+ */
+qg_status qg_qgemv(const qg_weight* w, int32_t amode, const void* x, int32_t xt,
+                   void* y, int32_t yt, int32_t* acc_out, void* stream);
+
+/*
+ * W8A8 prefill GEMM with the outlier-channel split ([SEP] section 2.2: outlier
+ * channels in high precision, the rest int8, contributions summed; [T158]:
+ * prefill is compute-bound, so the int8 part runs on the matrix cores).
+ *   (xq, s_x, x_out) = qg_quantize_absmax_split(x, idx);
+ *   acc[m][n] = sum_k xq[m][k] * wq[n][k]            (int32, exact);
+ *   y[m][n]   = acc[m][n] / (s_x[m] * s_w[n])
+ *             + sum_j x_out[m][j] * w_out[n][j]      (fp32).
+ * x      : [m][k] bf16.   idx: HOST int32 list as in qg_quantize_absmax_split.
+ * wq     : [n][k] int8 (per-row absmax codes of W, from qg_quantize_absmax).
+ * s_w    : [n] fp32.      w_out: [n][n_out] bf16 (qg_gather_columns_bf16).
+ * y      : [m][n] fp32 (out).   acc_out: [m][n] int32 (out) or NULL.
+ * ws     : qg_qgemm_workspace_bytes(m, k, n_out) bytes, 16-B aligned.
+ * k % 128 == 0, k <= 262144; m, n >= 1.
+ */
+size_t qg_qgemm_workspace_bytes(int64_t m, int64_t k, int32_t n_out);
+qg_status qg_qgemm_w8a8_outlier(const void* x, int64_t m, int64_t k,
+                                const int32_t* idx, int32_t n_out,
+                                const int8_t* wq, const float* s_w, const void* w_out,
+                                int64_t n, float* y, int32_t* acc_out,
+                                void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QGEMV_H */

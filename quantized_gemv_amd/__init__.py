@@ -1,0 +1,15 @@
+"""quantized_gemv_amd -- MI355X (gfx950) quantized GEMV library.
+
+Python side of the C ABI in include/qgemv.h: symmetric absmax / absmean
+quantization to int8, ternary and sign + int8-residual formats, bit packing,
+batch-1 quantized GEMV for decode and the W8A8 prefill GEMM with an
+activation outlier split.  All arithmetic runs in the HIP kernels of
+libqgemv.so; this package only marshals arguments (see _binding.py).
+"""
+from ._binding import (QgError, QWeight, CWeight, EXPORTED, LIB_PATH, lib, status_str,
+                       quantize_absmax, quantize_absmax_split, gather_columns_bf16, quantize_ternary,
+                       split_sign_residual, pack, unpack, qgemv, qgemv_launch_raw, qgemm_w8a8_outlier,
+                       QG_F32, QG_BF16, QG_PER_TENSOR, QG_PER_ROW, QG_WFMT_INT8, QG_WFMT_TERNARY2,
+                       QG_WFMT_SIGN1_RES8, QG_ACT_INT8, QG_ACT_FLOAT, QG_MAX_OUTLIERS, QG_QGEMV_MAX_K)
+
+__all__ = [n for n in dir() if not n.startswith("_")]

@@ -1,0 +1,269 @@
+"""ctypes binding over libqgemv.so (the C ABI declared in include/qgemv.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their data pointers and the current HIP stream are passed to the
+library, and a non-zero status raises ``QgError``.  Every computation runs in
+the library's HIP kernels; there is no fallback of any kind.  PyTorch is used
+for device memory (output and workspace allocation) and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgemv.so")
+
+QG_OK = 0
+QG_F32, QG_BF16 = 0, 1
+QG_PER_TENSOR, QG_PER_ROW = 0, 1
+QG_WFMT_INT8, QG_WFMT_TERNARY2, QG_WFMT_SIGN1_RES8 = 0, 1, 2
+QG_ACT_INT8, QG_ACT_FLOAT = 0, 1
+QG_MAX_OUTLIERS = 256
+QG_QGEMV_MAX_K = 32768
+
+_c_i32, _c_i64, _c_sz, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+
+class QgError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s failed: %s (status %d)" % (what, status_str(status), status))
+        self.status = status
+
+
+class CWeight(ctypes.Structure):
+    _fields_ = [("fmt", _c_i32), ("reserved", _c_i32), ("n", _c_i64), ("k", _c_i64),
+                ("codes", _c_vp), ("resid", _c_vp), ("scale", _c_vp), ("scale2", _c_vp)]
+
+
+_SIGS = {
+    "qg_status_str": (ctypes.c_char_p, [_c_i32]),
+    "qg_abi_version": (_c_i32, []),
+    "qg_quantize_absmax_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i32]),
+    "qg_quantize_absmax": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "qg_quantize_absmax_split": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "qg_gather_columns_bf16": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_vp, _c_vp]),
+    "qg_ternary_workspace_bytes": (_c_sz, [_c_i64, _c_i64]),
+    "qg_quantize_ternary": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "qg_split_sign_residual": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "qg_pack": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp]),
+    "qg_unpack": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp]),
+    "qg_qgemv": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp]),
+    "qg_qgemm_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i32]),
+    "qg_qgemm_w8a8_outlier": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i64,
+                                       _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+}
+EXPORTED = tuple(_SIGS)
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqgemv.so (built in-tree by quantized_gemv_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libqgemv.so is not built (%s); run quantized_gemv_amd.build.build()" % LIB_PATH)
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def status_str(st: int) -> str:
+    return lib().qg_status_str(st).decode()
+
+
+def _check(st: int, what: str):
+    if st != QG_OK:
+        raise QgError(st, what)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    return t
+
+
+def _xt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return QG_F32
+    if t.dtype == torch.bfloat16:
+        return QG_BF16
+    raise ValueError("activation dtype must be float32 or bfloat16")
+
+
+def _idx_host(idx: Optional[Sequence[int]]):
+    if idx is None:
+        return None, 0
+    arr = (ctypes.c_int32 * max(len(idx), 1))(*[int(v) for v in idx])
+    return arr, len(idx)
+
+
+# ------------------------------------------------------------------ quantizers
+
+def quantize_absmax(x: torch.Tensor, per_row: bool = True, q: torch.Tensor = None, s: torch.Tensor = None):
+    """Symmetric absmax int8 quantization (qg_quantize_absmax). Returns (q, s)."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    rows, cols = (1, x.shape[0]) if x.dim() == 1 else tuple(x.shape)
+    q = torch.empty(x.shape, dtype=torch.int8, device=x.device) if q is None else _dev(q, "q", torch.int8)
+    s = torch.empty(rows if per_row else 1, dtype=torch.float32, device=x.device) if s is None else _dev(s, "s", torch.float32)
+    gran = QG_PER_ROW if per_row else QG_PER_TENSOR
+    nws = lib().qg_quantize_absmax_workspace_bytes(rows, cols, gran)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=x.device) if nws else None
+    _check(lib().qg_quantize_absmax(_p(x), _xt(x), rows, cols, gran, _p(q), _p(s), _p(ws), nws, _stream(x)),
+           "qg_quantize_absmax")
+    return q, s
+
+
+def quantize_absmax_split(x: torch.Tensor, idx: Sequence[int]):
+    """Per-token int8 quantization with outlier channels split out
+    (qg_quantize_absmax_split). Returns (q, s, x_out)."""
+    _dev(x, "x", torch.bfloat16)
+    rows, cols = x.shape
+    cidx, n_out = _idx_host(idx)
+    q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    s = torch.empty(rows, dtype=torch.float32, device=x.device)
+    xo = torch.empty((rows, n_out), dtype=torch.bfloat16, device=x.device)
+    _check(lib().qg_quantize_absmax_split(_p(x), rows, cols, cidx, n_out, _p(q), _p(s), _p(xo) if n_out else None,
+                                          _stream(x)), "qg_quantize_absmax_split")
+    return q, s, xo
+
+
+def gather_columns_bf16(w: torch.Tensor, idx: Sequence[int]):
+    """W_out[n][j] = bf16(W[n][idx[j]]) (qg_gather_columns_bf16)."""
+    _dev(w, "w", torch.float32)
+    n, k = w.shape
+    cidx, n_out = _idx_host(idx)
+    wo = torch.empty((n, n_out), dtype=torch.bfloat16, device=w.device)
+    _check(lib().qg_gather_columns_bf16(_p(w), n, k, cidx, n_out, _p(wo) if n_out else None, _stream(w)),
+           "qg_gather_columns_bf16")
+    return wo
+
+
+def quantize_ternary(w: torch.Tensor):
+    """Ternary absmean quantization (qg_quantize_ternary). Returns (codes, gamma[1])."""
+    _dev(w, "w", torch.float32)
+    n, k = (1, w.shape[0]) if w.dim() == 1 else tuple(w.shape)
+    q = torch.empty(w.shape, dtype=torch.int8, device=w.device)
+    g = torch.empty(1, dtype=torch.float32, device=w.device)
+    nws = lib().qg_ternary_workspace_bytes(n, k)
+    ws = torch.empty(nws, dtype=torch.uint8, device=w.device)
+    _check(lib().qg_quantize_ternary(_p(w), n, k, _p(q), _p(g), _p(ws), nws, _stream(w)), "qg_quantize_ternary")
+    return q, g
+
+
+def split_sign_residual(w: torch.Tensor):
+    """Sign backbone + int8 residual split (qg_split_sign_residual).
+    Returns (sign int8, alpha, rq int8, s_r)."""
+    _dev(w, "w", torch.float32)
+    n, k = w.shape
+    sign = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    rq = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    alpha = torch.empty(n, dtype=torch.float32, device=w.device)
+    s_r = torch.empty(n, dtype=torch.float32, device=w.device)
+    _check(lib().qg_split_sign_residual(_p(w), n, k, _p(sign), _p(alpha), _p(rq), _p(s_r), _stream(w)),
+           "qg_split_sign_residual")
+    return sign, alpha, rq, s_r
+
+
+def pack(codes: torch.Tensor, bits: int, out: torch.Tensor = None):
+    """Bit packing (qg_pack): bits=2 ternary, bits=1 sign."""
+    _dev(codes, "codes", torch.int8)
+    n, k = (1, codes.shape[0]) if codes.dim() == 1 else tuple(codes.shape)
+    if bits not in (1, 2) or k % (8 // bits):
+        raise ValueError("bad bits or row length")
+    out = torch.empty((n, k * bits // 8), dtype=torch.uint8, device=codes.device) if out is None else out
+    _check(lib().qg_pack(_p(codes), n, k, bits, _p(out), _stream(codes)), "qg_pack")
+    return out
+
+
+def unpack(packed: torch.Tensor, bits: int, k: int):
+    """Inverse of pack (qg_unpack)."""
+    _dev(packed, "packed", torch.uint8)
+    n = packed.shape[0] if packed.dim() == 2 else 1
+    out = torch.empty((n, k), dtype=torch.int8, device=packed.device)
+    _check(lib().qg_unpack(_p(packed), n, k, bits, _p(out), _stream(packed)), "qg_unpack")
+    return out
+
+
+# ------------------------------------------------------------------ products
+
+@dataclass
+class QWeight:
+    """A quantized weight matrix as the library stores it."""
+    fmt: int
+    n: int
+    k: int
+    codes: torch.Tensor
+    scale: torch.Tensor
+    resid: Optional[torch.Tensor] = None
+    scale2: Optional[torch.Tensor] = None
+
+    def c_struct(self) -> CWeight:
+        return CWeight(self.fmt, 0, self.n, self.k, self.codes.data_ptr(),
+                       self.resid.data_ptr() if self.resid is not None else None,
+                       self.scale.data_ptr(),
+                       self.scale2.data_ptr() if self.scale2 is not None else None)
+
+
+def qgemv(w: QWeight, x: torch.Tensor, act_int8: bool, y_dtype=torch.float32, y: torch.Tensor = None,
+          acc_out: torch.Tensor = None):
+    """Batch-1 quantized GEMV (qg_qgemv). Returns y."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    if y is None:
+        y = torch.empty(w.n, dtype=y_dtype, device=x.device)
+    _dev(y, "y", (torch.float32, torch.bfloat16))
+    if acc_out is not None:
+        _dev(acc_out, "acc_out", torch.int32)
+    cw = w.c_struct()
+    _check(lib().qg_qgemv(ctypes.byref(cw), QG_ACT_INT8 if act_int8 else QG_ACT_FLOAT, _p(x), _xt(x), _p(y), _xt(y),
+                          _p(acc_out), _stream(x)), "qg_qgemv")
+    return y
+
+
+def qgemv_launch_raw(cw: CWeight, amode: int, x_ptr: int, xt: int, y_ptr: int, yt: int, stream_ptr: int) -> int:
+    """Pre-marshalled launch for tight timing loops (returns the status)."""
+    return lib().qg_qgemv(ctypes.byref(cw), amode, ctypes.c_void_p(x_ptr), xt, ctypes.c_void_p(y_ptr), yt, None,
+                          ctypes.c_void_p(stream_ptr))
+
+
+def qgemm_w8a8_outlier(x: torch.Tensor, idx: Sequence[int], wq: torch.Tensor, s_w: torch.Tensor,
+                       w_out: Optional[torch.Tensor], y: torch.Tensor = None, acc_out: torch.Tensor = None,
+                       ws: torch.Tensor = None):
+    """W8A8 prefill GEMM with the outlier split (qg_qgemm_w8a8_outlier). Returns y."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(wq, "wq", torch.int8)
+    _dev(s_w, "s_w", torch.float32)
+    m, k = x.shape
+    n = wq.shape[0]
+    cidx, n_out = _idx_host(idx)
+    if n_out:
+        _dev(w_out, "w_out", torch.bfloat16)
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    nws = lib().qg_qgemm_workspace_bytes(m, k, n_out)
+    if ws is None:
+        ws = torch.empty(nws, dtype=torch.uint8, device=x.device)
+    _check(lib().qg_qgemm_w8a8_outlier(_p(x), m, k, cidx, n_out, _p(wq), _p(s_w), _p(w_out) if n_out else None, n,
+                                       _p(y), _p(acc_out), _p(ws), ws.numel(), _stream(x)), "qg_qgemm_w8a8_outlier")
+    return y

@@ -1,0 +1,230 @@
+// api.cpp -- the C ABI of include/qgemv.h: host-side argument validation,
+// workspace carving and dispatch to the launchers.  Every check runs before
+// any HIP call, so invalid arguments are rejected without touching a device.
+#include "../../include/qgemv.h"
+
+#include <hip/hip_runtime.h>
+
+#include "qg_launch.h"
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline qg_status from_hip(hipError_t e) { return e == hipSuccess ? QG_OK : QG_ERR_HIP; }
+
+// Validates a host index list: strictly increasing, inside [0, cols).
+qg_status check_idx(const int32_t* idx, int32_t n_out, int64_t cols, qg::OutlierIdx* out) {
+    if (n_out < 0 || n_out > QG_MAX_OUTLIERS) return QG_ERR_ARG;
+    if (n_out > 0 && !idx) return QG_ERR_NULLPTR;
+    for (int i = 0; i < qg::kMaxOutliers; ++i) out->v[i] = 0;
+    for (int32_t j = 0; j < n_out; ++j) {
+        if (idx[j] < 0 || idx[j] >= cols) return QG_ERR_ARG;
+        if (j > 0 && idx[j] <= idx[j - 1]) return QG_ERR_ARG;
+        out->v[j] = idx[j];
+    }
+    return QG_OK;
+}
+
+size_t qgemm_layout(int64_t m, int64_t k, int32_t n_out, size_t* off_sx, size_t* off_xo, int* ld) {
+    const int l = n_out > 0 ? (int)align_up((size_t)n_out, 16) : 0;
+    const size_t xq = (size_t)m * (size_t)k;
+    const size_t sx = align_up(xq, 256);
+    const size_t xo = align_up(sx + (size_t)m * sizeof(float), 256);
+    const size_t total = align_up(xo + (size_t)m * (size_t)l * 2, 256);
+    if (off_sx) *off_sx = sx;
+    if (off_xo) *off_xo = xo;
+    if (ld) *ld = l;
+    return total;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qg_status_str(qg_status s) {
+    switch (s) {
+        case QG_OK: return "ok";
+        case QG_ERR_NULLPTR: return "a required pointer is NULL";
+        case QG_ERR_SHAPE: return "a size is out of range or not a required multiple";
+        case QG_ERR_ALIGN: return "a streamed pointer is not 16-byte aligned";
+        case QG_ERR_ARG: return "unsupported format/mode/dtype or bad index list";
+        case QG_ERR_WORKSPACE: return "workspace missing or too small";
+        case QG_ERR_HIP: return "HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+int32_t qg_abi_version(void) { return 10000; }
+
+size_t qg_quantize_absmax_workspace_bytes(int64_t rows, int64_t cols, int32_t gran) {
+    if (gran != QG_PER_TENSOR || rows < 1 || cols < 8) return 0;
+    return (size_t)qg::absmax_tensor_parts(rows * cols) * sizeof(float);
+}
+
+qg_status qg_quantize_absmax(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t gran, int8_t* q,
+                             float* s, void* ws, size_t ws_bytes, void* stream) {
+    if (!x || !q || !s) return QG_ERR_NULLPTR;
+    if (xt != QG_F32 && xt != QG_BF16) return QG_ERR_ARG;
+    if (gran != QG_PER_TENSOR && gran != QG_PER_ROW) return QG_ERR_ARG;
+    if (rows < 1 || cols < 8 || cols % 8 != 0 || rows > ((int64_t)1 << 40) / cols) return QG_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(q)) return QG_ERR_ALIGN;
+    if (gran == QG_PER_ROW) return from_hip(qg::launch_absmax_rows(x, xt, rows, cols, q, s, as_stream(stream)));
+    const size_t need = qg_quantize_absmax_workspace_bytes(rows, cols, gran);
+    if (!ws || ws_bytes < need) return QG_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & 3u) != 0) return QG_ERR_ALIGN;
+    return from_hip(qg::launch_absmax_tensor(x, xt, rows * cols, q, s, static_cast<float*>(ws), as_stream(stream)));
+}
+
+qg_status qg_quantize_absmax_split(const void* x, int64_t rows, int64_t cols, const int32_t* idx, int32_t n_out,
+                                   int8_t* q, float* s, void* x_out, void* stream) {
+    if (!x || !q || !s) return QG_ERR_NULLPTR;
+    if (n_out > 0 && !x_out) return QG_ERR_NULLPTR;
+    if (rows < 1 || cols < 8 || cols % 8 != 0 || cols > 262144 || rows > ((int64_t)1 << 40) / cols)
+        return QG_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(q)) return QG_ERR_ALIGN;
+    qg::OutlierIdx oi;
+    const qg_status st = check_idx(idx, n_out, cols, &oi);
+    if (st != QG_OK) return st;
+    return from_hip(qg::launch_absmax_split(static_cast<const uint16_t*>(x), rows, cols, oi, n_out, q, s,
+                                            static_cast<uint16_t*>(x_out), n_out, as_stream(stream)));
+}
+
+qg_status qg_gather_columns_bf16(const float* w, int64_t n, int64_t k, const int32_t* idx, int32_t n_out,
+                                 void* w_out, void* stream) {
+    if (!w) return QG_ERR_NULLPTR;
+    if (n_out > 0 && !w_out) return QG_ERR_NULLPTR;
+    if (n < 1 || k < 1) return QG_ERR_SHAPE;
+    qg::OutlierIdx oi;
+    const qg_status st = check_idx(idx, n_out, k, &oi);
+    if (st != QG_OK) return st;
+    return from_hip(qg::launch_gather_cols_bf16(w, n, k, oi, n_out, static_cast<uint16_t*>(w_out),
+                                                as_stream(stream)));
+}
+
+size_t qg_ternary_workspace_bytes(int64_t n, int64_t k) {
+    (void)n;
+    (void)k;
+    return 256 * sizeof(uint64_t);
+}
+
+qg_status qg_quantize_ternary(const float* w, int64_t n, int64_t k, int8_t* q, float* gamma, void* ws,
+                              size_t ws_bytes, void* stream) {
+    if (!w || !q || !gamma) return QG_ERR_NULLPTR;
+    if (n < 1 || k < 1) return QG_ERR_SHAPE;
+    if (n > ((int64_t)1 << 39) / k) return QG_ERR_SHAPE;
+    const int64_t count = n * k;
+    if (count % 4 != 0) return QG_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(q)) return QG_ERR_ALIGN;
+    if (!ws || ws_bytes < qg_ternary_workspace_bytes(n, k)) return QG_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & 7u) != 0) return QG_ERR_ALIGN;
+    return from_hip(qg::launch_ternary(w, count, q, gamma, static_cast<uint64_t*>(ws), as_stream(stream)));
+}
+
+qg_status qg_split_sign_residual(const float* w, int64_t n, int64_t k, int8_t* sign, float* alpha, int8_t* rq,
+                                 float* s_r, void* stream) {
+    if (!w || !sign || !alpha || !rq || !s_r) return QG_ERR_NULLPTR;
+    if (n < 1 || k < 8 || k % 8 != 0 || k >= ((int64_t)1 << 31)) return QG_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(sign) || !aligned16(rq)) return QG_ERR_ALIGN;
+    return from_hip(qg::launch_split_sign_residual(w, n, k, sign, alpha, rq, s_r, as_stream(stream)));
+}
+
+qg_status qg_pack(const int8_t* codes, int64_t n, int64_t k, int32_t bits, uint8_t* packed, void* stream) {
+    if (!codes || !packed) return QG_ERR_NULLPTR;
+    if (bits != 1 && bits != 2) return QG_ERR_ARG;
+    if (n < 1 || k < 1 || k % (8 / bits) != 0 || n > ((int64_t)1 << 40) / k) return QG_ERR_SHAPE;
+    if (!aligned16(codes)) return QG_ERR_ALIGN;
+    return from_hip(qg::launch_pack(codes, n * k, bits, packed, as_stream(stream)));
+}
+
+qg_status qg_unpack(const uint8_t* packed, int64_t n, int64_t k, int32_t bits, int8_t* codes, void* stream) {
+    if (!codes || !packed) return QG_ERR_NULLPTR;
+    if (bits != 1 && bits != 2) return QG_ERR_ARG;
+    if (n < 1 || k < 1 || k % (8 / bits) != 0 || n > ((int64_t)1 << 40) / k) return QG_ERR_SHAPE;
+    if (!aligned16(codes)) return QG_ERR_ALIGN;
+    return from_hip(qg::launch_unpack(packed, n * k, bits, codes, as_stream(stream)));
+}
+
+qg_status qg_qgemv(const qg_weight* w, int32_t amode, const void* x, int32_t xt, void* y, int32_t yt,
+                   int32_t* acc_out, void* stream) {
+    if (!w || !x || !y) return QG_ERR_NULLPTR;
+    if (!w->codes || !w->scale) return QG_ERR_NULLPTR;
+    if (xt != QG_F32 && xt != QG_BF16) return QG_ERR_ARG;
+    if (yt != QG_F32 && yt != QG_BF16) return QG_ERR_ARG;
+    if (amode != QG_ACT_INT8 && amode != QG_ACT_FLOAT) return QG_ERR_ARG;
+    switch (w->fmt) {
+        case QG_WFMT_INT8: break;
+        case QG_WFMT_TERNARY2:
+            if (amode != QG_ACT_INT8) return QG_ERR_ARG;
+            break;
+        case QG_WFMT_SIGN1_RES8:
+            if (amode != QG_ACT_FLOAT || xt != QG_BF16) return QG_ERR_ARG;
+            if (!w->resid || !w->scale2) return QG_ERR_NULLPTR;
+            break;
+        default: return QG_ERR_ARG;
+    }
+    if (acc_out && amode != QG_ACT_INT8) return QG_ERR_ARG;
+    if (w->n < 1 || w->n >= ((int64_t)1 << 31)) return QG_ERR_SHAPE;
+    if (w->k < 128 || w->k % 128 != 0 || w->k > QG_QGEMV_MAX_K) return QG_ERR_SHAPE;
+    if (!aligned16(w->codes) || !aligned16(x)) return QG_ERR_ALIGN;
+    if (w->fmt == QG_WFMT_SIGN1_RES8 && !aligned16(w->resid)) return QG_ERR_ALIGN;
+    qg::QgemvArgs a;
+    a.fmt = w->fmt;
+    a.amode = amode;
+    a.xt = xt;
+    a.yt = yt;
+    a.n = w->n;
+    a.k = w->k;
+    a.codes = w->codes;
+    a.resid = w->resid;
+    a.scale = w->scale;
+    a.scale2 = w->scale2;
+    a.x = x;
+    a.y = y;
+    a.acc_out = acc_out;
+    return from_hip(qg::launch_qgemv(a, as_stream(stream)));
+}
+
+size_t qg_qgemm_workspace_bytes(int64_t m, int64_t k, int32_t n_out) {
+    if (m < 1 || k < 1 || n_out < 0 || n_out > QG_MAX_OUTLIERS) return 0;
+    return qgemm_layout(m, k, n_out, nullptr, nullptr, nullptr);
+}
+
+qg_status qg_qgemm_w8a8_outlier(const void* x, int64_t m, int64_t k, const int32_t* idx, int32_t n_out,
+                                const int8_t* wq, const float* s_w, const void* w_out, int64_t n, float* y,
+                                int32_t* acc_out, void* ws, size_t ws_bytes, void* stream) {
+    if (!x || !wq || !s_w || !y) return QG_ERR_NULLPTR;
+    if (n_out > 0 && !w_out) return QG_ERR_NULLPTR;
+    if (m < 1 || n < 1 || m >= ((int64_t)1 << 31) || n >= ((int64_t)1 << 31)) return QG_ERR_SHAPE;
+    if (k < 128 || k % 128 != 0 || k > 262144) return QG_ERR_SHAPE;
+    if (m > ((int64_t)1 << 40) / k || n > ((int64_t)1 << 40) / k) return QG_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(wq)) return QG_ERR_ALIGN;
+    qg::OutlierIdx oi;
+    const qg_status st = check_idx(idx, n_out, k, &oi);
+    if (st != QG_OK) return st;
+    size_t off_sx = 0, off_xo = 0;
+    int ld = 0;
+    const size_t need = qgemm_layout(m, k, n_out, &off_sx, &off_xo, &ld);
+    if (!ws || ws_bytes < need) return QG_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QG_ERR_ALIGN;
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    qg::QgemmArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.m = m;
+    a.k = k;
+    a.n = n;
+    a.wq = wq;
+    a.s_w = s_w;
+    a.w_out = static_cast<const uint16_t*>(w_out);
+    a.n_out = n_out;
+    a.y = y;
+    a.acc_out = acc_out;
+    a.xq = reinterpret_cast<int8_t*>(base);
+    a.s_x = reinterpret_cast<float*>(base + off_sx);
+    a.x_out = reinterpret_cast<uint16_t*>(base + off_xo);
+    a.x_out_ld = ld;
+    return from_hip(qg::launch_qgemm(a, oi, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// qg_device.h -- device helpers shared by the gfx950 kernels.
+//
+// Everything here is written for CDNA4 wave64: 256-thread workgroups are
+// four waves, wave-level reductions use cross-lane shuffles, and streamed
+// loads go through buffer resources so that out-of-range lanes read zeros
+// instead of faulting.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "exact_mean.h"
+
+namespace qg {
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
+
+// Round-to-nearest-even narrowing of a finite fp32 to bf16 bits.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ------------------------------------------------------------------ absmax step
+// s = 127 / alpha as one IEEE fp32 division (the build keeps division
+// correctly rounded); an all-zero group gets s = 1 so its codes are 0.
+__device__ __forceinline__ float absmax_scale(float alpha) {
+    return alpha == 0.0f ? 1.0f : 127.0f / alpha;
+}
+
+// clip(round_half_even(fl32(x * s)), -127, 127).  The build disables FP
+// contraction, so the product is rounded on its own before rint.
+__device__ __forceinline__ int qcode(float x, float s) {
+    float t = x * s;
+    t = __builtin_rintf(t);
+    t = __builtin_fminf(__builtin_fmaxf(t, -127.0f), 127.0f);
+    return (int)t;
+}
+
+// ------------------------------------------------------------------ reductions
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+// Block-wide max / sum over a 256-thread workgroup; `scratch` holds >= 4
+// elements of shared memory.  All threads receive the result.  Contains two
+// barriers, so every thread of the block must call it.
+__device__ __forceinline__ float block_max(float v, float* scratch) {
+    v = wave_max(v);
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    if (lane == 0) scratch[w] = v;
+    __syncthreads();
+    float r = scratch[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) r = __builtin_fmaxf(r, scratch[i]);
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ int block_sum_int(int v, int* scratch) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    if (lane == 0) scratch[w] = v;
+    __syncthreads();
+    int r = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) r += scratch[i];
+    __syncthreads();
+    return r;
+}
+
+// ------------------------------------------------------------------ buffer loads
+// Raw buffer resource over [base, base + bytes): loads whose range ends past
+// `bytes` return zeros (hardware range check), so tails need no branches.
+// Word 3 0x00020000 is the gfx9-family raw 32-bit data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+}  // namespace qg

@@ -1,0 +1,64 @@
+// qg_launch.h -- host-side launchers implemented in the .hip translation
+// units and called by the C ABI layer (api.cpp) after argument validation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+constexpr int kMaxOutliers = 256;
+
+// The cached outlier channel list travels by value in the kernel arguments.
+struct OutlierIdx {
+    int32_t v[kMaxOutliers];
+};
+
+hipError_t launch_absmax_rows(const void* x, int xt, int64_t rows, int64_t cols, int8_t* q, float* s,
+                              hipStream_t st);
+int absmax_tensor_parts(int64_t elems);
+hipError_t launch_absmax_tensor(const void* x, int xt, int64_t elems, int8_t* q, float* s, float* partial,
+                                hipStream_t st);
+hipError_t launch_absmax_split(const uint16_t* x, int64_t rows, int64_t cols, const OutlierIdx& idx, int n_out,
+                               int8_t* q, float* s, uint16_t* x_out, int x_out_ld, hipStream_t st);
+hipError_t launch_gather_cols_bf16(const float* w, int64_t n, int64_t k, const OutlierIdx& idx, int n_out,
+                                   uint16_t* w_out, hipStream_t st);
+hipError_t launch_ternary(const float* w, int64_t count, int8_t* q, float* gamma, uint64_t* hist, hipStream_t st);
+hipError_t launch_split_sign_residual(const float* w, int64_t n, int64_t k, int8_t* sign, float* alpha, int8_t* rq,
+                                      float* s_r, hipStream_t st);
+hipError_t launch_pack(const int8_t* codes, int64_t count, int bits, uint8_t* packed, hipStream_t st);
+hipError_t launch_unpack(const uint8_t* packed, int64_t count, int bits, int8_t* codes, hipStream_t st);
+
+struct QgemvArgs {
+    int fmt, amode, xt, yt;
+    int64_t n, k;
+    const void* codes;
+    const int8_t* resid;
+    const float* scale;
+    const float* scale2;
+    const void* x;
+    void* y;
+    int32_t* acc_out;
+};
+hipError_t launch_qgemv(const QgemvArgs& a, hipStream_t st);
+
+struct QgemmArgs {
+    const uint16_t* x;
+    int64_t m, k, n;
+    const int8_t* wq;
+    const float* s_w;
+    const uint16_t* w_out;
+    int n_out;
+    float* y;
+    int32_t* acc_out;
+    // workspace views
+    int8_t* xq;
+    float* s_x;
+    uint16_t* x_out;
+    int x_out_ld;
+};
+hipError_t launch_qgemm(const QgemmArgs& a, const OutlierIdx& idx, hipStream_t st);
+
+int device_cu_count();
+
+}  // namespace qg

@@ -1,0 +1,423 @@
+// qgemv.hip -- batch-1 quantized matrix-vector products for gfx950.
+//
+// At batch 1 every weight byte is read once per token and the arithmetic per
+// byte is a handful of ALU operations, so the kernel is bound by HBM
+// bandwidth: the design goal is to keep enough 16-byte loads in flight on
+// every CU and to keep the per-byte ALU work well under the VALU budget.
+//
+// Layout of the work
+//   * grid: about one 256-thread workgroup per CU, each owning a contiguous
+//     block of rows;
+//   * the activation vector is staged once per workgroup in LDS, in the form
+//     the inner loop wants (fp32; int8 codes quantized in-kernel; int8 codes
+//     permuted to the ternary unpack order; bf16 pairs for the sign path),
+//     zero-padded so ragged K needs no branches;
+//   * each wave takes groups of U rows; an "item" is U rows x JS chunk
+//     columns per lane; items are double-buffered in registers so the next
+//     item's loads are in flight while the current one is reduced;
+//   * weights are read through buffer resources: out-of-range lanes (ragged
+//     rows or chunks) get zeros from the hardware range check;
+//   * per-row partial sums are reduced across the wave with lane shuffles and
+//     lane 0 applies the per-row scale and stores.
+//
+// Formats (codes as stored by the library's packing):
+//   INT8 (x float) : 16 B chunk = 16 int8 weights; v_cvt_f32_i32 (SDWA byte
+//                    select) + FMA against fp32 x.
+//   INT8 (x int8)  : 16 B chunk = 16 weights; v_dot4 against in-kernel int8 x.
+//   TERNARY2       : 16 B chunk = 64 weights as 2-bit fields q+1; each dword
+//                    is split into 4 masked byte planes (fields stay in place,
+//                    i.e. scaled by 1, 4, 16, 16) and fed to v_dot4 against x
+//                    permuted to the same order; sum_k (q+1) x - sum_k x.
+//   SIGN1_RES8     : 32-column unit = 32 B int8 residual + 4 B sign bits; the
+//                    residual becomes bf16 pairs (col j, col j+16) and the sign
+//                    bits become +-1.0 bf16 pairs with one bit-field insert;
+//                    both go through v_dot2_f32_bf16 against bf16 x pairs.
+#include "qg_device.h"
+#include "qg_launch.h"
+
+namespace qg {
+
+enum { F_INT8F = 0, F_INT8I = 1, F_TERN = 2, F_SR = 3 };
+
+struct KParams {
+    const uint8_t* codes;
+    const int8_t* resid;
+    const float* scale;
+    const float* scale2;
+    const void* x;
+    void* y;
+    int32_t* acc_out;
+    int32_t n, k, rows_per_wg;
+};
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+__device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+template <int F>
+struct Fmt;
+template <>
+struct Fmt<F_INT8F> {
+    static constexpr int kColsPerChunk = 16;
+    static constexpr int kLdsBytesPerCol = 4;
+    struct Frag { u32x4 w; };
+};
+template <>
+struct Fmt<F_INT8I> {
+    static constexpr int kColsPerChunk = 16;
+    static constexpr int kLdsBytesPerCol = 1;
+    struct Frag { u32x4 w; };
+};
+template <>
+struct Fmt<F_TERN> {
+    static constexpr int kColsPerChunk = 64;
+    static constexpr int kLdsBytesPerCol = 1;
+    struct Frag { u32x4 w; };
+};
+template <>
+struct Fmt<F_SR> {
+    static constexpr int kColsPerChunk = 32;
+    static constexpr int kLdsBytesPerCol = 2;
+    struct Frag { u32x4 r0, r1; uint32_t s; };
+};
+
+template <int XT>
+__device__ __forceinline__ void load8x(const void* base, int c, float v[8]) {
+    if constexpr (XT == 0) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + c);
+        const float4 a = p[0], b = p[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+        const uint4 h = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + c);
+        const uint32_t w[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+            v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+        }
+    }
+}
+
+template <int F, int XT, int YT, int U, int JS>
+__global__ __launch_bounds__(kThreads) void qgemv_kernel(KParams p) {
+    using Frag = typename Fmt<F>::Frag;
+    constexpr int kCols = Fmt<F>::kColsPerChunk;
+    extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+    __shared__ float redf[kWaves];
+    __shared__ int redi[kWaves];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int K = p.k;
+    const int row0 = blockIdx.x * p.rows_per_wg;
+    const int rows = min(p.rows_per_wg, p.n - row0);
+    const int C = K / kCols;           // chunks per row
+    const int J = (C + 63) / 64;       // chunk iterations per lane per row
+    const int nseg = (J + JS - 1) / JS;
+    // x is staged (zero-padded) for every chunk iteration a segment can touch
+    const int padded_cols = nseg * JS * 64 * kCols;
+
+    // ------------------------------------------------------------ stage x
+    float sx = 1.0f;  // activation scale (integer modes)
+    int sum_xq = 0;   // sum of int8 activations (ternary offset correction)
+    if constexpr (F == F_INT8F) {
+        float* xf = reinterpret_cast<float*>(xs);
+        for (int i = tid; i < padded_cols / 8; i += kThreads) {
+            float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (8 * i < K) load8x<XT>(p.x, 8 * i, v);
+            reinterpret_cast<float4*>(xf + 8 * i)[0] = make_float4(v[0], v[1], v[2], v[3]);
+            reinterpret_cast<float4*>(xf + 8 * i)[1] = make_float4(v[4], v[5], v[6], v[7]);
+        }
+    } else if constexpr (F == F_INT8I || F == F_TERN) {
+        float m = 0.0f;
+        for (int i = tid; i < K / 8; i += kThreads) {
+            float v[8];
+            load8x<XT>(p.x, 8 * i, v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
+        }
+        sx = absmax_scale(block_max(m, redf));
+        for (int i = tid; i < padded_cols / 8; i += kThreads) {
+            const int c0 = 8 * i;
+            int c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (c0 < K) {
+                float v[8];
+                load8x<XT>(p.x, c0, v);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    c[j] = qcode(v[j], sx);
+                    sum_xq += c[j];
+                }
+            }
+            if constexpr (F == F_INT8I) {
+                uint2 o;
+                o.x = (c[0] & 0xFF) | ((c[1] & 0xFF) << 8) | ((c[2] & 0xFF) << 16) | ((uint32_t)(c[3] & 0xFF) << 24);
+                o.y = (c[4] & 0xFF) | ((c[5] & 0xFF) << 8) | ((c[6] & 0xFF) << 16) | ((uint32_t)(c[7] & 0xFF) << 24);
+                *reinterpret_cast<uint2*>(xs + c0) = o;
+            } else {
+                // column 16g + 4b + f is stored at 16g + 4f + b (byte-plane order)
+                const int l0 = c0 & 15, g16 = c0 - l0;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const int l = l0 + t;
+                    xs[g16 + 4 * (l & 3) + (l >> 2)] = (uint8_t)(c[t] & 0xFF);
+                }
+            }
+        }
+        if constexpr (F == F_TERN) sum_xq = block_sum_int(sum_xq, redi);
+    } else {  // F_SR: dword (unit u, pair q) = bf16 x[32u+q] | bf16 x[32u+q+16] << 16
+        const uint16_t* xh = static_cast<const uint16_t*>(p.x);
+        uint32_t* xw = reinterpret_cast<uint32_t*>(xs);
+        for (int i = tid; i < padded_cols / 2; i += kThreads) {
+            const int c = 32 * (i >> 4) + (i & 15);
+            uint32_t d = 0;
+            if (c < K) d = (uint32_t)xh[c] | ((uint32_t)xh[c + 16] << 16);
+            xw[i] = d;
+        }
+    }
+    __syncthreads();
+
+    // ------------------------------------------------------------ stream
+    const int rowB = (F == F_TERN) ? K / 4 : (F == F_SR) ? K / 8 : K;  // code bytes per row
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.codes + (int64_t)row0 * rowB, (uint32_t)(rows * rowB));
+    __amdgpu_buffer_rsrc_t rr = rc;
+    if constexpr (F == F_SR) rr = make_rsrc(p.resid + (int64_t)row0 * K, (uint32_t)(rows * K));
+    const uint32_t oob_c = (uint32_t)(rows * rowB);
+    const uint32_t oob_r = (uint32_t)(rows * K);
+
+    const int ngroups = (rows + U - 1) / U;
+    const int my_groups = ngroups > wave ? (ngroups - wave + kWaves - 1) / kWaves : 0;
+    const int nit = my_groups * nseg;
+
+    // Loads are issued without branches: an item past the end (it >= nit)
+    // turns into out-of-range offsets, so the waitcnt bookkeeping sees the
+    // same load sequence on every path and waits only for the item consumed.
+    auto issue = [&](int it, Frag (&fr)[U][JS]) {
+        const bool live = it < nit;
+        const int g = wave + kWaves * (it / nseg);
+        const int seg = it % nseg;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = g * U + u;
+#pragma unroll
+            for (int j = 0; j < JS; ++j) {
+                const int c = lane + 64 * (seg * JS + j);
+                const bool ok = live && (r < rows) && (c < C);
+                if constexpr (F == F_SR) {
+                    const uint32_t orr = ok ? (uint32_t)(r * K + 32 * c) : oob_r;
+                    fr[u][j].r0 = load16(rr, orr);
+                    fr[u][j].r1 = load16(rr, ok ? orr + 16 : oob_r);
+                    fr[u][j].s = load4(rc, ok ? (uint32_t)(r * rowB + 4 * c) : oob_c);
+                } else {
+                    fr[u][j].w = load16(rc, ok ? (uint32_t)(r * rowB + 16 * c) : oob_c);
+                }
+            }
+        }
+    };
+
+    float accf[U], accf2[U];
+    int acc1[U], acc4[U], acc16[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) { accf[u] = 0.f; accf2[u] = 0.f; acc1[u] = 0; acc4[u] = 0; acc16[u] = 0; }
+
+    auto consume = [&](int it, Frag (&fr)[U][JS]) {
+        const int g = wave + kWaves * (it / nseg);
+        const int seg = it % nseg;
+        if (seg == 0) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) { accf[u] = 0.f; accf2[u] = 0.f; acc1[u] = 0; acc4[u] = 0; acc16[u] = 0; }
+        }
+#pragma unroll
+        for (int j = 0; j < JS; ++j) {
+            const int c = lane + 64 * (seg * JS + j);  // < nseg * JS * 64: inside the padded LDS copy
+            if constexpr (F == F_INT8F) {
+                const float4* xp = reinterpret_cast<const float4*>(xs) + 4 * c;
+                float xv[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 t = xp[q];
+                    xv[4 * q] = t.x; xv[4 * q + 1] = t.y; xv[4 * q + 2] = t.z; xv[4 * q + 3] = t.w;
+                }
+#pragma unroll
+                for (int b = 0; b < 16; ++b) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const uint32_t wd = fr[u][j].w[b >> 2];
+                        const float wv = (float)(int8_t)(wd >> (8 * (b & 3)));
+                        accf[u] = __builtin_fmaf(wv, xv[b], accf[u]);
+                    }
+                }
+            } else if constexpr (F == F_INT8I) {
+                const u32x4 xq = reinterpret_cast<const u32x4*>(xs)[c];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) acc1[u] = sdot4(fr[u][j].w[d], xq[d], acc1[u]);
+                }
+            } else if constexpr (F == F_TERN) {
+                const u32x4* xp = reinterpret_cast<const u32x4*>(xs) + 4 * c;
+                u32x4 xq[4];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) xq[d] = xp[d];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const uint32_t w = fr[u][j].w[d];
+                        acc1[u] = sdot4(w & 0x03030303u, xq[d][0], acc1[u]);
+                        acc4[u] = sdot4(w & 0x0C0C0C0Cu, xq[d][1], acc4[u]);
+                        acc16[u] = sdot4(w & 0x30303030u, xq[d][2], acc16[u]);
+                        acc16[u] = sdot4((w >> 2) & 0x30303030u, xq[d][3], acc16[u]);
+                    }
+                }
+            } else {  // F_SR
+                const u32x4* xp = reinterpret_cast<const u32x4*>(xs) + 4 * c;
+                uint32_t xv[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x4 t = xp[q];
+                    xv[4 * q] = t[0]; xv[4 * q + 1] = t[1]; xv[4 * q + 2] = t[2]; xv[4 * q + 3] = t[3];
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const uint32_t ns = ~fr[u][j].s;
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const float lo = (float)(int8_t)(fr[u][j].r0[q >> 2] >> (8 * (q & 3)));
+                        const float hi = (float)(int8_t)(fr[u][j].r1[q >> 2] >> (8 * (q & 3)));
+                        const uint32_t rp = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+                        accf2[u] = dot2bf(rp, xv[q], accf2[u]);
+                        const uint32_t sp = ((ns << (15 - q)) & 0x80008000u) | 0x3F803F80u;
+                        accf[u] = dot2bf(sp, xv[q], accf[u]);
+                    }
+                }
+            }
+        }
+        if (seg == nseg - 1) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int r = g * U + u;
+                if constexpr (F == F_INT8F || F == F_SR) {
+                    float v;
+                    if constexpr (F == F_SR) {
+                        v = wave_sum(accf[u]);
+                        const float v2 = wave_sum(accf2[u]);
+                        if (lane == 0 && r < rows) {
+                            const int row = row0 + r;
+                            v = p.scale[row] * v + v2 / p.scale2[row];
+                        }
+                    } else {
+                        v = wave_sum(accf[u]);
+                        if (lane == 0 && r < rows) v = v / p.scale[row0 + r];
+                    }
+                    if (lane == 0 && r < rows) {
+                        if constexpr (YT == 0) static_cast<float*>(p.y)[row0 + r] = v;
+                        else static_cast<uint16_t*>(p.y)[row0 + r] = (uint16_t)f32_to_bf16(v);
+                    }
+                } else {
+                    int a;
+                    if constexpr (F == F_TERN) a = wave_sum(acc1[u] + (acc4[u] >> 2) + (acc16[u] >> 4)) - sum_xq;
+                    else a = wave_sum(acc1[u]);
+                    if (lane == 0 && r < rows) {
+                        const int row = row0 + r;
+                        float v;
+                        if constexpr (F == F_TERN) v = (float)a * p.scale[0] / sx;
+                        else v = (float)a / (p.scale[row] * sx);
+                        if (p.acc_out) p.acc_out[row] = a;
+                        if constexpr (YT == 0) static_cast<float*>(p.y)[row] = v;
+                        else static_cast<uint16_t*>(p.y)[row] = (uint16_t)f32_to_bf16(v);
+                    }
+                }
+            }
+        }
+    };
+
+    Frag fa[U][JS], fb[U][JS];
+    issue(0, fa);
+    for (int it = 0; it < nit; it += 2) {
+        issue(it + 1, fb);
+        consume(it, fa);
+        issue(it + 2, fa);
+        if (it + 1 < nit) consume(it + 1, fb);
+    }
+}
+
+// ------------------------------------------------------------------ host side
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) cu = 256;
+        cached[dev] = cu;
+    }
+    return cached[dev];
+}
+
+template <int F, int XT, int YT, int U, int JS>
+static hipError_t run(const QgemvArgs& a, hipStream_t st) {
+    constexpr int kCols = Fmt<F>::kColsPerChunk;
+    const int K = (int)a.k, N = (int)a.n;
+    const int C = K / kCols;
+    const int J = (C + 63) / 64;
+    const int nseg = (J + JS - 1) / JS;
+    const size_t lds = (size_t)nseg * JS * 64 * kCols * Fmt<F>::kLdsBytesPerCol;
+    const int64_t rowB = (F == F_TERN) ? K / 4 : (F == F_SR) ? K / 8 : K;
+    const int64_t resB = (F == F_SR) ? K : 0;
+    const int cus = device_cu_count();
+    int64_t rpw = (N + cus - 1) / cus;
+    const int64_t cap = ((int64_t)1 << 31) / (rowB > resB ? rowB : resB);  // buffer ranges stay below 2 GiB
+    if (rpw > cap) rpw = cap;
+    if (rpw < 1) rpw = 1;
+    const int grid = (int)((N + rpw - 1) / rpw);
+    KParams p;
+    p.codes = static_cast<const uint8_t*>(a.codes);
+    p.resid = a.resid;
+    p.scale = a.scale;
+    p.scale2 = a.scale2;
+    p.x = a.x;
+    p.y = a.y;
+    p.acc_out = a.acc_out;
+    p.n = N;
+    p.k = K;
+    p.rows_per_wg = (int32_t)rpw;
+    auto kern = qgemv_kernel<F, XT, YT, U, JS>;
+    if (lds > 64 * 1024) {
+        static bool attr_set = false;  // per instantiation
+        if (!attr_set) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+    }
+    kern<<<grid, kThreads, lds, st>>>(p);
+    return hipGetLastError();
+}
+
+template <int F, int U, int JS>
+static hipError_t run_xy(const QgemvArgs& a, hipStream_t st) {
+    if (a.xt == 0 && a.yt == 0) return run<F, 0, 0, U, JS>(a, st);
+    if (a.xt == 0 && a.yt == 1) return run<F, 0, 1, U, JS>(a, st);
+    if (a.xt == 1 && a.yt == 0) return run<F, 1, 0, U, JS>(a, st);
+    return run<F, 1, 1, U, JS>(a, st);
+}
+
+hipError_t launch_qgemv(const QgemvArgs& a, hipStream_t st) {
+    // (format, activation mode) combinations validated by the caller
+    if (a.fmt == 0 && a.amode == 1) return run_xy<F_INT8F, 4, 4>(a, st);
+    if (a.fmt == 0 && a.amode == 0) return run_xy<F_INT8I, 4, 4>(a, st);
+    if (a.fmt == 1) return run_xy<F_TERN, 8, 1>(a, st);
+    if (a.yt == 0) return run<F_SR, 1, 0, 2, 4>(a, st);
+    return run<F_SR, 1, 1, 2, 4>(a, st);
+}
+
+}  // namespace qg

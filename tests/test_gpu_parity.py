@@ -1,0 +1,346 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bar: bit-exact on quantized codes, scales, packed bytes and int32
+accumulators; float outputs within the normwise tolerances of gpu_util
+(1e-5 on fp32-activation paths, 2e-3 on bf16-activation paths) against the
+oracle's fp64 reference computed from the oracle's own codes.
+
+Sizes: small shapes spanning several workgroups with ragged tails, the five
+workloads at full size (sampled rows where the oracle is too slow for every
+row), and edge cases (minimum / maximum K, single rows, zero inputs).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import TOL_BF16, TOL_F32, bf16_to_f64, canaries_intact, dev, dev_bf16, guarded, host
+
+pytestmark = pytest.mark.gpu
+
+
+def note(msg):
+    print("[case] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def qg():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import quantized_gemv_amd as q
+    q.lib()  # fails loudly if the HIP library is not built
+    return q
+
+
+# ------------------------------------------------------------------ quantizers
+
+@pytest.mark.parametrize("rows,cols", [(1, 8), (7, 264), (33, 4096), (4, 11008)])
+@pytest.mark.parametrize("bf16_in", [False, True])
+def test_absmax_per_row(qg, rows, cols, bf16_in):
+    note("absmax per_row %dx%d bf16=%s" % (rows, cols, bf16_in))
+    g = synth.rng(rows * 1000 + cols)
+    w = synth.gaussian(g, (rows, cols), 0.02)
+    if rows > 2:
+        w[2] = 0.0
+    if bf16_in:
+        bits = synth.to_bf16_bits(w)
+        xin = dev_bf16(bits)
+        w = synth.bf16_bits_to_f32(bits)
+    else:
+        xin = dev(w)
+    q, s = qg.quantize_absmax(xin, per_row=True)
+    q_ref, s_ref = oracle.quantize_absmax(w, per_row=True)
+    assert np.array_equal(host(s), s_ref)
+    assert np.array_equal(host(q), q_ref)
+
+
+@pytest.mark.parametrize("n", [8, 256, 4096, 65536 + 8, 3 * 1024 * 1024])
+def test_absmax_per_tensor(qg, n):
+    note("absmax per_tensor n=%d" % n)
+    g = synth.rng(n)
+    x = synth.gaussian(g, (n,), 1.0)
+    q, s = qg.quantize_absmax(dev(x), per_row=False)
+    q_ref, s_ref = oracle.quantize_absmax(x, per_row=False)
+    assert host(s)[0] == s_ref[0]
+    assert np.array_equal(host(q), q_ref)
+
+
+def test_absmax_worked_example_on_gpu(qg):
+    note("absmax worked example")
+    x = np.array([10.8, 3.08, 3.02, -7.59, 0, 0, 0, 0], np.float32)
+    q, s = qg.quantize_absmax(dev(x), per_row=False)
+    assert host(q).tolist()[:4] == [127, 36, 36, -89]
+    assert host(s)[0] == np.float32(127) / np.float32(10.8)
+
+
+@pytest.mark.parametrize("m,k,n_out", [(5, 64, 3), (64, 512, 6), (2048, 4096, 20), (3, 4096, 0), (2, 64, 64)])
+def test_outlier_split(qg, m, k, n_out):
+    note("outlier split m=%d k=%d n_out=%d" % (m, k, n_out))
+    wl = synth.prefill_outlier(m=m, k=k, n=8, n_out=n_out, seed=5)
+    xb, idx = wl.tensors["x_bf16"], wl.tensors["idx"]
+    xq, s, xo = qg.quantize_absmax_split(dev_bf16(xb), idx.tolist())
+    xq_ref, s_ref, xo_ref = oracle.outlier_split_quantize(xb, idx)
+    assert np.array_equal(host(s), s_ref)
+    assert np.array_equal(host(xq), xq_ref)
+    assert np.array_equal(host(xo), xo_ref)
+
+
+def test_gather_columns(qg):
+    note("gather outlier weights")
+    wl = synth.prefill_outlier(m=4, k=4096, n=4096, n_out=20, seed=5)
+    w, idx = wl.tensors["w"], wl.tensors["idx"]
+    wo = qg.gather_columns_bf16(dev(w), idx.tolist())
+    assert np.array_equal(host(wo), oracle.gather_outlier_weights(w, idx))
+
+
+@pytest.mark.parametrize("n,k", [(3, 4), (64, 256), (11008, 4096)])
+def test_ternary_quantize(qg, n, k):
+    note("ternary quantize %dx%d" % (n, k))
+    w = synth.ternary_decode(n=n, k=k, seed=3).tensors["w"]
+    q, gamma = qg.quantize_ternary(dev(w))
+    q_ref, g_ref = oracle.ternary_absmean(w)
+    assert host(gamma)[0] == g_ref
+    assert np.array_equal(host(q), q_ref)
+
+
+def test_ternary_special_values(qg):
+    note("ternary special values")
+    for w in (np.array([[1.9486494, 5.8459477, 0, 0]], np.float32),
+              np.zeros((2, 8), np.float32),
+              np.array([[0.5, 1.5, 1.0, -1.0]], np.float32)):
+        q, gamma = qg.quantize_ternary(dev(w))
+        q_ref, g_ref = oracle.ternary_absmean(w)
+        assert host(gamma)[0] == g_ref
+        assert np.array_equal(host(q), q_ref)
+
+
+@pytest.mark.parametrize("n,k", [(5, 8), (37, 520), (130, 8192)])
+def test_split_sign_residual_small(qg, n, k):
+    note("sign/residual split %dx%d" % (n, k))
+    w = synth.sign_residual_decode(n=n, k=k, seed=4).tensors["w"]
+    w[0, :4] = [0.0, -0.0, 1e-30, -1e-30]
+    if n > 3:
+        w[3] = 0
+    sign, alpha, rq, s_r = qg.split_sign_residual(dev(w))
+    s_ref, a_ref, rq_ref, sr_ref = oracle.sign_residual_split(w)
+    assert np.array_equal(host(alpha), a_ref)
+    assert np.array_equal(host(s_r), sr_ref)
+    assert np.array_equal(host(sign), s_ref)
+    assert np.array_equal(host(rq), rq_ref)
+
+
+# ------------------------------------------------------------------ packing
+
+@pytest.mark.parametrize("bits", [1, 2])
+@pytest.mark.parametrize("n,k", [(1, 8), (9, 264), (300, 4096)])
+def test_pack_unpack(qg, bits, n, k):
+    note("pack bits=%d %dx%d" % (bits, n, k))
+    g = synth.rng(bits * 7 + n)
+    if bits == 2:
+        c = (g.integers(0, 3, size=(n, k)) - 1).astype(np.int8)
+    else:
+        c = np.where(g.random((n, k)) < 0.5, -1, 1).astype(np.int8)
+    p = qg.pack(dev(c), bits)
+    p_ref = oracle.pack(c, bits)
+    assert np.array_equal(host(p), p_ref)
+    assert np.array_equal(host(qg.unpack(p, bits, k)), c)
+
+
+def test_pack_exhaustive_bytes(qg):
+    note("pack exhaustive")
+    allbytes = np.arange(256, dtype=np.uint8)[None, :].repeat(2, axis=0)
+    codes = oracle.unpack(allbytes, 1, 8 * 256)
+    assert np.array_equal(host(qg.pack(dev(codes), 1)), allbytes)
+    tern = oracle.unpack(np.array([[b for b in range(256) if all(((b >> (2 * j)) & 3) != 3 for j in range(4))]],
+                                  np.uint8), 2, 4 * 81)
+    assert np.array_equal(host(qg.pack(dev(tern), 2)), oracle.pack(tern, 2))
+
+
+# ------------------------------------------------------------------ qgemv
+
+def _int8_weight(qg, w):
+    wq, s_w = qg.quantize_absmax(dev(w), per_row=True)
+    return qg.QWeight(qg.QG_WFMT_INT8, w.shape[0], w.shape[1], wq, s_w), wq, s_w
+
+
+@pytest.mark.parametrize("n,k", [(256, 256), (1, 128), (77, 1152), (300, 4096), (129, 11008)])
+def test_qgemv_w8a8(qg, n, k):
+    note("qgemv w8a8 %dx%d" % (n, k))
+    wl = synth.tiny_gemv(n=n, k=k, seed=1)
+    w, x = wl.tensors["w"], wl.tensors["x"]
+    W, wq, s_w = _int8_weight(qg, w)
+    wq_ref, sw_ref = oracle.quantize_absmax(w, per_row=True)
+    assert np.array_equal(host(wq), wq_ref) and np.array_equal(host(s_w), sw_ref)
+    xq_ref, sx_ref = oracle.quantize_absmax(x, per_row=False)
+    acc_ref = oracle.int_dot_exact(wq_ref, xq_ref)
+    y_ref = oracle.y_w8a8(acc_ref, sw_ref, sx_ref)
+    acc_full, acc = guarded(n, torch.int32)
+    y_full, y = guarded(n, torch.float32)
+    qg.qgemv(W, dev(x), act_int8=True, y=y, acc_out=acc)
+    assert np.array_equal(host(acc), acc_ref.astype(np.int32))
+    assert oracle.normwise_error(host(y), y_ref) <= TOL_F32
+    assert canaries_intact(acc_full, n) and canaries_intact(y_full, n)
+
+
+@pytest.mark.parametrize("name", list(synth.DECODE_7B_SHAPES))
+def test_qgemv_w8a16_decode_shapes(qg, name):
+    n, k = synth.DECODE_7B_SHAPES[name]
+    note("qgemv w8a16 %s" % name)
+    wl = synth.decode_w8a16(n=n, k=k, seed=synth.DECODE_7B_SEEDS[name])
+    w, xb = wl.tensors["w"], wl.tensors["x_bf16"]
+    W, wq, s_w = _int8_weight(qg, w)
+    wq_ref, sw_ref = oracle.quantize_absmax(w, per_row=True)
+    assert np.array_equal(host(s_w), sw_ref)
+    assert np.array_equal(host(wq), wq_ref)
+    y_ref = oracle.y_w8a16(wq_ref, sw_ref, xb)
+    y_full, y = guarded(n, torch.bfloat16)
+    x = dev_bf16(xb)
+    qg.qgemv(W, x, act_int8=False, y=y)
+    yb = host(y)
+    assert oracle.normwise_error(bf16_to_f64(yb), y_ref) <= TOL_BF16
+    assert canaries_intact(y_full, n)
+    # fp32 output: only the accumulation error remains
+    y32 = qg.qgemv(W, x, act_int8=False, y_dtype=torch.float32)
+    assert oracle.normwise_error(host(y32), y_ref) <= 1e-5
+    # determinism: a second launch is bit-identical
+    y2 = qg.qgemv(W, x, act_int8=False, y_dtype=torch.bfloat16)
+    assert np.array_equal(host(y2), yb)
+
+
+@pytest.mark.parametrize("n,k", [(8, 128), (77, 1152), (11008, 4096), (33, 32768)])
+def test_qgemv_w8a16_small_and_edges(qg, n, k):
+    note("qgemv w8a16 %dx%d" % (n, k))
+    wl = synth.decode_w8a16(n=n, k=k, seed=21)
+    w, xb = wl.tensors["w"], wl.tensors["x_bf16"]
+    W, wq, s_w = _int8_weight(qg, w)
+    wq_ref, sw_ref = oracle.quantize_absmax(w, per_row=True)
+    assert np.array_equal(host(wq), wq_ref)
+    y_ref = oracle.y_w8a16(wq_ref, sw_ref, xb)
+    y = qg.qgemv(W, dev_bf16(xb), act_int8=False, y_dtype=torch.float32)
+    assert oracle.normwise_error(host(y), y_ref) <= 1e-5
+    # fp32 activations take the same path (converted exactly to fp32 on chip)
+    xf = synth.bf16_bits_to_f32(xb)
+    y2 = qg.qgemv(W, dev(xf), act_int8=False, y_dtype=torch.float32)
+    assert np.array_equal(host(y2), host(y))
+
+
+def _ternary_case(qg, n, k, seed=3, x_bf16=False):
+    wl = synth.ternary_decode(n=n, k=k, seed=seed)
+    w, x = wl.tensors["w"], wl.tensors["x"]
+    if x_bf16:
+        xb = synth.to_bf16_bits(x)
+        x = synth.bf16_bits_to_f32(xb)
+        xin = dev_bf16(xb)
+    else:
+        xin = dev(x)
+    q, gamma = qg.quantize_ternary(dev(w))
+    packed = qg.pack(q, 2)
+    q_ref, g_ref = oracle.ternary_absmean(w)
+    p_ref = oracle.pack(q_ref, 2)
+    assert host(gamma)[0] == g_ref
+    assert np.array_equal(host(packed), p_ref)
+    W = qg.QWeight(qg.QG_WFMT_TERNARY2, n, k, packed, gamma)
+    xq_ref, sx_ref = oracle.quantize_absmax(x, per_row=False)
+    acc_ref = oracle.int_dot_exact(q_ref, xq_ref)
+    y_ref = oracle.y_ternary(acc_ref, g_ref, sx_ref)
+    acc_full, acc = guarded(n, torch.int32)
+    y_full, y = guarded(n, torch.float32)
+    qg.qgemv(W, xin, act_int8=True, y=y, acc_out=acc)
+    assert np.array_equal(host(acc), acc_ref.astype(np.int32))
+    assert oracle.normwise_error(host(y), y_ref) <= TOL_F32
+    assert canaries_intact(acc_full, n) and canaries_intact(y_full, n)
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (13, 384), (300, 4096), (11008, 4096), (40, 32768)])
+def test_qgemv_ternary(qg, n, k):
+    note("qgemv ternary %dx%d" % (n, k))
+    _ternary_case(qg, n, k)
+
+
+def test_qgemv_ternary_bf16_activations(qg):
+    note("qgemv ternary bf16 x")
+    _ternary_case(qg, 100, 1024, x_bf16=True)
+
+
+def _sr_case(qg, n, k, seed=4, rows=None):
+    wl = synth.sign_residual_decode(n=n, k=k, seed=seed)
+    w, xb = wl.tensors["w"], wl.tensors["x_bf16"]
+    sign, alpha, rq, s_r = qg.split_sign_residual(dev(w))
+    sp = qg.pack(sign, 1)
+    W = qg.QWeight(qg.QG_WFMT_SIGN1_RES8, n, k, sp, alpha, resid=rq, scale2=s_r)
+    y_full, y = guarded(n, torch.bfloat16)
+    qg.qgemv(W, dev_bf16(xb), act_int8=False, y=y)
+    y32 = qg.qgemv(W, dev_bf16(xb), act_int8=False, y_dtype=torch.float32)
+    sel = np.arange(n) if rows is None else rows
+    ws = np.ascontiguousarray(w[sel])
+    s_ref, a_ref, rq_ref, sr_ref = oracle.sign_residual_split(ws)
+    assert np.array_equal(host(alpha)[sel], a_ref)
+    assert np.array_equal(host(s_r)[sel], sr_ref)
+    assert np.array_equal(host(sp)[sel], oracle.pack(s_ref, 1))
+    assert np.array_equal(host(rq)[sel], rq_ref)
+    y_ref = oracle.y_sign_residual(s_ref, a_ref, rq_ref, sr_ref, xb)
+    assert oracle.normwise_error(bf16_to_f64(host(y)[sel]), y_ref) <= TOL_BF16
+    assert oracle.normwise_error(host(y32)[sel], y_ref) <= 1e-5
+    assert canaries_intact(y_full, n)
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (9, 1152), (700, 8192), (31, 32768)])
+def test_qgemv_sign_residual(qg, n, k):
+    note("qgemv sign+residual %dx%d" % (n, k))
+    _sr_case(qg, n, k)
+
+
+def test_qgemv_sign_residual_full(qg):
+    note("qgemv sign+residual 28672x8192 (sampled rows)")
+    g = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 1, 28671, 28670, 14335], g.choice(28672, 123, replace=False)]))
+    _sr_case(qg, 28672, 8192, rows=rows)
+
+
+def test_qgemv_zero_inputs(qg):
+    note("qgemv zero inputs")
+    n, k = 70, 1024
+    w = np.zeros((n, k), np.float32)
+    W, wq, s_w = _int8_weight(qg, w)
+    acc = torch.empty(n, dtype=torch.int32, device="cuda")
+    y = qg.qgemv(W, dev(np.zeros(k, np.float32)), act_int8=True, acc_out=acc)
+    assert not host(acc).any() and not host(y).any()
+    q, gamma = qg.quantize_ternary(dev(w))
+    Wt = qg.QWeight(qg.QG_WFMT_TERNARY2, n, k, qg.pack(q, 2), gamma)
+    y = qg.qgemv(Wt, dev(np.ones(k, np.float32)), act_int8=True, acc_out=acc)
+    assert not host(acc).any() and not host(y).any()
+
+
+# ------------------------------------------------------------------ prefill GEMM
+
+def _qgemm_case(qg, m, k, n, n_out, seed=5, check_acc=True):
+    wl = synth.prefill_outlier(m=m, k=k, n=n, n_out=n_out, seed=seed)
+    w, xb, idx = wl.tensors["w"], wl.tensors["x_bf16"], wl.tensors["idx"]
+    wq, s_w = qg.quantize_absmax(dev(w), per_row=True)
+    w_out = qg.gather_columns_bf16(dev(w), idx.tolist())
+    acc = torch.empty((m, n), dtype=torch.int32, device="cuda") if check_acc else None
+    y = qg.qgemm_w8a8_outlier(dev_bf16(xb), idx.tolist(), wq, s_w, w_out, acc_out=acc)
+    xq_ref, sx_ref, xo_ref = oracle.outlier_split_quantize(xb, idx)
+    wq_ref, sw_ref = oracle.quantize_absmax(w, per_row=True)
+    wo_ref = oracle.gather_outlier_weights(w, idx)
+    assert np.array_equal(host(wq), wq_ref) and np.array_equal(host(s_w), sw_ref)
+    acc_ref = oracle.int_gemm_exact(xq_ref, wq_ref)
+    if check_acc:
+        assert np.array_equal(host(acc), acc_ref.astype(np.int32))
+    y_ref = oracle.y_prefill(acc_ref, sx_ref, sw_ref, xo_ref, wo_ref)
+    assert oracle.normwise_error(host(y), y_ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("m,k,n,n_out", [(32, 128, 32, 0), (64, 256, 96, 5), (130, 384, 200, 16), (1, 128, 1, 1),
+                                         (257, 1024, 129, 20)])
+def test_qgemm_small(qg, m, k, n, n_out):
+    note("qgemm m=%d k=%d n=%d n_out=%d" % (m, k, n, n_out))
+    _qgemm_case(qg, m, k, n, n_out)
+
+
+def test_qgemm_full(qg):
+    note("qgemm 2048x4096x4096 n_out=20")
+    _qgemm_case(qg, 2048, 4096, 4096, 20)
