@@ -1,0 +1,401 @@
+"""Benchmark of the quantized-GEMV hot path on one MI355X.
+
+Headline step: one batch-1 decode token through the linear layers of a
+32-layer 7B-style transformer (4096 hidden, 11008 FFN) with weight-only int8
+weights (per-row absmax scales) and bf16 activations: per layer q, k, v, o
+(4096 x 4096), gate, up (11008 x 4096) and down (4096 x 11008).  Every layer
+has its own weight copy (6.5 GB in total), so nothing is served from the
+256 MB Infinity Cache.  The step's 224 GEMV launches are captured once in a
+HIP graph and replayed.  `value` = weight bytes streamed per second.
+
+Also measured (in the same JSON line): each workload of the suite on its
+own (tiny W8A8, the three decode shapes, ternary, sign + residual, W8A8
+prefill GEMM with outlier split), the roofline of the dominant kernel and the
+CPU oracle's throughput on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
+                       [--no-cpu-baseline] [--only-headline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+INT8_MFMA_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, TOP/s
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "qgemv_w8a16_decode7b_counters.json")
+QGEMV_SRC = os.path.join(ROOT, "quantized_gemv_amd", "csrc", "qgemv.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-headline", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+class Timed:
+    """Capture a list of launch closures into one HIP graph; replay and time it."""
+
+    def __init__(self, torch, launches):
+        self.torch = torch
+        self.n = len(launches)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for f in launches:  # eager warm-up outside the capture
+                f()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            for f in launches:
+                f()
+        torch.cuda.synchronize()
+
+    def run(self, reps):
+        """Returns seconds per replay measured with events on the launching stream."""
+        torch = self.torch
+        st = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            self.graph.replay()
+        e1.record(st)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantized_gemv_amd as qg
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    qg.lib()
+    dev = torch.device("cuda:0")
+
+    def cur_stream():
+        return torch.cuda.current_stream().cuda_stream
+
+    # ---------------------------------------------------------------- headline stack
+    shapes = synth.DECODE_7B_SHAPES
+    log("quantizing the three 7B projection shapes on the GPU")
+    base = {}
+    xs = {}
+    for name, (n, k) in shapes.items():
+        wl = synth.decode_w8a16(n=n, k=k, seed=synth.DECODE_7B_SEEDS[name])
+        wq, s_w = qg.quantize_absmax(torch.from_numpy(wl.tensors["w"]).to(dev), per_row=True)
+        base[name] = (wq, s_w)
+        xs[k] = torch.from_numpy(wl.tensors["x_bf16"]).to(dev).view(torch.bfloat16)
+    layer_plan = ["attn_4096x4096"] * 4 + ["ffn_up_11008x4096"] * 2 + ["ffn_down_4096x11008"]
+    L = args.layers
+    log("replicating weights for %d layers" % L)
+    weights = []  # (name, QWeight, CWeight)
+    for _ in range(L):
+        for name in layer_plan:
+            n, k = shapes[name]
+            wq, s_w = base[name]
+            W = qg.QWeight(qg.QG_WFMT_INT8, n, k, wq.clone(), s_w.clone())
+            weights.append((name, W, W.c_struct()))
+    torch.cuda.synchronize()
+    ys = {n: torch.empty(n, dtype=torch.bfloat16, device=dev) for n in (4096, 11008)}
+
+    def gemv_launch(W, cw):
+        def f():
+            st = qg.qgemv_launch_raw(cw, qg.QG_ACT_FLOAT, xs[W.k].data_ptr(), qg.QG_BF16, ys[W.n].data_ptr(),
+                                     qg.QG_BF16, cur_stream())
+            if st != 0:
+                raise RuntimeError("qg_qgemv failed: %s" % qg.status_str(st))
+        return f
+
+    step_bytes = 0
+    for name, W, _ in weights:
+        step_bytes += W.n * W.k + 4 * W.n  # int8 codes + fp32 per-row scales
+    act_bytes = sum(2 * (W.k + W.n) for _, W, _ in weights)  # bf16 x read + y written
+    launches_per_step = len(weights)
+
+    log("capturing the decode step (%d launches, %.2f GB of weights)" % (launches_per_step, step_bytes / 1e9))
+    step = Timed(torch, [gemv_launch(W, cw) for _, W, cw in weights])
+    for _ in range(args.warmup):
+        step.graph.replay()
+    torch.cuda.synchronize()
+    ev_s = step.run(max(1, args.steps // 10))  # event-timed pass (roofline), same work
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step.graph.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    value = step_bytes / (wall / args.steps) / 1e9
+    # dominant kernel: the W8A16 qgemv (the step contains nothing else)
+    per_launch_s = ev_s / launches_per_step
+    per_launch_bytes = (step_bytes + act_bytes) / launches_per_step
+    achieved = per_launch_bytes / per_launch_s / 1e9
+    traffic = None
+    if os.path.exists(COUNTERS_FILE):
+        try:
+            with open(COUNTERS_FILE) as f:
+                cnt = json.load(f)
+            if cnt.get("qgemv_src_sha256_16") == src_hash(QGEMV_SRC):
+                traffic = cnt.get("hbm_bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "qgemv_kernel<INT8,x bf16,y bf16> (W8A16)",
+                "algorithmic_bytes_per_launch": round(per_launch_bytes), "avg_launch_us": round(per_launch_s * 1e6, 3)}
+    log("decode step: %.3f ms, %.1f GB/s weights (%.1f%% of HBM peak)" % (ms_per_step, value, 100 * value / HBM_PEAK_GBS))
+
+    result = {
+        "metric": "qgemv weight GB/s & % of HBM peak at batch 1; prefill int8 TOPS & % MFMA peak",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "7B-style decode, weight-only int8 (W8A16), batch 1: %d layers x "
+                               "[4 x 4096x4096, 2 x 11008x4096, 1 x 4096x11008] per token" % L,
+                   "weight_bytes_per_step": step_bytes, "launches_per_step": launches_per_step,
+                   "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": roofline,
+    }
+
+    if not args.only_headline:
+        result["configs"] = bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys)
+        result["prefill"] = result["configs"].pop("prefill_w8a8_outlier")
+    result["context"] = {
+        "note": "figures quoted from the pages for context; not targets",
+        "fp16_7b_bytes_per_token_GB": 14, "fp16_7b_ms_per_token_at_2TBps": 7.0,
+        "separated_quant_claimed_decode_speedup": 1.78,
+        "qadd_prefill_speedup_dgx_spark": 1.49,
+        "this_step_weight_GB": round(step_bytes / 1e9, 3),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(np, synth)
+    print(json.dumps(result), flush=True)
+
+
+def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
+    out = {}
+    GiB = 1 << 30
+
+    def rotate_count(bytes_per_copy):
+        return max(2, -(-GiB // bytes_per_copy))
+
+    # -- the three decode shapes on their own, rotating through the stack's copies
+    for name in synth.DECODE_7B_SHAPES:
+        ws = [(W, cw) for nm, W, cw in weights if nm == name]
+        W0 = ws[0][0]
+        per = W0.n * W0.k + 4 * W0.n
+        ws = ws[:rotate_count(per)]
+
+        def mk(W, cw):
+            def f():
+                qg.qgemv_launch_raw(cw, qg.QG_ACT_FLOAT, xs[W.k].data_ptr(), qg.QG_BF16, ys[W.n].data_ptr(),
+                                    qg.QG_BF16, cur_stream())
+            return f
+        t = Timed(torch, [mk(W, cw) for W, cw in ws])
+        t.run(2)
+        sec = t.run(10) / t.n
+        out["decode_w8a16_" + name] = {"us": round(sec * 1e6, 3), "weight_GBps": round(per / sec / 1e9, 1),
+                                       "hbm_frac": round(per / sec / 1e9 / HBM_PEAK_GBS, 4),
+                                       "rotating_copies": len(ws)}
+        log("%s: %.2f us, %.0f GB/s" % (name, sec * 1e6, per / sec / 1e9))
+
+    # -- tiny W8A8 GEMV (launch-latency bound)
+    wl = synth.tiny_gemv()
+    wq, s_w = qg.quantize_absmax(torch.from_numpy(wl.tensors["w"]).to(dev), per_row=True)
+    Wt = qg.QWeight(qg.QG_WFMT_INT8, 256, 256, wq, s_w)
+    cwt = Wt.c_struct()
+    xt = torch.from_numpy(wl.tensors["x"]).to(dev)
+    yt = torch.empty(256, dtype=torch.float32, device=dev)
+
+    def tiny():
+        qg.qgemv_launch_raw(cwt, qg.QG_ACT_INT8, xt.data_ptr(), qg.QG_F32, yt.data_ptr(), qg.QG_F32, cur_stream())
+    t = Timed(torch, [tiny] * 100)
+    t.run(2)
+    sec = t.run(10) / t.n
+    out["tiny_w8a8_256x256"] = {"us": round(sec * 1e6, 3), "weight_GBps": round((65536 + 1024) / sec / 1e9, 1),
+                                "note": "launch-latency bound"}
+    log("tiny: %.2f us" % (sec * 1e6))
+
+    # -- ternary 11008 x 4096
+    wl = synth.ternary_decode()
+    q, gamma = qg.quantize_ternary(torch.from_numpy(wl.tensors["w"]).to(dev))
+    packed = qg.pack(q, 2)
+    del q
+    per = packed.numel() + 4
+    copies = [qg.QWeight(qg.QG_WFMT_TERNARY2, 11008, 4096, packed.clone(), gamma.clone())
+              for _ in range(rotate_count(per))]
+    xtn = torch.from_numpy(wl.tensors["x"]).to(dev)
+    ytn = torch.empty(11008, dtype=torch.float32, device=dev)
+    cws = [W.c_struct() for W in copies]
+
+    def mkt(cw):
+        def f():
+            qg.qgemv_launch_raw(cw, qg.QG_ACT_INT8, xtn.data_ptr(), qg.QG_F32, ytn.data_ptr(), qg.QG_F32, cur_stream())
+        return f
+    t = Timed(torch, [mkt(cw) for cw in cws])
+    t.run(2)
+    sec = t.run(10) / t.n
+    out["ternary_11008x4096"] = {"us": round(sec * 1e6, 3), "weight_GBps": round(per / sec / 1e9, 1),
+                                 "hbm_frac": round(per / sec / 1e9 / HBM_PEAK_GBS, 4), "rotating_copies": len(copies)}
+    log("ternary: %.2f us, %.0f GB/s" % (sec * 1e6, per / sec / 1e9))
+    del copies, cws, packed
+    torch.cuda.empty_cache()
+
+    # -- sign backbone + int8 residual, 28672 x 8192
+    wl = synth.sign_residual_decode()
+    wdev = torch.from_numpy(wl.tensors["w"]).to(dev)
+    sign, alpha, rq, s_r = qg.split_sign_residual(wdev)
+    sp = qg.pack(sign, 1)
+    del sign, wdev
+    per = sp.numel() + rq.numel() + 8 * 28672
+    copies = [qg.QWeight(qg.QG_WFMT_SIGN1_RES8, 28672, 8192, sp.clone(), alpha.clone(), resid=rq.clone(),
+                         scale2=s_r.clone()) for _ in range(rotate_count(per))]
+    xsr = torch.from_numpy(wl.tensors["x_bf16"]).to(dev).view(torch.bfloat16)
+    ysr = torch.empty(28672, dtype=torch.bfloat16, device=dev)
+    cws = [W.c_struct() for W in copies]
+
+    def mks(cw):
+        def f():
+            qg.qgemv_launch_raw(cw, qg.QG_ACT_FLOAT, xsr.data_ptr(), qg.QG_BF16, ysr.data_ptr(), qg.QG_BF16,
+                                cur_stream())
+        return f
+    t = Timed(torch, [mks(cw) for cw in cws])
+    t.run(1)
+    sec = t.run(5) / t.n
+    out["sign1_res8_28672x8192"] = {"us": round(sec * 1e6, 3), "weight_GBps": round(per / sec / 1e9, 1),
+                                    "hbm_frac": round(per / sec / 1e9 / HBM_PEAK_GBS, 4),
+                                    "rotating_copies": len(copies)}
+    log("sign+residual: %.2f us, %.0f GB/s" % (sec * 1e6, per / sec / 1e9))
+    del copies, cws, sp, rq
+    torch.cuda.empty_cache()
+
+    # -- W8A8 prefill GEMM with outlier split, 2048 x 4096 x 4096, 20 outlier channels
+    wl = synth.prefill_outlier()
+    m, k, n, n_out = 2048, 4096, 4096, 20
+    idx = wl.tensors["idx"].tolist()
+    wdev = torch.from_numpy(wl.tensors["w"]).to(dev)
+    wq, s_w = qg.quantize_absmax(wdev, per_row=True)
+    w_out = qg.gather_columns_bf16(wdev, idx)
+    del wdev
+    xp = torch.from_numpy(wl.tensors["x_bf16"]).to(dev).view(torch.bfloat16)
+    yp = torch.empty((m, n), dtype=torch.float32, device=dev)
+    ws = torch.empty(qg.lib().qg_qgemm_workspace_bytes(m, k, n_out), dtype=torch.uint8, device=dev)
+    xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+    sx = torch.empty(m, dtype=torch.float32, device=dev)
+    xo = torch.empty((m, n_out), dtype=torch.bfloat16, device=dev)
+    import ctypes
+    cidx = (ctypes.c_int32 * n_out)(*idx)
+    L = qg.lib()
+
+    def full():
+        L.qg_qgemm_w8a8_outlier(ctypes.c_void_p(xp.data_ptr()), m, k, cidx, n_out, ctypes.c_void_p(wq.data_ptr()),
+                                ctypes.c_void_p(s_w.data_ptr()), ctypes.c_void_p(w_out.data_ptr()), n,
+                                ctypes.c_void_p(yp.data_ptr()), None, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                ctypes.c_void_p(cur_stream()))
+
+    def split_only():
+        L.qg_quantize_absmax_split(ctypes.c_void_p(xp.data_ptr()), m, k, cidx, n_out, ctypes.c_void_p(xq.data_ptr()),
+                                   ctypes.c_void_p(sx.data_ptr()), ctypes.c_void_p(xo.data_ptr()),
+                                   ctypes.c_void_p(cur_stream()))
+    tf = Timed(torch, [full] * 20)
+    tf.run(2)
+    sec_full = tf.run(10) / 20
+    ts = Timed(torch, [split_only] * 20)
+    ts.run(2)
+    sec_split = ts.run(10) / 20
+    sec_gemm = max(sec_full - sec_split, 1e-9)
+    int8_ops = 2.0 * m * n * (k - n_out)
+    bf16_ops = 2.0 * m * n * n_out
+    tops = int8_ops / sec_gemm / 1e12
+    out["prefill_w8a8_outlier"] = {
+        "metric": "int8 TOPS of the W8A8 GEMM (2*M*N*(K-n_out) int8 ops / GEMM time)",
+        "shape": "M=2048 K=4096 N=4096 n_out=20",
+        "gemm_us": round(sec_gemm * 1e6, 2), "split_us": round(sec_split * 1e6, 2),
+        "call_us": round(sec_full * 1e6, 2), "int8_TOPS": round(tops, 1),
+        "mfma_frac": round(tops / INT8_MFMA_PEAK_TOPS, 4),
+        "call_TOPS": round((int8_ops + bf16_ops) / sec_full / 1e12, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": INT8_MFMA_PEAK_TOPS, "unit": "TFLOP/s",
+                     "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4), "traffic": None},
+    }
+    log("prefill: gemm %.1f us (%.0f TOPS), split %.1f us" % (sec_gemm * 1e6, tops, sec_split * 1e6))
+    return out
+
+
+def cpu_baseline(np, synth):
+    """The oracle as it stands (fp64 dequantize-then-multiply) on a bounded
+    sample of the headline workload: the seven projections of a few layers."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity size
+        threads = len(os.sched_getaffinity(0))
+    log("cpu baseline: preparing oracle operands")
+    ops = {}
+    for name, (n, k) in synth.DECODE_7B_SHAPES.items():
+        wl = synth.decode_w8a16(n=n, k=k, seed=synth.DECODE_7B_SEEDS[name])
+        wq, s_w = oracle.quantize_absmax(wl.tensors["w"], per_row=True)
+        ops[name] = (wq, s_w, wl.tensors["x_bf16"])
+    plan = ["attn_4096x4096"] * 4 + ["ffn_up_11008x4096"] * 2 + ["ffn_down_4096x11008"]
+    done_bytes = 0
+    layers = 0
+    t0 = time.perf_counter()
+    while True:
+        for name in plan:
+            wq, s_w, xb = ops[name]
+            oracle.y_w8a16(wq, s_w, xb)
+            done_bytes += wq.size + 4 * s_w.size
+        layers += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or layers >= 32:
+            break
+    return {"value": round(done_bytes / el / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%d of 32 layers of the decode step (%d projections, %.2f GB of int8 weights), "
+                      "fp64 dequantize-then-multiply, %.1f s" % (layers, 7 * layers, done_bytes / 1e9, el),
+            "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

@@ -57,9 +57,40 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// Block-wide max / sum over a 256-thread workgroup; `scratch` holds >= 4
+// DPP (data-parallel primitive) reductions: each step adds a lane permutation
+// of the value within rows of 16 lanes (quad swaps, half-row and row
+// mirrors), then row_bcast15 / row_bcast31 carry row totals into the upper
+// rows.  The full 64-lane sum ends in lane 63.  No LDS round trips, and the
+// chains of several rows are independent, so they interleave.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_mov(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+__device__ __forceinline__ float wave_sum_to_lane63(float v) {
+    v += __int_as_float(dpp_mov<0xB1>(__float_as_int(v)));        // quad_perm [1,0,3,2]
+    v += __int_as_float(dpp_mov<0x4E>(__float_as_int(v)));        // quad_perm [2,3,0,1]
+    v += __int_as_float(dpp_mov<0x141>(__float_as_int(v)));       // row_half_mirror
+    v += __int_as_float(dpp_mov<0x140>(__float_as_int(v)));       // row_mirror
+    v += __int_as_float(dpp_mov<0x142, 0xA>(__float_as_int(v)));  // row_bcast:15 into rows 1, 3
+    v += __int_as_float(dpp_mov<0x143, 0xC>(__float_as_int(v)));  // row_bcast:31 into rows 2, 3
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_to_lane63(int v) {
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    v += dpp_mov<0x141>(v);
+    v += dpp_mov<0x140>(v);
+    v += dpp_mov<0x142, 0xA>(v);
+    v += dpp_mov<0x143, 0xC>(v);
+    return v;
+}
+
+// Block-wide max / sum over a workgroup of NW waves; `scratch` holds >= NW
 // elements of shared memory.  All threads receive the result.  Contains two
 // barriers, so every thread of the block must call it.
+template <int NW = kWaves>
 __device__ __forceinline__ float block_max(float v, float* scratch) {
     v = wave_max(v);
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
@@ -67,11 +98,12 @@ __device__ __forceinline__ float block_max(float v, float* scratch) {
     __syncthreads();
     float r = scratch[0];
 #pragma unroll
-    for (int i = 1; i < kWaves; ++i) r = __builtin_fmaxf(r, scratch[i]);
+    for (int i = 1; i < NW; ++i) r = __builtin_fmaxf(r, scratch[i]);
     __syncthreads();
     return r;
 }
 
+template <int NW = kWaves>
 __device__ __forceinline__ int block_sum_int(int v, int* scratch) {
     v = wave_sum(v);
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
@@ -79,7 +111,7 @@ __device__ __forceinline__ int block_sum_int(int v, int* scratch) {
     __syncthreads();
     int r = 0;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) r += scratch[i];
+    for (int i = 0; i < NW; ++i) r += scratch[i];
     __syncthreads();
     return r;
 }

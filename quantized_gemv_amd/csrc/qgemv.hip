@@ -86,31 +86,19 @@ struct Fmt<F_SR> {
     struct Frag { u32x4 r0, r1; uint32_t s; };
 };
 
-template <int XT>
-__device__ __forceinline__ void load8x(const void* base, int c, float v[8]) {
-    if constexpr (XT == 0) {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + c);
-        const float4 a = p[0], b = p[1];
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
-        const uint4 h = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + c);
-        const uint32_t w[4] = {h.x, h.y, h.z, h.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
-            v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
-        }
-    }
-}
+// Workgroup shape: 8 waves (2 per SIMD, so one wave's LDS / ALU latency is
+// covered by the other's work), one workgroup per CU.
+constexpr int kQThreads = 512;
+constexpr int kQWaves = kQThreads / kWave;
+constexpr int kXL = 4;  // x pieces of 16 B held in registers per thread (K <= 16384 bf16 / 8192 fp32)
 
 template <int F, int XT, int YT, int U, int JS>
-__global__ __launch_bounds__(kThreads) void qgemv_kernel(KParams p) {
+__global__ __launch_bounds__(kQThreads) void qgemv_kernel(KParams p) {
     using Frag = typename Fmt<F>::Frag;
     constexpr int kCols = Fmt<F>::kColsPerChunk;
     extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
-    __shared__ float redf[kWaves];
-    __shared__ int redi[kWaves];
+    __shared__ float redf[kQWaves];
+    __shared__ int redi[kQWaves];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -124,66 +112,6 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(KParams p) {
     // x is staged (zero-padded) for every chunk iteration a segment can touch
     const int padded_cols = nseg * JS * 64 * kCols;
 
-    // ------------------------------------------------------------ stage x
-    float sx = 1.0f;  // activation scale (integer modes)
-    int sum_xq = 0;   // sum of int8 activations (ternary offset correction)
-    if constexpr (F == F_INT8F) {
-        float* xf = reinterpret_cast<float*>(xs);
-        for (int i = tid; i < padded_cols / 8; i += kThreads) {
-            float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (8 * i < K) load8x<XT>(p.x, 8 * i, v);
-            reinterpret_cast<float4*>(xf + 8 * i)[0] = make_float4(v[0], v[1], v[2], v[3]);
-            reinterpret_cast<float4*>(xf + 8 * i)[1] = make_float4(v[4], v[5], v[6], v[7]);
-        }
-    } else if constexpr (F == F_INT8I || F == F_TERN) {
-        float m = 0.0f;
-        for (int i = tid; i < K / 8; i += kThreads) {
-            float v[8];
-            load8x<XT>(p.x, 8 * i, v);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
-        }
-        sx = absmax_scale(block_max(m, redf));
-        for (int i = tid; i < padded_cols / 8; i += kThreads) {
-            const int c0 = 8 * i;
-            int c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (c0 < K) {
-                float v[8];
-                load8x<XT>(p.x, c0, v);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    c[j] = qcode(v[j], sx);
-                    sum_xq += c[j];
-                }
-            }
-            if constexpr (F == F_INT8I) {
-                uint2 o;
-                o.x = (c[0] & 0xFF) | ((c[1] & 0xFF) << 8) | ((c[2] & 0xFF) << 16) | ((uint32_t)(c[3] & 0xFF) << 24);
-                o.y = (c[4] & 0xFF) | ((c[5] & 0xFF) << 8) | ((c[6] & 0xFF) << 16) | ((uint32_t)(c[7] & 0xFF) << 24);
-                *reinterpret_cast<uint2*>(xs + c0) = o;
-            } else {
-                // column 16g + 4b + f is stored at 16g + 4f + b (byte-plane order)
-                const int l0 = c0 & 15, g16 = c0 - l0;
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const int l = l0 + t;
-                    xs[g16 + 4 * (l & 3) + (l >> 2)] = (uint8_t)(c[t] & 0xFF);
-                }
-            }
-        }
-        if constexpr (F == F_TERN) sum_xq = block_sum_int(sum_xq, redi);
-    } else {  // F_SR: dword (unit u, pair q) = bf16 x[32u+q] | bf16 x[32u+q+16] << 16
-        const uint16_t* xh = static_cast<const uint16_t*>(p.x);
-        uint32_t* xw = reinterpret_cast<uint32_t*>(xs);
-        for (int i = tid; i < padded_cols / 2; i += kThreads) {
-            const int c = 32 * (i >> 4) + (i & 15);
-            uint32_t d = 0;
-            if (c < K) d = (uint32_t)xh[c] | ((uint32_t)xh[c + 16] << 16);
-            xw[i] = d;
-        }
-    }
-    __syncthreads();
-
     // ------------------------------------------------------------ stream
     const int rowB = (F == F_TERN) ? K / 4 : (F == F_SR) ? K / 8 : K;  // code bytes per row
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.codes + (int64_t)row0 * rowB, (uint32_t)(rows * rowB));
@@ -193,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(KParams p) {
     const uint32_t oob_r = (uint32_t)(rows * K);
 
     const int ngroups = (rows + U - 1) / U;
-    const int my_groups = ngroups > wave ? (ngroups - wave + kWaves - 1) / kWaves : 0;
+    const int my_groups = ngroups > wave ? (ngroups - wave + kQWaves - 1) / kQWaves : 0;
     const int nit = my_groups * nseg;
 
     // Loads are issued without branches: an item past the end (it >= nit)
@@ -201,14 +129,14 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(KParams p) {
     // same load sequence on every path and waits only for the item consumed.
     auto issue = [&](int it, Frag (&fr)[U][JS]) {
         const bool live = it < nit;
-        const int g = wave + kWaves * (it / nseg);
+        const int g = wave + kQWaves * (it / nseg);
         const int seg = it % nseg;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int r = g * U + u;
+        for (int j = 0; j < JS; ++j) {  // issue in the order consume() uses the data
+            const int c = lane + 64 * (seg * JS + j);
 #pragma unroll
-            for (int j = 0; j < JS; ++j) {
-                const int c = lane + 64 * (seg * JS + j);
+            for (int u = 0; u < U; ++u) {
+                const int r = g * U + u;
                 const bool ok = live && (r < rows) && (c < C);
                 if constexpr (F == F_SR) {
                     const uint32_t orr = ok ? (uint32_t)(r * K + 32 * c) : oob_r;
@@ -222,13 +150,108 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(KParams p) {
         }
     };
 
+    // ------------------------------------------------------------ stage x
+    // vmcnt retires loads in issue order, so x must be requested BEFORE the
+    // first weights: then staging waits only for x while the weights stream
+    // in.  Each thread loads kXL pieces of 16 B (8 bf16 or 4 fp32) into
+    // registers through a buffer resource (pieces past K read as zeros).
+    constexpr int kElems = (XT == 0) ? 4 : 8;  // elements per 16 B piece
+    const int npieces = K / kElems;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)(K * (XT == 0 ? 4 : 2)));
+    u32x4 xr[kXL];
+#pragma unroll
+    for (int l = 0; l < kXL; ++l) xr[l] = load16(rx, (uint32_t)(16 * (tid + kQThreads * l)));
+    Frag fa[U][JS], fb[U][JS];
+    issue(0, fa);
+
+    // piece -> fp32 values
+    auto piece_vals = [&](const u32x4& r, float v[kElems]) {
+        if constexpr (XT == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(r[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[2 * e] = bf16_to_f32(r[e] & 0xFFFFu);
+                v[2 * e + 1] = bf16_to_f32(r[e] >> 16);
+            }
+        }
+    };
+    // visit every real piece of x once: f(piece index, values); pieces past
+    // the register window (K > kXL * 256 pieces) are loaded here, after the
+    // weights, and so wait for them
+    auto for_pieces = [&](auto&& f) {
+#pragma unroll
+        for (int l = 0; l < kXL; ++l) {
+            const int pi = tid + kQThreads * l;
+            if (pi < npieces) {
+                float v[kElems];
+                piece_vals(xr[l], v);
+                f(pi, v);
+            }
+        }
+        for (int pi = tid + kQThreads * kXL; pi < npieces; pi += kQThreads) {
+            float v[kElems];
+            piece_vals(load16(rx, (uint32_t)(16 * pi)), v);
+            f(pi, v);
+        }
+    };
+
+    float sx = 1.0f;  // activation scale (integer modes)
+    int sum_xq = 0;   // sum of int8 activations (ternary offset correction)
+    if constexpr (F == F_INT8F) {
+        float* xf = reinterpret_cast<float*>(xs);
+        for_pieces([&](int pi, const float* v) {
+#pragma unroll
+            for (int e = 0; e < kElems; e += 4)
+                *reinterpret_cast<float4*>(xf + pi * kElems + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+        });
+        for (int i = K / 4 + tid; i < padded_cols / 4; i += kQThreads)
+            reinterpret_cast<float4*>(xf)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else if constexpr (F == F_INT8I || F == F_TERN) {
+        float m = 0.0f;
+        for_pieces([&](int, const float* v) {
+#pragma unroll
+            for (int e = 0; e < kElems; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
+        });
+        sx = absmax_scale(block_max<kQWaves>(m, redf));
+        for_pieces([&](int pi, const float* v) {
+#pragma unroll
+            for (int e = 0; e < kElems; ++e) {
+                const int q = qcode(v[e], sx);
+                sum_xq += q;
+                const int c = pi * kElems + e;
+                if constexpr (F == F_INT8I) {
+                    xs[c] = (uint8_t)(q & 0xFF);
+                } else {  // column 16g + 4b + f is stored at 16g + 4f + b (byte-plane order)
+                    const int l = c & 15;
+                    xs[(c - l) + 4 * (l & 3) + (l >> 2)] = (uint8_t)(q & 0xFF);
+                }
+            }
+        });
+        for (int i = K / 4 + tid; i < padded_cols / 4; i += kQThreads) reinterpret_cast<uint32_t*>(xs)[i] = 0u;
+        if constexpr (F == F_TERN) sum_xq = block_sum_int<kQWaves>(sum_xq, redi);
+    } else {  // F_SR: dword (unit u, pair q) = bf16 x[32u+q] | bf16 x[32u+q+16] << 16
+        uint16_t* xh = reinterpret_cast<uint16_t*>(xs);
+        for_pieces([&](int pi, const float* v) {
+#pragma unroll
+            for (int e = 0; e < kElems; ++e) {
+                const int c = pi * kElems + e;
+                const int u = c >> 5, q = c & 31;
+                xh[2 * (16 * u + (q & 15)) + (q >> 4)] = (uint16_t)(__float_as_uint(v[e]) >> 16);
+            }
+        });
+        for (int i = K / 2 + tid; i < padded_cols / 2; i += kQThreads) reinterpret_cast<uint32_t*>(xs)[i] = 0u;
+    }
+    __syncthreads();
+
     float accf[U], accf2[U];
     int acc1[U], acc4[U], acc16[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) { accf[u] = 0.f; accf2[u] = 0.f; acc1[u] = 0; acc4[u] = 0; acc16[u] = 0; }
 
     auto consume = [&](int it, Frag (&fr)[U][JS]) {
-        const int g = wave + kWaves * (it / nseg);
+        const int g = wave + kQWaves * (it / nseg);
         const int seg = it % nseg;
         if (seg == 0) {
 #pragma unroll
@@ -301,46 +324,56 @@ __global__ __launch_bounds__(kThreads) void qgemv_kernel(KParams p) {
             }
         }
         if (seg == nseg - 1) {
+            // reduce every row of the group at once (independent DPP chains);
+            // lane 63 holds the sums and writes the outputs
+            if constexpr (F == F_INT8F || F == F_SR) {
+                float v[U], v2[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int r = g * U + u;
-                if constexpr (F == F_INT8F || F == F_SR) {
-                    float v;
-                    if constexpr (F == F_SR) {
-                        v = wave_sum(accf[u]);
-                        const float v2 = wave_sum(accf2[u]);
-                        if (lane == 0 && r < rows) {
+                for (int u = 0; u < U; ++u) {
+                    v[u] = wave_sum_to_lane63(accf[u]);
+                    if constexpr (F == F_SR) v2[u] = wave_sum_to_lane63(accf2[u]);
+                }
+                if (lane == 63) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int r = g * U + u;
+                        if (r < rows) {
                             const int row = row0 + r;
-                            v = p.scale[row] * v + v2 / p.scale2[row];
+                            float o;
+                            if constexpr (F == F_SR) o = p.scale[row] * v[u] + v2[u] / p.scale2[row];
+                            else o = v[u] / p.scale[row];
+                            if constexpr (YT == 0) static_cast<float*>(p.y)[row] = o;
+                            else static_cast<uint16_t*>(p.y)[row] = (uint16_t)f32_to_bf16(o);
                         }
-                    } else {
-                        v = wave_sum(accf[u]);
-                        if (lane == 0 && r < rows) v = v / p.scale[row0 + r];
                     }
-                    if (lane == 0 && r < rows) {
-                        if constexpr (YT == 0) static_cast<float*>(p.y)[row0 + r] = v;
-                        else static_cast<uint16_t*>(p.y)[row0 + r] = (uint16_t)f32_to_bf16(v);
-                    }
-                } else {
-                    int a;
-                    if constexpr (F == F_TERN) a = wave_sum(acc1[u] + (acc4[u] >> 2) + (acc16[u] >> 4)) - sum_xq;
-                    else a = wave_sum(acc1[u]);
-                    if (lane == 0 && r < rows) {
-                        const int row = row0 + r;
-                        float v;
-                        if constexpr (F == F_TERN) v = (float)a * p.scale[0] / sx;
-                        else v = (float)a / (p.scale[row] * sx);
-                        if (p.acc_out) p.acc_out[row] = a;
-                        if constexpr (YT == 0) static_cast<float*>(p.y)[row] = v;
-                        else static_cast<uint16_t*>(p.y)[row] = (uint16_t)f32_to_bf16(v);
+                }
+            } else {
+                int v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if constexpr (F == F_TERN) v[u] = wave_sum_to_lane63(acc1[u] + (acc4[u] >> 2) + (acc16[u] >> 4));
+                    else v[u] = wave_sum_to_lane63(acc1[u]);
+                }
+                if (lane == 63) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int r = g * U + u;
+                        if (r < rows) {
+                            const int row = row0 + r;
+                            const int a = (F == F_TERN) ? v[u] - sum_xq : v[u];
+                            float o;
+                            if constexpr (F == F_TERN) o = (float)a * p.scale[0] / sx;
+                            else o = (float)a / (p.scale[row] * sx);
+                            if (p.acc_out) p.acc_out[row] = a;
+                            if constexpr (YT == 0) static_cast<float*>(p.y)[row] = o;
+                            else static_cast<uint16_t*>(p.y)[row] = (uint16_t)f32_to_bf16(o);
+                        }
                     }
                 }
             }
         }
     };
 
-    Frag fa[U][JS], fb[U][JS];
-    issue(0, fa);
     for (int it = 0; it < nit; it += 2) {
         issue(it + 1, fb);
         consume(it, fa);
@@ -399,7 +432,7 @@ static hipError_t run(const QgemvArgs& a, hipStream_t st) {
             attr_set = true;
         }
     }
-    kern<<<grid, kThreads, lds, st>>>(p);
+    kern<<<grid, kQThreads, lds, st>>>(p);
     return hipGetLastError();
 }
 
@@ -412,10 +445,12 @@ static hipError_t run_xy(const QgemvArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_qgemv(const QgemvArgs& a, hipStream_t st) {
-    // (format, activation mode) combinations validated by the caller
-    if (a.fmt == 0 && a.amode == 1) return run_xy<F_INT8F, 4, 4>(a, st);
-    if (a.fmt == 0 && a.amode == 0) return run_xy<F_INT8I, 4, 4>(a, st);
-    if (a.fmt == 1) return run_xy<F_TERN, 8, 1>(a, st);
+    // (format, activation mode) combinations validated by the caller.
+    // Rows per group U and chunk iterations per item JS keep all 8 waves busy
+    // at the decode shapes (16-112 rows per workgroup).
+    if (a.fmt == 0 && a.amode == 1) return run_xy<F_INT8F, 2, 4>(a, st);
+    if (a.fmt == 0 && a.amode == 0) return run_xy<F_INT8I, 2, 4>(a, st);
+    if (a.fmt == 1) return run_xy<F_TERN, 4, 1>(a, st);
     if (a.yt == 0) return run<F_SR, 1, 0, 2, 4>(a, st);
     return run<F_SR, 1, 1, 2, 4>(a, st);
 }
