@@ -64,8 +64,8 @@ struct Fmt;
 template <>
 struct Fmt<F_INT8F> {
     static constexpr int kColsPerChunk = 16;
-    static constexpr int kLdsBytesPerCol = 4;
-    struct Frag { u32x4 w; };
+    static constexpr int kLdsBytesPerCol = 0;  // x travels with each item instead
+    struct Frag { u32x4 w; u32x4 x[4]; };      // x: 16 activations (bf16: x[0..1], fp32: x[0..3])
 };
 template <>
 struct Fmt<F_INT8I> {
@@ -124,11 +124,14 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KParams p) {
     const int my_groups = ngroups > wave ? (ngroups - wave + kQWaves - 1) / kQWaves : 0;
     const int nit = my_groups * nseg;
 
-    // Loads are issued without branches: an item past the end (it >= nit)
-    // turns into out-of-range offsets, so the waitcnt bookkeeping sees the
-    // same load sequence on every path and waits only for the item consumed.
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)(K * (XT == 0 ? 4 : 2)));
+    // Only real items are issued (the main loop below is peeled so that no
+    // load is conditional after a load that is waited on: the waitcnt pass
+    // would otherwise merge paths and wait for the prefetched item too).
+    // Ragged rows / chunks inside an item read zeros through out-of-range
+    // offsets.
     auto issue = [&](int it, Frag (&fr)[U][JS]) {
-        const bool live = it < nit;
+        const bool live = true;
         const int g = wave + kQWaves * (it / nseg);
         const int seg = it % nseg;
 #pragma unroll
@@ -144,6 +147,16 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KParams p) {
                     fr[u][j].r1 = load16(rr, ok ? orr + 16 : oob_r);
                     fr[u][j].s = load4(rc, ok ? (uint32_t)(r * rowB + 4 * c) : oob_c);
                 } else {
+                    if constexpr (F == F_INT8F) {
+                        // the 16 activations of this chunk, requested just ahead of the
+                        // chunk's weights and shared by the U rows of the item
+                        if (u == 0) {
+                            constexpr int kXB = (XT == 0) ? 64 : 32;  // bytes of x per chunk
+                            const uint32_t xo = (c < C) ? (uint32_t)(kXB * c) : (uint32_t)(K * (XT == 0 ? 4 : 2));
+#pragma unroll
+                            for (int h = 0; h < kXB / 16; ++h) fr[0][j].x[h] = load16(rx, xo + 16 * h);
+                        }
+                    }
                     fr[u][j].w = load16(rc, ok ? (uint32_t)(r * rowB + 16 * c) : oob_c);
                 }
             }
@@ -157,12 +170,14 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KParams p) {
     // registers through a buffer resource (pieces past K read as zeros).
     constexpr int kElems = (XT == 0) ? 4 : 8;  // elements per 16 B piece
     const int npieces = K / kElems;
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)(K * (XT == 0 ? 4 : 2)));
     u32x4 xr[kXL];
 #pragma unroll
-    for (int l = 0; l < kXL; ++l) xr[l] = load16(rx, (uint32_t)(16 * (tid + kQThreads * l)));
+    for (int l = 0; l < kXL; ++l) {
+        xr[l] = u32x4{0, 0, 0, 0};
+        if (F != F_INT8F && tid + kQThreads * l < npieces) xr[l] = load16(rx, (uint32_t)(16 * (tid + kQThreads * l)));
+    }
     Frag fa[U][JS], fb[U][JS];
-    issue(0, fa);
+    if (nit > 0) issue(0, fa);
 
     // piece -> fp32 values
     auto piece_vals = [&](const u32x4& r, float v[kElems]) {
@@ -200,14 +215,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KParams p) {
     float sx = 1.0f;  // activation scale (integer modes)
     int sum_xq = 0;   // sum of int8 activations (ternary offset correction)
     if constexpr (F == F_INT8F) {
-        float* xf = reinterpret_cast<float*>(xs);
-        for_pieces([&](int pi, const float* v) {
-#pragma unroll
-            for (int e = 0; e < kElems; e += 4)
-                *reinterpret_cast<float4*>(xf + pi * kElems + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
-        });
-        for (int i = K / 4 + tid; i < padded_cols / 4; i += kQThreads)
-            reinterpret_cast<float4*>(xf)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        // nothing to stage: every item carries its own slice of x
     } else if constexpr (F == F_INT8I || F == F_TERN) {
         float m = 0.0f;
         for_pieces([&](int, const float* v) {
@@ -243,7 +251,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KParams p) {
         });
         for (int i = K / 2 + tid; i < padded_cols / 2; i += kQThreads) reinterpret_cast<uint32_t*>(xs)[i] = 0u;
     }
-    __syncthreads();
+    if constexpr (F != F_INT8F) __syncthreads();
 
     float accf[U], accf2[U];
     int acc1[U], acc4[U], acc16[U];
@@ -261,12 +269,17 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KParams p) {
         for (int j = 0; j < JS; ++j) {
             const int c = lane + 64 * (seg * JS + j);  // < nseg * JS * 64: inside the padded LDS copy
             if constexpr (F == F_INT8F) {
-                const float4* xp = reinterpret_cast<const float4*>(xs) + 4 * c;
                 float xv[16];
+                if constexpr (XT == 0) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 t = xp[q];
-                    xv[4 * q] = t.x; xv[4 * q + 1] = t.y; xv[4 * q + 2] = t.z; xv[4 * q + 3] = t.w;
+                    for (int q = 0; q < 16; ++q) xv[q] = __uint_as_float(fr[0][j].x[q >> 2][q & 3]);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const uint32_t d = fr[0][j].x[q >> 2][q & 3];
+                        xv[2 * q] = bf16_to_f32(d & 0xFFFFu);
+                        xv[2 * q + 1] = __uint_as_float(d & 0xFFFF0000u);
+                    }
                 }
 #pragma unroll
                 for (int b = 0; b < 16; ++b) {
@@ -374,11 +387,20 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KParams p) {
         }
     };
 
-    for (int it = 0; it < nit; it += 2) {
+    // steady state: item `it` is in flight in fa at the top of every trip
+    int it = 0;
+    for (; it + 2 < nit; it += 2) {
         issue(it + 1, fb);
         consume(it, fa);
         issue(it + 2, fa);
-        if (it + 1 < nit) consume(it + 1, fb);
+        consume(it + 1, fb);
+    }
+    if (it + 2 == nit) {  // two items left
+        issue(it + 1, fb);
+        consume(it, fa);
+        consume(it + 1, fb);
+    } else if (it + 1 == nit) {  // one item left
+        consume(it, fa);
     }
 }
 
@@ -447,12 +469,14 @@ static hipError_t run_xy(const QgemvArgs& a, hipStream_t st) {
 hipError_t launch_qgemv(const QgemvArgs& a, hipStream_t st) {
     // (format, activation mode) combinations validated by the caller.
     // Rows per group U and chunk iterations per item JS keep all 8 waves busy
-    // at the decode shapes (16-112 rows per workgroup).
+    // at the decode shapes (16-112 rows per workgroup) while holding the
+    // bytes in flight per CU near 32-64 KB (two items per wave), where HBM
+    // streaming measured fastest on MI355X.
     if (a.fmt == 0 && a.amode == 1) return run_xy<F_INT8F, 2, 4>(a, st);
     if (a.fmt == 0 && a.amode == 0) return run_xy<F_INT8I, 2, 4>(a, st);
     if (a.fmt == 1) return run_xy<F_TERN, 4, 1>(a, st);
-    if (a.yt == 0) return run<F_SR, 1, 0, 2, 4>(a, st);
-    return run<F_SR, 1, 1, 2, 4>(a, st);
+    if (a.yt == 0) return run<F_SR, 1, 0, 1, 2>(a, st);
+    return run<F_SR, 1, 1, 1, 2>(a, st);
 }
 
 }  // namespace qg
