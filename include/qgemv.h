@@ -75,7 +75,8 @@ typedef int32_t qg_status;
 
 /* limits */
 #define QG_MAX_OUTLIERS 256     /* n_out of the outlier split                     */
-#define QG_QGEMV_MAX_K  32768   /* k of qg_qgemv (the activation vector is staged on chip) */
+#define QG_QGEMV_MAX_K  32768   /* k of qg_qgemv (bounded by the on-chip activation staging)  */
+#define QG_MAX_GROUP    8       /* matrices per qg_qgemv_grouped launch              */
 
 /* Human-readable text for a status code (static storage). */
 const char* qg_status_str(qg_status s);
@@ -226,6 +227,22 @@ typedef struct qg_weight {
  */
 qg_status qg_qgemv(const qg_weight* w, int32_t amode, const void* x, int32_t xt,
                    void* y, int32_t yt, int32_t* acc_out, void* stream);
+
+/*
+ * Several batch-1 products that read the same activation vector, in one
+ * launch: y[m] = W[m] x for m < count (for example the q, k and v projections
+ * of a layer, or its gate and up projections).  Each product follows
+ * qg_qgemv's definition exactly and gives bit-identical outputs; a single
+ * launch pays the kernel start-up and drain once instead of count times
+ * ([SEP] section 3.3: launch overhead is one reason measured speed-ups fall
+ * short of the bandwidth model; fusing operators into one kernel recovers it).
+ * w       : HOST array of count descriptors; all share fmt and k.
+ * y       : HOST array of count device pointers ([w[m].n] of type yt).
+ * acc_out : HOST array of count device pointers (each may be NULL), or NULL.
+ * count in [1, QG_MAX_GROUP]; other arguments as qg_qgemv.
+ */
+qg_status qg_qgemv_grouped(const qg_weight* w, int32_t count, int32_t amode, const void* x, int32_t xt,
+                           void* const* y, int32_t yt, int32_t* const* acc_out, void* stream);
 
 /*
  * W8A8 prefill GEMM with the outlier-channel split ([SEP] section 2.2: outlier

@@ -25,6 +25,7 @@ QG_WFMT_INT8, QG_WFMT_TERNARY2, QG_WFMT_SIGN1_RES8 = 0, 1, 2
 QG_ACT_INT8, QG_ACT_FLOAT = 0, 1
 QG_MAX_OUTLIERS = 256
 QG_QGEMV_MAX_K = 32768
+QG_MAX_GROUP = 8
 
 _c_i32, _c_i64, _c_sz, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
@@ -53,6 +54,8 @@ _SIGS = {
     "qg_pack": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp]),
     "qg_unpack": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp]),
     "qg_qgemv": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp]),
+    "qg_qgemv_grouped": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_i32, _c_vp, _c_i32, ctypes.POINTER(_c_vp),
+                                  _c_i32, ctypes.POINTER(_c_vp), _c_vp]),
     "qg_qgemm_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i32]),
     "qg_qgemm_w8a8_outlier": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i64,
                                        _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
@@ -239,6 +242,40 @@ def qgemv(w: QWeight, x: torch.Tensor, act_int8: bool, y_dtype=torch.float32, y:
     _check(lib().qg_qgemv(ctypes.byref(cw), QG_ACT_INT8 if act_int8 else QG_ACT_FLOAT, _p(x), _xt(x), _p(y), _xt(y),
                           _p(acc_out), _stream(x)), "qg_qgemv")
     return y
+
+
+class GroupLaunch:
+    """Pre-marshalled arguments of one qg_qgemv_grouped call (kept alive by
+    this object); launch() enqueues it on the current stream."""
+
+    def __init__(self, weights: Sequence[QWeight], x: torch.Tensor, ys: Sequence[torch.Tensor], act_int8: bool,
+                 accs: Optional[Sequence[torch.Tensor]] = None):
+        _dev(x, "x", (torch.float32, torch.bfloat16))
+        n = len(weights)
+        if not 1 <= n <= QG_MAX_GROUP or len(ys) != n:
+            raise ValueError("need 1..%d weights and as many outputs" % QG_MAX_GROUP)
+        for y in ys:
+            _dev(y, "y", (torch.float32, torch.bfloat16))
+        self.x, self.ys, self.accs = x, list(ys), accs
+        self.cw = (CWeight * n)(*[w.c_struct() for w in weights])
+        self.yp = (_c_vp * n)(*[y.data_ptr() for y in ys])
+        self.ap = None if accs is None else (_c_vp * n)(*[None if a is None else a.data_ptr() for a in accs])
+        self.n = n
+        self.amode = QG_ACT_INT8 if act_int8 else QG_ACT_FLOAT
+        self.xt = _xt(x)
+        self.yt = _xt(ys[0])
+
+    def launch(self):
+        _check(lib().qg_qgemv_grouped(self.cw, self.n, self.amode, _p(self.x), self.xt, self.yp, self.yt, self.ap,
+                                      _stream(self.x)), "qg_qgemv_grouped")
+
+
+def qgemv_grouped(weights: Sequence[QWeight], x: torch.Tensor, act_int8: bool, y_dtype=torch.float32,
+                  accs: Optional[Sequence[torch.Tensor]] = None):
+    """Several GEMVs on the same x in one launch (qg_qgemv_grouped). Returns [y]."""
+    ys = [torch.empty(w.n, dtype=y_dtype, device=x.device) for w in weights]
+    GroupLaunch(weights, x, ys, act_int8, accs).launch()
+    return ys
 
 
 def qgemv_launch_raw(cw: CWeight, amode: int, x_ptr: int, xt: int, y_ptr: int, yt: int, stream_ptr: int) -> int:

@@ -146,8 +146,8 @@ qg_status qg_unpack(const uint8_t* packed, int64_t n, int64_t k, int32_t bits, i
     return from_hip(qg::launch_unpack(packed, n * k, bits, codes, as_stream(stream)));
 }
 
-qg_status qg_qgemv(const qg_weight* w, int32_t amode, const void* x, int32_t xt, void* y, int32_t yt,
-                   int32_t* acc_out, void* stream) {
+static qg_status check_qgemv(const qg_weight* w, int32_t amode, const void* x, int32_t xt, const void* y,
+                             int32_t yt, const int32_t* acc_out) {
     if (!w || !x || !y) return QG_ERR_NULLPTR;
     if (!w->codes || !w->scale) return QG_ERR_NULLPTR;
     if (xt != QG_F32 && xt != QG_BF16) return QG_ERR_ARG;
@@ -169,6 +169,11 @@ qg_status qg_qgemv(const qg_weight* w, int32_t amode, const void* x, int32_t xt,
     if (w->k < 128 || w->k % 128 != 0 || w->k > QG_QGEMV_MAX_K) return QG_ERR_SHAPE;
     if (!aligned16(w->codes) || !aligned16(x)) return QG_ERR_ALIGN;
     if (w->fmt == QG_WFMT_SIGN1_RES8 && !aligned16(w->resid)) return QG_ERR_ALIGN;
+    return QG_OK;
+}
+
+static qg::QgemvArgs qgemv_args(const qg_weight* w, int32_t amode, const void* x, int32_t xt, void* y, int32_t yt,
+                                int32_t* acc_out) {
     qg::QgemvArgs a;
     a.fmt = w->fmt;
     a.amode = amode;
@@ -183,7 +188,30 @@ qg_status qg_qgemv(const qg_weight* w, int32_t amode, const void* x, int32_t xt,
     a.x = x;
     a.y = y;
     a.acc_out = acc_out;
-    return from_hip(qg::launch_qgemv(a, as_stream(stream)));
+    return a;
+}
+
+qg_status qg_qgemv(const qg_weight* w, int32_t amode, const void* x, int32_t xt, void* y, int32_t yt,
+                   int32_t* acc_out, void* stream) {
+    const qg_status st = check_qgemv(w, amode, x, xt, y, yt, acc_out);
+    if (st != QG_OK) return st;
+    return from_hip(qg::launch_qgemv(qgemv_args(w, amode, x, xt, y, yt, acc_out), as_stream(stream)));
+}
+
+qg_status qg_qgemv_grouped(const qg_weight* w, int32_t count, int32_t amode, const void* x, int32_t xt,
+                           void* const* y, int32_t yt, int32_t* const* acc_out, void* stream) {
+    if (!w || !y) return QG_ERR_NULLPTR;
+    if (count < 1 || count > QG_MAX_GROUP) return QG_ERR_ARG;
+    qg::QgemvArgs a[QG_MAX_GROUP];
+    for (int32_t m = 0; m < count; ++m) {
+        int32_t* acc = acc_out ? acc_out[m] : nullptr;
+        const qg_status st = check_qgemv(&w[m], amode, x, xt, y[m], yt, acc);
+        if (st != QG_OK) return st;
+        if (w[m].fmt != w[0].fmt) return QG_ERR_ARG;
+        if (w[m].k != w[0].k) return QG_ERR_SHAPE;
+        a[m] = qgemv_args(&w[m], amode, x, xt, y[m], yt, acc);
+    }
+    return from_hip(qg::launch_qgemv_group(a, count, as_stream(stream)));
 }
 
 size_t qg_qgemm_workspace_bytes(int64_t m, int64_t k, int32_t n_out) {

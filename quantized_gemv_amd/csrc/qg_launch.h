@@ -41,6 +41,8 @@ struct QgemvArgs {
     int32_t* acc_out;
 };
 hipError_t launch_qgemv(const QgemvArgs& a, hipStream_t st);
+constexpr int kMaxGroupLaunch = 8;
+hipError_t launch_qgemv_group(const QgemvArgs* a, int count, hipStream_t st);
 
 struct QgemmArgs {
     const uint16_t* x;

@@ -50,6 +50,17 @@ struct KParams {
     int32_t n, k, rows_per_wg;
 };
 
+// A launch covers up to kMaxGroup weight matrices that share K and x (for
+// example the q, k and v projections of a layer).  Workgroups are handed out
+// per matrix in proportion to its rows; wg_start[m] is the first workgroup
+// of matrix m.
+constexpr int kMaxGroup = 8;
+struct KGroup {
+    int32_t count;
+    int32_t wg_start[kMaxGroup + 1];
+    KParams mats[kMaxGroup];
+};
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
@@ -93,7 +104,7 @@ constexpr int kQWaves = kQThreads / kWave;
 constexpr int kXL = 4;  // x pieces of 16 B held in registers per thread (K <= 16384 bf16 / 8192 fp32)
 
 template <int F, int XT, int YT, int U, int JS>
-__global__ __launch_bounds__(kQThreads) void qgemv_kernel(KParams p) {
+__global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     using Frag = typename Fmt<F>::Frag;
     constexpr int kCols = Fmt<F>::kColsPerChunk;
     extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
@@ -103,8 +114,11 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KParams p) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int mi = 0;
+    while (mi + 1 < grp.count && (int)blockIdx.x >= grp.wg_start[mi + 1]) ++mi;
+    const KParams& p = grp.mats[mi];
     const int K = p.k;
-    const int row0 = blockIdx.x * p.rows_per_wg;
+    const int row0 = ((int)blockIdx.x - grp.wg_start[mi]) * p.rows_per_wg;
     const int rows = min(p.rows_per_wg, p.n - row0);
     const int C = K / kCols;           // chunks per row
     const int J = (C + 63) / 64;       // chunk iterations per lane per row
@@ -418,32 +432,44 @@ int device_cu_count() {
 }
 
 template <int F, int XT, int YT, int U, int JS>
-static hipError_t run(const QgemvArgs& a, hipStream_t st) {
+static hipError_t run(const QgemvArgs* a, int count, hipStream_t st) {
     constexpr int kCols = Fmt<F>::kColsPerChunk;
-    const int K = (int)a.k, N = (int)a.n;
+    const int K = (int)a[0].k;
     const int C = K / kCols;
     const int J = (C + 63) / 64;
     const int nseg = (J + JS - 1) / JS;
     const size_t lds = (size_t)nseg * JS * 64 * kCols * Fmt<F>::kLdsBytesPerCol;
     const int64_t rowB = (F == F_TERN) ? K / 4 : (F == F_SR) ? K / 8 : K;
     const int64_t resB = (F == F_SR) ? K : 0;
-    const int cus = device_cu_count();
-    int64_t rpw = (N + cus - 1) / cus;
     const int64_t cap = ((int64_t)1 << 31) / (rowB > resB ? rowB : resB);  // buffer ranges stay below 2 GiB
-    if (rpw > cap) rpw = cap;
-    if (rpw < 1) rpw = 1;
-    const int grid = (int)((N + rpw - 1) / rpw);
-    KParams p;
-    p.codes = static_cast<const uint8_t*>(a.codes);
-    p.resid = a.resid;
-    p.scale = a.scale;
-    p.scale2 = a.scale2;
-    p.x = a.x;
-    p.y = a.y;
-    p.acc_out = a.acc_out;
-    p.n = N;
-    p.k = K;
-    p.rows_per_wg = (int32_t)rpw;
+    const int cus = device_cu_count();
+    int64_t total_rows = 0;
+    for (int m = 0; m < count; ++m) total_rows += a[m].n;
+    KGroup g;
+    g.count = count;
+    int wg = 0;
+    for (int m = 0; m < count; ++m) {
+        const int64_t N = a[m].n;
+        int64_t share = (cus * N + total_rows / 2) / total_rows;  // workgroups for this matrix
+        if (share < 1) share = 1;
+        int64_t rpw = (N + share - 1) / share;
+        if (rpw > cap) rpw = cap;
+        if (rpw < 1) rpw = 1;
+        KParams& p = g.mats[m];
+        p.codes = static_cast<const uint8_t*>(a[m].codes);
+        p.resid = a[m].resid;
+        p.scale = a[m].scale;
+        p.scale2 = a[m].scale2;
+        p.x = a[m].x;
+        p.y = a[m].y;
+        p.acc_out = a[m].acc_out;
+        p.n = (int32_t)N;
+        p.k = K;
+        p.rows_per_wg = (int32_t)rpw;
+        g.wg_start[m] = wg;
+        wg += (int)((N + rpw - 1) / rpw);
+    }
+    for (int m = count; m <= kMaxGroup; ++m) g.wg_start[m] = wg;
     auto kern = qgemv_kernel<F, XT, YT, U, JS>;
     if (lds > 64 * 1024) {
         static bool attr_set = false;  // per instantiation
@@ -454,29 +480,32 @@ static hipError_t run(const QgemvArgs& a, hipStream_t st) {
             attr_set = true;
         }
     }
-    kern<<<grid, kQThreads, lds, st>>>(p);
+    kern<<<wg, kQThreads, lds, st>>>(g);
     return hipGetLastError();
 }
 
 template <int F, int U, int JS>
-static hipError_t run_xy(const QgemvArgs& a, hipStream_t st) {
-    if (a.xt == 0 && a.yt == 0) return run<F, 0, 0, U, JS>(a, st);
-    if (a.xt == 0 && a.yt == 1) return run<F, 0, 1, U, JS>(a, st);
-    if (a.xt == 1 && a.yt == 0) return run<F, 1, 0, U, JS>(a, st);
-    return run<F, 1, 1, U, JS>(a, st);
+static hipError_t run_xy(const QgemvArgs* a, int count, hipStream_t st) {
+    if (a[0].xt == 0 && a[0].yt == 0) return run<F, 0, 0, U, JS>(a, count, st);
+    if (a[0].xt == 0 && a[0].yt == 1) return run<F, 0, 1, U, JS>(a, count, st);
+    if (a[0].xt == 1 && a[0].yt == 0) return run<F, 1, 0, U, JS>(a, count, st);
+    return run<F, 1, 1, U, JS>(a, count, st);
 }
 
-hipError_t launch_qgemv(const QgemvArgs& a, hipStream_t st) {
-    // (format, activation mode) combinations validated by the caller.
+// All entries share fmt, amode, xt, yt and k (validated by the caller).
+hipError_t launch_qgemv_group(const QgemvArgs* a, int count, hipStream_t st) {
     // Rows per group U and chunk iterations per item JS keep all 8 waves busy
     // at the decode shapes (16-112 rows per workgroup) while holding the
     // bytes in flight per CU near 32-64 KB (two items per wave), where HBM
     // streaming measured fastest on MI355X.
-    if (a.fmt == 0 && a.amode == 1) return run_xy<F_INT8F, 2, 4>(a, st);
-    if (a.fmt == 0 && a.amode == 0) return run_xy<F_INT8I, 2, 4>(a, st);
-    if (a.fmt == 1) return run_xy<F_TERN, 4, 1>(a, st);
-    if (a.yt == 0) return run<F_SR, 1, 0, 1, 2>(a, st);
-    return run<F_SR, 1, 1, 1, 2>(a, st);
+    const QgemvArgs& h = a[0];
+    if (h.fmt == 0 && h.amode == 1) return run_xy<F_INT8F, 2, 4>(a, count, st);
+    if (h.fmt == 0 && h.amode == 0) return run_xy<F_INT8I, 2, 4>(a, count, st);
+    if (h.fmt == 1) return run_xy<F_TERN, 4, 1>(a, count, st);
+    if (h.yt == 0) return run<F_SR, 1, 0, 1, 2>(a, count, st);
+    return run<F_SR, 1, 1, 1, 2>(a, count, st);
 }
+
+hipError_t launch_qgemv(const QgemvArgs& a, hipStream_t st) { return launch_qgemv_group(&a, 1, st); }
 
 }  // namespace qg

@@ -139,6 +139,33 @@ def test_validation_qgemv(qg):
     assert call(xt=3) == 4 and call(yt=3) == 4 and call(amode=2) == 4
 
 
+def test_validation_qgemv_grouped(qg):
+    l = qg.lib()
+    W = qg.CWeight * 3
+    ws = W(qg.CWeight(0, 0, 64, 256, A, A, A, A), qg.CWeight(0, 0, 32, 256, A, A, A, A),
+           qg.CWeight(0, 0, 16, 256, A, A, A, A))
+    ys = (ctypes.c_void_p * 3)(A, A, A)
+    f = l.qg_qgemv_grouped
+    assert f(None, 3, 1, A, 1, ys, 1, None, None) == 1
+    assert f(ws, 3, 1, A, 1, None, 1, None, None) == 1
+    assert f(ws, 0, 1, A, 1, ys, 1, None, None) == 4
+    assert f(ws, 9, 1, A, 1, ys, 1, None, None) == 4
+    ys_null = (ctypes.c_void_p * 3)(A, None, A)
+    assert f(ws, 3, 1, A, 1, ys_null, 1, None, None) == 1
+    mixed_k = W(qg.CWeight(0, 0, 64, 256, A, A, A, A), qg.CWeight(0, 0, 32, 384, A, A, A, A),
+                qg.CWeight(0, 0, 16, 256, A, A, A, A))
+    assert f(mixed_k, 3, 1, A, 1, ys, 1, None, None) == 2
+    mixed_fmt = W(qg.CWeight(0, 0, 64, 256, A, A, A, A), qg.CWeight(1, 0, 32, 256, A, A, A, A),
+                  qg.CWeight(0, 0, 16, 256, A, A, A, A))
+    assert f(mixed_fmt, 3, 0, A, 1, ys, 1, None, None) == 4
+    bad_n = W(qg.CWeight(0, 0, 64, 256, A, A, A, A), qg.CWeight(0, 0, 0, 256, A, A, A, A),
+              qg.CWeight(0, 0, 16, 256, A, A, A, A))
+    assert f(bad_n, 3, 1, A, 1, ys, 1, None, None) == 2
+    accs = (ctypes.c_void_p * 3)(A, None, A)
+    assert f(ws, 3, 1, A, 1, ys, 1, accs, None) == 4  # accumulators only in integer mode
+    assert f(ws, 3, 1, U, 1, ys, 1, None, None) == 3
+
+
 def test_validation_qgemm(qg):
     l = qg.lib()
     f = l.qg_qgemm_w8a8_outlier

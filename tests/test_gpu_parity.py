@@ -301,6 +301,47 @@ def test_qgemv_sign_residual_full(qg):
     _sr_case(qg, 28672, 8192, rows=rows)
 
 
+@pytest.mark.parametrize("fmt", ["int8_f", "int8_i", "ternary", "sign_res"])
+def test_qgemv_grouped_matches_single(qg, fmt):
+    note("qgemv grouped %s" % fmt)
+    shapes = [(4096, 4096), (1024, 4096), (777, 4096)] if fmt != "sign_res" else [(300, 4096), (64, 4096)]
+    g = synth.rng(77)
+    Ws, refs = [], []
+    for i, (n, k) in enumerate(shapes):
+        w = synth.gaussian(g, (n, k), 0.02)
+        if fmt.startswith("int8"):
+            Wd, wq, s_w = _int8_weight(qg, w)
+            Ws.append(Wd)
+            refs.append(oracle.quantize_absmax(w, per_row=True))
+        elif fmt == "ternary":
+            q, gamma = qg.quantize_ternary(dev(w))
+            Ws.append(qg.QWeight(qg.QG_WFMT_TERNARY2, n, k, qg.pack(q, 2), gamma))
+            refs.append(oracle.ternary_absmean(w))
+        else:
+            sign, alpha, rq, s_r = qg.split_sign_residual(dev(w))
+            Ws.append(qg.QWeight(qg.QG_WFMT_SIGN1_RES8, n, k, qg.pack(sign, 1), alpha, resid=rq, scale2=s_r))
+            refs.append(oracle.sign_residual_split(w))
+    xf = synth.gaussian(g, (4096,), 1.0)
+    xb = synth.to_bf16_bits(xf)
+    act_int8 = fmt in ("int8_i", "ternary")
+    x = dev(xf) if act_int8 else dev_bf16(xb)
+    accs = [torch.empty(W.n, dtype=torch.int32, device="cuda") for W in Ws] if act_int8 else None
+    ys = qg.qgemv_grouped(Ws, x, act_int8=act_int8, y_dtype=torch.float32, accs=accs)
+    for i, W in enumerate(Ws):
+        acc1 = torch.empty(W.n, dtype=torch.int32, device="cuda") if act_int8 else None
+        y1 = qg.qgemv(W, x, act_int8=act_int8, y_dtype=torch.float32, acc_out=acc1)
+        assert np.array_equal(host(ys[i]), host(y1)), "grouped output differs from the single launch"
+        if act_int8:
+            assert np.array_equal(host(accs[i]), host(acc1))
+            xq_r, sx_r = oracle.quantize_absmax(xf, per_row=False)
+            acc_r = oracle.int_dot_exact(refs[i][0], xq_r)
+            assert np.array_equal(host(accs[i]), acc_r.astype(np.int32))
+        elif fmt == "int8_f":
+            assert oracle.normwise_error(host(ys[i]), oracle.y_w8a16(refs[i][0], refs[i][1], xb)) <= 1e-5
+        else:
+            assert oracle.normwise_error(host(ys[i]), oracle.y_sign_residual(*refs[i], xb)) <= 1e-5
+
+
 def test_qgemv_zero_inputs(qg):
     note("qgemv zero inputs")
     n, k = 70, 1024
