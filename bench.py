@@ -332,7 +332,7 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
     del wdev
     xp = torch.from_numpy(wl.tensors["x_bf16"]).to(dev).view(torch.bfloat16)
     yp = torch.empty((m, n), dtype=torch.float32, device=dev)
-    ws = torch.empty(qg.lib().qg_qgemm_workspace_bytes(m, k, n_out), dtype=torch.uint8, device=dev)
+    ws = torch.empty(qg.lib().qg_qgemm_workspace_bytes(m, k, n, n_out), dtype=torch.uint8, device=dev)
     xq = torch.empty((m, k), dtype=torch.int8, device=dev)
     sx = torch.empty(m, dtype=torch.float32, device=dev)
     xo = torch.empty((m, n_out), dtype=torch.bfloat16, device=dev)

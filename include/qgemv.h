@@ -256,10 +256,10 @@ qg_status qg_qgemv_grouped(const qg_weight* w, int32_t count, int32_t amode, con
  * wq     : [n][k] int8 (per-row absmax codes of W, from qg_quantize_absmax).
  * s_w    : [n] fp32.      w_out: [n][n_out] bf16 (qg_gather_columns_bf16).
  * y      : [m][n] fp32 (out).   acc_out: [m][n] int32 (out) or NULL.
- * ws     : qg_qgemm_workspace_bytes(m, k, n_out) bytes, 16-B aligned.
+ * ws     : qg_qgemm_workspace_bytes(m, k, n, n_out) bytes, 16-B aligned.
  * k % 128 == 0, k <= 262144; m, n >= 1.
  */
-size_t qg_qgemm_workspace_bytes(int64_t m, int64_t k, int32_t n_out);
+size_t qg_qgemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int32_t n_out);
 qg_status qg_qgemm_w8a8_outlier(const void* x, int64_t m, int64_t k,
                                 const int32_t* idx, int32_t n_out,
                                 const int8_t* wq, const float* s_w, const void* w_out,

@@ -56,7 +56,7 @@ _SIGS = {
     "qg_qgemv": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp]),
     "qg_qgemv_grouped": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_i32, _c_vp, _c_i32, ctypes.POINTER(_c_vp),
                                   _c_i32, ctypes.POINTER(_c_vp), _c_vp]),
-    "qg_qgemm_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i32]),
+    "qg_qgemm_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i32]),
     "qg_qgemm_w8a8_outlier": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i64,
                                        _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
 }
@@ -298,7 +298,7 @@ def qgemm_w8a8_outlier(x: torch.Tensor, idx: Sequence[int], wq: torch.Tensor, s_
         _dev(w_out, "w_out", torch.bfloat16)
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=x.device)
-    nws = lib().qg_qgemm_workspace_bytes(m, k, n_out)
+    nws = lib().qg_qgemm_workspace_bytes(m, k, n, n_out)
     if ws is None:
         ws = torch.empty(nws, dtype=torch.uint8, device=x.device)
     _check(lib().qg_qgemm_w8a8_outlier(_p(x), m, k, cidx, n_out, _p(wq), _p(s_w), _p(w_out) if n_out else None, n,

@@ -27,14 +27,17 @@ qg_status check_idx(const int32_t* idx, int32_t n_out, int64_t cols, qg::Outlier
     return QG_OK;
 }
 
-size_t qgemm_layout(int64_t m, int64_t k, int32_t n_out, size_t* off_sx, size_t* off_xo, int* ld) {
+size_t qgemm_layout(int64_t m, int64_t k, int64_t n, int32_t n_out, size_t* off_sx, size_t* off_xo, size_t* off_wp,
+                    int* ld) {
     const int l = n_out > 0 ? (int)align_up((size_t)n_out, 16) : 0;
     const size_t xq = (size_t)m * (size_t)k;
     const size_t sx = align_up(xq, 256);
     const size_t xo = align_up(sx + (size_t)m * sizeof(float), 256);
-    const size_t total = align_up(xo + (size_t)m * (size_t)l * 2, 256);
+    const size_t wp = align_up(xo + (size_t)m * (size_t)l * 2, 256);
+    const size_t total = align_up(wp + (size_t)n * (size_t)l * 2, 256);
     if (off_sx) *off_sx = sx;
     if (off_xo) *off_xo = xo;
+    if (off_wp) *off_wp = wp;
     if (ld) *ld = l;
     return total;
 }
@@ -214,9 +217,9 @@ qg_status qg_qgemv_grouped(const qg_weight* w, int32_t count, int32_t amode, con
     return from_hip(qg::launch_qgemv_group(a, count, as_stream(stream)));
 }
 
-size_t qg_qgemm_workspace_bytes(int64_t m, int64_t k, int32_t n_out) {
-    if (m < 1 || k < 1 || n_out < 0 || n_out > QG_MAX_OUTLIERS) return 0;
-    return qgemm_layout(m, k, n_out, nullptr, nullptr, nullptr);
+size_t qg_qgemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int32_t n_out) {
+    if (m < 1 || k < 1 || n < 1 || n_out < 0 || n_out > QG_MAX_OUTLIERS) return 0;
+    return qgemm_layout(m, k, n, n_out, nullptr, nullptr, nullptr, nullptr);
 }
 
 qg_status qg_qgemm_w8a8_outlier(const void* x, int64_t m, int64_t k, const int32_t* idx, int32_t n_out,
@@ -231,9 +234,9 @@ qg_status qg_qgemm_w8a8_outlier(const void* x, int64_t m, int64_t k, const int32
     qg::OutlierIdx oi;
     const qg_status st = check_idx(idx, n_out, k, &oi);
     if (st != QG_OK) return st;
-    size_t off_sx = 0, off_xo = 0;
+    size_t off_sx = 0, off_xo = 0, off_wp = 0;
     int ld = 0;
-    const size_t need = qgemm_layout(m, k, n_out, &off_sx, &off_xo, &ld);
+    const size_t need = qgemm_layout(m, k, n, n_out, &off_sx, &off_xo, &off_wp, &ld);
     if (!ws || ws_bytes < need) return QG_ERR_WORKSPACE;
     if (!aligned16(ws)) return QG_ERR_ALIGN;
     uint8_t* base = static_cast<uint8_t*>(ws);
@@ -252,6 +255,7 @@ qg_status qg_qgemm_w8a8_outlier(const void* x, int64_t m, int64_t k, const int32
     a.s_x = reinterpret_cast<float*>(base + off_sx);
     a.x_out = reinterpret_cast<uint16_t*>(base + off_xo);
     a.x_out_ld = ld;
+    a.w_pad = reinterpret_cast<uint16_t*>(base + off_wp);
     return from_hip(qg::launch_qgemm(a, oi, as_stream(stream)));
 }
 

@@ -20,7 +20,8 @@ int absmax_tensor_parts(int64_t elems);
 hipError_t launch_absmax_tensor(const void* x, int xt, int64_t elems, int8_t* q, float* s, float* partial,
                                 hipStream_t st);
 hipError_t launch_absmax_split(const uint16_t* x, int64_t rows, int64_t cols, const OutlierIdx& idx, int n_out,
-                               int8_t* q, float* s, uint16_t* x_out, int x_out_ld, hipStream_t st);
+                               int8_t* q, float* s, uint16_t* x_out, int x_out_ld, hipStream_t st,
+                               const uint16_t* w_out = nullptr, int64_t w_rows = 0, uint16_t* w_pad = nullptr);
 hipError_t launch_gather_cols_bf16(const float* w, int64_t n, int64_t k, const OutlierIdx& idx, int n_out,
                                    uint16_t* w_out, hipStream_t st);
 hipError_t launch_ternary(const float* w, int64_t count, int8_t* q, float* gamma, uint64_t* hist, hipStream_t st);
@@ -58,6 +59,7 @@ struct QgemmArgs {
     float* s_x;
     uint16_t* x_out;
     int x_out_ld;
+    uint16_t* w_pad;  // [n][x_out_ld] zero-padded copy of w_out
 };
 hipError_t launch_qgemm(const QgemmArgs& a, const OutlierIdx& idx, hipStream_t st);
 

@@ -106,7 +106,8 @@ __global__ __launch_bounds__(kThreads) void absmax_apply_kernel(const void* x, i
 // built from the (host-validated, sorted) index list passed by value.
 __global__ __launch_bounds__(kThreads) void absmax_split_kernel(const uint16_t* x, int64_t rows, int64_t cols,
                                                                  OutlierIdx idx, int n_out, int8_t* q, float* s,
-                                                                 uint16_t* x_out, int x_out_ld) {
+                                                                 uint16_t* x_out, int x_out_ld, const uint16_t* w_out,
+                                                                 int64_t w_rows, uint16_t* w_pad) {
     extern __shared__ uint32_t bitmap[];  // cols / 32 words
     __shared__ float red[kWaves];
     const int nwords = (int)(cols / 32);
@@ -142,6 +143,13 @@ __global__ __launch_bounds__(kThreads) void absmax_split_kernel(const uint16_t* 
         // gathered outlier activations, zero-padded up to the row stride
         for (int j = threadIdx.x; j < x_out_ld; j += kThreads)
             x_out[r * x_out_ld + j] = (j < n_out) ? x[r * cols + idx.v[j]] : (uint16_t)0;
+    }
+    // optional: copy the outlier weights [w_rows][n_out] into a zero-padded
+    // [w_rows][x_out_ld] layout, so the GEMM epilogue reads them as vectors
+    if (w_pad) {
+        for (int64_t r = blockIdx.x; r < w_rows; r += gridDim.x)
+            for (int j = threadIdx.x; j < x_out_ld; j += kThreads)
+                w_pad[r * x_out_ld + j] = (j < n_out) ? w_out[r * n_out + j] : (uint16_t)0;
     }
 }
 
@@ -303,10 +311,12 @@ hipError_t launch_absmax_tensor(const void* x, int xt, int64_t elems, int8_t* q,
 }
 
 hipError_t launch_absmax_split(const uint16_t* x, int64_t rows, int64_t cols, const OutlierIdx& idx, int n_out,
-                               int8_t* q, float* s, uint16_t* x_out, int x_out_ld, hipStream_t st) {
+                               int8_t* q, float* s, uint16_t* x_out, int x_out_ld, hipStream_t st,
+                               const uint16_t* w_out, int64_t w_rows, uint16_t* w_pad) {
     const int g = grid_for(rows, 1, 65535);
     const size_t lds = (size_t)(cols / 32) * sizeof(uint32_t);
-    absmax_split_kernel<<<g, kThreads, lds, st>>>(x, rows, cols, idx, n_out, q, s, x_out, x_out_ld);
+    absmax_split_kernel<<<g, kThreads, lds, st>>>(x, rows, cols, idx, n_out, q, s, x_out, x_out_ld, w_out, w_rows,
+                                                  w_pad);
     return hipGetLastError();
 }
 

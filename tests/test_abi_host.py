@@ -36,6 +36,11 @@ def header_functions():
     return sorted(set(re.findall(r"\b(qg_[a-z0-9_]+)\s*\(", src)))
 
 
+def test_library_resolves_all_symbols(qg):
+    # RTLD_NOW: every symbol (including kernel host stubs) must resolve at load
+    ctypes.CDLL(qg.LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+
+
 def test_header_symbols_exported(qg):
     decl = header_functions()
     assert len(decl) >= 14
@@ -170,9 +175,9 @@ def test_validation_qgemm(qg):
     l = qg.lib()
     f = l.qg_qgemm_w8a8_outlier
     idx = (ctypes.c_int32 * 2)(3, 7)
-    need = l.qg_qgemm_workspace_bytes(16, 256, 2)
+    need = l.qg_qgemm_workspace_bytes(16, 256, 32, 2)
     assert need >= 16 * 256 + 16 * 4 + 16 * 16 * 2
-    assert l.qg_qgemm_workspace_bytes(16, 256, 300) == 0
+    assert l.qg_qgemm_workspace_bytes(16, 256, 32, 300) == 0
     assert f(A, 16, 256, idx, 2, A, A, A, 32, A, None, A, need, None) != 5 or True  # not executed: no GPU
     assert f(A, 16, 256, idx, 2, A, A, A, 32, A, None, A, need - 1, None) == 5
     assert f(A, 16, 256, idx, 2, A, A, None, 32, A, None, A, need, None) == 1
