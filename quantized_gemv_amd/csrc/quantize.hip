@@ -103,7 +103,11 @@ __global__ __launch_bounds__(kThreads) void absmax_apply_kernel(const void* x, i
 
 // ---------------------------------------------------------------- outlier split
 // One workgroup per token row.  The outlier channel set is a bitmap in LDS
-// built from the (host-validated, sorted) index list passed by value.
+// built from the (host-validated, sorted) index list passed by value.  For
+// rows of up to NP * 2048 columns each thread keeps its share of the row in
+// registers between the max pass and the quantize pass (one HBM read);
+// longer rows re-read the row from cache for the second pass (NP = 0).
+template <int NP>
 __global__ __launch_bounds__(kThreads) void absmax_split_kernel(const uint16_t* x, int64_t rows, int64_t cols,
                                                                  OutlierIdx idx, int n_out, int8_t* q, float* s,
                                                                  uint16_t* x_out, int x_out_ld, const uint16_t* w_out,
@@ -120,29 +124,64 @@ __global__ __launch_bounds__(kThreads) void absmax_split_kernel(const uint16_t* 
     __syncthreads();
     const int64_t c8 = cols / 8;
     for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const uint16_t* xr = x + r * cols;
         float m = 0.0f;
-        for (int64_t i = threadIdx.x; i < c8; i += kThreads) {
+        auto unpack8 = [](uint4 h, float v[8]) {
+            const uint32_t w[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[2 * e] = bf16_to_f32(w[e] & 0xFFFFu);
+                v[2 * e + 1] = bf16_to_f32(w[e] >> 16);
+            }
+        };
+        auto inliers = [&](int64_t i) { return ~(bitmap[(i * 8) >> 5] >> ((i * 8) & 31)) & 0xFFu; };
+        auto piece_max = [&](int64_t i, uint4 h) {
             float v[8];
-            load8<1>(x, r * cols + i * 8, v);
-            const uint32_t bits = (bitmap[(i * 8) >> 5] >> ((i * 8) & 31)) & 0xFFu;
+            unpack8(h, v);
+            const uint32_t keep_bits = inliers(i);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                if (!((bits >> j) & 1u)) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
-        }
-        const float sc = absmax_scale(block_max(m, red));
-        if (threadIdx.x == 0) s[r] = sc;
-        for (int64_t i = threadIdx.x; i < c8; i += kThreads) {
+                if ((keep_bits >> j) & 1u) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
+        };
+        auto piece_quant = [&](int64_t i, uint4 h, float sc) {
             float v[8];
             int c[8];
-            load8<1>(x, r * cols + i * 8, v);
-            const uint32_t bits = (bitmap[(i * 8) >> 5] >> ((i * 8) & 31)) & 0xFFu;
+            unpack8(h, v);
+            const uint32_t keep_bits = inliers(i);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) c[j] = ((bits >> j) & 1u) ? 0 : qcode(v[j], sc);
+            for (int j = 0; j < 8; ++j) c[j] = ((keep_bits >> j) & 1u) ? qcode(v[j], sc) : 0;
             store8_codes(q, r * cols + i * 8, c);
+        };
+        if constexpr (NP > 0) {
+            uint4 keep[NP];
+#pragma unroll
+            for (int t = 0; t < NP; ++t) {
+                const int64_t i = threadIdx.x + (int64_t)kThreads * t;
+                keep[t] = (i < c8) ? *reinterpret_cast<const uint4*>(xr + i * 8) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int t = 0; t < NP; ++t) {
+                const int64_t i = threadIdx.x + (int64_t)kThreads * t;
+                if (i < c8) piece_max(i, keep[t]);
+            }
+            const float sc = absmax_scale(block_max(m, red));
+            if (threadIdx.x == 0) s[r] = sc;
+#pragma unroll
+            for (int t = 0; t < NP; ++t) {
+                const int64_t i = threadIdx.x + (int64_t)kThreads * t;
+                if (i < c8) piece_quant(i, keep[t], sc);
+            }
+        } else {
+            for (int64_t i = threadIdx.x; i < c8; i += kThreads)
+                piece_max(i, *reinterpret_cast<const uint4*>(xr + i * 8));
+            const float sc = absmax_scale(block_max(m, red));
+            if (threadIdx.x == 0) s[r] = sc;
+            for (int64_t i = threadIdx.x; i < c8; i += kThreads)
+                piece_quant(i, *reinterpret_cast<const uint4*>(xr + i * 8), sc);
         }
         // gathered outlier activations, zero-padded up to the row stride
         for (int j = threadIdx.x; j < x_out_ld; j += kThreads)
-            x_out[r * x_out_ld + j] = (j < n_out) ? x[r * cols + idx.v[j]] : (uint16_t)0;
+            x_out[r * x_out_ld + j] = (j < n_out) ? xr[idx.v[j]] : (uint16_t)0;
     }
     // optional: copy the outlier weights [w_rows][n_out] into a zero-padded
     // [w_rows][x_out_ld] layout, so the GEMM epilogue reads them as vectors
@@ -315,8 +354,19 @@ hipError_t launch_absmax_split(const uint16_t* x, int64_t rows, int64_t cols, co
                                const uint16_t* w_out, int64_t w_rows, uint16_t* w_pad) {
     const int g = grid_for(rows, 1, 65535);
     const size_t lds = (size_t)(cols / 32) * sizeof(uint32_t);
-    absmax_split_kernel<<<g, kThreads, lds, st>>>(x, rows, cols, idx, n_out, q, s, x_out, x_out_ld, w_out, w_rows,
-                                                  w_pad);
+    const int64_t per_thread = (cols / 8 + kThreads - 1) / kThreads;  // 16-byte pieces per thread
+    if (per_thread <= 1)
+        absmax_split_kernel<1><<<g, kThreads, lds, st>>>(x, rows, cols, idx, n_out, q, s, x_out, x_out_ld, w_out,
+                                                         w_rows, w_pad);
+    else if (per_thread <= 2)
+        absmax_split_kernel<2><<<g, kThreads, lds, st>>>(x, rows, cols, idx, n_out, q, s, x_out, x_out_ld, w_out,
+                                                         w_rows, w_pad);
+    else if (per_thread <= 4)
+        absmax_split_kernel<4><<<g, kThreads, lds, st>>>(x, rows, cols, idx, n_out, q, s, x_out, x_out_ld, w_out,
+                                                         w_rows, w_pad);
+    else
+        absmax_split_kernel<0><<<g, kThreads, lds, st>>>(x, rows, cols, idx, n_out, q, s, x_out, x_out_ld, w_out,
+                                                         w_rows, w_pad);
     return hipGetLastError();
 }
 
