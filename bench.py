@@ -5,16 +5,25 @@ Headline step: one batch-1 decode token through the linear layers of a
 weights (per-row absmax scales) and bf16 activations: per layer q, k, v, o
 (4096 x 4096), gate, up (11008 x 4096) and down (4096 x 11008).  Every layer
 has its own weight copy (6.5 GB in total), so nothing is served from the
-256 MB Infinity Cache.  The step's 224 GEMV launches are captured once in a
-HIP graph and replayed.  `value` = weight bytes streamed per second.
+256 MB Infinity Cache.  Projections that read the same activation share one
+grouped launch, so a layer is 4 launches -- (q,k,v), o, (gate,up), down --
+and the step's 128 launches are captured once in a HIP graph and replayed.
+`value` = weight bytes streamed per second.
 
 Also measured (in the same JSON line): each workload of the suite on its
 own (tiny W8A8, the three decode shapes, ternary, sign + residual, W8A8
 prefill GEMM with outlier split), the roofline of the dominant kernel and the
 CPU oracle's throughput on a bounded sample of the same workload.
 
+HBM traffic (roofline "traffic") comes from two rocprofv3 --pmc passes over
+`--profile-workload` (FETCH_SIZE, then WRITE_SIZE), turned into
+profiles/hbm_traffic_counters.json by `--summarize-counters`; the figures are
+used only while the kernel sources still hash to the values recorded there.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
                        [--no-cpu-baseline] [--only-headline]
+       python bench.py --profile-workload
+       python bench.py --summarize-counters FETCH_DIR WRITE_DIR
 """
 from __future__ import annotations
 
@@ -31,8 +40,15 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 INT8_MFMA_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, TOP/s
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "qgemv_w8a16_decode7b_counters.json")
-QGEMV_SRC = os.path.join(ROOT, "quantized_gemv_amd", "csrc", "qgemv.hip")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
+CSRC = os.path.join(ROOT, "quantized_gemv_amd", "csrc")
+# sources whose hash keys the recorded counters of each kernel
+KERNEL_SOURCES = {
+    "qgemv": ("qgemv.hip", "qg_device.h", "qg_launch.h"),
+    "qgemm": ("qgemm.hip", "qg_device.h", "qg_launch.h"),
+}
+KERNEL_NAME_KEYS = {"qgemv": "qgemv_kernel", "qgemm": "qgemm_w8a8_kernel"}
+COPY_BYTES = 256 << 20           # calibration copy: bytes read and bytes written
 
 
 def parse():
@@ -43,6 +59,14 @@ def parse():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--profile-workload", action="store_true",
+                    help="run the calibration copy, 2 decode steps and 2 prefill calls, then exit "
+                         "(the workload of the rocprofv3 --pmc passes)")
+    ap.add_argument("--hashes-out", metavar="PATH",
+                    help="with --profile-workload: write the kernel source hashes the run used to PATH")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "HASHES"),
+                    help="turn the two rocprofv3 --pmc output folders (and the hashes written by the "
+                         "profiled runs) into " + os.path.relpath(COUNTERS_FILE, ROOT))
     return ap.parse_args()
 
 
@@ -50,9 +74,26 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def src_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def src_hash(kernel):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch from the recorded counters, or None when they are
+    missing or were taken on other kernel sources."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            cnt = json.load(f)
+        rec = cnt["kernels"][kernel]
+        if rec.get("src_sha256_16") == src_hash(kernel):
+            return rec.get("hbm_bytes_per_launch")
+    except (OSError, ValueError, KeyError, TypeError):
+        pass
+    return None
 
 
 class Timed:
@@ -75,7 +116,8 @@ class Timed:
         torch.cuda.synchronize()
 
     def run(self, reps):
-        """Returns seconds per replay measured with events on the launching stream."""
+        """Returns seconds per replay measured with events on the launching
+        stream (graph replays run on the current stream)."""
         torch = self.torch
         st = torch.cuda.current_stream()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -88,12 +130,207 @@ class Timed:
         return e0.elapsed_time(e1) / 1e3 / reps
 
 
+def build_headline(torch, qg, synth, dev, L):
+    """Weights of L decode layers (own copy per layer) and the step's launches."""
+    shapes = synth.DECODE_7B_SHAPES
+    log("quantizing the three 7B projection shapes on the GPU")
+    base = {}
+    xs = {}
+    for name, (n, k) in shapes.items():
+        wl = synth.decode_w8a16(n=n, k=k, seed=synth.DECODE_7B_SEEDS[name])
+        wq, s_w = qg.quantize_absmax(torch.from_numpy(wl.tensors["w"]).to(dev), per_row=True)
+        base[name] = (wq, s_w)
+        xs[k] = torch.from_numpy(wl.tensors["x_bf16"]).to(dev).view(torch.bfloat16)
+    layer_plan = ["attn_4096x4096"] * 4 + ["ffn_up_11008x4096"] * 2 + ["ffn_down_4096x11008"]
+    log("replicating weights for %d layers" % L)
+    weights = []  # (name, QWeight, CWeight)
+    for _ in range(L):
+        for name in layer_plan:
+            n, k = shapes[name]
+            wq, s_w = base[name]
+            W = qg.QWeight(qg.QG_WFMT_INT8, n, k, wq.clone(), s_w.clone())
+            weights.append((name, W, W.c_struct()))
+    torch.cuda.synchronize()
+    ys = {n: torch.empty(n, dtype=torch.bfloat16, device=dev) for n in (4096, 11008)}
+    # One decode layer = 4 dependent launches: the projections that read the
+    # same activation go in one grouped launch (q, k, v) and (gate, up).
+    y_proj = [torch.empty(shapes[name][0], dtype=torch.bfloat16, device=dev) for name in layer_plan]
+    groups_per_layer = [[0, 1, 2], [3], [4, 5], [6]]
+    launches = []
+    keep = []
+    for li in range(L):
+        for grp in groups_per_layer:
+            ws_ = [weights[li * len(layer_plan) + i][1] for i in grp]
+            gl = qg.GroupLaunch(ws_, xs[ws_[0].k], [y_proj[i] for i in grp], act_int8=False)
+            keep.append(gl)
+            launches.append(gl.launch)
+    step_bytes = sum(W.n * W.k + 4 * W.n for _, W, _ in weights)  # int8 codes + fp32 per-row scales
+    act_bytes = sum(2 * (W.k + W.n) for _, W, _ in weights)       # bf16 x read + y written
+    return dict(weights=weights, xs=xs, ys=ys, y_proj=y_proj, launches=launches, keep=keep,
+                step_bytes=step_bytes, act_bytes=act_bytes)
+
+
+def build_prefill(torch, qg, synth, dev, cur_stream):
+    """Operands of the 2048 x 4096 x 4096 prefill with 20 outlier channels;
+    returns closures for the full call, its split alone and its GEMM alone
+    (on the split's outputs; run the split once before timing it)."""
+    import ctypes
+    wl = synth.prefill_outlier()
+    m, k, n, n_out = 2048, 4096, 4096, 20
+    idx = wl.tensors["idx"].tolist()
+    wdev = torch.from_numpy(wl.tensors["w"]).to(dev)
+    wq, s_w = qg.quantize_absmax(wdev, per_row=True)
+    w_out = qg.gather_columns_bf16(wdev, idx)
+    del wdev
+    xp = torch.from_numpy(wl.tensors["x_bf16"]).to(dev).view(torch.bfloat16)
+    yp = torch.empty((m, n), dtype=torch.float32, device=dev)
+    ws = torch.empty(qg.lib().qg_qgemm_workspace_bytes(m, k, n_out), dtype=torch.uint8, device=dev)
+    xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+    sx = torch.empty(m, dtype=torch.float32, device=dev)
+    ld = qg.out_ld(n_out)  # row stride of the outlier operands (w_out comes back as [n][ld])
+    xo = torch.empty((m, ld), dtype=torch.bfloat16, device=dev)
+    cidx = (ctypes.c_int32 * n_out)(*idx)
+    L = qg.lib()
+    hold = (wq, s_w, w_out, xp, yp, ws, xq, sx, xo, cidx)
+
+    def full():
+        st = L.qg_qgemm_w8a8_outlier(ctypes.c_void_p(xp.data_ptr()), m, k, cidx, n_out,
+                                     ctypes.c_void_p(wq.data_ptr()), ctypes.c_void_p(s_w.data_ptr()),
+                                     ctypes.c_void_p(w_out.data_ptr()), ld, n, ctypes.c_void_p(yp.data_ptr()),
+                                     None, ctypes.c_void_p(ws.data_ptr()), ws.numel(), ctypes.c_void_p(cur_stream()))
+        if st != 0:
+            raise RuntimeError("qg_qgemm_w8a8_outlier failed: %s" % qg.status_str(st))
+
+    def split_only():
+        st = L.qg_quantize_absmax_split(ctypes.c_void_p(xp.data_ptr()), m, k, cidx, n_out,
+                                        ctypes.c_void_p(xq.data_ptr()), ctypes.c_void_p(sx.data_ptr()),
+                                        ctypes.c_void_p(xo.data_ptr()), ld, ctypes.c_void_p(cur_stream()))
+        if st != 0:
+            raise RuntimeError("qg_quantize_absmax_split failed: %s" % qg.status_str(st))
+
+    def gemm_only():
+        st = L.qg_qgemm_w8a8(ctypes.c_void_p(xq.data_ptr()), ctypes.c_void_p(sx.data_ptr()),
+                             ctypes.c_void_p(xo.data_ptr()), ld, m, k, n_out, ctypes.c_void_p(wq.data_ptr()),
+                             ctypes.c_void_p(s_w.data_ptr()), ctypes.c_void_p(w_out.data_ptr()), ld, n,
+                             ctypes.c_void_p(yp.data_ptr()), None, ctypes.c_void_p(cur_stream()))
+        if st != 0:
+            raise RuntimeError("qg_qgemm_w8a8 failed: %s" % qg.status_str(st))
+    full.hold = hold
+    dims = dict(m=m, k=k, n=n, n_out=n_out, xq=xq, wq=wq, gemm_only=gemm_only)
+    # algorithmic HBM bytes of the GEMM kernel: int8 X and W, their scales, the
+    # bf16 outlier operands (rows of ld), fp32 Y written
+    gemm_bytes = m * k + n * k + 4 * (m + n) + 2 * ld * (m + n) + 4 * m * n
+    return full, split_only, dims, gemm_bytes
+
+
+def profile_workload(args):
+    """Fixed workload for the rocprofv3 --pmc passes: a device copy of known
+    size (the calibration), two decode steps and two prefill calls."""
+    import torch
+    import quantized_gemv_amd as qg
+    import synth
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    qg.lib()
+    dev = torch.device("cuda:0")
+
+    def cur_stream():
+        return torch.cuda.current_stream().cuda_stream
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    h = build_headline(torch, qg, synth, dev, args.layers)
+    for _ in range(2):
+        for f in h["launches"]:
+            f()
+    torch.cuda.synchronize()
+    del h
+    torch.cuda.empty_cache()
+    full, _, _, _ = build_prefill(torch, qg, synth, dev, cur_stream)
+    for _ in range(2):
+        full()
+    torch.cuda.synchronize()
+    if args.hashes_out:
+        with open(args.hashes_out, "w") as f:
+            json.dump({k: src_hash(k) for k in KERNEL_SOURCES}, f)
+    log("profile workload done")
+
+
+def _counter_means(folder, counter):
+    """{kernel name: (mean value, dispatches)} from a rocprofv3 --pmc csv folder."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no *counter_collection.csv under %s" % folder)
+    acc = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = r["Kernel_Name"]
+                v = float(r["Counter_Value"])
+                s_, c_ = acc.get(k, (0.0, 0))
+                acc[k] = (s_ + v, c_ + 1)
+    return {k: (s_ / c_, c_) for k, (s_, c_) in acc.items()}
+
+
+def summarize_counters(fetch_dir, write_dir, hashes_path):
+    """Scale the qgemv / qgemm FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by
+    what the same counters read for the calibration copy, and record them
+    under the source hashes of the kernels the profiled run executed."""
+    with open(hashes_path) as f:
+        hashes = json.load(f)
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+
+    def pick(d, key):
+        ks = [k for k in d if key in k]
+        if not ks:
+            raise SystemExit("no kernel matching %r in %s" % (key, sorted(d)))
+        tot = sum(d[k][0] * d[k][1] for k in ks)
+        n = sum(d[k][1] for k in ks)
+        return tot / n, n, ks
+    copy_keys = [k for k in fetch if "copy" in k.lower()]
+    if not copy_keys:
+        raise SystemExit("calibration copy kernel not found among %s" % sorted(fetch))
+    cf, cn, ck = pick(fetch, copy_keys[0])
+    cw, _, _ = pick(write, copy_keys[0])
+    f_fetch = COPY_BYTES / (cf * 1024.0)
+    f_write = COPY_BYTES / (cw * 1024.0)
+    out = {"calibration": {"kernel": ck[0], "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                           "fetch_kib": round(cf, 1), "write_kib": round(cw, 1),
+                           "fetch_scale": round(f_fetch, 4), "write_scale": round(f_write, 4)},
+           "kernels": {}}
+    for kern, key in KERNEL_NAME_KEYS.items():
+        fk, nf, names = pick(fetch, key)
+        wk, nw, _ = pick(write, key)
+        hbm = fk * 1024.0 * f_fetch + wk * 1024.0 * f_write
+        out["kernels"][kern] = {"src_sha256_16": hashes[kern], "dispatches": nf, "kernel_names": names,
+                                "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+                                "hbm_bytes_per_launch": round(hbm)}
+    with open(COUNTERS_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
+    if args.profile_workload:
+        profile_workload(args)
+        return
 
     import numpy as np
     import torch
@@ -110,50 +347,9 @@ def main():
         return torch.cuda.current_stream().cuda_stream
 
     # ---------------------------------------------------------------- headline stack
-    shapes = synth.DECODE_7B_SHAPES
-    log("quantizing the three 7B projection shapes on the GPU")
-    base = {}
-    xs = {}
-    for name, (n, k) in shapes.items():
-        wl = synth.decode_w8a16(n=n, k=k, seed=synth.DECODE_7B_SEEDS[name])
-        wq, s_w = qg.quantize_absmax(torch.from_numpy(wl.tensors["w"]).to(dev), per_row=True)
-        base[name] = (wq, s_w)
-        xs[k] = torch.from_numpy(wl.tensors["x_bf16"]).to(dev).view(torch.bfloat16)
-    layer_plan = ["attn_4096x4096"] * 4 + ["ffn_up_11008x4096"] * 2 + ["ffn_down_4096x11008"]
     L = args.layers
-    log("replicating weights for %d layers" % L)
-    weights = []  # (name, QWeight, CWeight)
-    for _ in range(L):
-        for name in layer_plan:
-            n, k = shapes[name]
-            wq, s_w = base[name]
-            W = qg.QWeight(qg.QG_WFMT_INT8, n, k, wq.clone(), s_w.clone())
-            weights.append((name, W, W.c_struct()))
-    torch.cuda.synchronize()
-    ys = {n: torch.empty(n, dtype=torch.bfloat16, device=dev) for n in (4096, 11008)}
-    # One decode layer = 4 dependent launches: the projections that read the
-    # same activation go in one grouped launch (q, k, v) and (gate, up).
-    y_proj = [torch.empty(shapes[name][0], dtype=torch.bfloat16, device=dev) for name in layer_plan]
-    groups_per_layer = [[0, 1, 2], [3], [4, 5], [6]]
-    launches = []
-    for li in range(L):
-        for grp in groups_per_layer:
-            ws_ = [weights[li * len(layer_plan) + i][1] for i in grp]
-            gl = qg.GroupLaunch(ws_, xs[ws_[0].k], [y_proj[i] for i in grp], act_int8=False)
-            launches.append(gl.launch)
-
-    def gemv_launch(W, cw):
-        def f():
-            st = qg.qgemv_launch_raw(cw, qg.QG_ACT_FLOAT, xs[W.k].data_ptr(), qg.QG_BF16, ys[W.n].data_ptr(),
-                                     qg.QG_BF16, cur_stream())
-            if st != 0:
-                raise RuntimeError("qg_qgemv failed: %s" % qg.status_str(st))
-        return f
-
-    step_bytes = 0
-    for name, W, _ in weights:
-        step_bytes += W.n * W.k + 4 * W.n  # int8 codes + fp32 per-row scales
-    act_bytes = sum(2 * (W.k + W.n) for _, W, _ in weights)  # bf16 x read + y written
+    h = build_headline(torch, qg, synth, dev, L)
+    launches, step_bytes, act_bytes = h["launches"], h["step_bytes"], h["act_bytes"]
     launches_per_step = len(launches)
 
     log("capturing the decode step (%d launches, %.2f GB of weights)" % (launches_per_step, step_bytes / 1e9))
@@ -161,31 +357,29 @@ def main():
     for _ in range(args.warmup):
         step.graph.replay()
     torch.cuda.synchronize()
-    ev_s = step.run(max(1, args.steps // 10))  # event-timed pass (roofline), same work
+    # timed region: K replays, bracketed by device synchronisation, with HIP
+    # events recorded on the stream the graph is replayed on
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(st)
     for _ in range(args.steps):
         step.graph.replay()
+    e1.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ev_s = e0.elapsed_time(e1) / 1e3 / args.steps
     ms_per_step = wall / args.steps * 1e3
     value = step_bytes / (wall / args.steps) / 1e9
     # dominant kernel: the W8A16 qgemv (the step contains nothing else)
     per_launch_s = ev_s / launches_per_step
     per_launch_bytes = (step_bytes + act_bytes) / launches_per_step
     achieved = per_launch_bytes / per_launch_s / 1e9
-    traffic = None
-    if os.path.exists(COUNTERS_FILE):
-        try:
-            with open(COUNTERS_FILE) as f:
-                cnt = json.load(f)
-            if cnt.get("qgemv_src_sha256_16") == src_hash(QGEMV_SRC):
-                traffic = cnt.get("hbm_bytes_per_launch")
-        except (OSError, ValueError):
-            traffic = None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "qgemv_kernel<INT8,x bf16,y bf16> (W8A16; grouped and single launches)",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic("qgemv"),
+                "kernel": "qgemv_kernel<INT8 weights, bf16 x, bf16 y> (grouped and single launches)",
                 "algorithmic_bytes_per_launch": round(per_launch_bytes), "avg_launch_us": round(per_launch_s * 1e6, 3)}
     log("decode step: %.3f ms, %.1f GB/s weights (%.1f%% of HBM peak)" % (ms_per_step, value, 100 * value / HBM_PEAK_GBS))
 
@@ -211,7 +405,7 @@ def main():
     }
 
     if not args.only_headline:
-        result["configs"] = bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys)
+        result["configs"] = bench_configs(torch, qg, synth, np, dev, cur_stream, h["weights"], h["xs"], h["ys"])
         result["prefill"] = result["configs"].pop("prefill_w8a8_outlier")
     result["context"] = {
         "note": "figures quoted from the pages for context; not targets",
@@ -323,40 +517,17 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
     torch.cuda.empty_cache()
 
     # -- W8A8 prefill GEMM with outlier split, 2048 x 4096 x 4096, 20 outlier channels
-    wl = synth.prefill_outlier()
-    m, k, n, n_out = 2048, 4096, 4096, 20
-    idx = wl.tensors["idx"].tolist()
-    wdev = torch.from_numpy(wl.tensors["w"]).to(dev)
-    wq, s_w = qg.quantize_absmax(wdev, per_row=True)
-    w_out = qg.gather_columns_bf16(wdev, idx)
-    del wdev
-    xp = torch.from_numpy(wl.tensors["x_bf16"]).to(dev).view(torch.bfloat16)
-    yp = torch.empty((m, n), dtype=torch.float32, device=dev)
-    ws = torch.empty(qg.lib().qg_qgemm_workspace_bytes(m, k, n, n_out), dtype=torch.uint8, device=dev)
-    xq = torch.empty((m, k), dtype=torch.int8, device=dev)
-    sx = torch.empty(m, dtype=torch.float32, device=dev)
-    xo = torch.empty((m, n_out), dtype=torch.bfloat16, device=dev)
-    import ctypes
-    cidx = (ctypes.c_int32 * n_out)(*idx)
-    L = qg.lib()
-
-    def full():
-        L.qg_qgemm_w8a8_outlier(ctypes.c_void_p(xp.data_ptr()), m, k, cidx, n_out, ctypes.c_void_p(wq.data_ptr()),
-                                ctypes.c_void_p(s_w.data_ptr()), ctypes.c_void_p(w_out.data_ptr()), n,
-                                ctypes.c_void_p(yp.data_ptr()), None, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
-                                ctypes.c_void_p(cur_stream()))
-
-    def split_only():
-        L.qg_quantize_absmax_split(ctypes.c_void_p(xp.data_ptr()), m, k, cidx, n_out, ctypes.c_void_p(xq.data_ptr()),
-                                   ctypes.c_void_p(sx.data_ptr()), ctypes.c_void_p(xo.data_ptr()),
-                                   ctypes.c_void_p(cur_stream()))
+    full, split_only, dims, gemm_bytes = build_prefill(torch, qg, synth, dev, cur_stream)
+    m, k, n, n_out = dims["m"], dims["k"], dims["n"], dims["n_out"]
     tf = Timed(torch, [full] * 20)
     tf.run(2)
     sec_full = tf.run(10) / 20
     ts = Timed(torch, [split_only] * 20)
     ts.run(2)
     sec_split = ts.run(10) / 20
-    sec_gemm = max(sec_full - sec_split, 1e-9)
+    tg = Timed(torch, [dims["gemm_only"]] * 20)  # on the split outputs left by the runs above
+    tg.run(2)
+    sec_gemm = tg.run(10) / 20
     int8_ops = 2.0 * m * n * (k - n_out)
     bf16_ops = 2.0 * m * n * n_out
     tops = int8_ops / sec_gemm / 1e12
@@ -364,14 +535,40 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
         "metric": "int8 TOPS of the W8A8 GEMM (2*M*N*(K-n_out) int8 ops / GEMM time)",
         "shape": "M=2048 K=4096 N=4096 n_out=20",
         "gemm_us": round(sec_gemm * 1e6, 2), "split_us": round(sec_split * 1e6, 2),
+        "timing": "HIP-graph replays of 20 launches each, HIP events on the replay stream: "
+                  "qg_qgemm_w8a8 (GEMM kernel alone), qg_quantize_absmax_split, qg_qgemm_w8a8_outlier (both)",
         "call_us": round(sec_full * 1e6, 2), "int8_TOPS": round(tops, 1),
         "mfma_frac": round(tops / INT8_MFMA_PEAK_TOPS, 4),
         "call_TOPS": round((int8_ops + bf16_ops) / sec_full / 1e12, 1),
         "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": INT8_MFMA_PEAK_TOPS, "unit": "TFLOP/s",
-                     "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4), "traffic": None},
+                     "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4), "traffic": recorded_traffic("qgemm"),
+                     "algorithmic_bytes_per_launch": gemm_bytes},
+        "vendor_int8_gemm_us": vendor_int8_gemm_us(torch, dims["xq"], dims["wq"]),
+        "vendor_note": "torch._int_mm (vendor BLAS) on the same int8 operands: int32 product only, "
+                       "no rescale or outlier path; context, not a target",
     }
     log("prefill: gemm %.1f us (%.0f TOPS), split %.1f us" % (sec_gemm * 1e6, tops, sec_split * 1e6))
     return out
+
+
+def vendor_int8_gemm_us(torch, xq, wq):
+    """Time of the vendor int8 GEMM (int32 out) on the same operands, or None."""
+    try:
+        b = wq.t()
+        for _ in range(3):
+            torch._int_mm(xq, b)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(50):
+            torch._int_mm(xq, b)
+        e1.record()
+        e1.synchronize()
+        return round(e0.elapsed_time(e1) * 1e3 / 50, 2)
+    except Exception as e:  # not available in this torch build
+        log("vendor int8 GEMM unavailable: %s" % e)
+        return None
 
 
 def cpu_baseline(np, synth):
@@ -393,18 +590,19 @@ def cpu_baseline(np, synth):
     done_bytes = 0
     layers = 0
     t0 = time.perf_counter()
-    while True:
+    while True:  # whole layers, until about 12 s of CPU work
         for name in plan:
             wq, s_w, xb = ops[name]
             oracle.y_w8a16(wq, s_w, xb)
             done_bytes += wq.size + 4 * s_w.size
         layers += 1
         el = time.perf_counter() - t0
-        if el > 10.0 or layers >= 32:
+        if el > 12.0:
             break
     return {"value": round(done_bytes / el / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": "%d of 32 layers of the decode step (%d projections, %.2f GB of int8 weights), "
-                      "fp64 dequantize-then-multiply, %.1f s" % (layers, 7 * layers, done_bytes / 1e9, el),
+            "sample": "%d decode layers (%d projections: 4 x 4096x4096, 2 x 11008x4096, 1 x 4096x11008 each; "
+                      "%.2f GB of int8 weights), fp64 dequantize-then-multiply, %.1f s" %
+                      (layers, 7 * layers, done_bytes / 1e9, el),
             "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
 
 

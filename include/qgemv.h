@@ -77,6 +77,9 @@ typedef int32_t qg_status;
 #define QG_MAX_OUTLIERS 256     /* n_out of the outlier split                     */
 #define QG_QGEMV_MAX_K  32768   /* k of qg_qgemv (bounded by the on-chip activation staging)  */
 #define QG_MAX_GROUP    8       /* matrices per qg_qgemv_grouped launch              */
+#define QG_OUT_LD_ALIGN 8       /* row stride (elements) of the outlier operands the
+                                   prefill GEMMs read: a multiple of 8 bf16 = 16 B    */
+#define QG_MAX_OUT_LD   65536   /* largest row stride of an outlier operand          */
 
 /* Human-readable text for a status code (static storage). */
 const char* qg_status_str(qg_status s);
@@ -110,28 +113,36 @@ qg_status qg_quantize_absmax(const void* x, int32_t xt, int64_t rows, int64_t co
  *   s[m]  = fl32(127 / max_{k not in idx} |x[m][k]|)  (1 when that max is 0);
  *   q[m][k] = clip(rne(fl32(x[m][k] * s[m])), -127, 127) for k not in idx,
  *             0 for k in idx;
- *   x_out[m][j] = x[m][idx[j]]  (bf16, copied bit for bit).
+ *   x_out[m][j] = x[m][idx[j]]  (bf16, copied bit for bit), j < n_out;
+ *   x_out[m][j] = 0 for n_out <= j < x_out_ld (padding).
  * x      : [rows][cols] bf16, 16-B aligned.
  * idx    : HOST array of n_out int32, strictly increasing, in [0, cols)
  *          (QG_ERR_ARG otherwise); n_out in [0, QG_MAX_OUTLIERS]; may be NULL
  *          when n_out = 0.
  * q      : [rows][cols] int8 (out), 16-B aligned.  s: [rows] fp32 (out).
- * x_out  : [rows][n_out] bf16 (out); may be NULL when n_out = 0.
+ * x_out  : [rows][x_out_ld] bf16 (out), n_out <= x_out_ld <= QG_MAX_OUT_LD;
+ *          not touched (may be NULL) when n_out = 0.  A stride that is a
+ *          multiple of QG_OUT_LD_ALIGN (and a 16-B aligned x_out) is what
+ *          qg_qgemm_w8a8 reads.
  * cols % 8 == 0; cols <= 262144.
  */
 qg_status qg_quantize_absmax_split(const void* x, int64_t rows, int64_t cols,
                                    const int32_t* idx, int32_t n_out,
-                                   int8_t* q, float* s, void* x_out, void* stream);
+                                   int8_t* q, float* s, void* x_out, int32_t x_out_ld,
+                                   void* stream);
 
 /*
  * Gather the outlier channels' weights in high precision:
- * w_out[n][j] = bf16_rne(w[n][idx[j]]) ([SEP] section 2.2, high-precision path).
+ * w_out[n][j] = bf16_rne(w[n][idx[j]]) ([SEP] section 2.2, high-precision path),
+ * j < n_out; w_out[n][j] = 0 for n_out <= j < w_out_ld (padding).
  * w      : [n][k] fp32.   idx: HOST array as in qg_quantize_absmax_split.
- * w_out  : [n][n_out] bf16 (out).
+ * w_out  : [n][w_out_ld] bf16 (out), n_out <= w_out_ld <= QG_MAX_OUT_LD; not
+ *          touched (may be NULL) when n_out = 0.  The prefill GEMMs read a
+ *          stride that is a multiple of QG_OUT_LD_ALIGN.
  */
 qg_status qg_gather_columns_bf16(const float* w, int64_t n, int64_t k,
                                  const int32_t* idx, int32_t n_out,
-                                 void* w_out, void* stream);
+                                 void* w_out, int32_t w_out_ld, void* stream);
 
 /*
  * Ternary (BitNet b1.58) absmean quantization of a whole tensor ([VG]
@@ -254,17 +265,42 @@ qg_status qg_qgemv_grouped(const qg_weight* w, int32_t count, int32_t amode, con
  *             + sum_j x_out[m][j] * w_out[n][j]      (fp32).
  * x      : [m][k] bf16.   idx: HOST int32 list as in qg_quantize_absmax_split.
  * wq     : [n][k] int8 (per-row absmax codes of W, from qg_quantize_absmax).
- * s_w    : [n] fp32.      w_out: [n][n_out] bf16 (qg_gather_columns_bf16).
+ * s_w    : [n] fp32.
+ * w_out  : [n][w_out_ld] bf16 (qg_gather_columns_bf16), 16-B aligned;
+ *          w_out_ld a multiple of QG_OUT_LD_ALIGN, n_out <= w_out_ld <=
+ *          QG_MAX_OUT_LD; columns >= n_out are never read.  Ignored (may be
+ *          NULL) when n_out = 0.
  * y      : [m][n] fp32 (out).   acc_out: [m][n] int32 (out) or NULL.
- * ws     : qg_qgemm_workspace_bytes(m, k, n, n_out) bytes, 16-B aligned.
- * k % 128 == 0, k <= 262144; m, n >= 1.
+ * ws     : qg_qgemm_workspace_bytes(m, k, n_out) bytes, 16-B aligned: the
+ *          call's scratch for (xq, s_x, x_out); its contents on entry do not
+ *          matter and are overwritten.
+ * k % 128 == 0, k <= 262144; 1 <= m, n < 2^31; m * k and n * k <= 2^40.
  */
-size_t qg_qgemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int32_t n_out);
+size_t qg_qgemm_workspace_bytes(int64_t m, int64_t k, int32_t n_out);  /* 0 if out of range */
 qg_status qg_qgemm_w8a8_outlier(const void* x, int64_t m, int64_t k,
                                 const int32_t* idx, int32_t n_out,
-                                const int8_t* wq, const float* s_w, const void* w_out,
+                                const int8_t* wq, const float* s_w,
+                                const void* w_out, int32_t w_out_ld,
                                 int64_t n, float* y, int32_t* acc_out,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The GEMM half of qg_qgemm_w8a8_outlier on activations that are already
+ * split, e.g. one qg_quantize_absmax_split output shared by several
+ * projections of the same tokens (q, k, v; gate, up).  Same definition and
+ * bit-identical results:
+ *   y[m][n] = acc[m][n] / (s_x[m] * s_w[n]) + sum_{j<n_out} x_out[m][j] * w_out[n][j].
+ * xq     : [m][k] int8, 16-B aligned.  s_x: [m] fp32.
+ * x_out  : [m][x_out_ld] bf16, 16-B aligned; x_out_ld a multiple of
+ *          QG_OUT_LD_ALIGN, n_out <= x_out_ld <= QG_MAX_OUT_LD; columns >= n_out
+ *          are never read.  Ignored (may be NULL) when n_out = 0.
+ * wq, s_w, w_out, w_out_ld, n, y, acc_out, shape limits: as
+ * qg_qgemm_w8a8_outlier; 0 <= n_out <= QG_MAX_OUTLIERS.
+ */
+qg_status qg_qgemm_w8a8(const int8_t* xq, const float* s_x, const void* x_out, int32_t x_out_ld,
+                        int64_t m, int64_t k, int32_t n_out,
+                        const int8_t* wq, const float* s_w, const void* w_out, int32_t w_out_ld,
+                        int64_t n, float* y, int32_t* acc_out, void* stream);
 
 #ifdef __cplusplus
 }

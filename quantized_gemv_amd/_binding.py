@@ -26,6 +26,8 @@ QG_ACT_INT8, QG_ACT_FLOAT = 0, 1
 QG_MAX_OUTLIERS = 256
 QG_QGEMV_MAX_K = 32768
 QG_MAX_GROUP = 8
+QG_OUT_LD_ALIGN = 8
+QG_MAX_OUT_LD = 65536
 
 _c_i32, _c_i64, _c_sz, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
@@ -46,8 +48,9 @@ _SIGS = {
     "qg_abi_version": (_c_i32, []),
     "qg_quantize_absmax_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i32]),
     "qg_quantize_absmax": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
-    "qg_quantize_absmax_split": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp]),
-    "qg_gather_columns_bf16": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_vp, _c_vp]),
+    "qg_quantize_absmax_split": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32,
+                                          _c_vp]),
+    "qg_gather_columns_bf16": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp]),
     "qg_ternary_workspace_bytes": (_c_sz, [_c_i64, _c_i64]),
     "qg_quantize_ternary": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "qg_split_sign_residual": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
@@ -56,9 +59,11 @@ _SIGS = {
     "qg_qgemv": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp]),
     "qg_qgemv_grouped": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_i32, _c_vp, _c_i32, ctypes.POINTER(_c_vp),
                                   _c_i32, ctypes.POINTER(_c_vp), _c_vp]),
-    "qg_qgemm_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i32]),
-    "qg_qgemm_w8a8_outlier": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i64,
+    "qg_qgemm_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i32]),
+    "qg_qgemm_w8a8_outlier": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, _c_i64,
                                        _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "qg_qgemm_w8a8": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32,
+                               _c_i64, _c_vp, _c_vp, _c_vp]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -138,27 +143,37 @@ def quantize_absmax(x: torch.Tensor, per_row: bool = True, q: torch.Tensor = Non
     return q, s
 
 
-def quantize_absmax_split(x: torch.Tensor, idx: Sequence[int]):
+def out_ld(n_out: int) -> int:
+    """Row stride of an outlier operand the prefill GEMMs read: n_out rounded
+    up to QG_OUT_LD_ALIGN elements."""
+    return -(-n_out // QG_OUT_LD_ALIGN) * QG_OUT_LD_ALIGN
+
+
+def quantize_absmax_split(x: torch.Tensor, idx: Sequence[int], ld: Optional[int] = None):
     """Per-token int8 quantization with outlier channels split out
-    (qg_quantize_absmax_split). Returns (q, s, x_out)."""
+    (qg_quantize_absmax_split). Returns (q, s, x_out) with x_out [rows][ld]
+    (ld defaults to out_ld(n_out); columns >= n_out are zero)."""
     _dev(x, "x", torch.bfloat16)
     rows, cols = x.shape
     cidx, n_out = _idx_host(idx)
+    ld = out_ld(n_out) if ld is None else ld
     q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
     s = torch.empty(rows, dtype=torch.float32, device=x.device)
-    xo = torch.empty((rows, n_out), dtype=torch.bfloat16, device=x.device)
+    xo = torch.empty((rows, ld), dtype=torch.bfloat16, device=x.device)
     _check(lib().qg_quantize_absmax_split(_p(x), rows, cols, cidx, n_out, _p(q), _p(s), _p(xo) if n_out else None,
-                                          _stream(x)), "qg_quantize_absmax_split")
+                                          ld, _stream(x)), "qg_quantize_absmax_split")
     return q, s, xo
 
 
-def gather_columns_bf16(w: torch.Tensor, idx: Sequence[int]):
-    """W_out[n][j] = bf16(W[n][idx[j]]) (qg_gather_columns_bf16)."""
+def gather_columns_bf16(w: torch.Tensor, idx: Sequence[int], ld: Optional[int] = None):
+    """W_out[n][j] = bf16(W[n][idx[j]]) (qg_gather_columns_bf16), as [n][ld]
+    (ld defaults to out_ld(n_out); columns >= n_out are zero)."""
     _dev(w, "w", torch.float32)
     n, k = w.shape
     cidx, n_out = _idx_host(idx)
-    wo = torch.empty((n, n_out), dtype=torch.bfloat16, device=w.device)
-    _check(lib().qg_gather_columns_bf16(_p(w), n, k, cidx, n_out, _p(wo) if n_out else None, _stream(w)),
+    ld = out_ld(n_out) if ld is None else ld
+    wo = torch.empty((n, ld), dtype=torch.bfloat16, device=w.device)
+    _check(lib().qg_gather_columns_bf16(_p(w), n, k, cidx, n_out, _p(wo) if n_out else None, ld, _stream(w)),
            "qg_gather_columns_bf16")
     return wo
 
@@ -294,13 +309,41 @@ def qgemm_w8a8_outlier(x: torch.Tensor, idx: Sequence[int], wq: torch.Tensor, s_
     m, k = x.shape
     n = wq.shape[0]
     cidx, n_out = _idx_host(idx)
+    w_ld = 0
     if n_out:
         _dev(w_out, "w_out", torch.bfloat16)
+        w_ld = w_out.shape[1]
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=x.device)
-    nws = lib().qg_qgemm_workspace_bytes(m, k, n, n_out)
+    nws = lib().qg_qgemm_workspace_bytes(m, k, n_out)
     if ws is None:
         ws = torch.empty(nws, dtype=torch.uint8, device=x.device)
-    _check(lib().qg_qgemm_w8a8_outlier(_p(x), m, k, cidx, n_out, _p(wq), _p(s_w), _p(w_out) if n_out else None, n,
-                                       _p(y), _p(acc_out), _p(ws), ws.numel(), _stream(x)), "qg_qgemm_w8a8_outlier")
+    _check(lib().qg_qgemm_w8a8_outlier(_p(x), m, k, cidx, n_out, _p(wq), _p(s_w), _p(w_out) if n_out else None, w_ld,
+                                       n, _p(y), _p(acc_out), _p(ws), ws.numel(), _stream(x)), "qg_qgemm_w8a8_outlier")
+    return y
+
+
+def qgemm_w8a8(xq: torch.Tensor, s_x: torch.Tensor, x_out: Optional[torch.Tensor], wq: torch.Tensor,
+               s_w: torch.Tensor, w_out: Optional[torch.Tensor], n_out: int, y: torch.Tensor = None,
+               acc_out: torch.Tensor = None):
+    """The GEMM half of the prefill on already split activations (qg_qgemm_w8a8):
+    xq [m][k] int8, s_x [m], x_out [m][x_ld] bf16 and w_out [n][w_ld] bf16 (as
+    quantize_absmax_split / gather_columns_bf16 return them), n_out outlier
+    channels. Returns y [m][n] fp32."""
+    _dev(xq, "xq", torch.int8)
+    _dev(s_x, "s_x", torch.float32)
+    _dev(wq, "wq", torch.int8)
+    _dev(s_w, "s_w", torch.float32)
+    m, k = xq.shape
+    n = wq.shape[0]
+    x_ld = w_ld = 0
+    if n_out:
+        _dev(x_out, "x_out", torch.bfloat16)
+        _dev(w_out, "w_out", torch.bfloat16)
+        x_ld, w_ld = x_out.shape[1], w_out.shape[1]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
+    _check(lib().qg_qgemm_w8a8(_p(xq), _p(s_x), _p(x_out) if n_out else None, x_ld, m, k, n_out, _p(wq), _p(s_w),
+                               _p(w_out) if n_out else None, w_ld, n, _p(y), _p(acc_out), _stream(xq)),
+           "qg_qgemm_w8a8")
     return y

@@ -27,19 +27,36 @@ qg_status check_idx(const int32_t* idx, int32_t n_out, int64_t cols, qg::Outlier
     return QG_OK;
 }
 
-size_t qgemm_layout(int64_t m, int64_t k, int64_t n, int32_t n_out, size_t* off_sx, size_t* off_xo, size_t* off_wp,
-                    int* ld) {
-    const int l = n_out > 0 ? (int)align_up((size_t)n_out, 16) : 0;
+// Workspace of the prefill call: the split activations xq [m][k] int8 |
+// s_x [m] fp32 | x_out [m][ld] bf16 with ld = n_out rounded up to
+// QG_OUT_LD_ALIGN, each part 256-B aligned.
+int out_ld(int32_t n_out) { return (int)align_up((size_t)n_out, QG_OUT_LD_ALIGN); }
+size_t qgemm_layout(int64_t m, int64_t k, int32_t n_out, size_t* off_sx, size_t* off_xo) {
     const size_t xq = (size_t)m * (size_t)k;
     const size_t sx = align_up(xq, 256);
     const size_t xo = align_up(sx + (size_t)m * sizeof(float), 256);
-    const size_t wp = align_up(xo + (size_t)m * (size_t)l * 2, 256);
-    const size_t total = align_up(wp + (size_t)n * (size_t)l * 2, 256);
+    const size_t total = align_up(xo + (size_t)m * (size_t)out_ld(n_out) * 2, 256);
     if (off_sx) *off_sx = sx;
     if (off_xo) *off_xo = xo;
-    if (off_wp) *off_wp = wp;
-    if (ld) *ld = l;
     return total;
+}
+
+// An outlier operand the GEMM reads: [rows][ld] bf16, 16-B aligned rows.
+qg_status check_out_operand(const void* p, int32_t ld, int32_t n_out) {
+    if (n_out == 0) return QG_OK;
+    if (!p) return QG_ERR_NULLPTR;
+    if (ld < n_out || ld > QG_MAX_OUT_LD || ld % QG_OUT_LD_ALIGN != 0) return QG_ERR_SHAPE;
+    if (!aligned16(p)) return QG_ERR_ALIGN;
+    return QG_OK;
+}
+
+// Sizes the prefill GEMM supports: K in whole 128-column steps, indices of
+// the [m][k] / [n][k] operands within 2^40 elements, m and n below 2^31.
+qg_status check_gemm_shape(int64_t m, int64_t k, int64_t n) {
+    if (m < 1 || n < 1 || m >= ((int64_t)1 << 31) || n >= ((int64_t)1 << 31)) return QG_ERR_SHAPE;
+    if (k < 128 || k % 128 != 0 || k > 262144) return QG_ERR_SHAPE;
+    if (m > ((int64_t)1 << 40) / k || n > ((int64_t)1 << 40) / k) return QG_ERR_SHAPE;
+    return QG_OK;
 }
 
 }  // namespace
@@ -59,7 +76,7 @@ const char* qg_status_str(qg_status s) {
     }
 }
 
-int32_t qg_abi_version(void) { return 10000; }
+int32_t qg_abi_version(void) { return 20000; }
 
 size_t qg_quantize_absmax_workspace_bytes(int64_t rows, int64_t cols, int32_t gran) {
     if (gran != QG_PER_TENSOR || rows < 1 || cols < 8) return 0;
@@ -81,28 +98,31 @@ qg_status qg_quantize_absmax(const void* x, int32_t xt, int64_t rows, int64_t co
 }
 
 qg_status qg_quantize_absmax_split(const void* x, int64_t rows, int64_t cols, const int32_t* idx, int32_t n_out,
-                                   int8_t* q, float* s, void* x_out, void* stream) {
+                                   int8_t* q, float* s, void* x_out, int32_t x_out_ld, void* stream) {
     if (!x || !q || !s) return QG_ERR_NULLPTR;
     if (n_out > 0 && !x_out) return QG_ERR_NULLPTR;
     if (rows < 1 || cols < 8 || cols % 8 != 0 || cols > 262144 || rows > ((int64_t)1 << 40) / cols)
         return QG_ERR_SHAPE;
+    if (n_out > 0 && (x_out_ld < n_out || x_out_ld > QG_MAX_OUT_LD)) return QG_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(q)) return QG_ERR_ALIGN;
     qg::OutlierIdx oi;
     const qg_status st = check_idx(idx, n_out, cols, &oi);
     if (st != QG_OK) return st;
     return from_hip(qg::launch_absmax_split(static_cast<const uint16_t*>(x), rows, cols, oi, n_out, q, s,
-                                            static_cast<uint16_t*>(x_out), n_out, as_stream(stream)));
+                                            static_cast<uint16_t*>(x_out), n_out > 0 ? x_out_ld : 0,
+                                            as_stream(stream)));
 }
 
 qg_status qg_gather_columns_bf16(const float* w, int64_t n, int64_t k, const int32_t* idx, int32_t n_out,
-                                 void* w_out, void* stream) {
+                                 void* w_out, int32_t w_out_ld, void* stream) {
     if (!w) return QG_ERR_NULLPTR;
     if (n_out > 0 && !w_out) return QG_ERR_NULLPTR;
     if (n < 1 || k < 1) return QG_ERR_SHAPE;
+    if (n_out > 0 && (w_out_ld < n_out || w_out_ld > QG_MAX_OUT_LD)) return QG_ERR_SHAPE;
     qg::OutlierIdx oi;
     const qg_status st = check_idx(idx, n_out, k, &oi);
     if (st != QG_OK) return st;
-    return from_hip(qg::launch_gather_cols_bf16(w, n, k, oi, n_out, static_cast<uint16_t*>(w_out),
+    return from_hip(qg::launch_gather_cols_bf16(w, n, k, oi, n_out, static_cast<uint16_t*>(w_out), w_out_ld,
                                                 as_stream(stream)));
 }
 
@@ -217,46 +237,80 @@ qg_status qg_qgemv_grouped(const qg_weight* w, int32_t count, int32_t amode, con
     return from_hip(qg::launch_qgemv_group(a, count, as_stream(stream)));
 }
 
-size_t qg_qgemm_workspace_bytes(int64_t m, int64_t k, int64_t n, int32_t n_out) {
-    if (m < 1 || k < 1 || n < 1 || n_out < 0 || n_out > QG_MAX_OUTLIERS) return 0;
-    return qgemm_layout(m, k, n, n_out, nullptr, nullptr, nullptr, nullptr);
+size_t qg_qgemm_workspace_bytes(int64_t m, int64_t k, int32_t n_out) {
+    if (m < 1 || k < 1 || n_out < 0 || n_out > QG_MAX_OUTLIERS) return 0;
+    if (m > ((int64_t)1 << 40) / k) return 0;
+    return qgemm_layout(m, k, n_out, nullptr, nullptr);
 }
 
-qg_status qg_qgemm_w8a8_outlier(const void* x, int64_t m, int64_t k, const int32_t* idx, int32_t n_out,
-                                const int8_t* wq, const float* s_w, const void* w_out, int64_t n, float* y,
-                                int32_t* acc_out, void* ws, size_t ws_bytes, void* stream) {
-    if (!x || !wq || !s_w || !y) return QG_ERR_NULLPTR;
-    if (n_out > 0 && !w_out) return QG_ERR_NULLPTR;
-    if (m < 1 || n < 1 || m >= ((int64_t)1 << 31) || n >= ((int64_t)1 << 31)) return QG_ERR_SHAPE;
-    if (k < 128 || k % 128 != 0 || k > 262144) return QG_ERR_SHAPE;
-    if (m > ((int64_t)1 << 40) / k || n > ((int64_t)1 << 40) / k) return QG_ERR_SHAPE;
-    if (!aligned16(x) || !aligned16(wq)) return QG_ERR_ALIGN;
-    qg::OutlierIdx oi;
-    const qg_status st = check_idx(idx, n_out, k, &oi);
+qg_status qg_qgemm_w8a8(const int8_t* xq, const float* s_x, const void* x_out, int32_t x_out_ld, int64_t m,
+                        int64_t k, int32_t n_out, const int8_t* wq, const float* s_w, const void* w_out,
+                        int32_t w_out_ld, int64_t n, float* y, int32_t* acc_out, void* stream) {
+    if (!xq || !s_x || !wq || !s_w || !y) return QG_ERR_NULLPTR;
+    if (n_out < 0 || n_out > QG_MAX_OUTLIERS) return QG_ERR_ARG;
+    qg_status st = check_gemm_shape(m, k, n);
     if (st != QG_OK) return st;
-    size_t off_sx = 0, off_xo = 0, off_wp = 0;
-    int ld = 0;
-    const size_t need = qgemm_layout(m, k, n, n_out, &off_sx, &off_xo, &off_wp, &ld);
-    if (!ws || ws_bytes < need) return QG_ERR_WORKSPACE;
-    if (!aligned16(ws)) return QG_ERR_ALIGN;
-    uint8_t* base = static_cast<uint8_t*>(ws);
+    if ((st = check_out_operand(x_out, x_out_ld, n_out)) != QG_OK) return st;
+    if ((st = check_out_operand(w_out, w_out_ld, n_out)) != QG_OK) return st;
+    if (!aligned16(xq) || !aligned16(wq)) return QG_ERR_ALIGN;
     qg::QgemmArgs a;
-    a.x = static_cast<const uint16_t*>(x);
     a.m = m;
     a.k = k;
     a.n = n;
+    a.xq = xq;
+    a.s_x = s_x;
+    a.x_out = static_cast<const uint16_t*>(x_out);
+    a.x_out_ld = x_out_ld;
     a.wq = wq;
     a.s_w = s_w;
     a.w_out = static_cast<const uint16_t*>(w_out);
+    a.w_out_ld = w_out_ld;
     a.n_out = n_out;
     a.y = y;
     a.acc_out = acc_out;
-    a.xq = reinterpret_cast<int8_t*>(base);
-    a.s_x = reinterpret_cast<float*>(base + off_sx);
-    a.x_out = reinterpret_cast<uint16_t*>(base + off_xo);
+    return from_hip(qg::launch_qgemm(a, as_stream(stream)));
+}
+
+qg_status qg_qgemm_w8a8_outlier(const void* x, int64_t m, int64_t k, const int32_t* idx, int32_t n_out,
+                                const int8_t* wq, const float* s_w, const void* w_out, int32_t w_out_ld, int64_t n,
+                                float* y, int32_t* acc_out, void* ws, size_t ws_bytes, void* stream) {
+    if (!x || !wq || !s_w || !y) return QG_ERR_NULLPTR;
+    if (n_out < 0 || n_out > QG_MAX_OUTLIERS) return QG_ERR_ARG;
+    qg_status st = check_gemm_shape(m, k, n);
+    if (st != QG_OK) return st;
+    if ((st = check_out_operand(w_out, w_out_ld, n_out)) != QG_OK) return st;
+    if (!aligned16(x) || !aligned16(wq)) return QG_ERR_ALIGN;
+    qg::OutlierIdx oi;
+    st = check_idx(idx, n_out, k, &oi);
+    if (st != QG_OK) return st;
+    size_t off_sx = 0, off_xo = 0;
+    const size_t need = qgemm_layout(m, k, n_out, &off_sx, &off_xo);
+    if (!ws || ws_bytes < need) return QG_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QG_ERR_ALIGN;
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    int8_t* xq = reinterpret_cast<int8_t*>(base);
+    float* s_x = reinterpret_cast<float*>(base + off_sx);
+    uint16_t* x_out = reinterpret_cast<uint16_t*>(base + off_xo);
+    const int ld = out_ld(n_out);
+    hipError_t e = qg::launch_absmax_split(static_cast<const uint16_t*>(x), m, k, oi, n_out, xq, s_x, x_out, ld,
+                                           as_stream(stream));
+    if (e != hipSuccess) return QG_ERR_HIP;
+    qg::QgemmArgs a;
+    a.m = m;
+    a.k = k;
+    a.n = n;
+    a.xq = xq;
+    a.s_x = s_x;
+    a.x_out = x_out;
     a.x_out_ld = ld;
-    a.w_pad = reinterpret_cast<uint16_t*>(base + off_wp);
-    return from_hip(qg::launch_qgemm(a, oi, as_stream(stream)));
+    a.wq = wq;
+    a.s_w = s_w;
+    a.w_out = static_cast<const uint16_t*>(w_out);
+    a.w_out_ld = w_out_ld;
+    a.n_out = n_out;
+    a.y = y;
+    a.acc_out = acc_out;
+    return from_hip(qg::launch_qgemm(a, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -20,10 +20,9 @@ int absmax_tensor_parts(int64_t elems);
 hipError_t launch_absmax_tensor(const void* x, int xt, int64_t elems, int8_t* q, float* s, float* partial,
                                 hipStream_t st);
 hipError_t launch_absmax_split(const uint16_t* x, int64_t rows, int64_t cols, const OutlierIdx& idx, int n_out,
-                               int8_t* q, float* s, uint16_t* x_out, int x_out_ld, hipStream_t st,
-                               const uint16_t* w_out = nullptr, int64_t w_rows = 0, uint16_t* w_pad = nullptr);
+                               int8_t* q, float* s, uint16_t* x_out, int x_out_ld, hipStream_t st);
 hipError_t launch_gather_cols_bf16(const float* w, int64_t n, int64_t k, const OutlierIdx& idx, int n_out,
-                                   uint16_t* w_out, hipStream_t st);
+                                   uint16_t* w_out, int w_out_ld, hipStream_t st);
 hipError_t launch_ternary(const float* w, int64_t count, int8_t* q, float* gamma, uint64_t* hist, hipStream_t st);
 hipError_t launch_split_sign_residual(const float* w, int64_t n, int64_t k, int8_t* sign, float* alpha, int8_t* rq,
                                       float* s_r, hipStream_t st);
@@ -45,23 +44,23 @@ hipError_t launch_qgemv(const QgemvArgs& a, hipStream_t st);
 constexpr int kMaxGroupLaunch = 8;
 hipError_t launch_qgemv_group(const QgemvArgs* a, int count, hipStream_t st);
 
+// The W8A8 GEMM over split activations (xq, s_x, x_out [m][x_out_ld]);
+// outlier operand strides are multiples of 8 elements, rows 16-B aligned.
 struct QgemmArgs {
-    const uint16_t* x;
     int64_t m, k, n;
+    const int8_t* xq;
+    const float* s_x;
+    const uint16_t* x_out;
+    int x_out_ld;
     const int8_t* wq;
     const float* s_w;
     const uint16_t* w_out;
+    int w_out_ld;
     int n_out;
     float* y;
     int32_t* acc_out;
-    // workspace views
-    int8_t* xq;
-    float* s_x;
-    uint16_t* x_out;
-    int x_out_ld;
-    uint16_t* w_pad;  // [n][x_out_ld] zero-padded copy of w_out
 };
-hipError_t launch_qgemm(const QgemmArgs& a, const OutlierIdx& idx, hipStream_t st);
+hipError_t launch_qgemm(const QgemmArgs& a, hipStream_t st);
 
 int device_cu_count();
 

@@ -42,11 +42,11 @@ struct GemmParams {
     const int8_t* wq;       // [N][K]
     const float* s_x;       // [M]
     const float* s_w;       // [N]
-    const uint16_t* x_out;  // [M][ld] bf16, zero beyond n_out
-    const uint16_t* w_pad;  // [N][ld] bf16, zero beyond n_out
+    const uint16_t* x_out;  // [M][x_ld] bf16, x_ld % 8 == 0 (columns < n_out are used)
+    const uint16_t* w_out;  // [N][w_ld] bf16, w_ld % 8 == 0 (columns < n_out are used)
     float* y;               // [M][N]
     int32_t* acc_out;       // [M][N] or null
-    int M, N, K, n_out, ld;
+    int M, N, K, n_out, x_ld, w_ld;
     int tiles_m, tiles_n;
 };
 
@@ -230,17 +230,36 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void qgemm_w8a8_kernel(Gemm
             for (int b = 0; b < WTN; ++b) f[a][b][r] = (float)acc[a][b][r] * isx * inv_sw[b];
         }
     }
-    // Outlier channels: bf16 MFMA over the zero-padded gathered activations
-    // and weights (both [rows][ld]), K = 16 per instruction, added on top.
-    for (int kb = 0; kb < p.ld; kb += 16) {
+    // Outlier channels: bf16 MFMA over the gathered activations [M][x_ld] and
+    // the outlier weights [N][w_ld], K = 16 per instruction, added on top.
+    // Rows are 16-B aligned (strides are multiples of 8 elements), so each
+    // fragment is one 16-byte load; lanes whose 8 columns start at or past
+    // the stride load nothing, and columns >= n_out are zeroed in registers
+    // (the padding of the operands is never trusted).
+    auto frag8 = [&](const uint16_t* row, int ld, int kc) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (kc < ld) v = *reinterpret_cast<const uint4*>(row + kc);
+        const int live = p.n_out - kc;  // columns of this fragment that are real
+        if (live < 8) {
+            uint32_t h[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (2 * e >= live) h[e] = 0u;
+                else if (2 * e + 1 >= live) h[e] &= 0xFFFFu;
+            }
+            v = make_uint4(h[0], h[1], h[2], h[3]);
+        }
+        return v;
+    };
+    for (int kb = 0; kb < p.n_out; kb += 16) {
         const int kc = kb + (lane >> 5) * 8;
         uint4 xa[WTM], wb[WTN];
 #pragma unroll
         for (int a = 0; a < WTM; ++a)
-            xa[a] = *reinterpret_cast<const uint4*>(p.x_out + (int64_t)min(wr0 + a * 32 + (lane & 31), p.M - 1) * p.ld + kc);
+            xa[a] = frag8(p.x_out + (int64_t)min(wr0 + a * 32 + (lane & 31), p.M - 1) * p.x_ld, p.x_ld, kc);
 #pragma unroll
         for (int b = 0; b < WTN; ++b)
-            wb[b] = *reinterpret_cast<const uint4*>(p.w_pad + (int64_t)min(wc0 + b * 32 + (lane & 31), p.N - 1) * p.ld + kc);
+            wb[b] = frag8(p.w_out + (int64_t)min(wc0 + b * 32 + (lane & 31), p.N - 1) * p.w_ld, p.w_ld, kc);
 #pragma unroll
         for (int a = 0; a < WTM; ++a)
 #pragma unroll
@@ -285,25 +304,22 @@ static hipError_t run_gemm(const GemmParams& p0, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_qgemm(const QgemmArgs& a, const OutlierIdx& idx, hipStream_t st) {
-    // the split kernel also pads the outlier weights into the workspace
-    hipError_t e = launch_absmax_split(a.x, a.m, a.k, idx, a.n_out, a.xq, a.s_x, a.x_out, a.x_out_ld, st, a.w_out,
-                                       a.n, a.w_pad);
-    if (e != hipSuccess) return e;
+hipError_t launch_qgemm(const QgemmArgs& a, hipStream_t st) {
     GemmParams p;
     p.xq = a.xq;
     p.wq = a.wq;
     p.s_x = a.s_x;
     p.s_w = a.s_w;
     p.x_out = a.x_out;
-    p.w_pad = a.w_pad;
+    p.w_out = a.w_out;
     p.y = a.y;
     p.acc_out = a.acc_out;
     p.M = (int)a.m;
     p.N = (int)a.n;
     p.K = (int)a.k;
     p.n_out = a.n_out;
-    p.ld = a.x_out_ld;
+    p.x_ld = a.x_out_ld;
+    p.w_ld = a.w_out_ld;
     // 8 waves of 64 x 64 in a 256 x 128 tile, K steps of 128, 3 stages
     // (fastest of the configurations measured on MI355X at 2048 x 4096 x 4096)
     return run_gemm<4, 2, 2, 2, 128, 3>(p, st);

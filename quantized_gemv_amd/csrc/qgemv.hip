@@ -6,19 +6,24 @@
 // every CU and to keep the per-byte ALU work well under the VALU budget.
 //
 // Layout of the work
-//   * grid: about one 256-thread workgroup per CU, each owning a contiguous
-//     block of rows;
-//   * the activation vector is staged once per workgroup in LDS, in the form
-//     the inner loop wants (fp32; int8 codes quantized in-kernel; int8 codes
-//     permuted to the ternary unpack order; bf16 pairs for the sign path),
-//     zero-padded so ragged K needs no branches;
+//   * grid: about one 512-thread workgroup (8 waves, 2 per SIMD) per CU, each
+//     owning a contiguous block of rows; a grouped launch covers several
+//     matrices that share x (q, k, v or gate, up) with workgroups handed out
+//     in proportion to their rows;
 //   * each wave takes groups of U rows; an "item" is U rows x JS chunk
 //     columns per lane; items are double-buffered in registers so the next
 //     item's loads are in flight while the current one is reduced;
+//   * the activation vector: for int8 weights with bf16 / fp32 x, every item
+//     loads its own 16-activation slice next to its weights (x is L2
+//     resident; no LDS and no barrier); the other formats stage x once per
+//     workgroup in LDS in the form the inner loop wants (int8 codes quantized
+//     in-kernel; codes permuted to the ternary unpack order; bf16 pairs for
+//     the sign path), zero-padded so ragged K needs no branches;
 //   * weights are read through buffer resources: out-of-range lanes (ragged
 //     rows or chunks) get zeros from the hardware range check;
-//   * per-row partial sums are reduced across the wave with lane shuffles and
-//     lane 0 applies the per-row scale and stores.
+//   * per-row partial sums are reduced across the wave with DPP row / bank
+//     moves, and lane 63, which ends up with the sums, applies the per-row
+//     scale and stores.
 //
 // Formats (codes as stored by the library's packing):
 //   INT8 (x float) : 16 B chunk = 16 int8 weights; v_cvt_f32_i32 (SDWA byte

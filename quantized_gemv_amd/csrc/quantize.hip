@@ -102,104 +102,122 @@ __global__ __launch_bounds__(kThreads) void absmax_apply_kernel(const void* x, i
 }
 
 // ---------------------------------------------------------------- outlier split
-// One workgroup per token row.  The outlier channel set is a bitmap in LDS
-// built from the (host-validated, sorted) index list passed by value.  For
-// rows of up to NP * 2048 columns each thread keeps its share of the row in
-// registers between the max pass and the quantize pass (one HBM read);
-// longer rows re-read the row from cache for the second pass (NP = 0).
+// One workgroup per token row (grid-stride when there are more rows than
+// workgroups).  The outlier channel set is a bitmap in LDS built from the
+// host-validated, sorted index list passed by value.  Everything a row needs
+// from memory -- its values and its outlier activations -- is requested
+// before the bitmap is built (those barriers wait for LDS traffic only), so a
+// row costs one memory round trip.  Rows of up to NP * 2048 columns stay in
+// registers between the max pass and the quantize pass; longer rows (NP = 0)
+// are read again, from cache, for the second pass.
+// n_out <= kThreads (at most 256 outliers): thread j handles outlier j.
+static_assert(kThreads <= kMaxOutliers, "every thread reads one entry of the index list");
 template <int NP>
 __global__ __launch_bounds__(kThreads) void absmax_split_kernel(const uint16_t* x, int64_t rows, int64_t cols,
                                                                  OutlierIdx idx, int n_out, int8_t* q, float* s,
-                                                                 uint16_t* x_out, int x_out_ld, const uint16_t* w_out,
-                                                                 int64_t w_rows, uint16_t* w_pad) {
-    extern __shared__ uint32_t bitmap[];  // cols / 32 words
+                                                                 uint16_t* x_out, int x_out_ld) {
+    extern __shared__ uint32_t bitmap[];  // ceil(cols / 32) words
     __shared__ float red[kWaves];
-    const int nwords = (int)(cols / 32);
-    for (int i = threadIdx.x; i < nwords; i += kThreads) bitmap[i] = 0u;
-    __syncthreads();
-    for (int j = threadIdx.x; j < n_out; j += kThreads) {
-        const int c = idx.v[j];
-        atomicOr(&bitmap[c >> 5], 1u << (c & 31));
-    }
-    __syncthreads();
+    const int nwords = (int)((cols + 31) / 32);
     const int64_t c8 = cols / 8;
-    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const int tid = threadIdx.x;
+    // this thread's outlier channel (n_out <= kThreads), requested before the
+    // row so that the gather below waits for it alone (loads retire in order)
+    const int c_raw = idx.v[tid];
+    __builtin_amdgcn_sched_barrier(0);
+    const int my_c = (tid < n_out) ? c_raw : 0;
+    // Row loads go through a buffer resource over the row: offsets past its
+    // end read zeros, so every load is issued unconditionally (a branch
+    // around a load makes the compiler wait for all loads at the join).
+    const uint32_t row_bytes = (uint32_t)(cols * 2);
+    u32x4 keep[NP > 0 ? NP : 1];
+    uint16_t gath = 0;  // this thread's outlier activation (tid < n_out)
+    auto fetch = [&](int64_t row) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(x + row * cols, row_bytes);
+        if constexpr (NP > 0) {
+#pragma unroll
+            for (int t = 0; t < NP; ++t) {
+                const int64_t i = tid + (int64_t)kThreads * t;
+                keep[t] = load16(rs, (i < c8) ? (uint32_t)(i * 16) : row_bytes);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // the row loads go out before the gather waits for its index
+        gath = load2(rs, (tid < n_out) ? (uint32_t)(2 * my_c) : row_bytes);
+    };
+    int64_t r = blockIdx.x;  // < rows: the grid never exceeds the row count
+    fetch(r);
+    for (int i = tid; i < nwords; i += kThreads) bitmap[i] = 0u;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (tid < n_out) atomicOr(&bitmap[my_c >> 5], 1u << (my_c & 31));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    auto unpack8 = [](u32x4 h, float v[8]) {
+        const uint32_t w[4] = {h[0], h[1], h[2], h[3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[2 * e] = bf16_to_f32(w[e] & 0xFFFFu);
+            v[2 * e + 1] = bf16_to_f32(w[e] >> 16);
+        }
+    };
+    // bit j set: column 8 i + j is not an outlier
+    auto inliers = [&](int64_t i) { return ~(bitmap[(i * 8) >> 5] >> ((i * 8) & 31)) & 0xFFu; };
+    for (; r < rows; r += gridDim.x) {
         const uint16_t* xr = x + r * cols;
         float m = 0.0f;
-        auto unpack8 = [](uint4 h, float v[8]) {
-            const uint32_t w[4] = {h.x, h.y, h.z, h.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[2 * e] = bf16_to_f32(w[e] & 0xFFFFu);
-                v[2 * e + 1] = bf16_to_f32(w[e] >> 16);
-            }
-        };
-        auto inliers = [&](int64_t i) { return ~(bitmap[(i * 8) >> 5] >> ((i * 8) & 31)) & 0xFFu; };
-        auto piece_max = [&](int64_t i, uint4 h) {
+        auto piece_max = [&](int64_t i, u32x4 h) {
             float v[8];
             unpack8(h, v);
-            const uint32_t keep_bits = inliers(i);
+            const uint32_t in = inliers(i);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                if ((keep_bits >> j) & 1u) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
+                if ((in >> j) & 1u) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
         };
-        auto piece_quant = [&](int64_t i, uint4 h, float sc) {
+        auto piece_quant = [&](int64_t i, u32x4 h, float sc) {
             float v[8];
             int c[8];
             unpack8(h, v);
-            const uint32_t keep_bits = inliers(i);
+            const uint32_t in = inliers(i);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) c[j] = ((keep_bits >> j) & 1u) ? qcode(v[j], sc) : 0;
+            for (int j = 0; j < 8; ++j) c[j] = ((in >> j) & 1u) ? qcode(v[j], sc) : 0;
             store8_codes(q, r * cols + i * 8, c);
         };
+        float sc;
         if constexpr (NP > 0) {
-            uint4 keep[NP];
 #pragma unroll
             for (int t = 0; t < NP; ++t) {
-                const int64_t i = threadIdx.x + (int64_t)kThreads * t;
-                keep[t] = (i < c8) ? *reinterpret_cast<const uint4*>(xr + i * 8) : make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int t = 0; t < NP; ++t) {
-                const int64_t i = threadIdx.x + (int64_t)kThreads * t;
+                const int64_t i = tid + (int64_t)kThreads * t;
                 if (i < c8) piece_max(i, keep[t]);
             }
-            const float sc = absmax_scale(block_max(m, red));
-            if (threadIdx.x == 0) s[r] = sc;
+            sc = absmax_scale(block_max(m, red));
 #pragma unroll
             for (int t = 0; t < NP; ++t) {
-                const int64_t i = threadIdx.x + (int64_t)kThreads * t;
+                const int64_t i = tid + (int64_t)kThreads * t;
                 if (i < c8) piece_quant(i, keep[t], sc);
             }
         } else {
-            for (int64_t i = threadIdx.x; i < c8; i += kThreads)
-                piece_max(i, *reinterpret_cast<const uint4*>(xr + i * 8));
-            const float sc = absmax_scale(block_max(m, red));
-            if (threadIdx.x == 0) s[r] = sc;
-            for (int64_t i = threadIdx.x; i < c8; i += kThreads)
-                piece_quant(i, *reinterpret_cast<const uint4*>(xr + i * 8), sc);
+            for (int64_t i = tid; i < c8; i += kThreads) piece_max(i, *reinterpret_cast<const u32x4*>(xr + i * 8));
+            sc = absmax_scale(block_max(m, red));
+            for (int64_t i = tid; i < c8; i += kThreads)
+                piece_quant(i, *reinterpret_cast<const u32x4*>(xr + i * 8), sc);
         }
+        if (tid == 0) s[r] = sc;
         // gathered outlier activations, zero-padded up to the row stride
-        for (int j = threadIdx.x; j < x_out_ld; j += kThreads)
-            x_out[r * x_out_ld + j] = (j < n_out) ? xr[idx.v[j]] : (uint16_t)0;
-    }
-    // optional: copy the outlier weights [w_rows][n_out] into a zero-padded
-    // [w_rows][x_out_ld] layout, so the GEMM epilogue reads them as vectors
-    if (w_pad) {
-        for (int64_t r = blockIdx.x; r < w_rows; r += gridDim.x)
-            for (int j = threadIdx.x; j < x_out_ld; j += kThreads)
-                w_pad[r * x_out_ld + j] = (j < n_out) ? w_out[r * n_out + j] : (uint16_t)0;
+        if (n_out > 0)
+            for (int j = tid; j < x_out_ld; j += kThreads) x_out[r * x_out_ld + j] = (j < n_out) ? gath : (uint16_t)0;
+        if (r + gridDim.x < rows) fetch(r + gridDim.x);
     }
 }
 
 // ---------------------------------------------------------------- outlier weight gather
+// w_out [n][ld]: column j < n_out holds bf16(w[r][idx[j]]), the rest zero.
 __global__ __launch_bounds__(kThreads) void gather_cols_bf16_kernel(const float* w, int64_t n, int64_t k,
-                                                                     OutlierIdx idx, int n_out, uint16_t* w_out) {
-    const int64_t total = n * n_out;
+                                                                     OutlierIdx idx, int n_out, uint16_t* w_out,
+                                                                     int ld) {
+    const int64_t total = n * ld;
     for (int64_t t = blockIdx.x * (int64_t)kThreads + threadIdx.x; t < total; t += (int64_t)gridDim.x * kThreads) {
-        const int64_t r = t / n_out;
-        const int j = (int)(t - r * n_out);
-        w_out[t] = (uint16_t)f32_to_bf16(w[r * k + idx.v[j]]);
+        const int64_t r = t / ld;
+        const int j = (int)(t - r * ld);
+        w_out[t] = (j < n_out) ? (uint16_t)f32_to_bf16(w[r * k + idx.v[j]]) : (uint16_t)0;
     }
 }
 
@@ -350,31 +368,26 @@ hipError_t launch_absmax_tensor(const void* x, int xt, int64_t elems, int8_t* q,
 }
 
 hipError_t launch_absmax_split(const uint16_t* x, int64_t rows, int64_t cols, const OutlierIdx& idx, int n_out,
-                               int8_t* q, float* s, uint16_t* x_out, int x_out_ld, hipStream_t st,
-                               const uint16_t* w_out, int64_t w_rows, uint16_t* w_pad) {
+                               int8_t* q, float* s, uint16_t* x_out, int x_out_ld, hipStream_t st) {
     const int g = grid_for(rows, 1, 65535);
-    const size_t lds = (size_t)(cols / 32) * sizeof(uint32_t);
+    const size_t lds = (size_t)((cols + 31) / 32) * sizeof(uint32_t);
     const int64_t per_thread = (cols / 8 + kThreads - 1) / kThreads;  // 16-byte pieces per thread
     if (per_thread <= 1)
-        absmax_split_kernel<1><<<g, kThreads, lds, st>>>(x, rows, cols, idx, n_out, q, s, x_out, x_out_ld, w_out,
-                                                         w_rows, w_pad);
+        absmax_split_kernel<1><<<g, kThreads, lds, st>>>(x, rows, cols, idx, n_out, q, s, x_out, x_out_ld);
     else if (per_thread <= 2)
-        absmax_split_kernel<2><<<g, kThreads, lds, st>>>(x, rows, cols, idx, n_out, q, s, x_out, x_out_ld, w_out,
-                                                         w_rows, w_pad);
+        absmax_split_kernel<2><<<g, kThreads, lds, st>>>(x, rows, cols, idx, n_out, q, s, x_out, x_out_ld);
     else if (per_thread <= 4)
-        absmax_split_kernel<4><<<g, kThreads, lds, st>>>(x, rows, cols, idx, n_out, q, s, x_out, x_out_ld, w_out,
-                                                         w_rows, w_pad);
+        absmax_split_kernel<4><<<g, kThreads, lds, st>>>(x, rows, cols, idx, n_out, q, s, x_out, x_out_ld);
     else
-        absmax_split_kernel<0><<<g, kThreads, lds, st>>>(x, rows, cols, idx, n_out, q, s, x_out, x_out_ld, w_out,
-                                                         w_rows, w_pad);
+        absmax_split_kernel<0><<<g, kThreads, lds, st>>>(x, rows, cols, idx, n_out, q, s, x_out, x_out_ld);
     return hipGetLastError();
 }
 
 hipError_t launch_gather_cols_bf16(const float* w, int64_t n, int64_t k, const OutlierIdx& idx, int n_out,
-                                   uint16_t* w_out, hipStream_t st) {
+                                   uint16_t* w_out, int w_out_ld, hipStream_t st) {
     if (n_out == 0) return hipSuccess;
-    const int g = grid_for(n * n_out, kThreads, 65535);
-    gather_cols_bf16_kernel<<<g, kThreads, 0, st>>>(w, n, k, idx, n_out, w_out);
+    const int g = grid_for(n * w_out_ld, kThreads, 65535);
+    gather_cols_bf16_kernel<<<g, kThreads, 0, st>>>(w, n, k, idx, n_out, w_out, w_out_ld);
     return hipGetLastError();
 }
 

@@ -48,7 +48,7 @@ def test_header_symbols_exported(qg):
     for name in decl:
         assert hasattr(l, name), name
     assert set(decl) == set(qg.EXPORTED)
-    assert qg.lib().qg_abi_version() == 10000
+    assert qg.lib().qg_abi_version() == 20000
     for st in range(0, 8):
         assert qg.status_str(st)
 
@@ -80,20 +80,25 @@ def test_validation_split_and_gather(qg):
     dup = (ctypes.c_int32 * 3)(1, 1, 9)
     oob = (ctypes.c_int32 * 3)(1, 5, 64)
     neg = (ctypes.c_int32 * 3)(-1, 5, 9)
-    assert f(A, 2, 64, unsorted, 3, A, A, A, None) == 4
-    assert f(A, 2, 64, dup, 3, A, A, A, None) == 4
-    assert f(A, 2, 64, oob, 3, A, A, A, None) == 4
-    assert f(A, 2, 64, neg, 3, A, A, A, None) == 4
-    assert f(A, 2, 64, good, 3, A, A, None, None) == 1
-    assert f(A, 2, 64, None, 3, A, A, A, None) == 1
-    assert f(A, 2, 64, good, 257, A, A, A, None) == 4
-    assert f(A, 2, 63, good, 3, A, A, A, None) == 2
-    assert f(A, 2, 8 * 40000, good, 3, A, A, A, None) == 2
-    assert f(U, 2, 64, good, 3, A, A, A, None) == 3
+    # (x, rows, cols, idx, n_out, q, s, x_out, x_out_ld, stream)
+    assert f(A, 2, 64, unsorted, 3, A, A, A, 8, None) == 4
+    assert f(A, 2, 64, dup, 3, A, A, A, 8, None) == 4
+    assert f(A, 2, 64, oob, 3, A, A, A, 8, None) == 4
+    assert f(A, 2, 64, neg, 3, A, A, A, 8, None) == 4
+    assert f(A, 2, 64, good, 3, A, A, None, 8, None) == 1
+    assert f(A, 2, 64, None, 3, A, A, A, 8, None) == 1
+    assert f(A, 2, 64, good, 257, A, A, A, 300, None) == 4
+    assert f(A, 2, 63, good, 3, A, A, A, 8, None) == 2
+    assert f(A, 2, 8 * 40000, good, 3, A, A, A, 8, None) == 2
+    assert f(A, 2, 64, good, 3, A, A, A, 2, None) == 2           # stride below n_out
+    assert f(A, 2, 64, good, 3, A, A, A, 65537, None) == 2       # stride above QG_MAX_OUT_LD
+    assert f(U, 2, 64, good, 3, A, A, A, 8, None) == 3
     g = l.qg_gather_columns_bf16
-    assert g(A, 4, 64, oob, 3, A, None) == 4
-    assert g(A, 4, 64, good, 3, None, None) == 1
-    assert g(None, 4, 64, good, 3, A, None) == 1
+    # (w, n, k, idx, n_out, w_out, w_out_ld, stream)
+    assert g(A, 4, 64, oob, 3, A, 8, None) == 4
+    assert g(A, 4, 64, good, 3, None, 8, None) == 1
+    assert g(None, 4, 64, good, 3, A, 8, None) == 1
+    assert g(A, 4, 64, good, 3, A, 2, None) == 2
 
 
 def test_validation_ternary_split_pack(qg):
@@ -175,17 +180,21 @@ def test_validation_qgemm(qg):
     l = qg.lib()
     f = l.qg_qgemm_w8a8_outlier
     idx = (ctypes.c_int32 * 2)(3, 7)
-    need = l.qg_qgemm_workspace_bytes(16, 256, 32, 2)
-    assert need >= 16 * 256 + 16 * 4 + 16 * 16 * 2
-    assert l.qg_qgemm_workspace_bytes(16, 256, 32, 300) == 0
-    assert f(A, 16, 256, idx, 2, A, A, A, 32, A, None, A, need, None) != 5 or True  # not executed: no GPU
-    assert f(A, 16, 256, idx, 2, A, A, A, 32, A, None, A, need - 1, None) == 5
-    assert f(A, 16, 256, idx, 2, A, A, None, 32, A, None, A, need, None) == 1
-    assert f(A, 16, 200, idx, 2, A, A, A, 32, A, None, A, need, None) == 2
-    assert f(A, 0, 256, idx, 2, A, A, A, 32, A, None, A, need, None) == 2
-    assert f(U, 16, 256, idx, 2, A, A, A, 32, A, None, A, need, None) == 3
+    need = l.qg_qgemm_workspace_bytes(16, 256, 2)
+    assert need >= 16 * 256 + 16 * 4 + 16 * 8 * 2  # xq, s_x, x_out [m][8]
+    assert l.qg_qgemm_workspace_bytes(16, 256, 300) == 0
+    assert l.qg_qgemm_workspace_bytes(0, 256, 2) == 0
+    # (x, m, k, idx, n_out, wq, s_w, w_out, w_out_ld, n, y, acc_out, ws, ws_bytes, stream)
+    assert f(A, 16, 256, idx, 2, A, A, A, 8, 32, A, None, A, need - 1, None) == 5
+    assert f(A, 16, 256, idx, 2, A, A, None, 8, 32, A, None, A, need, None) == 1
+    assert f(A, 16, 200, idx, 2, A, A, A, 8, 32, A, None, A, need, None) == 2
+    assert f(A, 0, 256, idx, 2, A, A, A, 8, 32, A, None, A, need, None) == 2
+    assert f(A, 16, 256, idx, 2, A, A, A, 2, 32, A, None, A, need, None) == 2    # w_out_ld not a multiple of 8
+    assert f(A, 16, 256, idx, 2, A, A, A, 0, 32, A, None, A, need, None) == 2    # w_out_ld below n_out
+    assert f(A, 16, 256, idx, 2, A, A, U, 8, 32, A, None, A, need, None) == 3    # w_out not 16-B aligned
+    assert f(U, 16, 256, idx, 2, A, A, A, 8, 32, A, None, A, need, None) == 3
     bad = (ctypes.c_int32 * 2)(7, 3)
-    assert f(A, 16, 256, bad, 2, A, A, A, 32, A, None, A, need, None) == 4
+    assert f(A, 16, 256, bad, 2, A, A, A, 8, 32, A, None, A, need, None) == 4
 
 
 def _run_driver(groups):
@@ -220,3 +229,34 @@ def test_library_exact_mean_matches_oracle():
     got = _run_driver(groups)
     for grp, r in zip(groups, got):
         assert r == oracle.mean_abs_f32(grp), (grp[:4], r, oracle.mean_abs_f32(grp))
+
+
+def test_validation_qgemm_presplit(qg):
+    f = qg.lib().qg_qgemm_w8a8
+    # (xq, s_x, x_out, x_out_ld, m, k, n_out, wq, s_w, w_out, w_out_ld, n, y, acc_out, stream)
+    assert f(None, A, A, 8, 16, 256, 2, A, A, A, 8, 32, A, None, None) == 1
+    assert f(A, A, None, 8, 16, 256, 2, A, A, A, 8, 32, A, None, None) == 1   # x_out needed when n_out > 0
+    assert f(A, A, A, 8, 16, 256, 2, A, A, None, 8, 32, A, None, None) == 1   # so is w_out
+    assert f(A, A, A, 0, 16, 256, 2, A, A, A, 8, 32, A, None, None) == 2      # x_out_ld < n_out
+    assert f(A, A, A, 4, 16, 256, 2, A, A, A, 8, 32, A, None, None) == 2      # x_out_ld not a multiple of 8
+    assert f(A, A, A, 8, 16, 256, 2, A, A, A, 12, 32, A, None, None) == 2     # w_out_ld not a multiple of 8
+    assert f(A, A, A, 8, 16, 200, 2, A, A, A, 8, 32, A, None, None) == 2      # k not a multiple of 128
+    assert f(A, A, A, 8, 0, 256, 2, A, A, A, 8, 32, A, None, None) == 2
+    assert f(A, A, A, 8, 16, 256, 2, A, A, A, 8, 0, A, None, None) == 2
+    assert f(A, A, A, 304, 16, 256, 300, A, A, A, 304, 32, A, None, None) == 4  # more than QG_MAX_OUTLIERS
+    assert f(A, A, A, 8, 16, 256, -1, A, A, A, 8, 32, A, None, None) == 4
+    assert f(U, A, A, 8, 16, 256, 2, A, A, A, 8, 32, A, None, None) == 3
+    assert f(A, A, A, 8, 16, 256, 2, U, A, A, 8, 32, A, None, None) == 3
+    assert f(A, A, U, 8, 16, 256, 2, A, A, A, 8, 32, A, None, None) == 3      # x_out rows must be 16-B aligned
+
+
+def test_header_constants_match_binding(qg):
+    """Every #define QG_* value in the header equals the binding's constant."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    defs = dict(re.findall(r"#define\s+(QG_[A-Z0-9_]+)\s+(-?\d+)", src))
+    assert len(defs) >= 20
+    for name, val in defs.items():
+        if name.startswith("QG_ERR_") or name == "QG_OK":
+            continue
+        assert hasattr(qg, name), name
+        assert getattr(qg, name) == int(val), name

@@ -11,6 +11,8 @@ row), and edge cases (minimum / maximum K, single rows, zero inputs).
 """
 import sys
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -77,24 +79,32 @@ def test_absmax_worked_example_on_gpu(qg):
     assert host(s)[0] == np.float32(127) / np.float32(10.8)
 
 
-@pytest.mark.parametrize("m,k,n_out", [(5, 64, 3), (64, 512, 6), (2048, 4096, 20), (3, 4096, 0), (2, 64, 64)])
+@pytest.mark.parametrize("m,k,n_out", [(5, 64, 3), (64, 512, 6), (2048, 4096, 20), (3, 4096, 0), (2, 64, 64),
+                                       (3, 40, 2),        # row length not a multiple of 32 columns
+                                       (9, 6152, 7),      # four 16-byte pieces per thread
+                                       (2, 16392, 5),     # row longer than the register window: two passes
+                                       (65537, 8, 1)])    # more rows than workgroups: grid-stride rows
 def test_outlier_split(qg, m, k, n_out):
     note("outlier split m=%d k=%d n_out=%d" % (m, k, n_out))
     wl = synth.prefill_outlier(m=m, k=k, n=8, n_out=n_out, seed=5)
     xb, idx = wl.tensors["x_bf16"], wl.tensors["idx"]
-    xq, s, xo = qg.quantize_absmax_split(dev_bf16(xb), idx.tolist())
+    xq, s, xo = qg.quantize_absmax_split(dev_bf16(xb), idx.tolist(), ld=n_out + 5)
     xq_ref, s_ref, xo_ref = oracle.outlier_split_quantize(xb, idx)
     assert np.array_equal(host(s), s_ref)
     assert np.array_equal(host(xq), xq_ref)
-    assert np.array_equal(host(xo), xo_ref)
+    if n_out:  # x_out is not touched when there are no outliers
+        xo = host(xo)
+        assert np.array_equal(xo[:, :n_out], xo_ref)
+        assert not xo[:, n_out:].any()  # the padding columns are zero
 
 
 def test_gather_columns(qg):
     note("gather outlier weights")
     wl = synth.prefill_outlier(m=4, k=4096, n=4096, n_out=20, seed=5)
     w, idx = wl.tensors["w"], wl.tensors["idx"]
-    wo = qg.gather_columns_bf16(dev(w), idx.tolist())
-    assert np.array_equal(host(wo), oracle.gather_outlier_weights(w, idx))
+    wo = host(qg.gather_columns_bf16(dev(w), idx.tolist(), ld=29))
+    assert np.array_equal(wo[:, :20], oracle.gather_outlier_weights(w, idx))
+    assert not wo[:, 20:].any()
 
 
 @pytest.mark.parametrize("n,k", [(3, 4), (64, 256), (11008, 4096)])
@@ -374,6 +384,24 @@ def _qgemm_case(qg, m, k, n, n_out, seed=5, check_acc=True):
         assert np.array_equal(host(acc), acc_ref.astype(np.int32))
     y_ref = oracle.y_prefill(acc_ref, sx_ref, sw_ref, xo_ref, wo_ref)
     assert oracle.normwise_error(host(y), y_ref) <= TOL_F32
+
+    # the GEMM alone on the split activations: the same bits as the full call
+    xq, sx, xo = qg.quantize_absmax_split(dev_bf16(xb), idx.tolist())
+    acc2 = torch.empty_like(acc) if check_acc else None
+    y2 = qg.qgemm_w8a8(xq, sx, xo, wq, s_w, w_out, n_out, acc_out=acc2)
+    assert torch.equal(y2.view(torch.int32), y.view(torch.int32))
+    if check_acc:
+        assert torch.equal(acc2, acc)
+    if n_out:
+        # wider row strides whose padding holds NaN: columns >= n_out are never used
+        def nan_padded(t, ld):
+            out = torch.full((t.shape[0], ld), 0x7FC0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+            out[:, :n_out] = t[:, :n_out]
+            return out
+        xo_pad = nan_padded(xo, qg.out_ld(n_out) + 16)
+        wo_pad = nan_padded(w_out, qg.out_ld(n_out) + 8)
+        y3 = qg.qgemm_w8a8(xq, sx, xo_pad, wq, s_w, wo_pad, n_out)
+        assert torch.equal(y3.view(torch.int32), y.view(torch.int32))
 
 
 @pytest.mark.parametrize("m,k,n,n_out", [(32, 128, 32, 0), (64, 256, 96, 5), (130, 384, 200, 16), (1, 128, 1, 1),
