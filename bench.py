@@ -49,6 +49,7 @@ KERNEL_SOURCES = {
 }
 KERNEL_NAME_KEYS = {"qgemv": "qgemv_kernel", "qgemm": "qgemm_w8a8_kernel"}
 COPY_BYTES = 256 << 20           # calibration copy: bytes read and bytes written
+COPY_REPS = 2                    # calibration copies: the first copy dispatches of the profiled run
 
 
 def parse():
@@ -239,7 +240,7 @@ def profile_workload(args):
     src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    for _ in range(2):
+    for _ in range(COPY_REPS):  # before any other copy of the process
         dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
@@ -260,24 +261,22 @@ def profile_workload(args):
     log("profile workload done")
 
 
-def _counter_means(folder, counter):
-    """{kernel name: (mean value, dispatches)} from a rocprofv3 --pmc csv folder."""
+def _counter_rows(folder, counter):
+    """[(dispatch id, kernel name, value)] of one counter from a rocprofv3
+    --pmc csv folder, in dispatch order."""
     import csv
     import glob
     files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         raise SystemExit("no *counter_collection.csv under %s" % folder)
-    acc = {}
+    rows = []
     for fn in files:
         with open(fn) as f:
             for r in csv.DictReader(f):
-                if r["Counter_Name"] != counter:
-                    continue
-                k = r["Kernel_Name"]
-                v = float(r["Counter_Value"])
-                s_, c_ = acc.get(k, (0.0, 0))
-                acc[k] = (s_ + v, c_ + 1)
-    return {k: (s_ / c_, c_) for k, (s_, c_) in acc.items()}
+                if r["Counter_Name"] == counter:
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return rows
 
 
 def summarize_counters(fetch_dir, write_dir, hashes_path):
@@ -286,30 +285,31 @@ def summarize_counters(fetch_dir, write_dir, hashes_path):
     under the source hashes of the kernels the profiled run executed."""
     with open(hashes_path) as f:
         hashes = json.load(f)
-    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
-    write = _counter_means(write_dir, "WRITE_SIZE")
+    fetch = _counter_rows(fetch_dir, "FETCH_SIZE")
+    write = _counter_rows(write_dir, "WRITE_SIZE")
 
-    def pick(d, key):
-        ks = [k for k in d if key in k]
-        if not ks:
-            raise SystemExit("no kernel matching %r in %s" % (key, sorted(d)))
-        tot = sum(d[k][0] * d[k][1] for k in ks)
-        n = sum(d[k][1] for k in ks)
-        return tot / n, n, ks
-    copy_keys = [k for k in fetch if "copy" in k.lower()]
-    if not copy_keys:
-        raise SystemExit("calibration copy kernel not found among %s" % sorted(fetch))
-    cf, cn, ck = pick(fetch, copy_keys[0])
-    cw, _, _ = pick(write, copy_keys[0])
+    def calibration(rows):
+        cps = [r for r in rows if "copyBuffer" in r[1]][:COPY_REPS]
+        if len(cps) < COPY_REPS:
+            raise SystemExit("calibration copies not found")
+        return cps[0][1], sum(v for _, _, v in cps) / len(cps)
+
+    def kernel_mean(rows, key):
+        vals = [(name, v) for _, name, v in rows if key in name]
+        if not vals:
+            raise SystemExit("no dispatch of a kernel matching %r" % key)
+        return sum(v for _, v in vals) / len(vals), len(vals), sorted({name for name, _ in vals})
+    ck, cf = calibration(fetch)
+    _, cw = calibration(write)
     f_fetch = COPY_BYTES / (cf * 1024.0)
     f_write = COPY_BYTES / (cw * 1024.0)
-    out = {"calibration": {"kernel": ck[0], "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
-                           "fetch_kib": round(cf, 1), "write_kib": round(cw, 1),
+    out = {"calibration": {"kernel": ck, "dispatches": COPY_REPS, "bytes_read": COPY_BYTES,
+                           "bytes_written": COPY_BYTES, "fetch_kib": round(cf, 1), "write_kib": round(cw, 1),
                            "fetch_scale": round(f_fetch, 4), "write_scale": round(f_write, 4)},
            "kernels": {}}
     for kern, key in KERNEL_NAME_KEYS.items():
-        fk, nf, names = pick(fetch, key)
-        wk, nw, _ = pick(write, key)
+        fk, nf, names = kernel_mean(fetch, key)
+        wk, _, _ = kernel_mean(write, key)
         hbm = fk * 1024.0 * f_fetch + wk * 1024.0 * f_write
         out["kernels"][kern] = {"src_sha256_16": hashes[kern], "dispatches": nf, "kernel_names": names,
                                 "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
