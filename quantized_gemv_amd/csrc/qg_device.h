@@ -87,6 +87,11 @@ __device__ __forceinline__ int wave_sum_to_lane63(int v) {
     return v;
 }
 
+// Workgroup barrier for LDS traffic: waits for this wave's LDS (and scalar)
+// operations only.  A fenced __syncthreads would also wait for every global
+// load in flight, i.e. for prefetched data that the barrier does not guard.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Block-wide max / sum over a workgroup of NW waves; `scratch` holds >= NW
 // elements of shared memory.  All threads receive the result.  Contains two
 // barriers, so every thread of the block must call it.
@@ -95,11 +100,11 @@ __device__ __forceinline__ float block_max(float v, float* scratch) {
     v = wave_max(v);
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     if (lane == 0) scratch[w] = v;
-    __syncthreads();
+    lds_barrier();
     float r = scratch[0];
 #pragma unroll
     for (int i = 1; i < NW; ++i) r = __builtin_fmaxf(r, scratch[i]);
-    __syncthreads();
+    lds_barrier();
     return r;
 }
 
@@ -108,11 +113,11 @@ __device__ __forceinline__ int block_sum_int(int v, int* scratch) {
     v = wave_sum(v);
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     if (lane == 0) scratch[w] = v;
-    __syncthreads();
+    lds_barrier();
     int r = 0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) r += scratch[i];
-    __syncthreads();
+    lds_barrier();
     return r;
 }
 

@@ -189,14 +189,23 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     // registers through a buffer resource (pieces past K read as zeros).
     constexpr int kElems = (XT == 0) ? 4 : 8;  // elements per 16 B piece
     const int npieces = K / kElems;
+    // (unconditional loads: pieces past K read zeros through the range check;
+    // a branch around a load would make the compiler wait for all loads at
+    // the join, the weights included)
     u32x4 xr[kXL];
+    if constexpr (F != F_INT8F) {
+        const uint32_t xend = (uint32_t)(K * (XT == 0 ? 4 : 2));
 #pragma unroll
-    for (int l = 0; l < kXL; ++l) {
-        xr[l] = u32x4{0, 0, 0, 0};
-        if (F != F_INT8F && tid + kQThreads * l < npieces) xr[l] = load16(rx, (uint32_t)(16 * (tid + kQThreads * l)));
+        for (int l = 0; l < kXL; ++l) {
+            const int pi = tid + kQThreads * l;
+            xr[l] = load16(rx, pi < npieces ? (uint32_t)(16 * pi) : xend);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // x goes out ahead of the first weights
     }
     Frag fa[U][JS], fb[U][JS];
-    if (nit > 0) issue(0, fa);
+    // unconditional, like the x loads: a wave without rows reads zeros (its
+    // offsets are out of range) and never consumes them
+    issue(0, fa);
 
     // piece -> fp32 values
     auto piece_vals = [&](const u32x4& r, float v[kElems]) {
@@ -214,11 +223,14 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     // visit every real piece of x once: f(piece index, values); pieces past
     // the register window (K > kXL * 256 pieces) are loaded here, after the
     // weights, and so wait for them
-    auto for_pieces = [&](auto&& f) {
+    // (guarded = false: the register window is visited unconditionally --
+    // its pieces past K hold zeros -- so no branch sits between the x loads
+    // and their use)
+    auto for_pieces = [&](auto&& f, bool guarded = true) {
 #pragma unroll
         for (int l = 0; l < kXL; ++l) {
             const int pi = tid + kQThreads * l;
-            if (pi < npieces) {
+            if (!guarded || pi < npieces) {
                 float v[kElems];
                 piece_vals(xr[l], v);
                 f(pi, v);
@@ -237,10 +249,12 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
         // nothing to stage: every item carries its own slice of x
     } else if constexpr (F == F_INT8I || F == F_TERN) {
         float m = 0.0f;
-        for_pieces([&](int, const float* v) {
+        for_pieces(
+            [&](int, const float* v) {
 #pragma unroll
-            for (int e = 0; e < kElems; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
-        });
+                for (int e = 0; e < kElems; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
+            },
+            false);
         sx = absmax_scale(block_max<kQWaves>(m, redf));
         for_pieces([&](int pi, const float* v) {
 #pragma unroll
@@ -270,7 +284,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
         });
         for (int i = K / 2 + tid; i < padded_cols / 2; i += kQThreads) reinterpret_cast<uint32_t*>(xs)[i] = 0u;
     }
-    if constexpr (F != F_INT8F) __syncthreads();
+    if constexpr (F != F_INT8F) lds_barrier();  // x staged; the prefetched weights stay in flight
 
     float accf[U], accf2[U];
     int acc1[U], acc4[U], acc16[U];
@@ -499,12 +513,19 @@ static hipError_t run_xy(const QgemvArgs* a, int count, hipStream_t st) {
 
 // All entries share fmt, amode, xt, yt and k (validated by the caller).
 hipError_t launch_qgemv_group(const QgemvArgs* a, int count, hipStream_t st) {
-    // Rows per group U and chunk iterations per item JS keep all 8 waves busy
-    // at the decode shapes (16-112 rows per workgroup) while holding the
-    // bytes in flight per CU near 32-64 KB (two items per wave), where HBM
-    // streaming measured fastest on MI355X.
+    // Rows per item U and chunk iterations per item JS, per format, are the
+    // fastest measured on MI355X at the decode shapes (16-112 rows per
+    // workgroup; two items in flight per wave).
     const QgemvArgs& h = a[0];
-    if (h.fmt == 0 && h.amode == 1) return run_xy<F_INT8F, 2, 4>(a, count, st);
+    if (h.fmt == 0 && h.amode == 1) {
+        // one row per item at the decode shapes (16-86 rows per workgroup);
+        // two rows per item once a workgroup owns hundreds of rows, where
+        // the longer items stream faster (measured on MI355X)
+        int64_t total_rows = 0;
+        for (int m = 0; m < count; ++m) total_rows += a[m].n;
+        if (total_rows >= (int64_t)256 * device_cu_count()) return run_xy<F_INT8F, 2, 4>(a, count, st);
+        return run_xy<F_INT8F, 1, 4>(a, count, st);
+    }
     if (h.fmt == 0 && h.amode == 0) return run_xy<F_INT8I, 2, 4>(a, count, st);
     if (h.fmt == 1) return run_xy<F_TERN, 4, 1>(a, count, st);
     if (h.yt == 0) return run<F_SR, 1, 0, 1, 2>(a, count, st);

@@ -221,7 +221,8 @@ def test_qgemv_w8a16_decode_shapes(qg, name):
     assert np.array_equal(host(y2), yb)
 
 
-@pytest.mark.parametrize("n,k", [(8, 128), (77, 1152), (11008, 4096), (33, 32768)])
+@pytest.mark.parametrize("n,k", [(8, 128), (77, 1152), (11008, 4096), (33, 32768),
+                                 (65600, 256)])  # hundreds of rows per workgroup: two-row items
 def test_qgemv_w8a16_small_and_edges(qg, n, k):
     note("qgemv w8a16 %dx%d" % (n, k))
     wl = synth.decode_w8a16(n=n, k=k, seed=21)
