@@ -31,7 +31,7 @@ from .numerics import (bf16_bits_to_f32, f32_to_bf16_bits, round_rational_to_f32
                        exact_abs_sum_units, mean_abs_f32, mean_abs_rows_f32)
 from .quant import (absmax_scale, quantize_with_scale, quantize_absmax,
                     ternary_absmean, sign_residual_split, outlier_split_quantize,
-                    gather_outlier_weights, dequantize)
+                    gather_outlier_weights, dequantize, detect_outlier_channels)
 from .packing import (pack, unpack, pack_loops, unpack_loops)
 from .products import (int_dot_exact, int_gemm_exact, int_dot_bruteforce,
                        y_w8a8, y_w8a16, y_ternary, y_sign_residual, y_prefill,

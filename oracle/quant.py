@@ -138,3 +138,23 @@ def gather_outlier_weights(w: np.ndarray, idx: np.ndarray) -> np.ndarray:
     Returns bf16 bit patterns [n][n_out]."""
     w = np.asarray(w, dtype=np.float32)
     return f32_to_bf16_bits(np.ascontiguousarray(w[:, np.asarray(idx, dtype=np.int64)]))
+
+
+def detect_outlier_channels(x_bf16_bits: np.ndarray, n_out: int) -> np.ndarray:
+    """The activation channels to split out, found once from calibration
+    activations ([SEP] section 2.2: a few channels are tens of times larger
+    than the rest; the list is found once and cached).  The pages give no
+    criterion; with a fixed budget of n_out channels the plain reading is:
+    a channel's range is its max |x| over the calibration rows, and the n_out
+    channels with the largest ranges are taken, equal ranges going to the
+    lower channel index.
+    Returns the chosen channel indices, int32, ascending."""
+    x = bf16_bits_to_f32(np.asarray(x_bf16_bits, dtype=np.uint16))
+    if x.ndim != 2:
+        raise ValueError("2-D activations expected")
+    k = x.shape[1]
+    if not 0 <= n_out <= k:
+        raise ValueError("n_out out of range")
+    rng = np.max(np.abs(x), axis=0) if x.shape[0] else np.zeros(k, np.float32)
+    order = sorted(range(k), key=lambda c: (-float(rng[c]), c))  # largest range first, then lower index
+    return np.array(sorted(order[:n_out]), dtype=np.int32)

@@ -235,3 +235,23 @@ def test_ternary_divides_rather_than_multiplying_by_reciprocal():
     assert q.tolist() == [1, 1]
     recip = np.clip(np.rint((w * (np.float32(1) / gamma)).astype(np.float32)), -1, 1)
     assert recip.tolist() == [0, 1]
+
+
+def test_detect_outlier_channels():
+    bf = synth.to_bf16_bits
+    # hand-worked: channel ranges (max |x| over rows) are 1, 5, 7, 5
+    x = bf(np.array([[1.0, -5.0, 2.0, 5.0], [0.0, 3.0, -7.0, 1.0]], np.float32))
+    assert oracle.detect_outlier_channels(x, 1).tolist() == [2]
+    assert oracle.detect_outlier_channels(x, 2).tolist() == [1, 2]      # tie 5 = 5 goes to the lower index
+    assert oracle.detect_outlier_channels(x, 3).tolist() == [1, 2, 3]
+    assert oracle.detect_outlier_channels(x, 4).tolist() == [0, 1, 2, 3]
+    assert oracle.detect_outlier_channels(x, 0).tolist() == []
+    # all ranges equal: the lowest channels
+    z = np.zeros((3, 16), np.uint16)
+    assert oracle.detect_outlier_channels(z, 5).tolist() == [0, 1, 2, 3, 4]
+    # the channels the generator scales x50 stand out by far and are found exactly
+    for (m, k, n_out, seed) in [(64, 256, 4, 5), (512, 4096, 20, 5), (8, 1024, 12, 9)]:
+        wl = synth.prefill_outlier(m=m, k=k, n=8, n_out=n_out, seed=seed)
+        got = oracle.detect_outlier_channels(wl.tensors["x_bf16"], n_out)
+        assert got.tolist() == wl.tensors["idx"].tolist()
+        assert got.dtype == np.int32
