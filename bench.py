@@ -217,7 +217,7 @@ def build_prefill(torch, qg, synth, dev, cur_stream):
         if st != 0:
             raise RuntimeError("qg_qgemm_w8a8 failed: %s" % qg.status_str(st))
     full.hold = hold
-    dims = dict(m=m, k=k, n=n, n_out=n_out, xq=xq, wq=wq, gemm_only=gemm_only)
+    dims = dict(m=m, k=k, n=n, n_out=n_out, xq=xq, wq=wq, gemm_only=gemm_only, idx=idx)
     # algorithmic HBM bytes of the GEMM kernel: int8 X and W, their scales, the
     # bf16 outlier operands (rows of ld), fp32 Y written
     gemm_bytes = m * k + n * k + 4 * (m + n) + 2 * ld * (m + n) + 4 * m * n
@@ -548,6 +548,28 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
                        "no rescale or outlier path; context, not a target",
     }
     log("prefill: gemm %.1f us (%.0f TOPS), split %.1f us" % (sec_gemm * 1e6, tops, sec_split * 1e6))
+
+    # -- outlier-channel detection on the same activations (run once, offline)
+    xp = full.hold[3]
+    idx_d = torch.empty(n_out, dtype=torch.int32, device=dev)
+    import ctypes
+    L = qg.lib()
+    ws_d = torch.empty(L.qg_detect_outliers_workspace_bytes(k), dtype=torch.uint8, device=dev)
+
+    def detect():
+        st = L.qg_detect_outliers(ctypes.c_void_p(xp.data_ptr()), m, k, n_out, ctypes.c_void_p(idx_d.data_ptr()),
+                                  ctypes.c_void_p(ws_d.data_ptr()), ws_d.numel(), ctypes.c_void_p(cur_stream()))
+        if st != 0:
+            raise RuntimeError("qg_detect_outliers failed: %s" % qg.status_str(st))
+    td = Timed(torch, [detect] * 20)
+    td.run(2)
+    sec_det = td.run(10) / 20
+    found = sorted(idx_d.cpu().tolist())
+    out["detect_outliers_2048x4096"] = {"us": round(sec_det * 1e6, 2),
+                                        "read_GBps": round(2.0 * m * k / sec_det / 1e9, 1),
+                                        "finds_planted_channels": found == sorted(dims["idx"]),
+                                        "note": "offline, once per model: per-channel ranges by row block, then a one-workgroup select"}
+    log("detect: %.1f us" % (sec_det * 1e6))
     return out
 
 

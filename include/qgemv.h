@@ -132,6 +132,28 @@ qg_status qg_quantize_absmax_split(const void* x, int64_t rows, int64_t cols,
                                    void* stream);
 
 /*
+ * Outlier-channel detection, run once on calibration activations ([SEP]
+ * section 2.2: a few channels run tens of times larger than the rest; their
+ * list is found once and cached).  The pages give no criterion; with a
+ * budget of n_out channels:
+ *   range[c] = max_m |x[m][c]|;
+ *   idx = the n_out channels with the largest range (equal ranges: the lower
+ *         channel index first), in ascending channel order -- the list that
+ *         qg_quantize_absmax_split and qg_qgemm_w8a8_outlier take (copy it to
+ *         the host).
+ * x      : [rows][cols] bf16, 16-B aligned; rows >= 1; cols % 8 == 0,
+ *          cols <= 262144.
+ * n_out  : 0 <= n_out <= min(cols, QG_MAX_OUTLIERS) (QG_ERR_ARG otherwise);
+ *          nothing is launched when 0.
+ * idx    : [n_out] int32 (out, device).
+ * ws     : qg_detect_outliers_workspace_bytes(cols) bytes, 16-B aligned
+ *          (per-channel partial ranges; contents on entry do not matter).
+ */
+size_t qg_detect_outliers_workspace_bytes(int64_t cols);
+qg_status qg_detect_outliers(const void* x, int64_t rows, int64_t cols, int32_t n_out,
+                             int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Gather the outlier channels' weights in high precision:
  * w_out[n][j] = bf16_rne(w[n][idx[j]]) ([SEP] section 2.2, high-precision path),
  * j < n_out; w_out[n][j] = 0 for n_out <= j < w_out_ld (padding).

@@ -50,6 +50,8 @@ _SIGS = {
     "qg_quantize_absmax": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "qg_quantize_absmax_split": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32,
                                           _c_vp]),
+    "qg_detect_outliers_workspace_bytes": (_c_sz, [_c_i64]),
+    "qg_detect_outliers": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_sz, _c_vp]),
     "qg_gather_columns_bf16": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp]),
     "qg_ternary_workspace_bytes": (_c_sz, [_c_i64, _c_i64]),
     "qg_quantize_ternary": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
@@ -163,6 +165,20 @@ def quantize_absmax_split(x: torch.Tensor, idx: Sequence[int], ld: Optional[int]
     _check(lib().qg_quantize_absmax_split(_p(x), rows, cols, cidx, n_out, _p(q), _p(s), _p(xo) if n_out else None,
                                           ld, _stream(x)), "qg_quantize_absmax_split")
     return q, s, xo
+
+
+def detect_outliers(x: torch.Tensor, n_out: int, ws: torch.Tensor = None) -> torch.Tensor:
+    """The n_out channels of calibration activations x [rows][cols] (bf16)
+    with the largest max |x| (qg_detect_outliers). Returns int32 [n_out] on
+    the device, ascending."""
+    _dev(x, "x", torch.bfloat16)
+    rows, cols = x.shape
+    idx = torch.empty(n_out, dtype=torch.int32, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(1, lib().qg_detect_outliers_workspace_bytes(cols)), dtype=torch.uint8, device=x.device)
+    _check(lib().qg_detect_outliers(_p(x), rows, cols, n_out, _p(idx) if n_out else None, _p(ws), ws.numel(),
+                                    _stream(x)), "qg_detect_outliers")
+    return idx
 
 
 def gather_columns_bf16(w: torch.Tensor, idx: Sequence[int], ld: Optional[int] = None):

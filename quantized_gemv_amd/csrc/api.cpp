@@ -113,6 +113,26 @@ qg_status qg_quantize_absmax_split(const void* x, int64_t rows, int64_t cols, co
                                             as_stream(stream)));
 }
 
+size_t qg_detect_outliers_workspace_bytes(int64_t cols) {
+    if (cols < 1 || cols > 262144) return 0;
+    return (size_t)qg::detect_row_blocks(cols) * (size_t)cols * sizeof(uint32_t);
+}
+
+qg_status qg_detect_outliers(const void* x, int64_t rows, int64_t cols, int32_t n_out, int32_t* idx, void* ws,
+                             size_t ws_bytes, void* stream) {
+    if (!x) return QG_ERR_NULLPTR;
+    if (rows < 1 || cols < 8 || cols % 8 != 0 || cols > 262144 || rows > ((int64_t)1 << 40) / cols)
+        return QG_ERR_SHAPE;
+    if (n_out < 0 || n_out > QG_MAX_OUTLIERS || n_out > cols) return QG_ERR_ARG;
+    if (n_out == 0) return QG_OK;
+    if (!idx) return QG_ERR_NULLPTR;
+    if (!aligned16(x)) return QG_ERR_ALIGN;
+    if (!ws || ws_bytes < qg_detect_outliers_workspace_bytes(cols)) return QG_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QG_ERR_ALIGN;
+    return from_hip(qg::launch_detect_outliers(static_cast<const uint16_t*>(x), rows, cols, n_out, idx,
+                                               static_cast<uint32_t*>(ws), as_stream(stream)));
+}
+
 qg_status qg_gather_columns_bf16(const float* w, int64_t n, int64_t k, const int32_t* idx, int32_t n_out,
                                  void* w_out, int32_t w_out_ld, void* stream) {
     if (!w) return QG_ERR_NULLPTR;

@@ -21,6 +21,15 @@ hipError_t launch_absmax_tensor(const void* x, int xt, int64_t elems, int8_t* q,
                                 hipStream_t st);
 hipError_t launch_absmax_split(const uint16_t* x, int64_t rows, int64_t cols, const OutlierIdx& idx, int n_out,
                                int8_t* q, float* s, uint16_t* x_out, int x_out_ld, hipStream_t st);
+// Row blocks of the detection's range pass (a function of cols only, so the
+// workspace size is too): about 1024 workgroups, at most 64 row blocks.
+inline int detect_row_blocks(int64_t cols) {
+    const int64_t gx = (cols / 8 + 255) / 256;
+    int64_t gy = (1024 + gx - 1) / gx;
+    return (int)(gy < 1 ? 1 : gy > 64 ? 64 : gy);
+}
+hipError_t launch_detect_outliers(const uint16_t* x, int64_t rows, int64_t cols, int n_out, int32_t* idx,
+                                  uint32_t* partial, hipStream_t st);
 hipError_t launch_gather_cols_bf16(const float* w, int64_t n, int64_t k, const OutlierIdx& idx, int n_out,
                                    uint16_t* w_out, int w_out_ld, hipStream_t st);
 hipError_t launch_ternary(const float* w, int64_t count, int8_t* q, float* gamma, uint64_t* hist, hipStream_t st);

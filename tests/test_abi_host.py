@@ -260,3 +260,24 @@ def test_header_constants_match_binding(qg):
             continue
         assert hasattr(qg, name), name
         assert getattr(qg, name) == int(val), name
+
+
+def test_validation_detect_outliers(qg):
+    l = qg.lib()
+    f = l.qg_detect_outliers
+    need = l.qg_detect_outliers_workspace_bytes(64)
+    assert need >= 64 * 4 and need % (64 * 4) == 0  # partial ranges of whole row blocks
+    assert l.qg_detect_outliers_workspace_bytes(0) == 0
+    # (x, rows, cols, n_out, idx, ws, ws_bytes, stream)
+    assert f(None, 4, 64, 3, A, A, need, None) == 1
+    assert f(A, 4, 64, 3, None, A, need, None) == 1
+    assert f(A, 0, 64, 3, A, A, need, None) == 2
+    assert f(A, 4, 60, 3, A, A, need, None) == 2          # cols not a multiple of 8
+    assert f(A, 4, 64, 65, A, A, need, None) == 4         # more than cols
+    assert f(A, 4, 512, 257, A, A, 2048, None) == 4       # more than QG_MAX_OUTLIERS
+    assert f(A, 4, 64, -1, A, A, need, None) == 4
+    assert f(U, 4, 64, 3, A, A, need, None) == 3
+    assert f(A, 4, 64, 3, A, A, need - 1, None) == 5
+    assert f(A, 4, 64, 3, A, None, need, None) == 5
+    assert f(A, 4, 64, 3, A, A + 4, need, None) == 3     # workspace not 16-B aligned
+    assert f(A, 4, 64, 0, None, None, 0, None) == 0       # nothing to find: no launch

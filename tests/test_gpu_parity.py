@@ -98,6 +98,27 @@ def test_outlier_split(qg, m, k, n_out):
         assert not xo[:, n_out:].any()  # the padding columns are zero
 
 
+@pytest.mark.parametrize("m,k,n_out,kind", [(2048, 4096, 20, "planted"), (64, 256, 4, "planted"),
+                                            (7, 520, 37, "ties"), (5, 64, 64, "gauss"), (300, 1024, 256, "ties"),
+                                            (3, 8, 1, "gauss"), (9, 128, 5, "zero"), (5000, 64, 17, "gauss"),
+                                            (2, 262144, 256, "gauss"), (4, 96, 0, "gauss")])
+def test_detect_outliers(qg, m, k, n_out, kind):
+    note("detect outliers m=%d k=%d n_out=%d %s" % (m, k, n_out, kind))
+    if kind == "planted":
+        xb = synth.prefill_outlier(m=m, k=k, n=8, n_out=n_out, seed=5).tensors["x_bf16"]
+    else:
+        g = synth.rng(11)
+        if kind == "gauss":
+            x = synth.gaussian(g, (m, k), 1.0)
+        elif kind == "ties":  # few distinct magnitudes: many equal ranges
+            x = g.integers(-4, 5, (m, k)).astype(np.float32)
+        else:
+            x = np.zeros((m, k), np.float32)
+        xb = synth.to_bf16_bits(x)
+    idx = qg.detect_outliers(dev_bf16(xb), n_out)
+    assert np.array_equal(host(idx), oracle.detect_outlier_channels(xb, n_out))
+
+
 def test_gather_columns(qg):
     note("gather outlier weights")
     wl = synth.prefill_outlier(m=4, k=4096, n=4096, n_out=20, seed=5)
