@@ -53,43 +53,31 @@ def group_params(w_group: np.ndarray):
 
 
 def quantize_q4k(w: np.ndarray):
-    """Two-level quantization of W [N][K] (K % 256 == 0).
+    """Two-level quantization of W [N][K] (K % 256 == 0), every group at once
+    (the same fp32 operations as group_params and the readings above).
     Returns (codes uint8 [N][K] in 0..15, sc uint8 [N][K/32] in 0..63,
     m int8 [N][K/32] in -31..31, d fp16 [N][K/256], dmin fp16 [N][K/256])."""
     w = np.asarray(w, dtype=np.float32)
     n, k = w.shape
     if k % SUPER:
         raise ValueError("K must be a multiple of 256")
-    ns = k // SUPER
-    codes = np.zeros((n, k), np.uint8)
-    sc = np.zeros((n, k // GROUP), np.uint8)
-    mm = np.zeros((n, k // GROUP), np.int8)
-    d = np.zeros((n, ns), np.float16)
-    dmin = np.zeros((n, ns), np.float16)
-    for r in range(n):
-        for b in range(ns):
-            blk = w[r, b * SUPER:(b + 1) * SUPER]
-            params = [group_params(blk[j * GROUP:(j + 1) * GROUP]) for j in range(GROUPS_PER_SUPER)]
-            scales = np.array([p[0] for p in params], np.float32)
-            mins = np.array([p[1] for p in params], np.float32)
-            d16 = np.float16(np.float32(np.max(scales) / np.float32(63)))
-            dm16 = np.float16(np.float32(np.max(np.abs(mins)) / np.float32(31)))
-            d[r, b], dmin[r, b] = d16, dm16
-            for j in range(GROUPS_PER_SUPER):
-                s_j = np.float32(0) if d16 == 0 else np.clip(np.rint(np.float32(scales[j] / np.float32(d16))), 0, 63)
-                m_j = np.float32(0) if dm16 == 0 else np.clip(np.rint(np.float32(mins[j] / np.float32(dm16))), -31, 31)
-                gi = b * GROUPS_PER_SUPER + j
-                sc[r, gi] = int(s_j)
-                mm[r, gi] = int(m_j)
-                S = np.float32(np.float32(d16) * np.float32(s_j))
-                M = np.float32(np.float32(dm16) * np.float32(m_j))
-                seg = blk[j * GROUP:(j + 1) * GROUP]
-                if S == 0:
-                    q = np.zeros(GROUP, np.float32)
-                else:
-                    q = np.clip(np.rint((seg - M).astype(np.float32) / S), 0, 15)
-                codes[r, b * SUPER + j * GROUP:b * SUPER + (j + 1) * GROUP] = q.astype(np.uint8)
-    return codes, sc, mm, d, dmin
+    f32 = np.float32
+    g = w.reshape(n, k // SUPER, GROUPS_PER_SUPER, GROUP)        # [row][super-block][group][32]
+    lo = g.min(axis=3)
+    hi = g.max(axis=3)
+    scale = ((hi - lo).astype(f32) / f32(15)).astype(f32)         # level 1: per group
+    d = (scale.max(axis=2) / f32(63)).astype(f32).astype(np.float16)          # level 2: per super-block
+    dmin = (np.abs(lo).max(axis=2) / f32(31)).astype(f32).astype(np.float16)
+    d32 = d.astype(f32)[..., None]
+    dm32 = dmin.astype(f32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        sc = np.where(d32 == 0, f32(0), np.clip(np.rint((scale / d32).astype(f32)), 0, 63)).astype(f32)
+        mm = np.where(dm32 == 0, f32(0), np.clip(np.rint((lo / dm32).astype(f32)), -31, 31)).astype(f32)
+        S = (d32 * sc).astype(f32)[..., None]
+        M = (dm32 * mm).astype(f32)[..., None]
+        q = np.where(S == 0, f32(0), np.clip(np.rint(((g - M).astype(f32) / S).astype(f32)), 0, 15))
+    codes = q.astype(np.uint8).reshape(n, k)
+    return (codes, sc.astype(np.uint8).reshape(n, -1), mm.astype(np.int8).reshape(n, -1), d, dmin)
 
 
 def reconstructed_params(sc, mm, d, dmin):
@@ -132,16 +120,15 @@ def pack_q4k(codes, sc, mm, d, dmin):
         raise ValueError("4-bit codes expected")
     plane = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
     ns = k // SUPER
+    fields = np.concatenate([np.asarray(sc, np.int64).reshape(n, ns, 8),
+                             np.asarray(mm, np.int64).reshape(n, ns, 8) + 32], axis=2)    # [n][ns][16]
+    if fields.min(initial=0) < 0 or fields.max(initial=0) > 63:
+        raise ValueError("6-bit field out of range")
+    bits = ((fields[..., None] >> np.arange(6)) & 1).astype(np.uint8).reshape(n, ns, 96)   # field i -> bits 6i..
     meta = np.zeros((n, ns, META_BYTES), np.uint8)
-    d_bits = np.asarray(d, np.float16).view(np.uint16)
-    dm_bits = np.asarray(dmin, np.float16).view(np.uint16)
-    for r in range(n):
-        for b in range(ns):
-            g = slice(b * GROUPS_PER_SUPER, (b + 1) * GROUPS_PER_SUPER)
-            fields = [int(v) for v in sc[r, g]] + [int(v) + 32 for v in mm[r, g]]
-            meta[r, b, :12] = np.frombuffer(pack_fields6(fields), np.uint8)
-            meta[r, b, 12:14] = np.frombuffer(int(d_bits[r, b]).to_bytes(2, "little"), np.uint8)
-            meta[r, b, 14:16] = np.frombuffer(int(dm_bits[r, b]).to_bytes(2, "little"), np.uint8)
+    meta[..., :12] = np.packbits(bits, axis=2, bitorder="little")
+    meta[..., 12:14] = np.asarray(d, np.float16).view(np.uint16)[..., None].view(np.uint8).reshape(n, ns, 2)
+    meta[..., 14:16] = np.asarray(dmin, np.float16).view(np.uint16)[..., None].view(np.uint8).reshape(n, ns, 2)
     return plane, meta
 
 
@@ -154,19 +141,13 @@ def unpack_q4k(plane, meta):
     codes[:, 0::2] = plane & 15
     codes[:, 1::2] = plane >> 4
     ns = meta.shape[1]
-    sc = np.zeros((n, ns * GROUPS_PER_SUPER), np.uint8)
-    mm = np.zeros((n, ns * GROUPS_PER_SUPER), np.int8)
-    d_bits = np.zeros((n, ns), np.uint16)
-    dm_bits = np.zeros((n, ns), np.uint16)
-    for r in range(n):
-        for b in range(ns):
-            f = unpack_fields6(meta[r, b, :12].tobytes())
-            g = slice(b * GROUPS_PER_SUPER, (b + 1) * GROUPS_PER_SUPER)
-            sc[r, g] = f[:8]
-            mm[r, g] = [v - 32 for v in f[8:]]
-            d_bits[r, b] = int.from_bytes(meta[r, b, 12:14].tobytes(), "little")
-            dm_bits[r, b] = int.from_bytes(meta[r, b, 14:16].tobytes(), "little")
-    return codes, sc, mm, d_bits.view(np.float16), dm_bits.view(np.float16)
+    bits = np.unpackbits(meta[..., :12], axis=2, bitorder="little").reshape(n, ns, 16, 6).astype(np.int64)
+    fields = (bits << np.arange(6)).sum(axis=3)
+    sc = fields[..., :8].reshape(n, -1).astype(np.uint8)
+    mm = (fields[..., 8:] - 32).reshape(n, -1).astype(np.int8)
+    d = np.ascontiguousarray(meta[..., 12:14]).view(np.uint16)[..., 0].view(np.float16)
+    dmin = np.ascontiguousarray(meta[..., 14:16]).view(np.uint16)[..., 0].view(np.float16)
+    return codes, sc, mm, d, dmin
 
 
 def y_q4k(codes, sc, mm, d, dmin, x_bf16_bits) -> np.ndarray:

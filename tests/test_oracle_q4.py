@@ -117,3 +117,28 @@ def test_product_against_exact_rationals():
         exact = sum((int(codes[r, k]) * Fraction(float(S[r, k // 32])) + Fraction(float(M[r, k // 32])))
                     * Fraction(float(x[k])) for k in range(256))
         assert abs(y[r] - float(exact)) <= 1e-12 * max(1.0, abs(float(exact)))
+
+
+def test_vectorized_forms_match_the_per_group_loops():
+    # the quantizer against group_params plus the readings, one group at a time
+    w = synth.laplace(synth.rng(13), (3, 512), 0.02)
+    w[0, :32] = 0.125
+    codes, sc, mm, d, dmin = q4.quantize_q4k(w)
+    for r in range(3):
+        for b in range(2):
+            blk = w[r, 256 * b:256 * (b + 1)]
+            params = [q4.group_params(blk[32 * j:32 * (j + 1)]) for j in range(8)]
+            d16 = np.float16(np.float32(max(p[0] for p in params) / np.float32(63)))
+            dm16 = np.float16(np.float32(max(abs(p[1]) for p in params) / np.float32(31)))
+            assert d[r, b] == d16 and dmin[r, b] == dm16
+            for j, (scale, lo) in enumerate(params):
+                s_j = 0 if d16 == 0 else int(np.clip(np.rint(np.float32(scale / np.float32(d16))), 0, 63))
+                m_j = 0 if dm16 == 0 else int(np.clip(np.rint(np.float32(lo / np.float32(dm16))), -31, 31))
+                assert sc[r, 8 * b + j] == s_j and mm[r, 8 * b + j] == m_j
+    # the packer against the field-by-field reference
+    plane, meta = q4.pack_q4k(codes, sc, mm, d, dmin)
+    for r in range(3):
+        for b in range(2):
+            f = [int(v) for v in sc[r, 8 * b:8 * b + 8]] + [int(v) + 32 for v in mm[r, 8 * b:8 * b + 8]]
+            assert meta[r, b, :12].tobytes() == q4.pack_fields6(f)
+            assert q4.unpack_fields6(meta[r, b, :12].tobytes()) == f
