@@ -488,6 +488,32 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
     del copies, cws, packed
     torch.cuda.empty_cache()
 
+    # -- group-wise 4-bit weights (two-level scales), W4A16, 11008 x 4096
+    wl = synth.q4_decode()
+    codes, meta = qg.quantize_q4k(torch.from_numpy(wl.tensors["w"]).to(dev))
+    per = codes.numel() + meta.numel()
+    copies = [qg.QWeight(qg.QG_WFMT_Q4K, 11008, 4096, codes.clone(), None, resid=meta.clone())
+              for _ in range(rotate_count(per))]
+    del codes, meta
+    xq4 = torch.from_numpy(wl.tensors["x_bf16"]).to(dev).view(torch.bfloat16)
+    yq4 = torch.empty(11008, dtype=torch.bfloat16, device=dev)
+    cws = [W.c_struct() for W in copies]
+
+    def mkq(cw):
+        def f():
+            qg.qgemv_launch_raw(cw, qg.QG_ACT_FLOAT, xq4.data_ptr(), qg.QG_BF16, yq4.data_ptr(), qg.QG_BF16,
+                                cur_stream())
+        return f
+    t = Timed(torch, [mkq(cw) for cw in cws])
+    t.run(2)
+    sec = t.run(10) / t.n
+    out["q4k_w4a16_11008x4096"] = {"us": round(sec * 1e6, 3), "weight_GBps": round(per / sec / 1e9, 1),
+                                   "hbm_frac": round(per / sec / 1e9 / HBM_PEAK_GBS, 4),
+                                   "bits_per_weight": 4.5, "rotating_copies": len(copies)}
+    log("q4k: %.2f us, %.0f GB/s" % (sec * 1e6, per / sec / 1e9))
+    del copies, cws
+    torch.cuda.empty_cache()
+
     # -- sign backbone + int8 residual, 28672 x 8192
     wl = synth.sign_residual_decode()
     wdev = torch.from_numpy(wl.tensors["w"]).to(dev)

@@ -68,6 +68,8 @@ typedef int32_t qg_status;
 #define QG_WFMT_TERNARY2   1  /* 2-bit packed ternary [n][k/4], per-tensor gamma    */
 #define QG_WFMT_SIGN1_RES8 2  /* 1-bit sign [n][k/8] + alpha[n], int8 residual      */
                               /* [n][k] + its own per-row scale s_r[n]              */
+#define QG_WFMT_Q4K        3  /* 4-bit codes [n][k/2] in groups of 32 with zero-    */
+                              /* points, two-level scales in [n][k/256][16] bytes   */
 
 /* activation modes of qg_qgemv */
 #define QG_ACT_INT8  0  /* x is quantized per tensor (absmax int8) inside the call */
@@ -200,6 +202,28 @@ qg_status qg_split_sign_residual(const float* w, int64_t n, int64_t k,
                                  void* stream);
 
 /*
+ * Group-wise 4-bit weights with zero-points and two-level scales ([VG] 'Why
+ * Q4_K splits weights into blocks', 'Q4_K uses two-level blocks', figs.
+ * 43-46).  Each row is cut along k into super-blocks of 256 = 8 groups of 32.
+ * For group j of a super-block (fp32 arithmetic in the order written, round
+ * half to even):
+ *   scale_j = (max - min) / 15, min_j = min over the group's 32 weights;
+ *   d    = fp16(max_j scale_j / 63),   sc_j = clip(rne(scale_j / d), 0, 63);
+ *   dmin = fp16(max_j |min_j| / 31),   m_j = clip(rne(min_j / dmin), -31, 31);
+ *   S_j = d * sc_j, M_j = dmin * m_j   (sc_j = 0 / m_j = 0 when d / dmin is 0);
+ *   q = clip(rne((w - M_j) / S_j), 0, 15)   (0 when S_j = 0);
+ *   w_hat = q * S_j + M_j.
+ * Storage (144 bytes per 256 weights, 4.5 bits per weight):
+ *   codes : [n][k/2] bytes, weight k of a row in byte k/2, low nibble first;
+ *   meta  : [n][k/256][16] bytes; bytes 0-11 hold sixteen 6-bit fields,
+ *           least significant first (sc_0..sc_7, then m_0+32..m_7+32); bytes
+ *           12-13 d and 14-15 dmin as little-endian fp16.
+ * w: [n][k] fp32, 16-B aligned; k % 256 == 0, k < 2^31; n * k < 2^40.
+ */
+qg_status qg_quantize_q4k(const float* w, int64_t n, int64_t k,
+                          uint8_t* codes, uint8_t* meta, void* stream);
+
+/*
  * Bit packing of low-bit codes (the storage format behind [SEP] section 3.2's
  * 0.125 byte per sign weight and [VG] 'BitNet b1.58''s log2(3) bits):
  *   bits = 2: field = q + 1 in {0, 1, 2} (q in {-1, 0, 1}), 4 per byte;
@@ -223,6 +247,9 @@ qg_status qg_unpack(const uint8_t* packed, int64_t n, int64_t k, int32_t bits,
  *   QG_WFMT_TERNARY2  : codes = packed 2-bit [n][k/4]; scale = &gamma (1 fp32)
  *   QG_WFMT_SIGN1_RES8: codes = packed 1-bit [n][k/8]; resid = int8 [n][k];
  *                       scale = alpha[n]; scale2 = s_r[n]
+ *   QG_WFMT_Q4K       : codes = 4-bit plane [n][k/2]; resid = the metadata
+ *                       plane [n][k/256][16] (as qg_quantize_q4k writes
+ *                       them); scale, scale2 unused (may be NULL)
  */
 typedef struct qg_weight {
     int32_t fmt;
@@ -253,7 +280,11 @@ typedef struct qg_weight {
  *       and residual products in one fused kernel, results added):
  *       y[n] = alpha[n] * sum_k sign[n][k] x[k] + (sum_k rq[n][k] x[k]) / s_r[n],
  *       fp32 accumulation.
- * x       : [k] of type xt (QG_F32 or QG_BF16; SIGN1_RES8 needs QG_BF16).
+ *   fmt Q4K, amode QG_ACT_FLOAT (W4A16; the codes and group parameters are
+ *       decoded in registers):
+ *       y[n] = sum_groups (S_j * sum_{k in j} q[n][k] x[k] + M_j * sum_{k in j} x[k]),
+ *       i.e. sum_k w_hat[n][k] x[k], fp32 accumulation; k % 256 == 0.
+ * x       : [k] of type xt (QG_F32 or QG_BF16; SIGN1_RES8 and Q4K need QG_BF16).
  * y       : [n] of type yt (QG_F32 or QG_BF16; bf16 is rounded to nearest even).
  * acc_out : [n] int32 raw accumulators (integer modes only); may be NULL.
  * k % 128 == 0, 128 <= k <= QG_QGEMV_MAX_K, n >= 1.

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 QG_OK = 0
 QG_F32, QG_BF16 = 0, 1
 QG_PER_TENSOR, QG_PER_ROW = 0, 1
-QG_WFMT_INT8, QG_WFMT_TERNARY2, QG_WFMT_SIGN1_RES8 = 0, 1, 2
+QG_WFMT_INT8, QG_WFMT_TERNARY2, QG_WFMT_SIGN1_RES8, QG_WFMT_Q4K = 0, 1, 2, 3
 QG_ACT_INT8, QG_ACT_FLOAT = 0, 1
 QG_MAX_OUTLIERS = 256
 QG_QGEMV_MAX_K = 32768
@@ -56,6 +56,7 @@ _SIGS = {
     "qg_ternary_workspace_bytes": (_c_sz, [_c_i64, _c_i64]),
     "qg_quantize_ternary": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "qg_split_sign_residual": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "qg_quantize_q4k": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
     "qg_pack": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp]),
     "qg_unpack": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp]),
     "qg_qgemv": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp]),
@@ -249,15 +250,27 @@ class QWeight:
     n: int
     k: int
     codes: torch.Tensor
-    scale: torch.Tensor
+    scale: Optional[torch.Tensor]
     resid: Optional[torch.Tensor] = None
     scale2: Optional[torch.Tensor] = None
 
     def c_struct(self) -> CWeight:
         return CWeight(self.fmt, 0, self.n, self.k, self.codes.data_ptr(),
                        self.resid.data_ptr() if self.resid is not None else None,
-                       self.scale.data_ptr(),
+                       self.scale.data_ptr() if self.scale is not None else None,
                        self.scale2.data_ptr() if self.scale2 is not None else None)
+
+
+def quantize_q4k(w: torch.Tensor):
+    """Group-wise 4-bit codes with two-level scales (qg_quantize_q4k).
+    Returns (codes plane uint8 [n][k/2], meta plane uint8 [n][k/256][16]);
+    QWeight(QG_WFMT_Q4K, n, k, codes, None, resid=meta) describes them."""
+    _dev(w, "w", torch.float32)
+    n, k = w.shape
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    meta = torch.empty((n, k // 256, 16), dtype=torch.uint8, device=w.device)
+    _check(lib().qg_quantize_q4k(_p(w), n, k, _p(codes), _p(meta), _stream(w)), "qg_quantize_q4k")
+    return codes, meta
 
 
 def qgemv(w: QWeight, x: torch.Tensor, act_int8: bool, y_dtype=torch.float32, y: torch.Tensor = None,

@@ -146,6 +146,14 @@ qg_status qg_gather_columns_bf16(const float* w, int64_t n, int64_t k, const int
                                                 as_stream(stream)));
 }
 
+qg_status qg_quantize_q4k(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* meta, void* stream) {
+    if (!w || !codes || !meta) return QG_ERR_NULLPTR;
+    if (n < 1 || k < 256 || k % 256 != 0 || k >= ((int64_t)1 << 31) || n > ((int64_t)1 << 40) / k)
+        return QG_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(codes) || !aligned16(meta)) return QG_ERR_ALIGN;
+    return from_hip(qg::launch_quantize_q4k(w, n, k, codes, meta, as_stream(stream)));
+}
+
 size_t qg_ternary_workspace_bytes(int64_t n, int64_t k) {
     (void)n;
     (void)k;
@@ -192,7 +200,7 @@ qg_status qg_unpack(const uint8_t* packed, int64_t n, int64_t k, int32_t bits, i
 static qg_status check_qgemv(const qg_weight* w, int32_t amode, const void* x, int32_t xt, const void* y,
                              int32_t yt, const int32_t* acc_out) {
     if (!w || !x || !y) return QG_ERR_NULLPTR;
-    if (!w->codes || !w->scale) return QG_ERR_NULLPTR;
+    if (!w->codes || (!w->scale && w->fmt != QG_WFMT_Q4K)) return QG_ERR_NULLPTR;
     if (xt != QG_F32 && xt != QG_BF16) return QG_ERR_ARG;
     if (yt != QG_F32 && yt != QG_BF16) return QG_ERR_ARG;
     if (amode != QG_ACT_INT8 && amode != QG_ACT_FLOAT) return QG_ERR_ARG;
@@ -205,13 +213,18 @@ static qg_status check_qgemv(const qg_weight* w, int32_t amode, const void* x, i
             if (amode != QG_ACT_FLOAT || xt != QG_BF16) return QG_ERR_ARG;
             if (!w->resid || !w->scale2) return QG_ERR_NULLPTR;
             break;
+        case QG_WFMT_Q4K:
+            if (amode != QG_ACT_FLOAT || xt != QG_BF16) return QG_ERR_ARG;
+            if (!w->resid) return QG_ERR_NULLPTR;
+            if (w->k % 256 != 0) return QG_ERR_SHAPE;
+            break;
         default: return QG_ERR_ARG;
     }
     if (acc_out && amode != QG_ACT_INT8) return QG_ERR_ARG;
     if (w->n < 1 || w->n >= ((int64_t)1 << 31)) return QG_ERR_SHAPE;
     if (w->k < 128 || w->k % 128 != 0 || w->k > QG_QGEMV_MAX_K) return QG_ERR_SHAPE;
     if (!aligned16(w->codes) || !aligned16(x)) return QG_ERR_ALIGN;
-    if (w->fmt == QG_WFMT_SIGN1_RES8 && !aligned16(w->resid)) return QG_ERR_ALIGN;
+    if ((w->fmt == QG_WFMT_SIGN1_RES8 || w->fmt == QG_WFMT_Q4K) && !aligned16(w->resid)) return QG_ERR_ALIGN;
     return QG_OK;
 }
 

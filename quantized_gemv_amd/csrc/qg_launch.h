@@ -35,6 +35,7 @@ hipError_t launch_gather_cols_bf16(const float* w, int64_t n, int64_t k, const O
 hipError_t launch_ternary(const float* w, int64_t count, int8_t* q, float* gamma, uint64_t* hist, hipStream_t st);
 hipError_t launch_split_sign_residual(const float* w, int64_t n, int64_t k, int8_t* sign, float* alpha, int8_t* rq,
                                       float* s_r, hipStream_t st);
+hipError_t launch_quantize_q4k(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* meta, hipStream_t st);
 hipError_t launch_pack(const int8_t* codes, int64_t count, int bits, uint8_t* packed, hipStream_t st);
 hipError_t launch_unpack(const uint8_t* packed, int64_t count, int bits, int8_t* codes, hipStream_t st);
 

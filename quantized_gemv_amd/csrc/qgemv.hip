@@ -37,12 +37,17 @@
 //                    residual becomes bf16 pairs (col j, col j+16) and the sign
 //                    bits become +-1.0 bf16 pairs with one bit-field insert;
 //                    both go through v_dot2_f32_bf16 against bf16 x pairs.
+//   Q4K            : 16 B chunk = one group of 32 4-bit codes; the chunk's
+//                    16-byte super-block record gives the group's S and M
+//                    (6-bit fields, fp16 d / dmin); sum_k q x by fp32 FMA
+//                    (v_cvt_f32_ubyte on nibble-masked dwords), then
+//                    S * that + M * sum_k x.
 #include "qg_device.h"
 #include "qg_launch.h"
 
 namespace qg {
 
-enum { F_INT8F = 0, F_INT8I = 1, F_TERN = 2, F_SR = 3 };
+enum { F_INT8F = 0, F_INT8I = 1, F_TERN = 2, F_SR = 3, F_Q4 = 4 };
 
 struct KParams {
     const uint8_t* codes;
@@ -101,6 +106,12 @@ struct Fmt<F_SR> {
     static constexpr int kLdsBytesPerCol = 2;
     struct Frag { u32x4 r0, r1; uint32_t s; };
 };
+template <>
+struct Fmt<F_Q4> {
+    static constexpr int kColsPerChunk = 32;   // one group: 16 B of 4-bit codes
+    static constexpr int kLdsBytesPerCol = 0;  // x (bf16) travels with each item
+    struct Frag { u32x4 w; u32x4 meta; u32x4 x[4]; };
+};
 
 // Workgroup shape: 8 waves (2 per SIMD, so one wave's LDS / ALU latency is
 // covered by the other's work), one workgroup per CU.
@@ -108,7 +119,11 @@ constexpr int kQThreads = 512;
 constexpr int kQWaves = kQThreads / kWave;
 constexpr int kXL = 4;  // x pieces of 16 B held in registers per thread (K <= 16384 bf16 / 8192 fp32)
 
-template <int F, int XT, int YT, int U, int JS>
+// XREG (4-bit groups, items spanning the whole row): lane l only ever
+// multiplies the columns of its chunks c = l + 64 j (j < JS), so it loads and
+// converts that x, and its groups' sums, once before the first item; the
+// items then carry codes and super-block records only.
+template <int F, int XT, int YT, int U, int JS, bool XREG = false>
 __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     using Frag = typename Fmt<F>::Frag;
     constexpr int kCols = Fmt<F>::kColsPerChunk;
@@ -132,12 +147,13 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     const int padded_cols = nseg * JS * 64 * kCols;
 
     // ------------------------------------------------------------ stream
-    const int rowB = (F == F_TERN) ? K / 4 : (F == F_SR) ? K / 8 : K;  // code bytes per row
+    const int rowB = (F == F_TERN) ? K / 4 : (F == F_SR) ? K / 8 : (F == F_Q4) ? K / 2 : K;  // code bytes per row
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.codes + (int64_t)row0 * rowB, (uint32_t)(rows * rowB));
     __amdgpu_buffer_rsrc_t rr = rc;
     if constexpr (F == F_SR) rr = make_rsrc(p.resid + (int64_t)row0 * K, (uint32_t)(rows * K));
+    if constexpr (F == F_Q4) rr = make_rsrc(p.resid + (int64_t)row0 * (K / 16), (uint32_t)(rows * (K / 16)));
     const uint32_t oob_c = (uint32_t)(rows * rowB);
-    const uint32_t oob_r = (uint32_t)(rows * K);
+    const uint32_t oob_r = (uint32_t)(rows * (F == F_Q4 ? K / 16 : K));
 
     const int ngroups = (rows + U - 1) / U;
     const int my_groups = ngroups > wave ? (ngroups - wave + kQWaves - 1) / kQWaves : 0;
@@ -165,6 +181,16 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
                     fr[u][j].r0 = load16(rr, orr);
                     fr[u][j].r1 = load16(rr, ok ? orr + 16 : oob_r);
                     fr[u][j].s = load4(rc, ok ? (uint32_t)(r * rowB + 4 * c) : oob_c);
+                } else if constexpr (F == F_Q4) {
+                    // the group's 32 activations (bf16, shared by the U rows; not
+                    // with XREG), then its super-block record, then its codes
+                    if (!XREG && u == 0) {
+                        const uint32_t xo = (c < C) ? (uint32_t)(64 * c) : (uint32_t)(K * 2);
+#pragma unroll
+                        for (int h = 0; h < 4; ++h) fr[0][j].x[h] = load16(rx, xo + 16 * h);
+                    }
+                    fr[u][j].meta = load16(rr, ok ? (uint32_t)(r * (K / 16) + 16 * (c >> 3)) : oob_r);
+                    fr[u][j].w = load16(rc, ok ? (uint32_t)(r * rowB + 16 * c) : oob_c);
                 } else {
                     if constexpr (F == F_INT8F) {
                         // the 16 activations of this chunk, requested just ahead of the
@@ -192,8 +218,34 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     // (unconditional loads: pieces past K read zeros through the range check;
     // a branch around a load would make the compiler wait for all loads at
     // the join, the weights included)
+    static_assert(F != F_Q4 || XT == 1, "4-bit groups take bf16 activations");
+    static_assert(!XREG || F == F_Q4, "register-resident x is for the 4-bit groups");
+    // XREG: this lane's x (fp32) and the sums of its groups, for every row
+    float xq4[XREG ? JS : 1][XREG ? 32 : 1];
+    float xsq4[XREG ? JS : 1];
+    if constexpr (XREG) {
+        const uint32_t xend = (uint32_t)(K * 2);
+#pragma unroll
+        for (int j = 0; j < JS; ++j) {
+            const int c = lane + 64 * j;
+            u32x4 h[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) h[q] = load16(rx, c < C ? (uint32_t)(64 * c + 16 * q) : xend);
+            float xs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const uint32_t d = h[t >> 2][t & 3];
+                xq4[j][2 * t] = bf16_to_f32(d & 0xFFFFu);
+                xq4[j][2 * t + 1] = __uint_as_float(d & 0xFFFF0000u);
+                xs[(2 * t) & 3] += xq4[j][2 * t];
+                xs[(2 * t + 1) & 3] += xq4[j][2 * t + 1];
+            }
+            xsq4[j] = (xs[0] + xs[1]) + (xs[2] + xs[3]);
+        }
+    }
+    constexpr bool kXPerItem = (F == F_INT8F || F == F_Q4);  // x travels with the items: nothing staged
     u32x4 xr[kXL];
-    if constexpr (F != F_INT8F) {
+    if constexpr (!kXPerItem) {
         const uint32_t xend = (uint32_t)(K * (XT == 0 ? 4 : 2));
 #pragma unroll
         for (int l = 0; l < kXL; ++l) {
@@ -245,7 +297,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
 
     float sx = 1.0f;  // activation scale (integer modes)
     int sum_xq = 0;   // sum of int8 activations (ternary offset correction)
-    if constexpr (F == F_INT8F) {
+    if constexpr (kXPerItem) {
         // nothing to stage: every item carries its own slice of x
     } else if constexpr (F == F_INT8I || F == F_TERN) {
         float m = 0.0f;
@@ -284,7 +336,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
         });
         for (int i = K / 2 + tid; i < padded_cols / 2; i += kQThreads) reinterpret_cast<uint32_t*>(xs)[i] = 0u;
     }
-    if constexpr (F != F_INT8F) lds_barrier();  // x staged; the prefetched weights stay in flight
+    if constexpr (!kXPerItem) lds_barrier();  // x staged; the prefetched weights stay in flight
 
     float accf[U], accf2[U];
     int acc1[U], acc4[U], acc16[U];
@@ -322,6 +374,50 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
                         const float wv = (float)(int8_t)(wd >> (8 * (b & 3)));
                         accf[u] = __builtin_fmaf(wv, xv[b], accf[u]);
                     }
+                }
+            } else if constexpr (F == F_Q4) {
+                float xv[32];
+                float xsum;
+                if constexpr (XREG) {
+#pragma unroll
+                    for (int t = 0; t < 32; ++t) xv[t] = xq4[j][t];
+                    xsum = xsq4[j];
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const uint32_t d = fr[0][j].x[q >> 2][q & 3];
+                        xv[2 * q] = bf16_to_f32(d & 0xFFFFu);
+                        xv[2 * q + 1] = __uint_as_float(d & 0xFFFF0000u);
+                    }
+                    float xs[4] = {0.f, 0.f, 0.f, 0.f};  // sum of the group's x, four chains
+#pragma unroll
+                    for (int t = 0; t < 32; ++t) xs[t & 3] += xv[t];
+                    xsum = (xs[0] + xs[1]) + (xs[2] + xs[3]);
+                }
+                const int grp = c & 7;  // group inside its super-block (= lane & 7)
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    // S = d * sc and M = dmin * m from the super-block record
+                    const u32x4 m = fr[u][j].meta;
+                    const uint64_t lo64 = (uint64_t)m[0] | ((uint64_t)m[1] << 32);  // bits 0..63
+                    const uint64_t hi64 = (uint64_t)m[1] | ((uint64_t)m[2] << 32);  // bits 32..95
+                    const float sc = (float)((uint32_t)(lo64 >> (6 * grp)) & 63u);
+                    const float mq = (float)((int)((uint32_t)(hi64 >> (16 + 6 * grp)) & 63u) - 32);
+                    const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(m[3] & 0xFFFFu));
+                    const float dm = (float)__builtin_bit_cast(_Float16, (uint16_t)(m[3] >> 16));
+                    const float S = d * sc, M = dm * mq;
+                    float a0 = 0.f, a1 = 0.f;  // sum_k q x, two chains
+#pragma unroll
+                    for (int dw = 0; dw < 4; ++dw) {
+                        const uint32_t wd = fr[u][j].w[dw];
+                        const uint32_t lo = wd & 0x0F0F0F0Fu, hi = (wd >> 4) & 0x0F0F0F0Fu;  // even, odd codes
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            a0 = __builtin_fmaf((float)((lo >> (8 * b)) & 0xFFu), xv[8 * dw + 2 * b], a0);
+                            a1 = __builtin_fmaf((float)((hi >> (8 * b)) & 0xFFu), xv[8 * dw + 2 * b + 1], a1);
+                        }
+                    }
+                    accf[u] += S * (a0 + a1) + M * xsum;
                 }
             } else if constexpr (F == F_INT8I) {
                 const u32x4 xq = reinterpret_cast<const u32x4*>(xs)[c];
@@ -372,7 +468,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
         if (seg == nseg - 1) {
             // reduce every row of the group at once (independent DPP chains);
             // lane 63 holds the sums and writes the outputs
-            if constexpr (F == F_INT8F || F == F_SR) {
+            if constexpr (F == F_INT8F || F == F_SR || F == F_Q4) {
                 float v[U], v2[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
@@ -387,6 +483,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
                             const int row = row0 + r;
                             float o;
                             if constexpr (F == F_SR) o = p.scale[row] * v[u] + v2[u] / p.scale2[row];
+                            else if constexpr (F == F_Q4) o = v[u];  // group scales already applied
                             else o = v[u] / p.scale[row];
                             if constexpr (YT == 0) static_cast<float*>(p.y)[row] = o;
                             else static_cast<uint16_t*>(p.y)[row] = (uint16_t)f32_to_bf16(o);
@@ -450,16 +547,17 @@ int device_cu_count() {
     return cached[dev];
 }
 
-template <int F, int XT, int YT, int U, int JS>
+template <int F, int XT, int YT, int U, int JS, bool XREG = false>
 static hipError_t run(const QgemvArgs* a, int count, hipStream_t st) {
     constexpr int kCols = Fmt<F>::kColsPerChunk;
     const int K = (int)a[0].k;
     const int C = K / kCols;
     const int J = (C + 63) / 64;
     const int nseg = (J + JS - 1) / JS;
+    if (XREG && nseg != 1) return hipErrorInvalidValue;  // register-resident x needs items spanning the row
     const size_t lds = (size_t)nseg * JS * 64 * kCols * Fmt<F>::kLdsBytesPerCol;
-    const int64_t rowB = (F == F_TERN) ? K / 4 : (F == F_SR) ? K / 8 : K;
-    const int64_t resB = (F == F_SR) ? K : 0;
+    const int64_t rowB = (F == F_TERN) ? K / 4 : (F == F_SR) ? K / 8 : (F == F_Q4) ? K / 2 : K;
+    const int64_t resB = (F == F_SR) ? K : (F == F_Q4) ? K / 16 : 0;
     const int64_t cap = ((int64_t)1 << 31) / (rowB > resB ? rowB : resB);  // buffer ranges stay below 2 GiB
     const int cus = device_cu_count();
     int64_t total_rows = 0;
@@ -489,7 +587,7 @@ static hipError_t run(const QgemvArgs* a, int count, hipStream_t st) {
         wg += (int)((N + rpw - 1) / rpw);
     }
     for (int m = count; m <= kMaxGroup; ++m) g.wg_start[m] = wg;
-    auto kern = qgemv_kernel<F, XT, YT, U, JS>;
+    auto kern = qgemv_kernel<F, XT, YT, U, JS, XREG>;
     if (lds > 64 * 1024) {
         static bool attr_set = false;  // per instantiation
         if (!attr_set) {
@@ -528,6 +626,11 @@ hipError_t launch_qgemv_group(const QgemvArgs* a, int count, hipStream_t st) {
     }
     if (h.fmt == 0 && h.amode == 0) return run_xy<F_INT8I, 2, 4>(a, count, st);
     if (h.fmt == 1) return run_xy<F_TERN, 4, 1>(a, count, st);
+    if (h.fmt == 3) {  // bf16 activations only
+        const bool spans = (h.k / 32 + 63) / 64 <= 2;  // one item of 2 chunk iterations covers the row
+        if (h.yt == 0) return spans ? run<F_Q4, 1, 0, 1, 2, true>(a, count, st) : run<F_Q4, 1, 0, 4, 1>(a, count, st);
+        return spans ? run<F_Q4, 1, 1, 1, 2, true>(a, count, st) : run<F_Q4, 1, 1, 4, 1>(a, count, st);
+    }
     if (h.yt == 0) return run<F_SR, 1, 0, 1, 2>(a, count, st);
     return run<F_SR, 1, 1, 1, 2>(a, count, st);
 }

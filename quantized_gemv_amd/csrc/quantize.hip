@@ -335,6 +335,66 @@ __global__ __launch_bounds__(kThreads) void split_sign_residual_kernel(const flo
     }
 }
 
+// ---------------------------------------------------------------- 4-bit groups, two-level scales
+// [VG] 'Q4_K uses two-level blocks': one wave per super-block of 256
+// weights.  Lane l holds weights 4l .. 4l+3, which lie in group l / 8: group
+// min / max over 8 lanes, super-block maxima over the wave (shuffles), then
+// every lane codes its 4 weights and lane 0 writes the 16-byte metadata
+// record.  fp32 arithmetic in the order of the definition; fp16 by RNE.
+__global__ __launch_bounds__(kThreads) void q4k_quantize_kernel(const float* w, int64_t n, int64_t k, uint8_t* codes,
+                                                                 uint8_t* meta) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t per_row = k / 256;
+    const int64_t total = n * per_row;
+    for (int64_t sb = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); sb < total; sb += (int64_t)gridDim.x * kWaves) {
+        const int64_t r = sb / per_row, b = sb - r * per_row;
+        const float4 v4 = *reinterpret_cast<const float4*>(w + r * k + b * 256 + 4 * lane);
+        const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+        float lo = __builtin_fminf(__builtin_fminf(v[0], v[1]), __builtin_fminf(v[2], v[3]));
+        float hi = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), __builtin_fmaxf(v[2], v[3]));
+#pragma unroll
+        for (int off = 1; off < 8; off <<= 1) {  // the 8 lanes of a group
+            lo = __builtin_fminf(lo, __shfl_xor(lo, off, kWave));
+            hi = __builtin_fmaxf(hi, __shfl_xor(hi, off, kWave));
+        }
+        const float scale = (hi - lo) / 15.0f;
+        float smax = scale, amax = __builtin_fabsf(lo);
+#pragma unroll
+        for (int off = 8; off < kWave; off <<= 1) {  // across the 8 groups
+            smax = __builtin_fmaxf(smax, __shfl_xor(smax, off, kWave));
+            amax = __builtin_fmaxf(amax, __shfl_xor(amax, off, kWave));
+        }
+        const _Float16 d16 = (_Float16)(smax / 63.0f);
+        const _Float16 dm16 = (_Float16)(amax / 31.0f);
+        const float d = (float)d16, dm = (float)dm16;
+        const float scq = (d == 0.0f) ? 0.0f : __builtin_fminf(__builtin_fmaxf(rintf(scale / d), 0.0f), 63.0f);
+        const float mq = (dm == 0.0f) ? 0.0f : __builtin_fminf(__builtin_fmaxf(rintf(lo / dm), -31.0f), 31.0f);
+        const float S = d * scq, M = dm * mq;
+        uint32_t packed = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int q = (S == 0.0f) ? 0 : (int)__builtin_fminf(__builtin_fmaxf(rintf((v[e] - M) / S), 0.0f), 15.0f);
+            packed |= (uint32_t)q << (4 * e);
+        }
+        reinterpret_cast<uint16_t*>(codes + r * (k / 2) + b * 128)[lane] = (uint16_t)packed;
+        // the record: field i (sc_0..sc_7, then m_0+32..m_7+32) at bits 6i..6i+5
+        const int fsc = (int)scq, fm = (int)mq + 32;
+        uint32_t rec[3] = {0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t f = (uint32_t)__shfl(i < 8 ? fsc : fm, 8 * (i & 7), kWave);
+            const int p = 6 * i, wd = p >> 5, sh = p & 31;
+            rec[wd] |= f << sh;
+            if (sh > 26) rec[wd + 1] |= f >> (32 - sh);
+        }
+        if (lane == 0) {
+            const uint32_t dd = (uint32_t)__builtin_bit_cast(uint16_t, d16) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, dm16) << 16);
+            *reinterpret_cast<uint4*>(meta + sb * 16) = make_uint4(rec[0], rec[1], rec[2], dd);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- launchers
 static int grid_for(int64_t work_items, int per_block_items, int cap) {
     int64_t g = (work_items + per_block_items - 1) / per_block_items;
@@ -405,6 +465,12 @@ hipError_t launch_split_sign_residual(const float* w, int64_t n, int64_t k, int8
                                       float* s_r, hipStream_t st) {
     const int g = grid_for(n, 1, 65535);
     split_sign_residual_kernel<<<g, kThreads, 0, st>>>(w, n, k, sign, alpha, rq, s_r);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_q4k(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* meta, hipStream_t st) {
+    const int64_t blocks = (n * (k / 256) + kWaves - 1) / kWaves;  // one wave per super-block
+    q4k_quantize_kernel<<<(int)(blocks < 16384 ? blocks : 16384), kThreads, 0, st>>>(w, n, k, codes, meta);
     return hipGetLastError();
 }
 

@@ -134,3 +134,13 @@ def prefill_outlier(m: int = 2048, k: int = 4096, n: int = 4096, n_out: int = 20
     return Workload("prefill_w8a8_outlier", seed,
                     {"w": w, "x_bf16": to_bf16_bits(x), "idx": idx},
                     {"m": m, "k": k, "n": n, "n_out": n_out})
+
+
+def q4_decode(n: int = 11008, k: int = 4096, seed: int = 6) -> Workload:
+    """Group-wise 4-bit decode at the 7B FFN shape: W ~ N(0, 0.02) with 0.1%
+    of entries x10 (the W8A16 decode recipe); x bf16 ~ N(0, 1)."""
+    g = rng(seed)
+    w = gaussian(g, (n, k), 0.02)
+    cnt = boost_entries(g, w, 0.001, 10.0)
+    x = to_bf16_bits(gaussian(g, (k,), 1.0))
+    return Workload("q4_decode", seed, {"w": w, "x_bf16": x}, {"n": n, "k": k, "boosted": cnt})

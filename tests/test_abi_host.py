@@ -147,6 +147,27 @@ def test_validation_qgemv(qg):
     assert call(codes=U) == 3
     assert call(x=U) == 3
     assert call(xt=3) == 4 and call(yt=3) == 4 and call(amode=2) == 4
+    # 4-bit groups: bf16 float activations, a metadata plane, k in whole super-blocks
+    assert call(fmt=3, amode=0) == 4
+    assert call(fmt=3, xt=0) == 4
+    assert call(fmt=3, resid=None) == 1
+    assert call(fmt=3, resid=U) == 3
+    assert call(fmt=3, k=384) == 2
+    q4 = qg.QG_WFMT_Q4K
+    assert q4 == 3
+
+
+def test_validation_quantize_q4k(qg):
+    f = qg.lib().qg_quantize_q4k
+    # (w, n, k, codes, meta, stream)
+    assert f(None, 4, 256, A, A, None) == 1
+    assert f(A, 4, 256, None, A, None) == 1
+    assert f(A, 4, 256, A, None, None) == 1
+    assert f(A, 0, 256, A, A, None) == 2
+    assert f(A, 4, 384, A, A, None) == 2          # k not a multiple of 256
+    assert f(A, 4, 128, A, A, None) == 2
+    assert f(U, 4, 256, A, A, None) == 3
+    assert f(A, 4, 256, A, U, None) == 3
 
 
 def test_validation_qgemv_grouped(qg):

@@ -18,6 +18,7 @@ import pytest
 import torch
 
 import oracle
+import oracle.q4 as oq4
 import synth
 from gpu_util import (TOL_BF16, TOL_F32, bf16_to_f64, canaries_intact, check_bf16_output, dev, dev_bf16, guarded,
                       host)
@@ -436,3 +437,61 @@ def test_qgemm_small(qg, m, k, n, n_out):
 def test_qgemm_full(qg):
     note("qgemm 2048x4096x4096 n_out=20")
     _qgemm_case(qg, 2048, 4096, 4096, 20)
+
+
+# ---------------------------------------------------------------- 4-bit groups, two-level scales
+def _q4_weights(n, k, seed):
+    w = synth.q4_decode(n=n, k=k, seed=seed).tensors["w"]
+    if n >= 6:
+        w[0] = 0.0                                       # all-zero row
+        w[1] = 0.125                                     # constant row
+        w[2] = np.abs(w[2])                              # all positive
+        w[3] = -np.abs(w[3]) - 0.01                      # all negative
+        w[4, 32:64] *= 40.0                              # one group with large values
+    return w
+
+
+@pytest.mark.parametrize("n,k", [(6, 256), (37, 512), (64, 4096), (6, 11008), (11008, 4096)])
+def test_quantize_q4k(qg, n, k):
+    note("quantize q4k %dx%d" % (n, k))
+    w = _q4_weights(n, k, 6)
+    codes, meta = qg.quantize_q4k(dev(w))
+    plane_ref, meta_ref = oq4.pack_q4k(*oq4.quantize_q4k(w))
+    assert np.array_equal(host(codes), plane_ref)
+    assert np.array_equal(host(meta), meta_ref)
+
+
+@pytest.mark.parametrize("n,k", [(6, 256), (37, 512), (11008, 4096), (77, 11008), (33, 32768)])
+def test_qgemv_q4k(qg, n, k):
+    note("qgemv q4k %dx%d" % (n, k))
+    w = _q4_weights(n, k, 6)
+    xb = synth.q4_decode(n=1, k=k, seed=7).tensors["x_bf16"]
+    codes, meta = qg.quantize_q4k(dev(w))
+    parts = oq4.quantize_q4k(w)
+    plane_ref, meta_ref = oq4.pack_q4k(*parts)
+    assert np.array_equal(host(codes), plane_ref) and np.array_equal(host(meta), meta_ref)
+    y_ref = oq4.y_q4k(*parts, xb)
+    W = qg.QWeight(qg.QG_WFMT_Q4K, n, k, codes, None, resid=meta)
+    x = dev_bf16(xb)
+    y32 = host(qg.qgemv(W, x, act_int8=False, y_dtype=torch.float32))
+    assert oracle.normwise_error(y32, y_ref) <= TOL_F32
+    y_full, y = guarded(n, torch.bfloat16)
+    qg.qgemv(W, x, act_int8=False, y=y)
+    check_bf16_output(host(y), y32, y_ref)
+    assert canaries_intact(y_full, n)
+
+
+def test_qgemv_q4k_grouped_matches_single(qg):
+    note("qgemv q4k grouped")
+    k = 4096
+    xb = synth.q4_decode(n=1, k=k, seed=7).tensors["x_bf16"]
+    x = dev_bf16(xb)
+    Ws, singles = [], []
+    for i, n in enumerate((4096, 1000, 2304)):
+        codes, meta = qg.quantize_q4k(dev(_q4_weights(n, k, 20 + i)))
+        W = qg.QWeight(qg.QG_WFMT_Q4K, n, k, codes, None, resid=meta)
+        Ws.append(W)
+        singles.append(host(qg.qgemv(W, x, act_int8=False, y_dtype=torch.bfloat16)))
+    ys = qg.qgemv_grouped(Ws, x, act_int8=False, y_dtype=torch.bfloat16)
+    for y, ref in zip(ys, singles):
+        assert np.array_equal(host(y), ref)
