@@ -82,6 +82,7 @@ typedef int32_t qg_status;
 #define QG_OUT_LD_ALIGN 8       /* row stride (elements) of the outlier operands the
                                    prefill GEMMs read: a multiple of 8 bf16 = 16 B    */
 #define QG_MAX_OUT_LD   65536   /* largest row stride of an outlier operand          */
+#define QG_SEP_MAX_K    65536   /* k of the thresholded separated format             */
 
 /* Human-readable text for a status code (static storage). */
 const char* qg_status_str(qg_status s);
@@ -307,6 +308,57 @@ qg_status qg_qgemv(const qg_weight* w, int32_t amode, const void* x, int32_t xt,
  */
 qg_status qg_qgemv_grouped(const qg_weight* w, int32_t count, int32_t amode, const void* x, int32_t xt,
                            void* const* y, int32_t yt, int32_t* const* acc_out, void* stream);
+
+/*
+ * Thresholded separated weights ([SEP] section 2.1: only the weights above a
+ * threshold go into the 1-bit backbone, the others into the residual;
+ * section 5.2: the threshold is a percentile of |W|, the 70th or 80th;
+ * section 3.3: residual entries near zero are dropped and the residual is
+ * stored sparse; section 5.3 (sep_linear): sign(W) times a scale on the
+ * backbone plus an int8 residual).  Per row n, with m_k = |w[n][k]| and the
+ * nearest-rank percentile P(p) = the j-th smallest m_k, j = ceil(p * k / 100):
+ *   tau = P(pct_backbone); eps = P(pct_zero) (no zero class if pct_zero = 0);
+ *   weight k is backbone if m_k > tau, zero if m_k <= eps, residual otherwise;
+ *   alpha[n] = the fp32 nearest to the mean of m_k over the backbone (0 if
+ *              the backbone is empty);
+ *   s_r[n]   = fl32(127 / max m_k over the residual) (1 if that is 0 or the
+ *              residual is empty);
+ *   residual code = clip(rne(fl32(w * s_r[n])), -127, 127).
+ * Storage:
+ *   cls : [n][k/4] bytes; weight k's 2-bit class in byte k/4 at bits
+ *         2*(k%4): 0 = backbone, w < 0 (-alpha); 1 = zero; 2 = backbone,
+ *         w > 0 (+alpha); 3 = residual;
+ *   rv  : [n][rv_ld] int8: row n's residual codes in increasing k, then
+ *         zeros; rv_ld >= qg_sep_resid_ld(k, pct_zero), a multiple of 16.
+ * w: [n][k] fp32; alpha, s_r: [n] fp32 (out).  1 <= pct_backbone <= 100,
+ * 0 <= pct_zero <= pct_backbone; k % 128 == 0, 128 <= k <= QG_SEP_MAX_K;
+ * 1 <= n, n * k < 2^40; w, cls, rv 16-B aligned.
+ * qg_sep_resid_ld returns the smallest valid rv_ld (the residual count of a
+ * row is at most k - j(pct_zero), rounded up to 16), or 0 for invalid
+ * arguments.
+ */
+int64_t qg_sep_resid_ld(int64_t k, int32_t pct_zero);
+qg_status qg_split_sep_threshold(const float* w, int64_t n, int64_t k, int32_t pct_backbone, int32_t pct_zero,
+                                 uint8_t* cls, int8_t* rv, int64_t rv_ld, float* alpha, float* s_r,
+                                 void* stream);
+
+/*
+ * Batch-1 product on thresholded separated weights with int8 activations
+ * ([SEP] section 5.3: the backbone and residual products are computed and
+ * added, here in one kernel; the residual product is an int8 product):
+ *   xq, s_x  = per-tensor absmax int8 of x (as qg_quantize_absmax);
+ *   acc_b[n] = sum over the backbone weights of sign(w) * xq[k]  (int32, exact);
+ *   acc_r[n] = sum over the residual weights of code * xq[k]     (int32, exact);
+ *   y[n]     = (alpha[n] * acc_b[n] + acc_r[n] / s_r[n]) / s_x  (fp32).
+ * skip_residual != 0 is [SEP] section 3.3's fast path: y[n] = alpha[n] *
+ * acc_b[n] / s_x; rv and s_r are not read (may be NULL) and acc_r is 0.
+ * x: [k] of type xt (QG_F32 or QG_BF16), 16-B aligned.  y: [n] fp32 (out).
+ * acc_out: [2][n] int32 (acc_b, then acc_r) or NULL.
+ * 16 <= rv_ld <= k, rv_ld % 16 == 0; other sizes as qg_split_sep_threshold.
+ */
+qg_status qg_qgemv_sep(const uint8_t* cls, const int8_t* rv, int64_t rv_ld, const float* alpha,
+                       const float* s_r, int64_t n, int64_t k, const void* x, int32_t xt,
+                       int32_t skip_residual, float* y, int32_t* acc_out, void* stream);
 
 /*
  * W8A8 prefill GEMM with the outlier-channel split ([SEP] section 2.2: outlier

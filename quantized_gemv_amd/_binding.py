@@ -28,6 +28,7 @@ QG_QGEMV_MAX_K = 32768
 QG_MAX_GROUP = 8
 QG_OUT_LD_ALIGN = 8
 QG_MAX_OUT_LD = 65536
+QG_SEP_MAX_K = 65536
 
 _c_i32, _c_i64, _c_sz, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
@@ -57,6 +58,11 @@ _SIGS = {
     "qg_quantize_ternary": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "qg_split_sign_residual": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
     "qg_quantize_q4k": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
+    "qg_sep_resid_ld": (_c_i64, [_c_i64, _c_i32]),
+    "qg_split_sep_threshold": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i32, _c_i32, _c_vp, _c_vp, _c_i64, _c_vp, _c_vp,
+                                        _c_vp]),
+    "qg_qgemv_sep": (_c_i32, [_c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_i32, _c_vp,
+                              _c_vp, _c_vp]),
     "qg_pack": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp]),
     "qg_unpack": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp]),
     "qg_qgemv": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp]),
@@ -271,6 +277,52 @@ def quantize_q4k(w: torch.Tensor):
     meta = torch.empty((n, k // 256, 16), dtype=torch.uint8, device=w.device)
     _check(lib().qg_quantize_q4k(_p(w), n, k, _p(codes), _p(meta), _stream(w)), "qg_quantize_q4k")
     return codes, meta
+
+
+class SepWeight:
+    """Thresholded separated weights as qg_split_sep_threshold writes them:
+    cls [n][k/4] uint8 (2-bit classes), rv [n][ld] int8 (residual codes in
+    increasing k, then zeros), alpha [n] and s_r [n] fp32."""
+
+    def __init__(self, cls: torch.Tensor, rv: torch.Tensor, alpha: torch.Tensor, s_r: torch.Tensor, k: int):
+        self.cls, self.rv, self.alpha, self.s_r = cls, rv, alpha, s_r
+        self.n, self.k = cls.shape[0], k
+        self.ld = rv.shape[1]
+
+
+def sep_resid_ld(k: int, pct_zero: int) -> int:
+    """Smallest valid row stride of the residual stream (qg_sep_resid_ld)."""
+    return int(lib().qg_sep_resid_ld(k, pct_zero))
+
+
+def split_sep_threshold(w: torch.Tensor, pct_backbone: int = 80, pct_zero: int = 50, ld: Optional[int] = None):
+    """Thresholded separated split (qg_split_sep_threshold). Returns SepWeight."""
+    _dev(w, "w", torch.float32)
+    n, k = w.shape
+    if ld is None:
+        ld = sep_resid_ld(k, pct_zero)
+    cls = torch.empty((n, k // 4), dtype=torch.uint8, device=w.device)
+    rv = torch.empty((n, max(int(ld), 1)), dtype=torch.int8, device=w.device)
+    alpha = torch.empty(n, dtype=torch.float32, device=w.device)
+    s_r = torch.empty(n, dtype=torch.float32, device=w.device)
+    _check(lib().qg_split_sep_threshold(_p(w), n, k, pct_backbone, pct_zero, _p(cls), _p(rv), int(ld), _p(alpha),
+                                        _p(s_r), _stream(w)), "qg_split_sep_threshold")
+    return SepWeight(cls, rv, alpha, s_r, k)
+
+
+def qgemv_sep(sw: SepWeight, x: torch.Tensor, skip_residual: bool = False, y: torch.Tensor = None,
+              acc_out: torch.Tensor = None):
+    """Batch-1 product on thresholded separated weights (qg_qgemv_sep);
+    acc_out, if given, is int32 [2][n] (backbone, residual). Returns y (fp32)."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    if y is None:
+        y = torch.empty(sw.n, dtype=torch.float32, device=x.device)
+    _dev(y, "y", torch.float32)
+    if acc_out is not None:
+        _dev(acc_out, "acc_out", torch.int32)
+    _check(lib().qg_qgemv_sep(_p(sw.cls), _p(sw.rv), sw.ld, _p(sw.alpha), _p(sw.s_r), sw.n, sw.k, _p(x), _xt(x),
+                              1 if skip_residual else 0, _p(y), _p(acc_out), _stream(x)), "qg_qgemv_sep")
+    return y
 
 
 def qgemv(w: QWeight, x: torch.Tensor, act_int8: bool, y_dtype=torch.float32, y: torch.Tensor = None,

@@ -76,7 +76,7 @@ const char* qg_status_str(qg_status s) {
     }
 }
 
-int32_t qg_abi_version(void) { return 20000; }
+int32_t qg_abi_version(void) { return 20100; }
 
 size_t qg_quantize_absmax_workspace_bytes(int64_t rows, int64_t cols, int32_t gran) {
     if (gran != QG_PER_TENSOR || rows < 1 || cols < 8) return 0;
@@ -152,6 +152,60 @@ qg_status qg_quantize_q4k(const float* w, int64_t n, int64_t k, uint8_t* codes, 
         return QG_ERR_SHAPE;
     if (!aligned16(w) || !aligned16(codes) || !aligned16(meta)) return QG_ERR_ALIGN;
     return from_hip(qg::launch_quantize_q4k(w, n, k, codes, meta, as_stream(stream)));
+}
+
+// Nearest rank ceil(pct * k / 100) of a percentile (0 for pct = 0).
+static int64_t nearest_rank(int32_t pct, int64_t k) { return (pct * k + 99) / 100; }
+
+static qg_status check_sep_shape(int64_t n, int64_t k) {
+    if (n < 1 || k < 128 || k % 128 != 0 || k > QG_SEP_MAX_K) return QG_ERR_SHAPE;
+    if (n > ((int64_t)1 << 40) / k) return QG_ERR_SHAPE;
+    return QG_OK;
+}
+
+int64_t qg_sep_resid_ld(int64_t k, int32_t pct_zero) {
+    if (k < 1 || k > QG_SEP_MAX_K || pct_zero < 0 || pct_zero > 100) return 0;
+    const int64_t ld = (k - nearest_rank(pct_zero, k) + 15) / 16 * 16;
+    return ld < 16 ? 16 : ld;
+}
+
+qg_status qg_split_sep_threshold(const float* w, int64_t n, int64_t k, int32_t pct_backbone, int32_t pct_zero,
+                                 uint8_t* cls, int8_t* rv, int64_t rv_ld, float* alpha, float* s_r, void* stream) {
+    if (!w || !cls || !rv || !alpha || !s_r) return QG_ERR_NULLPTR;
+    const qg_status sh = check_sep_shape(n, k);
+    if (sh != QG_OK) return sh;
+    if (pct_backbone < 1 || pct_backbone > 100 || pct_zero < 0 || pct_zero > pct_backbone) return QG_ERR_ARG;
+    if (rv_ld % 16 != 0 || rv_ld < qg_sep_resid_ld(k, pct_zero) || rv_ld > k) return QG_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(cls) || !aligned16(rv)) return QG_ERR_ALIGN;
+    return from_hip(qg::launch_sep_split(w, n, k, (int)nearest_rank(pct_backbone, k), (int)nearest_rank(pct_zero, k),
+                                         cls, rv, rv_ld, alpha, s_r, as_stream(stream)));
+}
+
+qg_status qg_qgemv_sep(const uint8_t* cls, const int8_t* rv, int64_t rv_ld, const float* alpha, const float* s_r,
+                       int64_t n, int64_t k, const void* x, int32_t xt, int32_t skip_residual, float* y,
+                       int32_t* acc_out, void* stream) {
+    const bool skip = skip_residual != 0;
+    if (!cls || !alpha || !x || !y || (!skip && (!rv || !s_r))) return QG_ERR_NULLPTR;
+    const qg_status sh = check_sep_shape(n, k);
+    if (sh != QG_OK) return sh;
+    if (n >= ((int64_t)1 << 31)) return QG_ERR_SHAPE;
+    if (xt != QG_F32 && xt != QG_BF16) return QG_ERR_ARG;
+    if (!skip && (rv_ld < 16 || rv_ld > k || rv_ld % 16 != 0)) return QG_ERR_SHAPE;
+    if (!aligned16(cls) || !aligned16(x) || (!skip && !aligned16(rv))) return QG_ERR_ALIGN;
+    qg::SepArgs a;
+    a.cls = cls;
+    a.rv = skip ? nullptr : rv;
+    a.ld = skip ? 16 : rv_ld;
+    a.alpha = alpha;
+    a.s_r = s_r;
+    a.n = n;
+    a.k = k;
+    a.x = x;
+    a.xt = xt;
+    a.skip = skip;
+    a.y = y;
+    a.acc_out = acc_out;
+    return from_hip(qg::launch_sep_qgemv(a, as_stream(stream)));
 }
 
 size_t qg_ternary_workspace_bytes(int64_t n, int64_t k) {

@@ -72,6 +72,25 @@ struct QgemmArgs {
 };
 hipError_t launch_qgemm(const QgemmArgs& a, hipStream_t st);
 
+// Thresholded separated weights: j_b, j_z are the nearest ranks of the two
+// percentiles (j_z = 0: no zero class).
+hipError_t launch_sep_split(const float* w, int64_t n, int64_t k, int j_b, int j_z, uint8_t* cls, int8_t* rv,
+                            int64_t ld, float* alpha, float* s_r, hipStream_t st);
+struct SepArgs {
+    const uint8_t* cls;
+    const int8_t* rv;
+    int64_t ld;
+    const float* alpha;
+    const float* s_r;
+    int64_t n, k;
+    const void* x;
+    int xt;
+    bool skip;
+    float* y;
+    int32_t* acc_out;
+};
+hipError_t launch_sep_qgemv(const SepArgs& a, hipStream_t st);
+
 int device_cu_count();
 
 }  // namespace qg

@@ -48,7 +48,7 @@ def test_header_symbols_exported(qg):
     for name in decl:
         assert hasattr(l, name), name
     assert set(decl) == set(qg.EXPORTED)
-    assert qg.lib().qg_abi_version() == 20000
+    assert qg.lib().qg_abi_version() == 20100
     for st in range(0, 8):
         assert qg.status_str(st)
 
@@ -302,3 +302,41 @@ def test_validation_detect_outliers(qg):
     assert f(A, 4, 64, 3, A, None, need, None) == 5
     assert f(A, 4, 64, 3, A, A + 4, need, None) == 3     # workspace not 16-B aligned
     assert f(A, 4, 64, 0, None, None, 0, None) == 0       # nothing to find: no launch
+
+
+def test_validation_sep_threshold(qg):
+    l = qg.lib()
+    import oracle.threshold as th
+    # the smallest residual stride: the oracle's bound, rounded up to 16
+    for k, pz in ((1024, 50), (1152, 0), (4096, 30), (128, 100), (8192, 40)):
+        assert l.qg_sep_resid_ld(k, pz) == max(16, th.resid_ld(k, pz))
+    assert l.qg_sep_resid_ld(1024, 101) == 0 and l.qg_sep_resid_ld(1024, -1) == 0
+    f = l.qg_split_sep_threshold
+    ld = l.qg_sep_resid_ld(1024, 50)
+    # (w, n, k, pct_b, pct_z, cls, rv, rv_ld, alpha, s_r, stream)
+    assert f(None, 4, 1024, 80, 50, A, A, ld, A, A, None) == 1
+    assert f(A, 4, 1024, 80, 50, A, A, ld, None, A, None) == 1
+    assert f(A, 0, 1024, 80, 50, A, A, ld, A, A, None) == 2
+    assert f(A, 4, 1000, 80, 50, A, A, ld, A, A, None) == 2        # k not a multiple of 128
+    assert f(A, 4, 65536 + 128, 80, 50, A, A, 65536, A, A, None) == 2  # beyond QG_SEP_MAX_K
+    assert f(A, 4, 1024, 0, 0, A, A, ld, A, A, None) == 4          # pct_backbone < 1
+    assert f(A, 4, 1024, 50, 60, A, A, ld, A, A, None) == 4        # pct_zero > pct_backbone
+    assert f(A, 4, 1024, 101, 50, A, A, ld, A, A, None) == 4
+    assert f(A, 4, 1024, 80, 50, A, A, ld - 16, A, A, None) == 2   # stride below the bound
+    assert f(A, 4, 1024, 80, 50, A, A, ld + 8, A, A, None) == 2    # not a multiple of 16
+    assert f(U, 4, 1024, 80, 50, A, A, ld, A, A, None) == 3
+    assert f(A, 4, 1024, 80, 50, A, U, ld, A, A, None) == 3
+    g = l.qg_qgemv_sep
+    # (cls, rv, rv_ld, alpha, s_r, n, k, x, xt, skip, y, acc_out, stream)
+    assert g(None, A, ld, A, A, 4, 1024, A, 0, 0, A, None, None) == 1
+    assert g(A, None, ld, A, A, 4, 1024, A, 0, 0, A, None, None) == 1  # residual needed unless skipped
+    assert g(A, A, ld, A, None, 4, 1024, A, 0, 0, A, None, None) == 1
+    assert g(A, A, ld, A, A, 4, 1024, None, 0, 0, A, None, None) == 1
+    assert g(A, A, ld, A, A, 0, 1024, A, 0, 0, A, None, None) == 2
+    assert g(A, A, ld, A, A, 4, 1000, A, 0, 0, A, None, None) == 2
+    assert g(A, A, 8, A, A, 4, 1024, A, 0, 0, A, None, None) == 2     # rv_ld below 16
+    assert g(A, A, 2048, A, A, 4, 1024, A, 0, 0, A, None, None) == 2  # rv_ld above k
+    assert g(A, A, ld, A, A, 4, 1024, A, 2, 0, A, None, None) == 4    # x dtype
+    assert g(U, A, ld, A, A, 4, 1024, A, 0, 0, A, None, None) == 3
+    assert g(A, U, ld, A, A, 4, 1024, A, 0, 0, A, None, None) == 3
+    assert g(A, A, ld, A, A, 4, 1024, U, 1, 0, A, None, None) == 3

@@ -1,0 +1,149 @@
+"""GPU parity of the thresholded separated format against the oracle.
+
+The split is compared byte for byte (classes, the residual stream with its
+zero tail, alpha and s_r); the product is run on the oracle's own packed
+bytes, its int32 accumulators compared exactly and its fp32 output within
+1e-5 normwise of the oracle's fp64 value ([SEP] sections 2.1, 3.3, 5.2 and
+5.3)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.threshold as th
+import synth
+from gpu_util import TOL_F32, canaries_intact, dev, dev_bf16, guarded, host
+
+pytestmark = pytest.mark.gpu
+
+
+def note(msg):
+    print("[case] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def qg():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import quantized_gemv_amd as q
+    q.lib()  # fails loudly if the HIP library is not built
+    return q
+
+
+def _weights(n, k, seed, special=True):
+    g = synth.rng(seed)
+    w = synth.laplace(g, (n, k), 0.015)
+    synth.boost_entries(g, w, 0.005, 20.0)
+    if special and n >= 4:
+        w[1] = 0.0                                   # all zero
+        w[2] = np.float32(0.03)                      # one magnitude everywhere
+        w[3, ::3] = -w[3, ::3]
+        w[3, : k // 2] = np.round(w[3, : k // 2] * 200) / 200  # many ties
+    return w
+
+
+def _check_split(qg, w, pb, pz, rows=None):
+    n, k = w.shape
+    sw = qg.split_sep_threshold(dev(w), pb, pz)
+    assert sw.ld == th.resid_ld(k, pz) or (sw.ld == 16 and th.resid_ld(k, pz) < 16)
+    sel = np.arange(n) if rows is None else np.asarray(rows)
+    f, a, rq, sr = th.threshold_split(np.ascontiguousarray(w[sel]), pb, pz)
+    plane, stream = th.pack_threshold(f, rq, sw.ld)
+    assert np.array_equal(host(sw.alpha)[sel], a)
+    assert np.array_equal(host(sw.s_r)[sel], sr)
+    assert np.array_equal(host(sw.cls)[sel], plane)
+    assert np.array_equal(host(sw.rv)[sel], stream)
+    return sw, (f, a, rq, sr)
+
+
+@pytest.mark.parametrize("n,k,pb,pz", [(1, 128, 80, 50), (7, 1152, 80, 50), (33, 4096, 70, 40), (6, 8192, 90, 0),
+                                       (5, 1024, 60, 60), (4, 2048, 100, 0), (5, 640 * 2, 80, 1), (3, 65536, 80, 50)])
+def test_split_sep_threshold(qg, n, k, pb, pz):
+    note("split thresholded %dx%d pb=%d pz=%d" % (n, k, pb, pz))
+    _check_split(qg, _weights(n, k, n * 7 + k), pb, pz)
+
+
+def test_split_sep_threshold_full_sampled(qg):
+    note("split thresholded 28672x8192 (sampled rows)")
+    wl = synth.sign_residual_decode()
+    g = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, 1, 28671, 14335], g.choice(28672, 60, replace=False)]))
+    _check_split(qg, wl.tensors["w"], 80, 50, rows=rows)
+
+
+def _product_case(qg, n, k, pb, pz, x_bf16, skip=False, seed=0, zero_x=False):
+    w = _weights(n, k, seed + n + k)
+    g = synth.rng(seed + 99)
+    x = synth.gaussian(g, (k,), 1.0)
+    if zero_x:
+        x[:] = 0
+    if x_bf16:
+        xb = synth.to_bf16_bits(x)
+        x = synth.bf16_bits_to_f32(xb)
+        xd = dev_bf16(xb)
+    else:
+        xd = dev(x)
+    f, a, rq, sr = th.threshold_split(w, pb, pz)
+    ld = th.resid_ld(k, pz)
+    ld = max(ld, 16)
+    plane, stream = th.pack_threshold(f, rq, ld)
+    sw = qg.SepWeight(dev(plane), dev(stream), dev(a), dev(sr), k)
+    y_full, y = guarded(n, torch.float32)
+    acc_full, acc = guarded(2 * n, torch.int32)
+    qg.qgemv_sep(sw, xd, skip_residual=skip, y=y, acc_out=acc)
+    xq, s_x = oracle.quantize_absmax(x, per_row=False)
+    acc_b, acc_r = th.int_products(f, rq, xq)
+    acc_h = host(acc)
+    assert np.array_equal(acc_h[:n], acc_b)
+    assert np.array_equal(acc_h[n:], np.zeros(n, np.int64) if skip else acc_r)
+    y_ref = th.y_threshold(acc_b, acc_r, a, sr, s_x, skip_residual=skip)
+    assert oracle.normwise_error(host(y), y_ref) <= TOL_F32
+    assert canaries_intact(y_full, n) and canaries_intact(acc_full, 2 * n)
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (9, 1152), (77, 4096), (300, 8192), (13, 11008), (8, 65536)])
+@pytest.mark.parametrize("x_bf16", [False, True])
+def test_qgemv_sep(qg, n, k, x_bf16):
+    note("qgemv thresholded %dx%d bf16=%s" % (n, k, x_bf16))
+    _product_case(qg, n, k, 80, 50, x_bf16)
+
+
+@pytest.mark.parametrize("pb,pz", [(100, 0), (60, 60), (90, 0), (70, 10)])
+def test_qgemv_sep_class_mixes(qg, pb, pz):
+    # all residual (every step's slice is 1024 codes), no residual, no zeros
+    note("qgemv thresholded mixes pb=%d pz=%d" % (pb, pz))
+    _product_case(qg, 40, 3072, pb, pz, True)
+
+
+@pytest.mark.parametrize("n,k", [(9, 1152), (300, 8192)])
+def test_qgemv_sep_skip_residual(qg, n, k):
+    note("qgemv thresholded skip residual %dx%d" % (n, k))
+    _product_case(qg, n, k, 80, 50, True, skip=True)
+
+
+def test_qgemv_sep_zero_activations(qg):
+    note("qgemv thresholded zero x")
+    _product_case(qg, 16, 1024, 80, 50, False, zero_x=True)
+
+
+def test_qgemv_sep_full_sampled(qg):
+    # the bench workload end to end on the GPU: split, then product; rows
+    # sampled for the oracle (rows are independent given x)
+    note("qgemv thresholded 28672x8192 (sampled rows)")
+    wl = synth.sign_residual_decode()
+    w, xb = wl.tensors["w"], wl.tensors["x_bf16"]
+    g = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([[0, 28671, 100], g.choice(28672, 40, replace=False)]))
+    sw, (f, a, rq, sr) = _check_split(qg, w, 80, 50, rows=rows)
+    n = w.shape[0]
+    acc = torch.empty(2 * n, dtype=torch.int32, device="cuda")
+    y = qg.qgemv_sep(sw, dev_bf16(xb), acc_out=acc)
+    x = synth.bf16_bits_to_f32(xb)
+    xq, s_x = oracle.quantize_absmax(x, per_row=False)
+    acc_b, acc_r = th.int_products(f, rq, xq)
+    acc_h = host(acc)
+    assert np.array_equal(acc_h[:n][rows], acc_b) and np.array_equal(acc_h[n:][rows], acc_r)
+    y_ref = th.y_threshold(acc_b, acc_r, a, sr, s_x)
+    assert oracle.normwise_error(host(y)[rows], y_ref) <= TOL_F32
