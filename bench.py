@@ -46,8 +46,9 @@ CSRC = os.path.join(ROOT, "quantized_gemv_amd", "csrc")
 KERNEL_SOURCES = {
     "qgemv": ("qgemv.hip", "qg_device.h", "qg_launch.h"),
     "qgemm": ("qgemm.hip", "qg_device.h", "qg_launch.h"),
+    "sepq": ("sepq.hip", "qg_device.h", "qg_launch.h"),
 }
-KERNEL_NAME_KEYS = {"qgemv": "qgemv_kernel", "qgemm": "qgemm_w8a8_kernel"}
+KERNEL_NAME_KEYS = {"qgemv": "qg::qgemv_kernel", "qgemm": "qgemm_w8a8_kernel", "sepq": "sep_qgemv_kernel"}
 COPY_BYTES = 256 << 20           # calibration copy: bytes read and bytes written
 COPY_REPS = 2                    # calibration copies: the first copy dispatches of the profiled run
 
@@ -226,7 +227,8 @@ def build_prefill(torch, qg, synth, dev, cur_stream):
 
 def profile_workload(args):
     """Fixed workload for the rocprofv3 --pmc passes: a device copy of known
-    size (the calibration), two decode steps and two prefill calls."""
+    size (the calibration), two decode steps, two prefill calls and two
+    thresholded separated products."""
     import torch
     import quantized_gemv_amd as qg
     import synth
@@ -254,6 +256,14 @@ def profile_workload(args):
     full, _, _, _ = build_prefill(torch, qg, synth, dev, cur_stream)
     for _ in range(2):
         full()
+    torch.cuda.synchronize()
+    del full
+    torch.cuda.empty_cache()
+    wl = synth.sign_residual_decode()
+    sw = qg.split_sep_threshold(torch.from_numpy(wl.tensors["w"]).to(dev), 80, 50)
+    xs = torch.from_numpy(wl.tensors["x_bf16"]).to(dev).view(torch.bfloat16)
+    for _ in range(2):
+        qg.qgemv_sep(sw, xs)
     torch.cuda.synchronize()
     if args.hashes_out:
         with open(args.hashes_out, "w") as f:
@@ -419,6 +429,47 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def sep_threshold_bytes(torch, sw, skip):
+    """Bytes one product reads by definition: the class plane, the residual
+    codes actually stored (not the zero tail) and the per-row scales."""
+    c = sw.cls.to(torch.int32)
+    nres = int(sum(((c >> (2 * i)) & 3).eq(3).sum().item() for i in range(4)))
+    if skip:
+        return sw.cls.numel() + 4 * sw.n, nres
+    return sw.cls.numel() + nres + 8 * sw.n, nres
+
+
+def bench_sep_threshold(torch, qg, synth, dev, rotate_count):
+    wl = synth.sign_residual_decode()
+    n, k = wl.tensors["w"].shape
+    sw = qg.split_sep_threshold(torch.from_numpy(wl.tensors["w"]).to(dev), 80, 50)
+    xs = torch.from_numpy(wl.tensors["x_bf16"]).to(dev).view(torch.bfloat16)
+    ys = torch.empty(n, dtype=torch.float32, device=dev)
+    out = {}
+    for skip in (False, True):
+        per, nres = sep_threshold_bytes(torch, sw, skip)
+        copies = [qg.SepWeight(sw.cls.clone(), sw.rv if skip else sw.rv.clone(), sw.alpha.clone(), sw.s_r.clone(), k)
+                  for _ in range(rotate_count(per))]
+
+        def mk(c):
+            return lambda: qg.qgemv_sep(c, xs, skip_residual=skip, y=ys)
+        t = Timed(torch, [mk(c) for c in copies])
+        t.run(1)
+        sec = t.run(5) / t.n
+        name = "sep_threshold_skip_residual_28672x8192" if skip else "sep_threshold_28672x8192"
+        out[name] = {"us": round(sec * 1e6, 3), "weight_GBps": round(per / sec / 1e9, 1),
+                     "hbm_frac": round(per / sec / 1e9 / HBM_PEAK_GBS, 4),
+                     "bytes_per_weight": round(per / (n * k), 4), "residual_share": round(nres / (n * k), 4),
+                     "weights_per_ns": round(n * k / sec / 1e9, 1), "rotating_copies": len(copies),
+                     "algorithmic_bytes": per}
+        if not skip:
+            out[name]["traffic"] = recorded_traffic("sepq")
+        log("%s: %.2f us, %.0f GB/s" % (name, sec * 1e6, per / sec / 1e9))
+        del copies, t
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
     out = {}
     GiB = 1 << 30
@@ -541,6 +592,10 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
     log("sign+residual: %.2f us, %.0f GB/s" % (sec * 1e6, per / sec / 1e9))
     del copies, cws, sp, rq
     torch.cuda.empty_cache()
+
+    # -- thresholded separated weights (80th-percentile backbone, 50th-percentile
+    #    zero class), int8 activations, same weights and x as the line above
+    out.update(bench_sep_threshold(torch, qg, synth, dev, rotate_count))
 
     # -- W8A8 prefill GEMM with outlier split, 2048 x 4096 x 4096, 20 outlier channels
     full, split_only, dims, gemm_bytes = build_prefill(torch, qg, synth, dev, cur_stream)

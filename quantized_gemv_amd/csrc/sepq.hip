@@ -10,12 +10,12 @@
 // the residual codes in increasing k ([N][ld] int8, zero-filled).
 //
 // The product (activations quantized per tensor to int8 in the prologue):
-//   * a wave step covers 1024 weights of a row: lane l owns weights
-//     16l .. 16l+15, i.e. one dword of classes;
+//   * an item covers 4096 weights of each of U rows: lane l owns weights
+//     64l .. 64l+63, i.e. 16 bytes (four dwords) of classes per row;
 //   * backbone: the residual classes are turned into zeros (3 -> 1), the
-//     four 2-bit planes of the dword are masked into bytes and fed to v_dot4
-//     against x permuted to the same order; sum (class - 1) x is that minus
-//     sum x;
+//     four 2-bit planes of each dword are masked into bytes and fed to v_dot4
+//     against x transposed (in registers, shared by the U rows) to the same
+//     order; sum (class - 1) x is that minus sum x;
 //   * residual: the wave loads the step's slice of the row's residual stream
 //     (contiguous: the lanes' runs follow each other) into LDS; a lane's run
 //     starts at the exclusive prefix (DPP scan) of the lanes' residual
@@ -23,15 +23,16 @@
 //     flags to a byte selector, v_perm places the next codes of the run in
 //     the flagged byte slots (zeros elsewhere), and v_dot4 multiplies them
 //     with x in natural order;
-//   * the class dwords and residual slices of the next step are requested
-//     before the current one is computed (one step in flight per wave).
+//   * the classes run two items ahead and the residual slice one item ahead
+//     of the item being computed; a slice is read in whole 16-byte blocks,
+//     only those that hold its codes.
 #include "qg_device.h"
 #include "qg_launch.h"
 
 namespace qg {
 
-constexpr int kSepStep = 1024;   // weights per wave step (64 lanes x 16)
-constexpr int kSepStage = 1056;  // staged bytes per row: 1024 codes + 15 misalignment + 8 window over-read
+constexpr int kSepStep = 4096;   // weights per row per item (64 lanes x 64)
+constexpr int kSepStage = 4128;  // staged bytes per row: 4096 codes + 16 (misalignment) + 16 (window over-read)
 
 // --------------------------------------------------------------------------- helpers
 // Exclusive prefix sum over the workgroup (thread order) of small
@@ -241,25 +242,61 @@ struct SepParams {
     int32_t n, k, rows_per_wg;
 };
 
+constexpr int kSepThreads = 512;  // 8 waves, two per SIMD
+constexpr int kSepWaves = kSepThreads / kWave;
+constexpr uint32_t kSepLdsHead = 1024 + 64;  // selectors + reduction scratch
+constexpr int kSepXR = 4;  // 16-byte pieces of x per thread held in registers in the prologue
+
 __device__ __forceinline__ int sdot4i(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
-template <int XT, int U, bool SKIP>
-__global__ __launch_bounds__(kThreads) void sep_qgemv_kernel(SepParams p) {
+// 4x4 byte transpose: t[j] = bytes (a0.j, a1.j, a2.j, a3.j), i.e. the
+// activations 4b + j (b = 0..3) of a 16-activation slice, the order in which
+// (classes >> 2j) & 0x03030303 holds the classes of those weights.
+__device__ __forceinline__ void transpose4x4(const u32x4& a, uint32_t t[4]) {
+    const uint32_t lo01 = __builtin_amdgcn_perm(a[1], a[0], 0x05010400u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(a[1], a[0], 0x07030602u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(a[3], a[2], 0x05010400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(a[3], a[2], 0x07030602u);
+    t[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+    t[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+    t[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+    t[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+}
+
+// Work: a workgroup owns rows_per_wg consecutive rows; wave w takes groups of
+// U rows (w, w + 8, ...); an item is one group x one step.  The classes of
+// item it + 2 and the residual slice of item it + 1 are in flight while item
+// it is computed: the classes run two items ahead so that the slice of the
+// next item (its start: the running residual count; its length: the scan of
+// its classes) is known when it is requested, and only the 16-byte blocks it
+// covers are read.
+template <int XT, int U, bool SKIP, bool XPL>
+__global__ __launch_bounds__(kSepThreads) void sep_qgemv_kernel(SepParams p) {
+    // The kernel's only LDS is this dynamic block (so it starts at address 0
+    // and byte offsets are addresses): 256 selectors | reduction scratch |
+    // int8 x (zero-padded to Kp) | with XPL the same x 4x4-byte-transposed |
+    // the waves' residual slices.  x is stored lane-interleaved: the 16
+    // activations that lane l multiplies as dword d of item s sit at
+    // s * 4096 + 1024 d + 16 l, so a wave's 16-byte reads are consecutive.
     extern __shared__ __attribute__((aligned(16))) uint8_t sm[];
-    __shared__ float redf[kWaves];
-    __shared__ int redi[kWaves];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int K = p.k;
     const int nsteps = (K + kSepStep - 1) / kSepStep;
     const int Kp = nsteps * kSepStep;
-    uint32_t* lut = reinterpret_cast<uint32_t*>(sm);  // 256 selectors
-    uint8_t* xn = sm + 1024;                          // int8 x, natural order [Kp]
-    uint8_t* xp = xn + Kp;                            // int8 x, 4x4 byte-transposed per 16 [Kp]
-    const uint32_t stage0 = 1024u + 2u * (uint32_t)Kp + (uint32_t)(wave * U * kSepStage);  // LDS byte offset
+    uint32_t* lut = reinterpret_cast<uint32_t*>(sm);
+    float* redf = reinterpret_cast<float*>(sm + 1024);
+    int* redi = reinterpret_cast<int*>(sm + 1024 + 4 * kSepWaves);
+    uint8_t* xn = sm + kSepLdsHead;
+    uint8_t* xp = xn + Kp;
+    const uint32_t stage0 = kSepLdsHead + (uint32_t)Kp * (XPL ? 2u : 1u) + (uint32_t)(wave * U * kSepStage);
+    // LDS offset of 16-activation block b (b = 256 s + 4 l + d)
+    auto lane_slot = [](int b) -> uint32_t {
+        return (uint32_t)((b >> 8) * kSepStep + ((b & 3) << 10) + (((b >> 2) & 63) << 4));
+    };
 
     const int row0 = (int)blockIdx.x * p.rows_per_wg;
     const int rows = min(p.rows_per_wg, p.n - row0);
@@ -272,42 +309,89 @@ __global__ __launch_bounds__(kThreads) void sep_qgemv_kernel(SepParams p) {
     const uint32_t ld = (uint32_t)p.ld;
 
     const int ngroups = (rows + U - 1) / U;
-    const int my_groups = ngroups > wave ? (ngroups - wave + kWaves - 1) / kWaves : 0;
+    const int my_groups = ngroups > wave ? (ngroups - wave + kSepWaves - 1) / kSepWaves : 0;
     const int nit = my_groups * nsteps;
 
-    // class dwords and residual slices of one item (U rows x one step), and
-    // the residual count of each row before that step
-    struct Buf {
-        uint32_t D[U];
-        u32x4 V1[U], V2[U];
-        int base[U];
+    // classes of one item and what their scan gives
+    struct Slot {
+        u32x4 D[U];
+        int excl[U];  // residual codes of the row's item before this lane's 64 weights
+        int T[U];     // residual codes in the row's item (wave-uniform)
+        int base[U];  // residual codes of the row before the item (wave-uniform)
     };
+    u32x4 V[U][4];     // the residual slice in flight: lane l holds blocks l + 64 j,
+    uint32_t X4[U];    // and lanes 0-3 the four dwords after them
+
     // items past the wave's last read zeros through out-of-range offsets
-    auto issue = [&](int it, Buf& b) {
-        const int g = wave + kWaves * (it / nsteps);
+    auto issue_codes = [&](int it, Slot& c) {
+        const int g = wave + kSepWaves * (it / nsteps);
         const int s = it % nsteps;
         const bool live = it < nit;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int r = g * U + u;
-            const bool ok = live && r < rows && s * kSepStep + 16 * lane < K;
-            b.D[u] = load4(rc, ok ? (uint32_t)(r * rowC + s * (kSepStep / 4) + 4 * lane) : oob_c);
-            if constexpr (!SKIP) {
-                const bool okr = live && r < rows;
-                const uint32_t a0 = (uint32_t)r * ld + ((uint32_t)b.base[u] & ~15u);
-                b.V1[u] = load16(rr, okr ? a0 + 16u * lane : oob_r);
-                b.V2[u] = load16(rr, (okr && lane == 0) ? a0 + (uint32_t)kSepStep : oob_r);
-            }
+            const bool ok = live && r < rows && s * kSepStep + 64 * lane < K;
+            c.D[u] = load16(rc, ok ? (uint32_t)(r * rowC + s * (kSepStep / 4) + 16 * lane) : oob_c);
         }
     };
-    Buf fa, fb;
+    // residual flags, their per-lane exclusive prefix and the step's total;
+    // `prev` is the item before (same rows, previous step) unless s == 0
+    auto scan = [&](int it, Slot& b, const Slot& prev, bool first) {
+        const int s = it % nsteps;
 #pragma unroll
-    for (int u = 0; u < U; ++u) fa.base[u] = 0;
-    issue(0, fa);
+        for (int u = 0; u < U; ++u) {
+            int cnt = 0;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) cnt += __builtin_popcount(b.D[u][d] & (b.D[u][d] >> 1) & 0x55555555u);
+            const int incl = wave_incl_scan(cnt);
+            b.excl[u] = incl - cnt;
+            b.T[u] = __builtin_amdgcn_readlane(incl, kWave - 1);
+            b.base[u] = (first || s == 0) ? 0 : prev.base[u] + prev.T[u];
+        }
+    };
+    auto issue_vals = [&](int it, const Slot& b) {
+        const int g = wave + kSepWaves * (it / nsteps);
+        const bool live = it < nit;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = g * U + u;
+            const uint32_t mis = (uint32_t)b.base[u] & 15u;
+            const uint32_t a0 = (uint32_t)r * ld + ((uint32_t)b.base[u] - mis);
+            const uint32_t end = mis + (uint32_t)b.T[u];  // bytes of the slice from a0
+            const bool okr = live && r < rows;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t o = 16u * (64u * j + lane);
+                V[u][j] = load16(rr, (okr && o < end) ? a0 + o : oob_r);
+            }
+            const uint32_t o4 = (uint32_t)kSepStep + 4u * lane;
+            X4[u] = load4(rr, (okr && lane < 4 && o4 < end) ? a0 + o4 : oob_r);
+        }
+    };
+
+    Slot S0, S1, S2;
+    issue_codes(0, S0);
+    issue_codes(1, S1);
+    // x pieces (16 B: 4 fp32 or 8 bf16) of this thread, requested next
+    constexpr int kElems = (XT == 0) ? 4 : 8;
+    const int npieces = K / kElems;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)(K * (XT == 0 ? 4 : 2)));
+    const uint32_t xend = (uint32_t)(K * (XT == 0 ? 4 : 2));
+    u32x4 xr[kSepXR];
+#pragma unroll
+    for (int l = 0; l < kSepXR; ++l) {
+        const int pi = tid + kSepThreads * l;
+        xr[l] = load16(rx, pi < npieces ? (uint32_t)(16 * pi) : xend);  // past K: zeros
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // item 0's residual slice goes out before the prologue arithmetic
+    scan(0, S0, S0, true);
+    if constexpr (!SKIP) issue_vals(0, S0);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---------------------------------------------------------------- prologue
-    {   // selector for 4 residual flags (bits 0, 2, 4, 6 of the index): the
+    if (tid < 256) {
+        // selector for 4 residual flags (bits 0, 2, 4, 6 of the index): the
         // i-th flagged slot takes byte 4 + (flags below it) of the window
         // operand, an unflagged slot byte 0 of the zero operand
         uint32_t sel = 0;
@@ -320,11 +404,7 @@ __global__ __launch_bounds__(kThreads) void sep_qgemv_kernel(SepParams p) {
         }
         lut[tid] = sel;
     }
-    constexpr int kElems = (XT == 0) ? 4 : 8;
-    const int npieces = K / kElems;
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)(K * (XT == 0 ? 4 : 2)));
-    auto piece = [&](int pi, float v[kElems]) {
-        const u32x4 r = load16(rx, (uint32_t)(16 * pi));
+    auto vals_of = [&](const u32x4& r, float v[kElems]) {
         if constexpr (XT == 0) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(r[e]);
@@ -336,91 +416,136 @@ __global__ __launch_bounds__(kThreads) void sep_qgemv_kernel(SepParams p) {
             }
         }
     };
+    // visit every piece once: the register window, then (K beyond it) loads
+    auto for_pieces = [&](auto&& f) {
+#pragma unroll
+        for (int l = 0; l < kSepXR; ++l) {
+            float v[kElems];
+            vals_of(xr[l], v);
+            f(tid + kSepThreads * l, v);
+        }
+        for (int pi = tid + kSepThreads * kSepXR; pi < npieces; pi += kSepThreads) {
+            float v[kElems];
+            vals_of(load16(rx, (uint32_t)(16 * pi)), v);
+            f(pi, v);
+        }
+    };
     float m = 0.0f;
-    for (int pi = tid; pi < npieces; pi += kThreads) {
-        float v[kElems];
-        piece(pi, v);
+    for_pieces([&](int, const float* v) {
 #pragma unroll
         for (int e = 0; e < kElems; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
-    }
-    const float sx = absmax_scale(block_max(m, redf));
+    });
+    const float sx = absmax_scale(block_max<kSepWaves>(m, redf));
     int sum_xq = 0;
-    for (int pi = tid; pi < npieces; pi += kThreads) {
-        float v[kElems];
-        piece(pi, v);
+    for_pieces([&](int pi, const float* v) {
+        if (pi >= npieces) return;  // register-window pieces past K
+        uint32_t packed[kElems / 4];
+#pragma unroll
+        for (int w4 = 0; w4 < kElems / 4; ++w4) packed[w4] = 0;
 #pragma unroll
         for (int e = 0; e < kElems; ++e) {
             const int q = qcode(v[e], sx);
             sum_xq += q;
-            const int c = pi * kElems + e;
-            const int l = c & 15;
-            xn[c] = (uint8_t)(q & 0xFF);
-            xp[(c - l) + 4 * (l & 3) + (l >> 2)] = (uint8_t)(q & 0xFF);
+            packed[e / 4] |= (uint32_t)(q & 0xFF) << (8 * (e % 4));
+        }
+        // activation c = 16 * blk + i goes to lane_slot(blk) + i; a piece lies in one block
+        const int c0 = pi * kElems;
+        const uint32_t off = lane_slot(c0 >> 4) + (uint32_t)(c0 & 15);
+#pragma unroll
+        for (int w4 = 0; w4 < kElems / 4; ++w4) *reinterpret_cast<uint32_t*>(xn + off + 4 * w4) = packed[w4];
+    });
+    for (int i = K / 4 + tid; i < Kp / 4; i += kSepThreads) {
+        const uint32_t off = lane_slot(i >> 2) + 4u * (uint32_t)(i & 3);
+        *reinterpret_cast<uint32_t*>(xn + off) = 0u;
+    }
+    if constexpr (XPL) {
+        // the transposed copy, one 16-activation block per thread
+        lds_barrier();
+        for (int b = tid; b < Kp / 16; b += kSepThreads) {
+            const uint32_t off = lane_slot(b);
+            const u32x4 a = *reinterpret_cast<const u32x4*>(xn + off);
+            uint32_t t[4];
+            transpose4x4(a, t);
+            *reinterpret_cast<u32x4*>(xp + off) = u32x4{t[0], t[1], t[2], t[3]};
         }
     }
-    for (int i = K / 4 + tid; i < Kp / 4; i += kThreads) {
-        reinterpret_cast<uint32_t*>(xn)[i] = 0u;
-        reinterpret_cast<uint32_t*>(xp)[i] = 0u;
-    }
-    sum_xq = block_sum_int(sum_xq, redi);  // its barriers also publish the LDS tables
+    sum_xq = block_sum_int<kSepWaves>(sum_xq, redi);  // its barriers also publish the LDS tables
 
     int accb[U], accr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) { accb[u] = 0; accr[u] = 0; }
 
-    // one item: scan the residual flags, request the next item (whose stream
-    // offsets that scan gives), stage this item's residual slice, multiply
-    auto body = [&](int it, Buf& cur, Buf& nxt) {
+    // item it: A holds its classes (scanned), B the next item's (in flight),
+    // C receives the classes of item it + 2
+    auto body = [&](int it, Slot& A, Slot& B, Slot& C) {
         const int s = it % nsteps;
-        const int g = wave + kWaves * (it / nsteps);
+        const int g = wave + kSepWaves * (it / nsteps);
         float al[U], sr[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {  // requested ahead of the next item's data
+        for (int u = 0; u < U; ++u) {  // requested ahead of the next items' data
             const int rcl = min(g * U + u, rows - 1);
             al[u] = p.alpha[(int64_t)row0 + rcl];
             sr[u] = SKIP ? 1.0f : p.s_r[(int64_t)row0 + rcl];
         }
-        uint32_t R[U];
-        int excl[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            R[u] = cur.D[u] & (cur.D[u] >> 1) & 0x55555555u;  // residual flags at even bits
-            const int cnt = __builtin_popcount(R[u]);
-            const int incl = wave_incl_scan(cnt);
-            excl[u] = incl - cnt;
-            const int tot = __builtin_amdgcn_readlane(incl, kWave - 1);
-            nxt.base[u] = (s + 1 < nsteps) ? cur.base[u] + tot : 0;
-        }
-        issue(it + 1, nxt);
+        issue_codes(it + 2, C);
+        scan(it + 1, B, A, false);
         if constexpr (!SKIP) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                *reinterpret_cast<u32x4*>(sm + stage0 + u * kSepStage + 16 * lane) = cur.V1[u];
-                if (lane == 0) *reinterpret_cast<u32x4*>(sm + stage0 + u * kSepStage + kSepStep) = cur.V2[u];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<u32x4*>(sm + stage0 + u * kSepStage + 16 * (64 * j + lane)) = V[u][j];
+                if (lane < 4) *reinterpret_cast<uint32_t*>(sm + stage0 + u * kSepStage + kSepStep + 4 * lane) = X4[u];
             }
+            issue_vals(it + 1, B);
         }
-        const u32x4 xnat = *reinterpret_cast<const u32x4*>(xn + s * kSepStep + 16 * lane);
-        const u32x4 xper = *reinterpret_cast<const u32x4*>(xp + s * kSepStep + 16 * lane);
+        uint32_t a[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t dz = cur.D[u] ^ (R[u] << 1);  // residual class 3 -> 1 (no backbone term)
-            accb[u] = sdot4i(dz & 0x03030303u, xper[0], accb[u]);
-            accb[u] = sdot4i((dz >> 2) & 0x03030303u, xper[1], accb[u]);
-            accb[u] = sdot4i((dz >> 4) & 0x03030303u, xper[2], accb[u]);
-            accb[u] = sdot4i((dz >> 6) & 0x03030303u, xper[3], accb[u]);
-            if constexpr (!SKIP) {
-                uint32_t a = stage0 + (uint32_t)(u * kSepStage) + ((uint32_t)cur.base[u] & 15u) + (uint32_t)excl[u];
+        for (int u = 0; u < U; ++u)
+            a[u] = stage0 + (uint32_t)(u * kSepStage) + ((uint32_t)A.base[u] & 15u) + (uint32_t)A.excl[u];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t fl = (R[u] >> (8 * q)) & 0xFFu;
-                    const uint32_t sel = lut[fl];
-                    const uint32_t aw = a & ~3u;
-                    const uint32_t w0 = *reinterpret_cast<const uint32_t*>(sm + aw);
-                    const uint32_t w1 = *reinterpret_cast<const uint32_t*>(sm + aw + 4);
-                    const uint32_t win = __builtin_amdgcn_alignbyte(w1, w0, a);
-                    const uint32_t vals = __builtin_amdgcn_perm(win, 0u, sel);
-                    accr[u] = sdot4i(vals, xnat[q], accr[u]);
-                    a += (uint32_t)__builtin_popcount(fl);
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t xo = (uint32_t)(s * kSepStep + 1024 * d + 16 * lane);
+            const u32x4 xnat = *reinterpret_cast<const u32x4*>(xn + xo);
+            uint32_t xper[4];
+            if constexpr (XPL) {
+                const u32x4 t = *reinterpret_cast<const u32x4*>(xp + xo);
+                xper[0] = t[0]; xper[1] = t[1]; xper[2] = t[2]; xper[3] = t[3];
+            } else {
+                transpose4x4(xnat, xper);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t D = A.D[u][d];
+                const uint32_t R = D & (D >> 1) & 0x55555555u;
+                const uint32_t dz = D ^ (R << 1);  // residual class 3 -> 1 (no backbone term)
+                accb[u] = sdot4i(dz & 0x03030303u, xper[0], accb[u]);
+                accb[u] = sdot4i((dz >> 2) & 0x03030303u, xper[1], accb[u]);
+                accb[u] = sdot4i((dz >> 4) & 0x03030303u, xper[2], accb[u]);
+                accb[u] = sdot4i((dz >> 6) & 0x03030303u, xper[3], accb[u]);
+                if constexpr (!SKIP) {
+                    // the 4 groups' window offsets first, then all their LDS
+                    // reads, then the arithmetic (one LDS round trip per dword)
+                    uint32_t fl[4], ag[4], sel[4], w0[4], w1[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        fl[q] = (R >> (8 * q)) & 0xFFu;
+                        ag[q] = a[u];
+                        a[u] += (uint32_t)__builtin_popcount(fl[q]);
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        sel[q] = lut[fl[q]];
+                        const uint32_t aw = ag[q] & ~3u;
+                        w0[q] = *reinterpret_cast<const uint32_t*>(sm + aw);
+                        w1[q] = *reinterpret_cast<const uint32_t*>(sm + aw + 4);
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t win = __builtin_amdgcn_alignbyte(w1[q], w0[q], ag[q]);
+                        const uint32_t vals = __builtin_amdgcn_perm(win, 0u, sel[q]);
+                        accr[u] = sdot4i(vals, xnat[q], accr[u]);
+                    }
                 }
             }
         }
@@ -446,23 +571,24 @@ __global__ __launch_bounds__(kThreads) void sep_qgemv_kernel(SepParams p) {
             }
         }
     };
-    // two buffers in turn, so that no register copy waits for a load in
-    // flight; an odd item count ends with one item past the wave's last,
-    // which reads zeros and stores nothing
-    for (int it = 0; it < nit; it += 2) {
-        body(it, fa, fb);
-        body(it + 1, fb, fa);
+    // three slots in turn, so that no register copy waits for a load in
+    // flight; the last round may run up to two items past the wave's last,
+    // which read zeros and store nothing
+    for (int it = 0; it < nit; it += 3) {
+        body(it, S0, S1, S2);
+        body(it + 1, S1, S2, S0);
+        body(it + 2, S2, S0, S1);
     }
 }
 
-template <int XT, int U, bool SKIP>
+template <int XT, int U, bool SKIP, bool XPL>
 static hipError_t run_sep(const SepArgs& a, hipStream_t st) {
     const int K = (int)a.k;
     const int nsteps = (K + kSepStep - 1) / kSepStep;
-    const size_t lds = 1024 + 2 * (size_t)nsteps * kSepStep + (size_t)kWaves * U * kSepStage;
+    const size_t lds = kSepLdsHead + (size_t)nsteps * kSepStep * (XPL ? 2 : 1) + (SKIP ? 0 : (size_t)kSepWaves * U * kSepStage);
     const int cus = device_cu_count();
     const int64_t N = a.n;
-    const int64_t quantum = (int64_t)kWaves * U;
+    const int64_t quantum = (int64_t)kSepWaves * U;
     int64_t rpw = (N + 2 * cus - 1) / (2 * cus);  // about two workgroups per CU
     rpw = (rpw + quantum - 1) / quantum * quantum;
     // buffer ranges stay below 2 GiB
@@ -482,7 +608,7 @@ static hipError_t run_sep(const SepArgs& a, hipStream_t st) {
     p.k = K;
     p.rows_per_wg = (int32_t)rpw;
     const int grid = (int)((N + rpw - 1) / rpw);
-    auto kern = sep_qgemv_kernel<XT, U, SKIP>;
+    auto kern = sep_qgemv_kernel<XT, U, SKIP, XPL>;
     if (lds > 64 * 1024) {
         static bool attr_set = false;  // per instantiation
         if (!attr_set) {
@@ -492,13 +618,21 @@ static hipError_t run_sep(const SepArgs& a, hipStream_t st) {
             attr_set = true;
         }
     }
-    kern<<<grid, kThreads, lds, st>>>(p);
+    kern<<<grid, kSepThreads, lds, st>>>(p);
     return hipGetLastError();
 }
 
 hipError_t launch_sep_qgemv(const SepArgs& a, hipStream_t st) {
-    if (a.xt == 0) return a.skip ? run_sep<0, 2, true>(a, st) : run_sep<0, 2, false>(a, st);
-    return a.skip ? run_sep<1, 2, true>(a, st) : run_sep<1, 2, false>(a, st);
+    // One row per item: at two rows the slices' LDS leaves room for only one
+    // workgroup per CU, which measured slower on MI355X; the skip path has no
+    // slices and takes two.  The transposed copy of x stays in LDS while
+    // K <= 32768 (else it is formed in registers).
+    if (a.k <= 32768) {
+        if (a.xt == 0) return a.skip ? run_sep<0, 2, true, true>(a, st) : run_sep<0, 1, false, true>(a, st);
+        return a.skip ? run_sep<1, 2, true, true>(a, st) : run_sep<1, 1, false, true>(a, st);
+    }
+    if (a.xt == 0) return a.skip ? run_sep<0, 2, true, false>(a, st) : run_sep<0, 1, false, false>(a, st);
+    return a.skip ? run_sep<1, 2, true, false>(a, st) : run_sep<1, 1, false, false>(a, st);
 }
 
 }  // namespace qg
