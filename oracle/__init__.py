@@ -34,7 +34,7 @@ from .quant import (absmax_scale, quantize_with_scale, quantize_absmax,
                     gather_outlier_weights, dequantize, detect_outlier_channels)
 from .packing import (pack, unpack, pack_loops, unpack_loops)
 from .products import (int_dot_exact, int_gemm_exact, int_dot_bruteforce,
-                       y_w8a8, y_w8a16, y_ternary, y_sign_residual, y_prefill,
+                       y_w8a8, y_w8a16, y_w8a16_batch, y_ternary, y_sign_residual, y_prefill,
                        relative_method_error, normwise_error)
 
 __all__ = [n for n in dir() if not n.startswith("_")]

@@ -70,6 +70,18 @@ def y_w8a16(wq, s_w, x_bf16_bits) -> np.ndarray:
     return (np.asarray(wq, np.float64) @ x) / np.asarray(s_w, np.float64)
 
 
+def y_w8a16_batch(wq, s_w, x_bf16_bits) -> np.ndarray:
+    """Weight-only int8 output for a small batch of M tokens (decode of
+    several sequences at once; [SEP] section 3.1: at batch 1 the weights are
+    read once per token, so a batch reads them once for all M tokens):
+    y[t][n] = sum_k (wq[n,k] / s_w[n]) * x[t][k], fp64; x [M][K] bf16 bits,
+    y [M][N]."""
+    x = bf16_bits_to_f32(np.asarray(x_bf16_bits, np.uint16)).astype(np.float64)
+    if x.ndim != 2:
+        raise ValueError("x must be [M][K]")
+    return (x @ np.asarray(wq, np.float64).T) / np.asarray(s_w, np.float64)[None, :]
+
+
 def y_ternary(acc, gamma, s_x) -> np.ndarray:
     """Ternary output: y[n] = gamma * acc[n] / s_x, fp64 ([VG] 'BitNet b1.58':
     ternary weights add, skip or subtract each int8 activation; the sum is

@@ -199,3 +199,25 @@ def test_prefill_reference_linearity():
 def test_normwise_error():
     assert oracle.normwise_error([1.0, 2.0], [1.0, 2.0]) == 0.0
     assert abs(oracle.normwise_error([1.0, 2.1], [1.0, 2.0]) - 0.05) < 1e-12
+
+
+def test_batched_weight_only_reference():
+    """The M-token product: each token row is the batch-1 product (itself
+    pinned above against exact rationals), the layout is [M][N], an exact
+    rational check on a tiny case, and linearity across the batch."""
+    g = synth.rng(41)
+    n, k, m = 5, 24, 3
+    w = synth.gaussian(g, (n, k), 0.02)
+    wq, s_w = oracle.quantize_absmax(w, per_row=True)
+    xb = synth.to_bf16_bits(synth.gaussian(g, (m, k), 1.0))
+    y = oracle.y_w8a16_batch(wq, s_w, xb)
+    assert y.shape == (m, n)
+    for t in range(m):
+        assert np.array_equal(y[t], oracle.y_w8a16(wq, s_w, xb[t]))
+    xf = synth.bf16_bits_to_f32(xb)
+    for t in range(m):
+        for r in range(n):
+            exact = sum(Fraction(int(wq[r, c])) * Fraction(float(xf[t, c])) for c in range(k)) / Fraction(float(s_w[r]))
+            assert abs(y[t, r] - float(exact)) <= 1e-12 * max(1.0, abs(float(exact)))
+    # reversing the batch reverses the rows of y
+    assert np.array_equal(oracle.y_w8a16_batch(wq, s_w, xb[::-1]), y[::-1])
