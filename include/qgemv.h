@@ -83,6 +83,8 @@ typedef int32_t qg_status;
                                    prefill GEMMs read: a multiple of 8 bf16 = 16 B    */
 #define QG_MAX_OUT_LD   65536   /* largest row stride of an outlier operand          */
 #define QG_SEP_MAX_K    65536   /* k of the thresholded separated format             */
+#define QG_BATCH_MAX_M  16      /* tokens of a qg_qgemv_batch launch                 */
+#define QG_BATCH_MAX_K  262144  /* k of qg_qgemv_batch                               */
 
 /* Human-readable text for a status code (static storage). */
 const char* qg_status_str(qg_status s);
@@ -308,6 +310,28 @@ qg_status qg_qgemv(const qg_weight* w, int32_t amode, const void* x, int32_t xt,
  */
 qg_status qg_qgemv_grouped(const qg_weight* w, int32_t count, int32_t amode, const void* x, int32_t xt,
                            void* const* y, int32_t yt, int32_t* const* acc_out, void* stream);
+
+/*
+ * Weight-only int8 products for a small batch of tokens (decode of m
+ * sequences at once; [SEP] section 3.1: at batch 1 every weight is read once
+ * per token and the compute idles, so serving several tokens per read of
+ * the weights is what batching buys).  For every token t < m:
+ *   y[t][n] = (sum_k codes[n][k] * x[t][k]) / s_w[n]
+ * i.e. qg_qgemv's INT8 / QG_ACT_FLOAT product of each row of x; the
+ * products are exact and summed in fp32 (in another order than qg_qgemv's,
+ * so results agree to rounding, not bit for bit).
+ * w  : QG_WFMT_INT8 (codes [n][k] int8, scale = s_w[n]), 16-B aligned codes.
+ * x  : [m][k] bf16 (xt must be QG_BF16), 16-B aligned; 1 <= m <= QG_BATCH_MAX_M.
+ * y  : [m][n] of type yt (QG_F32 or QG_BF16, bf16 rounded to nearest even).
+ * k % 128 == 0, 128 <= k <= QG_BATCH_MAX_K; 1 <= n < 2^31.
+ * The grouped form runs count (1..QG_MAX_GROUP) matrices that share k, m and
+ * x in one launch (q, k and v; gate and up); w and y are HOST arrays of
+ * count entries, y[j] holding [m][w[j].n] outputs.
+ */
+qg_status qg_qgemv_batch(const qg_weight* w, int32_t m, const void* x, int32_t xt, void* y, int32_t yt,
+                         void* stream);
+qg_status qg_qgemv_batch_grouped(const qg_weight* w, int32_t count, int32_t m, const void* x, int32_t xt,
+                                 void* const* y, int32_t yt, void* stream);
 
 /*
  * Thresholded separated weights ([SEP] section 2.1: only the weights above a

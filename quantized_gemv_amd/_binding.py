@@ -29,6 +29,8 @@ QG_MAX_GROUP = 8
 QG_OUT_LD_ALIGN = 8
 QG_MAX_OUT_LD = 65536
 QG_SEP_MAX_K = 65536
+QG_BATCH_MAX_M = 16
+QG_BATCH_MAX_K = 262144
 
 _c_i32, _c_i64, _c_sz, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
@@ -58,6 +60,9 @@ _SIGS = {
     "qg_quantize_ternary": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "qg_split_sign_residual": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
     "qg_quantize_q4k": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
+    "qg_qgemv_batch": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp]),
+    "qg_qgemv_batch_grouped": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_i32, _c_vp, _c_i32,
+                                        ctypes.POINTER(_c_vp), _c_i32, _c_vp]),
     "qg_sep_resid_ld": (_c_i64, [_c_i64, _c_i32]),
     "qg_split_sep_threshold": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i32, _c_i32, _c_vp, _c_vp, _c_i64, _c_vp, _c_vp,
                                         _c_vp]),
@@ -277,6 +282,38 @@ def quantize_q4k(w: torch.Tensor):
     meta = torch.empty((n, k // 256, 16), dtype=torch.uint8, device=w.device)
     _check(lib().qg_quantize_q4k(_p(w), n, k, _p(codes), _p(meta), _stream(w)), "qg_quantize_q4k")
     return codes, meta
+
+
+def qgemv_batch(w: QWeight, x: torch.Tensor, y_dtype=torch.float32, y: torch.Tensor = None):
+    """Weight-only int8 product of a batch of tokens (qg_qgemv_batch): x bf16
+    [m][k] -> y [m][n]. Returns y."""
+    _dev(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be [m][k]")
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, w.n), dtype=y_dtype, device=x.device)
+    _dev(y, "y", (torch.float32, torch.bfloat16))
+    cw = w.c_struct()
+    _check(lib().qg_qgemv_batch(ctypes.byref(cw), m, _p(x), QG_BF16, _p(y), _xt(y), _stream(x)), "qg_qgemv_batch")
+    return y
+
+
+def qgemv_batch_grouped(weights: Sequence[QWeight], x: torch.Tensor, y_dtype=torch.float32, ys=None):
+    """qg_qgemv_batch_grouped: several int8 matrices sharing x [m][k] in one
+    launch. Returns the list of y [m][n_j]."""
+    _dev(x, "x", torch.bfloat16)
+    m = x.shape[0]
+    cnt = len(weights)
+    if not 1 <= cnt <= QG_MAX_GROUP:
+        raise ValueError("need 1..%d weights" % QG_MAX_GROUP)
+    if ys is None:
+        ys = [torch.empty((m, W.n), dtype=y_dtype, device=x.device) for W in weights]
+    arr = (CWeight * cnt)(*[W.c_struct() for W in weights])
+    yp = (_c_vp * cnt)(*[y.data_ptr() for y in ys])
+    _check(lib().qg_qgemv_batch_grouped(arr, cnt, m, _p(x), QG_BF16, yp, _xt(ys[0]), _stream(x)),
+           "qg_qgemv_batch_grouped")
+    return ys
 
 
 class SepWeight:

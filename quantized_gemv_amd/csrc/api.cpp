@@ -76,7 +76,7 @@ const char* qg_status_str(qg_status s) {
     }
 }
 
-int32_t qg_abi_version(void) { return 20100; }
+int32_t qg_abi_version(void) { return 20200; }
 
 size_t qg_quantize_absmax_workspace_bytes(int64_t rows, int64_t cols, int32_t gran) {
     if (gran != QG_PER_TENSOR || rows < 1 || cols < 8) return 0;
@@ -322,6 +322,39 @@ qg_status qg_qgemv_grouped(const qg_weight* w, int32_t count, int32_t amode, con
         a[m] = qgemv_args(&w[m], amode, x, xt, y[m], yt, acc);
     }
     return from_hip(qg::launch_qgemv_group(a, count, as_stream(stream)));
+}
+
+qg_status qg_qgemv_batch_grouped(const qg_weight* w, int32_t count, int32_t m, const void* x, int32_t xt,
+                                 void* const* y, int32_t yt, void* stream) {
+    if (!w || !y || !x) return QG_ERR_NULLPTR;
+    if (count < 1 || count > QG_MAX_GROUP) return QG_ERR_ARG;
+    if (xt != QG_BF16 || (yt != QG_F32 && yt != QG_BF16)) return QG_ERR_ARG;
+    if (m < 1 || m > QG_BATCH_MAX_M) return QG_ERR_SHAPE;
+    if (!aligned16(x)) return QG_ERR_ALIGN;
+    qg::BatchArgs a[QG_MAX_GROUP];
+    for (int32_t j = 0; j < count; ++j) {
+        const qg_weight& wj = w[j];
+        if (!wj.codes || !wj.scale || !y[j]) return QG_ERR_NULLPTR;
+        if (wj.fmt != QG_WFMT_INT8) return QG_ERR_ARG;
+        if (wj.n < 1 || wj.n >= ((int64_t)1 << 31)) return QG_ERR_SHAPE;
+        if (wj.k < 128 || wj.k % 128 != 0 || wj.k > QG_BATCH_MAX_K || wj.k != w[0].k) return QG_ERR_SHAPE;
+        if (!aligned16(wj.codes)) return QG_ERR_ALIGN;
+        a[j].n = wj.n;
+        a[j].k = wj.k;
+        a[j].m = m;
+        a[j].wq = static_cast<const int8_t*>(wj.codes);
+        a[j].s_w = wj.scale;
+        a[j].x = x;
+        a[j].y = y[j];
+        a[j].yt = yt;
+    }
+    return from_hip(qg::launch_qgemv_batch(a, count, as_stream(stream)));
+}
+
+qg_status qg_qgemv_batch(const qg_weight* w, int32_t m, const void* x, int32_t xt, void* y, int32_t yt,
+                         void* stream) {
+    void* ys[1] = {y};
+    return qg_qgemv_batch_grouped(w, 1, m, x, xt, ys, yt, stream);
 }
 
 size_t qg_qgemm_workspace_bytes(int64_t m, int64_t k, int32_t n_out) {

@@ -91,6 +91,19 @@ struct SepArgs {
 };
 hipError_t launch_sep_qgemv(const SepArgs& a, hipStream_t st);
 
+// Weight-only int8 products for a batch of m tokens (x bf16 [m][k]); the
+// entries of one launch share k, m, x and yt.
+struct BatchArgs {
+    int64_t n, k;
+    int m;
+    const int8_t* wq;
+    const float* s_w;
+    const void* x;
+    void* y;
+    int yt;
+};
+hipError_t launch_qgemv_batch(const BatchArgs* a, int count, hipStream_t st);
+
 int device_cu_count();
 
 }  // namespace qg

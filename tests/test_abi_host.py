@@ -48,7 +48,7 @@ def test_header_symbols_exported(qg):
     for name in decl:
         assert hasattr(l, name), name
     assert set(decl) == set(qg.EXPORTED)
-    assert qg.lib().qg_abi_version() == 20100
+    assert qg.lib().qg_abi_version() == 20200
     for st in range(0, 8):
         assert qg.status_str(st)
 
@@ -340,3 +340,35 @@ def test_validation_sep_threshold(qg):
     assert g(U, A, ld, A, A, 4, 1024, A, 0, 0, A, None, None) == 3
     assert g(A, U, ld, A, A, 4, 1024, A, 0, 0, A, None, None) == 3
     assert g(A, A, ld, A, A, 4, 1024, U, 1, 0, A, None, None) == 3
+
+
+def test_validation_qgemv_batch(qg):
+    l = qg.lib()
+
+    def W(fmt=0, n=64, k=256, codes=A, scale=A):
+        return qg.CWeight(fmt, 0, n, k, codes, None, scale, None)
+    f = l.qg_qgemv_batch
+    # (w, m, x, xt, y, yt, stream)
+    assert f(None, 4, A, 1, A, 0, None) == 1
+    assert f(ctypes.byref(W(codes=None)), 4, A, 1, A, 0, None) == 1
+    assert f(ctypes.byref(W(scale=None)), 4, A, 1, A, 0, None) == 1
+    assert f(ctypes.byref(W()), 4, None, 1, A, 0, None) == 1
+    assert f(ctypes.byref(W()), 4, A, 0, A, 0, None) == 4          # x must be bf16
+    assert f(ctypes.byref(W()), 4, A, 1, A, 2, None) == 4          # y dtype
+    assert f(ctypes.byref(W(fmt=1)), 4, A, 1, A, 0, None) == 4     # int8 weights only
+    assert f(ctypes.byref(W()), 0, A, 1, A, 0, None) == 2          # m >= 1
+    assert f(ctypes.byref(W()), 17, A, 1, A, 0, None) == 2         # m <= QG_BATCH_MAX_M
+    assert f(ctypes.byref(W(k=192)), 4, A, 1, A, 0, None) == 2     # k % 128
+    assert f(ctypes.byref(W(k=262144 + 128)), 4, A, 1, A, 0, None) == 2
+    assert f(ctypes.byref(W(n=0)), 4, A, 1, A, 0, None) == 2
+    assert f(ctypes.byref(W(codes=U)), 4, A, 1, A, 0, None) == 3
+    assert f(ctypes.byref(W()), 4, U, 1, A, 0, None) == 3
+    g = l.qg_qgemv_batch_grouped
+    arr = (qg.CWeight * 2)(W(), W(k=512))
+    ys = (ctypes.c_void_p * 2)(A, A)
+    assert g(arr, 2, 4, A, 1, ys, 0, None) == 2                    # k must agree
+    assert g(arr, 0, 4, A, 1, ys, 0, None) == 4
+    assert g(arr, 9, 4, A, 1, ys, 0, None) == 4
+    ys0 = (ctypes.c_void_p * 2)(A, None)
+    arr2 = (qg.CWeight * 2)(W(), W())
+    assert g(arr2, 2, 4, A, 1, ys0, 0, None) == 1
