@@ -470,6 +470,36 @@ def bench_sep_threshold(torch, qg, synth, dev, rotate_count):
     return out
 
 
+def bench_small_batch(torch, qg, dev, weights, batches=(4, 16)):
+    """The headline's decode step (32 layers, the same weights and the same
+    four launches per layer) for a batch of M tokens."""
+    per_layer = 7
+    layers = len(weights) // per_layer
+    groups_per_layer = [[0, 1, 2], [3], [4, 5], [6]]
+    step_bytes = sum(W.n * W.k + 4 * W.n for _, W, _ in weights)
+    out = {}
+    for m in batches:
+        xs = {k: torch.randn(m, k, device=dev).to(torch.bfloat16) for k in (4096, 11008)}
+        ys = [torch.empty((m, W.n), dtype=torch.bfloat16, device=dev) for _, W, _ in weights[:per_layer]]
+        launches = []
+        for li in range(layers):
+            for grp in groups_per_layer:
+                ws_ = [weights[li * per_layer + i][1] for i in grp]
+                yy = [ys[i] for i in grp]
+                launches.append((lambda ws_, yy: (lambda: qg.qgemv_batch_grouped(ws_, xs[ws_[0].k], ys=yy)))(ws_, yy))
+        t = Timed(torch, launches)
+        t.run(1)
+        sec = t.run(5)
+        out["small_batch_decode_step_m%d" % m] = {
+            "tokens": m, "ms_per_step": round(sec * 1e3, 4), "tokens_per_s": round(m / sec, 1),
+            "weight_GBps": round(step_bytes / sec / 1e9, 1), "hbm_frac": round(step_bytes / sec / 1e9 / HBM_PEAK_GBS, 4),
+            "launches_per_step": len(launches),
+            "note": "32 layers x (q,k,v grouped, o, (gate,up) grouped, down), bf16 MFMA on int8 codes widened in registers"}
+        log("small batch m=%d: %.3f ms per step, %.0f tokens/s" % (m, sec * 1e3, m / sec))
+        del t, launches
+    return out
+
+
 def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
     out = {}
     GiB = 1 << 30
@@ -496,6 +526,10 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
                                        "hbm_frac": round(per / sec / 1e9 / HBM_PEAK_GBS, 4),
                                        "rotating_copies": len(ws)}
         log("%s: %.2f us, %.0f GB/s" % (name, sec * 1e6, per / sec / 1e9))
+
+    # -- small-batch decode: the same 32-layer step for M tokens at once
+    #    (weight-only int8 products of qg_qgemv_batch_grouped on bf16 MFMA)
+    out.update(bench_small_batch(torch, qg, dev, weights))
 
     # -- tiny W8A8 GEMV (launch-latency bound)
     wl = synth.tiny_gemv()

@@ -324,6 +324,7 @@ qg_status qg_qgemv_grouped(const qg_weight* w, int32_t count, int32_t amode, con
  * x  : [m][k] bf16 (xt must be QG_BF16), 16-B aligned; 1 <= m <= QG_BATCH_MAX_M.
  * y  : [m][n] of type yt (QG_F32 or QG_BF16, bf16 rounded to nearest even).
  * k % 128 == 0, 128 <= k <= QG_BATCH_MAX_K; 1 <= n < 2^31.
+ * m = 1 (with k <= QG_QGEMV_MAX_K) runs qg_qgemv's batch-1 kernel.
  * The grouped form runs count (1..QG_MAX_GROUP) matrices that share k, m and
  * x in one launch (q, k and v; gate and up); w and y are HOST arrays of
  * count entries, y[j] holding [m][w[j].n] outputs.

@@ -348,6 +348,12 @@ qg_status qg_qgemv_batch_grouped(const qg_weight* w, int32_t count, int32_t m, c
         a[j].y = y[j];
         a[j].yt = yt;
     }
+    if (m == 1 && w[0].k <= QG_QGEMV_MAX_K) {
+        // one token: the batch-1 kernel (same definition, y [1][n] is y [n])
+        qg::QgemvArgs b[QG_MAX_GROUP];
+        for (int32_t j = 0; j < count; ++j) b[j] = qgemv_args(&w[j], QG_ACT_FLOAT, x, xt, y[j], yt, nullptr);
+        return from_hip(qg::launch_qgemv_group(b, count, as_stream(stream)));
+    }
     return from_hip(qg::launch_qgemv_batch(a, count, as_stream(stream)));
 }
 

@@ -10,9 +10,11 @@
 // batch-1 weight-only product of every token: y[t][n] = (sum_k q[n][k] *
 // x[t][k]) / s_w[n].
 //
-// Work: a workgroup owns one 16-row tile of a matrix (a grouped launch
-// covers several matrices that share x); its 8 waves split K in units of 64
-// (wave w takes units w, w + 8, ...).  In a unit, lane l loads 16 codes of
+// Work: the tiles are 16 rows of a matrix (a grouped launch covers several
+// matrices that share x); a workgroup takes tiles in turn (the grid is one
+// round of resident workgroups) and its 8 waves split K in units of 64
+// (wave w takes a contiguous range of them, so each row is read in long
+// runs).  In a unit, lane l loads 16 codes of
 // row l % 16 and the same 16 activations (k group l / 16) of token l % 16
 // (tokens >= M read zeros through the range check, no traffic): the A and B
 // fragments of two MFMAs.  Four units per iteration, double-buffered.  The
@@ -68,38 +70,65 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_kernel(BGroup grp) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int mi = 0;
-    while (mi + 1 < grp.count && (int)blockIdx.x >= grp.wg_start[mi + 1]) ++mi;
-    const BMat& mat = grp.mats[mi];
     const int K = grp.k, M = grp.m;
-    const int row0 = ((int)blockIdx.x - grp.wg_start[mi]) * 16;
-    const int rows = min(16, mat.n - row0);
     const int i = lane & 15, g = lane >> 4;  // A row / B token, k group
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(mat.wq + (int64_t)row0 * K, (uint32_t)(rows * K));
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(grp.x, (uint32_t)(M * K * 2));
-    const uint32_t oob_w = (uint32_t)(rows * K), oob_x = (uint32_t)(M * K * 2);
+    const uint32_t oob_x = (uint32_t)(M * K * 2);
     const int C = K / kBUnit;
-    const int mine = C > wave ? (C - wave + kBWaves - 1) / kBWaves : 0;  // units of this wave
-    const int nit = (mine + kBJS - 1) / kBJS;
+    // iterations per tile: the same for every wave (the largest share), since
+    // the tile-end barriers are counted in items; shorter shares read zeros
+    const int most = (C + kBWaves - 1) / kBWaves;
+    const int nit = most > 0 ? (most + kBJS - 1) / kBJS : 1;
+    const int ntiles = grp.wg_start[grp.count];
+    // the workgroup's tiles are blockIdx.x + gridDim.x * j; every wave walks
+    // the flat sequence of (tile, iteration) items of them, so the next
+    // tile's loads are in flight while a tile is reduced
+    const int my_tiles = ntiles > (int)blockIdx.x ? (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
+    const int nitems = my_tiles * nit;
 
+    struct Tile {
+        const BMat* mat;
+        int row0, rows;
+    };
+    auto tile_of = [&](int it) {
+        const int tile = (int)blockIdx.x + (int)gridDim.x * (it / nit);
+        int mi = 0;
+        while (mi + 1 < grp.count && tile >= grp.wg_start[mi + 1]) ++mi;
+        Tile t;
+        t.mat = &grp.mats[mi];
+        t.row0 = (tile - grp.wg_start[mi]) * 16;
+        t.rows = it < nitems ? min(16, t.mat->n - t.row0) : 0;  // past the last item: nothing to read
+        return t;
+    };
     struct Frag {
         u32x4 w[kBJS], xa[kBJS], xb[kBJS];
+        float sw[4];  // this lane's four row scales (used by wave 0)
     };
     auto issue = [&](int it, Frag& f) {
+        const Tile t = tile_of(it);
+        const int itn = it % nit;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(t.mat->s_w + t.row0, (uint32_t)(t.rows * 4));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 4 * g + r;
+            f.sw[r] = __uint_as_float(load4(rs, row < t.rows ? (uint32_t)(4 * row) : (uint32_t)(t.rows * 4)));
+        }
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(t.mat->wq + (int64_t)t.row0 * K, (uint32_t)(t.rows * K));
+        const uint32_t oob_w = (uint32_t)(t.rows * K);
 #pragma unroll
         for (int j = 0; j < kBJS; ++j) {
-            const int u = kBJS * it + j;
-            const int c = wave + kBWaves * u;
-            const bool ok = u < mine;
+            const int u = kBJS * itn + j;
+            const int c = wave * most + u;  // this wave's contiguous range of units
+            const bool ok = u < most && c < C && t.rows > 0;
             const int kk = c * kBUnit + 16 * g;
-            f.w[j] = load16(rw, (ok && i < rows) ? (uint32_t)(i * K + kk) : oob_w);
+            f.w[j] = load16(rw, (ok && i < t.rows) ? (uint32_t)(i * K + kk) : oob_w);
             const uint32_t xo = (uint32_t)((i * K + kk) * 2);
             f.xa[j] = load16(rx, (ok && i < M) ? xo : oob_x);
             f.xb[j] = load16(rx, (ok && i < M) ? xo + 16u : oob_x);
         }
     };
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    auto consume = [&](const Frag& f) {
+    auto consume = [&](int it, const Frag& f) {
 #pragma unroll
         for (int j = 0; j < kBJS; ++j) {
             bf16x8 a0, a1;
@@ -107,48 +136,55 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_kernel(BGroup grp) {
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8, f.xa[j]), acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8, f.xb[j]), acc, 0, 0, 0);
         }
+        if (it % nit == nit - 1 && it < nitems) {
+            // end of a tile: sum the eight waves' partial tiles (LDS-only
+            // barriers: the next items' loads stay in flight)
+            part[wave][lane] = acc;
+            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            lds_barrier();
+            if (wave == 0) {
+                const Tile t = tile_of(it);
+                f32x4 s = part[0][lane];
+#pragma unroll
+                for (int w = 1; w < kBWaves; ++w) {
+                    const f32x4 q = part[w][lane];
+                    s[0] += q[0];
+                    s[1] += q[1];
+                    s[2] += q[2];
+                    s[3] += q[3];
+                }
+                const int tok = lane & 15;
+                if (tok < M) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 4 * g + r;
+                        if (row < t.rows) {
+                            const float o = s[r] / f.sw[r];
+                            const int64_t at = (int64_t)tok * t.mat->n + t.row0 + row;
+                            if constexpr (YT == 0) static_cast<float*>(t.mat->y)[at] = o;
+                            else static_cast<uint16_t*>(t.mat->y)[at] = (uint16_t)f32_to_bf16(o);
+                        }
+                    }
+                }
+            }
+            lds_barrier();  // part[] is reused by the next tile
+        }
     };
     Frag fa, fb;
     issue(0, fa);
     // two buffers in turn (no register copy waits for a load in flight); the
-    // last round may consume one iteration past the wave's last, all zeros.
-    // The scheduling barriers keep each iteration's loads ahead of the
-    // arithmetic on the previous one.
-    for (int it = 0; it < nit; it += 2) {
+    // last round may run one item past the wave's last, which reads zeros
+    // and stores nothing.  The scheduling barriers keep each item's loads
+    // ahead of the arithmetic on the previous one.
+    for (int it = 0; it < nitems; it += 2) {
         issue(it + 1, fb);
         __builtin_amdgcn_sched_barrier(0);
-        consume(fa);
+        consume(it, fa);
         __builtin_amdgcn_sched_barrier(0);
         issue(it + 2, fa);
         __builtin_amdgcn_sched_barrier(0);
-        consume(fb);
+        consume(it + 1, fb);
         __builtin_amdgcn_sched_barrier(0);
-    }
-    part[wave][lane] = acc;
-    __syncthreads();
-    if (wave == 0) {
-        f32x4 s = part[0][lane];
-#pragma unroll
-        for (int w = 1; w < kBWaves; ++w) {
-            const f32x4 t = part[w][lane];
-            s[0] += t[0];
-            s[1] += t[1];
-            s[2] += t[2];
-            s[3] += t[3];
-        }
-        const int t = lane & 15;  // token
-        if (t < M) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 4 * (lane >> 4) + r;
-                if (row < rows) {
-                    const float o = s[r] / mat.s_w[row0 + row];
-                    const int64_t at = (int64_t)t * mat.n + row0 + row;
-                    if constexpr (YT == 0) static_cast<float*>(mat.y)[at] = o;
-                    else static_cast<uint16_t*>(mat.y)[at] = (uint16_t)f32_to_bf16(o);
-                }
-            }
-        }
     }
 }
 
@@ -158,18 +194,22 @@ hipError_t launch_qgemv_batch(const BatchArgs* a, int count, hipStream_t st) {
     g.k = (int32_t)a[0].k;
     g.m = a[0].m;
     g.x = static_cast<const uint16_t*>(a[0].x);
-    int wg = 0;
+    int tiles = 0;
     for (int j = 0; j < count; ++j) {
         g.mats[j].wq = a[j].wq;
         g.mats[j].s_w = a[j].s_w;
         g.mats[j].y = a[j].y;
         g.mats[j].n = (int32_t)a[j].n;
-        g.wg_start[j] = wg;
-        wg += (int)((a[j].n + 15) / 16);
+        g.wg_start[j] = tiles;
+        tiles += (int)((a[j].n + 15) / 16);
     }
-    for (int j = count; j <= kMaxGroupLaunch; ++j) g.wg_start[j] = wg;
-    if (a[0].yt == 0) qgemv_batch_kernel<0><<<wg, kBThreads, 0, st>>>(g);
-    else qgemv_batch_kernel<1><<<wg, kBThreads, 0, st>>>(g);
+    for (int j = count; j <= kMaxGroupLaunch; ++j) g.wg_start[j] = tiles;
+    // two resident workgroups per CU (the register budget); more tiles than
+    // that are walked by the workgroups in turn
+    const int slots = 2 * device_cu_count();
+    const int grid = tiles < slots ? tiles : slots;
+    if (a[0].yt == 0) qgemv_batch_kernel<0><<<grid, kBThreads, 0, st>>>(g);
+    else qgemv_batch_kernel<1><<<grid, kBThreads, 0, st>>>(g);
     return hipGetLastError();
 }
 

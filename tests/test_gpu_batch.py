@@ -55,7 +55,8 @@ def _guarded2(m, n, dtype, guard=64):
 
 
 @pytest.mark.parametrize("n,k,m", [(16, 128, 1), (7, 256, 16), (40, 1152, 2), (300, 4096, 5), (4096, 4096, 16),
-                                   (11008, 4096, 8), (4096, 11008, 3), (33, 32768, 16), (1000, 128, 9)])
+                                   (11008, 4096, 8), (4096, 11008, 3), (33, 32768, 16), (1000, 128, 9),
+                                   (2000, 2176, 4)])
 def test_qgemv_batch(qg, n, k, m):
     note("qgemv batch %dx%d m=%d" % (n, k, m))
     w, xb = _case(n, k, m, n + 3 * k + m)
@@ -75,14 +76,23 @@ def test_qgemv_batch(qg, n, k, m):
 
 
 def test_qgemv_batch_one_token_matches_batch1(qg):
-    # m = 1 is the batch-1 product: the same values to rounding
+    # m = 1 runs the batch-1 kernel: bit-identical to qg_qgemv
     note("qgemv batch m=1 vs qg_qgemv")
     w, xb = _case(4096, 4096, 1, 77)
     W, _, _ = _weight(qg, w)
     y1 = qg.qgemv(W, dev_bf16(xb[0]), act_int8=False, y_dtype=torch.float32)
     yb = qg.qgemv_batch(W, dev_bf16(xb))
-    a, b = host(y1), host(yb)[0]
-    assert np.max(np.abs(a - b)) <= 1e-5 * np.max(np.abs(a))
+    assert np.array_equal(host(y1), host(yb)[0])
+
+
+def test_qgemv_batch_one_token_large_k(qg):
+    # m = 1 beyond the batch-1 kernel's K: the MFMA kernel
+    note("qgemv batch m=1 k=65536")
+    w, xb = _case(64, 65536, 1, 78)
+    W, wq, s_w = _weight(qg, w)
+    q_ref, s_ref = oracle.quantize_absmax(w, per_row=True)
+    y = qg.qgemv_batch(W, dev_bf16(xb))
+    assert oracle.normwise_error(host(y), oracle.y_w8a16_batch(q_ref, s_ref, xb)) <= TOL_F32
 
 
 def test_qgemv_batch_grouped_matches_single(qg):
