@@ -13,6 +13,8 @@
  *   [VG]   "A Visual Guide to LLM Quantization" (Chinese translation),
  *          puppylpg.github.io.
  *   [OVR]  LLM quantization overview, 2048ai.net/68d1f9e38867235e13877cac.html.
+ *   [DQ]   news report on ISTA-DASLab's quantization split by inference
+ *          phase, ai4snews.wisdomeyes.cn/zh/news/786ff1c6c728dd1806bd2871.
  *   [T158] "1.58 bits vs FP8: what ternary weights actually buy",
  *          feinterview.poetries.top.
  *
@@ -85,6 +87,7 @@ typedef int32_t qg_status;
 #define QG_SEP_MAX_K    65536   /* k of the thresholded separated format             */
 #define QG_BATCH_MAX_M  16      /* tokens of a qg_qgemv_batch launch                 */
 #define QG_BATCH_MAX_K  262144  /* k of qg_qgemv_batch                               */
+#define QG_MX_BLOCK     32      /* values per MXFP4 block (one E8M0 scale)           */
 
 /* Human-readable text for a status code (static storage). */
 const char* qg_status_str(qg_status s);
@@ -384,6 +387,40 @@ qg_status qg_split_sep_threshold(const float* w, int64_t n, int64_t k, int32_t p
 qg_status qg_qgemv_sep(const uint8_t* cls, const int8_t* rv, int64_t rv_ld, const float* alpha,
                        const float* s_r, int64_t n, int64_t k, const void* x, int32_t xt,
                        int32_t skip_residual, float* y, int32_t* acc_out, void* stream);
+
+/*
+ * MXFP4 block-scaled 4-bit floats for the format-separated prefill ([DQ]:
+ * "format separation" runs the prefill on the accelerator's native low-bit
+ * compute -- NVFP4 on the hardware it measures -- while decode keeps a
+ * low-bit weight-only format).  MI355X's matrix cores take OCP MXFP4 natively:
+ *   a block is QG_MX_BLOCK consecutive values of a row (along K);
+ *   e = floor(log2 max|v|) - 2 of the block, clamped to [-127, 127] (0 for an
+ *       all-zero block), stored as the E8M0 byte e + 127;
+ *   element = the E2M1 value (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes
+ *       0..7) nearest to v / 2^e, ties to the even code, saturating at 6;
+ *       bit 3 is the sign, set for v < 0.
+ * Storage: codes [rows][cols/2] bytes, element 2j in the low nibble of byte
+ * j; scales [rows][cols/32] bytes.
+ *
+ * qg_quantize_mxfp4: x [rows][cols] of type xt (QG_F32 or QG_BF16);
+ *   cols % 32 == 0; rows >= 1; x and codes 16-B aligned.
+ * qg_gemm_mxfp4: Y[m][n] = sum_k A[m][k] * B[n][k] over the decoded values,
+ *   products exact, fp32 sums.  a, b: codes of [m][k] and [n][k]; as, bs
+ *   their scales; y [m][n] fp32.  k % 256 == 0, 256 <= k <= 262144;
+ *   1 <= m, n < 2^31, m * k and n * k <= 2^40; code and scale pointers
+ *   16-B aligned.
+ * qg_prefill_mxfp4: the format-separated prefill of activations x [m][k]
+ *   bf16 against MXFP4 weights: qg_quantize_mxfp4 of x into the workspace
+ *   (qg_prefill_mxfp4_workspace_bytes(m, k) bytes, 16-B aligned; its
+ *   contents on entry do not matter), then qg_gemm_mxfp4.
+ */
+qg_status qg_quantize_mxfp4(const void* x, int32_t xt, int64_t rows, int64_t cols, uint8_t* codes,
+                            uint8_t* scales, void* stream);
+qg_status qg_gemm_mxfp4(const uint8_t* a, const uint8_t* a_scales, int64_t m, int64_t k, const uint8_t* b,
+                        const uint8_t* b_scales, int64_t n, float* y, void* stream);
+size_t qg_prefill_mxfp4_workspace_bytes(int64_t m, int64_t k);
+qg_status qg_prefill_mxfp4(const void* x, int64_t m, int64_t k, const uint8_t* w, const uint8_t* w_scales,
+                           int64_t n, float* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * W8A8 prefill GEMM with the outlier-channel split ([SEP] section 2.2: outlier

@@ -19,6 +19,8 @@ Sources (cited by short tag throughout)
          BitNet, BitNet b1.58; figures 15-60).
   [OVR]  LLM quantization overview, 2048ai.net/68d1f9e38867235e13877cac.html
          (sections 1-6).
+  [DQ]   news report on ISTA-DASLab's quantization split by inference
+         phase (prefill / decode), ai4snews.wisdomeyes.cn/zh/news/786ff1c6c728dd1806bd2871.
   [T158] "1.58 bits vs FP8: what ternary weights actually buy",
          feinterview.poetries.top.
 

@@ -3,8 +3,7 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-[DQ] (the fourth page, on splitting quantization by inference phase):
-"format separation" runs the prefill on the accelerator's native low-bit
+[DQ] (quantization split by inference phase): "format separation" runs the prefill on the accelerator's native low-bit
 quantized compute (NVFP4 on the hardware the page measures) while decode
 keeps a low-bit weight-only format; the prefill speed-up comes from that
 native compute.  The native 4-bit block format of this library's matrix
@@ -36,8 +35,16 @@ EMAX_ELEM = 2
 
 def e2m1_round(a: np.ndarray) -> np.ndarray:
     """Magnitude code 0..7 of |value| a >= 0: nearest E2M1 value, ties to the
-    even code, saturating at 6 (brute force over the 8 values)."""
-    a = np.minimum(np.asarray(a, np.float64), 6.0)
+    even code, saturating at 6 (brute force over the 8 values; large inputs
+    are taken a slice at a time to bound memory)."""
+    a = np.asarray(a, np.float64)
+    if a.size > (1 << 20):
+        flat = a.ravel()
+        out = np.empty(flat.size, np.uint8)
+        for lo in range(0, flat.size, 1 << 20):
+            out[lo:lo + (1 << 20)] = e2m1_round(flat[lo:lo + (1 << 20)])
+        return out.reshape(a.shape)
+    a = np.minimum(a, 6.0)
     d = np.abs(a[..., None] - E2M1)                       # distance to every value
     best = d.min(axis=-1, keepdims=True)
     cand = d == best                                       # nearest (one or two)

@@ -31,6 +31,7 @@ QG_MAX_OUT_LD = 65536
 QG_SEP_MAX_K = 65536
 QG_BATCH_MAX_M = 16
 QG_BATCH_MAX_K = 262144
+QG_MX_BLOCK = 32
 
 _c_i32, _c_i64, _c_sz, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
@@ -63,6 +64,10 @@ _SIGS = {
     "qg_qgemv_batch": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp]),
     "qg_qgemv_batch_grouped": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_i32, _c_vp, _c_i32,
                                         ctypes.POINTER(_c_vp), _c_i32, _c_vp]),
+    "qg_quantize_mxfp4": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
+    "qg_gemm_mxfp4": (_c_i32, [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp, _c_vp]),
+    "qg_prefill_mxfp4_workspace_bytes": (_c_sz, [_c_i64, _c_i64]),
+    "qg_prefill_mxfp4": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_sz, _c_vp]),
     "qg_sep_resid_ld": (_c_i64, [_c_i64, _c_i32]),
     "qg_split_sep_threshold": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i32, _c_i32, _c_vp, _c_vp, _c_i64, _c_vp, _c_vp,
                                         _c_vp]),
@@ -314,6 +319,47 @@ def qgemv_batch_grouped(weights: Sequence[QWeight], x: torch.Tensor, y_dtype=tor
     _check(lib().qg_qgemv_batch_grouped(arr, cnt, m, _p(x), QG_BF16, yp, _xt(ys[0]), _stream(x)),
            "qg_qgemv_batch_grouped")
     return ys
+
+
+def quantize_mxfp4(x: torch.Tensor):
+    """MXFP4 quantization of the rows of x [rows][cols] (fp32 or bf16)
+    (qg_quantize_mxfp4). Returns (codes uint8 [rows][cols/2], scales uint8
+    [rows][cols/32])."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    r, c = x.shape
+    codes = torch.empty((r, c // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((r, c // 32), dtype=torch.uint8, device=x.device)
+    _check(lib().qg_quantize_mxfp4(_p(x), _xt(x), r, c, _p(codes), _p(scales), _stream(x)), "qg_quantize_mxfp4")
+    return codes, scales
+
+
+def gemm_mxfp4(a, a_scales, b, b_scales, y: torch.Tensor = None):
+    """Y = A B^T of two MXFP4 operands (qg_gemm_mxfp4). Returns y fp32 [m][n]."""
+    for t, nm in ((a, "a"), (a_scales, "a_scales"), (b, "b"), (b_scales, "b_scales")):
+        _dev(t, nm, torch.uint8)
+    m, n, k = a.shape[0], b.shape[0], 2 * a.shape[1]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=a.device)
+    _dev(y, "y", torch.float32)
+    _check(lib().qg_gemm_mxfp4(_p(a), _p(a_scales), m, k, _p(b), _p(b_scales), n, _p(y), _stream(a)),
+           "qg_gemm_mxfp4")
+    return y
+
+
+def prefill_mxfp4(x: torch.Tensor, w, w_scales, y: torch.Tensor = None, ws: torch.Tensor = None):
+    """Format-separated prefill (qg_prefill_mxfp4): x bf16 [m][k] quantized to
+    MXFP4 in the workspace, times the MXFP4 weights. Returns y fp32 [m][n]."""
+    _dev(x, "x", torch.bfloat16)
+    m, k = x.shape
+    n = w.shape[0]
+    need = int(lib().qg_prefill_mxfp4_workspace_bytes(m, k))
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _check(lib().qg_prefill_mxfp4(_p(x), m, k, _p(w), _p(w_scales), n, _p(y), _p(ws), ws.numel(), _stream(x)),
+           "qg_prefill_mxfp4")
+    return y
 
 
 class SepWeight:

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqgemv.so")
-SOURCES = ["api.cpp", "quantize.hip", "pack.hip", "qgemv.hip", "qgemm.hip", "detect.hip", "sepq.hip", "qgemv_batch.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "pack.hip", "qgemv.hip", "qgemm.hip", "detect.hip", "sepq.hip", "qgemv_batch.hip", "mx.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -76,7 +76,7 @@ const char* qg_status_str(qg_status s) {
     }
 }
 
-int32_t qg_abi_version(void) { return 20200; }
+int32_t qg_abi_version(void) { return 20300; }
 
 size_t qg_quantize_absmax_workspace_bytes(int64_t rows, int64_t cols, int32_t gran) {
     if (gran != QG_PER_TENSOR || rows < 1 || cols < 8) return 0;
@@ -361,6 +361,62 @@ qg_status qg_qgemv_batch(const qg_weight* w, int32_t m, const void* x, int32_t x
                          void* stream) {
     void* ys[1] = {y};
     return qg_qgemv_batch_grouped(w, 1, m, x, xt, ys, yt, stream);
+}
+
+qg_status qg_quantize_mxfp4(const void* x, int32_t xt, int64_t rows, int64_t cols, uint8_t* codes,
+                            uint8_t* scales, void* stream) {
+    if (!x || !codes || !scales) return QG_ERR_NULLPTR;
+    if (xt != QG_F32 && xt != QG_BF16) return QG_ERR_ARG;
+    if (rows < 1 || cols < QG_MX_BLOCK || cols % QG_MX_BLOCK != 0 || rows > ((int64_t)1 << 40) / cols)
+        return QG_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(codes)) return QG_ERR_ALIGN;
+    return from_hip(qg::launch_quantize_mxfp4(x, xt, rows, cols, codes, scales, as_stream(stream)));
+}
+
+static qg_status check_mx_gemm(int64_t m, int64_t k, int64_t n) {
+    if (m < 1 || n < 1 || m >= ((int64_t)1 << 31) || n >= ((int64_t)1 << 31)) return QG_ERR_SHAPE;
+    if (k < 256 || k % 256 != 0 || k > 262144) return QG_ERR_SHAPE;
+    if (m > ((int64_t)1 << 40) / k || n > ((int64_t)1 << 40) / k) return QG_ERR_SHAPE;
+    return QG_OK;
+}
+
+qg_status qg_gemm_mxfp4(const uint8_t* a, const uint8_t* a_scales, int64_t m, int64_t k, const uint8_t* b,
+                        const uint8_t* b_scales, int64_t n, float* y, void* stream) {
+    if (!a || !a_scales || !b || !b_scales || !y) return QG_ERR_NULLPTR;
+    const qg_status st = check_mx_gemm(m, k, n);
+    if (st != QG_OK) return st;
+    if (!aligned16(a) || !aligned16(a_scales) || !aligned16(b) || !aligned16(b_scales)) return QG_ERR_ALIGN;
+    return from_hip(qg::launch_gemm_mxfp4(a, a_scales, m, k, b, b_scales, n, y, as_stream(stream)));
+}
+
+// workspace of the MXFP4 prefill: codes [m][k/2] | scales [m][k/32], 256-B aligned parts
+static size_t mx_layout(int64_t m, int64_t k, size_t* off_scales) {
+    const size_t codes = align_up((size_t)m * (size_t)(k / 2), 256);
+    if (off_scales) *off_scales = codes;
+    return codes + align_up((size_t)m * (size_t)(k / 32), 256);
+}
+
+size_t qg_prefill_mxfp4_workspace_bytes(int64_t m, int64_t k) {
+    if (check_mx_gemm(m, k, 1) != QG_OK) return 0;
+    return mx_layout(m, k, nullptr);
+}
+
+qg_status qg_prefill_mxfp4(const void* x, int64_t m, int64_t k, const uint8_t* w, const uint8_t* w_scales,
+                           int64_t n, float* y, void* ws, size_t ws_bytes, void* stream) {
+    if (!x || !w || !w_scales || !y) return QG_ERR_NULLPTR;
+    const qg_status st = check_mx_gemm(m, k, n);
+    if (st != QG_OK) return st;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(w_scales)) return QG_ERR_ALIGN;
+    size_t off_s = 0;
+    const size_t need = mx_layout(m, k, &off_s);
+    if (!ws || ws_bytes < need) return QG_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QG_ERR_ALIGN;
+    uint8_t* xc = static_cast<uint8_t*>(ws);
+    uint8_t* xs = xc + off_s;
+    hipStream_t s = as_stream(stream);
+    hipError_t e = qg::launch_quantize_mxfp4(x, QG_BF16, m, k, xc, xs, s);
+    if (e != hipSuccess) return QG_ERR_HIP;
+    return from_hip(qg::launch_gemm_mxfp4(xc, xs, m, k, w, w_scales, n, y, s));
 }
 
 size_t qg_qgemm_workspace_bytes(int64_t m, int64_t k, int32_t n_out) {

@@ -104,6 +104,13 @@ struct BatchArgs {
 };
 hipError_t launch_qgemv_batch(const BatchArgs* a, int count, hipStream_t st);
 
+// MXFP4: codes [rows][cols/2] (low nibble first) and E8M0 scales
+// [rows][cols/32]; GEMM Y[m][n] = sum_k A[m][k] B[n][k] (fp32).
+hipError_t launch_quantize_mxfp4(const void* x, int xt, int64_t rows, int64_t cols, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t st);
+hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* as, int64_t m, int64_t k, const uint8_t* b,
+                             const uint8_t* bs, int64_t n, float* y, hipStream_t st);
+
 int device_cu_count();
 
 }  // namespace qg

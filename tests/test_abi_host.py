@@ -48,7 +48,7 @@ def test_header_symbols_exported(qg):
     for name in decl:
         assert hasattr(l, name), name
     assert set(decl) == set(qg.EXPORTED)
-    assert qg.lib().qg_abi_version() == 20200
+    assert qg.lib().qg_abi_version() == 20300
     for st in range(0, 8):
         assert qg.status_str(st)
 
@@ -372,3 +372,36 @@ def test_validation_qgemv_batch(qg):
     ys0 = (ctypes.c_void_p * 2)(A, None)
     arr2 = (qg.CWeight * 2)(W(), W())
     assert g(arr2, 2, 4, A, 1, ys0, 0, None) == 1
+
+
+def test_validation_mxfp4(qg):
+    l = qg.lib()
+    q = l.qg_quantize_mxfp4
+    # (x, xt, rows, cols, codes, scales, stream)
+    assert q(None, 1, 4, 64, A, A, None) == 1
+    assert q(A, 1, 4, 64, A, None, None) == 1
+    assert q(A, 2, 4, 64, A, A, None) == 4
+    assert q(A, 1, 0, 64, A, A, None) == 2
+    assert q(A, 1, 4, 48, A, A, None) == 2      # cols % 32
+    assert q(U, 1, 4, 64, A, A, None) == 3
+    assert q(A, 1, 4, 64, U, A, None) == 3
+    g = l.qg_gemm_mxfp4
+    # (a, as, m, k, b, bs, n, y, stream)
+    assert g(None, A, 4, 256, A, A, 4, A, None) == 1
+    assert g(A, A, 4, 256, A, A, 4, None, None) == 1
+    assert g(A, A, 0, 256, A, A, 4, A, None) == 2
+    assert g(A, A, 4, 128, A, A, 4, A, None) == 2  # k % 256
+    assert g(A, A, 4, 256 + 128, A, A, 4, A, None) == 2
+    assert g(A, A, 4, 256, A, A, 0, A, None) == 2
+    assert g(A, U, 4, 256, A, A, 4, A, None) == 3
+    assert g(A, A, 4, 256, U, A, 4, A, None) == 3
+    need = l.qg_prefill_mxfp4_workspace_bytes(64, 512)
+    assert need >= 64 * 256 + 64 * 16 and need % 256 == 0
+    assert l.qg_prefill_mxfp4_workspace_bytes(64, 100) == 0
+    p = l.qg_prefill_mxfp4
+    # (x, m, k, w, ws_scales, n, y, ws, ws_bytes, stream)
+    assert p(None, 64, 512, A, A, 8, A, A, need, None) == 1
+    assert p(A, 64, 512, A, A, 8, A, None, need, None) == 5
+    assert p(A, 64, 512, A, A, 8, A, A, need - 1, None) == 5
+    assert p(A, 64, 512, A, A, 8, A, U, need, None) == 3
+    assert p(A, 64, 500, A, A, 8, A, A, need, None) == 2
