@@ -19,8 +19,11 @@ give NVFP4's or MXFP4's encoding; this is the reading):
     two), ties to the even code, magnitudes above 6 saturating to 6.  E2M1
     magnitudes are {0, 0.5, 1, 1.5, 2, 3, 4, 6} for codes 0..7; bit 3 is the
     sign, set for v < 0 (so -0.0 encodes as +0);
-  * storage: codes [R][K/2] bytes, element 2j of a row in the low nibble of
-    byte j; scales [R][K/32] E8M0 bytes.
+  * storage (this library's layout, K % 256 == 0): codes [R][K/2] bytes,
+    element 2j of a row in the low nibble of byte j; scales [K/256][R][8]
+    E8M0 bytes -- the 8 block scales of 256 consecutive values of a row
+    together, and those of all rows for one 256-value slice of K together
+    (the slices a GEMM stages).
 The product of two quantized operands is sum_k a[m][k] * b[n][k] with each
 operand value = E2M1 value * 2**e of its block (fp64 here).
 """
@@ -92,10 +95,14 @@ def dequantize_mxfp4(codes, e) -> np.ndarray:
 
 
 def pack_mxfp4(codes, e):
-    """-> (packed codes uint8 [R][K/2], E8M0 scales uint8 [R][K/32])."""
+    """-> (packed codes uint8 [R][K/2], E8M0 scales uint8 [K/256][R][8])."""
     codes = np.asarray(codes, np.uint8)
+    r, k = codes.shape
+    if k % 256:
+        raise ValueError("K must be a multiple of 256")
     packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
-    return packed, (np.asarray(e) + 127).astype(np.uint8)
+    sc = (np.asarray(e) + 127).astype(np.uint8).reshape(r, k // 256, 8)
+    return packed, np.ascontiguousarray(sc.transpose(1, 0, 2))
 
 
 def unpack_mxfp4(packed, scales):
@@ -104,7 +111,8 @@ def unpack_mxfp4(packed, scales):
     codes = np.empty((r, 2 * h), np.uint8)
     codes[:, 0::2] = packed & 15
     codes[:, 1::2] = packed >> 4
-    return codes, np.asarray(scales, np.int64) - 127
+    sc = np.asarray(scales, np.int64).transpose(1, 0, 2).reshape(r, -1)
+    return codes, sc - 127
 
 
 def gemm_mxfp4(ca, ea, cb, eb) -> np.ndarray:

@@ -86,12 +86,14 @@ def test_error_bound_and_signs():
 
 def test_packing_layout_and_roundtrip():
     g = synth.rng(54)
-    x = synth.gaussian(g, (3, 96), 1.0)
+    x = synth.gaussian(g, (3, 512), 1.0)
     codes, e = mx.quantize_mxfp4(x)
     packed, sc = mx.pack_mxfp4(codes, e)
-    assert packed.shape == (3, 48) and sc.shape == (3, 3)
+    assert packed.shape == (3, 256) and sc.shape == (2, 3, 8)
     assert packed[1, 5] == codes[1, 10] | (codes[1, 11] << 4)  # low nibble = even element
-    assert np.array_equal(sc, e + 127)
+    for r in range(3):
+        for b in range(16):  # block b of row r: slice b // 8, position b % 8
+            assert sc[b // 8, r, b % 8] == e[r, b] + 127
     c2, e2 = mx.unpack_mxfp4(packed, sc)
     assert np.array_equal(c2, codes) and np.array_equal(e2, e)
 
