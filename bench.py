@@ -40,6 +40,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 INT8_MFMA_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, TOP/s
+FP4_MFMA_PEAK_TFLOPS = 10100.0   # MI355X dense FP4 (MXFP4) MFMA, TFLOP/s
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
 CSRC = os.path.join(ROOT, "quantized_gemv_amd", "csrc")
 # sources whose hash keys the recorded counters of each kernel
@@ -500,6 +501,35 @@ def bench_small_batch(torch, qg, dev, weights, batches=(4, 16)):
     return out
 
 
+def bench_mxfp4_prefill(torch, qg, synth, dev, int8_gemm_sec):
+    wl = synth.prefill_outlier()
+    xb = torch.from_numpy(wl.tensors["x_bf16"]).to(dev).view(torch.bfloat16)
+    m, k = xb.shape
+    wc, wsc = qg.quantize_mxfp4(torch.from_numpy(wl.tensors["w"]).to(dev))
+    n = wc.shape[0]
+    xc, xsc = qg.quantize_mxfp4(xb)
+    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    ws = torch.empty(int(qg.lib().qg_prefill_mxfp4_workspace_bytes(m, k)), dtype=torch.uint8, device=dev)
+    tg = Timed(torch, [lambda: qg.gemm_mxfp4(xc, xsc, wc, wsc, y=y)] * 20)
+    tg.run(2)
+    sec_gemm = tg.run(10) / 20
+    tq = Timed(torch, [lambda: qg.quantize_mxfp4(xb)] * 20)
+    tq.run(2)
+    sec_q = tq.run(10) / 20
+    tp = Timed(torch, [lambda: qg.prefill_mxfp4(xb, wc, wsc, y=y, ws=ws)] * 20)
+    tp.run(2)
+    sec_call = tp.run(10) / 20
+    flops = 2.0 * m * n * k
+    tf = flops / sec_gemm / 1e12
+    log("mxfp4 prefill: gemm %.1f us (%.0f TFLOP/s), call %.1f us" % (sec_gemm * 1e6, tf, sec_call * 1e6))
+    return {"metric": "FP4 TFLOP/s of the MXFP4 GEMM (2*M*N*K / GEMM time)", "shape": "M=2048 K=4096 N=4096",
+            "gemm_us": round(sec_gemm * 1e6, 2), "quantize_x_us": round(sec_q * 1e6, 2),
+            "call_us": round(sec_call * 1e6, 2), "fp4_TFLOPs": round(tf, 1),
+            "mfma_frac": round(tf / FP4_MFMA_PEAK_TFLOPS, 4),
+            "speedup_vs_int8_gemm": round(int8_gemm_sec / sec_gemm, 3),
+            "note": "format separation: the prefill in the matrix cores' native MXFP4, decode weight-only int8"}
+
+
 def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
     out = {}
     GiB = 1 << 30
@@ -663,6 +693,10 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
                        "no rescale or outlier path; context, not a target",
     }
     log("prefill: gemm %.1f us (%.0f TOPS), split %.1f us" % (sec_gemm * 1e6, tops, sec_split * 1e6))
+
+    # -- format-separated prefill: the same activations and weights in MXFP4
+    #    (E2M1 + E8M0 per 32) on the block-scaled FP4 matrix cores
+    out["prefill_mxfp4"] = bench_mxfp4_prefill(torch, qg, synth, dev, sec_gemm)
 
     # -- outlier-channel detection on the same activations (run once, offline)
     xp = full.hold[3]

@@ -399,11 +399,13 @@ qg_status qg_qgemv_sep(const uint8_t* cls, const int8_t* rv, int64_t rv_ld, cons
  *   element = the E2M1 value (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes
  *       0..7) nearest to v / 2^e, ties to the even code, saturating at 6;
  *       bit 3 is the sign, set for v < 0.
- * Storage: codes [rows][cols/2] bytes, element 2j in the low nibble of byte
- * j; scales [rows][cols/32] bytes.
+ * Storage (cols % 256 == 0): codes [rows][cols/2] bytes, element 2j in the
+ * low nibble of byte j; scales [cols/256][rows][8] bytes: the 8 block scales
+ * of 256 consecutive values of a row together, and those of all rows for
+ * one 256-slice of the columns together (the slices the GEMM stages).
  *
  * qg_quantize_mxfp4: x [rows][cols] of type xt (QG_F32 or QG_BF16);
- *   cols % 32 == 0; rows >= 1; x and codes 16-B aligned.
+ *   cols % 256 == 0; rows >= 1; x and codes 16-B aligned.
  * qg_gemm_mxfp4: Y[m][n] = sum_k A[m][k] * B[n][k] over the decoded values,
  *   products exact, fp32 sums.  a, b: codes of [m][k] and [n][k]; as, bs
  *   their scales; y [m][n] fp32.  k % 256 == 0, 256 <= k <= 262144;

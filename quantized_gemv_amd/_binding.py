@@ -324,11 +324,11 @@ def qgemv_batch_grouped(weights: Sequence[QWeight], x: torch.Tensor, y_dtype=tor
 def quantize_mxfp4(x: torch.Tensor):
     """MXFP4 quantization of the rows of x [rows][cols] (fp32 or bf16)
     (qg_quantize_mxfp4). Returns (codes uint8 [rows][cols/2], scales uint8
-    [rows][cols/32])."""
+    [cols/256][rows][8])."""
     _dev(x, "x", (torch.float32, torch.bfloat16))
     r, c = x.shape
     codes = torch.empty((r, c // 2), dtype=torch.uint8, device=x.device)
-    scales = torch.empty((r, c // 32), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((c // 256, r, 8), dtype=torch.uint8, device=x.device)
     _check(lib().qg_quantize_mxfp4(_p(x), _xt(x), r, c, _p(codes), _p(scales), _stream(x)), "qg_quantize_mxfp4")
     return codes, scales
 

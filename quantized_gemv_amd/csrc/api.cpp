@@ -367,7 +367,7 @@ qg_status qg_quantize_mxfp4(const void* x, int32_t xt, int64_t rows, int64_t col
                             uint8_t* scales, void* stream) {
     if (!x || !codes || !scales) return QG_ERR_NULLPTR;
     if (xt != QG_F32 && xt != QG_BF16) return QG_ERR_ARG;
-    if (rows < 1 || cols < QG_MX_BLOCK || cols % QG_MX_BLOCK != 0 || rows > ((int64_t)1 << 40) / cols)
+    if (rows < 1 || cols < 256 || cols % 256 != 0 || rows > ((int64_t)1 << 40) / cols)
         return QG_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(codes)) return QG_ERR_ALIGN;
     return from_hip(qg::launch_quantize_mxfp4(x, xt, rows, cols, codes, scales, as_stream(stream)));
@@ -389,7 +389,7 @@ qg_status qg_gemm_mxfp4(const uint8_t* a, const uint8_t* a_scales, int64_t m, in
     return from_hip(qg::launch_gemm_mxfp4(a, a_scales, m, k, b, b_scales, n, y, as_stream(stream)));
 }
 
-// workspace of the MXFP4 prefill: codes [m][k/2] | scales [m][k/32], 256-B aligned parts
+// workspace of the MXFP4 prefill: codes [m][k/2] | scales [k/256][m][8], 256-B aligned parts
 static size_t mx_layout(int64_t m, int64_t k, size_t* off_scales) {
     const size_t codes = align_up((size_t)m * (size_t)(k / 2), 256);
     if (off_scales) *off_scales = codes;

@@ -11,7 +11,9 @@
 // Format (rows of K values):
 //   codes  [R][K/2] bytes: element 2j in the low nibble of byte j; a code is
 //          sign (bit 3) | E2M1 magnitude code (0..7 = 0, 0.5, 1, 1.5, 2, 3, 4, 6);
-//   scales [R][K/32] E8M0 bytes: block exponent e + 127, with
+//   scales [K/256][R][8] E8M0 bytes (the 8 block scales of 256 values of a
+//          row, all rows of one 256-slice of K together; K % 256 == 0):
+//          block exponent e + 127, with
 //          e = floor(log2 max|v|) - 2 clamped to [-127, 127] (0 for an
 //          all-zero block); an element is the E2M1 value nearest to v / 2^e
 //          (ties to the even code, saturating at 6).
@@ -21,8 +23,10 @@
 // 128 workgroup tile, 8 waves of 2 x 2 tiles of 32 x 32, a 3-stage LDS ring
 // fed by direct global->LDS loads, XOR-swizzled 16-byte chunks), with K
 // steps of 256 elements (128 bytes per row) and the stage's scale bytes (8
-// per row) staged beside the codes: a 16-byte fragment chunk is exactly one
-// 32-element block, so lane l of a fragment also reads its block's scale.
+// per row, contiguous over rows in the slice-major layout, so a 256-byte
+// wave load of them touches two cache lines) staged beside the codes: a
+// 16-byte fragment chunk is exactly one 32-element block, so lane l of a
+// fragment also reads its block's scale.
 #include "qg_device.h"
 #include "qg_gemm.h"
 
@@ -32,8 +36,10 @@ namespace qg {
 // One thread per 8 consecutive values; the 4 threads of a 32-block are
 // consecutive lanes (shuffles give the block max).
 template <int XT>
-__global__ __launch_bounds__(kThreads) void mxfp4_quantize_kernel(const void* x, int64_t n8, uint8_t* codes,
-                                                                  uint8_t* scales) {
+__global__ __launch_bounds__(kThreads) void mxfp4_quantize_kernel(const void* x, int64_t rows, int64_t cols,
+                                                                  uint8_t* codes, uint8_t* scales) {
+    const int64_t n8 = rows * cols / 8;
+    const int64_t nb = cols / 32;  // blocks per row
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < n8; g += stride) {
         float v[8];
@@ -72,7 +78,10 @@ __global__ __launch_bounds__(kThreads) void mxfp4_quantize_kernel(const void* x,
             packed |= (mag | (v[j] < 0.0f ? 8u : 0u)) << (4 * j);
         }
         reinterpret_cast<uint32_t*>(codes)[g] = packed;
-        if ((g & 3) == 0) scales[g >> 2] = (uint8_t)(e + 127);
+        if ((g & 3) == 0) {
+            const int64_t r = (g >> 2) / nb, b = (g >> 2) - r * nb;  // row, block
+            scales[((b >> 3) * rows + r) * 8 + (b & 7)] = (uint8_t)(e + 127);
+        }
     }
 }
 
@@ -81,17 +90,17 @@ hipError_t launch_quantize_mxfp4(const void* x, int xt, int64_t rows, int64_t co
     const int64_t n8 = rows * cols / 8;
     const int64_t want = (n8 + kThreads - 1) / kThreads;
     const int grid = (int)(want < 16384 ? want : 16384);
-    if (xt == 1) mxfp4_quantize_kernel<1><<<grid, kThreads, 0, st>>>(x, n8, codes, scales);
-    else mxfp4_quantize_kernel<0><<<grid, kThreads, 0, st>>>(x, n8, codes, scales);
+    if (xt == 1) mxfp4_quantize_kernel<1><<<grid, kThreads, 0, st>>>(x, rows, cols, codes, scales);
+    else mxfp4_quantize_kernel<0><<<grid, kThreads, 0, st>>>(x, rows, cols, codes, scales);
     return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ GEMM
 struct MxParams {
     const uint8_t* a;   // [M][K/2]
-    const uint8_t* as;  // [M][K/32]
+    const uint8_t* as;  // [K/256][M][8]
     const uint8_t* b;   // [N][K/2]
-    const uint8_t* bs;  // [N][K/32]
+    const uint8_t* bs;  // [K/256][N][8]
     float* y;           // [M][N]
     int M, N, K;
     int tiles_m, tiles_n;
@@ -124,7 +133,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mxfp4_kernel(MxPa
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     const int KB = p.K / 2;    // code bytes per row
-    const int KS = p.K / 32;   // scale bytes per row
 
     // XCD-aware tile order (as the int8 GEMM): each XCD gets a contiguous run
     // of the tile sequence, rasterised in supertiles of 4 M-tiles
@@ -141,7 +149,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mxfp4_kernel(MxPa
 
     // ---- DMA plan: the codes as in the int8 GEMM (A rows, then B rows, BK
     // bytes each, chunks swizzled), then the scales: row R's 8 bytes of the
-    // stage at kStageBytes + 8 R (wave load j covers rows 32 j .. 32 j + 31)
+    // stage at kStageBytes + 8 R (wave load j covers rows 32 j .. 32 j + 31;
+    // in global memory slice ks of row r is at (ks * rows + r) * 8)
     const uint8_t* src[kDataLoads];
 #pragma unroll
     for (int l = 0; l < kDataLoads; ++l) {
@@ -164,10 +173,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mxfp4_kernel(MxPa
         const int j = min(wave + kNW * l, MC::kScaleLoads - 1);
         const int R = 32 * j + lane / 2;
         const int d = lane & 1;
-        if (R < BM) ssrc[l] = p.as + (int64_t)min(m0 + R, p.M - 1) * KS + 4 * d;
-        else ssrc[l] = p.bs + (int64_t)min(n0 + R - BM, p.N - 1) * KS + 4 * d;
+        if (R < BM) ssrc[l] = p.as + (int64_t)min(m0 + R, p.M - 1) * 8 + 4 * d;
+        else ssrc[l] = p.bs + (int64_t)min(n0 + R - BM, p.N - 1) * 8 + 4 * d;
         sdst[l] = CF::kStageBytes + 256 * j;
     }
+    int64_t sstr[MC::kSLPW];  // bytes per K slice of the A or B scales this lane loads
+#pragma unroll
+    for (int l = 0; l < MC::kSLPW; ++l)
+        sstr[l] = (32 * min(wave + kNW * l, MC::kScaleLoads - 1) + lane / 2) < BM ? (int64_t)p.M * 8 : (int64_t)p.N * 8;
     auto issue_stage = [&](int ks) {
         uint8_t* base = smem + (ks % STAGES) * MC::kStage;
 #pragma unroll
@@ -176,7 +189,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mxfp4_kernel(MxPa
             dma16(src[l] + (int64_t)ks * BK, base + blk * 1024);
         }
 #pragma unroll
-        for (int l = 0; l < MC::kSLPW; ++l) dma4(ssrc[l] + (int64_t)ks * 8, base + sdst[l]);
+        for (int l = 0; l < MC::kSLPW; ++l) dma4(ssrc[l] + (int64_t)ks * sstr[l], base + sdst[l]);
     };
 
     f32x16 acc[WTM][WTN];

@@ -378,13 +378,14 @@ def test_validation_mxfp4(qg):
     l = qg.lib()
     q = l.qg_quantize_mxfp4
     # (x, xt, rows, cols, codes, scales, stream)
-    assert q(None, 1, 4, 64, A, A, None) == 1
-    assert q(A, 1, 4, 64, A, None, None) == 1
-    assert q(A, 2, 4, 64, A, A, None) == 4
-    assert q(A, 1, 0, 64, A, A, None) == 2
-    assert q(A, 1, 4, 48, A, A, None) == 2      # cols % 32
-    assert q(U, 1, 4, 64, A, A, None) == 3
-    assert q(A, 1, 4, 64, U, A, None) == 3
+    assert q(None, 1, 4, 256, A, A, None) == 1
+    assert q(A, 1, 4, 256, A, None, None) == 1
+    assert q(A, 2, 4, 256, A, A, None) == 4
+    assert q(A, 1, 0, 256, A, A, None) == 2
+    assert q(A, 1, 4, 48, A, A, None) == 2      # cols % 256
+    assert q(A, 1, 4, 288, A, A, None) == 2
+    assert q(U, 1, 4, 256, A, A, None) == 3
+    assert q(A, 1, 4, 256, U, A, None) == 3
     g = l.qg_gemm_mxfp4
     # (a, as, m, k, b, bs, n, y, stream)
     assert g(None, A, 4, 256, A, A, 4, A, None) == 1
