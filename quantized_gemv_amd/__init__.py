@@ -1,9 +1,10 @@
 """quantized_gemv_amd -- MI355X (gfx950) quantized GEMV library.
 
 Python side of the C ABI in include/qgemv.h: symmetric absmax / absmean
-quantization to int8, ternary and sign + int8-residual formats, bit packing,
-batch-1 quantized GEMV for decode and the W8A8 prefill GEMM with an
-activation outlier split.  All arithmetic runs in the HIP kernels of
+quantization to int8, ternary, sign + int8-residual, thresholded separated
+and group-wise 4-bit formats, bit packing, quantized GEMV for decode (batch 1
+and small batches), the W8A8 prefill GEMM with an activation outlier split,
+and an MXFP4 prefill on the FP4 matrix cores.  All arithmetic runs in the HIP kernels of
 libqgemv.so; this package only marshals arguments (see _binding.py).
 """
 from ._binding import (QgError, QWeight, CWeight, EXPORTED, LIB_PATH, lib, status_str,
