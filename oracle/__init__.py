@@ -33,10 +33,12 @@ from .numerics import (bf16_bits_to_f32, f32_to_bf16_bits, round_rational_to_f32
                        exact_abs_sum_units, mean_abs_f32, mean_abs_rows_f32)
 from .quant import (absmax_scale, quantize_with_scale, quantize_absmax,
                     ternary_absmean, sign_residual_split, outlier_split_quantize,
-                    gather_outlier_weights, dequantize, detect_outlier_channels)
+                    gather_outlier_weights, dequantize, detect_outlier_channels,
+                    asym_params, quantize_with_zero_point, quantize_asym, dequantize_asym,
+                    sign_residual_split_zp)
 from .packing import (pack, unpack, pack_loops, unpack_loops)
 from .products import (int_dot_exact, int_gemm_exact, int_dot_bruteforce,
-                       y_w8a8, y_w8a16, y_w8a16_batch, y_ternary, y_sign_residual, y_prefill,
+                       y_w8a8, y_w8a16, y_w8a16_batch, y_ternary, y_sign_residual, y_sign_residual_zp, y_prefill,
                        relative_method_error, normwise_error)
 
 __all__ = [n for n in dir() if not n.startswith("_")]

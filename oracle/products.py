@@ -99,6 +99,17 @@ def y_sign_residual(sign, alpha, rq, s_r, x_bf16_bits) -> np.ndarray:
     return np.asarray(alpha, np.float64) * b + r / np.asarray(s_r, np.float64)
 
 
+def y_sign_residual_zp(sign, alpha, rq, s_r, z_r, x_bf16_bits) -> np.ndarray:
+    """Output with the zero-point residual: y = alpha * (sign . x) +
+    ((rq - z_r) . x) / s_r, fp64 ([SEP] sections 2.3 and 6.3; [VG]
+    'Asymmetric quantization', fig. 25: subtract the zero-point, then divide
+    by the scale)."""
+    x = bf16_bits_to_f32(x_bf16_bits).astype(np.float64)
+    b = np.asarray(sign, np.float64) @ x
+    r = (np.asarray(rq, np.float64) - np.asarray(z_r, np.float64)[:, None]) @ x
+    return np.asarray(alpha, np.float64) * b + r / np.asarray(s_r, np.float64)
+
+
 def y_prefill(acc, s_x, s_w, x_out_bits, w_out_bits) -> np.ndarray:
     """Prefill output with the outlier path: Y = acc / (s_x[m] * s_w[n]) +
     X_out . W_out^T in fp64 ([SEP] section 2.2: outlier channels run in high

@@ -105,6 +105,78 @@ def sign_residual_split(w: np.ndarray):
     return sign, alpha, rq, s_r
 
 
+Q_MIN_ASYM, Q_MAX_ASYM = -128, 127  # the int8 range the asymmetric form maps onto ([OVR] section 3 item 2)
+
+
+def asym_params(lo, hi):
+    """Scale and zero-point of asymmetric int8 quantization, per group.
+
+    [VG] 'Asymmetric quantization' (figs. 22-26), in its multiplier notation:
+    the float minimum beta and maximum alpha go to the ends of [q_min, q_max],
+    s = (q_max - q_min) / (alpha - beta), z = round(q_min - s * beta).
+    Readings: the range is widened to contain 0 (beta = min(lo, 0),
+    alpha = max(hi, 0)), so that 0 is representable exactly and z lies in
+    [q_min, q_max] (any range the data straddles 0 with is unchanged); an
+    all-zero group (alpha = beta = 0) gets s = 1, z = q_min.  fp32 steps:
+    d = fl32(alpha - beta), s = fl32(255 / d), z = rint(fl32(q_min - fl32(s * beta)))
+    clipped to [q_min, q_max] (the clip is inactive up to rounding).
+    lo, hi: fp32 arrays of group minima / maxima.  Returns (s fp32, z int32)."""
+    lo = np.minimum(np.asarray(lo, np.float32), np.float32(0))
+    hi = np.maximum(np.asarray(hi, np.float32), np.float32(0))
+    d = (hi - lo).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        s = (np.float32(Q_MAX_ASYM - Q_MIN_ASYM) / d).astype(np.float32)
+    s = np.where(d == np.float32(0), np.float32(1), s).astype(np.float32)
+    t = (s * lo).astype(np.float32)
+    z = np.rint((np.float32(Q_MIN_ASYM) - t).astype(np.float32))
+    z = np.clip(z, Q_MIN_ASYM, Q_MAX_ASYM).astype(np.int32)
+    return s, z
+
+
+def quantize_with_zero_point(x: np.ndarray, s, z) -> np.ndarray:
+    """x_q = clip(round(s * x + z), q_min, q_max): one fp32 multiply, one fp32
+    add, round-half-to-even ([VG] 'Asymmetric quantization', fig. 24)."""
+    x = np.asarray(x, dtype=np.float32)
+    t = (x * np.asarray(s, dtype=np.float32)).astype(np.float32)
+    u = (t + np.asarray(z, dtype=np.float32)).astype(np.float32)
+    return np.clip(np.rint(u), Q_MIN_ASYM, Q_MAX_ASYM).astype(np.int8)
+
+
+def quantize_asym(x: np.ndarray):
+    """Asymmetric int8 quantization with one (s, z) per row of x [rows][cols].
+    Returns (codes int8 [rows][cols], s fp32 [rows], z int32 [rows])."""
+    x = np.asarray(x, dtype=np.float32)
+    if x.ndim != 2:
+        raise ValueError("2-D input expected")
+    if x.shape[1]:
+        lo, hi = x.min(axis=1), x.max(axis=1)
+    else:
+        lo = hi = np.zeros(x.shape[0], np.float32)
+    s, z = asym_params(lo, hi)
+    return quantize_with_zero_point(x, s[:, None], z[:, None]), s, z
+
+
+def dequantize_asym(q, s, z) -> np.ndarray:
+    """x_hat = (x_q - z) / s in fp64 ([VG] 'Asymmetric quantization', fig. 25)."""
+    return (np.asarray(q, np.float64) - np.asarray(z, np.float64)) / np.asarray(s, np.float64)
+
+
+def sign_residual_split_zp(w: np.ndarray):
+    """The sign backbone of sign_residual_split with an asymmetric int8
+    residual: [SEP] section 6.3 gives the residual its own min / max, scale
+    and zero-point.  sign and alpha as in sign_residual_split;
+    R = fl32(W - alpha * sign); (rq, s_r, z_r) = quantize_asym(R) per row.
+    Returns (sign int8 +-1, alpha fp32 [n], rq int8 [n][k], s_r fp32 [n], z_r int32 [n])."""
+    w = np.asarray(w, dtype=np.float32)
+    if w.ndim != 2:
+        raise ValueError("2-D weight expected")
+    sign = np.where(w >= np.float32(0), 1, -1).astype(np.int8)
+    alpha = mean_abs_rows_f32(w) if w.shape[1] else np.zeros(w.shape[0], np.float32)
+    r = (w - (alpha[:, None] * sign.astype(np.float32)).astype(np.float32)).astype(np.float32)
+    rq, s_r, z_r = quantize_asym(r)
+    return sign, alpha, rq, s_r, z_r
+
+
 def outlier_split_quantize(x_bf16_bits: np.ndarray, idx: np.ndarray):
     """Activation outlier-channel split with per-token int8 quantization.
 
