@@ -657,6 +657,25 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
     del copies, cws, sp, rq
     torch.cuda.empty_cache()
 
+    # -- the same with the zero-point residual (asymmetric int8, z per row)
+    wdev = torch.from_numpy(wl.tensors["w"]).to(dev)
+    sign, alpha, rq, s_r, z_r = qg.split_sign_residual_zp(wdev)
+    sp = qg.pack(sign, 1)
+    del sign, wdev
+    per = sp.numel() + rq.numel() + 9 * 28672
+    copies = [qg.QWeight(qg.QG_WFMT_SIGN1_RES8Z, 28672, 8192, sp.clone(), alpha.clone(), resid=rq.clone(),
+                         scale2=s_r.clone(), zero=z_r.clone()) for _ in range(rotate_count(per))]
+    cws = [W.c_struct() for W in copies]
+    t = Timed(torch, [mks(cw) for cw in cws])
+    t.run(1)
+    sec = t.run(5) / t.n
+    out["sign1_res8z_28672x8192"] = {"us": round(sec * 1e6, 3), "weight_GBps": round(per / sec / 1e9, 1),
+                                     "hbm_frac": round(per / sec / 1e9 / HBM_PEAK_GBS, 4),
+                                     "rotating_copies": len(copies)}
+    log("sign+zero-point residual: %.2f us, %.0f GB/s" % (sec * 1e6, per / sec / 1e9))
+    del copies, cws, sp, rq
+    torch.cuda.empty_cache()
+
     # -- thresholded separated weights (80th-percentile backbone, 50th-percentile
     #    zero class), int8 activations, same weights and x as the line above
     out.update(bench_sep_threshold(torch, qg, synth, dev, rotate_count))

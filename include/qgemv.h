@@ -72,6 +72,8 @@ typedef int32_t qg_status;
                               /* [n][k] + its own per-row scale s_r[n]              */
 #define QG_WFMT_Q4K        3  /* 4-bit codes [n][k/2] in groups of 32 with zero-    */
                               /* points, two-level scales in [n][k/256][16] bytes   */
+#define QG_WFMT_SIGN1_RES8Z 4 /* as SIGN1_RES8 with an asymmetric residual: codes   */
+                              /* in [-128, 127], s_r[n] and a zero-point z_r[n]     */
 
 /* activation modes of qg_qgemv */
 #define QG_ACT_INT8  0  /* x is quantized per tensor (absmax int8) inside the call */
@@ -208,6 +210,37 @@ qg_status qg_split_sign_residual(const float* w, int64_t n, int64_t k,
                                  void* stream);
 
 /*
+ * Asymmetric (zero-point) int8 quantization, one scale and zero-point per row
+ * ([VG] 'Asymmetric quantization', figs. 22-26, in its multiplier notation;
+ * [OVR] section 3 item 2 gives the same map with the reciprocal step).
+ * The row's minimum beta and maximum alpha go to the ends of [-128, 127]:
+ *   beta = min(min x[r][:], 0), alpha = max(max x[r][:], 0)  (the range is
+ *          widened to contain 0, so 0 is exact and z fits in int8);
+ *   d = fl32(alpha - beta);  s = fl32(255 / d)  (s = 1 when d = 0);
+ *   z = clip(rne(fl32(-128 - fl32(s * beta))), -128, 127);
+ *   q = clip(rne(fl32(fl32(x * s) + z)), -128, 127);
+ *   dequantized value (q - z) / s.
+ * x : [rows][cols] of type xt (QG_F32 or QG_BF16), 16-B aligned.
+ * q : [rows][cols] int8 (out), 16-B aligned.  s: [rows] fp32 (out).
+ * z : [rows] int8 (out).
+ * cols % 8 == 0; rows >= 1; cols >= 8; cols < 2^31.
+ */
+qg_status qg_quantize_asym(const void* x, int32_t xt, int64_t rows, int64_t cols,
+                           int8_t* q, float* s, int8_t* z, void* stream);
+
+/*
+ * Sign backbone + asymmetric int8 residual ([SEP] section 6.3: the residual
+ * gets its own min / max, scale and zero-point, never the backbone's).
+ * sign, alpha and R as in qg_split_sign_residual; then per row
+ * (rq, s_r, z_r) = qg_quantize_asym of R.
+ * w: [n][k] fp32; sign, rq: [n][k] int8 (out); alpha, s_r: [n] fp32 (out);
+ * z_r: [n] int8 (out).  w, sign, rq 16-B aligned; k % 8 == 0; k < 2^31.
+ */
+qg_status qg_split_sign_residual_zp(const float* w, int64_t n, int64_t k,
+                                    int8_t* sign, float* alpha, int8_t* rq, float* s_r,
+                                    int8_t* z_r, void* stream);
+
+/*
  * Group-wise 4-bit weights with zero-points and two-level scales ([VG] 'Why
  * Q4_K splits weights into blocks', 'Q4_K uses two-level blocks', figs.
  * 43-46).  Each row is cut along k into super-blocks of 256 = 8 groups of 32.
@@ -256,6 +289,9 @@ qg_status qg_unpack(const uint8_t* packed, int64_t n, int64_t k, int32_t bits,
  *   QG_WFMT_Q4K       : codes = 4-bit plane [n][k/2]; resid = the metadata
  *                       plane [n][k/256][16] (as qg_quantize_q4k writes
  *                       them); scale, scale2 unused (may be NULL)
+ *   QG_WFMT_SIGN1_RES8Z: as SIGN1_RES8 (rq from qg_split_sign_residual_zp);
+ *                       zero = z_r[n]
+ * zero is read for QG_WFMT_SIGN1_RES8Z only (may be NULL otherwise).
  */
 typedef struct qg_weight {
     int32_t fmt;
@@ -265,6 +301,7 @@ typedef struct qg_weight {
     const int8_t* resid;
     const float* scale;
     const float* scale2;
+    const int8_t* zero;
 } qg_weight;
 
 /*
@@ -286,11 +323,16 @@ typedef struct qg_weight {
  *       and residual products in one fused kernel, results added):
  *       y[n] = alpha[n] * sum_k sign[n][k] x[k] + (sum_k rq[n][k] x[k]) / s_r[n],
  *       fp32 accumulation.
+ *   fmt SIGN1_RES8Z, amode QG_ACT_FLOAT (the residual dequantized as
+ *       (rq - z_r) / s_r, [VG] 'Asymmetric quantization', fig. 25):
+ *       y[n] = alpha[n] * sum_k sign[n][k] x[k] + (sum_k (rq[n][k] - z_r[n]) x[k]) / s_r[n],
+ *       fp32 accumulation of the differences (no z * sum_k x correction).
  *   fmt Q4K, amode QG_ACT_FLOAT (W4A16; the codes and group parameters are
  *       decoded in registers):
  *       y[n] = sum_groups (S_j * sum_{k in j} q[n][k] x[k] + M_j * sum_{k in j} x[k]),
  *       i.e. sum_k w_hat[n][k] x[k], fp32 accumulation; k % 256 == 0.
- * x       : [k] of type xt (QG_F32 or QG_BF16; SIGN1_RES8 and Q4K need QG_BF16).
+ * x       : [k] of type xt (QG_F32 or QG_BF16; SIGN1_RES8, SIGN1_RES8Z and Q4K
+ *           need QG_BF16).
  * y       : [n] of type yt (QG_F32 or QG_BF16; bf16 is rounded to nearest even).
  * acc_out : [n] int32 raw accumulators (integer modes only); may be NULL.
  * k % 128 == 0, 128 <= k <= QG_QGEMV_MAX_K, n >= 1.

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 QG_OK = 0
 QG_F32, QG_BF16 = 0, 1
 QG_PER_TENSOR, QG_PER_ROW = 0, 1
-QG_WFMT_INT8, QG_WFMT_TERNARY2, QG_WFMT_SIGN1_RES8, QG_WFMT_Q4K = 0, 1, 2, 3
+QG_WFMT_INT8, QG_WFMT_TERNARY2, QG_WFMT_SIGN1_RES8, QG_WFMT_Q4K, QG_WFMT_SIGN1_RES8Z = 0, 1, 2, 3, 4
 QG_ACT_INT8, QG_ACT_FLOAT = 0, 1
 QG_MAX_OUTLIERS = 256
 QG_QGEMV_MAX_K = 32768
@@ -44,7 +44,7 @@ class QgError(RuntimeError):
 
 class CWeight(ctypes.Structure):
     _fields_ = [("fmt", _c_i32), ("reserved", _c_i32), ("n", _c_i64), ("k", _c_i64),
-                ("codes", _c_vp), ("resid", _c_vp), ("scale", _c_vp), ("scale2", _c_vp)]
+                ("codes", _c_vp), ("resid", _c_vp), ("scale", _c_vp), ("scale2", _c_vp), ("zero", _c_vp)]
 
 
 _SIGS = {
@@ -60,6 +60,8 @@ _SIGS = {
     "qg_ternary_workspace_bytes": (_c_sz, [_c_i64, _c_i64]),
     "qg_quantize_ternary": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "qg_split_sign_residual": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "qg_split_sign_residual_zp": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "qg_quantize_asym": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp]),
     "qg_quantize_q4k": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
     "qg_qgemv_batch": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp]),
     "qg_qgemv_batch_grouped": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_i32, _c_vp, _c_i32,
@@ -237,6 +239,35 @@ def split_sign_residual(w: torch.Tensor):
     return sign, alpha, rq, s_r
 
 
+def split_sign_residual_zp(w: torch.Tensor):
+    """Sign backbone + asymmetric int8 residual (qg_split_sign_residual_zp).
+    Returns (sign int8, alpha, rq int8, s_r, z_r int8)."""
+    _dev(w, "w", torch.float32)
+    n, k = w.shape
+    sign = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    rq = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    alpha = torch.empty(n, dtype=torch.float32, device=w.device)
+    s_r = torch.empty(n, dtype=torch.float32, device=w.device)
+    z_r = torch.empty(n, dtype=torch.int8, device=w.device)
+    _check(lib().qg_split_sign_residual_zp(_p(w), n, k, _p(sign), _p(alpha), _p(rq), _p(s_r), _p(z_r), _stream(w)),
+           "qg_split_sign_residual_zp")
+    return sign, alpha, rq, s_r, z_r
+
+
+def quantize_asym(x: torch.Tensor):
+    """Asymmetric int8 quantization per row (qg_quantize_asym): x [rows][cols]
+    fp32 or bf16. Returns (q int8, s fp32 [rows], z int8 [rows])."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    if x.dim() != 2:
+        raise ValueError("x must be [rows][cols]")
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    s = torch.empty(rows, dtype=torch.float32, device=x.device)
+    z = torch.empty(rows, dtype=torch.int8, device=x.device)
+    _check(lib().qg_quantize_asym(_p(x), _xt(x), rows, cols, _p(q), _p(s), _p(z), _stream(x)), "qg_quantize_asym")
+    return q, s, z
+
+
 def pack(codes: torch.Tensor, bits: int, out: torch.Tensor = None):
     """Bit packing (qg_pack): bits=2 ternary, bits=1 sign."""
     _dev(codes, "codes", torch.int8)
@@ -269,12 +300,14 @@ class QWeight:
     scale: Optional[torch.Tensor]
     resid: Optional[torch.Tensor] = None
     scale2: Optional[torch.Tensor] = None
+    zero: Optional[torch.Tensor] = None
 
     def c_struct(self) -> CWeight:
         return CWeight(self.fmt, 0, self.n, self.k, self.codes.data_ptr(),
                        self.resid.data_ptr() if self.resid is not None else None,
                        self.scale.data_ptr() if self.scale is not None else None,
-                       self.scale2.data_ptr() if self.scale2 is not None else None)
+                       self.scale2.data_ptr() if self.scale2 is not None else None,
+                       self.zero.data_ptr() if self.zero is not None else None)
 
 
 def quantize_q4k(w: torch.Tensor):

@@ -76,7 +76,7 @@ const char* qg_status_str(qg_status s) {
     }
 }
 
-int32_t qg_abi_version(void) { return 20300; }
+int32_t qg_abi_version(void) { return 20400; }
 
 size_t qg_quantize_absmax_workspace_bytes(int64_t rows, int64_t cols, int32_t gran) {
     if (gran != QG_PER_TENSOR || rows < 1 || cols < 8) return 0;
@@ -232,7 +232,25 @@ qg_status qg_split_sign_residual(const float* w, int64_t n, int64_t k, int8_t* s
     if (!w || !sign || !alpha || !rq || !s_r) return QG_ERR_NULLPTR;
     if (n < 1 || k < 8 || k % 8 != 0 || k >= ((int64_t)1 << 31)) return QG_ERR_SHAPE;
     if (!aligned16(w) || !aligned16(sign) || !aligned16(rq)) return QG_ERR_ALIGN;
-    return from_hip(qg::launch_split_sign_residual(w, n, k, sign, alpha, rq, s_r, as_stream(stream)));
+    return from_hip(qg::launch_split_sign_residual(w, n, k, sign, alpha, rq, s_r, nullptr, as_stream(stream)));
+}
+
+qg_status qg_split_sign_residual_zp(const float* w, int64_t n, int64_t k, int8_t* sign, float* alpha, int8_t* rq,
+                                    float* s_r, int8_t* z_r, void* stream) {
+    if (!w || !sign || !alpha || !rq || !s_r || !z_r) return QG_ERR_NULLPTR;
+    if (n < 1 || k < 8 || k % 8 != 0 || k >= ((int64_t)1 << 31)) return QG_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(sign) || !aligned16(rq)) return QG_ERR_ALIGN;
+    return from_hip(qg::launch_split_sign_residual(w, n, k, sign, alpha, rq, s_r, z_r, as_stream(stream)));
+}
+
+qg_status qg_quantize_asym(const void* x, int32_t xt, int64_t rows, int64_t cols, int8_t* q, float* s, int8_t* z,
+                           void* stream) {
+    if (!x || !q || !s || !z) return QG_ERR_NULLPTR;
+    if (xt != QG_F32 && xt != QG_BF16) return QG_ERR_ARG;
+    if (rows < 1 || cols < 8 || cols % 8 != 0 || cols >= ((int64_t)1 << 31)) return QG_ERR_SHAPE;
+    if (rows > ((int64_t)1 << 40) / cols) return QG_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(q)) return QG_ERR_ALIGN;
+    return from_hip(qg::launch_asym_rows(x, xt, rows, cols, q, s, z, as_stream(stream)));
 }
 
 qg_status qg_pack(const int8_t* codes, int64_t n, int64_t k, int32_t bits, uint8_t* packed, void* stream) {
@@ -267,6 +285,10 @@ static qg_status check_qgemv(const qg_weight* w, int32_t amode, const void* x, i
             if (amode != QG_ACT_FLOAT || xt != QG_BF16) return QG_ERR_ARG;
             if (!w->resid || !w->scale2) return QG_ERR_NULLPTR;
             break;
+        case QG_WFMT_SIGN1_RES8Z:
+            if (amode != QG_ACT_FLOAT || xt != QG_BF16) return QG_ERR_ARG;
+            if (!w->resid || !w->scale2 || !w->zero) return QG_ERR_NULLPTR;
+            break;
         case QG_WFMT_Q4K:
             if (amode != QG_ACT_FLOAT || xt != QG_BF16) return QG_ERR_ARG;
             if (!w->resid) return QG_ERR_NULLPTR;
@@ -278,7 +300,9 @@ static qg_status check_qgemv(const qg_weight* w, int32_t amode, const void* x, i
     if (w->n < 1 || w->n >= ((int64_t)1 << 31)) return QG_ERR_SHAPE;
     if (w->k < 128 || w->k % 128 != 0 || w->k > QG_QGEMV_MAX_K) return QG_ERR_SHAPE;
     if (!aligned16(w->codes) || !aligned16(x)) return QG_ERR_ALIGN;
-    if ((w->fmt == QG_WFMT_SIGN1_RES8 || w->fmt == QG_WFMT_Q4K) && !aligned16(w->resid)) return QG_ERR_ALIGN;
+    if ((w->fmt == QG_WFMT_SIGN1_RES8 || w->fmt == QG_WFMT_SIGN1_RES8Z || w->fmt == QG_WFMT_Q4K) &&
+        !aligned16(w->resid))
+        return QG_ERR_ALIGN;
     return QG_OK;
 }
 
@@ -295,6 +319,7 @@ static qg::QgemvArgs qgemv_args(const qg_weight* w, int32_t amode, const void* x
     a.resid = w->resid;
     a.scale = w->scale;
     a.scale2 = w->scale2;
+    a.zero = w->fmt == QG_WFMT_SIGN1_RES8Z ? w->zero : nullptr;
     a.x = x;
     a.y = y;
     a.acc_out = acc_out;

@@ -43,6 +43,29 @@ __device__ __forceinline__ int qcode(float x, float s) {
     return (int)t;
 }
 
+// ------------------------------------------------------------------ asymmetric step
+// The range [lo, hi] of a group, widened to contain 0, goes to [-128, 127]:
+// s = 255 / (hi - lo) (1 for an empty range) and z = rne(-128 - s * lo),
+// clipped to int8; every product and sum is rounded on its own.
+__device__ __forceinline__ void asym_params(float lo, float hi, float& s, float& z) {
+    lo = __builtin_fminf(lo, 0.0f);
+    hi = __builtin_fmaxf(hi, 0.0f);
+    const float d = hi - lo;
+    s = d == 0.0f ? 1.0f : 255.0f / d;
+    const float t = s * lo;
+    const float u = -128.0f - t;
+    z = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(u), -128.0f), 127.0f);
+}
+
+// clip(round_half_even(fl32(fl32(x * s) + z)), -128, 127)
+__device__ __forceinline__ int qcode_zp(float x, float s, float z) {
+    const float t = x * s;
+    float u = t + z;
+    u = __builtin_rintf(u);
+    u = __builtin_fminf(__builtin_fmaxf(u, -128.0f), 127.0f);
+    return (int)u;
+}
+
 // ------------------------------------------------------------------ reductions
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
@@ -139,6 +162,9 @@ __device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off
 }
 __device__ __forceinline__ uint16_t load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ uint8_t load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
 
 }  // namespace qg

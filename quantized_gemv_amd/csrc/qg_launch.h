@@ -33,8 +33,11 @@ hipError_t launch_detect_outliers(const uint16_t* x, int64_t rows, int64_t cols,
 hipError_t launch_gather_cols_bf16(const float* w, int64_t n, int64_t k, const OutlierIdx& idx, int n_out,
                                    uint16_t* w_out, int w_out_ld, hipStream_t st);
 hipError_t launch_ternary(const float* w, int64_t count, int8_t* q, float* gamma, uint64_t* hist, hipStream_t st);
+// z_r == nullptr: symmetric residual; otherwise the zero-point residual
 hipError_t launch_split_sign_residual(const float* w, int64_t n, int64_t k, int8_t* sign, float* alpha, int8_t* rq,
-                                      float* s_r, hipStream_t st);
+                                      float* s_r, int8_t* z_r, hipStream_t st);
+hipError_t launch_asym_rows(const void* x, int xt, int64_t rows, int64_t cols, int8_t* q, float* s, int8_t* z,
+                            hipStream_t st);
 hipError_t launch_quantize_q4k(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* meta, hipStream_t st);
 hipError_t launch_pack(const int8_t* codes, int64_t count, int bits, uint8_t* packed, hipStream_t st);
 hipError_t launch_unpack(const uint8_t* packed, int64_t count, int bits, int8_t* codes, hipStream_t st);
@@ -46,6 +49,7 @@ struct QgemvArgs {
     const int8_t* resid;
     const float* scale;
     const float* scale2;
+    const int8_t* zero;
     const void* x;
     void* y;
     int32_t* acc_out;

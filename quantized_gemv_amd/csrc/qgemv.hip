@@ -37,6 +37,11 @@
 //                    residual becomes bf16 pairs (col j, col j+16) and the sign
 //                    bits become +-1.0 bf16 pairs with one bit-field insert;
 //                    both go through v_dot2_f32_bf16 against bf16 x pairs.
+//   SIGN1_RES8Z    : the same units; every residual pair also goes through
+//                    one more v_dot2 with the pair (-z, -z), so the sum is
+//                    sum_k (rq - z) x[k] as it accumulates (a z * sum_k x[k]
+//                    correction at the end would cancel in fp32 whenever the
+//                    activations have a large mean).
 //   Q4K            : 16 B chunk = one group of 32 4-bit codes; the chunk's
 //                    16-byte super-block record gives the group's S and M
 //                    (6-bit fields, fp16 d / dmin); sum_k q x by fp32 FMA
@@ -47,13 +52,17 @@
 
 namespace qg {
 
-enum { F_INT8F = 0, F_INT8I = 1, F_TERN = 2, F_SR = 3, F_Q4 = 4 };
+enum { F_INT8F = 0, F_INT8I = 1, F_TERN = 2, F_SR = 3, F_Q4 = 4, F_SRZ = 5 };
+// the sign + residual formats (symmetric residual, or with a zero-point)
+template <int F>
+constexpr bool kSignRes = (F == F_SR || F == F_SRZ);
 
 struct KParams {
     const uint8_t* codes;
     const int8_t* resid;
     const float* scale;
     const float* scale2;
+    const int8_t* zero;
     const void* x;
     void* y;
     int32_t* acc_out;
@@ -107,6 +116,12 @@ struct Fmt<F_SR> {
     struct Frag { u32x4 r0, r1; uint32_t s; };
 };
 template <>
+struct Fmt<F_SRZ> {
+    static constexpr int kColsPerChunk = 32;
+    static constexpr int kLdsBytesPerCol = 2;
+    struct Frag { u32x4 r0, r1; uint32_t s, z; };  // z: the row's zero-point (j = 0 only)
+};
+template <>
 struct Fmt<F_Q4> {
     static constexpr int kColsPerChunk = 32;   // one group: 16 B of 4-bit codes
     static constexpr int kLdsBytesPerCol = 0;  // x (bf16) travels with each item
@@ -147,11 +162,13 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     const int padded_cols = nseg * JS * 64 * kCols;
 
     // ------------------------------------------------------------ stream
-    const int rowB = (F == F_TERN) ? K / 4 : (F == F_SR) ? K / 8 : (F == F_Q4) ? K / 2 : K;  // code bytes per row
+    const int rowB = (F == F_TERN) ? K / 4 : kSignRes<F> ? K / 8 : (F == F_Q4) ? K / 2 : K;  // code bytes per row
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.codes + (int64_t)row0 * rowB, (uint32_t)(rows * rowB));
     __amdgpu_buffer_rsrc_t rr = rc;
-    if constexpr (F == F_SR) rr = make_rsrc(p.resid + (int64_t)row0 * K, (uint32_t)(rows * K));
+    if constexpr (kSignRes<F>) rr = make_rsrc(p.resid + (int64_t)row0 * K, (uint32_t)(rows * K));
     if constexpr (F == F_Q4) rr = make_rsrc(p.resid + (int64_t)row0 * (K / 16), (uint32_t)(rows * (K / 16)));
+    __amdgpu_buffer_rsrc_t rz = rc;  // zero-points of this workgroup's rows (SIGN1_RES8Z)
+    if constexpr (F == F_SRZ) rz = make_rsrc(p.zero + row0, (uint32_t)rows);
     const uint32_t oob_c = (uint32_t)(rows * rowB);
     const uint32_t oob_r = (uint32_t)(rows * (F == F_Q4 ? K / 16 : K));
 
@@ -176,11 +193,14 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
             for (int u = 0; u < U; ++u) {
                 const int r = g * U + u;
                 const bool ok = live && (r < rows) && (c < C);
-                if constexpr (F == F_SR) {
+                if constexpr (kSignRes<F>) {
                     const uint32_t orr = ok ? (uint32_t)(r * K + 32 * c) : oob_r;
                     fr[u][j].r0 = load16(rr, orr);
                     fr[u][j].r1 = load16(rr, ok ? orr + 16 : oob_r);
                     fr[u][j].s = load4(rc, ok ? (uint32_t)(r * rowB + 4 * c) : oob_c);
+                    if constexpr (F == F_SRZ) {
+                        if (j == 0) fr[u][0].z = load1(rz, r < rows ? (uint32_t)r : (uint32_t)rows);
+                    }
                 } else if constexpr (F == F_Q4) {
                     // the group's 32 activations (bf16, shared by the U rows; not
                     // with XREG), then its super-block record, then its codes
@@ -324,7 +344,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
         });
         for (int i = K / 4 + tid; i < padded_cols / 4; i += kQThreads) reinterpret_cast<uint32_t*>(xs)[i] = 0u;
         if constexpr (F == F_TERN) sum_xq = block_sum_int<kQWaves>(sum_xq, redi);
-    } else {  // F_SR: dword (unit u, pair q) = bf16 x[32u+q] | bf16 x[32u+q+16] << 16
+    } else {  // sign + residual: dword (unit u, pair q) = bf16 x[32u+q] | bf16 x[32u+q+16] << 16
         uint16_t* xh = reinterpret_cast<uint16_t*>(xs);
         for_pieces([&](int pi, const float* v) {
 #pragma unroll
@@ -453,12 +473,18 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const uint32_t ns = ~fr[u][j].s;
+                    uint32_t zz = 0;  // bf16 pair (-z, -z): exact, |z| <= 128
+                    if constexpr (F == F_SRZ) {
+                        const uint32_t h = __float_as_uint(-(float)(int8_t)fr[u][0].z) >> 16;
+                        zz = h | (h << 16);
+                    }
 #pragma unroll
                     for (int q = 0; q < 16; ++q) {
                         const float lo = (float)(int8_t)(fr[u][j].r0[q >> 2] >> (8 * (q & 3)));
                         const float hi = (float)(int8_t)(fr[u][j].r1[q >> 2] >> (8 * (q & 3)));
                         const uint32_t rp = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
                         accf2[u] = dot2bf(rp, xv[q], accf2[u]);
+                        if constexpr (F == F_SRZ) accf2[u] = dot2bf(zz, xv[q], accf2[u]);
                         const uint32_t sp = ((ns << (15 - q)) & 0x80008000u) | 0x3F803F80u;
                         accf[u] = dot2bf(sp, xv[q], accf[u]);
                     }
@@ -468,12 +494,12 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
         if (seg == nseg - 1) {
             // reduce every row of the group at once (independent DPP chains);
             // lane 63 holds the sums and writes the outputs
-            if constexpr (F == F_INT8F || F == F_SR || F == F_Q4) {
+            if constexpr (F == F_INT8F || kSignRes<F> || F == F_Q4) {
                 float v[U], v2[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     v[u] = wave_sum_to_lane63(accf[u]);
-                    if constexpr (F == F_SR) v2[u] = wave_sum_to_lane63(accf2[u]);
+                    if constexpr (kSignRes<F>) v2[u] = wave_sum_to_lane63(accf2[u]);
                 }
                 if (lane == 63) {
 #pragma unroll
@@ -482,7 +508,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
                         if (r < rows) {
                             const int row = row0 + r;
                             float o;
-                            if constexpr (F == F_SR) o = p.scale[row] * v[u] + v2[u] / p.scale2[row];
+                            if constexpr (kSignRes<F>) o = p.scale[row] * v[u] + v2[u] / p.scale2[row];
                             else if constexpr (F == F_Q4) o = v[u];  // group scales already applied
                             else o = v[u] / p.scale[row];
                             if constexpr (YT == 0) static_cast<float*>(p.y)[row] = o;
@@ -556,8 +582,8 @@ static hipError_t run(const QgemvArgs* a, int count, hipStream_t st) {
     const int nseg = (J + JS - 1) / JS;
     if (XREG && nseg != 1) return hipErrorInvalidValue;  // register-resident x needs items spanning the row
     const size_t lds = (size_t)nseg * JS * 64 * kCols * Fmt<F>::kLdsBytesPerCol;
-    const int64_t rowB = (F == F_TERN) ? K / 4 : (F == F_SR) ? K / 8 : (F == F_Q4) ? K / 2 : K;
-    const int64_t resB = (F == F_SR) ? K : (F == F_Q4) ? K / 16 : 0;
+    const int64_t rowB = (F == F_TERN) ? K / 4 : kSignRes<F> ? K / 8 : (F == F_Q4) ? K / 2 : K;
+    const int64_t resB = kSignRes<F> ? K : (F == F_Q4) ? K / 16 : 0;
     const int64_t cap = ((int64_t)1 << 31) / (rowB > resB ? rowB : resB);  // buffer ranges stay below 2 GiB
     const int cus = device_cu_count();
     int64_t total_rows = 0;
@@ -577,6 +603,7 @@ static hipError_t run(const QgemvArgs* a, int count, hipStream_t st) {
         p.resid = a[m].resid;
         p.scale = a[m].scale;
         p.scale2 = a[m].scale2;
+        p.zero = a[m].zero;
         p.x = a[m].x;
         p.y = a[m].y;
         p.acc_out = a[m].acc_out;
@@ -630,6 +657,10 @@ hipError_t launch_qgemv_group(const QgemvArgs* a, int count, hipStream_t st) {
         const bool spans = (h.k / 32 + 63) / 64 <= 2;  // one item of 2 chunk iterations covers the row
         if (h.yt == 0) return spans ? run<F_Q4, 1, 0, 1, 2, true>(a, count, st) : run<F_Q4, 1, 0, 4, 1>(a, count, st);
         return spans ? run<F_Q4, 1, 1, 1, 2, true>(a, count, st) : run<F_Q4, 1, 1, 4, 1>(a, count, st);
+    }
+    if (h.fmt == 4) {  // sign + zero-point residual
+        if (h.yt == 0) return run<F_SRZ, 1, 0, 1, 2>(a, count, st);
+        return run<F_SRZ, 1, 1, 1, 2>(a, count, st);
     }
     if (h.yt == 0) return run<F_SR, 1, 0, 1, 2>(a, count, st);
     return run<F_SR, 1, 1, 1, 2>(a, count, st);

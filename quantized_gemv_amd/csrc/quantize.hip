@@ -65,6 +65,44 @@ __global__ __launch_bounds__(kThreads) void absmax_rows_kernel(const void* x, in
     }
 }
 
+// ---------------------------------------------------------------- asymmetric per row
+// [VG] 'Asymmetric quantization': one workgroup per row finds the row's
+// minimum and maximum, derives (s, z) and writes the codes.
+template <int XT>
+__global__ __launch_bounds__(kThreads) void asym_rows_kernel(const void* x, int64_t rows, int64_t cols, int8_t* q,
+                                                             float* s, int8_t* z) {
+    __shared__ float red[kWaves];
+    const int64_t c8 = cols / 8;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        float lo = 0.0f, hi = 0.0f;  // the range always contains 0
+        for (int64_t i = threadIdx.x; i < c8; i += kThreads) {
+            float v[8];
+            load8<XT>(x, r * cols + i * 8, v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                lo = __builtin_fminf(lo, v[j]);
+                hi = __builtin_fmaxf(hi, v[j]);
+            }
+        }
+        hi = block_max(hi, red);
+        lo = -block_max(-lo, red);
+        float sc, zp;
+        asym_params(lo, hi, sc, zp);
+        if (threadIdx.x == 0) {
+            s[r] = sc;
+            z[r] = (int8_t)(int)zp;
+        }
+        for (int64_t i = threadIdx.x; i < c8; i += kThreads) {
+            float v[8];
+            int c[8];
+            load8<XT>(x, r * cols + i * 8, v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[j] = qcode_zp(v[j], sc, zp);
+            store8_codes(q, r * cols + i * 8, c);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- absmax per tensor
 // Pass 1: each workgroup writes the max |x| of its grid-stride share.
 template <int XT>
@@ -276,9 +314,10 @@ __global__ __launch_bounds__(kThreads) void ternary_codes_kernel(const float* w,
 // ---------------------------------------------------------------- sign + residual
 // One workgroup per weight row: exact mean |w| -> alpha, then the residual
 // R = w - alpha * sign(w), its absmax scale and int8 codes.
+template <bool ZP>
 __global__ __launch_bounds__(kThreads) void split_sign_residual_kernel(const float* w, int64_t n, int64_t k,
                                                                         int8_t* sign, float* alpha, int8_t* rq,
-                                                                        float* s_r) {
+                                                                        float* s_r, int8_t* z_r) {
     __shared__ unsigned long long h[256];
     __shared__ float red[kWaves];
     __shared__ float alpha_sh;
@@ -305,17 +344,30 @@ __global__ __launch_bounds__(kThreads) void split_sign_residual_kernel(const flo
         }
         __syncthreads();
         const float a = alpha_sh;
-        float m = 0.0f;
+        float m = 0.0f, lo = 0.0f;  // max |R| (symmetric) or max R and min R (zero-point)
         for (int64_t i = threadIdx.x; i < k4; i += kThreads) {
             const float4 v = row[i];
             const float e[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float res = e[j] - (e[j] >= 0.0f ? a : -a);
-                m = __builtin_fmaxf(m, __builtin_fabsf(res));
+                if constexpr (ZP) {
+                    m = __builtin_fmaxf(m, res);
+                    lo = __builtin_fminf(lo, res);
+                } else {
+                    m = __builtin_fmaxf(m, __builtin_fabsf(res));
+                }
             }
         }
-        const float sc = absmax_scale(block_max(m, red));
+        float sc, zp = 0.0f;
+        if constexpr (ZP) {
+            const float hi = block_max(m, red);
+            lo = -block_max(-lo, red);
+            asym_params(lo, hi, sc, zp);
+            if (threadIdx.x == 0) z_r[r] = (int8_t)(int)zp;
+        } else {
+            sc = absmax_scale(block_max(m, red));
+        }
         if (threadIdx.x == 0) s_r[r] = sc;
         for (int64_t i = threadIdx.x; i < k4; i += kThreads) {
             const float4 v = row[i];
@@ -326,7 +378,8 @@ __global__ __launch_bounds__(kThreads) void split_sign_residual_kernel(const flo
                 const bool pos = e[j] >= 0.0f;
                 const float res = e[j] - (pos ? a : -a);
                 so |= (uint32_t)(pos ? 0x01u : 0xFFu) << (8 * j);
-                ro |= (uint32_t)(qcode(res, sc) & 0xFF) << (8 * j);
+                const int qc = ZP ? qcode_zp(res, sc, zp) : qcode(res, sc);
+                ro |= (uint32_t)(qc & 0xFF) << (8 * j);
             }
             reinterpret_cast<uint32_t*>(sign + r * k)[i] = so;
             reinterpret_cast<uint32_t*>(rq + r * k)[i] = ro;
@@ -462,9 +515,18 @@ hipError_t launch_ternary(const float* w, int64_t count, int8_t* q, float* gamma
 }
 
 hipError_t launch_split_sign_residual(const float* w, int64_t n, int64_t k, int8_t* sign, float* alpha, int8_t* rq,
-                                      float* s_r, hipStream_t st) {
+                                      float* s_r, int8_t* z_r, hipStream_t st) {
     const int g = grid_for(n, 1, 65535);
-    split_sign_residual_kernel<<<g, kThreads, 0, st>>>(w, n, k, sign, alpha, rq, s_r);
+    if (z_r) split_sign_residual_kernel<true><<<g, kThreads, 0, st>>>(w, n, k, sign, alpha, rq, s_r, z_r);
+    else split_sign_residual_kernel<false><<<g, kThreads, 0, st>>>(w, n, k, sign, alpha, rq, s_r, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_asym_rows(const void* x, int xt, int64_t rows, int64_t cols, int8_t* q, float* s, int8_t* z,
+                            hipStream_t st) {
+    const int g = grid_for(rows, 1, 65535);
+    if (xt == 0) asym_rows_kernel<0><<<g, kThreads, 0, st>>>(x, rows, cols, q, s, z);
+    else asym_rows_kernel<1><<<g, kThreads, 0, st>>>(x, rows, cols, q, s, z);
     return hipGetLastError();
 }
 

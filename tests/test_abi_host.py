@@ -48,7 +48,7 @@ def test_header_symbols_exported(qg):
     for name in decl:
         assert hasattr(l, name), name
     assert set(decl) == set(qg.EXPORTED)
-    assert qg.lib().qg_abi_version() == 20300
+    assert qg.lib().qg_abi_version() == 20400
     for st in range(0, 8):
         assert qg.status_str(st)
 
@@ -127,8 +127,8 @@ def test_validation_ternary_split_pack(qg):
 def test_validation_qgemv(qg):
     l = qg.lib()
 
-    def call(fmt=0, n=64, k=256, amode=1, xt=1, yt=1, acc=None, codes=A, resid=A, scale=A, scale2=A, x=A):
-        w = qg.CWeight(fmt, 0, n, k, codes, resid, scale, scale2)
+    def call(fmt=0, n=64, k=256, amode=1, xt=1, yt=1, acc=None, codes=A, resid=A, scale=A, scale2=A, x=A, zero=A):
+        w = qg.CWeight(fmt, 0, n, k, codes, resid, scale, scale2, zero)
         return l.qg_qgemv(ctypes.byref(w), amode, x, xt, A, yt, acc, None)
 
     assert l.qg_qgemv(None, 1, A, 1, A, 1, None, None) == 1
@@ -155,6 +155,30 @@ def test_validation_qgemv(qg):
     assert call(fmt=3, k=384) == 2
     q4 = qg.QG_WFMT_Q4K
     assert q4 == 3
+    # sign + zero-point residual: as sign + residual, and the zero-points are required
+    z = qg.QG_WFMT_SIGN1_RES8Z
+    assert call(fmt=z, amode=0) == 4
+    assert call(fmt=z, xt=0) == 4
+    assert call(fmt=z, zero=None) == 1
+    assert call(fmt=z, scale2=None) == 1
+    assert call(fmt=z, resid=U) == 3
+    assert call(fmt=2, zero=None) != 1  # zero is not read by the other formats
+
+
+def test_validation_asym_and_zp_split(qg):
+    l = qg.lib()
+    q = l.qg_quantize_asym
+    assert q(None, 0, 4, 64, A, A, A, None) == 1
+    assert q(A, 0, 4, 64, A, A, None, None) == 1
+    assert q(A, 2, 4, 64, A, A, A, None) == 4
+    assert q(A, 0, 4, 12, A, A, A, None) == 2
+    assert q(A, 0, 0, 64, A, A, A, None) == 2
+    assert q(U, 1, 4, 64, A, A, A, None) == 3
+    assert q(A, 1, 4, 64, U, A, A, None) == 3
+    s = l.qg_split_sign_residual_zp
+    assert s(A, 4, 12, A, A, A, A, A, None) == 2
+    assert s(A, 4, 64, A, A, A, A, None, None) == 1
+    assert s(A, 4, 64, U, A, A, A, A, None) == 3
 
 
 def test_validation_quantize_q4k(qg):
