@@ -582,7 +582,6 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
     wl = synth.ternary_decode()
     q, gamma = qg.quantize_ternary(torch.from_numpy(wl.tensors["w"]).to(dev))
     packed = qg.pack(q, 2)
-    del q
     per = packed.numel() + 4
     copies = [qg.QWeight(qg.QG_WFMT_TERNARY2, 11008, 4096, packed.clone(), gamma.clone())
               for _ in range(rotate_count(per))]
@@ -600,6 +599,23 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
     out["ternary_11008x4096"] = {"us": round(sec * 1e6, 3), "weight_GBps": round(per / sec / 1e9, 1),
                                  "hbm_frac": round(per / sec / 1e9 / HBM_PEAK_GBS, 4), "rotating_copies": len(copies)}
     log("ternary: %.2f us, %.0f GB/s" % (sec * 1e6, per / sec / 1e9))
+    del copies, cws, packed
+
+    # -- the same codes packed five per byte in base 3 (1.6 bits per weight)
+    packed = qg.pack_base3(q)
+    del q
+    per = packed.numel() + 4
+    copies = [qg.QWeight(qg.QG_WFMT_TERNARY3, 11008, 4096, packed.clone(), gamma.clone())
+              for _ in range(rotate_count(per))]
+    cws = [W.c_struct() for W in copies]
+    t = Timed(torch, [mkt(cw) for cw in cws])
+    t.run(2)
+    sec = t.run(10) / t.n
+    out["ternary_base3_11008x4096"] = {"us": round(sec * 1e6, 3), "weight_GBps": round(per / sec / 1e9, 1),
+                                       "hbm_frac": round(per / sec / 1e9 / HBM_PEAK_GBS, 4),
+                                       "bytes": per, "weights_per_ns": round(11008 * 4096 / sec / 1e9, 1),
+                                       "rotating_copies": len(copies)}
+    log("ternary base 3: %.2f us, %.0f GB/s" % (sec * 1e6, per / sec / 1e9))
     del copies, cws, packed
     torch.cuda.empty_cache()
 

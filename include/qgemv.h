@@ -74,6 +74,8 @@ typedef int32_t qg_status;
                               /* points, two-level scales in [n][k/256][16] bytes   */
 #define QG_WFMT_SIGN1_RES8Z 4 /* as SIGN1_RES8 with an asymmetric residual: codes   */
                               /* in [-128, 127], s_r[n] and a zero-point z_r[n]     */
+#define QG_WFMT_TERNARY3   5  /* ternary, five per byte in base 3 (1.6 bits per     */
+                              /* weight), [n][16 ceil(k/80)], per-tensor gamma      */
 
 /* activation modes of qg_qgemv */
 #define QG_ACT_INT8  0  /* x is quantized per tensor (absmax int8) inside the call */
@@ -280,6 +282,25 @@ qg_status qg_unpack(const uint8_t* packed, int64_t n, int64_t k, int32_t bits,
                     int8_t* codes, void* stream);
 
 /*
+ * Base-3 packing of ternary codes, five per byte ([VG] 'BitNet b1.58': three
+ * states carry log2(3) ~ 1.58 bits; 3^5 = 243 <= 256 gives 1.6 bits per
+ * weight, against 2 for qg_pack's 2-bit fields).  The pages fix no layout;
+ * this library's:
+ *   digit f = q + 1 in {0, 1, 2};
+ *   byte j of a row holds weights 5j .. 5j+4 as v = sum_i f[5j+i] 3^(4-i)
+ *   (first weight = leading digit), stored as t = ceil(256 v / 243), so that
+ *   digit i = (3 t_i) >> 8 with t_{i+1} = (3 t_i) & 255;
+ *   a row takes qg_base3_row_bytes(k) = 16 * ceil(k / 80) bytes (80 weights
+ *   per 16-byte chunk); weights past k are digit 1 (q = 0).
+ * codes : [n][k] int8 in {-1, 0, 1} (other values give unspecified bytes).
+ * packed: [n][qg_base3_row_bytes(k)] uint8.
+ * qg_base3_row_bytes returns 0 for k < 1.
+ */
+int64_t qg_base3_row_bytes(int64_t k);
+qg_status qg_pack_base3(const int8_t* codes, int64_t n, int64_t k, uint8_t* packed, void* stream);
+qg_status qg_unpack_base3(const uint8_t* packed, int64_t n, int64_t k, int8_t* codes, void* stream);
+
+/*
  * A quantized weight matrix, described on the host (the struct lives in host
  * memory; its pointers are device pointers, all 16-B aligned).
  *   QG_WFMT_INT8      : codes = int8 [n][k];           scale = s_w[n]
@@ -289,6 +310,8 @@ qg_status qg_unpack(const uint8_t* packed, int64_t n, int64_t k, int32_t bits,
  *   QG_WFMT_Q4K       : codes = 4-bit plane [n][k/2]; resid = the metadata
  *                       plane [n][k/256][16] (as qg_quantize_q4k writes
  *                       them); scale, scale2 unused (may be NULL)
+ *   QG_WFMT_TERNARY3  : codes = base-3 bytes [n][qg_base3_row_bytes(k)];
+ *                       scale = &gamma (1 fp32)
  *   QG_WFMT_SIGN1_RES8Z: as SIGN1_RES8 (rq from qg_split_sign_residual_zp);
  *                       zero = z_r[n]
  * zero is read for QG_WFMT_SIGN1_RES8Z only (may be NULL otherwise).
@@ -319,6 +342,7 @@ typedef struct qg_weight {
  *   fmt TERNARY2, amode QG_ACT_INT8 ([VG] 'BitNet b1.58' Fig. 58-59: +1 adds,
  *       0 skips, -1 subtracts the int8 activation):
  *       acc[n] = sum_k t[n][k] * xq[k] (int32, exact); y[n] = acc[n] * gamma / s_x.
+ *   fmt TERNARY3, amode QG_ACT_INT8: the same product on base-3 packed codes.
  *   fmt SIGN1_RES8, amode QG_ACT_FLOAT ([SEP] sections 2.3 and 3.3: backbone
  *       and residual products in one fused kernel, results added):
  *       y[n] = alpha[n] * sum_k sign[n][k] x[k] + (sum_k rq[n][k] x[k]) / s_r[n],

@@ -9,10 +9,10 @@ libqgemv.so; this package only marshals arguments (see _binding.py).
 """
 from ._binding import (QgError, QWeight, CWeight, EXPORTED, LIB_PATH, lib, status_str,
                        quantize_absmax, quantize_absmax_split, detect_outliers, gather_columns_bf16, quantize_ternary,
-                       split_sign_residual, split_sign_residual_zp, quantize_asym, quantize_q4k, SepWeight, sep_resid_ld, quantize_mxfp4, gemm_mxfp4, prefill_mxfp4, split_sep_threshold, qgemv_sep, pack, unpack, qgemv, qgemv_grouped, qgemv_batch, qgemv_batch_grouped, GroupLaunch, qgemv_launch_raw,
+                       split_sign_residual, split_sign_residual_zp, quantize_asym, quantize_q4k, SepWeight, sep_resid_ld, quantize_mxfp4, gemm_mxfp4, prefill_mxfp4, split_sep_threshold, qgemv_sep, pack, unpack, base3_row_bytes, pack_base3, unpack_base3, qgemv, qgemv_grouped, qgemv_batch, qgemv_batch_grouped, GroupLaunch, qgemv_launch_raw,
                        qgemm_w8a8_outlier, qgemm_w8a8, out_ld, QG_MAX_GROUP, QG_OUT_LD_ALIGN, QG_MAX_OUT_LD,
                        QG_F32, QG_BF16, QG_PER_TENSOR, QG_PER_ROW, QG_WFMT_INT8, QG_WFMT_TERNARY2,
-                       QG_WFMT_SIGN1_RES8, QG_WFMT_Q4K, QG_WFMT_SIGN1_RES8Z, QG_ACT_INT8, QG_ACT_FLOAT, QG_MAX_OUTLIERS, QG_QGEMV_MAX_K,
+                       QG_WFMT_SIGN1_RES8, QG_WFMT_Q4K, QG_WFMT_SIGN1_RES8Z, QG_WFMT_TERNARY3, QG_ACT_INT8, QG_ACT_FLOAT, QG_MAX_OUTLIERS, QG_QGEMV_MAX_K,
                        QG_SEP_MAX_K, QG_BATCH_MAX_M, QG_BATCH_MAX_K, QG_MX_BLOCK)
 
 __all__ = [n for n in dir() if not n.startswith("_")]

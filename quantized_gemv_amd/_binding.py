@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 QG_OK = 0
 QG_F32, QG_BF16 = 0, 1
 QG_PER_TENSOR, QG_PER_ROW = 0, 1
-QG_WFMT_INT8, QG_WFMT_TERNARY2, QG_WFMT_SIGN1_RES8, QG_WFMT_Q4K, QG_WFMT_SIGN1_RES8Z = 0, 1, 2, 3, 4
+QG_WFMT_INT8, QG_WFMT_TERNARY2, QG_WFMT_SIGN1_RES8, QG_WFMT_Q4K, QG_WFMT_SIGN1_RES8Z, QG_WFMT_TERNARY3 = 0, 1, 2, 3, 4, 5
 QG_ACT_INT8, QG_ACT_FLOAT = 0, 1
 QG_MAX_OUTLIERS = 256
 QG_QGEMV_MAX_K = 32768
@@ -76,6 +76,9 @@ _SIGS = {
     "qg_qgemv_sep": (_c_i32, [_c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_i32, _c_vp,
                               _c_vp, _c_vp]),
     "qg_pack": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp]),
+    "qg_base3_row_bytes": (_c_i64, [_c_i64]),
+    "qg_pack_base3": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp]),
+    "qg_unpack_base3": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp]),
     "qg_unpack": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp]),
     "qg_qgemv": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp]),
     "qg_qgemv_grouped": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_i32, _c_vp, _c_i32, ctypes.POINTER(_c_vp),
@@ -285,6 +288,30 @@ def unpack(packed: torch.Tensor, bits: int, k: int):
     n = packed.shape[0] if packed.dim() == 2 else 1
     out = torch.empty((n, k), dtype=torch.int8, device=packed.device)
     _check(lib().qg_unpack(_p(packed), n, k, bits, _p(out), _stream(packed)), "qg_unpack")
+    return out
+
+
+def base3_row_bytes(k: int) -> int:
+    """Bytes of one base-3 packed row (qg_base3_row_bytes): 16 per 80 weights."""
+    return int(lib().qg_base3_row_bytes(k))
+
+
+def pack_base3(codes: torch.Tensor, out: torch.Tensor = None):
+    """Ternary codes, five per byte (qg_pack_base3): [n][k] int8 -> [n][base3_row_bytes(k)] uint8."""
+    _dev(codes, "codes", torch.int8)
+    n, k = (1, codes.shape[0]) if codes.dim() == 1 else tuple(codes.shape)
+    rb = base3_row_bytes(k)
+    out = torch.empty((n, rb), dtype=torch.uint8, device=codes.device) if out is None else out
+    _check(lib().qg_pack_base3(_p(codes), n, k, _p(out), _stream(codes)), "qg_pack_base3")
+    return out
+
+
+def unpack_base3(packed: torch.Tensor, k: int):
+    """Inverse of pack_base3 (qg_unpack_base3)."""
+    _dev(packed, "packed", torch.uint8)
+    n = packed.shape[0] if packed.dim() == 2 else 1
+    out = torch.empty((n, k), dtype=torch.int8, device=packed.device)
+    _check(lib().qg_unpack_base3(_p(packed), n, k, _p(out), _stream(packed)), "qg_unpack_base3")
     return out
 
 

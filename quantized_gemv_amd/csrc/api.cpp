@@ -76,7 +76,7 @@ const char* qg_status_str(qg_status s) {
     }
 }
 
-int32_t qg_abi_version(void) { return 20400; }
+int32_t qg_abi_version(void) { return 20500; }
 
 size_t qg_quantize_absmax_workspace_bytes(int64_t rows, int64_t cols, int32_t gran) {
     if (gran != QG_PER_TENSOR || rows < 1 || cols < 8) return 0;
@@ -269,6 +269,23 @@ qg_status qg_unpack(const uint8_t* packed, int64_t n, int64_t k, int32_t bits, i
     return from_hip(qg::launch_unpack(packed, n * k, bits, codes, as_stream(stream)));
 }
 
+int64_t qg_base3_row_bytes(int64_t k) {
+    if (k < 1 || k >= ((int64_t)1 << 40)) return 0;
+    return 16 * ((k + 79) / 80);
+}
+
+qg_status qg_pack_base3(const int8_t* codes, int64_t n, int64_t k, uint8_t* packed, void* stream) {
+    if (!codes || !packed) return QG_ERR_NULLPTR;
+    if (n < 1 || k < 1 || n > ((int64_t)1 << 40) / k) return QG_ERR_SHAPE;
+    return from_hip(qg::launch_pack3(codes, n, k, packed, as_stream(stream)));
+}
+
+qg_status qg_unpack_base3(const uint8_t* packed, int64_t n, int64_t k, int8_t* codes, void* stream) {
+    if (!codes || !packed) return QG_ERR_NULLPTR;
+    if (n < 1 || k < 1 || n > ((int64_t)1 << 40) / k) return QG_ERR_SHAPE;
+    return from_hip(qg::launch_unpack3(packed, n, k, codes, as_stream(stream)));
+}
+
 static qg_status check_qgemv(const qg_weight* w, int32_t amode, const void* x, int32_t xt, const void* y,
                              int32_t yt, const int32_t* acc_out) {
     if (!w || !x || !y) return QG_ERR_NULLPTR;
@@ -279,6 +296,7 @@ static qg_status check_qgemv(const qg_weight* w, int32_t amode, const void* x, i
     switch (w->fmt) {
         case QG_WFMT_INT8: break;
         case QG_WFMT_TERNARY2:
+        case QG_WFMT_TERNARY3:
             if (amode != QG_ACT_INT8) return QG_ERR_ARG;
             break;
         case QG_WFMT_SIGN1_RES8:

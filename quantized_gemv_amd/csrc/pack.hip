@@ -1,4 +1,5 @@
-// pack.hip -- bit packing of ternary (2-bit) and sign (1-bit) codes.
+// pack.hip -- bit packing of ternary (2-bit), sign (1-bit) and base-3
+// ternary (five per byte) codes.
 //
 // Layout: code k of a row sits in byte k / v at bit offset bits * (k % v),
 // least significant field first, v = 8 / bits.  Since every row length is a
@@ -53,6 +54,44 @@ __global__ __launch_bounds__(kThreads) void unpack1_kernel(const uint8_t* in, in
     }
 }
 
+// ---------------------------------------------------------------- base 3
+// Five ternary digits f = q + 1 per byte, leading digit first, stored as the
+// base-3 fraction rounded up to 8 bits, t = ceil(256 v / 243); a row takes
+// rb = 16 * ceil(k / 80) bytes and the weights past k are digit 1 (q = 0).
+// One thread per packed byte.
+__global__ __launch_bounds__(kThreads) void pack3_kernel(const int8_t* codes, int64_t n, int64_t k, int64_t rb,
+                                                         uint8_t* out) {
+    const int64_t total = n * rb;
+    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
+        const int64_t r = i / rb, j = i - r * rb;
+        uint32_t v = 0;
+#pragma unroll
+        for (int t = 0; t < 5; ++t) {
+            const int64_t c = 5 * j + t;
+            const uint32_t f = c < k ? (uint32_t)((int)codes[r * k + c] + 1) : 1u;
+            v = 3u * v + f;
+        }
+        out[i] = (uint8_t)((256u * v + 242u) / 243u);
+    }
+}
+
+// digits by repeated multiplication by 3: digit = (3 t) >> 8, t = (3 t) & 255
+__global__ __launch_bounds__(kThreads) void unpack3_kernel(const uint8_t* in, int64_t n, int64_t k, int64_t rb,
+                                                           int8_t* codes) {
+    const int64_t total = n * rb;
+    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
+        const int64_t r = i / rb, j = i - r * rb;
+        uint32_t t = in[i];
+#pragma unroll
+        for (int d = 0; d < 5; ++d) {
+            const uint32_t m = 3u * t;
+            t = m & 255u;
+            const int64_t c = 5 * j + d;
+            if (c < k) codes[r * k + c] = (int8_t)((int)(m >> 8) - 1);
+        }
+    }
+}
+
 static int pack_grid(int64_t nbytes) {
     int64_t g = (nbytes + kThreads * 4 - 1) / (kThreads * 4);
     if (g < 1) g = 1;
@@ -73,6 +112,18 @@ hipError_t launch_unpack(const uint8_t* packed, int64_t count, int bits, int8_t*
     if (nbytes == 0) return hipSuccess;
     if (bits == 2) unpack2_kernel<<<pack_grid(nbytes), kThreads, 0, st>>>(packed, nbytes, codes);
     else unpack1_kernel<<<pack_grid(nbytes), kThreads, 0, st>>>(packed, nbytes, codes);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack3(const int8_t* codes, int64_t n, int64_t k, uint8_t* packed, hipStream_t st) {
+    const int64_t rb = 16 * ((k + 79) / 80);
+    pack3_kernel<<<pack_grid(n * rb), kThreads, 0, st>>>(codes, n, k, rb, packed);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack3(const uint8_t* packed, int64_t n, int64_t k, int8_t* codes, hipStream_t st) {
+    const int64_t rb = 16 * ((k + 79) / 80);
+    unpack3_kernel<<<pack_grid(n * rb), kThreads, 0, st>>>(packed, n, k, rb, codes);
     return hipGetLastError();
 }
 

@@ -41,6 +41,8 @@ hipError_t launch_asym_rows(const void* x, int xt, int64_t rows, int64_t cols, i
 hipError_t launch_quantize_q4k(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* meta, hipStream_t st);
 hipError_t launch_pack(const int8_t* codes, int64_t count, int bits, uint8_t* packed, hipStream_t st);
 hipError_t launch_unpack(const uint8_t* packed, int64_t count, int bits, int8_t* codes, hipStream_t st);
+hipError_t launch_pack3(const int8_t* codes, int64_t n, int64_t k, uint8_t* packed, hipStream_t st);
+hipError_t launch_unpack3(const uint8_t* packed, int64_t n, int64_t k, int8_t* codes, hipStream_t st);
 
 struct QgemvArgs {
     int fmt, amode, xt, yt;

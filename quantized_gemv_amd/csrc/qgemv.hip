@@ -37,6 +37,13 @@
 //                    residual becomes bf16 pairs (col j, col j+16) and the sign
 //                    bits become +-1.0 bf16 pairs with one bit-field insert;
 //                    both go through v_dot2_f32_bf16 against bf16 x pairs.
+//   TERNARY3       : 16 B chunk = 80 weights, five per byte as the base-3
+//                    fraction ceil(256 v / 243); the bytes of a dword are
+//                    split into two 16-bit lanes (v_perm), and each x3 moves
+//                    the next digit of every byte into bits 8-9 of its lane:
+//                    one v_perm gathers the four digits, v_dot4 takes them
+//                    against x staged in the same (dword, digit) order;
+//                    sum_k (q+1) x - sum_k x as for TERNARY2.
 //   SIGN1_RES8Z    : the same units; every residual pair also goes through
 //                    one more v_dot2 with the pair (-z, -z), so the sum is
 //                    sum_k (rq - z) x[k] as it accumulates (a z * sum_k x[k]
@@ -52,7 +59,7 @@
 
 namespace qg {
 
-enum { F_INT8F = 0, F_INT8I = 1, F_TERN = 2, F_SR = 3, F_Q4 = 4, F_SRZ = 5 };
+enum { F_INT8F = 0, F_INT8I = 1, F_TERN = 2, F_SR = 3, F_Q4 = 4, F_SRZ = 5, F_TERN3 = 6 };
 // the sign + residual formats (symmetric residual, or with a zero-point)
 template <int F>
 constexpr bool kSignRes = (F == F_SR || F == F_SRZ);
@@ -110,6 +117,12 @@ struct Fmt<F_TERN> {
     struct Frag { u32x4 w; };
 };
 template <>
+struct Fmt<F_TERN3> {
+    static constexpr int kColsPerChunk = 80;  // 16 B of base-3 bytes, 5 weights each
+    static constexpr int kLdsBytesPerCol = 1;
+    struct Frag { u32x4 w; };
+};
+template <>
 struct Fmt<F_SR> {
     static constexpr int kColsPerChunk = 32;
     static constexpr int kLdsBytesPerCol = 2;
@@ -127,6 +140,15 @@ struct Fmt<F_Q4> {
     static constexpr int kLdsBytesPerCol = 0;  // x (bf16) travels with each item
     struct Frag { u32x4 w; u32x4 meta; u32x4 x[4]; };
 };
+
+// LDS byte of activation column c for the base-3 format: chunk c / 80 holds
+// 20 dwords, dword 5 d + i carrying column 80 g + 20 d + 5 b + i in byte b.
+__device__ __forceinline__ int tern3_slot(int c) {
+    const int g = c / 80, r = c - 80 * g;
+    const int d = r / 20, r2 = r - 20 * d;
+    const int b = r2 / 5, i = r2 - 5 * b;
+    return 80 * g + 4 * (5 * d + i) + b;
+}
 
 // Workgroup shape: 8 waves (2 per SIMD, so one wave's LDS / ALU latency is
 // covered by the other's work), one workgroup per CU.
@@ -155,14 +177,14 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     const int K = p.k;
     const int row0 = ((int)blockIdx.x - grp.wg_start[mi]) * p.rows_per_wg;
     const int rows = min(p.rows_per_wg, p.n - row0);
-    const int C = K / kCols;           // chunks per row
+    const int C = (K + kCols - 1) / kCols;  // chunks per row (the last may be partly padding)
     const int J = (C + 63) / 64;       // chunk iterations per lane per row
     const int nseg = (J + JS - 1) / JS;
     // x is staged (zero-padded) for every chunk iteration a segment can touch
     const int padded_cols = nseg * JS * 64 * kCols;
 
     // ------------------------------------------------------------ stream
-    const int rowB = (F == F_TERN) ? K / 4 : kSignRes<F> ? K / 8 : (F == F_Q4) ? K / 2 : K;  // code bytes per row
+    const int rowB = (F == F_TERN) ? K / 4 : kSignRes<F> ? K / 8 : (F == F_Q4) ? K / 2 : (F == F_TERN3) ? 16 * C : K;  // code bytes per row
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.codes + (int64_t)row0 * rowB, (uint32_t)(rows * rowB));
     __amdgpu_buffer_rsrc_t rr = rc;
     if constexpr (kSignRes<F>) rr = make_rsrc(p.resid + (int64_t)row0 * K, (uint32_t)(rows * K));
@@ -319,7 +341,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     int sum_xq = 0;   // sum of int8 activations (ternary offset correction)
     if constexpr (kXPerItem) {
         // nothing to stage: every item carries its own slice of x
-    } else if constexpr (F == F_INT8I || F == F_TERN) {
+    } else if constexpr (F == F_INT8I || F == F_TERN || F == F_TERN3) {
         float m = 0.0f;
         for_pieces(
             [&](int, const float* v) {
@@ -336,14 +358,20 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
                 const int c = pi * kElems + e;
                 if constexpr (F == F_INT8I) {
                     xs[c] = (uint8_t)(q & 0xFF);
+                } else if constexpr (F == F_TERN3) {
+                    xs[tern3_slot(c)] = (uint8_t)(q & 0xFF);
                 } else {  // column 16g + 4b + f is stored at 16g + 4f + b (byte-plane order)
                     const int l = c & 15;
                     xs[(c - l) + 4 * (l & 3) + (l >> 2)] = (uint8_t)(q & 0xFF);
                 }
             }
         });
-        for (int i = K / 4 + tid; i < padded_cols / 4; i += kQThreads) reinterpret_cast<uint32_t*>(xs)[i] = 0u;
-        if constexpr (F == F_TERN) sum_xq = block_sum_int<kQWaves>(sum_xq, redi);
+        if constexpr (F == F_TERN3) {  // padding columns sit inside the last chunk's permutation
+            for (int c = K + tid; c < padded_cols; c += kQThreads) xs[tern3_slot(c)] = 0;
+        } else {
+            for (int i = K / 4 + tid; i < padded_cols / 4; i += kQThreads) reinterpret_cast<uint32_t*>(xs)[i] = 0u;
+        }
+        if constexpr (F == F_TERN || F == F_TERN3) sum_xq = block_sum_int<kQWaves>(sum_xq, redi);
     } else {  // sign + residual: dword (unit u, pair q) = bf16 x[32u+q] | bf16 x[32u+q+16] << 16
         uint16_t* xh = reinterpret_cast<uint16_t*>(xs);
         for_pieces([&](int pi, const float* v) {
@@ -446,6 +474,34 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
 #pragma unroll
                     for (int d = 0; d < 4; ++d) acc1[u] = sdot4(fr[u][j].w[d], xq[d], acc1[u]);
                 }
+            } else if constexpr (F == F_TERN3) {
+                // x of the chunk: dword 5 d + i holds the activations of digit i
+                // of the four bytes of weight dword d
+                const u32x4* xp = reinterpret_cast<const u32x4*>(xs) + 5 * c;
+                uint32_t xv[20];
+#pragma unroll
+                for (int q = 0; q < 5; ++q) {
+                    const u32x4 t = xp[q];
+                    xv[4 * q] = t[0]; xv[4 * q + 1] = t[1]; xv[4 * q + 2] = t[2]; xv[4 * q + 3] = t[3];
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const uint32_t w = fr[u][j].w[d];
+                        uint32_t a = __builtin_amdgcn_perm(0u, w, 0x0C020C00u);  // bytes 0, 2 in 16-bit lanes
+                        uint32_t b = __builtin_amdgcn_perm(0u, w, 0x0C030C01u);  // bytes 1, 3
+#pragma unroll
+                        for (int i = 0; i < 5; ++i) {
+                            a = a + (a << 1);  // x3: digit i of each byte now in bits 8-9 of its lane
+                            b = b + (b << 1);
+                            const uint32_t dg = __builtin_amdgcn_perm(b, a, 0x07030501u);  // digits of bytes 0..3
+                            acc1[u] = sdot4(dg, xv[5 * d + i], acc1[u]);
+                            a &= 0x00FF00FFu;
+                            b &= 0x00FF00FFu;
+                        }
+                    }
+                }
             } else if constexpr (F == F_TERN) {
                 const u32x4* xp = reinterpret_cast<const u32x4*>(xs) + 4 * c;
                 u32x4 xq[4];
@@ -529,9 +585,9 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
                         const int r = g * U + u;
                         if (r < rows) {
                             const int row = row0 + r;
-                            const int a = (F == F_TERN) ? v[u] - sum_xq : v[u];
+                            const int a = (F == F_TERN || F == F_TERN3) ? v[u] - sum_xq : v[u];
                             float o;
-                            if constexpr (F == F_TERN) o = (float)a * p.scale[0] / sx;
+                            if constexpr (F == F_TERN || F == F_TERN3) o = (float)a * p.scale[0] / sx;
                             else o = (float)a / (p.scale[row] * sx);
                             if (p.acc_out) p.acc_out[row] = a;
                             if constexpr (YT == 0) static_cast<float*>(p.y)[row] = o;
@@ -577,12 +633,12 @@ template <int F, int XT, int YT, int U, int JS, bool XREG = false>
 static hipError_t run(const QgemvArgs* a, int count, hipStream_t st) {
     constexpr int kCols = Fmt<F>::kColsPerChunk;
     const int K = (int)a[0].k;
-    const int C = K / kCols;
+    const int C = (K + kCols - 1) / kCols;
     const int J = (C + 63) / 64;
     const int nseg = (J + JS - 1) / JS;
     if (XREG && nseg != 1) return hipErrorInvalidValue;  // register-resident x needs items spanning the row
     const size_t lds = (size_t)nseg * JS * 64 * kCols * Fmt<F>::kLdsBytesPerCol;
-    const int64_t rowB = (F == F_TERN) ? K / 4 : kSignRes<F> ? K / 8 : (F == F_Q4) ? K / 2 : K;
+    const int64_t rowB = (F == F_TERN) ? K / 4 : kSignRes<F> ? K / 8 : (F == F_Q4) ? K / 2 : (F == F_TERN3) ? 16 * C : K;
     const int64_t resB = kSignRes<F> ? K : (F == F_Q4) ? K / 16 : 0;
     const int64_t cap = ((int64_t)1 << 31) / (rowB > resB ? rowB : resB);  // buffer ranges stay below 2 GiB
     const int cus = device_cu_count();
@@ -653,6 +709,7 @@ hipError_t launch_qgemv_group(const QgemvArgs* a, int count, hipStream_t st) {
     }
     if (h.fmt == 0 && h.amode == 0) return run_xy<F_INT8I, 2, 4>(a, count, st);
     if (h.fmt == 1) return run_xy<F_TERN, 4, 1>(a, count, st);
+    if (h.fmt == 5) return run_xy<F_TERN3, 4, 1>(a, count, st);
     if (h.fmt == 3) {  // bf16 activations only
         const bool spans = (h.k / 32 + 63) / 64 <= 2;  // one item of 2 chunk iterations covers the row
         if (h.yt == 0) return spans ? run<F_Q4, 1, 0, 1, 2, true>(a, count, st) : run<F_Q4, 1, 0, 4, 1>(a, count, st);

@@ -14,6 +14,7 @@ import subprocess
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 
@@ -48,7 +49,7 @@ def test_header_symbols_exported(qg):
     for name in decl:
         assert hasattr(l, name), name
     assert set(decl) == set(qg.EXPORTED)
-    assert qg.lib().qg_abi_version() == 20400
+    assert qg.lib().qg_abi_version() == 20500
     for st in range(0, 8):
         assert qg.status_str(st)
 
@@ -56,7 +57,16 @@ def test_header_symbols_exported(qg):
 A = 4096  # a 16-B aligned fake address: validation rejects before any use
 U = 4097  # misaligned
 
+# Every call below that passes A or U must be rejected by the library's
+# argument checks: a call that got through would launch a kernel on a fake
+# device address.  On a machine with a visible GPU that would fault the card,
+# so these tests run only where no GPU is visible (device_count() does not
+# initialise the runtime).
+needs_no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                  reason="passes fake device addresses; runs where no GPU is visible")
 
+
+@needs_no_gpu
 def test_validation_quantize_absmax(qg):
     l = qg.lib()
     f = l.qg_quantize_absmax
@@ -72,6 +82,7 @@ def test_validation_quantize_absmax(qg):
     assert f(A, 0, 4, 64, 0, A, A, A, need - 1, None) == 5
 
 
+@needs_no_gpu
 def test_validation_split_and_gather(qg):
     l = qg.lib()
     f = l.qg_quantize_absmax_split
@@ -101,6 +112,7 @@ def test_validation_split_and_gather(qg):
     assert g(A, 4, 64, good, 3, A, 2, None) == 2
 
 
+@needs_no_gpu
 def test_validation_ternary_split_pack(qg):
     l = qg.lib()
     ws = l.qg_ternary_workspace_bytes(4, 64)
@@ -124,6 +136,7 @@ def test_validation_ternary_split_pack(qg):
     assert l.qg_unpack(A, 4, 64, 0, A, None) == 4
 
 
+@needs_no_gpu
 def test_validation_qgemv(qg):
     l = qg.lib()
 
@@ -162,9 +175,30 @@ def test_validation_qgemv(qg):
     assert call(fmt=z, zero=None) == 1
     assert call(fmt=z, scale2=None) == 1
     assert call(fmt=z, resid=U) == 3
-    assert call(fmt=2, zero=None) != 1  # zero is not read by the other formats
+    # zero is required by SIGN1_RES8Z only: with a bad k the symmetric format
+    # gets past the pointer checks to the shape check (no launch either way)
+    assert call(fmt=2, zero=None, k=200) == 2
+    assert call(fmt=z, zero=None, k=200) == 1
+    # base-3 ternary: int8 activations only
+    assert call(fmt=qg.QG_WFMT_TERNARY3, amode=1) == 4
+    assert call(fmt=qg.QG_WFMT_TERNARY3, scale=None) == 1
+    assert call(fmt=qg.QG_WFMT_TERNARY3, k=200, amode=0) == 2
 
 
+@needs_no_gpu
+def test_base3_row_bytes_and_validation(qg):
+    l = qg.lib()
+    import oracle.base3 as b3
+    for k in (1, 5, 79, 80, 81, 4096, 11008, 32768):
+        assert l.qg_base3_row_bytes(k) == b3.row_bytes(k)
+    assert l.qg_base3_row_bytes(0) == 0
+    assert l.qg_pack_base3(None, 4, 64, A, None) == 1
+    assert l.qg_pack_base3(A, 0, 64, A, None) == 2
+    assert l.qg_unpack_base3(A, 4, 0, A, None) == 2
+    assert l.qg_unpack_base3(A, 4, 64, None, None) == 1
+
+
+@needs_no_gpu
 def test_validation_asym_and_zp_split(qg):
     l = qg.lib()
     q = l.qg_quantize_asym
@@ -181,6 +215,7 @@ def test_validation_asym_and_zp_split(qg):
     assert s(A, 4, 64, U, A, A, A, A, None) == 3
 
 
+@needs_no_gpu
 def test_validation_quantize_q4k(qg):
     f = qg.lib().qg_quantize_q4k
     # (w, n, k, codes, meta, stream)
@@ -194,6 +229,7 @@ def test_validation_quantize_q4k(qg):
     assert f(A, 4, 256, A, U, None) == 3
 
 
+@needs_no_gpu
 def test_validation_qgemv_grouped(qg):
     l = qg.lib()
     W = qg.CWeight * 3
@@ -221,6 +257,7 @@ def test_validation_qgemv_grouped(qg):
     assert f(ws, 3, 1, U, 1, ys, 1, None, None) == 3
 
 
+@needs_no_gpu
 def test_validation_qgemm(qg):
     l = qg.lib()
     f = l.qg_qgemm_w8a8_outlier
@@ -276,6 +313,7 @@ def test_library_exact_mean_matches_oracle():
         assert r == oracle.mean_abs_f32(grp), (grp[:4], r, oracle.mean_abs_f32(grp))
 
 
+@needs_no_gpu
 def test_validation_qgemm_presplit(qg):
     f = qg.lib().qg_qgemm_w8a8
     # (xq, s_x, x_out, x_out_ld, m, k, n_out, wq, s_w, w_out, w_out_ld, n, y, acc_out, stream)
@@ -307,6 +345,7 @@ def test_header_constants_match_binding(qg):
         assert getattr(qg, name) == int(val), name
 
 
+@needs_no_gpu
 def test_validation_detect_outliers(qg):
     l = qg.lib()
     f = l.qg_detect_outliers
@@ -328,6 +367,7 @@ def test_validation_detect_outliers(qg):
     assert f(A, 4, 64, 0, None, None, 0, None) == 0       # nothing to find: no launch
 
 
+@needs_no_gpu
 def test_validation_sep_threshold(qg):
     l = qg.lib()
     import oracle.threshold as th
@@ -366,6 +406,7 @@ def test_validation_sep_threshold(qg):
     assert g(A, A, ld, A, A, 4, 1024, U, 1, 0, A, None, None) == 3
 
 
+@needs_no_gpu
 def test_validation_qgemv_batch(qg):
     l = qg.lib()
 
@@ -398,6 +439,7 @@ def test_validation_qgemv_batch(qg):
     assert g(arr2, 2, 4, A, 1, ys0, 0, None) == 1
 
 
+@needs_no_gpu
 def test_validation_mxfp4(qg):
     l = qg.lib()
     q = l.qg_quantize_mxfp4
