@@ -38,12 +38,14 @@
 //                    bits become +-1.0 bf16 pairs with one bit-field insert;
 //                    both go through v_dot2_f32_bf16 against bf16 x pairs.
 //   TERNARY3       : 16 B chunk = 80 weights, five per byte as the base-3
-//                    fraction ceil(256 v / 243); the bytes of a dword are
-//                    split into two 16-bit lanes (v_perm), and each x3 moves
-//                    the next digit of every byte into bits 8-9 of its lane:
-//                    one v_perm gathers the four digits, v_dot4 takes them
-//                    against x staged in the same (dword, digit) order;
-//                    sum_k (q+1) x - sum_k x as for TERNARY2.
+//                    fraction t = ceil(256 v / 243).  The four bytes of a
+//                    dword sit in four 16-bit lanes of a 64-bit value; one
+//                    64-bit shift-add multiplies every lane by 3, which moves
+//                    the next digit into bits 8-9 of the lane; one v_perm
+//                    gathers the four digits, v_dot4 takes them against x
+//                    staged in the same (dword, digit) order, and a mask
+//                    keeps the fraction; then sum_k (q+1) x - sum_k x as for
+//                    TERNARY2.
 //   SIGN1_RES8Z    : the same units; every residual pair also goes through
 //                    one more v_dot2 with the pair (-z, -z), so the sum is
 //                    sum_k (rq - z) x[k] as it accumulates (a z * sum_k x[k]
@@ -95,6 +97,7 @@ __device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
 __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
+
 
 template <int F>
 struct Fmt;
@@ -489,16 +492,19 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
                         const uint32_t w = fr[u][j].w[d];
-                        uint32_t a = __builtin_amdgcn_perm(0u, w, 0x0C020C00u);  // bytes 0, 2 in 16-bit lanes
-                        uint32_t b = __builtin_amdgcn_perm(0u, w, 0x0C030C01u);  // bytes 1, 3
+                        // the four bytes in four 16-bit lanes: bytes 0, 2 low, 1, 3 high
+                        uint64_t m = (uint64_t)__builtin_amdgcn_perm(0u, w, 0x0C020C00u) |
+                                     ((uint64_t)__builtin_amdgcn_perm(0u, w, 0x0C030C01u) << 32);
 #pragma unroll
                         for (int i = 0; i < 5; ++i) {
-                            a = a + (a << 1);  // x3: digit i of each byte now in bits 8-9 of its lane
-                            b = b + (b << 1);
-                            const uint32_t dg = __builtin_amdgcn_perm(b, a, 0x07030501u);  // digits of bytes 0..3
+                            // x3 in every lane (< 2^10: no carry between lanes) as one
+                            // 64-bit shift-add; the compiler's own form is two 32-bit
+                            // multiplies, measured slower on MI355X
+                            asm("v_lshl_add_u64 %0, %1, 1, %1" : "=v"(m) : "v"(m));
+                            // digit i of each byte is now bits 8-9 of its lane: gather bytes 1 and 3
+                            const uint32_t dg = __builtin_amdgcn_perm((uint32_t)(m >> 32), (uint32_t)m, 0x07030501u);
                             acc1[u] = sdot4(dg, xv[5 * d + i], acc1[u]);
-                            a &= 0x00FF00FFu;
-                            b &= 0x00FF00FFu;
+                            if (i < 4) m &= 0x00FF00FF00FF00FFull;  // keep the fraction
                         }
                     }
                 }
