@@ -301,8 +301,13 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     }
     Frag fa[U][JS], fb[U][JS];
     // unconditional, like the x loads: a wave without rows reads zeros (its
-    // offsets are out of range) and never consumes them
+    // offsets are out of range) and never consumes them.  Where x is staged
+    // (a prologue of block reductions and LDS writes), the second item goes
+    // out before it too: at the decode shapes a wave owns only one or two
+    // items, which then all stream while x is prepared.
+    constexpr bool kTwoAhead = !kXPerItem;
     issue(0, fa);
+    if constexpr (kTwoAhead) issue(1, fb);
 
     // piece -> fp32 values
     auto piece_vals = [&](const u32x4& r, float v[kElems]) {
@@ -605,20 +610,37 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
         }
     };
 
-    // steady state: item `it` is in flight in fa at the top of every trip
     int it = 0;
-    for (; it + 2 < nit; it += 2) {
-        issue(it + 1, fb);
-        consume(it, fa);
-        issue(it + 2, fa);
-        consume(it + 1, fb);
-    }
-    if (it + 2 == nit) {  // two items left
-        issue(it + 1, fb);
-        consume(it, fa);
-        consume(it + 1, fb);
-    } else if (it + 1 == nit) {  // one item left
-        consume(it, fa);
+    if constexpr (kTwoAhead) {
+        // items `it` (fa) and `it + 1` (fb) are in flight at the top of every
+        // trip; issues past nit read zeros and are never consumed
+        for (; it + 2 < nit; it += 2) {
+            consume(it, fa);
+            issue(it + 2, fa);
+            consume(it + 1, fb);
+            issue(it + 3, fb);
+        }
+        if (it + 2 == nit) {  // two items left
+            consume(it, fa);
+            consume(it + 1, fb);
+        } else if (it + 1 == nit) {  // one item left
+            consume(it, fa);
+        }
+    } else {
+        // steady state: item `it` is in flight in fa at the top of every trip
+        for (; it + 2 < nit; it += 2) {
+            issue(it + 1, fb);
+            consume(it, fa);
+            issue(it + 2, fa);
+            consume(it + 1, fb);
+        }
+        if (it + 2 == nit) {  // two items left
+            issue(it + 1, fb);
+            consume(it, fa);
+            consume(it + 1, fb);
+        } else if (it + 1 == nit) {  // one item left
+            consume(it, fa);
+        }
     }
 }
 
