@@ -67,18 +67,6 @@ __device__ __forceinline__ int qcode_zp(float x, float s, float z) {
 }
 
 // ------------------------------------------------------------------ reductions
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, kWave));
-    return v;
-}
 
 // DPP (data-parallel primitive) reductions: each step adds a lane permutation
 // of the value within rows of 16 lanes (quad swaps, half-row and row
@@ -100,6 +88,18 @@ __device__ __forceinline__ float wave_sum_to_lane63(float v) {
     return v;
 }
 
+// max of non-negative values over the wave, in lane 63 (the lanes that the
+// row_bcast steps leave out combine with 0, which cannot raise the max)
+__device__ __forceinline__ float wave_max_to_lane63(float v) {
+    v = __builtin_fmaxf(v, __int_as_float(dpp_mov<0xB1>(__float_as_int(v))));
+    v = __builtin_fmaxf(v, __int_as_float(dpp_mov<0x4E>(__float_as_int(v))));
+    v = __builtin_fmaxf(v, __int_as_float(dpp_mov<0x141>(__float_as_int(v))));
+    v = __builtin_fmaxf(v, __int_as_float(dpp_mov<0x140>(__float_as_int(v))));
+    v = __builtin_fmaxf(v, __int_as_float(dpp_mov<0x142, 0xA>(__float_as_int(v))));
+    v = __builtin_fmaxf(v, __int_as_float(dpp_mov<0x143, 0xC>(__float_as_int(v))));
+    return v;
+}
+
 __device__ __forceinline__ int wave_sum_to_lane63(int v) {
     v += dpp_mov<0xB1>(v);
     v += dpp_mov<0x4E>(v);
@@ -109,6 +109,14 @@ __device__ __forceinline__ int wave_sum_to_lane63(int v) {
     v += dpp_mov<0x143, 0xC>(v);
     return v;
 }
+
+// Whole-wave reductions broadcast to every lane: the DPP chain to lane 63,
+// then v_readlane (no LDS round trips).  All 64 lanes must be active.
+// wave_max takes non-negative values only (see wave_max_to_lane63).
+__device__ __forceinline__ float wave_max(float v) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_max_to_lane63(v)), 63));
+}
+__device__ __forceinline__ int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_sum_to_lane63(v), 63); }
 
 // Workgroup barrier for LDS traffic: waits for this wave's LDS (and scalar)
 // operations only.  A fenced __syncthreads would also wait for every global

@@ -301,11 +301,12 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     }
     Frag fa[U][JS], fb[U][JS];
     // unconditional, like the x loads: a wave without rows reads zeros (its
-    // offsets are out of range) and never consumes them.  Where x is staged
-    // (a prologue of block reductions and LDS writes), the second item goes
-    // out before it too: at the decode shapes a wave owns only one or two
-    // items, which then all stream while x is prepared.
-    constexpr bool kTwoAhead = !kXPerItem;
+    // offsets are out of range) and never consumes them.  For the ternary
+    // formats, whose x prologue is a quantization with a workgroup max, the
+    // second item goes out before it too: at the decode shapes a wave owns
+    // only one or two items, which then all stream while x is prepared
+    // (measured faster there, and slower for the other staged formats).
+    constexpr bool kTwoAhead = (F == F_TERN || F == F_TERN3);
     issue(0, fa);
     if constexpr (kTwoAhead) issue(1, fb);
 
@@ -357,7 +358,14 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
                 for (int e = 0; e < kElems; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
             },
             false);
-        sx = absmax_scale(block_max<kQWaves>(m, redf));
+        // max over the workgroup with a single barrier (redf is not reused);
+        // DPP within the wave, no LDS round trips
+        m = wave_max_to_lane63(m);
+        if (lane == 63) redf[wave] = m;
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < kQWaves; ++i) m = __builtin_fmaxf(m, redf[i]);
+        sx = absmax_scale(m);
         for_pieces([&](int pi, const float* v) {
 #pragma unroll
             for (int e = 0; e < kElems; ++e) {
@@ -379,7 +387,10 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
         } else {
             for (int i = K / 4 + tid; i < padded_cols / 4; i += kQThreads) reinterpret_cast<uint32_t*>(xs)[i] = 0u;
         }
-        if constexpr (F == F_TERN || F == F_TERN3) sum_xq = block_sum_int<kQWaves>(sum_xq, redi);
+        if constexpr (F == F_TERN || F == F_TERN3) {  // per-wave partials, summed after the staging barrier
+            sum_xq = wave_sum_to_lane63(sum_xq);
+            if (lane == 63) redi[wave] = sum_xq;
+        }
     } else {  // sign + residual: dword (unit u, pair q) = bf16 x[32u+q] | bf16 x[32u+q+16] << 16
         uint16_t* xh = reinterpret_cast<uint16_t*>(xs);
         for_pieces([&](int pi, const float* v) {
@@ -393,6 +404,11 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
         for (int i = K / 2 + tid; i < padded_cols / 2; i += kQThreads) reinterpret_cast<uint32_t*>(xs)[i] = 0u;
     }
     if constexpr (!kXPerItem) lds_barrier();  // x staged; the prefetched weights stay in flight
+    if constexpr (F == F_TERN || F == F_TERN3) {
+        sum_xq = 0;
+#pragma unroll
+        for (int i = 0; i < kQWaves; ++i) sum_xq += redi[i];
+    }
 
     float accf[U], accf2[U];
     int acc1[U], acc4[U], acc16[U];
