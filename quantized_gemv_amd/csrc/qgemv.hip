@@ -80,12 +80,9 @@ struct KParams {
 
 // A launch covers up to kMaxGroup weight matrices that share K and x (for
 // example the q, k and v projections of a layer).  Workgroups are handed out
-// per matrix in proportion to its rows; wg_start[m] is the first workgroup
-// of matrix m.
+// per matrix in proportion to its rows; matrix m is grid row blockIdx.y = m.
 constexpr int kMaxGroup = 8;
 struct KGroup {
-    int32_t count;
-    int32_t wg_start[kMaxGroup + 1];
     KParams mats[kMaxGroup];
 };
 
@@ -174,11 +171,14 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int mi = 0;
-    while (mi + 1 < grp.count && (int)blockIdx.x >= grp.wg_start[mi + 1]) ++mi;
+    // the matrix is blockIdx.y: its parameters come in the first round of
+    // kernel-argument reads, with no search over the group before them
+    // (measured 0.19 us per launch at the decode shapes)
+    const int mi = blockIdx.y;
     const KParams& p = grp.mats[mi];
     const int K = p.k;
-    const int row0 = ((int)blockIdx.x - grp.wg_start[mi]) * p.rows_per_wg;
+    const int row0 = (int)blockIdx.x * p.rows_per_wg;
+    if (row0 >= p.n) return;  // a smaller matrix of the group needs fewer workgroups
     const int rows = min(p.rows_per_wg, p.n - row0);
     const int C = (K + kCols - 1) / kCols;  // chunks per row (the last may be partly padding)
     const int J = (C + 63) / 64;       // chunk iterations per lane per row
@@ -689,8 +689,7 @@ static hipError_t run(const QgemvArgs* a, int count, hipStream_t st) {
     int64_t total_rows = 0;
     for (int m = 0; m < count; ++m) total_rows += a[m].n;
     KGroup g;
-    g.count = count;
-    int wg = 0;
+    int wgx = 1;  // grid: (workgroups of the largest matrix) x (matrices)
     for (int m = 0; m < count; ++m) {
         const int64_t N = a[m].n;
         int64_t share = (cus * N + total_rows / 2) / total_rows;  // workgroups for this matrix
@@ -710,10 +709,9 @@ static hipError_t run(const QgemvArgs* a, int count, hipStream_t st) {
         p.n = (int32_t)N;
         p.k = K;
         p.rows_per_wg = (int32_t)rpw;
-        g.wg_start[m] = wg;
-        wg += (int)((N + rpw - 1) / rpw);
+        const int nwg = (int)((N + rpw - 1) / rpw);
+        if (nwg > wgx) wgx = nwg;
     }
-    for (int m = count; m <= kMaxGroup; ++m) g.wg_start[m] = wg;
     auto kern = qgemv_kernel<F, XT, YT, U, JS, XREG>;
     if (lds > 64 * 1024) {
         static bool attr_set = false;  // per instantiation
@@ -724,7 +722,7 @@ static hipError_t run(const QgemvArgs* a, int count, hipStream_t st) {
             attr_set = true;
         }
     }
-    kern<<<wg, kQThreads, lds, st>>>(g);
+    kern<<<dim3(wgx, count), kQThreads, lds, st>>>(g);
     return hipGetLastError();
 }
 
