@@ -20,6 +20,16 @@
 // fragments of two MFMAs.  Four units per iteration, double-buffered.  The
 // eight partial 16x16 tiles are summed through LDS; lane l of wave 0 then
 // holds token l % 16, rows 4 (l / 16) + r, r < 4.
+//
+// A wave's K range is the same for every tile, so its activation fragments
+// are too.  When a workgroup walks several tiles and the fragments of all
+// eight waves fit in LDS (K <= 4608: 32 B per lane and unit), every wave
+// loads its fragments once, keeps them in its own LDS region and the items
+// then carry only weights: at 16 tokens the activations are twice the weight
+// bytes of a 16-row tile, and re-reading them from L2 for every tile was the
+// larger part of the time (measured: a grouped 3 x 4096 x 4096 launch at 16
+// tokens took 22.8 us, 13.5 us with no activation reads at all).  The sums
+// are the same operations in the same order either way.
 #include "qg_device.h"
 #include "qg_launch.h"
 
@@ -32,6 +42,11 @@ constexpr int kBThreads = 512;
 constexpr int kBWaves = kBThreads / kWave;
 constexpr int kBUnit = 64;  // k per unit: 4 lane groups x 16
 constexpr int kBJS = 4;     // units per iteration
+// LDS for the activation fragments of the eight waves (with the 8 KB of
+// partial tiles, within the 160 KB of a CU): K <= 4608
+constexpr size_t kBatchXlMaxLds = 144 * 1024;
+constexpr int kBXlUnits = 9;  // units per wave that fit: 8 waves x 9 x 2 KB = 144 KB
+static_assert((size_t)kBXlUnits * 8 * 2 * 64 * 16 == kBatchXlMaxLds, "LDS budget and unit count agree");
 
 struct BMat {
     const int8_t* wq;
@@ -64,9 +79,10 @@ __device__ __forceinline__ void widen16(const u32x4& w, bf16x8& a0, bf16x8& a1) 
     a1 = __builtin_bit_cast(bf16x8, u32x4{h[4], h[5], h[6], h[7]});
 }
 
-template <int YT>
+template <int YT, bool XL>
 __global__ __launch_bounds__(kBThreads) void qgemv_batch_kernel(BGroup grp) {
     __shared__ f32x4 part[kBWaves][kWave];
+    extern __shared__ u32x4 xsh[];  // XL: [wave][unit][xa | xb][lane]
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -101,9 +117,10 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_kernel(BGroup grp) {
         return t;
     };
     struct Frag {
-        u32x4 w[kBJS], xa[kBJS], xb[kBJS];
+        u32x4 w[kBJS], xa[XL ? 1 : kBJS], xb[XL ? 1 : kBJS];
         float sw[4];  // this lane's four row scales (used by wave 0)
     };
+    u32x4* const xw = xsh + (size_t)wave * most * 2 * kWave;  // XL: this wave's fragments
     auto issue = [&](int it, Frag& f) {
         const Tile t = tile_of(it);
         const int itn = it % nit;
@@ -122,19 +139,33 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_kernel(BGroup grp) {
             const bool ok = u < most && c < C && t.rows > 0;
             const int kk = c * kBUnit + 16 * g;
             f.w[j] = load16(rw, (ok && i < t.rows) ? (uint32_t)(i * K + kk) : oob_w);
-            const uint32_t xo = (uint32_t)((i * K + kk) * 2);
-            f.xa[j] = load16(rx, (ok && i < M) ? xo : oob_x);
-            f.xb[j] = load16(rx, (ok && i < M) ? xo + 16u : oob_x);
+            if constexpr (!XL) {
+                const uint32_t xo = (uint32_t)((i * K + kk) * 2);
+                f.xa[j] = load16(rx, (ok && i < M) ? xo : oob_x);
+                f.xb[j] = load16(rx, (ok && i < M) ? xo + 16u : oob_x);
+            }
         }
     };
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     auto consume = [&](int it, const Frag& f) {
+        const int itn = it % nit;
 #pragma unroll
         for (int j = 0; j < kBJS; ++j) {
             bf16x8 a0, a1;
             widen16(f.w[j], a0, a1);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8, f.xa[j]), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8, f.xb[j]), acc, 0, 0, 0);
+            u32x4 xa, xb;
+            if constexpr (XL) {
+                // units past the wave's range hold zeros in registers, never read LDS
+                const int u = kBJS * itn + j;
+                const bool in = u < most;
+                xa = in ? xw[(2 * u) * kWave + lane] : u32x4{0u, 0u, 0u, 0u};
+                xb = in ? xw[(2 * u + 1) * kWave + lane] : u32x4{0u, 0u, 0u, 0u};
+            } else {
+                xa = f.xa[j];
+                xb = f.xb[j];
+            }
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8, xa), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8, xb), acc, 0, 0, 0);
         }
         if (it % nit == nit - 1 && it < nitems) {
             // end of a tile: sum the eight waves' partial tiles (LDS-only
@@ -171,7 +202,35 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_kernel(BGroup grp) {
         }
     };
     Frag fa, fb;
-    issue(0, fa);
+    if constexpr (XL) {
+        // this wave's activation fragments, once.  All of them are requested
+        // (unconditionally: units past the range read zeros), then the first
+        // item's weights, and only then are they written to LDS, so the
+        // writes wait for the activations while the weights stay in flight.
+        // Each wave reads only what it wrote: no barrier, the LDS counter
+        // orders its own writes before its reads.
+        u32x4 v0[kBXlUnits], v1[kBXlUnits];
+#pragma unroll
+        for (int u = 0; u < kBXlUnits; ++u) {
+            const int c = wave * most + u;
+            const bool ok = u < most && c < C && i < M;
+            const uint32_t xo = (uint32_t)((i * K + c * kBUnit + 16 * g) * 2);
+            v0[u] = load16(rx, ok ? xo : oob_x);
+            v1[u] = load16(rx, ok ? xo + 16u : oob_x);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        issue(0, fa);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kBXlUnits; ++u) {
+            if (u < most) {
+                xw[(2 * u) * kWave + lane] = v0[u];
+                xw[(2 * u + 1) * kWave + lane] = v1[u];
+            }
+        }
+    } else {
+        issue(0, fa);
+    }
     // two buffers in turn (no register copy waits for a load in flight); the
     // last round may run one item past the wave's last, which reads zeros
     // and stores nothing.  The scheduling barriers keep each item's loads
@@ -204,12 +263,36 @@ hipError_t launch_qgemv_batch(const BatchArgs* a, int count, hipStream_t st) {
         tiles += (int)((a[j].n + 15) / 16);
     }
     for (int j = count; j <= kMaxGroupLaunch; ++j) g.wg_start[j] = tiles;
+    const int cus = device_cu_count();
+    const int C = (int)(a[0].k / kBUnit);
+    const int most = (C + kBWaves - 1) / kBWaves;
+    const size_t xl_bytes = (size_t)kBWaves * most * 2 * kWave * sizeof(u32x4);
+    if (tiles > cus && xl_bytes <= kBatchXlMaxLds) {
+        // activations kept in LDS: one workgroup per CU, each walking its
+        // tiles with the fragments loaded once
+        const int grid = cus;
+        auto k0 = qgemv_batch_kernel<0, true>;
+        auto k1 = qgemv_batch_kernel<1, true>;
+        static bool attr_set = false;
+        if (!attr_set) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k0),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBatchXlMaxLds);
+            if (e == hipSuccess)
+                e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        (int)kBatchXlMaxLds);
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+        if (a[0].yt == 0) k0<<<grid, kBThreads, xl_bytes, st>>>(g);
+        else k1<<<grid, kBThreads, xl_bytes, st>>>(g);
+        return hipGetLastError();
+    }
     // two resident workgroups per CU (the register budget); more tiles than
     // that are walked by the workgroups in turn
-    const int slots = 2 * device_cu_count();
+    const int slots = 2 * cus;
     const int grid = tiles < slots ? tiles : slots;
-    if (a[0].yt == 0) qgemv_batch_kernel<0><<<grid, kBThreads, 0, st>>>(g);
-    else qgemv_batch_kernel<1><<<grid, kBThreads, 0, st>>>(g);
+    if (a[0].yt == 0) qgemv_batch_kernel<0, false><<<grid, kBThreads, 0, st>>>(g);
+    else qgemv_batch_kernel<1, false><<<grid, kBThreads, 0, st>>>(g);
     return hipGetLastError();
 }
 

@@ -56,7 +56,10 @@ def _guarded2(m, n, dtype, guard=64):
 
 @pytest.mark.parametrize("n,k,m", [(16, 128, 1), (7, 256, 16), (40, 1152, 2), (300, 4096, 5), (4096, 4096, 16),
                                    (11008, 4096, 8), (4096, 11008, 3), (33, 32768, 16), (1000, 128, 9),
-                                   (2000, 2176, 4)])
+                                   (2000, 2176, 4),
+                                   # more 16-row tiles than CUs, K <= 4608: activations kept in LDS
+                                   # (ragged units per wave; the largest K that fits; the first that does not)
+                                   (5000, 2176, 16), (4200, 4608, 7), (4200, 4736, 16)])
 def test_qgemv_batch(qg, n, k, m):
     note("qgemv batch %dx%d m=%d" % (n, k, m))
     w, xb = _case(n, k, m, n + 3 * k + m)
@@ -110,3 +113,27 @@ def test_qgemv_batch_grouped_matches_single(qg):
     for W, y in zip(Ws, ys):
         y1 = qg.qgemv_batch(W, xd, y_dtype=torch.bfloat16)
         assert np.array_equal(host(y), host(y1))
+
+
+def test_qgemv_batch_grouped_qkv_16_tokens(qg):
+    # the grouped launch (768 tiles) keeps the activations in LDS; each
+    # single 4096-row launch (256 tiles) reads them per tile: bit-identical
+    note("qgemv batch grouped 3 x 4096x4096, m=16, vs single launches and the oracle")
+    k, m = 4096, 16
+    g = synth.rng(92)
+    xb = synth.to_bf16_bits(synth.gaussian(g, (m, k), 1.0))
+    xd = dev_bf16(xb)
+    Ws, refs = [], []
+    for j in range(3):
+        w = synth.gaussian(synth.rng(200 + j), (4096, k), 0.02)
+        W, _, _ = _weight(qg, w)
+        Ws.append(W)
+        refs.append(w)
+    ys = qg.qgemv_batch_grouped(Ws, xd, y_dtype=torch.float32)
+    rows = np.unique(np.concatenate([[0, 1, 4095], synth.rng(93).choice(4096, 61, replace=False)]))
+    for W, y, w in zip(Ws, ys, refs):
+        y1 = qg.qgemv_batch(W, xd, y_dtype=torch.float32)
+        assert np.array_equal(host(y), host(y1))
+        q_ref, s_ref = oracle.quantize_absmax(np.ascontiguousarray(w[rows]), per_row=True)
+        y_ref = oracle.y_w8a16_batch(q_ref, s_ref, xb)
+        assert oracle.normwise_error(host(y)[:, rows], y_ref) <= TOL_F32
