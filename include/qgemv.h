@@ -92,6 +92,9 @@ typedef int32_t qg_status;
 #define QG_BATCH_MAX_M  16      /* tokens of a qg_qgemv_batch launch                 */
 #define QG_BATCH_MAX_K  262144  /* k of qg_qgemv_batch                               */
 #define QG_MX_BLOCK     32      /* values per MXFP4 block (one E8M0 scale)           */
+#define QG_QGEMM_MAX_K  133120  /* k of the W8A8 prefill GEMM: the largest multiple
+                                   of 128 with k * 127^2 < 2^31, so that the int32
+                                   sums are exact for any codes                      */
 
 /* Human-readable text for a status code (static storage). */
 const char* qg_status_str(qg_status s);
@@ -509,7 +512,7 @@ qg_status qg_prefill_mxfp4(const void* x, int64_t m, int64_t k, const uint8_t* w
  * ws     : qg_qgemm_workspace_bytes(m, k, n_out) bytes, 16-B aligned: the
  *          call's scratch for (xq, s_x, x_out); its contents on entry do not
  *          matter and are overwritten.
- * k % 128 == 0, k <= 262144; 1 <= m, n < 2^31; m * k and n * k <= 2^40.
+ * k % 128 == 0, k <= QG_QGEMM_MAX_K; 1 <= m, n < 2^31; m * k and n * k <= 2^40.
  */
 size_t qg_qgemm_workspace_bytes(int64_t m, int64_t k, int32_t n_out);  /* 0 if out of range */
 qg_status qg_qgemm_w8a8_outlier(const void* x, int64_t m, int64_t k,

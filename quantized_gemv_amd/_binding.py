@@ -32,6 +32,7 @@ QG_SEP_MAX_K = 65536
 QG_BATCH_MAX_M = 16
 QG_BATCH_MAX_K = 262144
 QG_MX_BLOCK = 32
+QG_QGEMM_MAX_K = 133120
 
 _c_i32, _c_i64, _c_sz, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 

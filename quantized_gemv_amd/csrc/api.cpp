@@ -50,11 +50,12 @@ qg_status check_out_operand(const void* p, int32_t ld, int32_t n_out) {
     return QG_OK;
 }
 
-// Sizes the prefill GEMM supports: K in whole 128-column steps, indices of
-// the [m][k] / [n][k] operands within 2^40 elements, m and n below 2^31.
+// Sizes the prefill GEMM supports: K in whole 128-column steps and small
+// enough that the int32 sums are exact (K * 127^2 < 2^31), indices of the
+// [m][k] / [n][k] operands within 2^40 elements, m and n below 2^31.
 qg_status check_gemm_shape(int64_t m, int64_t k, int64_t n) {
     if (m < 1 || n < 1 || m >= ((int64_t)1 << 31) || n >= ((int64_t)1 << 31)) return QG_ERR_SHAPE;
-    if (k < 128 || k % 128 != 0 || k > 262144) return QG_ERR_SHAPE;
+    if (k < 128 || k % 128 != 0 || k > QG_QGEMM_MAX_K) return QG_ERR_SHAPE;
     if (m > ((int64_t)1 << 40) / k || n > ((int64_t)1 << 40) / k) return QG_ERR_SHAPE;
     return QG_OK;
 }
@@ -76,7 +77,7 @@ const char* qg_status_str(qg_status s) {
     }
 }
 
-int32_t qg_abi_version(void) { return 20500; }
+int32_t qg_abi_version(void) { return 20501; }
 
 size_t qg_quantize_absmax_workspace_bytes(int64_t rows, int64_t cols, int32_t gran) {
     if (gran != QG_PER_TENSOR || rows < 1 || cols < 8) return 0;
@@ -463,7 +464,7 @@ qg_status qg_prefill_mxfp4(const void* x, int64_t m, int64_t k, const uint8_t* w
 }
 
 size_t qg_qgemm_workspace_bytes(int64_t m, int64_t k, int32_t n_out) {
-    if (m < 1 || k < 1 || n_out < 0 || n_out > QG_MAX_OUTLIERS) return 0;
+    if (m < 1 || k < 1 || k > QG_QGEMM_MAX_K || n_out < 0 || n_out > QG_MAX_OUTLIERS) return 0;
     if (m > ((int64_t)1 << 40) / k) return 0;
     return qgemm_layout(m, k, n_out, nullptr, nullptr);
 }

@@ -49,7 +49,7 @@ def test_header_symbols_exported(qg):
     for name in decl:
         assert hasattr(l, name), name
     assert set(decl) == set(qg.EXPORTED)
-    assert qg.lib().qg_abi_version() == 20500
+    assert qg.lib().qg_abi_version() == 20501
     for st in range(0, 8):
         assert qg.status_str(st)
 
@@ -266,11 +266,17 @@ def test_validation_qgemm(qg):
     assert need >= 16 * 256 + 16 * 4 + 16 * 8 * 2  # xq, s_x, x_out [m][8]
     assert l.qg_qgemm_workspace_bytes(16, 256, 300) == 0
     assert l.qg_qgemm_workspace_bytes(0, 256, 2) == 0
+    # K past the int32-exact bound is refused
+    kmax = qg.QG_QGEMM_MAX_K
+    assert kmax % 128 == 0 and kmax * 127 * 127 < 2 ** 31 and (kmax + 128) * 127 * 127 >= 2 ** 31
+    assert l.qg_qgemm_workspace_bytes(16, kmax, 2) > 0 and l.qg_qgemm_workspace_bytes(16, kmax + 128, 2) == 0
     # (x, m, k, idx, n_out, wq, s_w, w_out, w_out_ld, n, y, acc_out, ws, ws_bytes, stream)
     assert f(A, 16, 256, idx, 2, A, A, A, 8, 32, A, None, A, need - 1, None) == 5
     assert f(A, 16, 256, idx, 2, A, A, None, 8, 32, A, None, A, need, None) == 1
     assert f(A, 16, 200, idx, 2, A, A, A, 8, 32, A, None, A, need, None) == 2
     assert f(A, 0, 256, idx, 2, A, A, A, 8, 32, A, None, A, need, None) == 2
+    assert f(A, 16, kmax + 128, idx, 2, A, A, A, 8, 32, A, None, A, 1 << 40, None) == 2
+    assert l.qg_qgemm_w8a8(A, A, A, 8, 16, kmax + 128, 2, A, A, A, 8, 32, A, None, None) == 2
     assert f(A, 16, 256, idx, 2, A, A, A, 2, 32, A, None, A, need, None) == 2    # w_out_ld not a multiple of 8
     assert f(A, 16, 256, idx, 2, A, A, A, 0, 32, A, None, A, need, None) == 2    # w_out_ld below n_out
     assert f(A, 16, 256, idx, 2, A, A, U, 8, 32, A, None, A, need, None) == 3    # w_out not 16-B aligned

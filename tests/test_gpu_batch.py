@@ -59,7 +59,9 @@ def _guarded2(m, n, dtype, guard=64):
                                    (2000, 2176, 4),
                                    # more 16-row tiles than CUs, K <= 4608: activations kept in LDS
                                    # (ragged units per wave; the largest K that fits; the first that does not)
-                                   (5000, 2176, 16), (4200, 4608, 7), (4200, 4736, 16)])
+                                   (5000, 2176, 16), (4200, 4608, 7), (4200, 4736, 16),
+                                   # the largest K
+                                   (16, 262144, 4)])
 def test_qgemv_batch(qg, n, k, m):
     note("qgemv batch %dx%d m=%d" % (n, k, m))
     w, xb = _case(n, k, m, n + 3 * k + m)

@@ -43,7 +43,7 @@ def _special_rows(x):
 
 
 @pytest.mark.parametrize("rows,cols,bf16", [(1, 256, False), (7, 1024, False), (7, 1024, True), (256, 4096, True),
-                                            (301, 768, False)])
+                                            (301, 768, False), (3, 262144, True)])
 def test_quantize_mxfp4(qg, rows, cols, bf16):
     note("mxfp4 quantize %dx%d bf16=%s" % (rows, cols, bf16))
     g = synth.rng(rows + cols)
@@ -77,7 +77,7 @@ def _guarded2(m, n, guard=64):
 
 
 @pytest.mark.parametrize("m,k,n", [(1, 256, 1), (33, 512, 65), (256, 1024, 128), (300, 768, 200),
-                                   (257, 2304, 129), (512, 4096, 512)])
+                                   (257, 2304, 129), (512, 4096, 512), (3, 262144, 5)])
 def test_gemm_mxfp4(qg, m, k, n):
     note("mxfp4 gemm %dx%dx%d" % (m, k, n))
     ca, ea, cb, eb = _operands(m, k, n, m * 7 + k + n)

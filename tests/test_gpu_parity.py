@@ -434,6 +434,30 @@ def test_qgemm_small(qg, m, k, n, n_out):
     _qgemm_case(qg, m, k, n, n_out)
 
 
+def test_qgemm_max_k(qg):
+    # the largest K the GEMM accepts, with ragged m and n tiles
+    note("qgemm m=33 k=133120 n=65 n_out=3")
+    _qgemm_case(qg, 33, qg.QG_QGEMM_MAX_K, 65, 3)
+
+
+def test_qgemm_int32_bound(qg):
+    # every product 127 * (+-127) over the largest K: sums of +-2,147,092,480,
+    # just inside int32, exact
+    note("qgemm extreme codes at k=133120")
+    m, k, n = 17, qg.QG_QGEMM_MAX_K, 33
+    xq = torch.full((m, k), 127, dtype=torch.int8, device="cuda")
+    wq = torch.full((n, k), 127, dtype=torch.int8, device="cuda")
+    wq[1::2] = -127
+    ones_m = torch.ones(m, dtype=torch.float32, device="cuda")
+    ones_n = torch.ones(n, dtype=torch.float32, device="cuda")
+    acc = torch.empty((m, n), dtype=torch.int32, device="cuda")
+    y = qg.qgemm_w8a8(xq, ones_m, None, wq, ones_n, None, 0, acc_out=acc)
+    expect = np.where(np.arange(n) % 2 == 0, 1, -1)[None, :] * np.full((m, n), k * 127 * 127, np.int64)
+    assert int(np.abs(expect).max()) < 2 ** 31
+    assert np.array_equal(host(acc).astype(np.int64), expect)
+    assert np.array_equal(host(y).astype(np.float64), expect.astype(np.float64))
+
+
 def test_qgemm_full(qg):
     note("qgemm 2048x4096x4096 n_out=20")
     _qgemm_case(qg, 2048, 4096, 4096, 20)
