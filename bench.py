@@ -46,7 +46,7 @@ CSRC = os.path.join(ROOT, "quantized_gemv_amd", "csrc")
 # sources whose hash keys the recorded counters of each kernel
 KERNEL_SOURCES = {
     "qgemv": ("qgemv.hip", "qg_device.h", "qg_launch.h"),
-    "qgemm": ("qgemm.hip", "qg_device.h", "qg_launch.h"),
+    "qgemm": ("qgemm.hip", "qg_gemm.h", "qg_device.h", "qg_launch.h"),
     "sepq": ("sepq.hip", "qg_device.h", "qg_launch.h"),
 }
 KERNEL_NAME_KEYS = {"qgemv": "qg::qgemv_kernel", "qgemm": "qgemm_w8a8_kernel", "sepq": "sep_qgemv_kernel"}

@@ -15,12 +15,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Physical 16-byte chunk of logical chunk c in tile row r, for CPR chunks per
-// row: the eight rows read together by a fragment load land in eight
-// different 16-byte bank groups.
+// row.  The gfx950 LDS has 64 banks of 4 bytes and serves a 128-bit read 16
+// lanes at a time; a fragment load's 16 lanes read 16 consecutive rows at the
+// same logical chunk.  A row of CPR * 16 bytes covers 4 * CPR banks, so rows
+// r and r + 64 / (4 * CPR) start on the same bank: XOR-ing the chunk with
+// r / (64 / (4 * CPR)) gives the 16 rows 16 different 4-bank groups (measured
+// on the prefill GEMM: no bank-conflict cycles, against 4 per read with the
+// 8-row pattern of a 32-bank LDS).
 template <int CPR>
 __device__ __forceinline__ int swz(int r, int c) {
-    if constexpr (CPR == 4) return c ^ ((r >> 1) & 3);
-    else return c ^ (r & 7);
+    if constexpr (CPR == 4) return c ^ ((r >> 2) & 3);
+    else return c ^ ((r >> 1) & 7);
 }
 
 // One 16-byte-per-lane direct global->LDS load; lane i's bytes land at
