@@ -185,6 +185,11 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     const int nseg = (J + JS - 1) / JS;
     // x is staged (zero-padded) for every chunk iteration a segment can touch
     const int padded_cols = nseg * JS * 64 * kCols;
+    // ternary 2-bit and sign + residual: a chunk's x is four 16-byte pieces,
+    // stored as four planes [piece][chunk], so that the 16 lanes of an LDS
+    // read phase take 16 consecutive 16-byte slots (one piece per lane at a
+    // 64-byte stride would put lanes l and l + 4 on the same banks)
+    const int NC = nseg * JS * 64;  // chunks in the staged copy
 
     // ------------------------------------------------------------ stream
     const int rowB = (F == F_TERN) ? K / 4 : kSignRes<F> ? K / 8 : (F == F_Q4) ? K / 2 : (F == F_TERN3) ? 16 * C : K;  // code bytes per row
@@ -376,14 +381,18 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
                     xs[c] = (uint8_t)(q & 0xFF);
                 } else if constexpr (F == F_TERN3) {
                     xs[tern3_slot(c)] = (uint8_t)(q & 0xFF);
-                } else {  // column 16g + 4b + f is stored at 16g + 4f + b (byte-plane order)
+                } else {  // column 64 ch + 16 d + 4 b + f: plane d, chunk ch, byte 4 f + b (byte-plane order)
                     const int l = c & 15;
-                    xs[(c - l) + 4 * (l & 3) + (l >> 2)] = (uint8_t)(q & 0xFF);
+                    xs[(((c >> 4) & 3) * NC + (c >> 6)) * 16 + 4 * (l & 3) + (l >> 2)] = (uint8_t)(q & 0xFF);
                 }
             }
         });
         if constexpr (F == F_TERN3) {  // padding columns sit inside the last chunk's permutation
             for (int c = K + tid; c < padded_cols; c += kQThreads) xs[tern3_slot(c)] = 0;
+        } else if constexpr (F == F_TERN) {  // whole padding chunks (K % 64 == 0), in all four planes
+            const int c0 = K / 64, npad = NC - c0;
+            for (int i = tid; i < 4 * npad; i += kQThreads)
+                reinterpret_cast<u32x4*>(xs)[(i / npad) * NC + c0 + i % npad] = u32x4{0u, 0u, 0u, 0u};
         } else {
             for (int i = K / 4 + tid; i < padded_cols / 4; i += kQThreads) reinterpret_cast<uint32_t*>(xs)[i] = 0u;
         }
@@ -391,17 +400,20 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
             sum_xq = wave_sum_to_lane63(sum_xq);
             if (lane == 63) redi[wave] = sum_xq;
         }
-    } else {  // sign + residual: dword (unit u, pair q) = bf16 x[32u+q] | bf16 x[32u+q+16] << 16
+    } else {  // sign + residual: pair p = q & 15 of unit u is bf16 x[32u+q] | bf16 x[32u+q+16] << 16,
+              // in plane p / 4, slot u, dword p % 4
         uint16_t* xh = reinterpret_cast<uint16_t*>(xs);
         for_pieces([&](int pi, const float* v) {
 #pragma unroll
             for (int e = 0; e < kElems; ++e) {
                 const int c = pi * kElems + e;
-                const int u = c >> 5, q = c & 31;
-                xh[2 * (16 * u + (q & 15)) + (q >> 4)] = (uint16_t)(__float_as_uint(v[e]) >> 16);
+                const int u = c >> 5, q = c & 31, pr = q & 15;
+                xh[2 * (4 * ((pr >> 2) * NC + u) + (pr & 3)) + (q >> 4)] = (uint16_t)(__float_as_uint(v[e]) >> 16);
             }
         });
-        for (int i = K / 2 + tid; i < padded_cols / 2; i += kQThreads) reinterpret_cast<uint32_t*>(xs)[i] = 0u;
+        const int c0 = K / 32, npad = NC - c0;  // whole padding units (K % 32 == 0), in all four planes
+        for (int i = tid; i < 4 * npad; i += kQThreads)
+            reinterpret_cast<u32x4*>(xs)[(i / npad) * NC + c0 + i % npad] = u32x4{0u, 0u, 0u, 0u};
     }
     if constexpr (!kXPerItem) lds_barrier();  // x staged; the prefetched weights stay in flight
     if constexpr (F == F_TERN || F == F_TERN3) {
@@ -530,10 +542,10 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
                     }
                 }
             } else if constexpr (F == F_TERN) {
-                const u32x4* xp = reinterpret_cast<const u32x4*>(xs) + 4 * c;
+                const u32x4* xp = reinterpret_cast<const u32x4*>(xs) + c;
                 u32x4 xq[4];
 #pragma unroll
-                for (int d = 0; d < 4; ++d) xq[d] = xp[d];
+                for (int d = 0; d < 4; ++d) xq[d] = xp[d * NC];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -546,11 +558,11 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
                     }
                 }
             } else {  // F_SR
-                const u32x4* xp = reinterpret_cast<const u32x4*>(xs) + 4 * c;
+                const u32x4* xp = reinterpret_cast<const u32x4*>(xs) + c;
                 uint32_t xv[16];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const u32x4 t = xp[q];
+                    const u32x4 t = xp[q * NC];
                     xv[4 * q] = t[0]; xv[4 * q + 1] = t[1]; xv[4 * q + 2] = t[2]; xv[4 * q + 3] = t[3];
                 }
 #pragma unroll
