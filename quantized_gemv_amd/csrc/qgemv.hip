@@ -225,9 +225,9 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
                 const bool ok = live && (r < rows) && (c < C);
                 if constexpr (kSignRes<F>) {
                     const uint32_t orr = ok ? (uint32_t)(r * K + 32 * c) : oob_r;
-                    fr[u][j].r0 = load16(rr, orr);
+                    fr[u][j].r0 = load16(rr, orr);  // r0 / r1 split each line: normal loads
                     fr[u][j].r1 = load16(rr, ok ? orr + 16 : oob_r);
-                    fr[u][j].s = load4(rc, ok ? (uint32_t)(r * rowB + 4 * c) : oob_c);
+                    fr[u][j].s = load4_nt(rc, ok ? (uint32_t)(r * rowB + 4 * c) : oob_c);
                     if constexpr (F == F_SRZ) {
                         if (j == 0) fr[u][0].z = load1(rz, r < rows ? (uint32_t)r : (uint32_t)rows);
                     }
@@ -239,8 +239,8 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
 #pragma unroll
                         for (int h = 0; h < 4; ++h) fr[0][j].x[h] = load16(rx, xo + 16 * h);
                     }
-                    fr[u][j].meta = load16(rr, ok ? (uint32_t)(r * (K / 16) + 16 * (c >> 3)) : oob_r);
-                    fr[u][j].w = load16(rc, ok ? (uint32_t)(r * rowB + 16 * c) : oob_c);
+                    fr[u][j].meta = load16_nt(rr, ok ? (uint32_t)(r * (K / 16) + 16 * (c >> 3)) : oob_r);
+                    fr[u][j].w = load16_nt(rc, ok ? (uint32_t)(r * rowB + 16 * c) : oob_c);
                 } else {
                     if constexpr (F == F_INT8F) {
                         // the 16 activations of this chunk, requested just ahead of the
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
                             for (int h = 0; h < kXB / 16; ++h) fr[0][j].x[h] = load16(rx, xo + 16 * h);
                         }
                     }
-                    fr[u][j].w = load16(rc, ok ? (uint32_t)(r * rowB + 16 * c) : oob_c);
+                    fr[u][j].w = load16_nt(rc, ok ? (uint32_t)(r * rowB + 16 * c) : oob_c);
                 }
             }
         }

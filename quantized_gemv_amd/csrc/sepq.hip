@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kSepThreads) void sep_qgemv_kernel(SepParams p) {
         for (int u = 0; u < U; ++u) {
             const int r = g * U + u;
             const bool ok = live && r < rows && s * kSepStep + 64 * lane < K;
-            c.D[u] = load16(rc, ok ? (uint32_t)(r * rowC + s * (kSepStep / 4) + 16 * lane) : oob_c);
+            c.D[u] = load16_nt(rc, ok ? (uint32_t)(r * rowC + s * (kSepStep / 4) + 16 * lane) : oob_c);
         }
     };
     // residual flags, their per-lane exclusive prefix and the step's total;
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kSepThreads) void sep_qgemv_kernel(SepParams p) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t o = 16u * (64u * j + lane);
-                V[u][j] = load16(rr, (okr && o < end) ? a0 + o : oob_r);
+                V[u][j] = load16(rr, (okr && o < end) ? a0 + o : oob_r);  // slices start anywhere in a line: normal loads
             }
             const uint32_t o4 = (uint32_t)kSepStep + 4u * lane;
             X4[u] = load4(rr, (okr && lane < 4 && o4 < end) ? a0 + o4 : oob_r);
