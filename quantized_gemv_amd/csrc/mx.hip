@@ -33,54 +33,110 @@
 namespace qg {
 
 // ------------------------------------------------------------------ quantizer
-// One thread per 8 consecutive values; the 4 threads of a 32-block are
-// consecutive lanes (shuffles give the block max).
+// One thread per 8 consecutive values, kMxQU such groups kThreads apart with
+// all loads issued first (clamped into range, so none waits behind a branch);
+// the 4 threads of a 32-block are consecutive lanes of one quad (DPP quad
+// permutes give the block max).
+//
+// The rounding is gfx950's scaled conversion (v_cvt_scalef32_pk_fp4_*): it
+// divides each input by the E8M0 scale given in a float's exponent field and
+// rounds to the nearest E2M1 value, ties to even, saturating at 6 -- the
+// element rule above, two values per instruction.  One difference is removed
+// before it: the instruction keeps the sign of -0, whose code here is +0, so
+// negative zeros are cleared first (a negative value that rounds to zero
+// keeps its sign bit, as the element rule says).
+constexpr int kMxQU = 2;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// the bf16 pair in w with a -0 half turned into +0
+__device__ __forceinline__ uint32_t bf16x2_clear_neg_zero(uint32_t w) {
+    const uint32_t mag = w & 0x7FFF7FFFu;
+    const uint32_t nonzero = (mag + 0x7FFF7FFFu) & 0x80008000u;  // bit 15 / 31 set where a half is nonzero
+    return mag | (w & nonzero);
+}
+
 template <int XT>
 __global__ __launch_bounds__(kThreads) void mxfp4_quantize_kernel(const void* x, int64_t rows, int64_t cols,
-                                                                  uint8_t* codes, uint8_t* scales) {
+                                                                 uint8_t* codes, uint8_t* scales) {
     const int64_t n8 = rows * cols / 8;
     const int64_t nb = cols / 32;  // blocks per row
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < n8; g += stride) {
-        float v[8];
-        if constexpr (XT == 1) {
-            const uint4 h = reinterpret_cast<const uint4*>(x)[g];
-            const uint32_t w[4] = {h.x, h.y, h.z, h.w};
+    const bool idx32 = rows * nb <= (int64_t)0xFFFFFFFF;  // block index fits 32 bits: cheaper division
+    const int64_t stride = (int64_t)gridDim.x * kThreads * kMxQU;
+    for (int64_t g0 = (int64_t)blockIdx.x * kThreads * kMxQU + threadIdx.x; g0 < n8; g0 += stride) {
+        uint32_t w[kMxQU][8];  // bf16: 4 pairs; fp32: 8 values (bits)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[2 * e] = bf16_to_f32(w[e] & 0xFFFFu);
-                v[2 * e + 1] = bf16_to_f32(w[e] >> 16);
+        for (int u = 0; u < kMxQU; ++u) {
+            const int64_t g = min(g0 + (int64_t)u * kThreads, n8 - 1);
+            if constexpr (XT == 1) {
+                const uint4 h = reinterpret_cast<const uint4*>(x)[g];
+                w[u][0] = h.x; w[u][1] = h.y; w[u][2] = h.z; w[u][3] = h.w;
+            } else {
+                const uint4 a = reinterpret_cast<const uint4*>(x)[2 * g];
+                const uint4 b = reinterpret_cast<const uint4*>(x)[2 * g + 1];
+                w[u][0] = a.x; w[u][1] = a.y; w[u][2] = a.z; w[u][3] = a.w;
+                w[u][4] = b.x; w[u][5] = b.y; w[u][6] = b.z; w[u][7] = b.w;
             }
-        } else {
-            const float4 a = reinterpret_cast<const float4*>(x)[2 * g];
-            const float4 b = reinterpret_cast<const float4*>(x)[2 * g + 1];
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
         }
-        float m = 0.0f;
+        __builtin_amdgcn_sched_barrier(0);  // keep every load issued before the first use
 #pragma unroll
-        for (int j = 0; j < 8; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
-        m = __builtin_fmaxf(m, __shfl_xor(m, 1, kWave));
-        m = __builtin_fmaxf(m, __shfl_xor(m, 2, kWave));
-        // floor(log2 m) is the unbiased exponent of m (exact); subnormal m
-        // and the lowest binade clamp to -127
-        const int E = (int)(__float_as_uint(m) >> 23);
-        const int e = (m == 0.0f) ? 0 : max(E - 129, -127);
-        const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e (127 - e in [2, 254])
-        uint32_t packed = 0;
+        for (int u = 0; u < kMxQU; ++u) {
+            // block max |v| (as bits: magnitudes of finite values order as integers)
+            uint32_t mb;
+            if constexpr (XT == 1) {
+                u16x2_t m2 = __builtin_bit_cast(u16x2_t, w[u][0] & 0x7FFF7FFFu);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float a = __builtin_fabsf(v[j]) * inv;  // exact
-            // nearest E2M1 value: count the midpoints below, ties to the even code
-            const uint32_t mag = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                                 (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                                 (uint32_t)(a > 5.0f);
-            packed |= (mag | (v[j] < 0.0f ? 8u : 0u)) << (4 * j);
-        }
-        reinterpret_cast<uint32_t*>(codes)[g] = packed;
-        if ((g & 3) == 0) {
-            const int64_t r = (g >> 2) / nb, b = (g >> 2) - r * nb;  // row, block
-            scales[((b >> 3) * rows + r) * 8 + (b & 7)] = (uint8_t)(e + 127);
+                for (int j = 1; j < 4; ++j)
+                    m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, w[u][j] & 0x7FFF7FFFu));
+                mb = (uint32_t)max(m2.x, m2.y) << 16;
+            } else {
+                mb = w[u][0] & 0x7FFFFFFFu;
+#pragma unroll
+                for (int j = 1; j < 8; ++j) mb = max(mb, w[u][j] & 0x7FFFFFFFu);
+            }
+            mb = max(mb, (uint32_t)dpp_mov<0xB1>((int)mb));  // quad_perm [1,0,3,2]
+            mb = max(mb, (uint32_t)dpp_mov<0x4E>((int)mb));  // quad_perm [2,3,0,1]
+            // floor(log2 m) is the unbiased exponent of m (exact); subnormal m
+            // and the lowest binade clamp to -127
+            const int E = (int)(mb >> 23);
+            const int e = (mb == 0u) ? 0 : max(E - 129, -127);
+            const float sc = __uint_as_float((uint32_t)(e + 127) << 23);  // E8M0 scale in the exponent field
+            uint32_t packed = 0;
+            if constexpr (XT == 1) {
+                packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+                    packed, __builtin_bit_cast(bf16x2_t, bf16x2_clear_neg_zero(w[u][0])), sc, 0);
+                packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+                    packed, __builtin_bit_cast(bf16x2_t, bf16x2_clear_neg_zero(w[u][1])), sc, 1);
+                packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+                    packed, __builtin_bit_cast(bf16x2_t, bf16x2_clear_neg_zero(w[u][2])), sc, 2);
+                packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(
+                    packed, __builtin_bit_cast(bf16x2_t, bf16x2_clear_neg_zero(w[u][3])), sc, 3);
+            } else {
+                float v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = __uint_as_float(w[u][j]) + 0.0f;  // -0 + 0 = +0
+                packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[0], v[1], sc, 0);
+                packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[2], v[3], sc, 1);
+                packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[4], v[5], sc, 2);
+                packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, v[6], v[7], sc, 3);
+            }
+            const int64_t g = g0 + (int64_t)u * kThreads;
+            if (g < n8) {
+                reinterpret_cast<uint32_t*>(codes)[g] = packed;
+                if ((g & 3) == 0) {
+                    int64_t r, b;  // row, block
+                    if (idx32) {
+                        const uint32_t gb = (uint32_t)(g >> 2), r32 = gb / (uint32_t)nb;
+                        r = r32;
+                        b = gb - r32 * (uint32_t)nb;
+                    } else {
+                        r = (g >> 2) / nb;
+                        b = (g >> 2) - r * nb;
+                    }
+                    scales[((b >> 3) * rows + r) * 8 + (b & 7)] = (uint8_t)(e + 127);
+                }
+            }
         }
     }
 }
@@ -88,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void mxfp4_quantize_kernel(const void* x,
 hipError_t launch_quantize_mxfp4(const void* x, int xt, int64_t rows, int64_t cols, uint8_t* codes,
                                  uint8_t* scales, hipStream_t st) {
     const int64_t n8 = rows * cols / 8;
-    const int64_t want = (n8 + kThreads - 1) / kThreads;
+    const int64_t want = (n8 + (int64_t)kThreads * kMxQU - 1) / ((int64_t)kThreads * kMxQU);
     const int grid = (int)(want < 16384 ? want : 16384);
     if (xt == 1) mxfp4_quantize_kernel<1><<<grid, kThreads, 0, st>>>(x, rows, cols, codes, scales);
     else mxfp4_quantize_kernel<0><<<grid, kThreads, 0, st>>>(x, rows, cols, codes, scales);
