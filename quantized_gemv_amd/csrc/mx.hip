@@ -277,11 +277,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mxfp4_kernel(MxPa
 #pragma unroll
         for (int b = 0; b < WTN; ++b)
             scB[b] = *reinterpret_cast<const uint2*>(sc + 8 * (BM + wn * (WTN * 32) + b * 32 + (lane & 31)));
-#pragma unroll
-        for (int kk = 0; kk < BK / 32; ++kk) {
+        auto frags = [&](int kk, i32x4 (&fa)[WTM], i32x4 (&fb)[WTN], int (&xa)[WTM], int (&xb)[WTN]) {
             const int c = kk * 2 + (lane >> 5);  // 16-byte chunk = one 32-element block
-            i32x4 fa[WTM], fb[WTN];
-            int xa[WTM], xb[WTN];
 #pragma unroll
             for (int a = 0; a < WTM; ++a) {
                 const int r = wm * (WTM * 32) + a * 32 + (lane & 31);
@@ -294,15 +291,25 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_mxfp4_kernel(MxPa
                 fb[b] = *reinterpret_cast<const i32x4*>(sb + r * BK + 16 * swz<CPR>(r, c));
                 xb[b] = (int)((kk < 2 ? scB[b].x : scB[b].y) >> (16 * (kk & 1) + hs));
             }
+        };
+        // two register sets: the reads of step kk + 1 go out before the MFMAs of step kk
+        i32x4 fa[2][WTM], fb[2][WTN];
+        int xa[2][WTM], xb[2][WTN];
+        frags(0, fa[0], fb[0], xa[0], xb[0]);
+#pragma unroll
+        for (int kk = 0; kk < BK / 32; ++kk) {
+            if (kk + 1 < BK / 32) frags(kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1], xa[(kk + 1) & 1], xb[(kk + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int a = 0; a < WTM; ++a)
 #pragma unroll
                 for (int b = 0; b < WTN; ++b) {
-                    const i32x8 A = {fa[a][0], fa[a][1], fa[a][2], fa[a][3], 0, 0, 0, 0};
-                    const i32x8 B = {fb[b][0], fb[b][1], fb[b][2], fb[b][3], 0, 0, 0, 0};
+                    const i32x4 fA = fa[kk & 1][a], fB = fb[kk & 1][b];
+                    const i32x8 A = {fA[0], fA[1], fA[2], fA[3], 0, 0, 0, 0};
+                    const i32x8 B = {fB[0], fB[1], fB[2], fB[3], 0, 0, 0, 0};
                     // cbsz = blgp = 4: both operands E2M1; scale byte 0 of xa / xb
-                    acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[a][b], 4, 4, 0, xa[a], 0,
-                                                                                xb[b]);
+                    acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc[a][b], 4, 4, 0, xa[kk & 1][a],
+                                                                                0, xb[kk & 1][b]);
                 }
         }
     }

@@ -129,10 +129,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void qgemm_w8a8_kernel(Gemm
 
         const uint8_t* sa = smem + (ks % STAGES) * kStageBytes;
         const uint8_t* sb = sa + kStageA;
-#pragma unroll
-        for (int kk = 0; kk < BK / 32; ++kk) {
+        auto frags = [&](int kk, i32x4 (&fa)[WTM], i32x4 (&fb)[WTN]) {
             const int c = kk * 2 + (lane >> 5);
-            i32x4 fa[WTM], fb[WTN];
 #pragma unroll
             for (int a = 0; a < WTM; ++a) {
                 const int r = wm * (WTM * 32) + a * 32 + (lane & 31);
@@ -143,11 +141,21 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void qgemm_w8a8_kernel(Gemm
                 const int r = wn * (WTN * 32) + b * 32 + (lane & 31);
                 fb[b] = *reinterpret_cast<const i32x4*>(sb + r * BK + 16 * swz<CPR>(r, c));
             }
+        };
+        // fragments in two register sets: the LDS reads of step kk + 1 are
+        // issued before the MFMAs of step kk (kept there by the scheduling
+        // barrier), so their latency runs under those MFMAs
+        i32x4 fa[2][WTM], fb[2][WTN];
+        frags(0, fa[0], fb[0]);
+#pragma unroll
+        for (int kk = 0; kk < BK / 32; ++kk) {
+            if (kk + 1 < BK / 32) frags(kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int a = 0; a < WTM; ++a)
 #pragma unroll
                 for (int b = 0; b < WTN; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[a], fb[b], acc[a][b], 0, 0, 0);
+                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[kk & 1][a], fb[kk & 1][b], acc[a][b], 0, 0, 0);
         }
     }
 
