@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     static_assert(F != F_Q4 || XT == 1, "4-bit groups take bf16 activations");
     static_assert(!XREG || F == F_Q4, "register-resident x is for the 4-bit groups");
     // XREG: this lane's x (fp32) and the sums of its groups, for every row
-    float xq4[XREG ? JS : 1][XREG ? 32 : 1];
+    uint32_t xq4[XREG ? JS : 1][XREG ? 16 : 1];  // bf16 pairs
     float xsq4[XREG ? JS : 1];
     if constexpr (XREG) {
         const uint32_t xend = (uint32_t)(K * 2);
@@ -285,10 +285,9 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
                 const uint32_t d = h[t >> 2][t & 3];
-                xq4[j][2 * t] = bf16_to_f32(d & 0xFFFFu);
-                xq4[j][2 * t + 1] = __uint_as_float(d & 0xFFFF0000u);
-                xs[(2 * t) & 3] += xq4[j][2 * t];
-                xs[(2 * t + 1) & 3] += xq4[j][2 * t + 1];
+                xq4[j][t] = d;
+                xs[(2 * t) & 3] += bf16_to_f32(d & 0xFFFFu);
+                xs[(2 * t + 1) & 3] += __uint_as_float(d & 0xFFFF0000u);
             }
             xsq4[j] = (xs[0] + xs[1]) + (xs[2] + xs[3]);
         }
@@ -460,22 +459,21 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
                     }
                 }
             } else if constexpr (F == F_Q4) {
-                float xv[32];
+                // x as bf16 pairs (element 2t low, 2t + 1 high) and the group's sum
+                uint32_t xp[16];
                 float xsum;
                 if constexpr (XREG) {
 #pragma unroll
-                    for (int t = 0; t < 32; ++t) xv[t] = xq4[j][t];
+                    for (int t = 0; t < 16; ++t) xp[t] = xq4[j][t];
                     xsum = xsq4[j];
                 } else {
-#pragma unroll
-                    for (int q = 0; q < 16; ++q) {
-                        const uint32_t d = fr[0][j].x[q >> 2][q & 3];
-                        xv[2 * q] = bf16_to_f32(d & 0xFFFFu);
-                        xv[2 * q + 1] = __uint_as_float(d & 0xFFFF0000u);
-                    }
                     float xs[4] = {0.f, 0.f, 0.f, 0.f};  // sum of the group's x, four chains
 #pragma unroll
-                    for (int t = 0; t < 32; ++t) xs[t & 3] += xv[t];
+                    for (int t = 0; t < 16; ++t) {
+                        xp[t] = fr[0][j].x[t >> 2][t & 3];
+                        xs[(2 * t) & 3] += bf16_to_f32(xp[t] & 0xFFFFu);
+                        xs[(2 * t + 1) & 3] += __uint_as_float(xp[t] & 0xFFFF0000u);
+                    }
                     xsum = (xs[0] + xs[1]) + (xs[2] + xs[3]);
                 }
                 const int grp = c & 7;  // group inside its super-block (= lane & 7)
@@ -490,18 +488,23 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
                     const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(m[3] & 0xFFFFu));
                     const float dm = (float)__builtin_bit_cast(_Float16, (uint16_t)(m[3] >> 16));
                     const float S = d * sc, M = dm * mq;
-                    float a0 = 0.f, a1 = 0.f;  // sum_k q x, two chains
+                    // code q as the bf16 value 128 + q (exact): a byte's two codes
+                    // become one bf16 pair for v_dot2 against the matching x pair,
+                    // and the 128 * sum(x) that this adds is taken off below
+                    float a0 = 0.f, a1 = 0.f;  // sum_k (128 + q) x, two chains
 #pragma unroll
                     for (int dw = 0; dw < 4; ++dw) {
                         const uint32_t wd = fr[u][j].w[dw];
                         const uint32_t lo = wd & 0x0F0F0F0Fu, hi = (wd >> 4) & 0x0F0F0F0Fu;  // even, odd codes
 #pragma unroll
                         for (int b = 0; b < 4; ++b) {
-                            a0 = __builtin_fmaf((float)((lo >> (8 * b)) & 0xFFu), xv[8 * dw + 2 * b], a0);
-                            a1 = __builtin_fmaf((float)((hi >> (8 * b)) & 0xFFu), xv[8 * dw + 2 * b + 1], a1);
+                            const uint32_t sel = (uint32_t)b | 0x0C00u | ((uint32_t)(4 + b) << 16) | 0x0C000000u;
+                            const uint32_t wp = __builtin_amdgcn_perm(hi, lo, sel) | 0x43004300u;
+                            if (b & 1) a1 = dot2bf(wp, xp[4 * dw + b], a1);
+                            else a0 = dot2bf(wp, xp[4 * dw + b], a0);
                         }
                     }
-                    accf[u] += S * (a0 + a1) + M * xsum;
+                    accf[u] += S * (a0 + a1) + (M - 128.0f * S) * xsum;
                 }
             } else if constexpr (F == F_INT8I) {
                 const u32x4 xq = reinterpret_cast<const u32x4*>(xs)[c];
