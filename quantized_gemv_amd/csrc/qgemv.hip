@@ -56,6 +56,8 @@
 //                    (6-bit fields, fp16 d / dmin); sum_k q x by fp32 FMA
 //                    (v_cvt_f32_ubyte on nibble-masked dwords), then
 //                    S * that + M * sum_k x.
+#include <type_traits>
+
 #include "qg_device.h"
 #include "qg_launch.h"
 
@@ -174,6 +176,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     // the matrix is blockIdx.y: its parameters come in the first round of
     // kernel-argument reads, with no search over the group before them
     // (measured 0.19 us per launch at the decode shapes)
+    constexpr bool kDynamic = kSignRes<F>;  // row groups handed out dynamically (see below)
     const int mi = blockIdx.y;
     const KParams& p = grp.mats[mi];
     const int K = p.k;
@@ -199,23 +202,82 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     if constexpr (F == F_Q4) rr = make_rsrc(p.resid + (int64_t)row0 * (K / 16), (uint32_t)(rows * (K / 16)));
     __amdgpu_buffer_rsrc_t rz = rc;  // zero-points of this workgroup's rows (SIGN1_RES8Z)
     if constexpr (F == F_SRZ) rz = make_rsrc(p.zero + row0, (uint32_t)rows);
+    // with the dynamic groups the row scales are prefetched with each item
+    // (read in the epilogue, their loads would be vector loads that wait for
+    // the prefetched item too); the fixed share reads them there (scalar loads)
+    constexpr bool kRowScale = kDynamic;
+    constexpr bool kTensorScale = (F == F_TERN || F == F_TERN3);
+    const __amdgpu_buffer_rsrc_t rs1 = make_rsrc(p.scale + (kTensorScale ? 0 : row0), kTensorScale ? 4u : (uint32_t)(rows * 4));
+    const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(kSignRes<F> ? p.scale2 + row0 : p.scale, kSignRes<F> ? (uint32_t)(rows * 4) : 0u);
     const uint32_t oob_c = (uint32_t)(rows * rowB);
     const uint32_t oob_r = (uint32_t)(rows * (F == F_Q4 ? K / 16 : K));
 
+    // Row groups (U rows).  Waves w and w + 4 share a SIMD and the older
+    // issues first: with a fixed share the younger waves of a sign + residual
+    // launch finished up to a quarter of the kernel later (per-wave
+    // timestamps on MI355X), streaming alone at the end.  For those formats
+    // the groups are handed out dynamically: a wave takes groups w and w + 8
+    // (known before any LDS access, which lets the prologue issue two items
+    // at once) and then the next free group from an LDS counter, fetched one
+    // group ahead of its use.  The other formats keep the fixed share (w,
+    // w + 8, ...): at their decode shapes the counter's atomic made the
+    // compiler wait for the prefetched item, which cost more than it saved.
     const int ngroups = (rows + U - 1) / U;
     const int my_groups = ngroups > wave ? (ngroups - wave + kQWaves - 1) / kQWaves : 0;
-    const int nit = my_groups * nseg;
+    const int nit = my_groups * nseg;  // fixed share: items of this wave
+    __shared__ int next_group;
+    if (kDynamic && tid == 0) next_group = 2 * kQWaves;  // read only after the prologue's barrier
+    struct Item {
+        int g, seg;  // row group, segment of the row (wave-uniform)
+    };
+    int started = 1;  // groups this wave has started
+    int g_pend = 0;   // lane 0: the group after the current one (LDS atomic in flight)
+    typedef __attribute__((address_space(3))) int lds_int;
+    lds_int* const ctr = (lds_int*)(&next_group);
+    auto fetch_group = [&]() {
+        if (lane == 0) g_pend = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    auto next_item = [&](const Item& x) -> Item {
+        if (x.seg + 1 < nseg) return Item{x.g, x.seg + 1};
+        int g;
+        if (!kDynamic || started == 1) {
+            g = wave + kQWaves;
+        } else {
+            g = __builtin_amdgcn_readfirstlane(g_pend);
+            fetch_group();
+        }
+        ++started;
+        return Item{g, 0};
+    };
 
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)(K * (XT == 0 ? 4 : 2)));
-    // Only real items are issued (the main loop below is peeled so that no
-    // load is conditional after a load that is waited on: the waitcnt pass
-    // would otherwise merge paths and wait for the prefetched item too).
-    // Ragged rows / chunks inside an item read zeros through out-of-range
-    // offsets.
-    auto issue = [&](int it, Frag (&fr)[U][JS]) {
+    // Every issue is unconditional (no load sits behind a branch after a
+    // load that is waited on: the waitcnt pass would otherwise merge paths
+    // and wait for the prefetched item too).  Groups past the last, ragged
+    // rows and chunks read zeros through out-of-range offsets.
+    // an item is named by its index in the wave's fixed share (int) or, with
+    // dynamic groups, by its Item
+    auto group_of = [&](const auto& x) -> int {
+        if constexpr (std::is_integral_v<std::decay_t<decltype(x)>>) return wave + kQWaves * ((int)x / nseg);
+        else return x.g;
+    };
+    auto seg_of = [&](const auto& x) -> int {
+        if constexpr (std::is_integral_v<std::decay_t<decltype(x)>>) return (int)x % nseg;
+        else return x.seg;
+    };
+    auto issue = [&](const auto& x, Frag (&fr)[U][JS], float (&sc)[U][2]) {
         const bool live = true;
-        const int g = wave + kQWaves * (it / nseg);
-        const int seg = it % nseg;
+        const int g = group_of(x);
+        const int seg = seg_of(x);
+        if constexpr (kRowScale) {  // every item (no load behind a branch)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int r = g * U + u;
+                const uint32_t o = kTensorScale ? 0u : (r < rows ? (uint32_t)(4 * r) : (uint32_t)(4 * rows));
+                sc[u][0] = __uint_as_float(load4(rs1, o));
+                if constexpr (kSignRes<F>) sc[u][1] = __uint_as_float(load4(rs2, o));
+            }
+        }
 #pragma unroll
         for (int j = 0; j < JS; ++j) {  // issue in the order consume() uses the data
             const int c = lane + 64 * (seg * JS + j);
@@ -304,6 +366,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
         __builtin_amdgcn_sched_barrier(0);  // x goes out ahead of the first weights
     }
     Frag fa[U][JS], fb[U][JS];
+    float sa[U][2] = {}, sb[U][2] = {};  // the items' row scales
     // unconditional, like the x loads: a wave without rows reads zeros (its
     // offsets are out of range) and never consumes them.  For the ternary
     // formats, whose x prologue is a quantization with a workgroup max, the
@@ -311,8 +374,13 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     // only one or two items, which then all stream while x is prepared
     // (measured faster there, and slower for the other staged formats).
     constexpr bool kTwoAhead = (F == F_TERN || F == F_TERN3);
-    issue(0, fa);
-    if constexpr (kTwoAhead) issue(1, fb);
+    Item ia{wave, 0}, ib{0, 0};
+    if constexpr (kDynamic) {
+        issue(ia, fa, sa);
+    } else {
+        issue(0, fa, sa);
+        if constexpr (kTwoAhead) issue(1, fb, sb);
+    }
 
     // piece -> fp32 values
     auto piece_vals = [&](const u32x4& r, float v[kElems]) {
@@ -414,7 +482,9 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
         for (int i = tid; i < 4 * npad; i += kQThreads)
             reinterpret_cast<u32x4*>(xs)[(i / npad) * NC + c0 + i % npad] = u32x4{0u, 0u, 0u, 0u};
     }
-    if constexpr (!kXPerItem) lds_barrier();  // x staged; the prefetched weights stay in flight
+    // x staged (and the group counter set); the prefetched weights stay in flight
+    if constexpr (kDynamic || !kXPerItem) lds_barrier();
+    if constexpr (kDynamic) fetch_group();
     if constexpr (F == F_TERN || F == F_TERN3) {
         sum_xq = 0;
 #pragma unroll
@@ -426,9 +496,9 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
 #pragma unroll
     for (int u = 0; u < U; ++u) { accf[u] = 0.f; accf2[u] = 0.f; acc1[u] = 0; acc4[u] = 0; acc16[u] = 0; }
 
-    auto consume = [&](int it, Frag (&fr)[U][JS]) {
-        const int g = wave + kQWaves * (it / nseg);
-        const int seg = it % nseg;
+    auto consume = [&](const auto& x, Frag (&fr)[U][JS], const float (&sc)[U][2]) {
+        const int g = group_of(x);
+        const int seg = seg_of(x);
         if (seg == 0) {
 #pragma unroll
             for (int u = 0; u < U; ++u) { accf[u] = 0.f; accf2[u] = 0.f; acc1[u] = 0; acc4[u] = 0; acc16[u] = 0; }
@@ -606,7 +676,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
                         if (r < rows) {
                             const int row = row0 + r;
                             float o;
-                            if constexpr (kSignRes<F>) o = p.scale[row] * v[u] + v2[u] / p.scale2[row];
+                            if constexpr (kSignRes<F>) o = sc[u][0] * v[u] + v2[u] / sc[u][1];
                             else if constexpr (F == F_Q4) o = v[u];  // group scales already applied
                             else o = v[u] / p.scale[row];
                             if constexpr (YT == 0) static_cast<float*>(p.y)[row] = o;
@@ -641,36 +711,63 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
         }
     };
 
-    int it = 0;
-    if constexpr (kTwoAhead) {
-        // items `it` (fa) and `it + 1` (fb) are in flight at the top of every
-        // trip; issues past nit read zeros and are never consumed
+    if constexpr (kDynamic) {
+        // The wave's groups are increasing, so the loop ends after the first
+        // item past the last group.  Every issued item is consumed on every
+        // path (such an item reads zeros and stores nothing): a load left
+        // unused on the exit path would be sunk below the exit test by the
+        // compiler, past the consumption of the item before it, which would
+        // then wait for both.  Item ia is in flight in fa at the top of
+        // every trip.
+        while (true) {
+            ib = next_item(ia);
+            issue(ib, fb, sb);
+            consume(ia, fa, sa);
+            if (ib.g >= ngroups) {
+                consume(ib, fb, sb);
+                break;
+            }
+            ia = next_item(ib);
+            issue(ia, fa, sa);
+            consume(ib, fb, sb);
+            if (ia.g >= ngroups) {
+                consume(ia, fa, sa);
+                break;
+            }
+        }
+    } else if constexpr (kTwoAhead) {
+        // fixed share, peeled so that no load is conditional behind a load
+        // that is waited on.  Items it (fa) and it + 1 (fb) are in flight at
+        // the top of every trip; issues past nit read zeros and are never
+        // consumed
+        int it = 0;
         for (; it + 2 < nit; it += 2) {
-            consume(it, fa);
-            issue(it + 2, fa);
-            consume(it + 1, fb);
-            issue(it + 3, fb);
+            consume(it, fa, sa);
+            issue(it + 2, fa, sa);
+            consume(it + 1, fb, sb);
+            issue(it + 3, fb, sb);
         }
         if (it + 2 == nit) {  // two items left
-            consume(it, fa);
-            consume(it + 1, fb);
+            consume(it, fa, sa);
+            consume(it + 1, fb, sb);
         } else if (it + 1 == nit) {  // one item left
-            consume(it, fa);
+            consume(it, fa, sa);
         }
     } else {
-        // steady state: item `it` is in flight in fa at the top of every trip
+        // fixed share: item it is in flight in fa at the top of every trip
+        int it = 0;
         for (; it + 2 < nit; it += 2) {
-            issue(it + 1, fb);
-            consume(it, fa);
-            issue(it + 2, fa);
-            consume(it + 1, fb);
+            issue(it + 1, fb, sb);
+            consume(it, fa, sa);
+            issue(it + 2, fa, sa);
+            consume(it + 1, fb, sb);
         }
         if (it + 2 == nit) {  // two items left
-            issue(it + 1, fb);
-            consume(it, fa);
-            consume(it + 1, fb);
+            issue(it + 1, fb, sb);
+            consume(it, fa, sa);
+            consume(it + 1, fb, sb);
         } else if (it + 1 == nit) {  // one item left
-            consume(it, fa);
+            consume(it, fa, sa);
         }
     }
 }
