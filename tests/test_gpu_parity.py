@@ -327,6 +327,21 @@ def test_qgemv_sign_residual(qg, n, k):
     _sr_case(qg, n, k)
 
 
+# Shapes where a workgroup owns more row groups than the two per wave it takes
+# first, so the rest are handed out through its LDS counter: 20 rows per
+# workgroup, 38 (ragged: the last workgroup has fewer), and 24 rows of four
+# segments each.  The rows of the first workgroups, the last ones and a random
+# sample are checked.
+@pytest.mark.parametrize("n,k", [(5120, 1152), (9477, 2048), (6144, 16384)])
+def test_qgemv_sign_residual_dynamic_groups(qg, n, k):
+    note("qgemv sign+residual %dx%d (dynamic row groups)" % (n, k))
+    g = np.random.default_rng(n)
+    per_wg = -(-n // 256)
+    rows = np.unique(np.concatenate([np.arange(0, 2 * per_wg), np.arange(n - 2 * per_wg, n),
+                                     g.choice(n, 200, replace=False)]))
+    _sr_case(qg, n, k, rows=rows)
+
+
 def test_qgemv_sign_residual_full(qg):
     note("qgemv sign+residual 28672x8192 (sampled rows)")
     g = np.random.default_rng(0)

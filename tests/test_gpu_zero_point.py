@@ -113,6 +113,19 @@ def test_qgemv_sign_residual_zp(qg, n, k):
     _zp_case(qg, n, k)
 
 
+# more row groups per workgroup than the two per wave taken first: the rest
+# come from the workgroup's LDS counter (rows of the first and last
+# workgroups and a random sample are checked)
+@pytest.mark.parametrize("n,k", [(5120, 1152), (9477, 2048), (6144, 16384)])
+def test_qgemv_sign_residual_zp_dynamic_groups(qg, n, k):
+    note("qgemv sign + zero-point residual %dx%d (dynamic row groups)" % (n, k))
+    g = np.random.default_rng(n + 1)
+    per_wg = -(-n // 256)
+    rows = np.unique(np.concatenate([np.arange(0, 2 * per_wg), np.arange(n - 2 * per_wg, n),
+                                     g.choice(n, 200, replace=False)]))
+    _zp_case(qg, n, k, rows=rows)
+
+
 def test_qgemv_sign_residual_zp_shifted_activations(qg):
     # activations with a large common offset: sum_k x[k] is large, so the
     # zero-point term z * sum_k x[k] matters in every row
