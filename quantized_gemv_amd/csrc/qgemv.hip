@@ -12,7 +12,11 @@
 //     in proportion to their rows;
 //   * each wave takes groups of U rows; an "item" is U rows x JS chunk
 //     columns per lane; items are double-buffered in registers so the next
-//     item's loads are in flight while the current one is reduced;
+//     item's loads are in flight while the current one is reduced; the
+//     groups of a workgroup are a fixed share per wave (w, w + 8, ...), or,
+//     for the sign + residual formats, two fixed groups and then the next
+//     free one from an LDS counter (the younger wave of each SIMD pair
+//     otherwise finishes far behind the older);
 //   * the activation vector: for int8 weights with bf16 / fp32 x, every item
 //     loads its own 16-activation slice next to its weights (x is L2
 //     resident; no LDS and no barrier); the other formats stage x once per
@@ -53,9 +57,10 @@
 //                    activations have a large mean).
 //   Q4K            : 16 B chunk = one group of 32 4-bit codes; the chunk's
 //                    16-byte super-block record gives the group's S and M
-//                    (6-bit fields, fp16 d / dmin); sum_k q x by fp32 FMA
-//                    (v_cvt_f32_ubyte on nibble-masked dwords), then
-//                    S * that + M * sum_k x.
+//                    (6-bit fields, fp16 d / dmin); a byte's two codes become
+//                    the bf16 pair (128 + q, 128 + q') by one v_perm and an
+//                    OR, v_dot2_f32_bf16 takes it against the x pair, and
+//                    S * that + (M - 128 S) * sum_k x removes the offset.
 #include <type_traits>
 
 #include "qg_device.h"
