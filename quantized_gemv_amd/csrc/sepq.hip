@@ -244,7 +244,7 @@ struct SepParams {
 
 constexpr int kSepThreads = 512;  // 8 waves, two per SIMD
 constexpr int kSepWaves = kSepThreads / kWave;
-constexpr uint32_t kSepLdsHead = 1024 + 64;  // selectors + reduction scratch
+constexpr uint32_t kSepLdsHead = 1024 + 64 + 16;  // selectors + reduction scratch + group counter
 constexpr int kSepXR = 4;  // 16-byte pieces of x per thread held in registers in the prologue
 
 __device__ __forceinline__ int sdot4i(uint32_t a, uint32_t b, int c) {
@@ -308,12 +308,25 @@ __global__ __launch_bounds__(kSepThreads) void sep_qgemv_kernel(SepParams p) {
     const uint32_t oob_r = SKIP ? 0u : (uint32_t)((int64_t)rows * p.ld);
     const uint32_t ld = (uint32_t)p.ld;
 
+    // Row groups: waves w and w + 4 (and the other workgroup's waves on the
+    // CU) share a SIMD, and the older issues first; with a fixed share the
+    // younger waves of a workgroup finished about 5 us after the older ones
+    // (per-wave timestamps on MI355X).  So a wave takes groups w and w + 8,
+    // then the next free group from a counter in the LDS head, fetched one
+    // group ahead of its use.
     const int ngroups = (rows + U - 1) / U;
-    const int my_groups = ngroups > wave ? (ngroups - wave + kSepWaves - 1) / kSepWaves : 0;
-    const int nit = my_groups * nsteps;
+    typedef __attribute__((address_space(3))) int lds_int;
+    lds_int* const ctr = (lds_int*)reinterpret_cast<int*>(sm + 1024 + 8 * kSepWaves);
+    if (tid == 0) *reinterpret_cast<int*>(sm + 1024 + 8 * kSepWaves) = 2 * kSepWaves;  // read after the prologue's barriers
+    int started = 1;  // groups this wave has started
+    int g_pend = 0;   // lane 0: the group after the current one (LDS atomic in flight)
+    auto fetch_group = [&]() {
+        if (lane == 0) g_pend = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
 
     // classes of one item and what their scan gives
     struct Slot {
+        int g, s;  // the item: row group and step (wave-uniform)
         u32x4 D[U];
         int excl[U];  // residual codes of the row's item before this lane's 64 weights
         int T[U];     // residual codes in the row's item (wave-uniform)
@@ -322,22 +335,37 @@ __global__ __launch_bounds__(kSepThreads) void sep_qgemv_kernel(SepParams p) {
     u32x4 V[U][4];     // the residual slice in flight: lane l holds blocks l + 64 j,
     uint32_t X4[U];    // and lanes 0-3 the four dwords after them
 
-    // items past the wave's last read zeros through out-of-range offsets
-    auto issue_codes = [&](int it, Slot& c) {
-        const int g = wave + kSepWaves * (it / nsteps);
-        const int s = it % nsteps;
-        const bool live = it < nit;
+    // the item after b's in the wave's sequence, into c
+    auto next_into = [&](const Slot& b, Slot& c) {
+        if (b.s + 1 < nsteps) {
+            c.g = b.g;
+            c.s = b.s + 1;
+            return;
+        }
+        if (started == 1) {
+            c.g = wave + kSepWaves;
+        } else {
+            c.g = __builtin_amdgcn_readfirstlane(g_pend);
+            fetch_group();
+        }
+        ++started;
+        c.s = 0;
+    };
+    // groups past the last read zeros through out-of-range offsets
+    auto issue_codes = [&](Slot& c) {
+        const int g = c.g;
+        const int s = c.s;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int r = g * U + u;
-            const bool ok = live && r < rows && s * kSepStep + 64 * lane < K;
+            const bool ok = r < rows && s * kSepStep + 64 * lane < K;
             c.D[u] = load16_nt(rc, ok ? (uint32_t)(r * rowC + s * (kSepStep / 4) + 16 * lane) : oob_c);
         }
     };
     // residual flags, their per-lane exclusive prefix and the step's total;
     // `prev` is the item before (same rows, previous step) unless s == 0
-    auto scan = [&](int it, Slot& b, const Slot& prev, bool first) {
-        const int s = it % nsteps;
+    auto scan = [&](Slot& b, const Slot& prev, bool first) {
+        const int s = b.s;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             int cnt = 0;
@@ -349,16 +377,15 @@ __global__ __launch_bounds__(kSepThreads) void sep_qgemv_kernel(SepParams p) {
             b.base[u] = (first || s == 0) ? 0 : prev.base[u] + prev.T[u];
         }
     };
-    auto issue_vals = [&](int it, const Slot& b) {
-        const int g = wave + kSepWaves * (it / nsteps);
-        const bool live = it < nit;
+    auto issue_vals = [&](const Slot& b) {
+        const int g = b.g;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int r = g * U + u;
             const uint32_t mis = (uint32_t)b.base[u] & 15u;
             const uint32_t a0 = (uint32_t)r * ld + ((uint32_t)b.base[u] - mis);
             const uint32_t end = mis + (uint32_t)b.T[u];  // bytes of the slice from a0
-            const bool okr = live && r < rows;
+            const bool okr = r < rows;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t o = 16u * (64u * j + lane);
@@ -370,8 +397,11 @@ __global__ __launch_bounds__(kSepThreads) void sep_qgemv_kernel(SepParams p) {
     };
 
     Slot S0, S1, S2;
-    issue_codes(0, S0);
-    issue_codes(1, S1);
+    S0.g = wave;
+    S0.s = 0;
+    next_into(S0, S1);  // the wave's own first two groups: no LDS access
+    issue_codes(S0);
+    issue_codes(S1);
     // x pieces (16 B: 4 fp32 or 8 bf16) of this thread, requested next
     constexpr int kElems = (XT == 0) ? 4 : 8;
     const int npieces = K / kElems;
@@ -385,8 +415,8 @@ __global__ __launch_bounds__(kSepThreads) void sep_qgemv_kernel(SepParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);
     // item 0's residual slice goes out before the prologue arithmetic
-    scan(0, S0, S0, true);
-    if constexpr (!SKIP) issue_vals(0, S0);
+    scan(S0, S0, true);
+    if constexpr (!SKIP) issue_vals(S0);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---------------------------------------------------------------- prologue
@@ -469,7 +499,8 @@ __global__ __launch_bounds__(kSepThreads) void sep_qgemv_kernel(SepParams p) {
             *reinterpret_cast<u32x4*>(xp + off) = u32x4{t[0], t[1], t[2], t[3]};
         }
     }
-    sum_xq = block_sum_int<kSepWaves>(sum_xq, redi);  // its barriers also publish the LDS tables
+    sum_xq = block_sum_int<kSepWaves>(sum_xq, redi);  // its barriers also publish the LDS tables (and the counter)
+    fetch_group();
 
     int accb[U], accr[U];
 #pragma unroll
@@ -477,9 +508,9 @@ __global__ __launch_bounds__(kSepThreads) void sep_qgemv_kernel(SepParams p) {
 
     // item it: A holds its classes (scanned), B the next item's (in flight),
     // C receives the classes of item it + 2
-    auto body = [&](int it, Slot& A, Slot& B, Slot& C) {
-        const int s = it % nsteps;
-        const int g = wave + kSepWaves * (it / nsteps);
+    auto body = [&](Slot& A, Slot& B, Slot& C) {
+        const int s = A.s;
+        const int g = A.g;
         float al[U], sr[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {  // requested ahead of the next items' data
@@ -487,8 +518,9 @@ __global__ __launch_bounds__(kSepThreads) void sep_qgemv_kernel(SepParams p) {
             al[u] = p.alpha[(int64_t)row0 + rcl];
             sr[u] = SKIP ? 1.0f : p.s_r[(int64_t)row0 + rcl];
         }
-        issue_codes(it + 2, C);
-        scan(it + 1, B, A, false);
+        next_into(B, C);
+        issue_codes(C);
+        scan(B, A, false);
         if constexpr (!SKIP) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -497,7 +529,7 @@ __global__ __launch_bounds__(kSepThreads) void sep_qgemv_kernel(SepParams p) {
                     *reinterpret_cast<u32x4*>(sm + stage0 + u * kSepStage + 16 * (64 * j + lane)) = V[u][j];
                 if (lane < 4) *reinterpret_cast<uint32_t*>(sm + stage0 + u * kSepStage + kSepStep + 4 * lane) = X4[u];
             }
-            issue_vals(it + 1, B);
+            issue_vals(B);
         }
         uint32_t a[U];
 #pragma unroll
@@ -572,13 +604,31 @@ __global__ __launch_bounds__(kSepThreads) void sep_qgemv_kernel(SepParams p) {
         }
     };
     // three slots in turn, so that no register copy waits for a load in
-    // flight; the last round may run up to two items past the wave's last,
-    // which read zeros and store nothing
-    for (int it = 0; it < nit; it += 3) {
-        body(it, S0, S1, S2);
-        body(it + 1, S1, S2, S0);
-        body(it + 2, S2, S0, S1);
+    // flight.  The wave's groups are increasing: the loop ends when the next
+    // item to compute is past the last group.  Its loads (and the ones of
+    // the item after it) read zeros; they are folded into an opaque use at
+    // the exit, since a load left unused there would be sunk by the compiler
+    // below the exit test, after the arithmetic it is meant to run under.
+    while (true) {
+        body(S0, S1, S2);
+        if (S1.g >= ngroups) break;
+        body(S1, S2, S0);
+        if (S2.g >= ngroups) break;
+        body(S2, S0, S1);
+        if (S0.g >= ngroups) break;
     }
+    uint32_t inflight = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) inflight ^= S0.D[u][d] ^ S1.D[u][d] ^ S2.D[u][d];
+        if constexpr (!SKIP) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) inflight ^= V[u][j][0] ^ V[u][j][1] ^ V[u][j][2] ^ V[u][j][3];
+            inflight ^= X4[u];
+        }
+    }
+    asm volatile("" ::"v"(inflight));
 }
 
 template <int XT, int U, bool SKIP, bool XPL>

@@ -123,6 +123,16 @@ def test_qgemv_sep_skip_residual(qg, n, k):
     _product_case(qg, n, k, 80, 50, True, skip=True)
 
 
+# more row groups per workgroup than the two per wave taken first, so the
+# rest come from the workgroup's LDS counter: 24 rows per workgroup (one step
+# per row; two steps and a ragged last workgroup), and 24 groups of two rows
+# in the skip-residual mode
+@pytest.mark.parametrize("n,k,skip", [(8800, 1152, False), (8300, 8192, False), (17000, 1152, True)])
+def test_qgemv_sep_dynamic_groups(qg, n, k, skip):
+    note("qgemv thresholded %dx%d skip=%s (dynamic row groups)" % (n, k, skip))
+    _product_case(qg, n, k, 80, 50, True, skip=skip)
+
+
 def test_qgemv_sep_zero_activations(qg):
     note("qgemv thresholded zero x")
     _product_case(qg, 16, 1024, 80, 50, False, zero_x=True)
