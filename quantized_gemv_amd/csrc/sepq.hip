@@ -265,10 +265,12 @@ __device__ __forceinline__ void transpose4x4(const u32x4& a, uint32_t t[4]) {
     t[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
 }
 
-// Work: a workgroup owns rows_per_wg consecutive rows; wave w takes groups of
-// U rows (w, w + 8, ...); an item is one group x one step.  The classes of
-// item it + 2 and the residual slice of item it + 1 are in flight while item
-// it is computed: the classes run two items ahead so that the slice of the
+// Work: a workgroup owns rows_per_wg consecutive rows in groups of U rows;
+// wave w takes groups w and w + 8, then the next free group from a counter in
+// the LDS head; an item is one group x one step, and a wave runs the steps
+// of its group in order.  The classes of the item two ahead and the residual
+// slice of the next item are in flight while an item is computed: the
+// classes run two items ahead so that the slice of the
 // next item (its start: the running residual count; its length: the scan of
 // its classes) is known when it is requested, and only the 16-byte blocks it
 // covers are read.
@@ -506,8 +508,8 @@ __global__ __launch_bounds__(kSepThreads) void sep_qgemv_kernel(SepParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) { accb[u] = 0; accr[u] = 0; }
 
-    // item it: A holds its classes (scanned), B the next item's (in flight),
-    // C receives the classes of item it + 2
+    // A holds the classes of the item computed now (scanned), B the next
+    // item's (in flight), C receives the classes of the item after B
     auto body = [&](Slot& A, Slot& B, Slot& C) {
         const int s = A.s;
         const int g = A.g;
