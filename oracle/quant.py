@@ -20,10 +20,13 @@ def absmax_scale(alpha: np.ndarray) -> np.ndarray:
     multiplier q_max / alpha.  [OVR] section 3.1 step 2 writes the reciprocal
     (alpha / 127, then divides); the stored value here is the multiplier.
     An all-zero group (alpha = 0) gets s = 1 so its codes are 0 (the pages do
-    not cover it)."""
+    not cover it).  A group so small that q_max / alpha exceeds the fp32
+    range (alpha below about 3.7e-37) gets s = FLT_MAX: the quotient is
+    clamped to the largest finite fp32, so every code stays finite, zeros
+    stay 0 and the codes still follow round(s * x)."""
     alpha = np.asarray(alpha, dtype=np.float32)
-    with np.errstate(divide="ignore"):
-        s = np.float32(Q_MAX) / alpha
+    with np.errstate(divide="ignore", over="ignore"):
+        s = np.minimum(np.float32(Q_MAX) / alpha, np.finfo(np.float32).max)
     return np.where(alpha == np.float32(0), np.float32(1), s).astype(np.float32)
 
 
@@ -119,13 +122,15 @@ def asym_params(lo, hi):
     [q_min, q_max] (any range the data straddles 0 with is unchanged); an
     all-zero group (alpha = beta = 0) gets s = 1, z = q_min.  fp32 steps:
     d = fl32(alpha - beta), s = fl32(255 / d), z = rint(fl32(q_min - fl32(s * beta)))
-    clipped to [q_min, q_max] (the clip is inactive up to rounding).
+    clipped to [q_min, q_max] (the clip is inactive up to rounding).  As for
+    the symmetric scale, s is clamped to FLT_MAX when 255 / d overflows
+    (d below about 7.5e-37).
     lo, hi: fp32 arrays of group minima / maxima.  Returns (s fp32, z int32)."""
     lo = np.minimum(np.asarray(lo, np.float32), np.float32(0))
     hi = np.maximum(np.asarray(hi, np.float32), np.float32(0))
     d = (hi - lo).astype(np.float32)
-    with np.errstate(divide="ignore"):
-        s = (np.float32(Q_MAX_ASYM - Q_MIN_ASYM) / d).astype(np.float32)
+    with np.errstate(divide="ignore", over="ignore"):
+        s = np.minimum(np.float32(Q_MAX_ASYM - Q_MIN_ASYM) / d, np.finfo(np.float32).max).astype(np.float32)
     s = np.where(d == np.float32(0), np.float32(1), s).astype(np.float32)
     t = (s * lo).astype(np.float32)
     z = np.rint((np.float32(Q_MIN_ASYM) - t).astype(np.float32))

@@ -29,9 +29,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 
 // ------------------------------------------------------------------ absmax step
 // s = 127 / alpha as one IEEE fp32 division (the build keeps division
-// correctly rounded); an all-zero group gets s = 1 so its codes are 0.
+// correctly rounded); an all-zero group gets s = 1 so its codes are 0.  For
+// alpha below about 3.7e-37 the quotient overflows: s is clamped to FLT_MAX,
+// so codes stay finite (|x * s| < 127) and zeros stay 0.
 __device__ __forceinline__ float absmax_scale(float alpha) {
-    return alpha == 0.0f ? 1.0f : 127.0f / alpha;
+    return alpha == 0.0f ? 1.0f : __builtin_fminf(127.0f / alpha, 3.40282347e38f);
 }
 
 // clip(round_half_even(fl32(x * s)), -127, 127).  The build disables FP
@@ -51,7 +53,7 @@ __device__ __forceinline__ void asym_params(float lo, float hi, float& s, float&
     lo = __builtin_fminf(lo, 0.0f);
     hi = __builtin_fmaxf(hi, 0.0f);
     const float d = hi - lo;
-    s = d == 0.0f ? 1.0f : 255.0f / d;
+    s = d == 0.0f ? 1.0f : __builtin_fminf(255.0f / d, 3.40282347e38f);  // clamped like absmax_scale
     const float t = s * lo;
     const float u = -128.0f - t;
     z = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(u), -128.0f), 127.0f);

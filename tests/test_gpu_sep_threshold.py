@@ -44,17 +44,18 @@ def _weights(n, k, seed, special=True):
     return w
 
 
-def _check_split(qg, w, pb, pz, rows=None):
+def _check_split(qg, w, pb, pz):
+    """GPU split against the oracle on every row: scales, class plane and
+    residual stream."""
     n, k = w.shape
     sw = qg.split_sep_threshold(dev(w), pb, pz)
     assert sw.ld == th.resid_ld(k, pz) or (sw.ld == 16 and th.resid_ld(k, pz) < 16)
-    sel = np.arange(n) if rows is None else np.asarray(rows)
-    f, a, rq, sr = th.threshold_split(np.ascontiguousarray(w[sel]), pb, pz)
+    f, a, rq, sr = th.threshold_split(w, pb, pz)
     plane, stream = th.pack_threshold(f, rq, sw.ld)
-    assert np.array_equal(host(sw.alpha)[sel], a)
-    assert np.array_equal(host(sw.s_r)[sel], sr)
-    assert np.array_equal(host(sw.cls)[sel], plane)
-    assert np.array_equal(host(sw.rv)[sel], stream)
+    assert np.array_equal(host(sw.alpha), a)
+    assert np.array_equal(host(sw.s_r), sr)
+    assert np.array_equal(host(sw.cls), plane)
+    assert np.array_equal(host(sw.rv), stream)
     return sw, (f, a, rq, sr)
 
 
@@ -65,12 +66,10 @@ def test_split_sep_threshold(qg, n, k, pb, pz):
     _check_split(qg, _weights(n, k, n * 7 + k), pb, pz)
 
 
-def test_split_sep_threshold_full_sampled(qg):
-    note("split thresholded 28672x8192 (sampled rows)")
+def test_split_sep_threshold_full(qg):
+    note("split thresholded 28672x8192 (every row)")
     wl = synth.sign_residual_decode()
-    g = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([[0, 1, 28671, 14335], g.choice(28672, 60, replace=False)]))
-    _check_split(qg, wl.tensors["w"], 80, 50, rows=rows)
+    _check_split(qg, wl.tensors["w"], 80, 50)
 
 
 def _product_case(qg, n, k, pb, pz, x_bf16, skip=False, seed=0, zero_x=False):
@@ -138,22 +137,22 @@ def test_qgemv_sep_zero_activations(qg):
     _product_case(qg, 16, 1024, 80, 50, False, zero_x=True)
 
 
-def test_qgemv_sep_full_sampled(qg):
-    # the bench workload end to end on the GPU: split, then product; rows
-    # sampled for the oracle (rows are independent given x)
-    note("qgemv thresholded 28672x8192 (sampled rows)")
+def test_qgemv_sep_full(qg):
+    # the bench workload end to end on the GPU: split, then product, with
+    # every row's classes, residual stream, scales, int32 sums and y checked
+    note("qgemv thresholded 28672x8192 (every row)")
     wl = synth.sign_residual_decode()
     w, xb = wl.tensors["w"], wl.tensors["x_bf16"]
-    g = np.random.default_rng(2)
-    rows = np.unique(np.concatenate([[0, 28671, 100], g.choice(28672, 40, replace=False)]))
-    sw, (f, a, rq, sr) = _check_split(qg, w, 80, 50, rows=rows)
+    sw, (f, a, rq, sr) = _check_split(qg, w, 80, 50)
     n = w.shape[0]
-    acc = torch.empty(2 * n, dtype=torch.int32, device="cuda")
-    y = qg.qgemv_sep(sw, dev_bf16(xb), acc_out=acc)
+    acc_full, acc = guarded(2 * n, torch.int32)
+    y_full, y = guarded(n, torch.float32)
+    qg.qgemv_sep(sw, dev_bf16(xb), y=y, acc_out=acc)
     x = synth.bf16_bits_to_f32(xb)
     xq, s_x = oracle.quantize_absmax(x, per_row=False)
     acc_b, acc_r = th.int_products(f, rq, xq)
     acc_h = host(acc)
-    assert np.array_equal(acc_h[:n][rows], acc_b) and np.array_equal(acc_h[n:][rows], acc_r)
+    assert np.array_equal(acc_h[:n], acc_b) and np.array_equal(acc_h[n:], acc_r)
     y_ref = th.y_threshold(acc_b, acc_r, a, sr, s_x)
-    assert oracle.normwise_error(host(y)[rows], y_ref) <= TOL_F32
+    assert oracle.normwise_error(host(y), y_ref) <= TOL_F32
+    assert canaries_intact(y_full, n) and canaries_intact(acc_full, 2 * n)

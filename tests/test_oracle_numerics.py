@@ -120,3 +120,38 @@ def test_mean_abs_special_cases():
     # the mean of [1, 2] is 1.5, of [1, 2, 2] is 5/3 rounded
     assert oracle.mean_abs_f32(np.array([1, -2], np.float32)) == np.float32(1.5)
     assert oracle.mean_abs_f32(np.array([1, 2, 2], np.float32)) == np.float32(5.0 / 3.0)
+
+
+def _pyint_abs_sum_units(a) -> int:
+    """sum |a_i| * 2**149 with Python integers, element by element: every
+    fp32 value times 2**149 is an integer, exact in fp64 (a power-of-two
+    scaling) and converted exactly by int().  No binade decomposition."""
+    flat = np.abs(np.ascontiguousarray(a, np.float32).ravel()).astype(np.float64) * 2.0 ** 149
+    total = 0
+    for lo in range(0, flat.size, 1 << 20):
+        total += sum(map(int, flat[lo:lo + (1 << 20)].tolist()))
+    return total
+
+
+def test_mean_abs_at_ternary_workload_size():
+    # gamma of the ternary decode workload (11008 x 4096 = 45,088,768
+    # Laplace weights, [VG] 'BitNet b1.58' Fig. 60): the oracle's binade sums
+    # against a plain integer sum, and its rounding against a search of the
+    # neighbouring fp32 values
+    import synth
+    w = synth.ternary_decode().tensors["w"]
+    s = _pyint_abs_sum_units(w)
+    assert exact_abs_sum_units(w) == s
+    assert oracle.mean_abs_f32(w) == _nearest_f32_bruteforce(Fraction(s, w.size << 149))
+
+
+def test_mean_abs_rows_at_separated_workload_shape():
+    # per-row alpha of the separated decode workload (rows of 8192 Laplace
+    # weights with 0.5% x20 outliers, [SEP] section 2.1), on a sample of rows
+    import synth
+    rows = np.random.default_rng(5).choice(28672, 96, replace=False)
+    w = synth.sign_residual_decode(rows=np.sort(rows)).tensors["w"]
+    got = oracle.mean_abs_rows_f32(w)
+    for i in range(w.shape[0]):
+        s = _pyint_abs_sum_units(w[i])
+        assert got[i] == _nearest_f32_bruteforce(Fraction(s, w.shape[1] << 149))

@@ -107,6 +107,38 @@ def test_absmax_granularity_and_zero_group():
     assert oracle.quantize_absmax(np.zeros(9, np.float32), per_row=False)[1][0] == 1
 
 
+
+def test_absmax_scale_clamped_for_tiny_groups():
+    # 127 / alpha overflows fp32 for alpha below 127 / FLT_MAX: the scale is
+    # clamped to FLT_MAX (reading of the pages' s = q_max / alpha, [VG]
+    # 'Symmetric quantization', for a range the fp32 quotient cannot hold)
+    fmax = np.finfo(np.float32).max
+    x = np.array([1e-37, -5e-38, 0.0, -0.0, 3e-38, 2.0 ** -149, 3.5e-37, -1e-38], np.float32)
+    q, s = oracle.quantize_absmax(x, per_row=False)
+    assert s[0] == fmax and np.isfinite(s).all()
+    # fl32(x * s): the fp64 product of two fp32 values is exact, so one
+    # narrowing to fp32 rounds it once; then half-even rounding and the clip
+    t = (x.astype(np.float64) * np.float64(fmax)).astype(np.float32)
+    assert np.array_equal(q, np.clip(np.rint(t), -127, 127).astype(np.int8))
+    assert q[2] == 0 and q[3] == 0 and q[0] == 34 and q[6] == 119
+    assert np.array_equal(oracle.quantize_absmax(-x, per_row=False)[0], -q)
+    # per row: only the tiny row is clamped; a row just above the bound is not
+    rows = np.stack([x, x * np.float32(1e30), np.full(8, 127 / fmax * 1.01, np.float32)])
+    qr, sr = oracle.quantize_absmax(rows, per_row=True)
+    assert sr[0] == fmax and sr[1] == np.float32(127) / np.max(np.abs(rows[1])) and sr[2] < fmax
+    assert np.array_equal(qr[0], q) and (qr[2] == 127).all()
+    # asymmetric: 255 / d overflows likewise (d = 3e-38); 0 still maps to z
+    lo, hi = np.float32(-1e-38), np.float32(2e-38)
+    sa, za = oracle.asym_params(np.array([lo]), np.array([hi]))
+    assert sa[0] == fmax
+    zt = np.float32(-128) - (np.float64(fmax) * np.float64(lo)).astype(np.float32)
+    assert za[0] == np.rint(zt) == -125
+    xa = np.array([lo, 0.0, hi], np.float32)
+    qa = oracle.quantize_with_zero_point(xa, sa, za)
+    ta = ((xa.astype(np.float64) * np.float64(fmax)).astype(np.float32) + np.float32(za[0])).astype(np.float32)
+    assert np.array_equal(qa, np.clip(np.rint(ta), -128, 127).astype(np.int8)) and qa[1] == za[0]
+
+
 # ---------------------------------------------------------------- ternary
 
 def test_ternary_codes_and_scale():
