@@ -121,6 +121,24 @@ qg_status qg_quantize_absmax(const void* x, int32_t xt, int64_t rows, int64_t co
                              void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * qg_quantize_absmax without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments (minus ws), checks and results, bit
+ * for bit, as qg_quantize_absmax.  QG_PER_TENSOR keeps its partial maxima
+ * (at most QG_ABSMAX_SCRATCH_PARTS floats, a bound no size exceeds: the first
+ * pass never uses more workgroups) in a file-scope device array of the
+ * library, one per device, set up on the first call on each device (the
+ * device current at the call must be the stream's).  Every call on a device
+ * shares that array; the first pass overwrites every entry the second reads,
+ * so no clearing is needed, but calls that overlap on one device race and
+ * must be serialized by the caller (one stream, or events).  QG_PER_ROW uses
+ * no scratch.  Allocates nothing and calls no allocating routine.
+ */
+#define QG_ABSMAX_SCRATCH_PARTS 1024
+qg_status qg_quantize_absmax_noalloc(const void* x, int32_t xt, int64_t rows, int64_t cols,
+                                     int32_t gran, int8_t* q, float* s, void* stream);
+
+/*
  * Activation outlier-channel split with per-token int8 quantization
  * ([SEP] section 2.2: a few channels tens of times larger are taken out and
  * kept in high precision; the rest go to int8; the channel list is found once

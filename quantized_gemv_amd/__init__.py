@@ -13,6 +13,7 @@ from ._binding import (QgError, QWeight, CWeight, EXPORTED, LIB_PATH, lib, statu
                        qgemm_w8a8_outlier, qgemm_w8a8, out_ld, QG_MAX_GROUP, QG_OUT_LD_ALIGN, QG_MAX_OUT_LD,
                        QG_F32, QG_BF16, QG_PER_TENSOR, QG_PER_ROW, QG_WFMT_INT8, QG_WFMT_TERNARY2,
                        QG_WFMT_SIGN1_RES8, QG_WFMT_Q4K, QG_WFMT_SIGN1_RES8Z, QG_WFMT_TERNARY3, QG_ACT_INT8, QG_ACT_FLOAT, QG_MAX_OUTLIERS, QG_QGEMV_MAX_K,
-                       QG_SEP_MAX_K, QG_BATCH_MAX_M, QG_BATCH_MAX_K, QG_MX_BLOCK, QG_QGEMM_MAX_K)
+                       QG_SEP_MAX_K, QG_BATCH_MAX_M, QG_BATCH_MAX_K, QG_MX_BLOCK, QG_QGEMM_MAX_K,
+                       QG_ABSMAX_SCRATCH_PARTS)
 
 __all__ = [n for n in dir() if not n.startswith("_")]

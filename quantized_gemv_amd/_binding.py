@@ -33,6 +33,7 @@ QG_BATCH_MAX_M = 16
 QG_BATCH_MAX_K = 262144
 QG_MX_BLOCK = 32
 QG_QGEMM_MAX_K = 133120
+QG_ABSMAX_SCRATCH_PARTS = 1024
 
 _c_i32, _c_i64, _c_sz, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
@@ -53,6 +54,7 @@ _SIGS = {
     "qg_abi_version": (_c_i32, []),
     "qg_quantize_absmax_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i32]),
     "qg_quantize_absmax": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
+    "qg_quantize_absmax_noalloc": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp]),
     "qg_quantize_absmax_split": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32,
                                           _c_vp]),
     "qg_detect_outliers_workspace_bytes": (_c_sz, [_c_i64]),

@@ -98,6 +98,19 @@ qg_status qg_quantize_absmax(const void* x, int32_t xt, int64_t rows, int64_t co
     return from_hip(qg::launch_absmax_tensor(x, xt, rows * cols, q, s, static_cast<float*>(ws), as_stream(stream)));
 }
 
+qg_status qg_quantize_absmax_noalloc(const void* x, int32_t xt, int64_t rows, int64_t cols, int32_t gran, int8_t* q,
+                                     float* s, void* stream) {
+    if (!x || !q || !s) return QG_ERR_NULLPTR;
+    if (xt != QG_F32 && xt != QG_BF16) return QG_ERR_ARG;
+    if (gran != QG_PER_TENSOR && gran != QG_PER_ROW) return QG_ERR_ARG;
+    if (rows < 1 || cols < 8 || cols % 8 != 0 || rows > ((int64_t)1 << 40) / cols) return QG_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(q)) return QG_ERR_ALIGN;
+    if (gran == QG_PER_ROW) return from_hip(qg::launch_absmax_rows(x, xt, rows, cols, q, s, as_stream(stream)));
+    static_assert(QG_ABSMAX_SCRATCH_PARTS == qg::kAbsmaxScratchParts, "header and library agree");
+    if (qg::absmax_tensor_parts(rows * cols) > QG_ABSMAX_SCRATCH_PARTS) return QG_ERR_WORKSPACE;
+    return from_hip(qg::launch_absmax_tensor_noalloc(x, xt, rows * cols, q, s, as_stream(stream)));
+}
+
 qg_status qg_quantize_absmax_split(const void* x, int64_t rows, int64_t cols, const int32_t* idx, int32_t n_out,
                                    int8_t* q, float* s, void* x_out, int32_t x_out_ld, void* stream) {
     if (!x || !q || !s) return QG_ERR_NULLPTR;

@@ -19,6 +19,12 @@ hipError_t launch_absmax_rows(const void* x, int xt, int64_t rows, int64_t cols,
 int absmax_tensor_parts(int64_t elems);
 hipError_t launch_absmax_tensor(const void* x, int xt, int64_t elems, int8_t* q, float* s, float* partial,
                                 hipStream_t st);
+// The same two passes with the partial maxima in a file-scope device array
+// (no workspace); absmax_tensor_parts() never exceeds its size.
+constexpr int kAbsmaxScratchParts = 1024;
+constexpr int kMaxDevices = 64;
+hipError_t launch_absmax_tensor_noalloc(const void* x, int xt, int64_t elems, int8_t* q, float* s,
+                                        hipStream_t st);
 hipError_t launch_absmax_split(const uint16_t* x, int64_t rows, int64_t cols, const OutlierIdx& idx, int n_out,
                                int8_t* q, float* s, uint16_t* x_out, int x_out_ld, hipStream_t st);
 // Row blocks of the detection's range pass (a function of cols only, so the

@@ -5,6 +5,8 @@
 // These run offline (weights) or once per step on small activations, so
 // they favour plain, exact code over speed: one 256-thread workgroup per row
 // where a row-wide statistic is needed, 16-byte vector loads along the row.
+#include <mutex>
+
 #include "qg_device.h"
 #include "qg_launch.h"
 
@@ -478,6 +480,43 @@ hipError_t launch_absmax_tensor(const void* x, int xt, int64_t elems, int8_t* q,
         absmax_apply_kernel<1><<<parts, kThreads, 0, st>>>(x, n8, partial, parts, q, s);
     }
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- no-allocation variant
+// The per-tensor quantizer's only scratch is its partial maxima, one per
+// workgroup of the first pass (absmax_tensor_parts(elems) <= 1024 floats).
+// For callers that cannot allocate, they live in this file-scope array: one
+// copy per device, held until the process ends.  The partial pass writes
+// every entry that the apply pass reads, so nothing needs clearing between
+// calls; calls that overlap on one device race for it.
+static __device__ __align__(256) float scratch[kAbsmaxScratchParts];
+
+namespace {
+std::mutex scratch_mu;
+float* scratch_dev[kMaxDevices] = {};  // device address of `scratch`, per device
+}  // namespace
+
+hipError_t launch_absmax_tensor_noalloc(const void* x, int xt, int64_t elems, int8_t* q, float* s,
+                                        hipStream_t st) {
+    if (absmax_tensor_parts(elems) > kAbsmaxScratchParts) return hipErrorInvalidValue;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    float* ptr = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(scratch_mu);
+        if (!scratch_dev[dev]) {  // once per device, with that device current
+            void* p = nullptr;
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            scratch_dev[dev] = static_cast<float*>(p);
+        }
+        ptr = scratch_dev[dev];
+    }
+    // the kernels take the device address, never the host-side name
+    return launch_absmax_tensor(x, xt, elems, q, s, ptr, st);
 }
 
 hipError_t launch_absmax_split(const uint16_t* x, int64_t rows, int64_t cols, const OutlierIdx& idx, int n_out,

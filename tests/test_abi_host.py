@@ -83,6 +83,21 @@ def test_validation_quantize_absmax(qg):
 
 
 @needs_no_gpu
+def test_validation_quantize_absmax_noalloc(qg):
+    # the same checks as qg_quantize_absmax, with no workspace to check
+    f = qg.lib().qg_quantize_absmax_noalloc
+    assert f(None, 0, 4, 64, 1, A, A, None) == 1
+    assert f(A, 0, 4, 64, 1, None, A, None) == 1
+    assert f(A, 7, 4, 64, 1, A, A, None) == 4
+    assert f(A, 0, 4, 64, 9, A, A, None) == 4
+    assert f(A, 0, 0, 64, 1, A, A, None) == 2
+    assert f(A, 0, 4, 60, 1, A, A, None) == 2
+    assert f(A, 0, 1 << 20, 1 << 21, 0, A, A, None) == 2
+    assert f(U, 0, 4, 64, 0, A, A, None) == 3
+    assert f(A, 0, 4, 64, 0, U, A, None) == 3
+
+
+@needs_no_gpu
 def test_validation_split_and_gather(qg):
     l = qg.lib()
     f = l.qg_quantize_absmax_split
