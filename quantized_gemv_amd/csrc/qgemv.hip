@@ -68,7 +68,7 @@
 
 namespace qg {
 
-enum { F_INT8F = 0, F_INT8I = 1, F_TERN = 2, F_SR = 3, F_Q4 = 4, F_SRZ = 5, F_TERN3 = 6 };
+enum { F_INT8F = 0, F_INT8I = 1, F_TERN = 2, F_SR = 3, F_Q4 = 4, F_SRZ = 5, F_TERN3 = 6, F_INT8L = 7 };
 // the sign + residual formats (symmetric residual, or with a zero-point)
 template <int F>
 constexpr bool kSignRes = (F == F_SR || F == F_SRZ);
@@ -110,6 +110,15 @@ struct Fmt<F_INT8F> {
     static constexpr int kColsPerChunk = 16;
     static constexpr int kLdsBytesPerCol = 0;  // x travels with each item instead
     struct Frag { u32x4 w; u32x4 x[4]; };      // x: 16 activations (bf16: x[0..1], fp32: x[0..3])
+};
+// int8 weights with float x staged once per workgroup in LDS as fp32 (rows
+// longer than one item of register-resident x): chunk c's 16 activations are
+// four 16-byte pieces, stored as four planes [piece][chunk]
+template <>
+struct Fmt<F_INT8L> {
+    static constexpr int kColsPerChunk = 16;
+    static constexpr int kLdsBytesPerCol = 4;
+    struct Frag { u32x4 w; };
 };
 template <>
 struct Fmt<F_INT8I> {
@@ -163,10 +172,11 @@ constexpr int kQThreads = 512;
 constexpr int kQWaves = kQThreads / kWave;
 constexpr int kXL = 4;  // x pieces of 16 B held in registers per thread (K <= 16384 bf16 / 8192 fp32)
 
-// XREG (4-bit groups, items spanning the whole row): lane l only ever
-// multiplies the columns of its chunks c = l + 64 j (j < JS), so it loads and
-// converts that x, and its groups' sums, once before the first item; the
-// items then carry codes and super-block records only.
+// XREG (items spanning the whole row; int8 weights with float x, or 4-bit
+// groups): lane l only ever multiplies the columns of its chunks
+// c = l + 64 j (j < JS), so it loads and converts that x (and, for the 4-bit
+// groups, the groups' sums) once before the first item; the items then carry
+// weights (and super-block records) only.
 template <int F, int XT, int YT, int U, int JS, bool XREG = false>
 __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     using Frag = typename Fmt<F>::Frag;
@@ -182,6 +192,14 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     // kernel-argument reads, with no search over the group before them
     // (measured 0.19 us per launch at the decode shapes)
     constexpr bool kDynamic = kSignRes<F>;  // row groups handed out dynamically (see below)
+    // int8 weights with x staged in LDS: the row groups of the two waves of
+    // a SIMD form one pool, taken from both ends (see below).  Measured on
+    // MI355X at 4096 x 11008: 10.6 -> 10.1 us.  Not for register-resident x:
+    // there the compiler reuses a register of the prefetched item for the
+    // LDS read and waits for every load at the loop head (4096 x 4096:
+    // 4.85 -> 5.14 us).
+    constexpr bool kPaired = F == F_INT8L;
+    constexpr bool kDynItems = kDynamic || kPaired;  // items named by (group, segment)
     const int mi = blockIdx.y;
     const KParams& p = grp.mats[mi];
     const int K = p.k;
@@ -200,7 +218,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     const int NC = nseg * JS * 64;  // chunks in the staged copy
 
     // ------------------------------------------------------------ stream
-    const int rowB = (F == F_TERN) ? K / 4 : kSignRes<F> ? K / 8 : (F == F_Q4) ? K / 2 : (F == F_TERN3) ? 16 * C : K;  // code bytes per row
+    const int rowB = (F == F_TERN) ? K / 4 : kSignRes<F> ? K / 8 : (F == F_Q4) ? K / 2 : (F == F_TERN3) ? 16 * C : K;  // code bytes per row (K for int8)
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.codes + (int64_t)row0 * rowB, (uint32_t)(rows * rowB));
     __amdgpu_buffer_rsrc_t rr = rc;
     if constexpr (kSignRes<F>) rr = make_rsrc(p.resid + (int64_t)row0 * K, (uint32_t)(rows * K));
@@ -210,7 +228,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     // with the dynamic groups the row scales are prefetched with each item
     // (read in the epilogue, their loads would be vector loads that wait for
     // the prefetched item too); the fixed share reads them there (scalar loads)
-    constexpr bool kRowScale = kDynamic;
+    constexpr bool kRowScale = kDynItems;
     constexpr bool kTensorScale = (F == F_TERN || F == F_TERN3);
     const __amdgpu_buffer_rsrc_t rs1 = make_rsrc(p.scale + (kTensorScale ? 0 : row0), kTensorScale ? 4u : (uint32_t)(rows * 4));
     const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(kSignRes<F> ? p.scale2 + row0 : p.scale, kSignRes<F> ? (uint32_t)(rows * 4) : 0u);
@@ -235,6 +253,35 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     struct Item {
         int g, seg;  // row group, segment of the row (wave-uniform)
     };
+    // Pairs (int8 weights, float x).  Waves w and w + 4 (one SIMD) share the
+    // groups g = w % 4 + 4 i, i < npool: the older wave takes i = 0, 1, ...
+    // from the front and owns [0, own_front); the younger takes
+    // i = npool - 1, npool - 2, ... from the back and owns [own_back, npool).
+    // Before taking its next index a wave reads the other's published bound
+    // and takes the index only if the other does not own it; after taking it
+    // the wave publishes its new bound.  Both accesses are plain LDS words
+    // written and read by the whole wave (no atomic, no branch); a race can
+    // only let both waves take the last index, which then is computed twice
+    // with identical results, never skipped.
+    __shared__ int pair_bound[kQWaves];  // [w]: own_front of front wave w, [w + 4]: own_back of back wave w + 4
+    const int pair = wave & 3;
+    const bool front = wave < 4;
+    const int npool = ngroups > pair ? (ngroups - pair + 3) / 4 : 0;
+    int own = front ? (npool >= 1 ? 1 : 0) : (npool >= 2 ? npool - 1 : npool);  // this wave's bound
+    if constexpr (kPaired) pair_bound[wave] = own;  // (whole wave, one value) read only after the prologue's barrier
+    auto next_pair_group = [&]() -> int {
+        const int other = __builtin_amdgcn_readfirstlane(pair_bound[front ? wave + 4 : wave - 4]);
+        int g = ngroups;  // past the last group: the item reads zeros and stores nothing
+        if (front) {
+            const int i = own;
+            if (i < other) { g = pair + 4 * i; own = i + 1; }
+        } else {
+            const int j = own - 1;
+            if (j >= other && j >= 0) { g = pair + 4 * j; own = j; }
+        }
+        pair_bound[wave] = own;
+        return g;
+    };
     int started = 1;  // groups this wave has started
     int g_pend = 0;   // lane 0: the group after the current one (LDS atomic in flight)
     typedef __attribute__((address_space(3))) int lds_int;
@@ -245,7 +292,9 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     auto next_item = [&](const Item& x) -> Item {
         if (x.seg + 1 < nseg) return Item{x.g, x.seg + 1};
         int g;
-        if (!kDynamic || started == 1) {
+        if constexpr (kPaired) {
+            g = next_pair_group();
+        } else if (!kDynamic || started == 1) {
             g = wave + kQWaves;
         } else {
             g = __builtin_amdgcn_readfirstlane(g_pend);
@@ -312,7 +361,8 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
                     if constexpr (F == F_INT8F) {
                         // the 16 activations of this chunk, requested just ahead of the
                         // chunk's weights and shared by the U rows of the item
-                        if (u == 0) {
+                        // (with XREG they are in registers already)
+                        if (!XREG && u == 0) {
                             constexpr int kXB = (XT == 0) ? 64 : 32;  // bytes of x per chunk
                             const uint32_t xo = (c < C) ? (uint32_t)(kXB * c) : (uint32_t)(K * (XT == 0 ? 4 : 2));
 #pragma unroll
@@ -336,11 +386,29 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     // a branch around a load would make the compiler wait for all loads at
     // the join, the weights included)
     static_assert(F != F_Q4 || XT == 1, "4-bit groups take bf16 activations");
-    static_assert(!XREG || F == F_Q4, "register-resident x is for the 4-bit groups");
-    // XREG: this lane's x (fp32) and the sums of its groups, for every row
-    uint32_t xq4[XREG ? JS : 1][XREG ? 16 : 1];  // bf16 pairs
-    float xsq4[XREG ? JS : 1];
-    if constexpr (XREG) {
+    static_assert(!XREG || F == F_Q4 || F == F_INT8F, "register-resident x: 4-bit groups and int8 weights");
+    // XREG, int8 weights: this lane's raw x (16 B pieces) is requested here,
+    // ahead of the first item's weights, and converted to fp32 after that
+    // item is issued (so the conversion waits for x only)
+    constexpr bool kXRegI8 = XREG && F == F_INT8F;
+    constexpr int kXPc = (XT == 0) ? 4 : 2;  // 16-byte pieces of x per chunk
+    u32x4 xraw[kXRegI8 ? JS : 1][kXRegI8 ? kXPc : 1];
+    float xf[kXRegI8 ? JS : 1][kXRegI8 ? 16 : 1];
+    if constexpr (kXRegI8) {
+        const uint32_t xend = (uint32_t)(K * (XT == 0 ? 4 : 2));
+#pragma unroll
+        for (int j = 0; j < JS; ++j) {
+            const int c = lane + 64 * j;
+#pragma unroll
+            for (int q = 0; q < kXPc; ++q) xraw[j][q] = load16(rx, c < C ? (uint32_t)(16 * kXPc * c + 16 * q) : xend);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // x goes out ahead of the first weights
+    }
+    // XREG, 4-bit groups: this lane's x (fp32) and the sums of its groups, for every row
+    constexpr bool kXRegQ4 = XREG && F == F_Q4;
+    uint32_t xq4[kXRegQ4 ? JS : 1][kXRegQ4 ? 16 : 1];  // bf16 pairs
+    float xsq4[kXRegQ4 ? JS : 1];
+    if constexpr (kXRegQ4) {
         const uint32_t xend = (uint32_t)(K * 2);
 #pragma unroll
         for (int j = 0; j < JS; ++j) {
@@ -359,7 +427,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
             xsq4[j] = (xs[0] + xs[1]) + (xs[2] + xs[3]);
         }
     }
-    constexpr bool kXPerItem = (F == F_INT8F || F == F_Q4);  // x travels with the items: nothing staged
+    constexpr bool kXPerItem = (F == F_INT8F || F == F_Q4);  // x travels with the items (or sits in registers): nothing staged
     u32x4 xr[kXL];
     if constexpr (!kXPerItem) {
         const uint32_t xend = (uint32_t)(K * (XT == 0 ? 4 : 2));
@@ -378,13 +446,31 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     // second item goes out before it too: at the decode shapes a wave owns
     // only one or two items, which then all stream while x is prepared
     // (measured faster there, and slower for the other staged formats).
-    constexpr bool kTwoAhead = (F == F_TERN || F == F_TERN3);
+    constexpr bool kTwoAhead = (F == F_TERN || F == F_TERN3 || F == F_INT8L);
     Item ia{wave, 0}, ib{0, 0};
-    if constexpr (kDynamic) {
+    if constexpr (kPaired) {  // the first index of each end (taken without a check)
+        ia.g = front ? (npool >= 1 ? pair : ngroups) : (npool >= 2 ? pair + 4 * (npool - 1) : ngroups);
+        issue(ia, fa, sa);
+    } else if constexpr (kDynamic) {
         issue(ia, fa, sa);
     } else {
         issue(0, fa, sa);
         if constexpr (kTwoAhead) issue(1, fb, sb);
+    }
+    if constexpr (kXRegI8) {
+        __builtin_amdgcn_sched_barrier(0);  // the first item is in flight before x is converted
+#pragma unroll
+        for (int j = 0; j < JS; ++j) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                if constexpr (XT == 0) {
+                    xf[j][q] = __uint_as_float(xraw[j][q >> 2][q & 3]);
+                } else {
+                    const uint32_t d = xraw[j][q >> 3][(q >> 1) & 3];
+                    xf[j][q] = (q & 1) ? __uint_as_float(d & 0xFFFF0000u) : bf16_to_f32(d & 0xFFFFu);
+                }
+            }
+        }
     }
 
     // piece -> fp32 values
@@ -472,6 +558,18 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
             sum_xq = wave_sum_to_lane63(sum_xq);
             if (lane == 63) redi[wave] = sum_xq;
         }
+    } else if constexpr (F == F_INT8L) {  // column 16 ch + 4 pc + e: plane pc, chunk ch, dword e (fp32)
+        float* xfl = reinterpret_cast<float*>(xs);
+        for_pieces([&](int pi, const float* v) {
+#pragma unroll
+            for (int e = 0; e < kElems; ++e) {
+                const int c = pi * kElems + e;
+                xfl[4 * (((c >> 2) & 3) * NC + (c >> 4)) + (c & 3)] = v[e];
+            }
+        });
+        const int c0 = K / 16, npad = NC - c0;  // whole padding chunks (K % 16 == 0), in all four planes
+        for (int i = tid; i < 4 * npad; i += kQThreads)
+            reinterpret_cast<u32x4*>(xs)[(i / npad) * NC + c0 + i % npad] = u32x4{0u, 0u, 0u, 0u};
     } else {  // sign + residual: pair p = q & 15 of unit u is bf16 x[32u+q] | bf16 x[32u+q+16] << 16,
               // in plane p / 4, slot u, dword p % 4
         uint16_t* xh = reinterpret_cast<uint16_t*>(xs);
@@ -488,7 +586,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
             reinterpret_cast<u32x4*>(xs)[(i / npad) * NC + c0 + i % npad] = u32x4{0u, 0u, 0u, 0u};
     }
     // x staged (and the group counter set); the prefetched weights stay in flight
-    if constexpr (kDynamic || !kXPerItem) lds_barrier();
+    if constexpr (kDynItems || !kXPerItem) lds_barrier();
     if constexpr (kDynamic) fetch_group();
     if constexpr (F == F_TERN || F == F_TERN3) {
         sum_xq = 0;
@@ -511,9 +609,20 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
 #pragma unroll
         for (int j = 0; j < JS; ++j) {
             const int c = lane + 64 * (seg * JS + j);  // < nseg * JS * 64: inside the padded LDS copy
-            if constexpr (F == F_INT8F) {
+            if constexpr (F == F_INT8F || F == F_INT8L) {
                 float xv[16];
-                if constexpr (XT == 0) {
+                if constexpr (F == F_INT8L) {
+                    const u32x4* xp = reinterpret_cast<const u32x4*>(xs) + c;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const u32x4 t = xp[q * NC];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) xv[4 * q + e] = __uint_as_float(t[e]);
+                    }
+                } else if constexpr (XREG) {
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) xv[q] = xf[j][q];
+                } else if constexpr (XT == 0) {
 #pragma unroll
                     for (int q = 0; q < 16; ++q) xv[q] = __uint_as_float(fr[0][j].x[q >> 2][q & 3]);
                 } else {
@@ -667,7 +776,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
         if (seg == nseg - 1) {
             // reduce every row of the group at once (independent DPP chains);
             // lane 63 holds the sums and writes the outputs
-            if constexpr (F == F_INT8F || kSignRes<F> || F == F_Q4) {
+            if constexpr (F == F_INT8F || F == F_INT8L || kSignRes<F> || F == F_Q4) {
                 float v[U], v2[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
@@ -683,6 +792,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
                             float o;
                             if constexpr (kSignRes<F>) o = sc[u][0] * v[u] + v2[u] / sc[u][1];
                             else if constexpr (F == F_Q4) o = v[u];  // group scales already applied
+                            else if constexpr (kRowScale) o = v[u] / sc[u][0];
                             else o = v[u] / p.scale[row];
                             if constexpr (YT == 0) static_cast<float*>(p.y)[row] = o;
                             else static_cast<uint16_t*>(p.y)[row] = (uint16_t)f32_to_bf16(o);
@@ -716,9 +826,10 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
         }
     };
 
-    if constexpr (kDynamic) {
-        // The wave's groups are increasing, so the loop ends after the first
-        // item past the last group.  Every issued item is consumed on every
+    if constexpr (kDynItems) {
+        // The loop ends after the first item past the wave's last group
+        // (the LDS counter's groups increase; a pair's ends stop once they
+        // meet).  Every issued item is consumed on every
         // path (such an item reads zeros and stores nothing): a load left
         // unused on the exit path would be sunk below the exit test by the
         // compiler, past the consumption of the item before it, which would
@@ -843,12 +954,38 @@ static hipError_t run(const QgemvArgs* a, int count, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int F, int U, int JS>
+template <int F, int U, int JS, bool XREG = false>
 static hipError_t run_xy(const QgemvArgs* a, int count, hipStream_t st) {
-    if (a[0].xt == 0 && a[0].yt == 0) return run<F, 0, 0, U, JS>(a, count, st);
-    if (a[0].xt == 0 && a[0].yt == 1) return run<F, 0, 1, U, JS>(a, count, st);
-    if (a[0].xt == 1 && a[0].yt == 0) return run<F, 1, 0, U, JS>(a, count, st);
-    return run<F, 1, 1, U, JS>(a, count, st);
+    if (a[0].xt == 0 && a[0].yt == 0) return run<F, 0, 0, U, JS, XREG>(a, count, st);
+    if (a[0].xt == 0 && a[0].yt == 1) return run<F, 0, 1, U, JS, XREG>(a, count, st);
+    if (a[0].xt == 1 && a[0].yt == 0) return run<F, 1, 0, U, JS, XREG>(a, count, st);
+    return run<F, 1, 1, U, JS, XREG>(a, count, st);
+}
+
+// int8 weights with float x.  The per-weight work is one conversion and one
+// FMA; x is converted once per launch, not per row:
+//   * rows of up to 4 chunk iterations (K <= 4096): one item spans the row,
+//     and each lane keeps the 16 fp32 activations of each of its chunks in
+//     registers (XREG), loaded before the first item;
+//   * rows of up to 12 chunk iterations (K <= 12288): x staged once per
+//     workgroup in LDS as fp32, items of 4 chunk iterations (measured on
+//     MI355X at 4096 x 11008: 10.6 us, against 11.3 us with x carried by
+//     each item and 12.2 us with one item per row), the first two out
+//     before the staging;
+//   * longer rows: each item carries its activations (bf16 or fp32) with it.
+// One row per item at the decode shapes (16-86 rows per workgroup); two rows
+// per item once a workgroup owns hundreds of rows, where the longer items
+// stream faster (measured on MI355X).
+static hipError_t run_int8_float_x(const QgemvArgs* a, int count, hipStream_t st) {
+    const int J = (int)((a[0].k / 16 + 63) / 64);  // chunk iterations per row
+    int64_t total_rows = 0;
+    for (int m = 0; m < count; ++m) total_rows += a[m].n;
+    const bool tall = total_rows >= (int64_t)256 * device_cu_count();
+    if (J <= 1) return run_xy<F_INT8F, 1, 1, true>(a, count, st);
+    if (J <= 2) return run_xy<F_INT8F, 1, 2, true>(a, count, st);
+    if (J <= 4) return tall ? run_xy<F_INT8F, 2, 4, true>(a, count, st) : run_xy<F_INT8F, 1, 4, true>(a, count, st);
+    if (J <= 12) return run_xy<F_INT8L, 1, 4>(a, count, st);
+    return tall ? run_xy<F_INT8F, 2, 4>(a, count, st) : run_xy<F_INT8F, 1, 4>(a, count, st);
 }
 
 // All entries share fmt, amode, xt, yt and k (validated by the caller).
@@ -857,15 +994,7 @@ hipError_t launch_qgemv_group(const QgemvArgs* a, int count, hipStream_t st) {
     // fastest measured on MI355X at the decode shapes (16-112 rows per
     // workgroup; two items in flight per wave).
     const QgemvArgs& h = a[0];
-    if (h.fmt == 0 && h.amode == 1) {
-        // one row per item at the decode shapes (16-86 rows per workgroup);
-        // two rows per item once a workgroup owns hundreds of rows, where
-        // the longer items stream faster (measured on MI355X)
-        int64_t total_rows = 0;
-        for (int m = 0; m < count; ++m) total_rows += a[m].n;
-        if (total_rows >= (int64_t)256 * device_cu_count()) return run_xy<F_INT8F, 2, 4>(a, count, st);
-        return run_xy<F_INT8F, 1, 4>(a, count, st);
-    }
+    if (h.fmt == 0 && h.amode == 1) return run_int8_float_x(a, count, st);
     if (h.fmt == 0 && h.amode == 0) return run_xy<F_INT8I, 2, 4>(a, count, st);
     if (h.fmt == 1) return run_xy<F_TERN, 4, 1>(a, count, st);
     if (h.fmt == 5) return run_xy<F_TERN3, 4, 1>(a, count, st);

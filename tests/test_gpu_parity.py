@@ -269,8 +269,14 @@ def test_qgemv_w8a16_decode_shapes(qg, name):
     assert np.array_equal(host(y2), yb)
 
 
-@pytest.mark.parametrize("n,k", [(8, 128), (77, 1152), (11008, 4096), (33, 32768),
-                                 (65600, 256)])  # hundreds of rows per workgroup: two-row items
+# x in registers (K <= 4096: 128, 1152, 4096; two-row items once a
+# workgroup owns 256 rows or more: 66000 x 4096), x staged in LDS as fp32
+# (4096 < K <= 12288: 5120, 8192, 11008, 12288; 13000 x 8192 puts 51 rows in
+# each workgroup, so the two ends of each SIMD's row pool meet after a dozen
+# claims), x with every item (12416, 32768); 65600 x 256: hundreds of rows
+# per workgroup on a one-chunk row
+@pytest.mark.parametrize("n,k", [(8, 128), (77, 1152), (11008, 4096), (66000, 4096), (77, 5120), (300, 8192),
+                                 (13000, 8192), (129, 12288), (40, 12416), (33, 32768), (65600, 256)])
 def test_qgemv_w8a16_small_and_edges(qg, n, k):
     note("qgemv w8a16 %dx%d" % (n, k))
     wl = synth.decode_w8a16(n=n, k=k, seed=21)
@@ -410,6 +416,28 @@ def test_qgemv_grouped_matches_single(qg, fmt):
             assert oracle.normwise_error(host(ys[i]), oracle.y_w8a16(refs[i][0], refs[i][1], xb)) <= 1e-5
         else:
             assert oracle.normwise_error(host(ys[i]), oracle.y_sign_residual(*refs[i], xb)) <= 1e-5
+
+
+@pytest.mark.parametrize("k", [11008, 1152])
+def test_qgemv_w8a16_grouped_matches_single(qg, k):
+    # a grouped launch of the W8A16 product at a K whose x is staged in LDS
+    # (11008) and one whose x sits in registers (1152): bit-identical to the
+    # single launches, and within tolerance of the oracle
+    note("qgemv w8a16 grouped k=%d" % k)
+    g = synth.rng(k)
+    Ws, refs = [], []
+    for n in (4096, 777, 1500):
+        w = synth.gaussian(g, (n, k), 0.02)
+        W, _, _ = _int8_weight(qg, w)
+        Ws.append(W)
+        refs.append(oracle.quantize_absmax(w, per_row=True))
+    xb = synth.to_bf16_bits(synth.gaussian(g, (k,), 1.0))
+    x = dev_bf16(xb)
+    ys = qg.qgemv_grouped(Ws, x, act_int8=False, y_dtype=torch.float32)
+    for i, W in enumerate(Ws):
+        y1 = qg.qgemv(W, x, act_int8=False, y_dtype=torch.float32)
+        assert np.array_equal(host(ys[i]), host(y1)), "grouped output differs from the single launch"
+        assert oracle.normwise_error(host(ys[i]), oracle.y_w8a16(refs[i][0], refs[i][1], xb)) <= 1e-5
 
 
 def test_qgemv_zero_inputs(qg):
