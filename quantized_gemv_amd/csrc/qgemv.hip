@@ -177,7 +177,11 @@ constexpr int kXL = 4;  // x pieces of 16 B held in registers per thread (K <= 1
 // c = l + 64 j (j < JS), so it loads and converts that x (and, for the 4-bit
 // groups, the groups' sums) once before the first item; the items then carry
 // weights (and super-block records) only.
-template <int F, int XT, int YT, int U, int JS, bool XREG = false>
+// NPF > 0: every item of a wave (at most NPF, which the host checks) goes
+// out in the prologue, so all of the wave's weights are in flight while x is
+// prepared and the decode work is spread over all waves (short rows, few per
+// wave: the ternary formats at the decode shapes).
+template <int F, int XT, int YT, int U, int JS, bool XREG = false, int NPF = 0>
 __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     using Frag = typename Fmt<F>::Frag;
     constexpr int kCols = Fmt<F>::kColsPerChunk;
@@ -428,18 +432,28 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
         }
     }
     constexpr bool kXPerItem = (F == F_INT8F || F == F_Q4);  // x travels with the items (or sits in registers): nothing staged
-    u32x4 xr[kXL];
+    // ternary 2-bit: a thread owns whole 16-column groups m = tid + 512 r
+    // (r < kGW in registers), so that it can write each group's codes to LDS
+    // as one 16-byte store in the byte-plane order
+    constexpr bool kGroups16 = (F == F_TERN);
+    constexpr int kPG = 16 / kElems;  // 16-byte pieces per 16-column group
+    constexpr int kGW = 2;            // groups per thread in registers (K <= 16384)
+    constexpr int kXW = kGroups16 ? kGW * kPG : kXL;
+    u32x4 xr[kXW];
     if constexpr (!kXPerItem) {
         const uint32_t xend = (uint32_t)(K * (XT == 0 ? 4 : 2));
 #pragma unroll
-        for (int l = 0; l < kXL; ++l) {
-            const int pi = tid + kQThreads * l;
+        for (int l = 0; l < kXW; ++l) {
+            const int pi = kGroups16 ? kPG * (tid + kQThreads * (l / kPG)) + l % kPG : tid + kQThreads * l;
             xr[l] = load16(rx, pi < npieces ? (uint32_t)(16 * pi) : xend);
         }
         __builtin_amdgcn_sched_barrier(0);  // x goes out ahead of the first weights
     }
     Frag fa[U][JS], fb[U][JS];
     float sa[U][2] = {}, sb[U][2] = {};  // the items' row scales
+    constexpr int kNP = NPF > 0 ? NPF : 1;
+    Frag fp[kNP][U][JS];   // NPF: every item of the wave
+    float sp[kNP][U][2] = {};
     // unconditional, like the x loads: a wave without rows reads zeros (its
     // offsets are out of range) and never consumes them.  For the ternary
     // formats, whose x prologue is a quantization with a workgroup max, the
@@ -448,7 +462,11 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     // (measured faster there, and slower for the other staged formats).
     constexpr bool kTwoAhead = (F == F_TERN || F == F_TERN3 || F == F_INT8L);
     Item ia{wave, 0}, ib{0, 0};
-    if constexpr (kPaired) {  // the first index of each end (taken without a check)
+    if constexpr (NPF > 0) {
+        static_assert(!kDynItems, "prefetch-all takes the fixed share");
+#pragma unroll
+        for (int i = 0; i < NPF; ++i) issue(i, fp[i], sp[i]);  // items past nit read zeros
+    } else if constexpr (kPaired) {  // the first index of each end (taken without a check)
         ia.g = front ? (npool >= 1 ? pair : ngroups) : (npool >= 2 ? pair + 4 * (npool - 1) : ngroups);
         issue(ia, fa, sa);
     } else if constexpr (kDynamic) {
@@ -513,6 +531,79 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
     int sum_xq = 0;   // sum of int8 activations (ternary offset correction)
     if constexpr (kXPerItem) {
         // nothing to stage: every item carries its own slice of x
+    } else if constexpr (kGroups16) {
+        // 16-column groups m: codes of columns 16 m + 4 b + f go to byte b of
+        // dword f of slot (m % 4, m / 4), i.e. chunk m / 4, plane m % 4 (the
+        // byte-plane order of the 2-bit decode); one 16-byte LDS store each
+        const int ngr = K / 16;  // K % 64 == 0
+        auto group_vals = [&](const u32x4* pc, float v[16]) {
+#pragma unroll
+            for (int q = 0; q < kPG; ++q) piece_vals(pc[q], v + q * kElems);
+        };
+        auto load_group = [&](int mg, u32x4* pc) {
+#pragma unroll
+            for (int q = 0; q < kPG; ++q) pc[q] = load16(rx, (uint32_t)(16 * (kPG * mg + q)));
+        };
+        float m = 0.0f;
+#pragma unroll
+        for (int r = 0; r < kGW; ++r) {  // unconditional: groups past K hold zeros
+            float v[16];
+            group_vals(xr + r * kPG, v);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
+        }
+        for (int mg = tid + kQThreads * kGW; mg < ngr; mg += kQThreads) {  // past the register window
+            u32x4 pc[kPG];
+            load_group(mg, pc);
+            float v[16];
+            group_vals(pc, v);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
+        }
+        m = wave_max_to_lane63(m);
+        if (lane == 63) redf[wave] = m;
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < kQWaves; ++i) m = __builtin_fmaxf(m, redf[i]);
+        sx = absmax_scale(m);
+        auto put_group = [&](int mg, const float* v) {
+            u32x4 d;
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int q = qcode(v[4 * b + f], sx);
+                    sum_xq += q;
+                    w |= (uint32_t)(q & 0xFF) << (8 * b);
+                }
+                d[f] = w;
+            }
+            reinterpret_cast<u32x4*>(xs)[(mg & 3) * NC + (mg >> 2)] = d;
+        };
+#pragma unroll
+        for (int r = 0; r < kGW; ++r) {
+            const int mg = tid + kQThreads * r;
+            if (mg < ngr) {
+                float v[16];
+                group_vals(xr + r * kPG, v);
+                put_group(mg, v);
+            }
+        }
+        for (int mg = tid + kQThreads * kGW; mg < ngr; mg += kQThreads) {
+            u32x4 pc[kPG];
+            load_group(mg, pc);
+            float v[16];
+            group_vals(pc, v);
+            put_group(mg, v);
+        }
+        {  // whole padding chunks (K % 64 == 0), in all four planes
+            const int c0 = K / 64, npad = NC - c0;
+            for (int i = tid; i < 4 * npad; i += kQThreads)
+                reinterpret_cast<u32x4*>(xs)[(i / npad) * NC + c0 + i % npad] = u32x4{0u, 0u, 0u, 0u};
+        }
+        sum_xq = wave_sum_to_lane63(sum_xq);  // per-wave partials, summed after the staging barrier
+        if (lane == 63) redi[wave] = sum_xq;
     } else if constexpr (F == F_INT8I || F == F_TERN || F == F_TERN3) {
         float m = 0.0f;
         for_pieces(
@@ -594,6 +685,11 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
         for (int i = 0; i < kQWaves; ++i) sum_xq += redi[i];
     }
 
+    // ternary 2-bit with every item in flight: each row's int32 total is
+    // kept (wave-uniform) and the rows of the wave are rescaled and stored
+    // together after the last item, one row per lane
+    constexpr bool kBatchRows = (NPF > 0 && F == F_TERN);
+    int rsum[kBatchRows ? NPF : 1][U];
     float accf[U], accf2[U];
     int acc1[U], acc4[U], acc16[U];
 #pragma unroll
@@ -806,7 +902,11 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
                     if constexpr (F == F_TERN) v[u] = wave_sum_to_lane63(acc1[u] + (acc4[u] >> 2) + (acc16[u] >> 4));
                     else v[u] = wave_sum_to_lane63(acc1[u]);
                 }
-                if (lane == 63) {
+                if constexpr (kBatchRows) {
+                    static_assert(std::is_integral_v<std::decay_t<decltype(x)>>, "fixed share");
+#pragma unroll
+                    for (int u = 0; u < U; ++u) rsum[(int)x][u] = __builtin_amdgcn_readlane(v[u], 63);
+                } else if (lane == 63) {
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const int r = g * U + u;
@@ -814,7 +914,7 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
                             const int row = row0 + r;
                             const int a = (F == F_TERN || F == F_TERN3) ? v[u] - sum_xq : v[u];
                             float o;
-                            if constexpr (F == F_TERN || F == F_TERN3) o = (float)a * p.scale[0] / sx;
+                            if constexpr (F == F_TERN || F == F_TERN3) o = (float)a * (p.scale[0] / sx);
                             else o = (float)a / (p.scale[row] * sx);
                             if (p.acc_out) p.acc_out[row] = a;
                             if constexpr (YT == 0) static_cast<float*>(p.y)[row] = o;
@@ -826,7 +926,33 @@ __global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
         }
     };
 
-    if constexpr (kDynItems) {
+    if constexpr (NPF > 0) {
+#pragma unroll
+        for (int i = 0; i < NPF; ++i)
+            if (i < nit) consume(i, fp[i], sp[i]);
+        if constexpr (kBatchRows) {
+            // lane j = U * (group ordinal) + u takes that row's total
+            int a = 0;
+#pragma unroll
+            for (int i = 0; i < NPF; ++i) {
+                if (i < nit && i % nseg == nseg - 1) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) a = (lane == U * (i / nseg) + u) ? rsum[i][u] : a;
+                }
+            }
+            const float gs = p.scale[0] / sx;  // gamma / s_x
+            const int gi = lane / U, u = lane % U;
+            const int r = (wave + kQWaves * gi) * U + u;
+            if (gi < my_groups && r < rows) {
+                const int t = a - sum_xq;
+                const int row = row0 + r;
+                if (p.acc_out) p.acc_out[row] = t;
+                const float o = (float)t * gs;
+                if constexpr (YT == 0) static_cast<float*>(p.y)[row] = o;
+                else static_cast<uint16_t*>(p.y)[row] = (uint16_t)f32_to_bf16(o);
+            }
+        }
+    } else if constexpr (kDynItems) {
         // The loop ends after the first item past the wave's last group
         // (the LDS counter's groups increase; a pair's ends stop once they
         // meet).  Every issued item is consumed on every
@@ -901,7 +1027,23 @@ int device_cu_count() {
     return cached[dev];
 }
 
-template <int F, int XT, int YT, int U, int JS, bool XREG = false>
+// Rows per workgroup of matrix m of a launch: workgroups are handed out per
+// matrix in proportion to its rows (about one per CU in all), each owning a
+// contiguous block of rows; `cap` keeps buffer ranges below 2 GiB.
+static int64_t rows_per_wg(const QgemvArgs* a, int count, int m, int64_t cap) {
+    const int cus = device_cu_count();
+    int64_t total_rows = 0;
+    for (int i = 0; i < count; ++i) total_rows += a[i].n;
+    const int64_t N = a[m].n;
+    int64_t share = (cus * N + total_rows / 2) / total_rows;  // workgroups for this matrix
+    if (share < 1) share = 1;
+    int64_t rpw = (N + share - 1) / share;
+    if (rpw > cap) rpw = cap;
+    if (rpw < 1) rpw = 1;
+    return rpw;
+}
+
+template <int F, int XT, int YT, int U, int JS, bool XREG = false, int NPF = 0>
 static hipError_t run(const QgemvArgs* a, int count, hipStream_t st) {
     constexpr int kCols = Fmt<F>::kColsPerChunk;
     const int K = (int)a[0].k;
@@ -913,18 +1055,15 @@ static hipError_t run(const QgemvArgs* a, int count, hipStream_t st) {
     const int64_t rowB = (F == F_TERN) ? K / 4 : kSignRes<F> ? K / 8 : (F == F_Q4) ? K / 2 : (F == F_TERN3) ? 16 * C : K;
     const int64_t resB = kSignRes<F> ? K : (F == F_Q4) ? K / 16 : 0;
     const int64_t cap = ((int64_t)1 << 31) / (rowB > resB ? rowB : resB);  // buffer ranges stay below 2 GiB
-    const int cus = device_cu_count();
-    int64_t total_rows = 0;
-    for (int m = 0; m < count; ++m) total_rows += a[m].n;
     KGroup g;
     int wgx = 1;  // grid: (workgroups of the largest matrix) x (matrices)
     for (int m = 0; m < count; ++m) {
         const int64_t N = a[m].n;
-        int64_t share = (cus * N + total_rows / 2) / total_rows;  // workgroups for this matrix
-        if (share < 1) share = 1;
-        int64_t rpw = (N + share - 1) / share;
-        if (rpw > cap) rpw = cap;
-        if (rpw < 1) rpw = 1;
+        const int64_t rpw = rows_per_wg(a, count, m, cap);
+        if (NPF > 0) {  // every item of every wave must fit the prefetch
+            const int64_t groups = (rpw + U - 1) / U;
+            if (((groups + kQWaves - 1) / kQWaves) * nseg > NPF) return hipErrorInvalidValue;
+        }
         KParams& p = g.mats[m];
         p.codes = static_cast<const uint8_t*>(a[m].codes);
         p.resid = a[m].resid;
@@ -940,7 +1079,7 @@ static hipError_t run(const QgemvArgs* a, int count, hipStream_t st) {
         const int nwg = (int)((N + rpw - 1) / rpw);
         if (nwg > wgx) wgx = nwg;
     }
-    auto kern = qgemv_kernel<F, XT, YT, U, JS, XREG>;
+    auto kern = qgemv_kernel<F, XT, YT, U, JS, XREG, NPF>;
     if (lds > 64 * 1024) {
         static bool attr_set = false;  // per instantiation
         if (!attr_set) {
@@ -954,12 +1093,12 @@ static hipError_t run(const QgemvArgs* a, int count, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int F, int U, int JS, bool XREG = false>
+template <int F, int U, int JS, bool XREG = false, int NPF = 0>
 static hipError_t run_xy(const QgemvArgs* a, int count, hipStream_t st) {
-    if (a[0].xt == 0 && a[0].yt == 0) return run<F, 0, 0, U, JS, XREG>(a, count, st);
-    if (a[0].xt == 0 && a[0].yt == 1) return run<F, 0, 1, U, JS, XREG>(a, count, st);
-    if (a[0].xt == 1 && a[0].yt == 0) return run<F, 1, 0, U, JS, XREG>(a, count, st);
-    return run<F, 1, 1, U, JS, XREG>(a, count, st);
+    if (a[0].xt == 0 && a[0].yt == 0) return run<F, 0, 0, U, JS, XREG, NPF>(a, count, st);
+    if (a[0].xt == 0 && a[0].yt == 1) return run<F, 0, 1, U, JS, XREG, NPF>(a, count, st);
+    if (a[0].xt == 1 && a[0].yt == 0) return run<F, 1, 0, U, JS, XREG, NPF>(a, count, st);
+    return run<F, 1, 1, U, JS, XREG, NPF>(a, count, st);
 }
 
 // int8 weights with float x.  The per-weight work is one conversion and one
@@ -996,7 +1135,21 @@ hipError_t launch_qgemv_group(const QgemvArgs* a, int count, hipStream_t st) {
     const QgemvArgs& h = a[0];
     if (h.fmt == 0 && h.amode == 1) return run_int8_float_x(a, count, st);
     if (h.fmt == 0 && h.amode == 0) return run_xy<F_INT8I, 2, 4>(a, count, st);
-    if (h.fmt == 1) return run_xy<F_TERN, 4, 1>(a, count, st);
+    if (h.fmt == 1) {
+        // short packed rows (K / 4 bytes): one or two rows per item, every item
+        // of a wave out in the prologue when each wave has at most 8; else
+        // four-row items, two in flight
+        const int64_t J = (h.k / 64 + 63) / 64;  // chunk iterations per row
+        int64_t rpw = 1;
+        for (int m = 0; m < count; ++m) {
+            const int64_t r = rows_per_wg(a, count, m, (int64_t)1 << 40);
+            if (r > rpw) rpw = r;
+        }
+        auto per_wave = [&](int64_t u) { return ((rpw + u - 1) / u + kQWaves - 1) / kQWaves * J; };
+        if (per_wave(1) <= 8) return run_xy<F_TERN, 1, 1, false, 8>(a, count, st);
+        if (per_wave(2) <= 8) return run_xy<F_TERN, 2, 1, false, 8>(a, count, st);
+        return run_xy<F_TERN, 4, 1>(a, count, st);
+    }
     if (h.fmt == 5) return run_xy<F_TERN3, 4, 1>(a, count, st);
     if (h.fmt == 3) {  // bf16 activations only
         const bool spans = (h.k / 32 + 63) / 64 <= 2;  // one item of 2 chunk iterations covers the row

@@ -320,7 +320,12 @@ def _ternary_case(qg, n, k, seed=3, x_bf16=False):
     assert canaries_intact(acc_full, n) and canaries_intact(y_full, n)
 
 
-@pytest.mark.parametrize("n,k", [(1, 128), (13, 384), (300, 4096), (11008, 4096), (40, 32768)])
+# one-row items with every item in flight (300, 11008 and 4096 rows; K =
+# 11008 keeps x in two 16-column groups per thread, K = 32768 quantizes the
+# groups past that window in a second pass), two-row items (30000 x 4096)
+# and four-row items two at a time (40000 x 1024)
+@pytest.mark.parametrize("n,k", [(1, 128), (13, 384), (300, 4096), (11008, 4096), (4096, 11008), (30000, 4096),
+                                 (40000, 1024), (40, 32768)])
 def test_qgemv_ternary(qg, n, k):
     note("qgemv ternary %dx%d" % (n, k))
     _ternary_case(qg, n, k)
