@@ -10,20 +10,30 @@ grouped launch, so a layer is 4 launches -- (q,k,v), o, (gate,up), down --
 and the step's 128 launches are captured once in a HIP graph and replayed.
 `value` = weight bytes streamed per second.
 
-Also measured (in the same JSON line): each workload of the suite on its
-own (tiny W8A8, the three decode shapes, ternary, sign + residual, W8A8
-prefill GEMM with outlier split), the roofline of the dominant kernel and the
-CPU oracle's throughput on a bounded sample of the same workload.
+Also measured (in the same JSON line): the on-box streaming-read ceiling
+(qg_probe_stream_read on 4 GiB, and the step's own launch sizes as pure
+reads); each workload of the suite on its own (tiny W8A8, the three decode
+shapes, ternary, base-3 ternary, 4-bit groups, sign + residual with and
+without zero-points, thresholded separated weights, small batches, the W8A8
+prefill GEMM with outlier split, the MXFP4 prefill, outlier detection); the
+same 32-layer step with ternary, sign + residual and thresholded weights;
+the roofline of the dominant kernel; and the CPU oracle's throughput on a
+bounded sample of the headline workload plus its seconds on each of the five
+workloads.
 
-HBM traffic (roofline "traffic") comes from two rocprofv3 --pmc passes over
-`--profile-workload` (FETCH_SIZE, then WRITE_SIZE), turned into
-profiles/hbm_traffic_counters.json by `--summarize-counters`; the figures are
-used only while the kernel sources still hash to the values recorded there.
+Recorded profiles (used only while the kernel sources hash as recorded):
+  * kernel durations per config (rocprof median / p10 / p90): a rocprofv3
+    --kernel-trace run of `bench.py --mark-configs ORDER`, whose separator
+    launches split the trace into configs, then `--summarize-trace`;
+  * HBM traffic and other counters per config: rocprofv3 --pmc passes over
+    `--profile-workload` (FETCH_SIZE, then WRITE_SIZE, then MFMA counters),
+    then `--summarize-counters`.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
-                       [--no-cpu-baseline] [--only-headline]
-       python bench.py --profile-workload
-       python bench.py --summarize-counters FETCH_DIR WRITE_DIR
+                       [--no-cpu-baseline] [--only-headline] [--mark-configs ORDER]
+       python bench.py --profile-workload [--mark-configs ORDER]
+       python bench.py --summarize-trace TRACE_DIR ORDER
+       python bench.py --summarize-counters ORDER PMC_DIR [PMC_DIR ...]
 """
 from __future__ import annotations
 
@@ -44,14 +54,15 @@ FP4_MFMA_PEAK_TFLOPS = 10100.0   # MI355X dense FP4 (MXFP4) MFMA, TFLOP/s
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
 CSRC = os.path.join(ROOT, "quantized_gemv_amd", "csrc")
 # sources whose hash keys the recorded counters of each kernel
-KERNEL_SOURCES = {
+KERNEL_SOURCES = {  # the recorded counters and durations hold while these hash as recorded
     "qgemv": ("qgemv.hip", "qg_device.h", "qg_launch.h"),
     "qgemm": ("qgemm.hip", "qg_gemm.h", "qg_device.h", "qg_launch.h"),
     "sepq": ("sepq.hip", "qg_device.h", "qg_launch.h"),
+    "batch": ("qgemv_batch.hip", "qg_gemm.h", "qg_device.h", "qg_launch.h"),
+    "mx": ("mx.hip", "qg_gemm.h", "qg_device.h", "qg_launch.h"),
+    "quantize": ("quantize.hip", "exact_mean.h", "qg_device.h", "qg_launch.h"),
 }
-KERNEL_NAME_KEYS = {"qgemv": "qg::qgemv_kernel", "qgemm": "qgemm_w8a8_kernel", "sepq": "sep_qgemv_kernel"}
 COPY_BYTES = 256 << 20           # calibration copy: bytes read and bytes written
-COPY_REPS = 2                    # calibration copies: the first copy dispatches of the profiled run
 
 
 def parse():
@@ -65,16 +76,42 @@ def parse():
     ap.add_argument("--profile-workload", action="store_true",
                     help="run the calibration copy, 2 decode steps and 2 prefill calls, then exit "
                          "(the workload of the rocprofv3 --pmc passes)")
-    ap.add_argument("--hashes-out", metavar="PATH",
-                    help="with --profile-workload: write the kernel source hashes the run used to PATH")
-    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "HASHES"),
-                    help="turn the two rocprofv3 --pmc output folders (and the hashes written by the "
-                         "profiled runs) into " + os.path.relpath(COUNTERS_FILE, ROOT))
+    ap.add_argument("--mark-configs", metavar="ORDER_JSON",
+                    help="launch a separator kernel before each timed config and write the config order to "
+                         "ORDER_JSON (for a rocprofv3 --kernel-trace run of the bench)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "ORDER_JSON"),
+                    help="turn the kernel trace of a --mark-configs run into per-config kernel durations "
+                         "(median, p10, p90) in " + os.path.relpath(os.path.join(ROOT, "profiles", "kernel_durations.json"), ROOT))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="ORDER_JSON_THEN_PMC_DIRS",
+                    help="ORDER_JSON of a --profile-workload run, then the rocprofv3 --pmc output folders of its "
+                         "passes: per-config counter means (and HBM bytes from FETCH_SIZE / WRITE_SIZE) into "
+                         + os.path.relpath(COUNTERS_FILE, ROOT))
     return ap.parse_args()
 
 
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+# --mark-configs: a separator launch (the per-tensor absmax quantizer on 8
+# values) before each timed config, so that a rocprofv3 kernel trace of the
+# run splits into configs; the order is written next to the trace
+MARKS = None
+
+
+def mark(torch, qg, name):
+    if MARKS is None:
+        return
+    import ctypes
+    x = MARKS["x"]
+    st = qg.lib().qg_quantize_absmax_noalloc(ctypes.c_void_p(x.data_ptr()), qg.QG_F32, 1, 8, qg.QG_PER_TENSOR,
+                                             ctypes.c_void_p(MARKS["q"].data_ptr()),
+                                             ctypes.c_void_p(MARKS["s"].data_ptr()),
+                                             ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if st != 0:
+        raise RuntimeError("separator launch failed: %s" % qg.status_str(st))
+    torch.cuda.synchronize()
+    MARKS["order"].append(name)
 
 
 def src_hash(kernel):
@@ -83,20 +120,6 @@ def src_hash(kernel):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
-
-
-def recorded_traffic(kernel):
-    """HBM bytes per launch from the recorded counters, or None when they are
-    missing or were taken on other kernel sources."""
-    try:
-        with open(COUNTERS_FILE) as f:
-            cnt = json.load(f)
-        rec = cnt["kernels"][kernel]
-        if rec.get("src_sha256_16") == src_hash(kernel):
-            return rec.get("hbm_bytes_per_launch")
-    except (OSError, ValueError, KeyError, TypeError):
-        pass
-    return None
 
 
 class Timed:
@@ -169,8 +192,10 @@ def build_headline(torch, qg, synth, dev, L):
             launches.append(gl.launch)
     step_bytes = sum(W.n * W.k + 4 * W.n for _, W, _ in weights)  # int8 codes + fp32 per-row scales
     act_bytes = sum(2 * (W.k + W.n) for _, W, _ in weights)       # bf16 x read + y written
+    launch_bytes = [sum(weights[li * len(layer_plan) + i][1].n * weights[li * len(layer_plan) + i][1].k
+                        for i in grp) for li in range(L) for grp in groups_per_layer]
     return dict(weights=weights, xs=xs, ys=ys, y_proj=y_proj, launches=launches, keep=keep,
-                step_bytes=step_bytes, act_bytes=act_bytes)
+                step_bytes=step_bytes, act_bytes=act_bytes, launch_bytes=launch_bytes)
 
 
 def build_prefill(torch, qg, synth, dev, cur_stream):
@@ -227,9 +252,13 @@ def build_prefill(torch, qg, synth, dev, cur_stream):
 
 
 def profile_workload(args):
-    """Fixed workload for the rocprofv3 --pmc passes: a device copy of known
-    size (the calibration), two decode steps, two prefill calls and two
-    thresholded separated products."""
+    """Fixed workload for the rocprofv3 --pmc passes, in segments started by
+    the separator launch (see mark()): two 256 MiB device copies (the
+    calibration of FETCH_SIZE / WRITE_SIZE), then two runs of each kernel
+    the bench reports: the W8A16 decode step, the prefill call, the MXFP4
+    GEMM, the thresholded, sign + residual, ternary and 4-bit products, the
+    small-batch step, and the ternary and sign + residual decode steps.
+    Launches are eager (no graphs)."""
     import torch
     import quantized_gemv_amd as qg
     import synth
@@ -237,103 +266,287 @@ def profile_workload(args):
     torch.cuda.set_device(0)
     qg.lib()
     dev = torch.device("cuda:0")
+    global MARKS
+    MARKS = {"x": torch.zeros(8, device=dev), "q": torch.empty(8, dtype=torch.int8, device=dev),
+             "s": torch.empty(1, device=dev), "order": []}
 
     def cur_stream():
         return torch.cuda.current_stream().cuda_stream
+
+    def twice(name, fs):
+        mark(torch, qg, name)
+        for _ in range(2):
+            for f in fs:
+                f()
+        torch.cuda.synchronize()
+        mark(torch, qg, "setup")  # what runs until the next profiled config
     src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    for _ in range(COPY_REPS):  # before any other copy of the process
-        dst.copy_(src)
-    torch.cuda.synchronize()
+    twice("calibration_copy", [lambda: dst.copy_(src)])
     del src, dst
     h = build_headline(torch, qg, synth, dev, args.layers)
-    for _ in range(2):
-        for f in h["launches"]:
-            f()
-    torch.cuda.synchronize()
-    del h
+    twice("decode_step_w8a16", h["launches"])
+    xb = {k: torch.randn(16, k, device=dev).to(torch.bfloat16) for k in (4096, 11008)}
+    ybs = [torch.empty((16, W.n), dtype=torch.bfloat16, device=dev) for _, W, _ in h["weights"][:7]]
+    batch_launches = []
+    for li in range(args.layers):
+        for grp in [[0, 1, 2], [3], [4, 5], [6]]:
+            ws_ = [h["weights"][li * 7 + i][1] for i in grp]
+            yy = [ybs[i] for i in grp]
+            batch_launches.append((lambda ws_, yy: (lambda: qg.qgemv_batch_grouped(ws_, xb[ws_[0].k], ys=yy)))(ws_, yy))
+    twice("small_batch_decode_step_m16", batch_launches)
+    del h, xb
     torch.cuda.empty_cache()
     full, _, _, _ = build_prefill(torch, qg, synth, dev, cur_stream)
-    for _ in range(2):
-        full()
-    torch.cuda.synchronize()
+    twice("prefill_w8a8_outlier", [full])
     del full
+    wl = synth.prefill_outlier()
+    xpf = torch.from_numpy(wl.tensors["x_bf16"]).to(dev).view(torch.bfloat16)
+    wc, wsc = qg.quantize_mxfp4(torch.from_numpy(wl.tensors["w"]).to(dev))
+    xc, xsc = qg.quantize_mxfp4(xpf)
+    ypf = torch.empty((xpf.shape[0], wc.shape[0]), dtype=torch.float32, device=dev)
+    twice("prefill_mxfp4", [lambda: qg.gemm_mxfp4(xc, xsc, wc, wsc, y=ypf)])
+    del wl, xpf, wc, wsc, xc, xsc, ypf
     torch.cuda.empty_cache()
     wl = synth.sign_residual_decode()
-    sw = qg.split_sep_threshold(torch.from_numpy(wl.tensors["w"]).to(dev), 80, 50)
+    wdev = torch.from_numpy(wl.tensors["w"]).to(dev)
     xs = torch.from_numpy(wl.tensors["x_bf16"]).to(dev).view(torch.bfloat16)
-    for _ in range(2):
-        qg.qgemv_sep(sw, xs)
-    torch.cuda.synchronize()
-    if args.hashes_out:
-        with open(args.hashes_out, "w") as f:
-            json.dump({k: src_hash(k) for k in KERNEL_SOURCES}, f)
-    log("profile workload done")
+    sw = qg.split_sep_threshold(wdev, 80, 50)
+    twice("sep_threshold_28672x8192", [lambda: qg.qgemv_sep(sw, xs)])
+    del sw
+    sign, alpha, rq, s_r = qg.split_sign_residual(wdev)
+    Wsr = qg.QWeight(qg.QG_WFMT_SIGN1_RES8, 28672, 8192, qg.pack(sign, 1), alpha, resid=rq, scale2=s_r)
+    del sign, wdev
+    twice("sign1_res8_28672x8192", [lambda: qg.qgemv(Wsr, xs, act_int8=False, y_dtype=torch.bfloat16)])
+    del Wsr, rq
+    torch.cuda.empty_cache()
+    wl = synth.ternary_decode()
+    q, gamma = qg.quantize_ternary(torch.from_numpy(wl.tensors["w"]).to(dev))
+    Wt = qg.QWeight(qg.QG_WFMT_TERNARY2, 11008, 4096, qg.pack(q, 2), gamma)
+    xt = torch.from_numpy(wl.tensors["x"]).to(dev)
+    twice("ternary_11008x4096", [lambda: qg.qgemv(Wt, xt, act_int8=True)])
+    del q, Wt
+    wl = synth.q4_decode()
+    codes, meta = qg.quantize_q4k(torch.from_numpy(wl.tensors["w"]).to(dev))
+    Wq4 = qg.QWeight(qg.QG_WFMT_Q4K, 11008, 4096, codes, None, resid=meta)
+    xq4 = torch.from_numpy(wl.tensors["x_bf16"]).to(dev).view(torch.bfloat16)
+    twice("q4k_w4a16_11008x4096", [lambda: qg.qgemv(Wq4, xq4, act_int8=False, y_dtype=torch.bfloat16)])
+    del codes, meta, Wq4
+    torch.cuda.empty_cache()
+    for fmt in ("ternary2", "sign1_res8"):
+        launches, _, keep, _ = build_format_step(torch, qg, synth, dev, args.layers, fmt)
+        twice("decode_step_" + fmt, launches)
+        del launches, keep
+        torch.cuda.empty_cache()
+    order = args.mark_configs or os.path.join(ROOT, "gpurun_out", "profile_order.json")
+    with open(order, "w") as f:
+        json.dump({"configs": MARKS["order"], "hashes": {k: src_hash(k) for k in KERNEL_SOURCES},
+                   "command": "python bench.py " + " ".join(sys.argv[1:])}, f, indent=1)
+    log("profile workload done (%d segments, order in %s)" % (len(MARKS["order"]), order))
 
 
-def _counter_rows(folder, counter):
-    """[(dispatch id, kernel name, value)] of one counter from a rocprofv3
-    --pmc csv folder, in dispatch order."""
+def _segments(rows, order_json):
+    """Split (dispatch id, kernel, record) rows, in dispatch order, at the
+    separator launches; returns [(config, [(kernel, record)])]."""
+    with open(order_json) as f:
+        order = json.load(f)
+    segs, cur = [], None
+    for _, name, rec in sorted(rows, key=lambda r: r[0]):
+        if SEPARATOR_KERNEL in name:
+            cur = []
+            segs.append(cur)
+        elif cur is not None and "absmax_apply_kernel" not in name:
+            cur.append((name, rec))
+    if len(segs) != len(order["configs"]):
+        raise SystemExit("%d separators, %d configs in %s" % (len(segs), len(order["configs"]), order_json))
+    return list(zip(order["configs"], segs)), order
+
+
+def summarize_counters(order_json, dirs):
+    """Per config and kernel, the mean of every counter collected in the
+    rocprofv3 --pmc output folders `dirs` (one pass each) of a
+    --profile-workload run.  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are
+    scaled to bytes by what they read for the calibration copies (256 MiB read
+    and written each)."""
     import csv
     import glob
-    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    per = {}  # config -> kernel -> counter -> [values]
+    order = None
+    for d in dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit("no *counter_collection.csv under %s" % d)
+        disp = {}
+        for fn in files:
+            with open(fn) as f:
+                for r in csv.DictReader(f):
+                    did = int(r["Dispatch_Id"])
+                    e = disp.setdefault(did, [r["Kernel_Name"], {}])
+                    e[1][r["Counter_Name"]] = e[1].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        segs, order = _segments([(did, v[0], v[1]) for did, v in disp.items()], order_json)
+        for cfg, recs in segs:
+            for name, cnt in recs:
+                k = per.setdefault(cfg, {}).setdefault(name, {})
+                for c, v in cnt.items():
+                    k.setdefault(c, []).append(v)
+    # the calibration segment holds exactly the two 256 MiB copies (the
+    # runtime may split each into several copy dispatches)
+    cal = per.get("calibration_copy", {})
+    fk = sum(v for c in cal.values() for v in c.get("FETCH_SIZE", []))
+    wk = sum(v for c in cal.values() for v in c.get("WRITE_SIZE", []))
+    f_fetch = 2 * COPY_BYTES / (fk * 1024.0) if fk else None
+    f_write = 2 * COPY_BYTES / (wk * 1024.0) if wk else None
+    out = {"source_hashes": order["hashes"], "command": order.get("command", ""),
+           "calibration": {"copies": 2, "bytes_read_each": COPY_BYTES, "bytes_written_each": COPY_BYTES,
+                           "fetch_kib_total": round(fk, 1), "write_kib_total": round(wk, 1),
+                           "fetch_scale": f_fetch and round(f_fetch, 4), "write_scale": f_write and round(f_write, 4)},
+           "configs": {}}
+    for cfg, ks in per.items():
+        if cfg in ("calibration_copy", "setup"):
+            continue
+        rec = {}
+        for name, cnt in ks.items():
+            if "copyBuffer" in name or "FillFunctor" in name or "elementwise" in name:
+                continue
+            r = {"dispatches": max(len(v) for v in cnt.values())}
+            for c, v in sorted(cnt.items()):
+                r[c] = round(sum(v) / len(v), 1)
+            if "FETCH_SIZE" in r and "WRITE_SIZE" in r and f_fetch and f_write:
+                r["hbm_bytes_per_dispatch"] = round(r["FETCH_SIZE"] * 1024.0 * f_fetch + r["WRITE_SIZE"] * 1024.0 * f_write)
+            rec[name[:160]] = r
+        out["configs"][cfg] = rec
+    with open(COUNTERS_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    cols = ["FETCH_SIZE", "WRITE_SIZE", "hbm_bytes_per_dispatch", "SQ_INSTS_VALU_MFMA_MOPS_I8",
+            "SQ_INSTS_VALU_MFMA_MOPS_F6F4", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU",
+            "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES"]
+    md = ["# Counters per bench config (rocprofv3 --pmc over `bench.py --profile-workload`)", "",
+          "Command of the profiled workload: `%s`" % out["command"], "",
+          "Calibration: %s" % json.dumps(out["calibration"]), "",
+          "| config | kernel | dispatches | " + " | ".join(cols) + " |", "|---|---|---|" + "---|" * len(cols)]
+    for cfg, ks in out["configs"].items():
+        for name, r in ks.items():
+            md.append("| %s | `%s` | %d | " % (cfg, name[:80], r["dispatches"]) +
+                      " | ".join(str(r.get(c, "")) for c in cols) + " |")
+    with open(COUNTERS_FILE[:-5] + ".md", "w") as f:
+        f.write("\n".join(md) + "\n")
+    print("\n".join(md[:6]))
+
+
+def recorded_traffic(cfg, key="qgemv_kernel"):
+    """HBM bytes per dispatch of one config's kernels (those whose name holds
+    `key`, averaged over their dispatches) from the recorded counters, or None
+    when missing or taken on other kernel sources."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            cnt = json.load(f)
+        if any(cnt["source_hashes"].get(k) != src_hash(k) for k in KERNEL_SOURCES):
+            return None
+        tot = n = 0
+        for name, r in cnt["configs"][cfg].items():
+            if key in name and "hbm_bytes_per_dispatch" in r and "absmax" not in name:
+                tot += r["hbm_bytes_per_dispatch"] * r["dispatches"]
+                n += r["dispatches"]
+        return round(tot / n) if n else None
+    except (OSError, ValueError, KeyError, TypeError, AttributeError):
+        return None
+
+
+DURATIONS_FILE = os.path.join(ROOT, "profiles", "kernel_durations.json")
+SEPARATOR_KERNEL = "absmax_partial_kernel"
+
+
+def summarize_trace(trace_dir, order_json):
+    """Per-config kernel durations from a rocprofv3 kernel trace of a
+    --mark-configs run: the dispatches between two separator launches belong
+    to the config named in the order file; for every kernel with at least 10
+    dispatches there, the median, p10, p90 and mean duration."""
+    import csv
+    import glob
+    import numpy as np
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
     if not files:
-        raise SystemExit("no *counter_collection.csv under %s" % folder)
+        raise SystemExit("no *kernel_trace.csv under %s" % trace_dir)
     rows = []
     for fn in files:
         with open(fn) as f:
             for r in csv.DictReader(f):
-                if r["Counter_Name"] == counter:
-                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
     rows.sort()
-    return rows
-
-
-def summarize_counters(fetch_dir, write_dir, hashes_path):
-    """Scale the qgemv / qgemm FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by
-    what the same counters read for the calibration copy, and record them
-    under the source hashes of the kernels the profiled run executed."""
-    with open(hashes_path) as f:
-        hashes = json.load(f)
-    fetch = _counter_rows(fetch_dir, "FETCH_SIZE")
-    write = _counter_rows(write_dir, "WRITE_SIZE")
-
-    def calibration(rows):
-        cps = [r for r in rows if "copyBuffer" in r[1]][:COPY_REPS]
-        if len(cps) < COPY_REPS:
-            raise SystemExit("calibration copies not found")
-        return cps[0][1], sum(v for _, _, v in cps) / len(cps)
-
-    def kernel_mean(rows, key):
-        vals = [(name, v) for _, name, v in rows if key in name]
-        if not vals:
-            raise SystemExit("no dispatch of a kernel matching %r" % key)
-        return sum(v for _, v in vals) / len(vals), len(vals), sorted({name for name, _ in vals})
-    ck, cf = calibration(fetch)
-    _, cw = calibration(write)
-    f_fetch = COPY_BYTES / (cf * 1024.0)
-    f_write = COPY_BYTES / (cw * 1024.0)
-    out = {"calibration": {"kernel": ck, "dispatches": COPY_REPS, "bytes_read": COPY_BYTES,
-                           "bytes_written": COPY_BYTES, "fetch_kib": round(cf, 1), "write_kib": round(cw, 1),
-                           "fetch_scale": round(f_fetch, 4), "write_scale": round(f_write, 4)},
-           "kernels": {}}
-    for kern, key in KERNEL_NAME_KEYS.items():
-        fk, nf, names = kernel_mean(fetch, key)
-        wk, _, _ = kernel_mean(write, key)
-        hbm = fk * 1024.0 * f_fetch + wk * 1024.0 * f_write
-        out["kernels"][kern] = {"src_sha256_16": hashes[kern], "dispatches": nf, "kernel_names": names,
-                                "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
-                                "hbm_bytes_per_launch": round(hbm)}
-    with open(COUNTERS_FILE, "w") as f:
+    with open(order_json) as f:
+        order = json.load(f)
+    segments, cur = [], None
+    for st, en, name in rows:
+        if SEPARATOR_KERNEL in name:
+            cur = []
+            segments.append(cur)
+        elif cur is not None and "absmax_apply_kernel" not in name:
+            cur.append((name, (en - st) / 1e3))
+    if len(segments) != len(order["configs"]):
+        raise SystemExit("%d separators in the trace, %d configs in the order file" % (len(segments), len(order["configs"])))
+    out = {"source_hashes": order["hashes"], "command": order.get("command", ""), "configs": {}}
+    for cfg, seg in zip(order["configs"], segments):
+        by = {}
+        for name, us in seg:
+            by.setdefault(name, []).append(us)
+        ks = {}
+        for name, v in sorted(by.items(), key=lambda kv: -len(kv[1])):
+            if len(v) < 10:
+                continue
+            a = np.array(v)
+            ks[name[:160]] = {"dispatches": len(v), "median_us": round(float(np.median(a)), 3),
+                              "p10_us": round(float(np.percentile(a, 10)), 3),
+                              "p90_us": round(float(np.percentile(a, 90)), 3), "mean_us": round(float(a.mean()), 3)}
+        out["configs"][cfg] = ks
+    with open(DURATIONS_FILE, "w") as f:
         json.dump(out, f, indent=1)
-    print(json.dumps(out, indent=1))
+    md = ["# Kernel durations per bench config (rocprofv3 --kernel-trace)", "",
+          "Command: `%s`" % out["command"], "",
+          "| config | kernel | dispatches | median us | p10 us | p90 us | mean us |", "|---|---|---|---|---|---|---|"]
+    for cfg, ks in out["configs"].items():
+        for name, r in ks.items():
+            md.append("| %s | `%s` | %d | %.3f | %.3f | %.3f | %.3f |" % (cfg, name[:90], r["dispatches"], r["median_us"],
+                                                                      r["p10_us"], r["p90_us"], r["mean_us"]))
+    with open(DURATIONS_FILE[:-5] + ".md", "w") as f:
+        f.write("\n".join(md) + "\n")
+    print("\n".join(md))
+    stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if stats:  # the --stats summary of the same run, top kernels by total time
+        with open(stats[0]) as f:
+            st = list(csv.DictReader(f))
+        md = ["# Kernel statistics of the marked bench run (rocprofv3 --kernel-trace --stats)", "",
+              "Command: `%s` under `rocprofv3 --kernel-trace --stats --output-format csv`" % out["command"], "",
+              "| kernel | calls | average us | min us | max us | share |", "|---|---|---|---|---|---|"]
+        for r in st[:30]:
+            md.append("| `%s` | %s | %.3f | %.3f | %.3f | %s%% |" % (r["Name"][:110], r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                                  float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+                                                                  r["Percentage"]))
+        with open(os.path.join(ROOT, "profiles", "bench_kernel_stats.md"), "w") as f:
+            f.write("\n".join(md) + "\n")
+
+
+def recorded_durations(cfg):
+    """rocprof durations of one config's kernels from the committed summary,
+    or None when missing or taken on other kernel sources."""
+    try:
+        with open(DURATIONS_FILE) as f:
+            d = json.load(f)
+        if any(d["source_hashes"].get(k) != src_hash(k) for k in KERNEL_SOURCES):
+            return None
+        ks = d["configs"].get(cfg)
+        return None if ks is None else {n: r for n, r in ks.items() if "qg::" in n}  # this library's kernels
+    except (OSError, ValueError, KeyError, TypeError, AttributeError):
+        return None
 
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1:])
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
@@ -353,6 +566,10 @@ def main():
     torch.cuda.set_device(0)
     qg.lib()
     dev = torch.device("cuda:0")
+    global MARKS
+    if args.mark_configs:
+        MARKS = {"x": torch.zeros(8, device=dev), "q": torch.empty(8, dtype=torch.int8, device=dev),
+                 "s": torch.empty(1, device=dev), "order": []}
 
     def cur_stream():
         return torch.cuda.current_stream().cuda_stream
@@ -364,6 +581,7 @@ def main():
     launches_per_step = len(launches)
 
     log("capturing the decode step (%d launches, %.2f GB of weights)" % (launches_per_step, step_bytes / 1e9))
+    mark(torch, qg, "decode_step_w8a16")
     step = Timed(torch, launches)
     for _ in range(args.warmup):
         step.graph.replay()
@@ -389,7 +607,7 @@ def main():
     per_launch_bytes = (step_bytes + act_bytes) / launches_per_step
     achieved = per_launch_bytes / per_launch_s / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic("qgemv"),
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic("decode_step_w8a16", "qgemv_kernel"),
                 "kernel": "qgemv_kernel<INT8 weights, bf16 x, bf16 y> (grouped and single launches)",
                 "algorithmic_bytes_per_launch": round(per_launch_bytes), "avg_launch_us": round(per_launch_s * 1e6, 3)}
     log("decode step: %.3f ms, %.1f GB/s weights (%.1f%% of HBM peak)" % (ms_per_step, value, 100 * value / HBM_PEAK_GBS))
@@ -415,9 +633,25 @@ def main():
         "roofline": roofline,
     }
 
+    result["roofline"]["rocprof"] = recorded_durations("decode_step_w8a16")
+    mark(torch, qg, "hbm_read_ceiling")
+    result["hbm_read_ceiling"] = hbm_read_ceiling(torch, qg, dev, h["launch_bytes"])
+    log("HBM read ceiling: %s" % json.dumps(result["hbm_read_ceiling"]))
     if not args.only_headline:
         result["configs"] = bench_configs(torch, qg, synth, np, dev, cur_stream, h["weights"], h["xs"], h["ys"])
         result["prefill"] = result["configs"].pop("prefill_w8a8_outlier")
+        del h, launches, step
+        torch.cuda.empty_cache()
+        result["decode_steps"] = bench_format_steps(torch, qg, synth, dev, L)
+        for name, rec in list(result["configs"].items()) + list(result["decode_steps"].items()) + \
+                [("prefill_w8a8_outlier", result["prefill"])]:
+            if isinstance(rec, dict):
+                rec["rocprof"] = recorded_durations(name)
+                if "traffic" not in rec:
+                    key = {"prefill_mxfp4": "gemm_mxfp4", "small_batch_decode_step_m16": "qgemv_batch",
+                           "decode_step_sep_threshold": "sep_qgemv",
+                           "prefill_w8a8_outlier": "qgemm_w8a8"}.get(name, "qgemv_kernel")
+                    rec["traffic"] = recorded_traffic(name, key)
     result["context"] = {
         "note": "figures quoted from the pages for context; not targets",
         "fp16_7b_bytes_per_token_GB": 14, "fp16_7b_ms_per_token_at_2TBps": 7.0,
@@ -425,6 +659,10 @@ def main():
         "qadd_prefill_speedup_dgx_spark": 1.49,
         "this_step_weight_GB": round(step_bytes / 1e9, 3),
     }
+    if MARKS is not None:
+        with open(args.mark_configs, "w") as f:
+            json.dump({"configs": MARKS["order"], "hashes": {k: src_hash(k) for k in KERNEL_SOURCES},
+                       "command": "python bench.py " + " ".join(sys.argv[1:])}, f, indent=1)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(np, synth)
     print(json.dumps(result), flush=True)
@@ -448,6 +686,7 @@ def bench_sep_threshold(torch, qg, synth, dev, rotate_count):
     ys = torch.empty(n, dtype=torch.float32, device=dev)
     out = {}
     for skip in (False, True):
+        mark(torch, qg, "sep_threshold_skip_residual_28672x8192" if skip else "sep_threshold_28672x8192")
         per, nres = sep_threshold_bytes(torch, sw, skip)
         copies = [qg.SepWeight(sw.cls.clone(), sw.rv if skip else sw.rv.clone(), sw.alpha.clone(), sw.s_r.clone(), k)
                   for _ in range(rotate_count(per))]
@@ -464,7 +703,7 @@ def bench_sep_threshold(torch, qg, synth, dev, rotate_count):
                      "weights_per_ns": round(n * k / sec / 1e9, 1), "rotating_copies": len(copies),
                      "algorithmic_bytes": per}
         if not skip:
-            out[name]["traffic"] = recorded_traffic("sepq")
+            out[name]["traffic"] = recorded_traffic(name, "sep_qgemv")
         log("%s: %.2f us, %.0f GB/s" % (name, sec * 1e6, per / sec / 1e9))
         del copies, t
         torch.cuda.empty_cache()
@@ -480,6 +719,7 @@ def bench_small_batch(torch, qg, dev, weights, batches=(4, 16)):
     step_bytes = sum(W.n * W.k + 4 * W.n for _, W, _ in weights)
     out = {}
     for m in batches:
+        mark(torch, qg, "small_batch_decode_step_m%d" % m)
         xs = {k: torch.randn(m, k, device=dev).to(torch.bfloat16) for k in (4096, 11008)}
         ys = [torch.empty((m, W.n), dtype=torch.bfloat16, device=dev) for _, W, _ in weights[:per_layer]]
         launches = []
@@ -539,6 +779,7 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
 
     # -- the three decode shapes on their own, rotating through the stack's copies
     for name in synth.DECODE_7B_SHAPES:
+        mark(torch, qg, "decode_w8a16_" + name)
         ws = [(W, cw) for nm, W, cw in weights if nm == name]
         W0 = ws[0][0]
         per = W0.n * W0.k + 4 * W0.n
@@ -562,6 +803,7 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
     out.update(bench_small_batch(torch, qg, dev, weights))
 
     # -- tiny W8A8 GEMV (launch-latency bound)
+    mark(torch, qg, "tiny_w8a8_256x256")
     wl = synth.tiny_gemv()
     wq, s_w = qg.quantize_absmax(torch.from_numpy(wl.tensors["w"]).to(dev), per_row=True)
     Wt = qg.QWeight(qg.QG_WFMT_INT8, 256, 256, wq, s_w)
@@ -579,6 +821,7 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
     log("tiny: %.2f us" % (sec * 1e6))
 
     # -- ternary 11008 x 4096
+    mark(torch, qg, "ternary_11008x4096")
     wl = synth.ternary_decode()
     q, gamma = qg.quantize_ternary(torch.from_numpy(wl.tensors["w"]).to(dev))
     packed = qg.pack(q, 2)
@@ -602,6 +845,7 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
     del copies, cws, packed
 
     # -- the same codes packed five per byte in base 3 (1.6 bits per weight)
+    mark(torch, qg, "ternary_base3_11008x4096")
     packed = qg.pack_base3(q)
     del q
     per = packed.numel() + 4
@@ -620,6 +864,7 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
     torch.cuda.empty_cache()
 
     # -- group-wise 4-bit weights (two-level scales), W4A16, 11008 x 4096
+    mark(torch, qg, "q4k_w4a16_11008x4096")
     wl = synth.q4_decode()
     codes, meta = qg.quantize_q4k(torch.from_numpy(wl.tensors["w"]).to(dev))
     per = codes.numel() + meta.numel()
@@ -646,6 +891,7 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
     torch.cuda.empty_cache()
 
     # -- sign backbone + int8 residual, 28672 x 8192
+    mark(torch, qg, "sign1_res8_28672x8192")
     wl = synth.sign_residual_decode()
     wdev = torch.from_numpy(wl.tensors["w"]).to(dev)
     sign, alpha, rq, s_r = qg.split_sign_residual(wdev)
@@ -674,6 +920,7 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
     torch.cuda.empty_cache()
 
     # -- the same with the zero-point residual (asymmetric int8, z per row)
+    mark(torch, qg, "sign1_res8z_28672x8192")
     wdev = torch.from_numpy(wl.tensors["w"]).to(dev)
     sign, alpha, rq, s_r, z_r = qg.split_sign_residual_zp(wdev)
     sp = qg.pack(sign, 1)
@@ -697,6 +944,7 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
     out.update(bench_sep_threshold(torch, qg, synth, dev, rotate_count))
 
     # -- W8A8 prefill GEMM with outlier split, 2048 x 4096 x 4096, 20 outlier channels
+    mark(torch, qg, "prefill_w8a8_outlier")
     full, split_only, dims, gemm_bytes = build_prefill(torch, qg, synth, dev, cur_stream)
     m, k, n, n_out = dims["m"], dims["k"], dims["n"], dims["n_out"]
     tf = Timed(torch, [full] * 20)
@@ -721,7 +969,7 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
         "mfma_frac": round(tops / INT8_MFMA_PEAK_TOPS, 4),
         "call_TOPS": round((int8_ops + bf16_ops) / sec_full / 1e12, 1),
         "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": INT8_MFMA_PEAK_TOPS, "unit": "TFLOP/s",
-                     "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4), "traffic": recorded_traffic("qgemm"),
+                     "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4), "traffic": recorded_traffic("prefill_w8a8_outlier", "qgemm_w8a8"),
                      "algorithmic_bytes_per_launch": gemm_bytes},
         "vendor_int8_gemm_us": vendor_int8_gemm_us(torch, dims["xq"], dims["wq"]),
         "vendor_note": "torch._int_mm (vendor BLAS) on the same int8 operands: int32 product only, "
@@ -731,9 +979,11 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
 
     # -- format-separated prefill: the same activations and weights in MXFP4
     #    (E2M1 + E8M0 per 32) on the block-scaled FP4 matrix cores
+    mark(torch, qg, "prefill_mxfp4")
     out["prefill_mxfp4"] = bench_mxfp4_prefill(torch, qg, synth, dev, sec_gemm)
 
     # -- outlier-channel detection on the same activations (run once, offline)
+    mark(torch, qg, "detect_outliers_2048x4096")
     xp = full.hold[3]
     idx_d = torch.empty(n_out, dtype=torch.int32, device=dev)
     import ctypes
@@ -754,6 +1004,152 @@ def bench_configs(torch, qg, synth, np, dev, cur_stream, weights, xs, ys):
                                         "finds_planted_channels": found == sorted(dims["idx"]),
                                         "note": "offline, once per model: per-channel ranges by row block, then a one-workgroup select"}
     log("detect: %.1f us" % (sec_det * 1e6))
+    return out
+
+
+def hbm_read_ceiling(torch, qg, dev, step_sizes):
+    """The on-box streaming-read rate (qg_probe_stream_read: every byte read
+    once with 128-bit non-temporal loads, nothing computed), on 4 GiB and as
+    the headline step's own sequence of launch sizes replayed as a graph of
+    pure reads over distinct buffers -- the floor the qgemv step is compared
+    with."""
+    import ctypes
+    L = qg.lib()
+    sink = torch.zeros(65536, dtype=torch.int32, device=dev)
+    out = {}
+    big = 4 << 30
+    buf = torch.ones(big, dtype=torch.uint8, device=dev)
+    for wgs in (256, 1024):
+        nb = int(L.qg_probe_stream_read_bytes(big, wgs))
+
+        def f():
+            st = L.qg_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), big, wgs, ctypes.c_void_p(sink.data_ptr()),
+                                        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if st != 0:
+                raise RuntimeError("qg_probe_stream_read: %s" % qg.status_str(st))
+        t = Timed(torch, [f] * 4)
+        t.run(1)
+        sec = t.run(5) / 4
+        out["read_4GiB_%dwg_GBps" % wgs] = round(nb / sec / 1e9, 1)
+    del buf
+    torch.cuda.empty_cache()
+    total = sum(step_sizes)
+    region = torch.ones(total + (1 << 20), dtype=torch.uint8, device=dev)
+    launches, offs, read = [], 0, 0
+    for b in step_sizes:
+        nb = int(L.qg_probe_stream_read_bytes(b, 256))
+        read += nb
+        base = region.data_ptr() + offs
+
+        def f(base=base, b=b):
+            st = L.qg_probe_stream_read(ctypes.c_void_p(base), b, 256, ctypes.c_void_p(sink.data_ptr()),
+                                        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if st != 0:
+                raise RuntimeError("qg_probe_stream_read: %s" % qg.status_str(st))
+        launches.append(f)
+        offs += (b + 255) // 256 * 256
+    t = Timed(torch, launches)
+    t.run(2)
+    sec = t.run(10)
+    out["step_sequence_ms"] = round(sec * 1e3, 4)
+    out["step_sequence_GBps"] = round(read / sec / 1e9, 1)
+    out["step_sequence_note"] = ("the decode step's %d launch sizes as pure streaming reads (256 workgroups, "
+                                 "HIP graph of distinct buffers)" % len(step_sizes))
+    best = max(v for k, v in out.items() if k.startswith("read_4GiB"))
+    out["ceiling_frac_of_peak"] = round(best / HBM_PEAK_GBS, 4)
+    del region
+    torch.cuda.empty_cache()
+    return out
+
+
+FORMAT_SEEDS = {"attn_4096x4096": 31, "ffn_up_11008x4096": 32, "ffn_down_4096x11008": 33}
+
+
+def build_format_step(torch, qg, synth, dev, L, fmt):
+    """The headline's 32-layer decode step (same shapes, launches grouped the
+    same way, every layer its own weight copy) with the weights in a low-bit
+    format: "ternary2" (2-bit ternary, int8 activations), "sign1_res8" (sign
+    backbone + int8 residual, bf16 activations) or "sep_threshold"
+    (thresholded separated weights, 80th / 50th percentiles, one launch per
+    projection).  Returns (launches, weight bytes per step, objects to keep)."""
+    shapes = synth.DECODE_7B_SHAPES
+    plan = ["attn_4096x4096"] * 4 + ["ffn_up_11008x4096"] * 2 + ["ffn_down_4096x11008"]
+    groups_per_layer = [[0, 1, 2], [3], [4, 5], [6]]
+    base = {}
+    for name, (n, k) in shapes.items():
+        if fmt == "ternary2":
+            w = torch.from_numpy(synth.ternary_decode(n=n, k=k, seed=FORMAT_SEEDS[name]).tensors["w"]).to(dev)
+            q, gamma = qg.quantize_ternary(w)
+            base[name] = (qg.pack(q, 2), gamma)
+            del q
+        else:
+            w = torch.from_numpy(synth.sign_residual_decode(n=n, k=k, seed=FORMAT_SEEDS[name]).tensors["w"]).to(dev)
+            if fmt == "sign1_res8":
+                sign, alpha, rq, s_r = qg.split_sign_residual(w)
+                base[name] = (qg.pack(sign, 1), alpha, rq, s_r)
+                del sign
+            else:
+                base[name] = qg.split_sep_threshold(w, 80, 50)
+        del w
+    torch.cuda.synchronize()
+    weights, nbytes = [], 0
+    for _ in range(L):
+        for name in plan:
+            n, k = shapes[name]
+            b = base[name]
+            if fmt == "ternary2":
+                W = qg.QWeight(qg.QG_WFMT_TERNARY2, n, k, b[0].clone(), b[1].clone())
+                nbytes += b[0].numel() + 4
+            elif fmt == "sign1_res8":
+                W = qg.QWeight(qg.QG_WFMT_SIGN1_RES8, n, k, b[0].clone(), b[1].clone(), resid=b[2].clone(),
+                               scale2=b[3].clone())
+                nbytes += b[0].numel() + b[2].numel() + 8 * n
+            else:
+                W = qg.SepWeight(b.cls.clone(), b.rv.clone(), b.alpha.clone(), b.s_r.clone(), k)
+                nbytes += sep_threshold_bytes(torch, b, False)[0]
+            weights.append(W)
+    del base
+    if fmt == "ternary2":
+        xs = {k: torch.randn(k, device=dev) for k in (4096, 11008)}
+    else:
+        xs = {k: torch.randn(k, device=dev).to(torch.bfloat16) for k in (4096, 11008)}
+    launches, keep = [], [weights, xs]
+    for li in range(L):
+        if fmt == "sep_threshold":
+            for i in range(len(plan)):
+                W = weights[li * len(plan) + i]
+                y = torch.empty(W.n, dtype=torch.float32, device=dev)
+                keep.append(y)
+                launches.append((lambda W, y: (lambda: qg.qgemv_sep(W, xs[W.k], y=y)))(W, y))
+        else:
+            for grp in groups_per_layer:
+                ws_ = [weights[li * len(plan) + i] for i in grp]
+                ydt = torch.float32 if fmt == "ternary2" else torch.bfloat16
+                ys_ = [torch.empty(W.n, dtype=ydt, device=dev) for W in ws_]
+                gl = qg.GroupLaunch(ws_, xs[ws_[0].k], ys_, act_int8=(fmt == "ternary2"))
+                keep.append(gl)
+                launches.append(gl.launch)
+    weights_per_step = L * sum(shapes[nm][0] * shapes[nm][1] for nm in plan)
+    return launches, nbytes, keep, weights_per_step
+
+
+def bench_format_steps(torch, qg, synth, dev, L):
+    """The 32-layer decode step in the low-bit formats (see build_format_step)."""
+    out = {}
+    for fmt in ("ternary2", "sign1_res8", "sep_threshold"):
+        mark(torch, qg, "decode_step_" + fmt)
+        launches, nbytes, keep, nw = build_format_step(torch, qg, synth, dev, L, fmt)
+        t = Timed(torch, launches)
+        t.run(2)
+        sec = t.run(10)
+        out["decode_step_%s" % fmt] = {
+            "ms_per_step": round(sec * 1e3, 4), "tokens_per_s": round(1.0 / sec, 1),
+            "weight_bytes_per_step": nbytes, "weight_GBps": round(nbytes / sec / 1e9, 1),
+            "hbm_frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4), "launches_per_step": len(launches),
+            "bytes_per_weight": round(nbytes / nw, 4)}
+        log("decode step %s: %.3f ms, %.0f GB/s of weights" % (fmt, sec * 1e3, nbytes / sec / 1e9))
+        del t, launches, keep
+        torch.cuda.empty_cache()
     return out
 
 
@@ -809,7 +1205,65 @@ def cpu_baseline(np, synth):
             "sample": "%d decode layers (%d projections: 4 x 4096x4096, 2 x 11008x4096, 1 x 4096x11008 each; "
                       "%.2f GB of int8 weights), fp64 dequantize-then-multiply, %.1f s" %
                       (layers, 7 * layers, done_bytes / 1e9, el),
-            "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+            "host_cpus": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+            "per_config": oracle_per_config(np, synth)}
+
+
+def oracle_per_config(np, synth):
+    """Seconds the oracle takes on each of the five workloads at full size:
+    the offline quantization (codes and scales from the fp32 weights) and the
+    product (integer sums and the fp64 reference output) timed apart; input
+    generation excluded."""
+    import oracle
+    out = {}
+
+    def timed(f):
+        t0 = time.perf_counter()
+        r = f()
+        return r, round(time.perf_counter() - t0, 3)
+    log("cpu baseline: oracle on the five workloads")
+    wl = synth.tiny_gemv()
+    (wq, sw), tq = timed(lambda: oracle.quantize_absmax(wl.tensors["w"], per_row=True))
+    (xq, sx), tx = timed(lambda: oracle.quantize_absmax(wl.tensors["x"], per_row=False))
+    _, tp = timed(lambda: oracle.y_w8a8(oracle.int_dot_exact(wq, xq), sw, sx))
+    out["tiny_w8a8_256x256"] = {"quantize_s": tq, "product_s": round(tx + tp, 3),
+                                "product_note": "activation quantization + exact int32 dot + fp64 rescale"}
+    for name, (n, k) in synth.DECODE_7B_SHAPES.items():
+        wl = synth.decode_w8a16(n=n, k=k, seed=synth.DECODE_7B_SEEDS[name])
+        (wq, sw), tq = timed(lambda: oracle.quantize_absmax(wl.tensors["w"], per_row=True))
+        _, tp = timed(lambda: oracle.y_w8a16(wq, sw, wl.tensors["x_bf16"]))
+        out["decode_w8a16_" + name] = {"quantize_s": tq, "product_s": tp}
+    wl = synth.ternary_decode()
+    (q, g), tq = timed(lambda: oracle.ternary_absmean(wl.tensors["w"]))
+
+    def tern():
+        xq, sx = oracle.quantize_absmax(wl.tensors["x"], per_row=False)
+        return oracle.y_ternary(oracle.int_dot_exact(q, xq), g, sx)
+    _, tp = timed(tern)
+    out["ternary_11008x4096"] = {"quantize_s": tq, "product_s": tp}
+    del q
+    wl = synth.sign_residual_decode()
+    (sgn, a, rq, sr), tq = timed(lambda: oracle.sign_residual_split(wl.tensors["w"]))
+    _, tp = timed(lambda: oracle.y_sign_residual(sgn, a, rq, sr, wl.tensors["x_bf16"]))
+    out["sign1_res8_28672x8192"] = {"quantize_s": tq, "product_s": tp}
+    del sgn, rq, wl
+    wl = synth.prefill_outlier()
+    idx = wl.tensors["idx"]
+
+    def wquant():
+        wq, sw = oracle.quantize_absmax(wl.tensors["w"], per_row=True)
+        return wq, sw, oracle.gather_outlier_weights(wl.tensors["w"], idx)
+    (wq, sw, wo), tq = timed(wquant)
+
+    def prefill():
+        xq, sx, xo = oracle.outlier_split_quantize(wl.tensors["x_bf16"], idx)
+        return oracle.y_prefill(oracle.int_gemm_exact(xq, wq), sx, sw, xo, wo)
+    _, tp = timed(prefill)
+    out["prefill_w8a8_outlier_2048x4096x4096"] = {"quantize_s": tq, "product_s": tp,
+                                                   "product_note": "outlier split + per-token quantization, exact "
+                                                                   "int32 GEMM (fp64 BLAS on integer values), fp64 "
+                                                                   "rescale and outlier GEMM"}
+    return out
 
 
 if __name__ == "__main__":

@@ -558,6 +558,21 @@ qg_status qg_qgemm_w8a8(const int8_t* xq, const float* s_x, const void* x_out, i
                         const int8_t* wq, const float* s_w, const void* w_out, int32_t w_out_ld,
                         int64_t n, float* y, int32_t* acc_out, void* stream);
 
+/*
+ * Measurement aid, not a step of the method: the streaming-read probe that
+ * gives the HBM read rate the qgemv kernels are compared with.  Reads the
+ * first qg_probe_stream_read_bytes(bytes, workgroups) bytes of buf (its
+ * largest prefix that splits into equal per-workgroup blocks of whole passes
+ * of 512 threads x 16 B x 8 loads) exactly once with 128-bit non-temporal
+ * loads, the access the weight streams use; computes nothing but an XOR.
+ * buf    : device buffer of at least that many bytes, 16-B aligned.
+ * sink   : device buffer of workgroups uint32 (practically never written).
+ * workgroups in [1, 65535]; each block must stay below 2^31 bytes
+ * (QG_ERR_SHAPE otherwise, also when the prefix is empty).
+ */
+size_t qg_probe_stream_read_bytes(int64_t bytes, int32_t workgroups);
+qg_status qg_probe_stream_read(const void* buf, int64_t bytes, int32_t workgroups, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

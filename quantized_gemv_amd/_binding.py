@@ -55,6 +55,8 @@ _SIGS = {
     "qg_quantize_absmax_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i32]),
     "qg_quantize_absmax": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]),
     "qg_quantize_absmax_noalloc": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp]),
+    "qg_probe_stream_read_bytes": (_c_sz, [_c_i64, _c_i32]),
+    "qg_probe_stream_read": (_c_i32, [_c_vp, _c_i64, _c_i32, _c_vp, _c_vp]),
     "qg_quantize_absmax_split": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32,
                                           _c_vp]),
     "qg_detect_outliers_workspace_bytes": (_c_sz, [_c_i64]),

@@ -552,4 +552,18 @@ qg_status qg_qgemm_w8a8_outlier(const void* x, int64_t m, int64_t k, const int32
     return from_hip(qg::launch_qgemm(a, as_stream(stream)));
 }
 
+size_t qg_probe_stream_read_bytes(int64_t bytes, int32_t workgroups) {
+    if (bytes < 1 || workgroups < 1 || workgroups > 65535) return 0;
+    const int64_t blk = qg::stream_read_block(bytes, workgroups);
+    if (blk < 1 || blk >= ((int64_t)1 << 31)) return 0;
+    return (size_t)(blk * workgroups);
+}
+
+qg_status qg_probe_stream_read(const void* buf, int64_t bytes, int32_t workgroups, uint32_t* sink, void* stream) {
+    if (!buf || !sink) return QG_ERR_NULLPTR;
+    if (qg_probe_stream_read_bytes(bytes, workgroups) == 0) return QG_ERR_SHAPE;
+    if (!aligned16(buf)) return QG_ERR_ALIGN;
+    return from_hip(qg::launch_stream_read(buf, bytes, workgroups, sink, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -125,4 +125,10 @@ hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* as, int64_t m, int
 
 int device_cu_count();
 
+// Streaming-read probe: workgroups of kQProbeThreads each read one block of
+// stream_read_block(bytes, wgs) bytes (a multiple of the per-pass span).
+constexpr int kQProbeThreads = 512;
+int64_t stream_read_block(int64_t bytes, int wgs);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, int wgs, uint32_t* sink, hipStream_t st);
+
 }  // namespace qg

@@ -97,6 +97,26 @@ def test_validation_quantize_absmax_noalloc(qg):
     assert f(A, 0, 4, 64, 0, U, A, None) == 3
 
 
+def test_probe_stream_read_sizes(qg):
+    # the probe reads the largest prefix that splits into equal blocks of
+    # whole passes (512 threads x 16 B x 8 loads = 64 KiB) per workgroup
+    f = qg.lib().qg_probe_stream_read_bytes
+    assert f(256 << 16, 256) == 256 << 16
+    assert f((256 << 16) + 5, 256) == 256 << 16
+    assert f((256 << 16) - 1, 256) == 0
+    assert f(4 << 30, 1024) == 4 << 30
+    assert f(1 << 40, 1) == 0 and f(1 << 20, 0) == 0 and f(1 << 20, 70000) == 0
+
+
+@needs_no_gpu
+def test_validation_probe_stream_read(qg):
+    f = qg.lib().qg_probe_stream_read
+    assert f(None, 1 << 20, 4, A, None) == 1
+    assert f(A, 1 << 20, 4, None, None) == 1
+    assert f(A, 100, 4, A, None) == 2
+    assert f(U, 1 << 20, 4, A, None) == 3
+
+
 @needs_no_gpu
 def test_validation_split_and_gather(qg):
     l = qg.lib()

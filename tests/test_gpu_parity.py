@@ -98,6 +98,20 @@ def test_absmax_tiny_groups(qg):
     assert np.array_equal(host(acc), oracle.int_dot_exact(q_ref, qt_ref).astype(np.int32))
 
 
+def test_probe_stream_read_runs(qg):
+    # the measurement aid: launches, returns, and leaves the sink untouched
+    # (it is written only on an XOR value that ones never produce)
+    note("probe stream read")
+    import ctypes
+    buf = torch.ones(4 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(8, dtype=torch.int32, device="cuda")
+    st = qg.lib().qg_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel(), 8,
+                                       ctypes.c_void_p(sink.data_ptr()),
+                                       ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    assert not host(sink).any()
+
+
 def test_absmax_worked_example_on_gpu(qg):
     note("absmax worked example")
     x = np.array([10.8, 3.08, 3.02, -7.59, 0, 0, 0, 0], np.float32)
