@@ -88,9 +88,13 @@ struct KParams {
 // A launch covers up to kMaxGroup weight matrices that share K and x (for
 // example the q, k and v projections of a layer).  Workgroups are handed out
 // per matrix in proportion to its rows; matrix m is grid row blockIdx.y = m.
+// The argument holds MG slots (1, 3 or 8, the fewest that fit the launch):
+// on MI355X a launch in a HIP graph costs about 0.15 us more with the full
+// 8-slot (576-byte) argument than with a small one.
 constexpr int kMaxGroup = 8;
+template <int MG>
 struct KGroup {
-    KParams mats[kMaxGroup];
+    KParams mats[MG];
 };
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -181,8 +185,8 @@ constexpr int kXL = 4;  // x pieces of 16 B held in registers per thread (K <= 1
 // out in the prologue, so all of the wave's weights are in flight while x is
 // prepared and the decode work is spread over all waves (short rows, few per
 // wave: the ternary formats at the decode shapes).
-template <int F, int XT, int YT, int U, int JS, bool XREG = false, int NPF = 0>
-__global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup grp) {
+template <int F, int XT, int YT, int U, int JS, bool XREG = false, int NPF = 0, int MG = kMaxGroup>
+__global__ __launch_bounds__(kQThreads) void qgemv_kernel(KGroup<MG> grp) {
     using Frag = typename Fmt<F>::Frag;
     constexpr int kCols = Fmt<F>::kColsPerChunk;
     extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
@@ -1055,42 +1059,48 @@ static hipError_t run(const QgemvArgs* a, int count, hipStream_t st) {
     const int64_t rowB = (F == F_TERN) ? K / 4 : kSignRes<F> ? K / 8 : (F == F_Q4) ? K / 2 : (F == F_TERN3) ? 16 * C : K;
     const int64_t resB = kSignRes<F> ? K : (F == F_Q4) ? K / 16 : 0;
     const int64_t cap = ((int64_t)1 << 31) / (rowB > resB ? rowB : resB);  // buffer ranges stay below 2 GiB
-    KGroup g;
-    int wgx = 1;  // grid: (workgroups of the largest matrix) x (matrices)
-    for (int m = 0; m < count; ++m) {
-        const int64_t N = a[m].n;
-        const int64_t rpw = rows_per_wg(a, count, m, cap);
-        if (NPF > 0) {  // every item of every wave must fit the prefetch
-            const int64_t groups = (rpw + U - 1) / U;
-            if (((groups + kQWaves - 1) / kQWaves) * nseg > NPF) return hipErrorInvalidValue;
+    auto launch = [&](auto slots) -> hipError_t {
+        constexpr int MG = decltype(slots)::value;
+        KGroup<MG> g;
+        int wgx = 1;  // grid: (workgroups of the largest matrix) x (matrices)
+        for (int m = 0; m < count; ++m) {
+            const int64_t N = a[m].n;
+            const int64_t rpw = rows_per_wg(a, count, m, cap);
+            if (NPF > 0) {  // every item of every wave must fit the prefetch
+                const int64_t groups = (rpw + U - 1) / U;
+                if (((groups + kQWaves - 1) / kQWaves) * nseg > NPF) return hipErrorInvalidValue;
+            }
+            KParams& p = g.mats[m];
+            p.codes = static_cast<const uint8_t*>(a[m].codes);
+            p.resid = a[m].resid;
+            p.scale = a[m].scale;
+            p.scale2 = a[m].scale2;
+            p.zero = a[m].zero;
+            p.x = a[m].x;
+            p.y = a[m].y;
+            p.acc_out = a[m].acc_out;
+            p.n = (int32_t)N;
+            p.k = K;
+            p.rows_per_wg = (int32_t)rpw;
+            const int nwg = (int)((N + rpw - 1) / rpw);
+            if (nwg > wgx) wgx = nwg;
         }
-        KParams& p = g.mats[m];
-        p.codes = static_cast<const uint8_t*>(a[m].codes);
-        p.resid = a[m].resid;
-        p.scale = a[m].scale;
-        p.scale2 = a[m].scale2;
-        p.zero = a[m].zero;
-        p.x = a[m].x;
-        p.y = a[m].y;
-        p.acc_out = a[m].acc_out;
-        p.n = (int32_t)N;
-        p.k = K;
-        p.rows_per_wg = (int32_t)rpw;
-        const int nwg = (int)((N + rpw - 1) / rpw);
-        if (nwg > wgx) wgx = nwg;
-    }
-    auto kern = qgemv_kernel<F, XT, YT, U, JS, XREG, NPF>;
-    if (lds > 64 * 1024) {
-        static bool attr_set = false;  // per instantiation
-        if (!attr_set) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            if (e != hipSuccess) return e;
-            attr_set = true;
+        auto kern = qgemv_kernel<F, XT, YT, U, JS, XREG, NPF, MG>;
+        if (lds > 64 * 1024) {
+            static bool attr_set = false;  // per instantiation
+            if (!attr_set) {
+                hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                if (e != hipSuccess) return e;
+                attr_set = true;
+            }
         }
-    }
-    kern<<<dim3(wgx, count), kQThreads, lds, st>>>(g);
-    return hipGetLastError();
+        kern<<<dim3(wgx, count), kQThreads, lds, st>>>(g);
+        return hipGetLastError();
+    };
+    if (count == 1) return launch(std::integral_constant<int, 1>{});
+    if (count <= 3) return launch(std::integral_constant<int, 3>{});
+    return launch(std::integral_constant<int, kMaxGroup>{});
 }
 
 template <int F, int U, int JS, bool XREG = false, int NPF = 0>

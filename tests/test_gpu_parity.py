@@ -437,15 +437,17 @@ def test_qgemv_grouped_matches_single(qg, fmt):
             assert oracle.normwise_error(host(ys[i]), oracle.y_sign_residual(*refs[i], xb)) <= 1e-5
 
 
-@pytest.mark.parametrize("k", [11008, 1152])
-def test_qgemv_w8a16_grouped_matches_single(qg, k):
+@pytest.mark.parametrize("k,ns", [(11008, (4096, 777, 1500)), (1152, (4096, 777, 1500)),
+                                  (4096, (4096, 300, 1000, 64, 2048))])
+def test_qgemv_w8a16_grouped_matches_single(qg, k, ns):
     # a grouped launch of the W8A16 product at a K whose x is staged in LDS
-    # (11008) and one whose x sits in registers (1152): bit-identical to the
-    # single launches, and within tolerance of the oracle
-    note("qgemv w8a16 grouped k=%d" % k)
+    # (11008) and ones whose x sits in registers (1152, 4096; five matrices
+    # take the 8-slot kernel argument): bit-identical to the single launches,
+    # and within tolerance of the oracle
+    note("qgemv w8a16 grouped k=%d, %d matrices" % (k, len(ns)))
     g = synth.rng(k)
     Ws, refs = [], []
-    for n in (4096, 777, 1500):
+    for n in ns:
         w = synth.gaussian(g, (n, k), 0.02)
         W, _, _ = _int8_weight(qg, w)
         Ws.append(W)
