@@ -287,16 +287,8 @@ def profile_workload(args):
     del src, dst
     h = build_headline(torch, qg, synth, dev, args.layers)
     twice("decode_step_w8a16", h["launches"])
-    xb = {k: torch.randn(16, k, device=dev).to(torch.bfloat16) for k in (4096, 11008)}
-    ybs = [torch.empty((16, W.n), dtype=torch.bfloat16, device=dev) for _, W, _ in h["weights"][:7]]
-    batch_launches = []
-    for li in range(args.layers):
-        for grp in [[0, 1, 2], [3], [4, 5], [6]]:
-            ws_ = [h["weights"][li * 7 + i][1] for i in grp]
-            yy = [ybs[i] for i in grp]
-            batch_launches.append((lambda ws_, yy: (lambda: qg.qgemv_batch_grouped(ws_, xb[ws_[0].k], ys=yy)))(ws_, yy))
-    twice("small_batch_decode_step_m16", batch_launches)
-    del h, xb
+    twice("small_batch_decode_step_m16", small_batch_launches(torch, qg, dev, h["weights"], 16))
+    del h
     torch.cuda.empty_cache()
     full, _, _, _ = build_prefill(torch, qg, synth, dev, cur_stream)
     twice("prefill_w8a8_outlier", [full])
@@ -710,34 +702,53 @@ def bench_sep_threshold(torch, qg, synth, dev, rotate_count):
     return out
 
 
+def small_batch_launches(torch, qg, dev, weights, m, split=True):
+    """Launch closures of the decode step for a batch of m tokens: per layer
+    (q, k, v) and (gate, up) grouped, o and down single launches with K split
+    over workgroups (qg_qgemv_batch_ws, one shared workspace: the launches run
+    in stream order) where the shape allows it."""
+    per_layer = 7
+    layers = len(weights) // per_layer
+    xs = {k: torch.randn(m, k, device=dev).to(torch.bfloat16) for k in (4096, 11008)}
+    ys = [torch.empty((m, W.n), dtype=torch.bfloat16, device=dev) for _, W, _ in weights[:per_layer]]
+    need = max(qg.batch_workspace_bytes(W.n, W.k, m) for _, W, _ in weights[:per_layer]) if split else 0
+    wsb = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+    launches = []
+    for li in range(layers):
+        for grp in [[0, 1, 2], [3], [4, 5], [6]]:
+            ws_ = [weights[li * per_layer + i][1] for i in grp]
+            yy = [ys[i] for i in grp]
+            if len(grp) == 1 and need > 0:
+                launches.append((lambda W, y: (lambda: qg.qgemv_batch(W, xs[W.k], y=y, ws=wsb)))(ws_[0], yy[0]))
+            else:
+                launches.append((lambda ws_, yy: (lambda: qg.qgemv_batch_grouped(ws_, xs[ws_[0].k], ys=yy)))(ws_, yy))
+    return launches
+
+
 def bench_small_batch(torch, qg, dev, weights, batches=(4, 16)):
     """The headline's decode step (32 layers, the same weights and the same
     four launches per layer) for a batch of M tokens."""
-    per_layer = 7
-    layers = len(weights) // per_layer
-    groups_per_layer = [[0, 1, 2], [3], [4, 5], [6]]
     step_bytes = sum(W.n * W.k + 4 * W.n for _, W, _ in weights)
     out = {}
     for m in batches:
         mark(torch, qg, "small_batch_decode_step_m%d" % m)
-        xs = {k: torch.randn(m, k, device=dev).to(torch.bfloat16) for k in (4096, 11008)}
-        ys = [torch.empty((m, W.n), dtype=torch.bfloat16, device=dev) for _, W, _ in weights[:per_layer]]
-        launches = []
-        for li in range(layers):
-            for grp in groups_per_layer:
-                ws_ = [weights[li * per_layer + i][1] for i in grp]
-                yy = [ys[i] for i in grp]
-                launches.append((lambda ws_, yy: (lambda: qg.qgemv_batch_grouped(ws_, xs[ws_[0].k], ys=yy)))(ws_, yy))
-        t = Timed(torch, launches)
-        t.run(1)
-        sec = t.run(5)
+        secs = {}
+        for split in (True, False):
+            t = Timed(torch, small_batch_launches(torch, qg, dev, weights, m, split))
+            t.run(1)
+            secs[split] = t.run(5)
+            n_launch = t.n
+            del t
+        sec = secs[True]
         out["small_batch_decode_step_m%d" % m] = {
             "tokens": m, "ms_per_step": round(sec * 1e3, 4), "tokens_per_s": round(m / sec, 1),
             "weight_GBps": round(step_bytes / sec / 1e9, 1), "hbm_frac": round(step_bytes / sec / 1e9 / HBM_PEAK_GBS, 4),
-            "launches_per_step": len(launches),
-            "note": "32 layers x (q,k,v grouped, o, (gate,up) grouped, down), bf16 MFMA on int8 codes widened in registers"}
-        log("small batch m=%d: %.3f ms per step, %.0f tokens/s" % (m, sec * 1e3, m / sec))
-        del t, launches
+            "launches_per_step": n_launch,
+            "ms_per_step_without_split_k": round(secs[False] * 1e3, 4),
+            "note": "32 layers x (q,k,v grouped, o, (gate,up) grouped, down), bf16 MFMA on int8 codes widened in "
+                    "registers; o and down with K split over workgroups"}
+        log("small batch m=%d: %.3f ms per step (%.3f without split K), %.0f tokens/s"
+            % (m, sec * 1e3, secs[False] * 1e3, m / sec))
     return out
 
 

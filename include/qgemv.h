@@ -421,6 +421,27 @@ qg_status qg_qgemv_grouped(const qg_weight* w, int32_t count, int32_t amode, con
  */
 qg_status qg_qgemv_batch(const qg_weight* w, int32_t m, const void* x, int32_t xt, void* y, int32_t yt,
                          void* stream);
+
+/*
+ * qg_qgemv_batch with K split over workgroups, for a single matrix of at
+ * most (CUs x 16) rows and k <= 16384 (the o and down projections at the
+ * decode shapes): a workgroup takes up to four 16-row tiles and a quarter of
+ * k, so it reads each activation row once for all its tiles instead of once
+ * per tile.  Same definition as qg_qgemv_batch; the four partial sums of
+ * each output are added in a fixed order (deterministic; rounding differs
+ * from qg_qgemv_batch's order).
+ * ws       : qg_qgemv_batch_workspace_bytes(n, k, m) bytes, 16-B aligned:
+ *            partial tiles and one counter per row block.  The counters must
+ *            be zero before the first call (e.g. zero-filled at allocation);
+ *            every call leaves them zero.  Calls that overlap on one
+ *            workspace race.
+ * When that size is 0 (m = 1, more tiles than CUs, or k too large) the call
+ * is qg_qgemv_batch and ws is not used.  Other arguments and checks as
+ * qg_qgemv_batch.
+ */
+size_t qg_qgemv_batch_workspace_bytes(int64_t n, int64_t k, int32_t m);
+qg_status qg_qgemv_batch_ws(const qg_weight* w, int32_t m, const void* x, int32_t xt, void* y, int32_t yt,
+                            void* ws, size_t ws_bytes, void* stream);
 qg_status qg_qgemv_batch_grouped(const qg_weight* w, int32_t count, int32_t m, const void* x, int32_t xt,
                                  void* const* y, int32_t yt, void* stream);
 

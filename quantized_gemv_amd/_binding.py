@@ -69,6 +69,8 @@ _SIGS = {
     "qg_quantize_asym": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp]),
     "qg_quantize_q4k": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
     "qg_qgemv_batch": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp]),
+    "qg_qgemv_batch_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i32]),
+    "qg_qgemv_batch_ws": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp, _c_sz, _c_vp]),
     "qg_qgemv_batch_grouped": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_i32, _c_vp, _c_i32,
                                         ctypes.POINTER(_c_vp), _c_i32, _c_vp]),
     "qg_quantize_mxfp4": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
@@ -354,9 +356,12 @@ def quantize_q4k(w: torch.Tensor):
     return codes, meta
 
 
-def qgemv_batch(w: QWeight, x: torch.Tensor, y_dtype=torch.float32, y: torch.Tensor = None):
+def qgemv_batch(w: QWeight, x: torch.Tensor, y_dtype=torch.float32, y: torch.Tensor = None,
+                ws: Optional[torch.Tensor] = None):
     """Weight-only int8 product of a batch of tokens (qg_qgemv_batch): x bf16
-    [m][k] -> y [m][n]. Returns y."""
+    [m][k] -> y [m][n]. Returns y.  With ws (a uint8 device tensor of at least
+    batch_workspace_bytes(w.n, w.k, m) bytes, zero-filled when allocated) the
+    call is qg_qgemv_batch_ws (K split over workgroups)."""
     _dev(x, "x", torch.bfloat16)
     if x.dim() != 2:
         raise ValueError("x must be [m][k]")
@@ -365,8 +370,18 @@ def qgemv_batch(w: QWeight, x: torch.Tensor, y_dtype=torch.float32, y: torch.Ten
         y = torch.empty((m, w.n), dtype=y_dtype, device=x.device)
     _dev(y, "y", (torch.float32, torch.bfloat16))
     cw = w.c_struct()
-    _check(lib().qg_qgemv_batch(ctypes.byref(cw), m, _p(x), QG_BF16, _p(y), _xt(y), _stream(x)), "qg_qgemv_batch")
+    if ws is None:
+        _check(lib().qg_qgemv_batch(ctypes.byref(cw), m, _p(x), QG_BF16, _p(y), _xt(y), _stream(x)), "qg_qgemv_batch")
+    else:
+        _dev(ws, "ws", torch.uint8)
+        _check(lib().qg_qgemv_batch_ws(ctypes.byref(cw), m, _p(x), QG_BF16, _p(y), _xt(y), _p(ws), ws.numel(),
+                                       _stream(x)), "qg_qgemv_batch_ws")
     return y
+
+
+def batch_workspace_bytes(n: int, k: int, m: int) -> int:
+    """Workspace of qg_qgemv_batch_ws (0: the split path does not apply)."""
+    return int(lib().qg_qgemv_batch_workspace_bytes(n, k, m))
 
 
 def qgemv_batch_grouped(weights: Sequence[QWeight], x: torch.Tensor, y_dtype=torch.float32, ys=None):

@@ -420,6 +420,35 @@ qg_status qg_qgemv_batch(const qg_weight* w, int32_t m, const void* x, int32_t x
     return qg_qgemv_batch_grouped(w, 1, m, x, xt, ys, yt, stream);
 }
 
+size_t qg_qgemv_batch_workspace_bytes(int64_t n, int64_t k, int32_t m) {
+    if (n < 1 || n >= ((int64_t)1 << 31) || k < 128 || k % 128 != 0 || k > QG_BATCH_MAX_K) return 0;
+    if (m < 2 || m > QG_BATCH_MAX_M) return 0;
+    return qg::qgemv_batch_splitk_workspace(n, k);
+}
+
+qg_status qg_qgemv_batch_ws(const qg_weight* w, int32_t m, const void* x, int32_t xt, void* y, int32_t yt, void* ws,
+                            size_t ws_bytes, void* stream) {
+    if (!w) return QG_ERR_NULLPTR;
+    const size_t need = qg_qgemv_batch_workspace_bytes(w->n, w->k, m);
+    if (need == 0) return qg_qgemv_batch(w, m, x, xt, y, yt, stream);  // no split for this shape
+    if (!x || !y || !w->codes || !w->scale) return QG_ERR_NULLPTR;
+    if (w->fmt != QG_WFMT_INT8) return QG_ERR_ARG;
+    if (xt != QG_BF16 || (yt != QG_F32 && yt != QG_BF16)) return QG_ERR_ARG;
+    if (!aligned16(x) || !aligned16(w->codes)) return QG_ERR_ALIGN;
+    if (!ws || ws_bytes < need) return QG_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QG_ERR_ALIGN;
+    qg::BatchArgs a;
+    a.n = w->n;
+    a.k = w->k;
+    a.m = m;
+    a.wq = static_cast<const int8_t*>(w->codes);
+    a.s_w = w->scale;
+    a.x = x;
+    a.y = y;
+    a.yt = yt;
+    return from_hip(qg::launch_qgemv_batch_splitk(a, ws, as_stream(stream)));
+}
+
 qg_status qg_quantize_mxfp4(const void* x, int32_t xt, int64_t rows, int64_t cols, uint8_t* codes,
                             uint8_t* scales, void* stream) {
     if (!x || !codes || !scales) return QG_ERR_NULLPTR;

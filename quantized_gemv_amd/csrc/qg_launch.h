@@ -115,6 +115,10 @@ struct BatchArgs {
     int yt;
 };
 hipError_t launch_qgemv_batch(const BatchArgs* a, int count, hipStream_t st);
+// One matrix with K split over workgroups (partials and row-block counters
+// in the workspace); 0 bytes when that path does not apply to (n, k).
+size_t qgemv_batch_splitk_workspace(int64_t n, int64_t k);
+hipError_t launch_qgemv_batch_splitk(const BatchArgs& a, void* ws, hipStream_t st);
 
 // MXFP4: codes [rows][cols/2] (low nibble first) and E8M0 scales
 // [rows][cols/32]; GEMM Y[m][n] = sum_k A[m][k] B[n][k] (fp32).

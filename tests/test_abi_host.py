@@ -480,6 +480,51 @@ def test_validation_qgemv_batch(qg):
     assert g(arr2, 2, 4, A, 1, ys0, 0, None) == 1
 
 
+def test_batch_workspace_bytes(qg):
+    # sizes on the 256-CU part (the library's count when no device answers):
+    # 4 splits x 256 tiles x 64 lanes x 16 B of partial tiles, then 64 row
+    # blocks of 4 tiles, one 4-B counter each, rounded up to 256 B
+    l = qg.lib()
+    if torch.cuda.device_count() > 0:
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        if cus != 256:
+            pytest.skip("sizes below are for 256 CUs")
+    f = l.qg_qgemv_batch_workspace_bytes
+    assert f(4096, 4096, 16) == 4 * 256 * 64 * 16 + 256
+    assert f(4096, 11008, 4) == 4 * 256 * 64 * 16 + 256
+    assert f(777, 4096, 7) == 4 * 49 * 64 * 16 + 256     # 49 tiles, one per row block
+    assert f(4096, 16384, 16) > 0                        # 64 units per split: 8 per wave
+    assert f(4096, 16384 + 128, 16) == 0                 # 9 per wave: no split
+    assert f(4097, 4096, 16) == 0                        # more tiles than CUs
+    assert f(4096, 4096, 1) == 0                         # one token: batch-1 kernel
+    assert f(4096, 4096, 17) == 0
+    assert f(4096, 192, 4) == 0                          # invalid k
+    assert f(0, 4096, 4) == 0
+
+
+@needs_no_gpu
+def test_validation_qgemv_batch_ws(qg):
+    l = qg.lib()
+    f = l.qg_qgemv_batch_ws
+    need = l.qg_qgemv_batch_workspace_bytes(4096, 4096, 16)
+    w = qg.CWeight(0, 0, 4096, 4096, A, None, A, None)
+    # (w, m, x, xt, y, yt, ws, ws_bytes, stream)
+    assert f(None, 16, A, 1, A, 0, A, need, None) == 1
+    assert f(ctypes.byref(w), 16, A, 1, A, 0, None, need, None) == 5       # no workspace
+    assert f(ctypes.byref(w), 16, A, 1, A, 0, A, need - 1, None) == 5      # too small
+    assert f(ctypes.byref(w), 16, A, 1, A, 0, U, need, None) == 3          # misaligned workspace
+    assert f(ctypes.byref(w), 16, U, 1, A, 0, A, need, None) == 3
+    assert f(ctypes.byref(w), 16, A, 0, A, 0, A, need, None) == 4          # x must be bf16
+    assert f(ctypes.byref(w), 16, A, 1, A, 2, A, need, None) == 4
+    assert f(ctypes.byref(w), 16, None, 1, A, 0, A, need, None) == 1
+    wt = qg.CWeight(1, 0, 4096, 4096, A, None, A, None)
+    assert f(ctypes.byref(wt), 16, A, 1, A, 0, A, need, None) == 4         # int8 weights only
+    # shapes without a split fall through to qg_qgemv_batch's checks
+    assert f(ctypes.byref(w), 17, A, 1, A, 0, None, 0, None) == 2
+    wk = qg.CWeight(0, 0, 4096, 192, A, None, A, None)
+    assert f(ctypes.byref(wk), 4, A, 1, A, 0, None, 0, None) == 2
+
+
 @needs_no_gpu
 def test_validation_mxfp4(qg):
     l = qg.lib()

@@ -1,5 +1,5 @@
 """GPU parity of the small-batch weight-only product (qg_qgemv_batch,
-qg_qgemv_batch_grouped) against the oracle's fp64 reference computed from
+qg_qgemv_batch_grouped, qg_qgemv_batch_ws) against the oracle's fp64 reference computed from
 the oracle's own int8 codes.
 
 fp32 outputs: within 1e-5 normwise (the products are exact; only the fp32
@@ -139,3 +139,83 @@ def test_qgemv_batch_grouped_qkv_16_tokens(qg):
         q_ref, s_ref = oracle.quantize_absmax(np.ascontiguousarray(w[rows]), per_row=True)
         y_ref = oracle.y_w8a16_batch(q_ref, s_ref, xb)
         assert oracle.normwise_error(host(y)[:, rows], y_ref) <= TOL_F32
+
+
+def _workspace(qg, n, k, m):
+    need = qg.batch_workspace_bytes(n, k, m)
+    return need, torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("n,k,m", [(4096, 4096, 16), (4096, 11008, 16), (4096, 11008, 4), (4096, 4096, 2),
+                                   # ragged rows: 49 tiles, one per row block; 250 tiles in row
+                                   # blocks of 4, the last of 2 tiles, its last tile of 6 rows
+                                   (777, 4096, 7), (3990, 2048, 16),
+                                   # K splits with no units (k = 128: two units, four splits)
+                                   (16, 128, 3),
+                                   # ragged units per wave (18 units: 5, 5, 5, 3 per split)
+                                   (100, 1152, 9),
+                                   # the largest K with register-resident activations: 8 units per wave
+                                   (4096, 16384, 16)])
+def test_qgemv_batch_splitk(qg, n, k, m):
+    note("qgemv batch split-K %dx%d m=%d" % (n, k, m))
+    need, ws = _workspace(qg, n, k, m)
+    assert need > 0
+    w, xb = _case(n, k, m, 5 * n + k + m)
+    W, wq, s_w = _weight(qg, w)
+    q_ref, s_ref = oracle.quantize_absmax(w, per_row=True)
+    assert np.array_equal(host(wq), q_ref) and np.array_equal(host(s_w), s_ref)
+    y_ref = oracle.y_w8a16_batch(q_ref, s_ref, xb)
+    xd = dev_bf16(xb)
+    full32, y32 = _guarded2(m, n, torch.float32)
+    qg.qgemv_batch(W, xd, y=y32, ws=ws)
+    fullb, yb = _guarded2(m, n, torch.bfloat16)
+    qg.qgemv_batch(W, xd, y=yb, ws=ws)
+    y32_h, yb_h = host(y32), host(yb)
+    assert oracle.normwise_error(y32_h, y_ref) <= TOL_F32
+    check_bf16_output(yb_h.ravel(), y32_h.ravel(), y_ref.ravel())
+    assert canaries_intact(full32, m * n) and canaries_intact(fullb, m * n)
+    # every call leaves the row-block counters at zero (they follow the
+    # partial tiles: 4 splits x tiles x 64 lanes x 16 B)
+    tiles = (n + 15) // 16
+    assert not host(ws)[4 * tiles * 64 * 16:].any()
+    # deterministic: the partials are added in split order whichever
+    # workgroup finishes last
+    again = qg.qgemv_batch(W, xd, y_dtype=torch.float32, ws=ws)
+    assert np.array_equal(host(again), y32_h)
+    # the same definition as the unsplit launch, to rounding
+    y_plain = host(qg.qgemv_batch(W, xd, y_dtype=torch.float32))
+    assert oracle.normwise_error(y_plain, y_ref) <= TOL_F32
+
+
+def test_qgemv_batch_splitk_shapes_alternate(qg):
+    # one workspace, calls of two shapes in turn (o: 4096 x 4096, down:
+    # 4096 x 11008, the sizes the decode step alternates) and two token counts
+    note("qgemv batch split-K alternating shapes on one workspace")
+    need = max(qg.batch_workspace_bytes(4096, 4096, 16), qg.batch_workspace_bytes(4096, 11008, 16))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    cases = []
+    for j, (k, m) in enumerate([(4096, 16), (11008, 16), (4096, 5), (11008, 3)]):
+        w, xb = _case(4096, k, m, 300 + j)
+        W, _, _ = _weight(qg, w)
+        q_ref, s_ref = oracle.quantize_absmax(w, per_row=True)
+        cases.append((W, dev_bf16(xb), oracle.y_w8a16_batch(q_ref, s_ref, xb)))
+    for rep in range(2):
+        for W, xd, y_ref in cases:
+            y = qg.qgemv_batch(W, xd, y_dtype=torch.float32, ws=ws)
+            assert oracle.normwise_error(host(y), y_ref) <= TOL_F32
+    assert not host(ws)[4 * 256 * 64 * 16:].any()
+
+
+@pytest.mark.parametrize("n,k,m", [(5000, 4096, 16), (4096, 4096, 1), (64, 32768, 8)])
+def test_qgemv_batch_ws_without_split(qg, n, k, m):
+    # shapes with no split (more tiles than CUs, one token, k beyond the
+    # register-resident fragments) run qg_qgemv_batch: bit-identical
+    note("qgemv batch ws fallback %dx%d m=%d" % (n, k, m))
+    assert qg.batch_workspace_bytes(n, k, m) == 0
+    w, xb = _case(n, k, m, 400 + m)
+    W, _, _ = _weight(qg, w)
+    xd = dev_bf16(xb)
+    ws = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    y1 = qg.qgemv_batch(W, xd, y_dtype=torch.float32, ws=ws)
+    y0 = qg.qgemv_batch(W, xd, y_dtype=torch.float32)
+    assert np.array_equal(host(y1), host(y0))
