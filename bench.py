@@ -287,8 +287,9 @@ def profile_workload(args):
     del src, dst
     h = build_headline(torch, qg, synth, dev, args.layers)
     twice("decode_step_w8a16", h["launches"])
-    twice("small_batch_decode_step_m16", small_batch_launches(torch, qg, dev, h["weights"], 16))
-    del h
+    tiled = tiled_weights(qg, h["weights"])
+    twice("small_batch_decode_step_m16", small_batch_launches(torch, qg, dev, tiled, 16))
+    del h, tiled
     torch.cuda.empty_cache()
     full, _, _, _ = build_prefill(torch, qg, synth, dev, cur_stream)
     twice("prefill_w8a8_outlier", [full])
@@ -702,53 +703,65 @@ def bench_sep_threshold(torch, qg, synth, dev, rotate_count):
     return out
 
 
-def small_batch_launches(torch, qg, dev, weights, m, split=True):
+def small_batch_launches(torch, qg, dev, weights, m):
     """Launch closures of the decode step for a batch of m tokens: per layer
-    (q, k, v) and (gate, up) grouped, o and down single launches with K split
-    over workgroups (qg_qgemv_batch_ws, one shared workspace: the launches run
-    in stream order) where the shape allows it."""
+    (q, k, v) and (gate, up) grouped, o and down single launches through
+    qg_qgemv_batch_ws (one shared workspace, the launches run in stream
+    order; the library splits K where that pays, i.e. for down).  `weights`
+    holds row-major or 16-row tiled matrices."""
     per_layer = 7
     layers = len(weights) // per_layer
     xs = {k: torch.randn(m, k, device=dev).to(torch.bfloat16) for k in (4096, 11008)}
     ys = [torch.empty((m, W.n), dtype=torch.bfloat16, device=dev) for _, W, _ in weights[:per_layer]]
-    need = max(qg.batch_workspace_bytes(W.n, W.k, m) for _, W, _ in weights[:per_layer]) if split else 0
+    need = max(qg.batch_workspace_bytes(W.n, W.k, m) for _, W, _ in weights[:per_layer])
     wsb = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
     launches = []
     for li in range(layers):
         for grp in [[0, 1, 2], [3], [4, 5], [6]]:
             ws_ = [weights[li * per_layer + i][1] for i in grp]
             yy = [ys[i] for i in grp]
-            if len(grp) == 1 and need > 0:
+            if len(grp) == 1:
                 launches.append((lambda W, y: (lambda: qg.qgemv_batch(W, xs[W.k], y=y, ws=wsb)))(ws_[0], yy[0]))
             else:
                 launches.append((lambda ws_, yy: (lambda: qg.qgemv_batch_grouped(ws_, xs[ws_[0].k], ys=yy)))(ws_, yy))
     return launches
 
 
+def tiled_weights(qg, weights):
+    """The step's matrices with their codes in 16-row tiles (qg_pack_tiles16)."""
+    return [(name, qg.tiled16(W), x) for name, W, x in weights]
+
+
 def bench_small_batch(torch, qg, dev, weights, batches=(4, 16)):
     """The headline's decode step (32 layers, the same weights and the same
-    four launches per layer) for a batch of M tokens."""
+    four launches per layer) for a batch of M tokens, on the weights in the
+    16-row tiled layout (and, for reference, on the row-major codes)."""
     step_bytes = sum(W.n * W.k + 4 * W.n for _, W, _ in weights)
+    tiled = tiled_weights(qg, weights)
+    torch.cuda.synchronize()
     out = {}
     for m in batches:
         mark(torch, qg, "small_batch_decode_step_m%d" % m)
         secs = {}
-        for split in (True, False):
-            t = Timed(torch, small_batch_launches(torch, qg, dev, weights, m, split))
+        for lay, ws_ in (("tiled", tiled), ("row_major", weights)):
+            t = Timed(torch, small_batch_launches(torch, qg, dev, ws_, m))
             t.run(1)
-            secs[split] = t.run(5)
+            secs[lay] = t.run(5)
             n_launch = t.n
             del t
-        sec = secs[True]
+        sec = secs["tiled"]
         out["small_batch_decode_step_m%d" % m] = {
             "tokens": m, "ms_per_step": round(sec * 1e3, 4), "tokens_per_s": round(m / sec, 1),
             "weight_GBps": round(step_bytes / sec / 1e9, 1), "hbm_frac": round(step_bytes / sec / 1e9 / HBM_PEAK_GBS, 4),
             "launches_per_step": n_launch,
-            "ms_per_step_without_split_k": round(secs[False] * 1e3, 4),
-            "note": "32 layers x (q,k,v grouped, o, (gate,up) grouped, down), bf16 MFMA on int8 codes widened in "
-                    "registers; o and down with K split over workgroups"}
-        log("small batch m=%d: %.3f ms per step (%.3f without split K), %.0f tokens/s"
-            % (m, sec * 1e3, secs[False] * 1e3, m / sec))
+            "ms_per_step_row_major_codes": round(secs["row_major"] * 1e3, 4),
+            "note": "32 layers x (q,k,v grouped, o, (gate,up) grouped, down) on int8 codes in 16-row tiles "
+                    "(qg_pack_tiles16), widened to bf16 in registers for the MFMAs; down with K split over "
+                    "workgroups"}
+        log("small batch m=%d: %.3f ms per step (%.3f on row-major codes), %.0f tokens/s"
+            % (m, sec * 1e3, secs["row_major"] * 1e3, m / sec))
+    del tiled
+    torch.cuda.empty_cache()
     return out
 
 

@@ -76,6 +76,8 @@ typedef int32_t qg_status;
                               /* in [-128, 127], s_r[n] and a zero-point z_r[n]     */
 #define QG_WFMT_TERNARY3   5  /* ternary, five per byte in base 3 (1.6 bits per     */
                               /* weight), [n][16 ceil(k/80)], per-tensor gamma      */
+#define QG_WFMT_INT8_T16   6  /* the codes of QG_WFMT_INT8 in 16-row tiles for the  */
+                              /* batch products (qg_pack_tiles16), s_w[n]           */
 
 /* activation modes of qg_qgemv */
 #define QG_ACT_INT8  0  /* x is quantized per tensor (absmax int8) inside the call */
@@ -322,6 +324,26 @@ qg_status qg_pack_base3(const int8_t* codes, int64_t n, int64_t k, uint8_t* pack
 qg_status qg_unpack_base3(const uint8_t* packed, int64_t n, int64_t k, int8_t* codes, void* stream);
 
 /*
+ * Int8 codes rearranged for the small-batch products' matrix-core fragments
+ * (a layout of this library; the pages fix none).  Rows go in tiles of 16
+ * (the last one zero-padded), k in units of 64: tile t, unit c is one
+ * contiguous 1 KB block at byte (t * k/64 + c) * 1024, whose bytes
+ * 16 L .. 16 L + 15 (L = 16 g + i; g < 4, i < 16) are the codes
+ * [16 t + i][64 c + 16 g .. 64 c + 16 g + 15].  Lane L of a wave loads
+ * exactly those 16 bytes as its fragment of row i, so one load instruction
+ * reads one whole block; with row-major codes the same fragments take 64
+ * bytes from each of 16 rows.  Same codes and scales as the row-major
+ * matrix: as qg_weight, fmt QG_WFMT_INT8_T16 with codes = the tiled buffer;
+ * qg_qgemv_batch, qg_qgemv_batch_grouped and qg_qgemv_batch_ws take it and
+ * give results identical to the row-major matrix's.
+ * codes: [n][k] int8, 16-B aligned;  out: qg_tiles16_bytes(n, k) bytes
+ * (16 ceil(n/16) k), 16-B aligned.  k % 128 == 0, k <= QG_BATCH_MAX_K;
+ * 1 <= n < 2^31.  qg_tiles16_bytes returns 0 for shapes outside these.
+ */
+int64_t qg_tiles16_bytes(int64_t n, int64_t k);
+qg_status qg_pack_tiles16(const int8_t* codes, int64_t n, int64_t k, int8_t* out, void* stream);
+
+/*
  * A quantized weight matrix, described on the host (the struct lives in host
  * memory; its pointers are device pointers, all 16-B aligned).
  *   QG_WFMT_INT8      : codes = int8 [n][k];           scale = s_w[n]
@@ -410,11 +432,14 @@ qg_status qg_qgemv_grouped(const qg_weight* w, int32_t count, int32_t amode, con
  * i.e. qg_qgemv's INT8 / QG_ACT_FLOAT product of each row of x; the
  * products are exact and summed in fp32 (in another order than qg_qgemv's,
  * so results agree to rounding, not bit for bit).
- * w  : QG_WFMT_INT8 (codes [n][k] int8, scale = s_w[n]), 16-B aligned codes.
+ * w  : QG_WFMT_INT8 (codes [n][k] int8, scale = s_w[n]) or the same codes in
+ *      16-row tiles (QG_WFMT_INT8_T16, qg_pack_tiles16; same results); 16-B
+ *      aligned codes.  A grouped launch takes one layout for all matrices.
  * x  : [m][k] bf16 (xt must be QG_BF16), 16-B aligned; 1 <= m <= QG_BATCH_MAX_M.
  * y  : [m][n] of type yt (QG_F32 or QG_BF16, bf16 rounded to nearest even).
  * k % 128 == 0, 128 <= k <= QG_BATCH_MAX_K; 1 <= n < 2^31.
- * m = 1 (with k <= QG_QGEMV_MAX_K) runs qg_qgemv's batch-1 kernel.
+ * m = 1 (with k <= QG_QGEMV_MAX_K, row-major codes) runs qg_qgemv's batch-1
+ * kernel.
  * The grouped form runs count (1..QG_MAX_GROUP) matrices that share k, m and
  * x in one launch (q, k and v; gate and up); w and y are HOST arrays of
  * count entries, y[j] holding [m][w[j].n] outputs.
@@ -424,7 +449,7 @@ qg_status qg_qgemv_batch(const qg_weight* w, int32_t m, const void* x, int32_t x
 
 /*
  * qg_qgemv_batch with K split over workgroups, for a single matrix of at
- * most (CUs x 16) rows and k <= 16384 (the o and down projections at the
+ * most (CUs x 16) rows and 8192 <= k <= 16384 (the down projection at the
  * decode shapes): a workgroup takes up to four 16-row tiles and a quarter of
  * k, so it reads each activation row once for all its tiles instead of once
  * per tile.  Same definition as qg_qgemv_batch; the four partial sums of
@@ -435,8 +460,9 @@ qg_status qg_qgemv_batch(const qg_weight* w, int32_t m, const void* x, int32_t x
  *            be zero before the first call (e.g. zero-filled at allocation);
  *            every call leaves them zero.  Calls that overlap on one
  *            workspace race.
- * When that size is 0 (m = 1, more tiles than CUs, or k too large) the call
- * is qg_qgemv_batch and ws is not used.  Other arguments and checks as
+ * When that size is 0 (m = 1, more tiles than CUs, k below 8192 -- where the
+ * partials' round trips through memory cost more than they save -- or k
+ * above 16384) the call is qg_qgemv_batch and ws is not used.  Other arguments and checks as
  * qg_qgemv_batch.
  */
 size_t qg_qgemv_batch_workspace_bytes(int64_t n, int64_t k, int32_t m);

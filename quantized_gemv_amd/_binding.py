@@ -22,6 +22,7 @@ QG_OK = 0
 QG_F32, QG_BF16 = 0, 1
 QG_PER_TENSOR, QG_PER_ROW = 0, 1
 QG_WFMT_INT8, QG_WFMT_TERNARY2, QG_WFMT_SIGN1_RES8, QG_WFMT_Q4K, QG_WFMT_SIGN1_RES8Z, QG_WFMT_TERNARY3 = 0, 1, 2, 3, 4, 5
+QG_WFMT_INT8_T16 = 6
 QG_ACT_INT8, QG_ACT_FLOAT = 0, 1
 QG_MAX_OUTLIERS = 256
 QG_QGEMV_MAX_K = 32768
@@ -85,6 +86,8 @@ _SIGS = {
     "qg_pack": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp]),
     "qg_base3_row_bytes": (_c_i64, [_c_i64]),
     "qg_pack_base3": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp]),
+    "qg_tiles16_bytes": (_c_i64, [_c_i64, _c_i64]),
+    "qg_pack_tiles16": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp]),
     "qg_unpack_base3": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp]),
     "qg_unpack": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp]),
     "qg_qgemv": (_c_i32, [ctypes.POINTER(CWeight), _c_i32, _c_vp, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp]),
@@ -311,6 +314,30 @@ def pack_base3(codes: torch.Tensor, out: torch.Tensor = None):
     out = torch.empty((n, rb), dtype=torch.uint8, device=codes.device) if out is None else out
     _check(lib().qg_pack_base3(_p(codes), n, k, _p(out), _stream(codes)), "qg_pack_base3")
     return out
+
+
+def pack_tiles16(codes: torch.Tensor, out: torch.Tensor = None):
+    """Int8 codes [n][k] in 16-row tiles for the batch products
+    (qg_pack_tiles16): returns a flat int8 tensor of qg_tiles16_bytes(n, k)."""
+    _dev(codes, "codes", torch.int8)
+    if codes.dim() != 2:
+        raise ValueError("codes must be [n][k]")
+    n, k = codes.shape
+    nb = int(lib().qg_tiles16_bytes(n, k))
+    if nb == 0:
+        raise ValueError("shape (%d, %d) has no 16-row tiled layout" % (n, k))
+    out = torch.empty(nb, dtype=torch.int8, device=codes.device) if out is None else out
+    if out.numel() < nb:
+        raise ValueError("out holds %d bytes, %d needed" % (out.numel(), nb))
+    _check(lib().qg_pack_tiles16(_p(codes), n, k, _p(out), _stream(codes)), "qg_pack_tiles16")
+    return out
+
+
+def tiled16(w: "QWeight") -> "QWeight":
+    """The QG_WFMT_INT8 matrix w with its codes in 16-row tiles."""
+    if w.fmt != QG_WFMT_INT8:
+        raise ValueError("tiled16 takes QG_WFMT_INT8 weights")
+    return QWeight(QG_WFMT_INT8_T16, w.n, w.k, pack_tiles16(w.codes.view(w.n, w.k)), w.scale)
 
 
 def unpack_base3(packed: torch.Tensor, k: int):

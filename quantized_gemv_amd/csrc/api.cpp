@@ -288,6 +288,18 @@ int64_t qg_base3_row_bytes(int64_t k) {
     return 16 * ((k + 79) / 80);
 }
 
+int64_t qg_tiles16_bytes(int64_t n, int64_t k) {
+    if (n < 1 || n >= ((int64_t)1 << 31) || k < 128 || k % 128 != 0 || k > QG_BATCH_MAX_K) return 0;
+    return qg::tiles16_bytes(n, k);
+}
+
+qg_status qg_pack_tiles16(const int8_t* codes, int64_t n, int64_t k, int8_t* out, void* stream) {
+    if (!codes || !out) return QG_ERR_NULLPTR;
+    if (qg_tiles16_bytes(n, k) == 0) return QG_ERR_SHAPE;
+    if (!aligned16(codes) || !aligned16(out)) return QG_ERR_ALIGN;
+    return from_hip(qg::launch_pack_tiles16(codes, n, k, out, as_stream(stream)));
+}
+
 qg_status qg_pack_base3(const int8_t* codes, int64_t n, int64_t k, uint8_t* packed, void* stream) {
     if (!codes || !packed) return QG_ERR_NULLPTR;
     if (n < 1 || k < 1 || n > ((int64_t)1 << 40) / k) return QG_ERR_SHAPE;
@@ -392,7 +404,8 @@ qg_status qg_qgemv_batch_grouped(const qg_weight* w, int32_t count, int32_t m, c
     for (int32_t j = 0; j < count; ++j) {
         const qg_weight& wj = w[j];
         if (!wj.codes || !wj.scale || !y[j]) return QG_ERR_NULLPTR;
-        if (wj.fmt != QG_WFMT_INT8) return QG_ERR_ARG;
+        if (wj.fmt != QG_WFMT_INT8 && wj.fmt != QG_WFMT_INT8_T16) return QG_ERR_ARG;
+        if (wj.fmt != w[0].fmt) return QG_ERR_ARG;  // one layout per launch
         if (wj.n < 1 || wj.n >= ((int64_t)1 << 31)) return QG_ERR_SHAPE;
         if (wj.k < 128 || wj.k % 128 != 0 || wj.k > QG_BATCH_MAX_K || wj.k != w[0].k) return QG_ERR_SHAPE;
         if (!aligned16(wj.codes)) return QG_ERR_ALIGN;
@@ -404,8 +417,9 @@ qg_status qg_qgemv_batch_grouped(const qg_weight* w, int32_t count, int32_t m, c
         a[j].x = x;
         a[j].y = y[j];
         a[j].yt = yt;
+        a[j].t16 = wj.fmt == QG_WFMT_INT8_T16;
     }
-    if (m == 1 && w[0].k <= QG_QGEMV_MAX_K) {
+    if (m == 1 && w[0].k <= QG_QGEMV_MAX_K && w[0].fmt == QG_WFMT_INT8) {
         // one token: the batch-1 kernel (same definition, y [1][n] is y [n])
         qg::QgemvArgs b[QG_MAX_GROUP];
         for (int32_t j = 0; j < count; ++j) b[j] = qgemv_args(&w[j], QG_ACT_FLOAT, x, xt, y[j], yt, nullptr);
@@ -432,7 +446,7 @@ qg_status qg_qgemv_batch_ws(const qg_weight* w, int32_t m, const void* x, int32_
     const size_t need = qg_qgemv_batch_workspace_bytes(w->n, w->k, m);
     if (need == 0) return qg_qgemv_batch(w, m, x, xt, y, yt, stream);  // no split for this shape
     if (!x || !y || !w->codes || !w->scale) return QG_ERR_NULLPTR;
-    if (w->fmt != QG_WFMT_INT8) return QG_ERR_ARG;
+    if (w->fmt != QG_WFMT_INT8 && w->fmt != QG_WFMT_INT8_T16) return QG_ERR_ARG;
     if (xt != QG_BF16 || (yt != QG_F32 && yt != QG_BF16)) return QG_ERR_ARG;
     if (!aligned16(x) || !aligned16(w->codes)) return QG_ERR_ALIGN;
     if (!ws || ws_bytes < need) return QG_ERR_WORKSPACE;
@@ -446,6 +460,7 @@ qg_status qg_qgemv_batch_ws(const qg_weight* w, int32_t m, const void* x, int32_
     a.x = x;
     a.y = y;
     a.yt = yt;
+    a.t16 = w->fmt == QG_WFMT_INT8_T16;
     return from_hip(qg::launch_qgemv_batch_splitk(a, ws, as_stream(stream)));
 }
 

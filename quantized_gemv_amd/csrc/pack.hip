@@ -1,5 +1,6 @@
 // pack.hip -- bit packing of ternary (2-bit), sign (1-bit) and base-3
-// ternary (five per byte) codes.
+// ternary (five per byte) codes; int8 codes in 16-row tiles for the
+// small-batch products.
 //
 // Layout: code k of a row sits in byte k / v at bit offset bits * (k % v),
 // least significant field first, v = 8 / bits.  Since every row length is a
@@ -112,6 +113,31 @@ hipError_t launch_unpack(const uint8_t* packed, int64_t count, int bits, int8_t*
     if (nbytes == 0) return hipSuccess;
     if (bits == 2) unpack2_kernel<<<pack_grid(nbytes), kThreads, 0, st>>>(packed, nbytes, codes);
     else unpack1_kernel<<<pack_grid(nbytes), kThreads, 0, st>>>(packed, nbytes, codes);
+    return hipGetLastError();
+}
+
+// 16-row tiles: output chunk q (16 bytes) is lane L = q % 64 of unit
+// c = (q / 64) % C of tile t = q / (64 C): row 16 t + L % 16, codes
+// 64 c + 16 (L / 16) .. + 15; rows past n are zeros.  Writes are contiguous.
+__global__ __launch_bounds__(kThreads) void pack_tiles16_kernel(const int8_t* codes, int64_t n, int64_t k,
+                                                                int64_t chunks, int8_t* out) {
+    const int64_t C = k / 64;
+    for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < chunks; q += (int64_t)gridDim.x * kThreads) {
+        const int L = (int)(q & 63);
+        const int64_t c = (q >> 6) % C;
+        const int64_t t = (q >> 6) / C;
+        const int64_t row = 16 * t + (L & 15);
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (row < n) v = *reinterpret_cast<const u32x4*>(codes + row * k + 64 * c + 16 * (L >> 4));
+        *reinterpret_cast<u32x4*>(out + 16 * q) = v;
+    }
+}
+
+int64_t tiles16_bytes(int64_t n, int64_t k) { return (n + 15) / 16 * 16 * k; }
+
+hipError_t launch_pack_tiles16(const int8_t* codes, int64_t n, int64_t k, int8_t* out, hipStream_t st) {
+    const int64_t chunks = tiles16_bytes(n, k) / 16;
+    pack_tiles16_kernel<<<pack_grid(chunks), kThreads, 0, st>>>(codes, n, k, chunks, out);
     return hipGetLastError();
 }
 

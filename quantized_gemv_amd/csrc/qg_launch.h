@@ -48,6 +48,8 @@ hipError_t launch_quantize_q4k(const float* w, int64_t n, int64_t k, uint8_t* co
 hipError_t launch_pack(const int8_t* codes, int64_t count, int bits, uint8_t* packed, hipStream_t st);
 hipError_t launch_unpack(const uint8_t* packed, int64_t count, int bits, int8_t* codes, hipStream_t st);
 hipError_t launch_pack3(const int8_t* codes, int64_t n, int64_t k, uint8_t* packed, hipStream_t st);
+int64_t tiles16_bytes(int64_t n, int64_t k);
+hipError_t launch_pack_tiles16(const int8_t* codes, int64_t n, int64_t k, int8_t* out, hipStream_t st);
 hipError_t launch_unpack3(const uint8_t* packed, int64_t n, int64_t k, int8_t* codes, hipStream_t st);
 
 struct QgemvArgs {
@@ -113,6 +115,7 @@ struct BatchArgs {
     const void* x;
     void* y;
     int yt;
+    bool t16;  // codes in 16-row tiles (else row-major)
 };
 hipError_t launch_qgemv_batch(const BatchArgs* a, int count, hipStream_t st);
 // One matrix with K split over workgroups (partials and row-block counters

@@ -55,7 +55,7 @@ struct BMat {
     int32_t n;
 };
 struct BGroup {
-    int32_t count, k, m;
+    int32_t count, k, m, t16;
     const uint16_t* x;
     int32_t wg_start[kMaxGroupLaunch + 1];
     BMat mats[kMaxGroupLaunch];
@@ -79,7 +79,13 @@ __device__ __forceinline__ void widen16(const u32x4& w, bf16x8& a0, bf16x8& a1) 
     a1 = __builtin_bit_cast(bf16x8, u32x4{h[4], h[5], h[6], h[7]});
 }
 
-template <int YT, bool XL>
+// Weight fragments: lane L = 16 g + i takes the 16 codes of row i of the
+// tile, k = 64 c + 16 g .. + 15.  Row-major codes hold them at i K + 64 c +
+// 16 g of the tile (64 bytes of each of 16 rows per load); the 16-row tiled
+// layout at 1024 c + 16 L (one contiguous 1 KB block per load, so the loads
+// can be non-temporal).  A tile is 16 K bytes in both (the tiled one
+// zero-padded past the last row).
+template <int YT, bool XL, bool T16>
 __global__ __launch_bounds__(kBThreads) void qgemv_batch_kernel(BGroup grp) {
     __shared__ f32x4 part[kBWaves][kWave];
     extern __shared__ u32x4 xsh[];  // XL: [wave][unit][xa | xb][lane]
@@ -130,15 +136,17 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_kernel(BGroup grp) {
             const int row = 4 * g + r;
             f.sw[r] = __uint_as_float(load4(rs, row < t.rows ? (uint32_t)(4 * row) : (uint32_t)(t.rows * 4)));
         }
-        const __amdgpu_buffer_rsrc_t rw = make_rsrc(t.mat->wq + (int64_t)t.row0 * K, (uint32_t)(t.rows * K));
-        const uint32_t oob_w = (uint32_t)(t.rows * K);
+        // the tiled layout's last tile is padded to 16 rows (zeros)
+        const uint32_t oob_w = (uint32_t)((T16 && t.rows > 0 ? 16 : t.rows) * K);
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(t.mat->wq + (int64_t)t.row0 * K, oob_w);
 #pragma unroll
         for (int j = 0; j < kBJS; ++j) {
             const int u = kBJS * itn + j;
             const int c = wave * most + u;  // this wave's contiguous range of units
             const bool ok = u < most && c < C && t.rows > 0;
             const int kk = c * kBUnit + 16 * g;
-            f.w[j] = load16(rw, (ok && i < t.rows) ? (uint32_t)(i * K + kk) : oob_w);
+            if constexpr (T16) f.w[j] = load16_nt(rw, ok ? (uint32_t)(c * 1024 + lane * 16) : oob_w);  // whole 1 KB blocks
+            else f.w[j] = load16(rw, (ok && i < t.rows) ? (uint32_t)(i * K + kk) : oob_w);
             if constexpr (!XL) {
                 const uint32_t xo = (uint32_t)((i * K + kk) * 2);
                 f.xa[j] = load16(rx, (ok && i < M) ? xo : oob_x);
@@ -247,6 +255,368 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_kernel(BGroup grp) {
     }
 }
 
+// ------------------------------------------------- activations in LDS
+// Grouped launches with more 16-row tiles than CUs and K <= 4608: one
+// workgroup per CU holds the activation fragments of all of K in LDS (wave
+// w keeps those of its MOST units, written once) and walks its tiles
+// blockIdx.x + gridDim.x * j.  Per tile a wave loads its MOST units of
+// weights (16 rows x 64 k each) and the tile's row scales in one go, the
+// next tile's loads in flight while it multiplies; MOST is a template
+// parameter, so there is no branch between the loads and the products.
+// The waves' partial tiles meet in LDS (two buffers, one barrier per tile)
+// and wave j % 8 reduces tile j, so the reductions are spread over the
+// waves and the others go on to the next tile at once.  The same products
+// and the same summation order as the tile loop above.
+template <int YT, int MOST>
+__global__ __launch_bounds__(kBThreads) void qgemv_batch_xl_kernel(BGroup grp) {
+    __shared__ f32x4 part[2][kBWaves][kWave];
+    extern __shared__ u32x4 xsh[];  // [wave][unit][xa | xb][lane]
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int K = grp.k, M = grp.m;
+    const int i = lane & 15, g = lane >> 4;  // A row / B token, k group
+    const int C = K / kBUnit;
+    const int c0 = wave * MOST;  // this wave's units c0 .. c0 + MOST - 1 (those >= C read zeros)
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(grp.x, (uint32_t)(M * K * 2));
+    const uint32_t oob_x = (uint32_t)(M * K * 2);
+    const int ntiles = grp.wg_start[grp.count];
+    const int my_tiles =
+        ntiles > (int)blockIdx.x ? (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
+    u32x4* const xw = xsh + (size_t)wave * MOST * 2 * kWave;
+
+    // the tile's matrix, selected with constant indices into the kernel
+    // argument (a computed index would take it through memory and make the
+    // buffer descriptors non-uniform: a loop over lanes around every load)
+    struct Tile {
+        BMat mat;
+        int row0, rows;
+    };
+    auto tile_of = [&](int j) {
+        const int tile = (int)blockIdx.x + (int)gridDim.x * j;
+        Tile t;
+        t.mat = grp.mats[0];
+        int start = 0;
+#pragma unroll
+        for (int q = 1; q < kMaxGroupLaunch; ++q) {
+            if (q < grp.count && tile >= grp.wg_start[q]) {
+                t.mat = grp.mats[q];
+                start = grp.wg_start[q];
+            }
+        }
+        t.row0 = (tile - start) * 16;
+        t.rows = j < my_tiles ? min(16, t.mat.n - t.row0) : 0;  // past the last tile: nothing to read
+        return t;
+    };
+    struct Frag {
+        u32x4 w[MOST];
+        float sw[4];  // this lane's four row scales (used by the reducing wave)
+    };
+    auto issue = [&](int j, Frag& f) {
+        const Tile t = tile_of(j);
+        // the last tile is padded to 16 rows (zeros)
+        const uint32_t tile_bytes = (uint32_t)((t.rows > 0 ? 16 : 0) * K);
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(t.mat.wq + (int64_t)t.row0 * K, tile_bytes);
+#pragma unroll
+        for (int u = 0; u < MOST; ++u) {
+            const int c = c0 + u;
+            // whole 1 KB blocks, each read once: non-temporal
+            f.w[u] = load16_nt(rw, c < C ? (uint32_t)(c * 1024 + lane * 16) : tile_bytes);
+        }
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(t.mat.s_w + t.row0, (uint32_t)(t.rows * 4));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 4 * g + r;
+            f.sw[r] = __uint_as_float(load4(rs, row < t.rows ? (uint32_t)(4 * row) : (uint32_t)(t.rows * 4)));
+        }
+    };
+    auto consume = [&](int j, const Frag& f) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < MOST; ++u) {
+            bf16x8 a0, a1;
+            widen16(f.w[u], a0, a1);
+            const u32x4 xa = xw[(2 * u) * kWave + lane];
+            const u32x4 xb = xw[(2 * u + 1) * kWave + lane];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8, xa), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8, xb), acc, 0, 0, 0);
+        }
+        part[j & 1][wave][lane] = acc;
+        lds_barrier();
+        if (wave == j % kBWaves) {
+            const Tile t = tile_of(j);
+            f32x4 s = part[j & 1][0][lane];
+#pragma unroll
+            for (int v = 1; v < kBWaves; ++v) {
+                const f32x4 q = part[j & 1][v][lane];
+                s[0] += q[0];
+                s[1] += q[1];
+                s[2] += q[2];
+                s[3] += q[3];
+            }
+            const int tok = lane & 15;
+            if (tok < M) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 4 * g + r;
+                    if (row < t.rows) {
+                        const float o = s[r] / f.sw[r];
+                        const int64_t at = (int64_t)tok * t.mat.n + t.row0 + row;
+                        if constexpr (YT == 0) static_cast<float*>(t.mat.y)[at] = o;
+                        else static_cast<uint16_t*>(t.mat.y)[at] = (uint16_t)f32_to_bf16(o);
+                    }
+                }
+            }
+        }
+        // part[j & 1] is written again at tile j + 2, after every wave has
+        // passed tile j + 1's barrier, which the reducing wave reaches only
+        // after its reads above
+    };
+    // this wave's activation fragments (all requested, then the first tile's
+    // weights, then written to LDS: the writes wait for the activations
+    // while the weights stay in flight); each wave reads only what it wrote
+    Frag fa, fb;
+    {
+        u32x4 v0[MOST], v1[MOST];
+#pragma unroll
+        for (int u = 0; u < MOST; ++u) {
+            const int c = c0 + u;
+            const bool ok = c < C && i < M;
+            const uint32_t xo = (uint32_t)((i * K + c * kBUnit + 16 * g) * 2);
+            v0[u] = load16(rx, ok ? xo : oob_x);
+            v1[u] = load16(rx, ok ? xo + 16u : oob_x);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        issue(0, fa);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < MOST; ++u) {
+            xw[(2 * u) * kWave + lane] = v0[u];
+            xw[(2 * u + 1) * kWave + lane] = v1[u];
+        }
+    }
+    // two tiles per round, each buffer reloaded right after its products; a
+    // last round past my_tiles reads zeros and its tile stores nothing
+    for (int j = 0; j < my_tiles; j += 2) {
+        issue(j + 1, fb);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(j, fa);
+        if (j + 1 >= my_tiles) break;
+        issue(j + 2, fa);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(j + 1, fb);
+    }
+}
+
+template <int YT>
+static hipError_t launch_xl(int most, int grid, size_t lds, const BGroup& g, hipStream_t st) {
+    const void* fn = nullptr;
+    switch (most) {
+        case 1: fn = reinterpret_cast<const void*>(qgemv_batch_xl_kernel<YT, 1>); break;
+        case 2: fn = reinterpret_cast<const void*>(qgemv_batch_xl_kernel<YT, 2>); break;
+        case 3: fn = reinterpret_cast<const void*>(qgemv_batch_xl_kernel<YT, 3>); break;
+        case 4: fn = reinterpret_cast<const void*>(qgemv_batch_xl_kernel<YT, 4>); break;
+        case 5: fn = reinterpret_cast<const void*>(qgemv_batch_xl_kernel<YT, 5>); break;
+        case 6: fn = reinterpret_cast<const void*>(qgemv_batch_xl_kernel<YT, 6>); break;
+        case 7: fn = reinterpret_cast<const void*>(qgemv_batch_xl_kernel<YT, 7>); break;
+        case 8: fn = reinterpret_cast<const void*>(qgemv_batch_xl_kernel<YT, 8>); break;
+        case 9: fn = reinterpret_cast<const void*>(qgemv_batch_xl_kernel<YT, 9>); break;
+        default: return hipErrorInvalidValue;
+    }
+    static bool attr_set[10] = {false};
+    if (!attr_set[most]) {
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBatchXlMaxLds);
+        if (e != hipSuccess) return e;
+        attr_set[most] = true;
+    }
+    switch (most) {
+        case 1: qgemv_batch_xl_kernel<YT, 1><<<grid, kBThreads, lds, st>>>(g); break;
+        case 2: qgemv_batch_xl_kernel<YT, 2><<<grid, kBThreads, lds, st>>>(g); break;
+        case 3: qgemv_batch_xl_kernel<YT, 3><<<grid, kBThreads, lds, st>>>(g); break;
+        case 4: qgemv_batch_xl_kernel<YT, 4><<<grid, kBThreads, lds, st>>>(g); break;
+        case 5: qgemv_batch_xl_kernel<YT, 5><<<grid, kBThreads, lds, st>>>(g); break;
+        case 6: qgemv_batch_xl_kernel<YT, 6><<<grid, kBThreads, lds, st>>>(g); break;
+        case 7: qgemv_batch_xl_kernel<YT, 7><<<grid, kBThreads, lds, st>>>(g); break;
+        case 8: qgemv_batch_xl_kernel<YT, 8><<<grid, kBThreads, lds, st>>>(g); break;
+        default: qgemv_batch_xl_kernel<YT, 9><<<grid, kBThreads, lds, st>>>(g); break;
+    }
+    return hipGetLastError();
+}
+
+// ------------------------------------------ one tile per wave (tiled)
+// Grouped launches of 16-row tiled codes with more tiles than CUs and
+// K <= 4608: one workgroup per CU holds the activation fragments of all of
+// K in LDS (loaded once, one barrier), and each wave multiplies whole tiles
+// alone -- all K of its 16 rows -- so the waves never wait for each other.
+// A wave's tiles are blockIdx.x + gridDim.x (w + 8 q); its units (tile,
+// unit c) form one stream that a ring of D loads in flight runs through,
+// across tile ends (D divides the units per tile, so a tile ends between two
+// turns of the ring and the loop body has no memory operation under a
+// branch).  Per unit: the 1 KB block of codes (non-temporal, read once),
+// widened to bf16, and the two activation fragments of unit c from LDS into
+// two MFMAs; after a tile's last unit its 16 x 16 products are complete
+// (summed in unit order), rescaled by the row scales (scalar loads, issued
+// when the tile starts) and stored.
+typedef const __attribute__((address_space(4))) float cfloat;
+
+template <int YT, int D, int MG>
+__global__ __launch_bounds__(kBThreads) void qgemv_batch_wt_kernel(BGroup grp) {
+    extern __shared__ u32x4 xsh[];  // [unit][xa | xb][lane]
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int K = grp.k, M = grp.m;
+    const int i = lane & 15, g = lane >> 4;  // A row / B token, k group
+    const int C = K / kBUnit;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(grp.x, (uint32_t)(M * K * 2));
+    const uint32_t oob_x = (uint32_t)(M * K * 2);
+    const int ntiles = grp.wg_start[grp.count];
+    const int my_tiles =
+        ntiles > (int)blockIdx.x ? (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
+    const int wt = my_tiles > wave ? (my_tiles - wave + kBWaves - 1) / kBWaves : 0;  // this wave's tiles
+
+    struct Tile {
+        BMat mat;
+        int row0, rows;
+    };
+    // the wave's tile q, with its matrix selected by constant indices (the
+    // buffer descriptors stay uniform; MG >= count slots are looked at)
+    auto tile_of = [&](int q) {
+        const int tile = (int)blockIdx.x + (int)gridDim.x * (wave + kBWaves * q);
+        Tile t;
+        t.mat = grp.mats[0];
+        int start = 0;
+#pragma unroll
+        for (int mq = 1; mq < MG; ++mq) {
+            if (mq < grp.count && tile >= grp.wg_start[mq]) {
+                t.mat = grp.mats[mq];
+                start = grp.wg_start[mq];
+            }
+        }
+        t.row0 = (tile - start) * 16;
+        t.rows = q < wt ? min(16, t.mat.n - t.row0) : 0;
+        return t;
+    };
+    // the prefetch cursor: tile pq, unit pc, and the tile's codes (tiles
+    // past the wave's last read zeros)
+    int pq = 0, pc = 0;
+    __amdgpu_buffer_rsrc_t prw;
+    {
+        const Tile t = tile_of(0);
+        prw = make_rsrc(t.mat.wq + (int64_t)t.row0 * K, (uint32_t)((t.rows > 0 ? 16 : 0) * K));
+    }
+    auto fetch = [&]() -> u32x4 {
+        const u32x4 v = load16_nt(prw, (uint32_t)(pc * 1024 + lane * 16));
+        if (++pc == C) {
+            pc = 0;
+            ++pq;
+            const Tile t = tile_of(pq);
+            prw = make_rsrc(t.mat.wq + (int64_t)t.row0 * K, (uint32_t)((t.rows > 0 ? 16 : 0) * K));
+        }
+        return v;
+    };
+
+    // activations: wave w loads units w, w + 8, ... into their fragment
+    // slots (requested first, the ring's first D units after them)
+    u32x4 ring[D];
+    {
+        constexpr int kXU = (kBatchXlMaxLds / 2048 + kBWaves - 1) / kBWaves;  // units per wave at most
+        u32x4 v0[kXU], v1[kXU];
+#pragma unroll
+        for (int q = 0; q < kXU; ++q) {
+            const int c = wave + kBWaves * q;
+            const bool ok = c < C && i < M;
+            const uint32_t xo = (uint32_t)((i * K + c * kBUnit + 16 * g) * 2);
+            v0[q] = load16(rx, ok ? xo : oob_x);
+            v1[q] = load16(rx, ok ? xo + 16u : oob_x);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int d = 0; d < D; ++d) ring[d] = fetch();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < kXU; ++q) {
+            const int c = wave + kBWaves * q;
+            if (c < C) {
+                xsh[(2 * c) * kWave + lane] = v0[q];
+                xsh[(2 * c + 1) * kWave + lane] = v1[q];
+            }
+        }
+        lds_barrier();
+    }
+    for (int q = 0; q < wt; ++q) {
+        const Tile ct = tile_of(q);
+        // the tile's 16 row scales, rows clamped into the matrix (rows past
+        // it are never stored)
+        cfloat* const sp = (cfloat*)ct.mat.s_w;
+        float srow[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) srow[r] = sp[min(ct.row0 + r, ct.mat.n - 1)];
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int cb = 0; cb < C; cb += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int c = cb + d;
+                bf16x8 a0, a1;
+                widen16(ring[d], a0, a1);
+                const u32x4 xa = xsh[(2 * c) * kWave + lane];
+                const u32x4 xb = xsh[(2 * c + 1) * kWave + lane];
+                ring[d] = fetch();
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8, xa), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8, xb), acc, 0, 0, 0);
+            }
+        }
+        // lane l holds token l % 16, rows 4 (l / 16) + r
+        const int tok = lane & 15;
+        if (tok < M) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * g + r;
+                const float s = g == 0 ? srow[r] : g == 1 ? srow[4 + r] : g == 2 ? srow[8 + r] : srow[12 + r];
+                if (row < ct.rows) {
+                    const float o = acc[r] / s;
+                    const int64_t at = (int64_t)tok * ct.mat.n + ct.row0 + row;
+                    if constexpr (YT == 0) static_cast<float*>(ct.mat.y)[at] = o;
+                    else static_cast<uint16_t*>(ct.mat.y)[at] = (uint16_t)f32_to_bf16(o);
+                }
+            }
+        }
+    }
+}
+
+// ring depth: the largest power of two up to 16 that divides the units per tile
+static int wt_ring(int C) { return C % 16 == 0 ? 16 : C % 8 == 0 ? 8 : C % 4 == 0 ? 4 : 2; }
+
+template <int YT, int D, int MG>
+static hipError_t launch_wt_d(int grid, size_t lds, const BGroup& g, hipStream_t st) {
+    auto fn = qgemv_batch_wt_kernel<YT, D, MG>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBatchXlMaxLds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    fn<<<grid, kBThreads, lds, st>>>(g);
+    return hipGetLastError();
+}
+template <int YT, int MG>
+static hipError_t launch_wt_mg(int C, int grid, size_t lds, const BGroup& g, hipStream_t st) {
+    switch (wt_ring(C)) {
+        case 16: return launch_wt_d<YT, 16, MG>(grid, lds, g, st);
+        case 8: return launch_wt_d<YT, 8, MG>(grid, lds, g, st);
+        case 4: return launch_wt_d<YT, 4, MG>(grid, lds, g, st);
+        default: return launch_wt_d<YT, 2, MG>(grid, lds, g, st);
+    }
+}
+// matrix slots the kernel looks at: 1, 3 (q, k, v; gate, up) or all
+template <int YT>
+static hipError_t launch_wt(int C, int grid, size_t lds, const BGroup& g, hipStream_t st) {
+    if (g.count == 1) return launch_wt_mg<YT, 1>(C, grid, lds, g, st);
+    if (g.count <= 3) return launch_wt_mg<YT, 3>(C, grid, lds, g, st);
+    return launch_wt_mg<YT, kMaxGroupLaunch>(C, grid, lds, g, st);
+}
+
 // ---------------------------------------------------------------- split K
 // One matrix whose 16-row tiles number no more than the CUs (o, down at the
 // decode shapes): with one tile per workgroup, every workgroup would read all
@@ -294,11 +664,14 @@ static SkPlan splitk_plan(int64_t n, int64_t k) {
     return p;
 }
 
-// 0 when the split path does not apply: more tiles than CUs, or K per split
-// beyond the register-resident fragments
+// 0 when the split path does not apply: more tiles than CUs, K per split
+// beyond the register-resident fragments, or K below kSkMinK (there the
+// reduction's three memory round trips cost more than the activation reads
+// they save: 4096 x 4096 at 4 tokens 8.0 against 6.6 us unsplit, tiled)
+constexpr int64_t kSkMinK = 8192;
 size_t qgemv_batch_splitk_workspace(int64_t n, int64_t k) {
     const SkPlan p = splitk_plan(n, k);
-    if (p.tiles > device_cu_count() || p.most > kSkMaxUnits || p.most < 1) return 0;
+    if (k < kSkMinK || p.tiles > device_cu_count() || p.most > kSkMaxUnits || p.most < 1) return 0;
     const size_t parts = (size_t)kSkS * p.tiles * kWave * sizeof(f32x4);
     return parts + ((size_t)p.nrb * sizeof(uint32_t) + 255) / 256 * 256;
 }
@@ -316,7 +689,7 @@ struct SkParams {
 // MOST units of 64 k per wave, T tiles per workgroup: every load of the
 // workgroup's share is issued up front, with no branches between them and
 // the products, so the waits count down through the loads in order.
-template <int YT, int MOST, int T>
+template <int YT, int MOST, int T, bool T16>
 __global__ __launch_bounds__(kBThreads) void qgemv_batch_splitk_kernel(SkParams p) {
     __shared__ f32x4 red[T][kBWaves][kWave];
     __shared__ int last;
@@ -341,12 +714,18 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_splitk_kernel(SkParams 
     for (int t = 0; t < T; ++t) {
         const int row0 = (t0 + t) * 16;
         const int rows = t < nt ? min(16, p.n - row0) : 0;
-        const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.wq + (int64_t)min(row0, p.n) * K, (uint32_t)(rows * K));
-        const uint32_t oob_w = (uint32_t)(rows * K);
+        // the tiled layout's last tile is padded to 16 rows (zeros)
+        const uint32_t tile_bytes = (uint32_t)((T16 && rows > 0 ? 16 : rows) * K);
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.wq + (int64_t)min(row0, p.n) * K, tile_bytes);
 #pragma unroll
         for (int u = 0; u < MOST; ++u) {
             const int c = c0 + u;
-            w[t][u] = load16(rw, (c < c1 && i < rows) ? (uint32_t)(i * K + c * kBUnit + 16 * g) : oob_w);
+            if constexpr (T16) {
+                // whole 1 KB blocks, each read once: non-temporal
+                w[t][u] = load16_nt(rw, c < c1 ? (uint32_t)(c * 1024 + lane * 16) : tile_bytes);
+            } else {
+                w[t][u] = load16(rw, (c < c1 && i < rows) ? (uint32_t)(i * K + c * kBUnit + 16 * g) : tile_bytes);
+            }
         }
     }
     u32x4 xa[MOST], xb[MOST];
@@ -432,23 +811,23 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_splitk_kernel(SkParams 
     if (tid == 0) __hip_atomic_store(p.ctr + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int YT, int MOST>
+template <int YT, int MOST, bool T16>
 static void launch_sk_t(int T, int grid, const SkParams& p, hipStream_t st) {
-    if (T == 1) qgemv_batch_splitk_kernel<YT, MOST, 1><<<grid, kBThreads, 0, st>>>(p);
-    else if (T == 2) qgemv_batch_splitk_kernel<YT, MOST, 2><<<grid, kBThreads, 0, st>>>(p);
-    else qgemv_batch_splitk_kernel<YT, MOST, 4><<<grid, kBThreads, 0, st>>>(p);
+    if (T == 1) qgemv_batch_splitk_kernel<YT, MOST, 1, T16><<<grid, kBThreads, 0, st>>>(p);
+    else if (T == 2) qgemv_batch_splitk_kernel<YT, MOST, 2, T16><<<grid, kBThreads, 0, st>>>(p);
+    else qgemv_batch_splitk_kernel<YT, MOST, 4, T16><<<grid, kBThreads, 0, st>>>(p);
 }
-template <int YT>
+template <int YT, bool T16>
 static void launch_sk(int most, int T, int grid, const SkParams& p, hipStream_t st) {
     switch (most) {
-        case 1: launch_sk_t<YT, 1>(T, grid, p, st); break;
-        case 2: launch_sk_t<YT, 2>(T, grid, p, st); break;
-        case 3: launch_sk_t<YT, 3>(T, grid, p, st); break;
-        case 4: launch_sk_t<YT, 4>(T, grid, p, st); break;
-        case 5: launch_sk_t<YT, 5>(T, grid, p, st); break;
-        case 6: launch_sk_t<YT, 6>(T, grid, p, st); break;
-        case 7: launch_sk_t<YT, 7>(T, grid, p, st); break;
-        default: launch_sk_t<YT, 8>(T, grid, p, st); break;
+        case 1: launch_sk_t<YT, 1, T16>(T, grid, p, st); break;
+        case 2: launch_sk_t<YT, 2, T16>(T, grid, p, st); break;
+        case 3: launch_sk_t<YT, 3, T16>(T, grid, p, st); break;
+        case 4: launch_sk_t<YT, 4, T16>(T, grid, p, st); break;
+        case 5: launch_sk_t<YT, 5, T16>(T, grid, p, st); break;
+        case 6: launch_sk_t<YT, 6, T16>(T, grid, p, st); break;
+        case 7: launch_sk_t<YT, 7, T16>(T, grid, p, st); break;
+        default: launch_sk_t<YT, 8, T16>(T, grid, p, st); break;
     }
 }
 
@@ -469,8 +848,8 @@ hipError_t launch_qgemv_batch_splitk(const BatchArgs& a, void* ws, hipStream_t s
     p.C = pl.C;
     p.Cs = pl.Cs;
     const int grid = pl.nrb * kSkS;
-    if (a.yt == 0) launch_sk<0>(pl.most, pl.T, grid, p, st);
-    else launch_sk<1>(pl.most, pl.T, grid, p, st);
+    if (a.yt == 0) a.t16 ? launch_sk<0, true>(pl.most, pl.T, grid, p, st) : launch_sk<0, false>(pl.most, pl.T, grid, p, st);
+    else a.t16 ? launch_sk<1, true>(pl.most, pl.T, grid, p, st) : launch_sk<1, false>(pl.most, pl.T, grid, p, st);
     return hipGetLastError();
 }
 
@@ -479,6 +858,7 @@ hipError_t launch_qgemv_batch(const BatchArgs* a, int count, hipStream_t st) {
     g.count = count;
     g.k = (int32_t)a[0].k;
     g.m = a[0].m;
+    g.t16 = a[0].t16 ? 1 : 0;
     g.x = static_cast<const uint16_t*>(a[0].x);
     int tiles = 0;
     for (int j = 0; j < count; ++j) {
@@ -498,8 +878,19 @@ hipError_t launch_qgemv_batch(const BatchArgs* a, int count, hipStream_t st) {
         // activations kept in LDS: one workgroup per CU, each walking its
         // tiles with the fragments loaded once
         const int grid = cus;
-        auto k0 = qgemv_batch_kernel<0, true>;
-        auto k1 = qgemv_batch_kernel<1, true>;
+        if (a[0].t16) {
+            // five or more tiles per workgroup keep five or more waves busy
+            // with one tile each; fewer, and the eight waves share each tile
+            // (measured on MI355X: 1376 tiles 24.0 against 25.4 us, 768 tiles
+            // 17.0 against 15.7 us, at 16 tokens)
+            if ((tiles + cus - 1) / cus >= 5) {
+                const size_t wt_bytes = (size_t)C * 2 * kWave * sizeof(u32x4);
+                return a[0].yt == 0 ? launch_wt<0>(C, grid, wt_bytes, g, st) : launch_wt<1>(C, grid, wt_bytes, g, st);
+            }
+            return a[0].yt == 0 ? launch_xl<0>(most, grid, xl_bytes, g, st) : launch_xl<1>(most, grid, xl_bytes, g, st);
+        }
+        auto k0 = qgemv_batch_kernel<0, true, false>;
+        auto k1 = qgemv_batch_kernel<1, true, false>;
         static bool attr_set = false;
         if (!attr_set) {
             hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k0),
@@ -518,8 +909,13 @@ hipError_t launch_qgemv_batch(const BatchArgs* a, int count, hipStream_t st) {
     // that are walked by the workgroups in turn
     const int slots = 2 * cus;
     const int grid = tiles < slots ? tiles : slots;
-    if (a[0].yt == 0) qgemv_batch_kernel<0, false><<<grid, kBThreads, 0, st>>>(g);
-    else qgemv_batch_kernel<1, false><<<grid, kBThreads, 0, st>>>(g);
+    if (a[0].t16) {
+        if (a[0].yt == 0) qgemv_batch_kernel<0, false, true><<<grid, kBThreads, 0, st>>>(g);
+        else qgemv_batch_kernel<1, false, true><<<grid, kBThreads, 0, st>>>(g);
+    } else {
+        if (a[0].yt == 0) qgemv_batch_kernel<0, false, false><<<grid, kBThreads, 0, st>>>(g);
+        else qgemv_batch_kernel<1, false, false><<<grid, kBThreads, 0, st>>>(g);
+    }
     return hipGetLastError();
 }
 

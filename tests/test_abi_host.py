@@ -490,24 +490,26 @@ def test_batch_workspace_bytes(qg):
         if cus != 256:
             pytest.skip("sizes below are for 256 CUs")
     f = l.qg_qgemv_batch_workspace_bytes
-    assert f(4096, 4096, 16) == 4 * 256 * 64 * 16 + 256
-    assert f(4096, 11008, 4) == 4 * 256 * 64 * 16 + 256
-    assert f(777, 4096, 7) == 4 * 49 * 64 * 16 + 256     # 49 tiles, one per row block
+    assert f(4096, 11008, 16) == 4 * 256 * 64 * 16 + 256
+    assert f(4096, 8192, 4) == 4 * 256 * 64 * 16 + 256
+    assert f(777, 8192, 7) == 4 * 49 * 64 * 16 + 256     # 49 tiles, one per row block
     assert f(4096, 16384, 16) > 0                        # 64 units per split: 8 per wave
     assert f(4096, 16384 + 128, 16) == 0                 # 9 per wave: no split
-    assert f(4097, 4096, 16) == 0                        # more tiles than CUs
-    assert f(4096, 4096, 1) == 0                         # one token: batch-1 kernel
-    assert f(4096, 4096, 17) == 0
+    assert f(4096, 8192 - 128, 16) == 0                  # below the split's smallest k
+    assert f(4096, 4096, 16) == 0
+    assert f(4097, 11008, 16) == 0                       # more tiles than CUs
+    assert f(4096, 11008, 1) == 0                        # one token: batch-1 kernel
+    assert f(4096, 11008, 17) == 0
     assert f(4096, 192, 4) == 0                          # invalid k
-    assert f(0, 4096, 4) == 0
+    assert f(0, 11008, 4) == 0
 
 
 @needs_no_gpu
 def test_validation_qgemv_batch_ws(qg):
     l = qg.lib()
     f = l.qg_qgemv_batch_ws
-    need = l.qg_qgemv_batch_workspace_bytes(4096, 4096, 16)
-    w = qg.CWeight(0, 0, 4096, 4096, A, None, A, None)
+    need = l.qg_qgemv_batch_workspace_bytes(4096, 11008, 16)
+    w = qg.CWeight(0, 0, 4096, 11008, A, None, A, None)
     # (w, m, x, xt, y, yt, ws, ws_bytes, stream)
     assert f(None, 16, A, 1, A, 0, A, need, None) == 1
     assert f(ctypes.byref(w), 16, A, 1, A, 0, None, need, None) == 5       # no workspace
@@ -517,12 +519,43 @@ def test_validation_qgemv_batch_ws(qg):
     assert f(ctypes.byref(w), 16, A, 0, A, 0, A, need, None) == 4          # x must be bf16
     assert f(ctypes.byref(w), 16, A, 1, A, 2, A, need, None) == 4
     assert f(ctypes.byref(w), 16, None, 1, A, 0, A, need, None) == 1
-    wt = qg.CWeight(1, 0, 4096, 4096, A, None, A, None)
+    wt = qg.CWeight(1, 0, 4096, 11008, A, None, A, None)
     assert f(ctypes.byref(wt), 16, A, 1, A, 0, A, need, None) == 4         # int8 weights only
     # shapes without a split fall through to qg_qgemv_batch's checks
     assert f(ctypes.byref(w), 17, A, 1, A, 0, None, 0, None) == 2
     wk = qg.CWeight(0, 0, 4096, 192, A, None, A, None)
     assert f(ctypes.byref(wk), 4, A, 1, A, 0, None, 0, None) == 2
+
+
+def test_tiles16_bytes(qg):
+    f = qg.lib().qg_tiles16_bytes
+    assert f(16, 128) == 16 * 128
+    assert f(17, 128) == 32 * 128          # the last tile padded to 16 rows
+    assert f(4096, 4096) == 4096 * 4096
+    assert f(777, 1152) == 784 * 1152
+    assert f(0, 128) == 0 and f(16, 192) == 0 and f(16, 64) == 0 and f(16, 262144 + 128) == 0
+
+
+@needs_no_gpu
+def test_validation_tiled16(qg):
+    l = qg.lib()
+    p = l.qg_pack_tiles16
+    # (codes, n, k, out, stream)
+    assert p(None, 16, 128, A, None) == 1
+    assert p(A, 16, 128, None, None) == 1
+    assert p(A, 0, 128, A, None) == 2
+    assert p(A, 16, 192, A, None) == 2
+    assert p(U, 16, 128, A, None) == 3
+    assert p(A, 16, 128, U, None) == 3
+    # a grouped batch launch takes one layout
+    g = l.qg_qgemv_batch_grouped
+    arr = (qg.CWeight * 2)(qg.CWeight(0, 0, 64, 256, A, None, A, None), qg.CWeight(6, 0, 64, 256, A, None, A, None))
+    ys = (ctypes.c_void_p * 2)(A, A)
+    assert g(arr, 2, 4, A, 1, ys, 0, None) == 4
+    # the batch-1 product does not read the tiled layout
+    q = l.qg_qgemv
+    wt = qg.CWeight(6, 0, 64, 256, A, None, A, None)
+    assert q(ctypes.byref(wt), 1, A, 1, A, 0, None, None) == 4
 
 
 @needs_no_gpu

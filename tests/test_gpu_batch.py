@@ -146,14 +146,12 @@ def _workspace(qg, n, k, m):
     return need, torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
 
 
-@pytest.mark.parametrize("n,k,m", [(4096, 4096, 16), (4096, 11008, 16), (4096, 11008, 4), (4096, 4096, 2),
+@pytest.mark.parametrize("n,k,m", [(4096, 11008, 16), (4096, 11008, 4), (4096, 8192, 2),
                                    # ragged rows: 49 tiles, one per row block; 250 tiles in row
                                    # blocks of 4, the last of 2 tiles, its last tile of 6 rows
-                                   (777, 4096, 7), (3990, 2048, 16),
-                                   # K splits with no units (k = 128: two units, four splits)
-                                   (16, 128, 3),
-                                   # ragged units per wave (18 units: 5, 5, 5, 3 per split)
-                                   (100, 1152, 9),
+                                   (777, 8192, 7), (3990, 8192, 16), (16, 8192, 3),
+                                   # ragged units per wave (130 units: 33, 33, 33, 31 per split)
+                                   (100, 8320, 9),
                                    # the largest K with register-resident activations: 8 units per wave
                                    (4096, 16384, 16)])
 def test_qgemv_batch_splitk(qg, n, k, m):
@@ -188,13 +186,13 @@ def test_qgemv_batch_splitk(qg, n, k, m):
 
 
 def test_qgemv_batch_splitk_shapes_alternate(qg):
-    # one workspace, calls of two shapes in turn (o: 4096 x 4096, down:
-    # 4096 x 11008, the sizes the decode step alternates) and two token counts
+    # one workspace, calls of two shapes in turn (4096 x 8192 and the down
+    # projection 4096 x 11008) and two token counts
     note("qgemv batch split-K alternating shapes on one workspace")
-    need = max(qg.batch_workspace_bytes(4096, 4096, 16), qg.batch_workspace_bytes(4096, 11008, 16))
+    need = max(qg.batch_workspace_bytes(4096, 8192, 16), qg.batch_workspace_bytes(4096, 11008, 16))
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     cases = []
-    for j, (k, m) in enumerate([(4096, 16), (11008, 16), (4096, 5), (11008, 3)]):
+    for j, (k, m) in enumerate([(8192, 16), (11008, 16), (8192, 5), (11008, 3)]):
         w, xb = _case(4096, k, m, 300 + j)
         W, _, _ = _weight(qg, w)
         q_ref, s_ref = oracle.quantize_absmax(w, per_row=True)
@@ -206,10 +204,10 @@ def test_qgemv_batch_splitk_shapes_alternate(qg):
     assert not host(ws)[4 * 256 * 64 * 16:].any()
 
 
-@pytest.mark.parametrize("n,k,m", [(5000, 4096, 16), (4096, 4096, 1), (64, 32768, 8)])
+@pytest.mark.parametrize("n,k,m", [(5000, 11008, 16), (4096, 11008, 1), (64, 32768, 8), (4096, 4096, 16)])
 def test_qgemv_batch_ws_without_split(qg, n, k, m):
     # shapes with no split (more tiles than CUs, one token, k beyond the
-    # register-resident fragments) run qg_qgemv_batch: bit-identical
+    # register-resident fragments, k below 8192) run qg_qgemv_batch: bit-identical
     note("qgemv batch ws fallback %dx%d m=%d" % (n, k, m))
     assert qg.batch_workspace_bytes(n, k, m) == 0
     w, xb = _case(n, k, m, 400 + m)
@@ -219,3 +217,93 @@ def test_qgemv_batch_ws_without_split(qg, n, k, m):
     y1 = qg.qgemv_batch(W, xd, y_dtype=torch.float32, ws=ws)
     y0 = qg.qgemv_batch(W, xd, y_dtype=torch.float32)
     assert np.array_equal(host(y1), host(y0))
+
+
+# ---------------------------------------------------------------- 16-row tiles
+def _tiles16_expected(codes):
+    """The tiled layout written out with numpy: tile t, unit c, lane
+    L = 16 g + i holds codes[16 t + i][64 c + 16 g .. + 15]; rows past n are 0."""
+    n, k = codes.shape
+    T, C = (n + 15) // 16, k // 64
+    pad = np.zeros((T * 16, k), np.int8)
+    pad[:n] = codes
+    return pad.reshape(T, 16, C, 4, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
+
+
+@pytest.mark.parametrize("n,k", [(16, 128), (777, 1152), (4096, 4096), (33, 32768)])
+def test_pack_tiles16_layout(qg, n, k):
+    note("pack tiles16 %dx%d" % (n, k))
+    codes = synth.rng(n + k).integers(-127, 128, size=(n, k), dtype=np.int64).astype(np.int8)
+    full, out = torch.empty(qg.lib().qg_tiles16_bytes(n, k) + 128, dtype=torch.int8, device="cuda"), None
+    full.view(torch.uint8).fill_(0x5A)
+    out = full[64:-64]
+    qg.pack_tiles16(dev(codes), out=out)
+    assert np.array_equal(host(out), _tiles16_expected(codes))
+    raw = host(full).view(np.uint8)
+    assert np.all(raw[:64] == 0x5A) and np.all(raw[-64:] == 0x5A)
+
+
+@pytest.mark.parametrize("n,k,m,same_order", [
+    # the tile loop (K beyond the LDS-resident activations, or few tiles):
+    # the same kernel as the row-major codes, bit-identical results
+    (300, 4096, 5, True), (33, 32768, 16, True), (4200, 4736, 16, True), (16, 128, 1, False),
+    # more tiles than CUs, fewer than five per CU: the eight waves share each
+    # tile (activations in LDS; the summation order of the row-major kernel,
+    # to rounding); ragged last tile
+    (5000, 2176, 16, False), (4200, 4608, 7, False), (11008, 4096, 16, False), (11008, 4096, 3, False),
+    # five or more tiles per CU: one tile per wave over all of K; ring
+    # depths 2 (34 units per tile), 8 (72) and 16 (64); ragged last tile
+    (20000, 2176, 5, False), (21000, 4608, 16, False), (22016, 4096, 16, False), (20007, 4096, 2, False)])
+def test_qgemv_batch_tiles16_matches_row_major(qg, n, k, m, same_order):
+    note("qgemv batch tiles16 %dx%d m=%d" % (n, k, m))
+    w, xb = _case(n, k, m, 7 * n + k + m)
+    W, _, _ = _weight(qg, w)
+    Wt = qg.tiled16(W)
+    xd = dev_bf16(xb)
+    q_ref, s_ref = oracle.quantize_absmax(w, per_row=True)
+    y_ref = oracle.y_w8a16_batch(q_ref, s_ref, xb)
+    full32, y32 = _guarded2(m, n, torch.float32)
+    qg.qgemv_batch(Wt, xd, y=y32)
+    fullb, yb = _guarded2(m, n, torch.bfloat16)
+    qg.qgemv_batch(Wt, xd, y=yb)
+    assert canaries_intact(full32, m * n) and canaries_intact(fullb, m * n)
+    y32_h = host(y32)
+    assert oracle.normwise_error(y32_h, y_ref) <= TOL_F32
+    check_bf16_output(host(yb).ravel(), y32_h.ravel(), y_ref.ravel())
+    if same_order:
+        assert np.array_equal(host(qg.qgemv_batch(W, xd, y_dtype=torch.float32)), y32_h)
+    # deterministic
+    assert np.array_equal(host(qg.qgemv_batch(Wt, xd, y_dtype=torch.float32)), y32_h)
+
+
+@pytest.mark.parametrize("n,k,m", [(4096, 11008, 16), (4096, 11008, 4), (3990, 8192, 16), (100, 8320, 9)])
+def test_qgemv_batch_splitk_tiles16(qg, n, k, m):
+    note("qgemv batch split-K tiles16 %dx%d m=%d" % (n, k, m))
+    need, ws = _workspace(qg, n, k, m)
+    w, xb = _case(n, k, m, 11 * n + k + m)
+    W, _, _ = _weight(qg, w)
+    Wt = qg.tiled16(W)
+    xd = dev_bf16(xb)
+    y0 = qg.qgemv_batch(W, xd, y_dtype=torch.float32, ws=ws)
+    full, y1 = _guarded2(m, n, torch.float32)
+    qg.qgemv_batch(Wt, xd, y=y1, ws=ws)
+    assert canaries_intact(full, m * n)
+    assert np.array_equal(host(y0), host(y1))
+    tiles = (n + 15) // 16
+    assert not host(ws)[4 * tiles * 64 * 16:].any()
+
+
+@pytest.mark.parametrize("rows", [[4096, 1024, 777], [11008, 11008]])
+def test_qgemv_batch_grouped_tiles16(qg, rows):
+    note("qgemv batch grouped tiles16 %s, m=16" % rows)
+    k, m = 4096, 16
+    xb = synth.to_bf16_bits(synth.gaussian(synth.rng(94), (m, k), 1.0))
+    xd = dev_bf16(xb)
+    ws = [synth.gaussian(synth.rng(300 + j), (n, k), 0.02) for j, n in enumerate(rows)]
+    Wts = [qg.tiled16(_weight(qg, w)[0]) for w in ws]
+    # 368 tiles (the waves share each tile) and 1376 (a tile per wave);
+    # every matrix against the oracle
+    ys = qg.qgemv_batch_grouped(Wts, xd, y_dtype=torch.float32)
+    for w, y in zip(ws, ys):
+        q_ref, s_ref = oracle.quantize_absmax(w, per_row=True)
+        assert oracle.normwise_error(host(y), oracle.y_w8a16_batch(q_ref, s_ref, xb)) <= TOL_F32
