@@ -335,7 +335,7 @@ def profile_workload(args):
     order = args.mark_configs or os.path.join(ROOT, "gpurun_out", "profile_order.json")
     with open(order, "w") as f:
         json.dump({"configs": MARKS["order"], "hashes": {k: src_hash(k) for k in KERNEL_SOURCES},
-                   "command": "python bench.py " + " ".join(sys.argv[1:])}, f, indent=1)
+                   "command": "python bench.py " + " ".join(_rel(a) for a in sys.argv[1:])}, f, indent=1)
     log("profile workload done (%d segments, order in %s)" % (len(MARKS["order"]), order))
 
 
@@ -354,6 +354,25 @@ def _segments(rows, order_json):
     if len(segs) != len(order["configs"]):
         raise SystemExit("%d separators, %d configs in %s" % (len(segs), len(order["configs"]), order_json))
     return list(zip(order["configs"], segs)), order
+
+
+def _rel(path):
+    """A path under the repository, relative to its root (as printed in the
+    profile summaries)."""
+    ap = os.path.abspath(path)
+    return os.path.relpath(ap, ROOT) if ap.startswith(ROOT + os.sep) else path
+
+
+def _pass_counters(d):
+    """The counters one rocprofv3 --pmc output folder holds."""
+    import csv
+    import glob
+    names = set()
+    for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                names.add(r["Counter_Name"])
+    return sorted(names)
 
 
 def summarize_counters(order_json, dirs):
@@ -409,13 +428,20 @@ def summarize_counters(order_json, dirs):
                 r["hbm_bytes_per_dispatch"] = round(r["FETCH_SIZE"] * 1024.0 * f_fetch + r["WRITE_SIZE"] * 1024.0 * f_write)
             rec[name[:160]] = r
         out["configs"][cfg] = rec
+    passes = []
+    for d in dirs:  # one rocprofv3 pass per folder, with the counters it holds
+        passes.append("rocprofv3 --pmc %s --output-format csv -d $R/%s -o run -- python3 $R/bench.py "
+                      "--profile-workload --mark-configs $R/%s" % (" ".join(_pass_counters(d)), _rel(d), _rel(order_json)))
+    out["commands"] = passes + ["python3 $R/bench.py --summarize-counters %s" % " ".join(
+        "$R/" + _rel(x) for x in [order_json] + list(dirs))]
     with open(COUNTERS_FILE, "w") as f:
         json.dump(out, f, indent=1)
     cols = ["FETCH_SIZE", "WRITE_SIZE", "hbm_bytes_per_dispatch", "SQ_INSTS_VALU_MFMA_MOPS_I8",
             "SQ_INSTS_VALU_MFMA_MOPS_F6F4", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU",
             "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES"]
     md = ["# Counters per bench config (rocprofv3 --pmc over `bench.py --profile-workload`)", "",
-          "Command of the profiled workload: `%s`" % out["command"], "",
+          "Commands (R = the repository root; run from /tmp with TMPDIR=/tmp for rocprofv3's own files; one pass "
+          "per counter group, then the summary):", ""] + ["    " + c for c in out["commands"]] + ["",
           "Calibration: %s" % json.dumps(out["calibration"]), "",
           "| config | kernel | dispatches | " + " | ".join(cols) + " |", "|---|---|---|" + "---|" * len(cols)]
     for cfg, ks in out["configs"].items():
@@ -478,7 +504,11 @@ def summarize_trace(trace_dir, order_json):
             cur.append((name, (en - st) / 1e3))
     if len(segments) != len(order["configs"]):
         raise SystemExit("%d separators in the trace, %d configs in the order file" % (len(segments), len(order["configs"])))
-    out = {"source_hashes": order["hashes"], "command": order.get("command", ""), "configs": {}}
+    out = {"source_hashes": order["hashes"], "command": order.get("command", ""), "configs": {},
+           "commands": ["rocprofv3 --kernel-trace --stats --output-format csv -d $R/%s -o run -- python3 $R/%s"
+                        % (_rel(trace_dir), order.get("command", "").replace("python ", "", 1).replace(
+                            "--mark-configs ", "--mark-configs $R/")),
+                        "python3 $R/bench.py --summarize-trace $R/%s $R/%s" % (_rel(trace_dir), _rel(order_json))]}
     for cfg, seg in zip(order["configs"], segments):
         by = {}
         for name, us in seg:
@@ -495,7 +525,8 @@ def summarize_trace(trace_dir, order_json):
     with open(DURATIONS_FILE, "w") as f:
         json.dump(out, f, indent=1)
     md = ["# Kernel durations per bench config (rocprofv3 --kernel-trace)", "",
-          "Command: `%s`" % out["command"], "",
+          "Commands (R = the repository root; run from /tmp with TMPDIR=/tmp for rocprofv3's own files):",
+          ""] + ["    " + c for c in out["commands"]] + ["",
           "| config | kernel | dispatches | median us | p10 us | p90 us | mean us |", "|---|---|---|---|---|---|---|"]
     for cfg, ks in out["configs"].items():
         for name, r in ks.items():
@@ -509,7 +540,7 @@ def summarize_trace(trace_dir, order_json):
         with open(stats[0]) as f:
             st = list(csv.DictReader(f))
         md = ["# Kernel statistics of the marked bench run (rocprofv3 --kernel-trace --stats)", "",
-              "Command: `%s` under `rocprofv3 --kernel-trace --stats --output-format csv`" % out["command"], "",
+              "Command (R = the repository root): `%s` (the `*_kernel_stats.csv` it writes)" % out["commands"][0], "",
               "| kernel | calls | average us | min us | max us | share |", "|---|---|---|---|---|---|"]
         for r in st[:30]:
             md.append("| `%s` | %s | %.3f | %.3f | %.3f | %s%% |" % (r["Name"][:110], r["Calls"], float(r["AverageNs"]) / 1e3,
@@ -655,7 +686,7 @@ def main():
     if MARKS is not None:
         with open(args.mark_configs, "w") as f:
             json.dump({"configs": MARKS["order"], "hashes": {k: src_hash(k) for k in KERNEL_SOURCES},
-                       "command": "python bench.py " + " ".join(sys.argv[1:])}, f, indent=1)
+                       "command": "python bench.py " + " ".join(_rel(a) for a in sys.argv[1:])}, f, indent=1)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(np, synth)
     print(json.dumps(result), flush=True)
