@@ -334,8 +334,11 @@ qg_status qg_unpack_base3(const uint8_t* packed, int64_t n, int64_t k, int8_t* c
  * reads one whole block; with row-major codes the same fragments take 64
  * bytes from each of 16 rows.  Same codes and scales as the row-major
  * matrix: as qg_weight, fmt QG_WFMT_INT8_T16 with codes = the tiled buffer;
- * qg_qgemv_batch, qg_qgemv_batch_grouped and qg_qgemv_batch_ws take it and
- * give results identical to the row-major matrix's.
+ * qg_qgemv_batch, qg_qgemv_batch_grouped and qg_qgemv_batch_ws take it.
+ * Results equal the row-major matrix's bit for bit where both run the same
+ * kernel, and to fp32 rounding otherwise: with five or more 16-row tiles per
+ * CU a launch on tiled codes gives each wave whole tiles, summed over k in
+ * another order.
  * codes: [n][k] int8, 16-B aligned;  out: qg_tiles16_bytes(n, k) bytes
  * (16 ceil(n/16) k), 16-B aligned.  k % 128 == 0, k <= QG_BATCH_MAX_K;
  * 1 <= n < 2^31.  qg_tiles16_bytes returns 0 for shapes outside these.
@@ -433,8 +436,11 @@ qg_status qg_qgemv_grouped(const qg_weight* w, int32_t count, int32_t amode, con
  * products are exact and summed in fp32 (in another order than qg_qgemv's,
  * so results agree to rounding, not bit for bit).
  * w  : QG_WFMT_INT8 (codes [n][k] int8, scale = s_w[n]) or the same codes in
- *      16-row tiles (QG_WFMT_INT8_T16, qg_pack_tiles16; same results); 16-B
- *      aligned codes.  A grouped launch takes one layout for all matrices.
+ *      16-row tiles (QG_WFMT_INT8_T16, qg_pack_tiles16; the same results to
+ *      rounding); 16-B aligned codes.  A grouped launch takes one layout for
+ *      all matrices.  Results of one call are deterministic; a grouped
+ *      launch and the single launches of its matrices may differ by rounding
+ *      (the kernel is chosen by the launch's number of tiles).
  * x  : [m][k] bf16 (xt must be QG_BF16), 16-B aligned; 1 <= m <= QG_BATCH_MAX_M.
  * y  : [m][n] of type yt (QG_F32 or QG_BF16, bf16 rounded to nearest even).
  * k % 128 == 0, 128 <= k <= QG_BATCH_MAX_K; 1 <= n < 2^31.
