@@ -427,6 +427,68 @@ qg_status qg_qgemv_grouped(const qg_weight* w, int32_t count, int32_t amode, con
                            void* const* y, int32_t yt, int32_t* const* acc_out, void* stream);
 
 /*
+ * The weight-only int8 products of a whole batch-1 decode step, with the
+ * data dependencies between them, in ONE launch ([SEP] section 3.3: the
+ * launch overhead of many small operators is one reason measured speed-ups
+ * fall short of the bandwidth model ([SEP] section 3.1: decode time is the
+ * time to read the weights once); this is the fused-operator remedy applied
+ * across the step's products).
+ *
+ * A stage is 1..QG_MAX_GROUP products that read the same x:
+ *     y_m[n] = (sum_k codes_m[n][k] * x[k]) / s_w_m[n]     (m < count)
+ * exactly qg_qgemv's QG_WFMT_INT8 / QG_ACT_FLOAT product with bf16 x and
+ * bf16 y (fp32 sums in another order, so results agree with qg_qgemv to
+ * rounding, not bit for bit; one call's results are deterministic).  x of a
+ * stage is read only after every output row of stage `dep` has been written
+ * (dep < the stage's index; -1: x is ready when the call starts).  The
+ * weights of every stage stream from the start of the call; only x waits.
+ * Rules the caller keeps: a stage's y must not be any stage's x other than
+ * that of stages depending on it (directly or through other stages), and
+ * outputs must not overlap.
+ *
+ *   qg_chain_plan (host only, no GPU call) validates the stages and writes
+ *   the plan IMAGE into host memory (a stage table and one record per slot
+ *   of up to 128 rows): image_bytes >= qg_chain_plan_bytes(stages, nstages,
+ *   workgroups), 16-B aligned.  `workgroups` is the grid of the launch (one
+ *   per CU is what the kernel is sized for).
+ *   qg_qgemv_chain runs the step: `image` is that host image, `plan` a
+ *   device copy of it (16-B aligned, same bytes; the caller copies it once).
+ *   The call updates control words in `plan` and restores them before it
+ *   ends, so the same device copy serves any number of calls (and graph
+ *   replays); calls that overlap on one plan race.
+ *
+ * Every wait inside the call is bounded (QG_CHAIN_TIMEOUT_TICKS of the
+ * 100 MHz real-time counter).  A wait that runs past it sets bit 0 of the
+ * uint32 at byte QG_CHAIN_ERROR_OFFSET of `plan`, the call ends normally
+ * with unspecified outputs, and `plan` must be copied from the image again
+ * before the next call.  The caller reads that word after the call.
+ *
+ * Stage: count in [1, QG_MAX_GROUP]; w = HOST array of count QG_WFMT_INT8
+ * descriptors sharing k (16-B aligned codes, scale = s_w[n]); y = HOST array
+ * of count device pointers (bf16 [w[m].n], 2-B aligned); x bf16 [k], 16-B
+ * aligned; k % 128 == 0, QG_CHAIN_MIN_K <= k <= QG_CHAIN_MAX_K; 1 <= n < 2^31.
+ * Errors: QG_ERR_ARG (count, dep, fmt, nstages, workgroups, or an image
+ * that qg_chain_plan did not write), QG_ERR_SHAPE, QG_ERR_ALIGN,
+ * QG_ERR_NULLPTR, QG_ERR_WORKSPACE (image too small).
+ */
+#define QG_CHAIN_MAX_STAGES    4096
+#define QG_CHAIN_MIN_K         128
+#define QG_CHAIN_MAX_K         16384
+#define QG_CHAIN_ERROR_OFFSET  64
+#define QG_CHAIN_TIMEOUT_TICKS 200000000ull   /* 2 s at 100 MHz */
+typedef struct qg_chain_stage {
+    int32_t count;
+    int32_t dep;
+    const void* x;
+    const qg_weight* w;
+    void* const* y;
+} qg_chain_stage;
+size_t qg_chain_plan_bytes(const qg_chain_stage* stages, int32_t nstages, int32_t workgroups);  /* 0 if invalid */
+qg_status qg_chain_plan(const qg_chain_stage* stages, int32_t nstages, int32_t workgroups, void* image,
+                        size_t image_bytes);
+qg_status qg_qgemv_chain(const void* image, void* plan, void* stream);
+
+/*
  * Weight-only int8 products for a small batch of tokens (decode of m
  * sequences at once; [SEP] section 3.1: at batch 1 every weight is read once
  * per token and the compute idles, so serving several tokens per read of

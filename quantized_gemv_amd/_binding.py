@@ -35,6 +35,11 @@ QG_BATCH_MAX_K = 262144
 QG_MX_BLOCK = 32
 QG_QGEMM_MAX_K = 133120
 QG_ABSMAX_SCRATCH_PARTS = 1024
+QG_CHAIN_MAX_STAGES = 4096
+QG_CHAIN_MIN_K = 128
+QG_CHAIN_MAX_K = 16384
+QG_CHAIN_ERROR_OFFSET = 64
+QG_CHAIN_TIMEOUT_TICKS = 200000000
 
 _c_i32, _c_i64, _c_sz, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
@@ -50,6 +55,11 @@ class CWeight(ctypes.Structure):
                 ("codes", _c_vp), ("resid", _c_vp), ("scale", _c_vp), ("scale2", _c_vp), ("zero", _c_vp)]
 
 
+class CChainStage(ctypes.Structure):
+    _fields_ = [("count", _c_i32), ("dep", _c_i32), ("x", _c_vp), ("w", ctypes.POINTER(CWeight)),
+                ("y", ctypes.POINTER(_c_vp))]
+
+
 _SIGS = {
     "qg_status_str": (ctypes.c_char_p, [_c_i32]),
     "qg_abi_version": (_c_i32, []),
@@ -58,6 +68,9 @@ _SIGS = {
     "qg_quantize_absmax_noalloc": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp, _c_vp]),
     "qg_probe_stream_read_bytes": (_c_sz, [_c_i64, _c_i32]),
     "qg_probe_stream_read": (_c_i32, [_c_vp, _c_i64, _c_i32, _c_vp, _c_vp]),
+    "qg_chain_plan_bytes": (_c_sz, [ctypes.POINTER(CChainStage), _c_i32, _c_i32]),
+    "qg_chain_plan": (_c_i32, [ctypes.POINTER(CChainStage), _c_i32, _c_i32, _c_vp, _c_sz]),
+    "qg_qgemv_chain": (_c_i32, [_c_vp, _c_vp, _c_vp]),
     "qg_quantize_absmax_split": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32,
                                           _c_vp]),
     "qg_detect_outliers_workspace_bytes": (_c_sz, [_c_i64]),
@@ -618,3 +631,64 @@ def qgemm_w8a8(xq: torch.Tensor, s_x: torch.Tensor, x_out: Optional[torch.Tensor
                                _p(w_out) if n_out else None, w_ld, n, _p(y), _p(acc_out), _stream(xq)),
            "qg_qgemm_w8a8")
     return y
+
+
+def chain_plan_image(stages, workgroups: int):
+    """qg_chain_plan on the host: `stages` is a list of (CWeight array, count,
+    x pointer, y pointer array, dep).  Returns the 16-B aligned uint8 image
+    (a numpy view) and the status; nothing is sent to a device."""
+    import numpy as np
+    n = len(stages)
+    cs = (CChainStage * n)()
+    for i, (cw, count, x_ptr, yp, dep) in enumerate(stages):
+        cs[i].count, cs[i].dep, cs[i].x = count, dep, x_ptr
+        cs[i].w = ctypes.cast(cw, ctypes.POINTER(CWeight))
+        cs[i].y = ctypes.cast(yp, ctypes.POINTER(_c_vp))
+    nbytes = lib().qg_chain_plan_bytes(cs, n, workgroups)
+    raw = np.zeros(max(int(nbytes), 64) + 16, np.uint8)
+    off = (-raw.ctypes.data) % 16
+    img = raw[off:off + max(int(nbytes), 64)]
+    st = lib().qg_chain_plan(cs, n, workgroups, ctypes.c_void_p(img.ctypes.data), nbytes)
+    return img, st
+
+
+class ChainStep:
+    """The weight-only int8 products of a decode step with their data
+    dependencies, run as one launch (qg_chain_plan once, then qg_qgemv_chain
+    per call).
+
+    stages: list of (weights, x, ys, dep): weights a list of QG_WFMT_INT8
+    QWeights sharing k, x a bf16 tensor [k], ys bf16 tensors [n] (one per
+    weight), dep the index of the stage whose outputs x holds (-1: none)."""
+
+    def __init__(self, stages, workgroups: Optional[int] = None):
+        self.keep = []
+        plan = []
+        dev = None
+        for weights, x, ys, dep in stages:
+            _dev(x, "x", torch.bfloat16)
+            dev = x.device
+            for y in ys:
+                _dev(y, "y", torch.bfloat16)
+            cw = (CWeight * len(weights))(*[w.c_struct() for w in weights])
+            yp = (_c_vp * len(ys))(*[y.data_ptr() for y in ys])
+            self.keep += [cw, yp, x, list(ys), list(weights)]
+            plan.append((cw, len(weights), x.data_ptr(), yp, dep))
+        if workgroups is None:
+            workgroups = torch.cuda.get_device_properties(dev).multi_processor_count
+        self.image, st = chain_plan_image(plan, workgroups)
+        _check(st, "qg_chain_plan")
+        self.plan = torch.from_numpy(self.image.copy()).to(dev)
+        self.device = dev
+
+    def launch(self):
+        _check(lib().qg_qgemv_chain(ctypes.c_void_p(self.image.ctypes.data), _p(self.plan), _stream(self.plan)),
+               "qg_qgemv_chain")
+
+    def error(self) -> int:
+        """The plan's error word (nonzero: a wait ran past its time bound)."""
+        return int(self.plan[QG_CHAIN_ERROR_OFFSET:QG_CHAIN_ERROR_OFFSET + 4].view(torch.int32).item())
+
+    def restore(self):
+        """Copy the plan image to the device again (after an error)."""
+        self.plan.copy_(torch.from_numpy(self.image))

@@ -5,9 +5,22 @@
 
 #include <hip/hip_runtime.h>
 
+#include <string.h>
+
+#include "qg_chain.h"
 #include "qg_launch.h"
 
 namespace {
+
+// rows per slot of a chained stage of `rows` rows in total: about one slot
+// per workgroup and stage (so that every workgroup works on every stage),
+// whole rows for each worker wave, at most kMaxRows
+int64_t chain_rows_per_slot(int64_t rows, int32_t workgroups) {
+    using namespace qg::chain;
+    int64_t r = (rows + (int64_t)workgroups - 1) / (int64_t)workgroups;
+    r = (r + kWorkers - 1) / kWorkers * kWorkers;
+    return r > kMaxRows ? kMaxRows : r;
+}
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -608,6 +621,127 @@ qg_status qg_probe_stream_read(const void* buf, int64_t bytes, int32_t workgroup
     if (qg_probe_stream_read_bytes(bytes, workgroups) == 0) return QG_ERR_SHAPE;
     if (!aligned16(buf)) return QG_ERR_ALIGN;
     return from_hip(qg::launch_stream_read(buf, bytes, workgroups, sink, as_stream(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validates the stages of a chained step and counts its slots.
+qg_status chain_check(const qg_chain_stage* stages, int32_t nstages, int32_t workgroups, int64_t* total_slots) {
+    using namespace qg::chain;
+    if (!stages) return QG_ERR_NULLPTR;
+    if (nstages < 1 || nstages > QG_CHAIN_MAX_STAGES) return QG_ERR_ARG;
+    if (workgroups < 1 || workgroups > 65535) return QG_ERR_ARG;
+    int64_t total = 0;
+    for (int32_t s = 0; s < nstages; ++s) {
+        const qg_chain_stage& st = stages[s];
+        if (st.count < 1 || st.count > QG_MAX_GROUP) return QG_ERR_ARG;
+        if (st.dep < -1 || st.dep >= s) return QG_ERR_ARG;  // an earlier stage only
+        if (!st.w || !st.y || !st.x) return QG_ERR_NULLPTR;
+        if (!aligned16(st.x)) return QG_ERR_ALIGN;
+        const int64_t k = st.w[0].k;
+        if (k < QG_CHAIN_MIN_K || k > QG_CHAIN_MAX_K || k % 128 != 0) return QG_ERR_SHAPE;
+        int64_t rows = 0;
+        for (int32_t m = 0; m < st.count; ++m) {
+            const qg_weight& w = st.w[m];
+            if (w.fmt != QG_WFMT_INT8) return QG_ERR_ARG;
+            if (!w.codes || !w.scale || !st.y[m]) return QG_ERR_NULLPTR;
+            if (w.k != k) return QG_ERR_SHAPE;
+            if (w.n < 1 || w.n >= ((int64_t)1 << 31)) return QG_ERR_SHAPE;
+            if (!aligned16(w.codes)) return QG_ERR_ALIGN;
+            if ((reinterpret_cast<uintptr_t>(st.y[m]) & 1u) != 0) return QG_ERR_ALIGN;
+            rows += w.n;
+        }
+        const int64_t r = chain_rows_per_slot(rows, workgroups);
+        for (int32_t m = 0; m < st.count; ++m) total += (st.w[m].n + r - 1) / r;
+        // slot records are addressed with 32-bit byte offsets
+        if (total * (int64_t)sizeof(SlotD) >= ((int64_t)1 << 31)) return QG_ERR_SHAPE;
+    }
+    *total_slots = total;
+    return QG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qg_chain_plan_bytes(const qg_chain_stage* stages, int32_t nstages, int32_t workgroups) {
+    int64_t total = 0;
+    if (chain_check(stages, nstages, workgroups, &total) != QG_OK) return 0;
+    return (size_t)qg::chain::plan_bytes(nstages, total);
+}
+
+qg_status qg_chain_plan(const qg_chain_stage* stages, int32_t nstages, int32_t workgroups, void* image,
+                        size_t image_bytes) {
+    using namespace qg::chain;
+    if (!image) return QG_ERR_NULLPTR;
+    int64_t total = 0;
+    const qg_status chk = chain_check(stages, nstages, workgroups, &total);
+    if (chk != QG_OK) return chk;
+    if (!aligned16(image)) return QG_ERR_ALIGN;
+    const uint64_t bytes = plan_bytes(nstages, total);
+    if (image_bytes < bytes) return QG_ERR_WORKSPACE;
+
+    uint8_t* img = static_cast<uint8_t*>(image);
+    memset(img, 0, (size_t)bytes);
+    Header* h = reinterpret_cast<Header*>(img);
+    h->magic = kMagic;
+    h->version = kVersion;
+    h->nstages = nstages;
+    h->total_slots = (int32_t)total;
+    h->stride = done_stride(nstages);
+    h->grid = workgroups;
+    h->stages_off = (uint64_t)kOffDone + (uint64_t)kRep * (uint64_t)h->stride * 4u;
+    h->slots_off = (h->stages_off + (uint64_t)nstages * sizeof(StageD) + 63) / 64 * 64;
+    h->timeout_ticks = QG_CHAIN_TIMEOUT_TICKS;
+    h->bytes = bytes;
+    StageD* sd = reinterpret_cast<StageD*>(img + h->stages_off);
+    SlotD* sl = reinterpret_cast<SlotD*>(img + h->slots_off);
+    int64_t slot = 0;
+    int32_t max_k = 0, nc = 0;
+    for (int32_t s = 0; s < nstages; ++s) {
+        const qg_chain_stage& st = stages[s];
+        const int32_t k = (int32_t)st.w[0].k;
+        int64_t rows = 0;
+        for (int32_t m = 0; m < st.count; ++m) rows += st.w[m].n;
+        const int64_t r = chain_rows_per_slot(rows, workgroups);
+        StageD& d = sd[s];
+        d.x = reinterpret_cast<uint64_t>(st.x);
+        d.k = k;
+        d.dep = st.dep;
+        d.slot0 = (int32_t)slot;
+        d.nseg = (k + kItemChunks * 16 - 1) / (kItemChunks * 16);
+        for (int32_t m = 0; m < st.count; ++m) {
+            const qg_weight& w = st.w[m];
+            for (int64_t row0 = 0; row0 < w.n; row0 += r) {
+                SlotD& t = sl[slot++];
+                t.codes = reinterpret_cast<uint64_t>(w.codes) + (uint64_t)row0 * (uint64_t)k;
+                t.scale = reinterpret_cast<uint64_t>(w.scale) + 4u * (uint64_t)row0;
+                t.y = reinterpret_cast<uint64_t>(st.y[m]) + 2u * (uint64_t)row0;
+                t.rows = (int32_t)(w.n - row0 < r ? w.n - row0 : r);
+                t.k = k;
+                t.nseg = d.nseg;
+                t.stage = s;
+            }
+        }
+        d.nslots = (int32_t)(slot - d.slot0);
+        if (k > max_k) max_k = k;
+        if (d.nseg * kItemChunks > nc) nc = d.nseg * kItemChunks;
+    }
+    h->max_k = max_k;
+    h->nc = nc;
+    return QG_OK;
+}
+
+qg_status qg_qgemv_chain(const void* image, void* plan, void* stream) {
+    using namespace qg::chain;
+    if (!image || !plan) return QG_ERR_NULLPTR;
+    if (!aligned16(image) || !aligned16(plan)) return QG_ERR_ALIGN;
+    const Header* h = static_cast<const Header*>(image);
+    if (h->magic != kMagic || h->version != kVersion) return QG_ERR_ARG;
+    if (h->nstages < 1 || h->nstages > QG_CHAIN_MAX_STAGES || h->grid < 1 || h->grid > 65535) return QG_ERR_ARG;
+    return from_hip(qg::launch_chain(image, plan, as_stream(stream)));
 }
 
 }  // extern "C"
