@@ -3,6 +3,7 @@
 // memory, with the control words the launch updates and leaves reset.
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace qg {
@@ -62,4 +63,9 @@ inline uint64_t plan_bytes(int32_t nstages, int64_t total_slots) {
 }
 
 }  // namespace chain
+
+// The chained decode step: `image` is the host copy of the plan built by
+// qg_chain_plan, `plan` its device copy (control words included).
+hipError_t launch_chain(const void* image, void* plan, hipStream_t st);
+
 }  // namespace qg

@@ -130,10 +130,6 @@ hipError_t launch_quantize_mxfp4(const void* x, int xt, int64_t rows, int64_t co
 hipError_t launch_gemm_mxfp4(const uint8_t* a, const uint8_t* as, int64_t m, int64_t k, const uint8_t* b,
                              const uint8_t* bs, int64_t n, float* y, hipStream_t st);
 
-// The chained decode step (chain.hip): `image` is the host copy of the plan
-// built by qg_chain_plan, `plan` its device copy (control words included).
-hipError_t launch_chain(const void* image, void* plan, hipStream_t st);
-
 int device_cu_count();
 
 // Streaming-read probe: workgroups of kQProbeThreads each read one block of
