@@ -446,18 +446,20 @@ static hipError_t launch_xl(int most, int grid, size_t lds, const BGroup& g, hip
 // ------------------------------------------ one tile per wave (tiled)
 // Grouped launches of 16-row tiled codes with more tiles than CUs and
 // K <= 4608: one workgroup per CU holds the activation fragments of all of
-// K in LDS (loaded once, one barrier), and each wave multiplies whole tiles
-// alone -- all K of its 16 rows -- so the waves never wait for each other.
-// A wave's tiles are blockIdx.x + gridDim.x (w + 8 q); its units (tile,
-// unit c) form one stream that a ring of D loads in flight runs through,
-// across tile ends (D divides the units per tile, so a tile ends between two
-// turns of the ring and the loop body has no memory operation under a
-// branch).  Per unit: the 1 KB block of codes (non-temporal, read once),
+// K in LDS (loaded once), and each wave multiplies whole tiles alone -- all
+// K of its 16 rows -- so after the first tile the waves never wait for each
+// other.  The fragments arrive in phases of 8 units (one per wave), each
+// written behind its own barrier, and the first tile's products of a phase
+// start as soon as it is in LDS (at 16 tokens the fragments are 128 KB per
+// CU, twice a tile's weights).  A wave's tiles are blockIdx.x + gridDim.x
+// (w + 8 q); its units (tile, unit c) form one stream that a ring of D loads
+// in flight runs through, across tile ends (D divides 8 and the units per
+// tile, so phases and tiles end between two turns of the ring and the loop
+// body has no memory operation under a branch).  Per unit: the 1 KB block of codes (non-temporal, read once),
 // widened to bf16, and the two activation fragments of unit c from LDS into
 // two MFMAs; after a tile's last unit its 16 x 16 products are complete
-// (summed in unit order), rescaled by the row scales (scalar loads, issued
-// when the tile starts) and stored.
-typedef const __attribute__((address_space(4))) float cfloat;
+// (summed in unit order), rescaled by the row scales (each lane's four,
+// loaded when the tile starts) and stored.
 
 template <int YT, int D, int MG>
 __global__ __launch_bounds__(kBThreads) void qgemv_batch_wt_kernel(BGroup grp) {
@@ -516,76 +518,114 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_wt_kernel(BGroup grp) {
         return v;
     };
 
-    // activations: wave w loads units w, w + 8, ... into their fragment
-    // slots (requested first, the ring's first D units after them)
-    u32x4 ring[D];
-    {
-        constexpr int kXU = (kBatchXlMaxLds / 2048 + kBWaves - 1) / kBWaves;  // units per wave at most
-        u32x4 v0[kXU], v1[kXU];
+    // activations: wave w requests units w, w + 8, ... (the fragments of
+    // phase p = units 8p .. 8p + 7 are one unit per wave), then the ring's
+    // first D units of weights
+    constexpr int kXU = (kBatchXlMaxLds / 2048 + kBWaves - 1) / kBWaves;  // phases (units per wave) at most
+    u32x4 v0[kXU], v1[kXU];
 #pragma unroll
-        for (int q = 0; q < kXU; ++q) {
-            const int c = wave + kBWaves * q;
-            const bool ok = c < C && i < M;
-            const uint32_t xo = (uint32_t)((i * K + c * kBUnit + 16 * g) * 2);
-            v0[q] = load16(rx, ok ? xo : oob_x);
-            v1[q] = load16(rx, ok ? xo + 16u : oob_x);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int d = 0; d < D; ++d) ring[d] = fetch();
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int q = 0; q < kXU; ++q) {
-            const int c = wave + kBWaves * q;
-            if (c < C) {
-                xsh[(2 * c) * kWave + lane] = v0[q];
-                xsh[(2 * c + 1) * kWave + lane] = v1[q];
-            }
-        }
-        lds_barrier();
+    for (int q = 0; q < kXU; ++q) {
+        const int c = wave + kBWaves * q;
+        const bool ok = c < C && i < M;
+        const uint32_t xo = (uint32_t)((i * K + c * kBUnit + 16 * g) * 2);
+        v0[q] = load16(rx, ok ? xo : oob_x);
+        v1[q] = load16(rx, ok ? xo + 16u : oob_x);
     }
-    for (int q = 0; q < wt; ++q) {
-        const Tile ct = tile_of(q);
-        // the tile's 16 row scales, rows clamped into the matrix (rows past
-        // it are never stored)
-        cfloat* const sp = (cfloat*)ct.mat.s_w;
-        float srow[16];
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 ring[D];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) srow[r] = sp[min(ct.row0 + r, ct.mat.n - 1)];
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int cb = 0; cb < C; cb += D) {
+    for (int d = 0; d < D; ++d) ring[d] = fetch();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // this lane's four row scales (rows 4 (l / 16) + r of the tile; rows
+    // past the matrix read zero and are never stored), vector loads issued
+    // when the tile starts: they complete long before the tile ends, so the
+    // wait for them does not wait for the ring
+    auto scales = [&](const Tile& ct, float (&sw)[4]) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(ct.mat.s_w + ct.row0, (uint32_t)(ct.rows * 4));
 #pragma unroll
-            for (int d = 0; d < D; ++d) {
-                const int c = cb + d;
+        for (int r = 0; r < 4; ++r) {
+            const int row = 4 * g + r;
+            sw[r] = __uint_as_float(load4(rs, row < ct.rows ? (uint32_t)(4 * row) : (uint32_t)(ct.rows * 4)));
+        }
+    };
+    // one turn of the ring: units cb .. cb + D - 1 of the current tile, the
+    // ring refilled unit by unit (a wave without tiles only keeps the
+    // prefetch cursor going: its loads read zeros, it multiplies nothing)
+    auto turn = [&](int cb, bool live, f32x4& acc) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int c = cb + d;
+            const u32x4 w = ring[d];
+            ring[d] = fetch();
+            if (live) {
                 bf16x8 a0, a1;
-                widen16(ring[d], a0, a1);
+                widen16(w, a0, a1);
                 const u32x4 xa = xsh[(2 * c) * kWave + lane];
                 const u32x4 xb = xsh[(2 * c + 1) * kWave + lane];
-                ring[d] = fetch();
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8, xa), acc, 0, 0, 0);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8, xb), acc, 0, 0, 0);
+            } else {
+                asm volatile("" ::"v"(w));  // the load is waited for in issue order either way
             }
         }
-        // lane l holds token l % 16, rows 4 (l / 16) + r
+    };
+    // lane l holds token l % 16, rows 4 (l / 16) + r
+    auto store = [&](const Tile& ct, const float (&sw)[4], const f32x4& acc) {
         const int tok = lane & 15;
         if (tok < M) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 4 * g + r;
-                const float s = g == 0 ? srow[r] : g == 1 ? srow[4 + r] : g == 2 ? srow[8 + r] : srow[12 + r];
                 if (row < ct.rows) {
-                    const float o = acc[r] / s;
+                    const float o = acc[r] / sw[r];
                     const int64_t at = (int64_t)tok * ct.mat.n + ct.row0 + row;
                     if constexpr (YT == 0) static_cast<float*>(ct.mat.y)[at] = o;
                     else static_cast<uint16_t*>(ct.mat.y)[at] = (uint16_t)f32_to_bf16(o);
                 }
             }
         }
+    };
+    // The first tile, with every wave taking part: phase p of the
+    // activations is written to LDS behind a barrier of its own, and the
+    // tile's products over that phase's units follow at once, while the
+    // later phases are still arriving.  Waves without a tile write their
+    // units and pass the barriers.
+    {
+        const bool live = wt > 0;
+        const Tile ct = tile_of(0);
+        float sw[4];
+        scales(ct, sw);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < kXU; ++p) {
+            if (kBWaves * p < C) {  // uniform: every wave passes the same barriers
+                const int c = wave + kBWaves * p;
+                if (c < C) {
+                    xsh[(2 * c) * kWave + lane] = v0[p];
+                    xsh[(2 * c + 1) * kWave + lane] = v1[p];
+                }
+                lds_barrier();
+                const int ce = min(kBWaves * (p + 1), C);  // D divides 8 and C
+                for (int cb = kBWaves * p; cb < ce; cb += D) turn(cb, live, acc);
+            }
+        }
+        if (live) store(ct, sw, acc);
+    }
+    for (int q = 1; q < wt; ++q) {
+        const Tile ct = tile_of(q);
+        float sw[4];
+        scales(ct, sw);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int cb = 0; cb < C; cb += D) turn(cb, true, acc);
+        store(ct, sw, acc);
     }
 }
 
-// ring depth: the largest power of two up to 16 that divides the units per tile
-static int wt_ring(int C) { return C % 16 == 0 ? 16 : C % 8 == 0 ? 8 : C % 4 == 0 ? 4 : 2; }
+// ring depth: 4 units (4 KB per wave in flight) where it divides the units
+// per tile, else 2 (C is even).  Measured on MI355X at 16 tokens, 1376 tiles
+// of 4096 columns: 16 units 24.1 us, 8 23.3 us, 4 22.85 us, 2 28.3 us.
+static int wt_ring(int C) { return C % 4 == 0 ? 4 : 2; }
 
 template <int YT, int D, int MG>
 static hipError_t launch_wt_d(int grid, size_t lds, const BGroup& g, hipStream_t st) {
@@ -603,8 +643,6 @@ static hipError_t launch_wt_d(int grid, size_t lds, const BGroup& g, hipStream_t
 template <int YT, int MG>
 static hipError_t launch_wt_mg(int C, int grid, size_t lds, const BGroup& g, hipStream_t st) {
     switch (wt_ring(C)) {
-        case 16: return launch_wt_d<YT, 16, MG>(grid, lds, g, st);
-        case 8: return launch_wt_d<YT, 8, MG>(grid, lds, g, st);
         case 4: return launch_wt_d<YT, 4, MG>(grid, lds, g, st);
         default: return launch_wt_d<YT, 2, MG>(grid, lds, g, st);
     }

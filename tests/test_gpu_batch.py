@@ -307,3 +307,30 @@ def test_qgemv_batch_grouped_tiles16(qg, rows):
     for w, y in zip(ws, ys):
         q_ref, s_ref = oracle.quantize_absmax(w, per_row=True)
         assert oracle.normwise_error(host(y), oracle.y_w8a16_batch(q_ref, s_ref, xb)) <= TOL_F32
+
+
+@pytest.mark.parametrize("rows,k,m", [([9000, 8000], 4224, 16), ([20000, 777], 1152, 3), ([10000, 7001], 4608, 7)])
+def test_qgemv_batch_grouped_tiles16_wave_tiles(qg, rows, k, m):
+    """The one-tile-per-wave path (five or more tiles per CU) that takes the
+    activations in phases of 8 units: short last phases (K = 4224 and 1152:
+    66 and 18 units, with 2-unit rings), the largest K it takes (4608, 9
+    phases), waves without a tile, ragged last tiles and fewer than 16
+    tokens.  Every row of every matrix, fp32 and bf16 outputs, against the
+    oracle; nothing is written past the outputs."""
+    note("qgemv batch grouped tiles16 wave tiles %s k=%d m=%d" % (rows, k, m))
+    tiles = sum((n + 15) // 16 for n in rows)
+    assert -(-tiles // 256) >= 5  # five or more tiles for some workgroups on 256 CUs
+    xb = synth.to_bf16_bits(synth.gaussian(synth.rng(95 + k), (m, k), 1.0))
+    xd = dev_bf16(xb)
+    ws = [synth.gaussian(synth.rng(400 + j + k), (n, k), 0.02) for j, n in enumerate(rows)]
+    Wts = [qg.tiled16(_weight(qg, w)[0]) for w in ws]
+    y32s = qg.qgemv_batch_grouped(Wts, xd, y_dtype=torch.float32)
+    guarded = [_guarded2(m, n, torch.bfloat16) for n in rows]
+    qg.qgemv_batch_grouped(Wts, xd, ys=[y for _, y in guarded])
+    for w, y32, (full, yb), n in zip(ws, y32s, guarded, rows):
+        q_ref, s_ref = oracle.quantize_absmax(w, per_row=True)
+        y_ref = oracle.y_w8a16_batch(q_ref, s_ref, xb)
+        y32_h = host(y32)
+        assert oracle.normwise_error(y32_h, y_ref) <= TOL_F32
+        check_bf16_output(host(yb).ravel(), y32_h.ravel(), y_ref.ravel())
+        assert canaries_intact(full, m * n)
