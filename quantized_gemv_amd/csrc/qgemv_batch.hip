@@ -255,11 +255,12 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_kernel(BGroup grp) {
     }
 }
 
-// ------------------------------------------------- activations in LDS
+// ------------------------------------------ activations in registers
 // Grouped launches with more 16-row tiles than CUs and K <= 4608: one
-// workgroup per CU holds the activation fragments of all of K in LDS (wave
-// w keeps those of its MOST units, written once) and walks its tiles
-// blockIdx.x + gridDim.x * j.  Per tile a wave loads its MOST units of
+// workgroup per CU; wave w keeps the activation fragments of its MOST units
+// of K in registers (loaded once: 4 MOST VGPRs, no LDS copy to write and
+// read back; measured 15.9 -> 15.6 us for q, k, v at 16 tokens against the
+// LDS copy) and the workgroup walks its tiles blockIdx.x + gridDim.x * j.  Per tile a wave loads its MOST units of
 // weights (16 rows x 64 k each) and the tile's row scales in one go, the
 // next tile's loads in flight while it multiplies; MOST is a template
 // parameter, so there is no branch between the loads and the products.
@@ -270,7 +271,6 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_kernel(BGroup grp) {
 template <int YT, int MOST>
 __global__ __launch_bounds__(kBThreads) void qgemv_batch_xl_kernel(BGroup grp) {
     __shared__ f32x4 part[2][kBWaves][kWave];
-    extern __shared__ u32x4 xsh[];  // [wave][unit][xa | xb][lane]
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -283,7 +283,6 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_xl_kernel(BGroup grp) {
     const int ntiles = grp.wg_start[grp.count];
     const int my_tiles =
         ntiles > (int)blockIdx.x ? (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
-    u32x4* const xw = xsh + (size_t)wave * MOST * 2 * kWave;
 
     // the tile's matrix, selected with constant indices into the kernel
     // argument (a computed index would take it through memory and make the
@@ -330,14 +329,15 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_xl_kernel(BGroup grp) {
             f.sw[r] = __uint_as_float(load4(rs, row < t.rows ? (uint32_t)(4 * row) : (uint32_t)(t.rows * 4)));
         }
     };
+    u32x4 xr0[MOST], xr1[MOST];  // this wave's activation fragments (units >= C: zeros)
     auto consume = [&](int j, const Frag& f) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < MOST; ++u) {
             bf16x8 a0, a1;
             widen16(f.w[u], a0, a1);
-            const u32x4 xa = xw[(2 * u) * kWave + lane];
-            const u32x4 xb = xw[(2 * u + 1) * kWave + lane];
+            const u32x4 xa = xr0[u];
+            const u32x4 xb = xr1[u];
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8, xa), acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8, xb), acc, 0, 0, 0);
         }
@@ -372,29 +372,20 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_xl_kernel(BGroup grp) {
         // passed tile j + 1's barrier, which the reducing wave reaches only
         // after its reads above
     };
-    // this wave's activation fragments (all requested, then the first tile's
-    // weights, then written to LDS: the writes wait for the activations
-    // while the weights stay in flight); each wave reads only what it wrote
+    // this wave's activation fragments, requested before the first tile's
+    // weights (the first products wait for them in issue order)
     Frag fa, fb;
-    {
-        u32x4 v0[MOST], v1[MOST];
 #pragma unroll
-        for (int u = 0; u < MOST; ++u) {
-            const int c = c0 + u;
-            const bool ok = c < C && i < M;
-            const uint32_t xo = (uint32_t)((i * K + c * kBUnit + 16 * g) * 2);
-            v0[u] = load16(rx, ok ? xo : oob_x);
-            v1[u] = load16(rx, ok ? xo + 16u : oob_x);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        issue(0, fa);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < MOST; ++u) {
-            xw[(2 * u) * kWave + lane] = v0[u];
-            xw[(2 * u + 1) * kWave + lane] = v1[u];
-        }
+    for (int u = 0; u < MOST; ++u) {
+        const int c = c0 + u;
+        const bool ok = c < C && i < M;
+        const uint32_t xo = (uint32_t)((i * K + c * kBUnit + 16 * g) * 2);
+        xr0[u] = load16(rx, ok ? xo : oob_x);
+        xr1[u] = load16(rx, ok ? xo + 16u : oob_x);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    issue(0, fa);
+    __builtin_amdgcn_sched_barrier(0);
     // two tiles per round, each buffer reloaded right after its products; a
     // last round past my_tiles reads zeros and its tile stores nothing
     for (int j = 0; j < my_tiles; j += 2) {
@@ -409,36 +400,18 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_xl_kernel(BGroup grp) {
 }
 
 template <int YT>
-static hipError_t launch_xl(int most, int grid, size_t lds, const BGroup& g, hipStream_t st) {
-    const void* fn = nullptr;
+static hipError_t launch_xl(int most, int grid, const BGroup& g, hipStream_t st) {
     switch (most) {
-        case 1: fn = reinterpret_cast<const void*>(qgemv_batch_xl_kernel<YT, 1>); break;
-        case 2: fn = reinterpret_cast<const void*>(qgemv_batch_xl_kernel<YT, 2>); break;
-        case 3: fn = reinterpret_cast<const void*>(qgemv_batch_xl_kernel<YT, 3>); break;
-        case 4: fn = reinterpret_cast<const void*>(qgemv_batch_xl_kernel<YT, 4>); break;
-        case 5: fn = reinterpret_cast<const void*>(qgemv_batch_xl_kernel<YT, 5>); break;
-        case 6: fn = reinterpret_cast<const void*>(qgemv_batch_xl_kernel<YT, 6>); break;
-        case 7: fn = reinterpret_cast<const void*>(qgemv_batch_xl_kernel<YT, 7>); break;
-        case 8: fn = reinterpret_cast<const void*>(qgemv_batch_xl_kernel<YT, 8>); break;
-        case 9: fn = reinterpret_cast<const void*>(qgemv_batch_xl_kernel<YT, 9>); break;
+        case 1: qgemv_batch_xl_kernel<YT, 1><<<grid, kBThreads, 0, st>>>(g); break;
+        case 2: qgemv_batch_xl_kernel<YT, 2><<<grid, kBThreads, 0, st>>>(g); break;
+        case 3: qgemv_batch_xl_kernel<YT, 3><<<grid, kBThreads, 0, st>>>(g); break;
+        case 4: qgemv_batch_xl_kernel<YT, 4><<<grid, kBThreads, 0, st>>>(g); break;
+        case 5: qgemv_batch_xl_kernel<YT, 5><<<grid, kBThreads, 0, st>>>(g); break;
+        case 6: qgemv_batch_xl_kernel<YT, 6><<<grid, kBThreads, 0, st>>>(g); break;
+        case 7: qgemv_batch_xl_kernel<YT, 7><<<grid, kBThreads, 0, st>>>(g); break;
+        case 8: qgemv_batch_xl_kernel<YT, 8><<<grid, kBThreads, 0, st>>>(g); break;
+        case 9: qgemv_batch_xl_kernel<YT, 9><<<grid, kBThreads, 0, st>>>(g); break;
         default: return hipErrorInvalidValue;
-    }
-    static bool attr_set[10] = {false};
-    if (!attr_set[most]) {
-        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBatchXlMaxLds);
-        if (e != hipSuccess) return e;
-        attr_set[most] = true;
-    }
-    switch (most) {
-        case 1: qgemv_batch_xl_kernel<YT, 1><<<grid, kBThreads, lds, st>>>(g); break;
-        case 2: qgemv_batch_xl_kernel<YT, 2><<<grid, kBThreads, lds, st>>>(g); break;
-        case 3: qgemv_batch_xl_kernel<YT, 3><<<grid, kBThreads, lds, st>>>(g); break;
-        case 4: qgemv_batch_xl_kernel<YT, 4><<<grid, kBThreads, lds, st>>>(g); break;
-        case 5: qgemv_batch_xl_kernel<YT, 5><<<grid, kBThreads, lds, st>>>(g); break;
-        case 6: qgemv_batch_xl_kernel<YT, 6><<<grid, kBThreads, lds, st>>>(g); break;
-        case 7: qgemv_batch_xl_kernel<YT, 7><<<grid, kBThreads, lds, st>>>(g); break;
-        case 8: qgemv_batch_xl_kernel<YT, 8><<<grid, kBThreads, lds, st>>>(g); break;
-        default: qgemv_batch_xl_kernel<YT, 9><<<grid, kBThreads, lds, st>>>(g); break;
     }
     return hipGetLastError();
 }
@@ -681,6 +654,7 @@ static hipError_t launch_wt(int C, int grid, size_t lds, const BGroup& g, hipStr
 // for the launch without split.
 constexpr int kCachePolicyAgent = 16;  // sc1: agent scope (gfx9.4/9.5 cache-policy bits)
 constexpr int kSkS = 4;          // splits of K
+constexpr int kSkDepth = 2;      // tiles of weights in flight per wave
 constexpr int kSkMaxT = kSkS;    // tiles per workgroup at most: T <= kSkS when tiles <= CUs
 constexpr int kSkMaxUnits = 8;   // units of 64 k per wave in registers (K / kSkS <= 8 x 8 x 64)
 
@@ -724,9 +698,14 @@ struct SkParams {
     int n, k, m, tiles, C, Cs;
 };
 
-// MOST units of 64 k per wave, T tiles per workgroup: every load of the
-// workgroup's share is issued up front, with no branches between them and
-// the products, so the waits count down through the loads in order.
+// MOST units of 64 k per wave, T tiles per workgroup: the wave's activation
+// fragments are requested first and kept in registers for all T tiles; the
+// tiles' weights follow two tiles ahead of the products, with no branches
+// between the loads and the products, so the waits count down through the
+// loads in order.  (Every tile requested up front measured 14.4 us for the
+// 4096 x 11008 product at 16 tokens, two tiles ahead 13.2 us, one 13.6 us:
+// with the whole share in flight no product starts before all of it has
+// arrived.)
 template <int YT, int MOST, int T, bool T16>
 __global__ __launch_bounds__(kBThreads) void qgemv_batch_splitk_kernel(SkParams p) {
     __shared__ f32x4 red[T][kBWaves][kWave];
@@ -744,12 +723,10 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_splitk_kernel(SkParams 
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.x, (uint32_t)(M * K * 2));
     const uint32_t oob_x = (uint32_t)(M * K * 2);
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.part, (uint32_t)(kSkS * p.tiles * kWave * 16));
-    // weights of the T tiles (rows past n and units past the range read
-    // zeros through the range check), then the activation fragments of the
-    // wave's units (tokens >= m read zeros)
+    // weights of tile t (rows past n and units past the range read zeros
+    // through the range check)
     u32x4 w[T][MOST];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
+    auto issue_t = [&](int t) {
         const int row0 = (t0 + t) * 16;
         const int rows = t < nt ? min(16, p.n - row0) : 0;
         // the tiled layout's last tile is padded to 16 rows (zeros)
@@ -765,7 +742,9 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_splitk_kernel(SkParams 
                 w[t][u] = load16(rw, (c < c1 && i < rows) ? (uint32_t)(i * K + c * kBUnit + 16 * g) : tile_bytes);
             }
         }
-    }
+    };
+    // the activation fragments of the wave's units, requested first (tokens
+    // >= m read zeros)
     u32x4 xa[MOST], xb[MOST];
 #pragma unroll
     for (int u = 0; u < MOST; ++u) {
@@ -775,10 +754,19 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_splitk_kernel(SkParams 
         xa[u] = load16(rx, ok ? xo : oob_x);
         xb[u] = load16(rx, ok ? xo + 16u : oob_x);
     }
-    __builtin_amdgcn_sched_barrier(0);  // all loads in flight before the first product
+    // kSkDepth tiles in flight: tile t + kSkDepth - 1 is requested when
+    // tile t's products begin
+#pragma unroll
+    for (int t = 0; t < (T < kSkDepth ? T : kSkDepth); ++t) issue_t(t);
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 acc[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
+        if (t > 0 && t - 1 + kSkDepth < T) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_t(t - 1 + kSkDepth);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < MOST; ++u) {
@@ -913,19 +901,20 @@ hipError_t launch_qgemv_batch(const BatchArgs* a, int count, hipStream_t st) {
     const int most = (C + kBWaves - 1) / kBWaves;
     const size_t xl_bytes = (size_t)kBWaves * most * 2 * kWave * sizeof(u32x4);
     if (tiles > cus && xl_bytes <= kBatchXlMaxLds) {
-        // activations kept in LDS: one workgroup per CU, each walking its
-        // tiles with the fragments loaded once
+        // activations loaded once per workgroup (into LDS, or into the
+        // waves' registers where the eight waves share each tile): one
+        // workgroup per CU, each walking its tiles
         const int grid = cus;
         if (a[0].t16) {
             // five or more tiles per workgroup keep five or more waves busy
             // with one tile each; fewer, and the eight waves share each tile
-            // (measured on MI355X: 1376 tiles 24.0 against 25.4 us, 768 tiles
-            // 17.0 against 15.7 us, at 16 tokens)
+            // (measured on MI355X at 16 tokens: 1376 tiles 21.4 against
+            // 25.4 us, 768 tiles 18.6 against 15.6 us)
             if ((tiles + cus - 1) / cus >= 5) {
                 const size_t wt_bytes = (size_t)C * 2 * kWave * sizeof(u32x4);
                 return a[0].yt == 0 ? launch_wt<0>(C, grid, wt_bytes, g, st) : launch_wt<1>(C, grid, wt_bytes, g, st);
             }
-            return a[0].yt == 0 ? launch_xl<0>(most, grid, xl_bytes, g, st) : launch_xl<1>(most, grid, xl_bytes, g, st);
+            return a[0].yt == 0 ? launch_xl<0>(most, grid, g, st) : launch_xl<1>(most, grid, g, st);
         }
         auto k0 = qgemv_batch_kernel<0, true, false>;
         auto k1 = qgemv_batch_kernel<1, true, false>;
