@@ -421,7 +421,10 @@ static hipError_t launch_xl(int most, int grid, const BGroup& g, hipStream_t st)
 // K <= 4608: one workgroup per CU holds the activation fragments of all of
 // K in LDS (loaded once), and each wave multiplies whole tiles alone -- all
 // K of its 16 rows -- so after the first tile the waves never wait for each
-// other.  The fragments arrive in phases of 8 units (one per wave), each
+// other.  With three or four tiles per CU (q, k, v: 768 tiles) that would
+// leave most waves idle, so there (H = 2) waves 2j and 2j + 1 take one half
+// of K of tile j each and add their halves through LDS once at the end:
+// 15.5 -> 13.1 us for q, k, v at 16 tokens against the shared-tile kernel.  The fragments arrive in phases of 8 units (one per wave), each
 // written behind its own barrier, and the first tile's products of a phase
 // start as soon as it is in LDS (at 16 tokens the fragments are 128 KB per
 // CU, twice a tile's weights).  A wave's tiles are blockIdx.x + gridDim.x
@@ -434,9 +437,11 @@ static hipError_t launch_xl(int most, int grid, const BGroup& g, hipStream_t st)
 // (summed in unit order), rescaled by the row scales (each lane's four,
 // loaded when the tile starts) and stored.
 
-template <int YT, int D, int MG>
+template <int YT, int D, int MG, int H>
 __global__ __launch_bounds__(kBThreads) void qgemv_batch_wt_kernel(BGroup grp) {
+    static_assert(H == 1 || H == 2, "whole tiles or halves");
     extern __shared__ u32x4 xsh[];  // [unit][xa | xb][lane]
+    __shared__ f32x4 hpart[H == 2 ? kBWaves / 2 : 1][kWave];  // H = 2: the second halves' partial tiles
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -448,7 +453,14 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_wt_kernel(BGroup grp) {
     const int ntiles = grp.wg_start[grp.count];
     const int my_tiles =
         ntiles > (int)blockIdx.x ? (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
-    const int wt = my_tiles > wave ? (my_tiles - wave + kBWaves - 1) / kBWaves : 0;  // this wave's tiles
+    // H = 1: wave w multiplies tiles w, w + 8, ... of the workgroup over all
+    // of K.  H = 2 (at most 4 tiles per workgroup): waves 2j and 2j + 1 take
+    // the two halves of K of tile j, one piece each.
+    const int CH = C / H;                     // units of a piece
+    const int half = H == 2 ? (wave & 1) : 0;
+    const int cbase = half * CH;              // the piece's first unit
+    const int wt = H == 1 ? (my_tiles > wave ? (my_tiles - wave + kBWaves - 1) / kBWaves : 0)
+                          : (wave / 2 < my_tiles ? 1 : 0);  // this wave's pieces
 
     struct Tile {
         BMat mat;
@@ -457,7 +469,7 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_wt_kernel(BGroup grp) {
     // the wave's tile q, with its matrix selected by constant indices (the
     // buffer descriptors stay uniform; MG >= count slots are looked at)
     auto tile_of = [&](int q) {
-        const int tile = (int)blockIdx.x + (int)gridDim.x * (wave + kBWaves * q);
+        const int tile = (int)blockIdx.x + (int)gridDim.x * (H == 1 ? wave + kBWaves * q : wave / 2 + 4 * q);
         Tile t;
         t.mat = grp.mats[0];
         int start = 0;
@@ -481,8 +493,8 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_wt_kernel(BGroup grp) {
         prw = make_rsrc(t.mat.wq + (int64_t)t.row0 * K, (uint32_t)((t.rows > 0 ? 16 : 0) * K));
     }
     auto fetch = [&]() -> u32x4 {
-        const u32x4 v = load16_nt(prw, (uint32_t)(pc * 1024 + lane * 16));
-        if (++pc == C) {
+        const u32x4 v = load16_nt(prw, (uint32_t)((cbase + pc) * 1024 + lane * 16));
+        if (++pc == CH) {
             pc = 0;
             ++pq;
             const Tile t = tile_of(pq);
@@ -491,14 +503,20 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_wt_kernel(BGroup grp) {
         return v;
     };
 
-    // activations: wave w requests units w, w + 8, ... (the fragments of
-    // phase p = units 8p .. 8p + 7 are one unit per wave), then the ring's
-    // first D units of weights
+    // activations: phase p holds 8 units, one written by each wave (H = 1:
+    // units 8p .. 8p + 7; H = 2: units 4p .. 4p + 3 of each half); wave w
+    // requests its unit of every phase, then the ring's first D units of
+    // weights
     constexpr int kXU = (kBatchXlMaxLds / 2048 + kBWaves - 1) / kBWaves;  // phases (units per wave) at most
+    auto phase_unit = [&](int q) -> int {  // C when past the last unit
+        if constexpr (H == 1) return min(wave + kBWaves * q, C);
+        const int u = 4 * q + (wave & 3);
+        return u < CH ? (wave < 4 ? 0 : CH) + u : C;
+    };
     u32x4 v0[kXU], v1[kXU];
 #pragma unroll
     for (int q = 0; q < kXU; ++q) {
-        const int c = wave + kBWaves * q;
+        const int c = phase_unit(q);
         const bool ok = c < C && i < M;
         const uint32_t xo = (uint32_t)((i * K + c * kBUnit + 16 * g) * 2);
         v0[q] = load16(rx, ok ? xo : oob_x);
@@ -573,24 +591,43 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_wt_kernel(BGroup grp) {
 #pragma unroll
         for (int p = 0; p < kXU; ++p) {
             if (kBWaves * p < C) {  // uniform: every wave passes the same barriers
-                const int c = wave + kBWaves * p;
+                const int c = phase_unit(p);
                 if (c < C) {
                     xsh[(2 * c) * kWave + lane] = v0[p];
                     xsh[(2 * c + 1) * kWave + lane] = v1[p];
                 }
                 lds_barrier();
-                const int ce = min(kBWaves * (p + 1), C);  // D divides 8 and C
-                for (int cb = kBWaves * p; cb < ce; cb += D) turn(cb, live, acc);
+                if constexpr (H == 1) {
+                    const int ce = min(kBWaves * (p + 1), C);  // D divides 8 and C
+                    for (int cb = kBWaves * p; cb < ce; cb += D) turn(cb, live, acc);
+                } else {
+#pragma unroll
+                    for (int cb = 0; cb < 4; cb += D) turn(cbase + 4 * p + cb, live, acc);  // 8 divides C
+                }
             }
         }
-        if (live) store(ct, sw, acc);
+        if constexpr (H == 1) {
+            if (live) store(ct, sw, acc);
+        } else {
+            // the pair's halves meet in LDS: first half + second half, in
+            // that order whichever finishes first
+            if (half == 1) hpart[wave >> 1][lane] = acc;
+            lds_barrier();
+            if (half == 0 && live) {
+                const f32x4 o = hpart[wave >> 1][lane];
+                f32x4 s;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s[r] = acc[r] + o[r];
+                store(ct, sw, s);
+            }
+        }
     }
     for (int q = 1; q < wt; ++q) {
         const Tile ct = tile_of(q);
         float sw[4];
         scales(ct, sw);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int cb = 0; cb < C; cb += D) turn(cb, true, acc);
+        for (int cb = 0; cb < CH; cb += D) turn(cbase + cb, true, acc);  // H = 1 only: one piece per wave otherwise
         store(ct, sw, acc);
     }
 }
@@ -600,9 +637,9 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_wt_kernel(BGroup grp) {
 // of 4096 columns: 16 units 24.1 us, 8 23.3 us, 4 22.85 us, 2 28.3 us.
 static int wt_ring(int C) { return C % 4 == 0 ? 4 : 2; }
 
-template <int YT, int D, int MG>
+template <int YT, int D, int MG, int H>
 static hipError_t launch_wt_d(int grid, size_t lds, const BGroup& g, hipStream_t st) {
-    auto fn = qgemv_batch_wt_kernel<YT, D, MG>;
+    auto fn = qgemv_batch_wt_kernel<YT, D, MG, H>;
     static bool attr_set = false;
     if (!attr_set) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
@@ -614,18 +651,19 @@ static hipError_t launch_wt_d(int grid, size_t lds, const BGroup& g, hipStream_t
     return hipGetLastError();
 }
 template <int YT, int MG>
-static hipError_t launch_wt_mg(int C, int grid, size_t lds, const BGroup& g, hipStream_t st) {
+static hipError_t launch_wt_mg(int C, bool halves, int grid, size_t lds, const BGroup& g, hipStream_t st) {
+    if (halves) return launch_wt_d<YT, 4, MG, 2>(grid, lds, g, st);  // C % 8 == 0
     switch (wt_ring(C)) {
-        case 4: return launch_wt_d<YT, 4, MG>(grid, lds, g, st);
-        default: return launch_wt_d<YT, 2, MG>(grid, lds, g, st);
+        case 4: return launch_wt_d<YT, 4, MG, 1>(grid, lds, g, st);
+        default: return launch_wt_d<YT, 2, MG, 1>(grid, lds, g, st);
     }
 }
 // matrix slots the kernel looks at: 1, 3 (q, k, v; gate, up) or all
 template <int YT>
-static hipError_t launch_wt(int C, int grid, size_t lds, const BGroup& g, hipStream_t st) {
-    if (g.count == 1) return launch_wt_mg<YT, 1>(C, grid, lds, g, st);
-    if (g.count <= 3) return launch_wt_mg<YT, 3>(C, grid, lds, g, st);
-    return launch_wt_mg<YT, kMaxGroupLaunch>(C, grid, lds, g, st);
+static hipError_t launch_wt(int C, bool halves, int grid, size_t lds, const BGroup& g, hipStream_t st) {
+    if (g.count == 1) return launch_wt_mg<YT, 1>(C, halves, grid, lds, g, st);
+    if (g.count <= 3) return launch_wt_mg<YT, 3>(C, halves, grid, lds, g, st);
+    return launch_wt_mg<YT, kMaxGroupLaunch>(C, halves, grid, lds, g, st);
 }
 
 // ---------------------------------------------------------------- split K
@@ -907,12 +945,16 @@ hipError_t launch_qgemv_batch(const BatchArgs* a, int count, hipStream_t st) {
         const int grid = cus;
         if (a[0].t16) {
             // five or more tiles per workgroup keep five or more waves busy
-            // with one tile each; fewer, and the eight waves share each tile
+            // with one tile each; three or four keep six to eight busy with
+            // half a tile each; fewer, and the eight waves share each tile
             // (measured on MI355X at 16 tokens: 1376 tiles 21.4 against
-            // 25.4 us, 768 tiles 18.6 against 15.6 us)
-            if ((tiles + cus - 1) / cus >= 5) {
+            // 25.4 us; 768 tiles 13.1 in halves, 18.6 whole, 15.6 shared)
+            const int per = (tiles + cus - 1) / cus;
+            const bool halves = per >= 3 && per <= 4 && C % 8 == 0;
+            if (per >= 5 || halves) {
                 const size_t wt_bytes = (size_t)C * 2 * kWave * sizeof(u32x4);
-                return a[0].yt == 0 ? launch_wt<0>(C, grid, wt_bytes, g, st) : launch_wt<1>(C, grid, wt_bytes, g, st);
+                return a[0].yt == 0 ? launch_wt<0>(C, halves, grid, wt_bytes, g, st)
+                                    : launch_wt<1>(C, halves, grid, wt_bytes, g, st);
             }
             return a[0].yt == 0 ? launch_xl<0>(most, grid, g, st) : launch_xl<1>(most, grid, g, st);
         }
