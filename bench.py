@@ -1268,40 +1268,87 @@ def oracle_per_config(np, synth):
     """Seconds the oracle takes on each of the five workloads at full size:
     the offline quantization (codes and scales from the fp32 weights) and the
     product (integer sums and the fp64 reference output) timed apart; input
-    generation excluded."""
+    generation excluded.  Beside each, the parity of the HIP path on the same
+    inputs against those oracle outputs: codes and scales bit for bit, int32
+    accumulators bit for bit where the path has them, and the fp32 output's
+    normwise error against the 1e-5 tolerance."""
     import oracle
+    import torch
+    import quantized_gemv_amd as qg
     out = {}
 
     def timed(f):
         t0 = time.perf_counter()
         r = f()
         return r, round(time.perf_counter() - t0, 3)
-    log("cpu baseline: oracle on the five workloads")
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    def dev_bf16(bits):
+        return dev(np.asarray(bits, np.uint16)).view(torch.bfloat16)
+
+    def host(t):
+        torch.cuda.synchronize()
+        return t.cpu().numpy()
+
+    def same(gpu, ref):
+        return bool(np.array_equal(host(gpu), np.asarray(ref)))
+
+    def parity(exact, y, y_ref):
+        err = oracle.normwise_error(host(y), y_ref)
+        exact = {k: bool(v) for k, v in exact.items()}
+        return {**exact, "y_normwise_err": float("%.3g" % err), "tol": 1e-5,
+                "ok": bool(all(exact.values()) and err <= 1e-5)}
+    log("cpu baseline: oracle on the five workloads (and the HIP path's parity against it)")
     wl = synth.tiny_gemv()
     (wq, sw), tq = timed(lambda: oracle.quantize_absmax(wl.tensors["w"], per_row=True))
     (xq, sx), tx = timed(lambda: oracle.quantize_absmax(wl.tensors["x"], per_row=False))
-    _, tp = timed(lambda: oracle.y_w8a8(oracle.int_dot_exact(wq, xq), sw, sx))
+    (acc, y_ref), tp = timed(lambda: (lambda a: (a, oracle.y_w8a8(a, sw, sx)))(oracle.int_dot_exact(wq, xq)))
+    gq, gs = qg.quantize_absmax(dev(wl.tensors["w"]), per_row=True)
+    gacc = torch.empty(256, dtype=torch.int32, device="cuda")
+    gy = qg.qgemv(qg.QWeight(qg.QG_WFMT_INT8, 256, 256, gq, gs), dev(wl.tensors["x"]), act_int8=True, acc_out=gacc)
     out["tiny_w8a8_256x256"] = {"quantize_s": tq, "product_s": round(tx + tp, 3),
-                                "product_note": "activation quantization + exact int32 dot + fp64 rescale"}
+                                "product_note": "activation quantization + exact int32 dot + fp64 rescale",
+                                "parity": parity({"codes_scales_exact": same(gq, wq) and same(gs, sw),
+                                                  "acc_exact": same(gacc, acc.astype(np.int32))}, gy, y_ref)}
     for name, (n, k) in synth.DECODE_7B_SHAPES.items():
         wl = synth.decode_w8a16(n=n, k=k, seed=synth.DECODE_7B_SEEDS[name])
         (wq, sw), tq = timed(lambda: oracle.quantize_absmax(wl.tensors["w"], per_row=True))
-        _, tp = timed(lambda: oracle.y_w8a16(wq, sw, wl.tensors["x_bf16"]))
-        out["decode_w8a16_" + name] = {"quantize_s": tq, "product_s": tp}
+        y_ref, tp = timed(lambda: oracle.y_w8a16(wq, sw, wl.tensors["x_bf16"]))
+        gq, gs = qg.quantize_absmax(dev(wl.tensors["w"]), per_row=True)
+        gy = qg.qgemv(qg.QWeight(qg.QG_WFMT_INT8, n, k, gq, gs), dev_bf16(wl.tensors["x_bf16"]), act_int8=False)
+        out["decode_w8a16_" + name] = {"quantize_s": tq, "product_s": tp,
+                                       "parity": parity({"codes_scales_exact": same(gq, wq) and same(gs, sw)},
+                                                        gy, y_ref)}
+        del gq, gy
     wl = synth.ternary_decode()
     (q, g), tq = timed(lambda: oracle.ternary_absmean(wl.tensors["w"]))
 
     def tern():
         xq, sx = oracle.quantize_absmax(wl.tensors["x"], per_row=False)
-        return oracle.y_ternary(oracle.int_dot_exact(q, xq), g, sx)
-    _, tp = timed(tern)
-    out["ternary_11008x4096"] = {"quantize_s": tq, "product_s": tp}
-    del q
+        acc = oracle.int_dot_exact(q, xq)
+        return acc, oracle.y_ternary(acc, g, sx)
+    (acc, y_ref), tp = timed(tern)
+    gq, gg = qg.quantize_ternary(dev(wl.tensors["w"]))
+    gacc = torch.empty(q.shape[0], dtype=torch.int32, device="cuda")
+    gy = qg.qgemv(qg.QWeight(qg.QG_WFMT_TERNARY2, q.shape[0], q.shape[1], qg.pack(gq, 2), gg),
+                  dev(wl.tensors["x"]), act_int8=True, acc_out=gacc)
+    out["ternary_11008x4096"] = {"quantize_s": tq, "product_s": tp,
+                                 "parity": parity({"codes_scales_exact": same(gq, q) and bool(host(gg)[0] == g),
+                                                   "acc_exact": same(gacc, acc.astype(np.int32))}, gy, y_ref)}
+    del q, gq, gy
     wl = synth.sign_residual_decode()
     (sgn, a, rq, sr), tq = timed(lambda: oracle.sign_residual_split(wl.tensors["w"]))
-    _, tp = timed(lambda: oracle.y_sign_residual(sgn, a, rq, sr, wl.tensors["x_bf16"]))
-    out["sign1_res8_28672x8192"] = {"quantize_s": tq, "product_s": tp}
-    del sgn, rq, wl
+    y_ref, tp = timed(lambda: oracle.y_sign_residual(sgn, a, rq, sr, wl.tensors["x_bf16"]))
+    n, k = sgn.shape
+    gsg, ga, grq, gsr = qg.split_sign_residual(dev(wl.tensors["w"]))
+    exact = {"codes_scales_exact": same(gsg, sgn) and same(ga, a) and same(grq, rq) and same(gsr, sr)}
+    gy = qg.qgemv(qg.QWeight(qg.QG_WFMT_SIGN1_RES8, n, k, qg.pack(gsg, 1), ga, resid=grq, scale2=gsr),
+                  dev_bf16(wl.tensors["x_bf16"]), act_int8=False)
+    out["sign1_res8_28672x8192"] = {"quantize_s": tq, "product_s": tp, "parity": parity(exact, gy, y_ref)}
+    del sgn, rq, wl, gsg, grq, gy
+    torch.cuda.empty_cache()
     wl = synth.prefill_outlier()
     idx = wl.tensors["idx"]
 
@@ -1312,12 +1359,23 @@ def oracle_per_config(np, synth):
 
     def prefill():
         xq, sx, xo = oracle.outlier_split_quantize(wl.tensors["x_bf16"], idx)
-        return oracle.y_prefill(oracle.int_gemm_exact(xq, wq), sx, sw, xo, wo)
-    _, tp = timed(prefill)
-    out["prefill_w8a8_outlier_2048x4096x4096"] = {"quantize_s": tq, "product_s": tp,
-                                                   "product_note": "outlier split + per-token quantization, exact "
-                                                                   "int32 GEMM (fp64 BLAS on integer values), fp64 "
-                                                                   "rescale and outlier GEMM"}
+        acc = oracle.int_gemm_exact(xq, wq)
+        return acc, oracle.y_prefill(acc, sx, sw, xo, wo)
+    (acc, y_ref), tp = timed(prefill)
+    wdev = dev(wl.tensors["w"])
+    gq, gs = qg.quantize_absmax(wdev, per_row=True)
+    gwo = qg.gather_columns_bf16(wdev, idx.tolist())
+    del wdev
+    gacc = torch.empty(acc.shape, dtype=torch.int32, device="cuda")
+    gy = qg.qgemm_w8a8_outlier(dev_bf16(wl.tensors["x_bf16"]), idx.tolist(), gq, gs, gwo, acc_out=gacc)
+    out["prefill_w8a8_outlier_2048x4096x4096"] = {
+        "quantize_s": tq, "product_s": tp,
+        "product_note": "outlier split + per-token quantization, exact int32 GEMM (fp64 BLAS on integer values), "
+                        "fp64 rescale and outlier GEMM",
+        "parity": parity({"codes_scales_exact": same(gq, wq) and same(gs, sw),
+                          "acc_exact": same(gacc, acc.astype(np.int32))}, gy, y_ref)}
+    del gq, gwo, gacc, gy
+    torch.cuda.empty_cache()
     return out
 
 
