@@ -37,6 +37,18 @@
  *     'Symmetric quantization', Fig. 17), except the ternary gamma and the
  *     sign-backbone alpha, which are dequantization steps (mean |W|).
  *   - Calls are stateless and may be issued from several host threads.
+ *   - Debug mode: with QG_DEBUG=1 in the environment (read at every call),
+ *     qg_quantize_absmax_split, qg_gather_columns_bf16 and
+ *     qg_qgemm_w8a8_outlier also run device-side checks of the outlier path
+ *     after their kernels (the index list as the kernels received it: in
+ *     range and strictly increasing; the gathered outlier values, zero codes
+ *     at the outlier columns and zero padding), then WAIT for the stream and
+ *     return QG_ERR_DEVICE_CHECK if a check failed.  This breaks the
+ *     never-synchronizes rule above on purpose, so it cannot be used while
+ *     the stream is captured into a graph.  QG_DEBUG=2 runs the same checks
+ *     expecting every gathered value with its lowest bit flipped, so that a
+ *     correct call with at least one outlier reports QG_ERR_DEVICE_CHECK:
+ *     a self-test of the reporting.
  */
 #ifndef QGEMV_H
 #define QGEMV_H
@@ -56,6 +68,7 @@ typedef int32_t qg_status;
 #define QG_ERR_ARG       4  /* unsupported format / mode / dtype, or bad index list */
 #define QG_ERR_WORKSPACE 5  /* workspace missing or too small */
 #define QG_ERR_HIP       6  /* the HIP runtime reported an error at launch */
+#define QG_ERR_DEVICE_CHECK 7  /* QG_DEBUG=1 only: a device-side check of the outlier path failed */
 
 /* element types */
 #define QG_F32  0

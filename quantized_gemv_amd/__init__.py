@@ -16,6 +16,6 @@ from ._binding import (QgError, QWeight, CWeight, EXPORTED, LIB_PATH, lib, statu
                        QG_F32, QG_BF16, QG_PER_TENSOR, QG_PER_ROW, QG_WFMT_INT8, QG_WFMT_TERNARY2,
                        QG_WFMT_SIGN1_RES8, QG_WFMT_Q4K, QG_WFMT_SIGN1_RES8Z, QG_WFMT_TERNARY3, QG_WFMT_INT8_T16, QG_ACT_INT8, QG_ACT_FLOAT, QG_MAX_OUTLIERS, QG_QGEMV_MAX_K,
                        QG_SEP_MAX_K, QG_BATCH_MAX_M, QG_BATCH_MAX_K, QG_MX_BLOCK, QG_QGEMM_MAX_K,
-                       QG_ABSMAX_SCRATCH_PARTS)
+                       QG_ABSMAX_SCRATCH_PARTS, QG_ERR_DEVICE_CHECK)
 
 __all__ = [n for n in dir() if not n.startswith("_")]

@@ -19,6 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 
 QG_OK = 0
+QG_ERR_DEVICE_CHECK = 7  # QG_DEBUG=1 (or 2) only: a device-side check of the outlier path failed
 QG_F32, QG_BF16 = 0, 1
 QG_PER_TENSOR, QG_PER_ROW = 0, 1
 QG_WFMT_INT8, QG_WFMT_TERNARY2, QG_WFMT_SIGN1_RES8, QG_WFMT_Q4K, QG_WFMT_SIGN1_RES8Z, QG_WFMT_TERNARY3 = 0, 1, 2, 3, 4, 5

@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include "qg_chain.h"
+#include "qg_debug.h"
 #include "qg_launch.h"
 
 namespace {
@@ -26,6 +27,22 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline qg_status from_hip(hipError_t e) { return e == hipSuccess ? QG_OK : QG_ERR_HIP; }
+
+// QG_DEBUG=1 in the environment (read at every call): the outlier-path
+// calls run the device-side checks of qg_debug.h after their kernels, wait
+// for the stream and report a failed check as QG_ERR_DEVICE_CHECK.
+// QG_DEBUG=2: the same with the checks' self-test expectation (a correct call
+// with outliers reports QG_ERR_DEVICE_CHECK).  0: off.
+int debug_mode() {
+    const char* e = getenv("QG_DEBUG");
+    if (!e || e[1] != 0) return 0;
+    return e[0] == '1' ? 1 : e[0] == '2' ? 2 : 0;
+}
+qg_status debug_result(hipStream_t st) {
+    uint32_t flags = 0;
+    if (qg::debug_take_flags(st, &flags) != hipSuccess) return QG_ERR_HIP;
+    return flags ? QG_ERR_DEVICE_CHECK : QG_OK;
+}
 
 // Validates a host index list: strictly increasing, inside [0, cols).
 qg_status check_idx(const int32_t* idx, int32_t n_out, int64_t cols, qg::OutlierIdx* out) {
@@ -86,6 +103,7 @@ const char* qg_status_str(qg_status s) {
         case QG_ERR_ARG: return "unsupported format/mode/dtype or bad index list";
         case QG_ERR_WORKSPACE: return "workspace missing or too small";
         case QG_ERR_HIP: return "HIP runtime error at launch";
+        case QG_ERR_DEVICE_CHECK: return "a QG_DEBUG device-side check of the outlier path failed";
         default: return "unknown status";
     }
 }
@@ -135,9 +153,13 @@ qg_status qg_quantize_absmax_split(const void* x, int64_t rows, int64_t cols, co
     qg::OutlierIdx oi;
     const qg_status st = check_idx(idx, n_out, cols, &oi);
     if (st != QG_OK) return st;
-    return from_hip(qg::launch_absmax_split(static_cast<const uint16_t*>(x), rows, cols, oi, n_out, q, s,
-                                            static_cast<uint16_t*>(x_out), n_out > 0 ? x_out_ld : 0,
-                                            as_stream(stream)));
+    const int ld = n_out > 0 ? x_out_ld : 0;
+    hipError_t e = qg::launch_absmax_split(static_cast<const uint16_t*>(x), rows, cols, oi, n_out, q, s,
+                                           static_cast<uint16_t*>(x_out), ld, as_stream(stream));
+    if (e != hipSuccess || !debug_mode()) return from_hip(e);
+    e = qg::debug_check_split(static_cast<const uint16_t*>(x), rows, cols, oi, n_out, q,
+                              static_cast<const uint16_t*>(x_out), ld, debug_mode() == 2, as_stream(stream));
+    return e != hipSuccess ? QG_ERR_HIP : debug_result(as_stream(stream));
 }
 
 size_t qg_detect_outliers_workspace_bytes(int64_t cols) {
@@ -169,8 +191,12 @@ qg_status qg_gather_columns_bf16(const float* w, int64_t n, int64_t k, const int
     qg::OutlierIdx oi;
     const qg_status st = check_idx(idx, n_out, k, &oi);
     if (st != QG_OK) return st;
-    return from_hip(qg::launch_gather_cols_bf16(w, n, k, oi, n_out, static_cast<uint16_t*>(w_out), w_out_ld,
-                                                as_stream(stream)));
+    hipError_t e = qg::launch_gather_cols_bf16(w, n, k, oi, n_out, static_cast<uint16_t*>(w_out), w_out_ld,
+                                               as_stream(stream));
+    if (e != hipSuccess || !debug_mode()) return from_hip(e);
+    e = qg::debug_check_gather(w, n, k, oi, n_out, static_cast<const uint16_t*>(w_out), w_out_ld,
+                               debug_mode() == 2, as_stream(stream));
+    return e != hipSuccess ? QG_ERR_HIP : debug_result(as_stream(stream));
 }
 
 qg_status qg_quantize_q4k(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* meta, void* stream) {
@@ -591,6 +617,10 @@ qg_status qg_qgemm_w8a8_outlier(const void* x, int64_t m, int64_t k, const int32
     hipError_t e = qg::launch_absmax_split(static_cast<const uint16_t*>(x), m, k, oi, n_out, xq, s_x, x_out, ld,
                                            as_stream(stream));
     if (e != hipSuccess) return QG_ERR_HIP;
+    const int dbg = debug_mode();
+    if (dbg && qg::debug_check_split(static_cast<const uint16_t*>(x), m, k, oi, n_out, xq, x_out, ld, dbg == 2,
+                                     as_stream(stream)) != hipSuccess)
+        return QG_ERR_HIP;
     qg::QgemmArgs a;
     a.m = m;
     a.k = k;
@@ -606,7 +636,9 @@ qg_status qg_qgemm_w8a8_outlier(const void* x, int64_t m, int64_t k, const int32
     a.n_out = n_out;
     a.y = y;
     a.acc_out = acc_out;
-    return from_hip(qg::launch_qgemm(a, as_stream(stream)));
+    e = qg::launch_qgemm(a, as_stream(stream));
+    if (e != hipSuccess || !dbg) return from_hip(e);
+    return debug_result(as_stream(stream));
 }
 
 size_t qg_probe_stream_read_bytes(int64_t bytes, int32_t workgroups) {

@@ -52,6 +52,9 @@ def test_header_symbols_exported(qg):
     assert qg.lib().qg_abi_version() == 20501
     for st in range(0, 8):
         assert qg.status_str(st)
+    # every status of the header has its own text
+    assert len({qg.status_str(st) for st in range(0, 8)}) == 8
+    assert qg.status_str(qg.QG_ERR_DEVICE_CHECK) != qg.status_str(99)
 
 
 A = 4096  # a 16-B aligned fake address: validation rejects before any use
