@@ -504,24 +504,29 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_wt_kernel(BGroup grp) {
     };
 
     // activations: phase p holds 8 units, one written by each wave (H = 1:
-    // units 8p .. 8p + 7; H = 2: units 4p .. 4p + 3 of each half); wave w
-    // requests its unit of every phase, then the ring's first D units of
-    // weights
+    // units 8p .. 8p + 7; H = 2: units 4p .. 4p + 3 of each half).  Wave w
+    // requests its unit of the first kXD phases, then the ring's first D
+    // units of weights; the unit of phase p + kXD is requested when phase p
+    // starts.  (Every phase requested up front -- 128 KB per CU at 16 tokens,
+    // from all CUs at once -- delayed the first phase to 4.8 us after the
+    // launch, per-wave timestamps on MI355X.)
     constexpr int kXU = (kBatchXlMaxLds / 2048 + kBWaves - 1) / kBWaves;  // phases (units per wave) at most
+    constexpr int kXD = 2;                                                // phases requested ahead
     auto phase_unit = [&](int q) -> int {  // C when past the last unit
         if constexpr (H == 1) return min(wave + kBWaves * q, C);
         const int u = 4 * q + (wave & 3);
         return u < CH ? (wave < 4 ? 0 : CH) + u : C;
     };
     u32x4 v0[kXU], v1[kXU];
-#pragma unroll
-    for (int q = 0; q < kXU; ++q) {
+    auto load_x = [&](int q) {  // unconditional: units past C read zeros
         const int c = phase_unit(q);
         const bool ok = c < C && i < M;
         const uint32_t xo = (uint32_t)((i * K + c * kBUnit + 16 * g) * 2);
         v0[q] = load16(rx, ok ? xo : oob_x);
         v1[q] = load16(rx, ok ? xo + 16u : oob_x);
-    }
+    };
+#pragma unroll
+    for (int q = 0; q < kXD; ++q) load_x(q);
     __builtin_amdgcn_sched_barrier(0);
     u32x4 ring[D];
 #pragma unroll
@@ -590,6 +595,7 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_wt_kernel(BGroup grp) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int p = 0; p < kXU; ++p) {
+            if (p + kXD < kXU) load_x(p + kXD);  // outside the branch below: no load under a branch
             if (kBWaves * p < C) {  // uniform: every wave passes the same barriers
                 const int c = phase_unit(p);
                 if (c < C) {
@@ -737,13 +743,14 @@ struct SkParams {
 };
 
 // MOST units of 64 k per wave, T tiles per workgroup: the wave's activation
-// fragments are requested first and kept in registers for all T tiles; the
-// tiles' weights follow two tiles ahead of the products, with no branches
-// between the loads and the products, so the waits count down through the
-// loads in order.  (Every tile requested up front measured 14.4 us for the
-// 4096 x 11008 product at 16 tokens, two tiles ahead 13.2 us, one 13.6 us:
-// with the whole share in flight no product starts before all of it has
-// arrived.)
+// fragments are requested with the first tile's weights, unit by unit, and
+// kept in registers for all T tiles; the other tiles' weights follow two
+// tiles ahead of the products, with no branches between the loads and the
+// products, so the waits count down through the loads in order.  (Every
+// tile requested up front measured 14.4 us for the 4096 x 11008 product at
+// 16 tokens, two tiles ahead 13.2 us, one 13.6 us: with the whole share in
+// flight no product starts before all of it has arrived; the activations
+// interleaved with the first tile: 13.0 us.)
 template <int YT, int MOST, int T, bool T16>
 __global__ __launch_bounds__(kBThreads) void qgemv_batch_splitk_kernel(SkParams p) {
     __shared__ f32x4 red[T][kBWaves][kWave];
@@ -781,21 +788,32 @@ __global__ __launch_bounds__(kBThreads) void qgemv_batch_splitk_kernel(SkParams 
             }
         }
     };
-    // the activation fragments of the wave's units, requested first (tokens
-    // >= m read zeros)
+    // the activation fragments of the wave's units (tokens >= m read zeros)
     u32x4 xa[MOST], xb[MOST];
+    {  // tile 0's weights interleaved with the activations, unit by unit, so
+       // that its first products wait for their own unit only
+        const int row0 = t0 * 16;
+        const int rows = 0 < nt ? min(16, p.n - row0) : 0;
+        const uint32_t tile_bytes = (uint32_t)((T16 && rows > 0 ? 16 : rows) * K);
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.wq + (int64_t)min(row0, p.n) * K, tile_bytes);
 #pragma unroll
-    for (int u = 0; u < MOST; ++u) {
-        const int c = c0 + u;
-        const bool ok = c < c1 && i < M;
-        const uint32_t xo = (uint32_t)((i * K + c * kBUnit + 16 * g) * 2);
-        xa[u] = load16(rx, ok ? xo : oob_x);
-        xb[u] = load16(rx, ok ? xo + 16u : oob_x);
+        for (int u = 0; u < MOST; ++u) {
+            const int c = c0 + u;
+            const bool ok = c < c1 && i < M;
+            const uint32_t xo = (uint32_t)((i * K + c * kBUnit + 16 * g) * 2);
+            xa[u] = load16(rx, ok ? xo : oob_x);
+            xb[u] = load16(rx, ok ? xo + 16u : oob_x);
+            if constexpr (T16) {  // whole 1 KB blocks, each read once: non-temporal
+                w[0][u] = load16_nt(rw, c < c1 ? (uint32_t)(c * 1024 + lane * 16) : tile_bytes);
+            } else {
+                w[0][u] = load16(rw, (c < c1 && i < rows) ? (uint32_t)(i * K + c * kBUnit + 16 * g) : tile_bytes);
+            }
+        }
     }
     // kSkDepth tiles in flight: tile t + kSkDepth - 1 is requested when
     // tile t's products begin
 #pragma unroll
-    for (int t = 0; t < (T < kSkDepth ? T : kSkDepth); ++t) issue_t(t);
+    for (int t = 1; t < (T < kSkDepth ? T : kSkDepth); ++t) issue_t(t);
     __builtin_amdgcn_sched_barrier(0);
     f32x4 acc[T];
 #pragma unroll
