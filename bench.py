@@ -359,8 +359,8 @@ def _segments(rows, order_json):
 def _rel(path):
     """A path under the repository, relative to its root (as printed in the
     profile summaries)."""
-    ap = os.path.abspath(path)
-    return os.path.relpath(ap, ROOT) if ap.startswith(ROOT + os.sep) else path
+    ap, root = os.path.realpath(path), os.path.realpath(ROOT)
+    return os.path.relpath(ap, root) if ap.startswith(root + os.sep) else path
 
 
 def _pass_counters(d):
@@ -453,6 +453,22 @@ def summarize_counters(order_json, dirs):
     print("\n".join(md[:6]))
 
 
+def config_sources(cfg):
+    """The kernel sources (keys of KERNEL_SOURCES) whose kernels a bench config
+    times: a recorded figure of that config holds while these are unchanged."""
+    if cfg.startswith("small_batch"):
+        return ("batch",)
+    if "sep_threshold" in cfg:
+        return ("sepq",)
+    if cfg.startswith("prefill_w8a8"):
+        return ("qgemm", "quantize")
+    if cfg.startswith("prefill_mxfp4"):
+        return ("mx",)
+    if cfg.startswith(("decode_", "tiny_", "ternary", "q4k_", "sign1_")):
+        return ("qgemv",)
+    return tuple(KERNEL_SOURCES)
+
+
 def recorded_traffic(cfg, key="qgemv_kernel"):
     """HBM bytes per dispatch of one config's kernels (those whose name holds
     `key`, averaged over their dispatches) from the recorded counters, or None
@@ -460,7 +476,7 @@ def recorded_traffic(cfg, key="qgemv_kernel"):
     try:
         with open(COUNTERS_FILE) as f:
             cnt = json.load(f)
-        if any(cnt["source_hashes"].get(k) != src_hash(k) for k in KERNEL_SOURCES):
+        if any(cnt["source_hashes"].get(k) != src_hash(k) for k in config_sources(cfg)):
             return None
         tot = n = 0
         for name, r in cnt["configs"][cfg].items():
@@ -556,7 +572,7 @@ def recorded_durations(cfg):
     try:
         with open(DURATIONS_FILE) as f:
             d = json.load(f)
-        if any(d["source_hashes"].get(k) != src_hash(k) for k in KERNEL_SOURCES):
+        if any(d["source_hashes"].get(k) != src_hash(k) for k in config_sources(cfg)):
             return None
         ks = d["configs"].get(cfg)
         return None if ks is None else {n: r for n, r in ks.items() if "qg::" in n}  # this library's kernels
