@@ -1141,8 +1141,8 @@ def build_format_step(torch, qg, synth, dev, L, fmt):
     same way, every layer its own weight copy) with the weights in a low-bit
     format: "ternary2" (2-bit ternary, int8 activations), "sign1_res8" (sign
     backbone + int8 residual, bf16 activations) or "sep_threshold"
-    (thresholded separated weights, 80th / 50th percentiles, one launch per
-    projection).  Returns (launches, weight bytes per step, objects to keep)."""
+    (thresholded separated weights, 80th / 50th percentiles, grouped with
+    qg_qgemv_sep_grouped).  Returns (launches, weight bytes per step, objects to keep)."""
     shapes = synth.DECODE_7B_SHAPES
     plan = ["attn_4096x4096"] * 4 + ["ffn_up_11008x4096"] * 2 + ["ffn_down_4096x11008"]
     groups_per_layer = [[0, 1, 2], [3], [4, 5], [6]]
@@ -1186,20 +1186,17 @@ def build_format_step(torch, qg, synth, dev, L, fmt):
         xs = {k: torch.randn(k, device=dev).to(torch.bfloat16) for k in (4096, 11008)}
     launches, keep = [], [weights, xs]
     for li in range(L):
-        if fmt == "sep_threshold":
-            for i in range(len(plan)):
-                W = weights[li * len(plan) + i]
-                y = torch.empty(W.n, dtype=torch.float32, device=dev)
-                keep.append(y)
-                launches.append((lambda W, y: (lambda: qg.qgemv_sep(W, xs[W.k], y=y)))(W, y))
-        else:
-            for grp in groups_per_layer:
-                ws_ = [weights[li * len(plan) + i] for i in grp]
+        for grp in groups_per_layer:
+            ws_ = [weights[li * len(plan) + i] for i in grp]
+            if fmt == "sep_threshold":
+                ys_ = [torch.empty(W.n, dtype=torch.float32, device=dev) for W in ws_]
+                gl = qg.SepGroupLaunch(ws_, xs[ws_[0].k], ys_)
+            else:
                 ydt = torch.float32 if fmt == "ternary2" else torch.bfloat16
                 ys_ = [torch.empty(W.n, dtype=ydt, device=dev) for W in ws_]
                 gl = qg.GroupLaunch(ws_, xs[ws_[0].k], ys_, act_int8=(fmt == "ternary2"))
-                keep.append(gl)
-                launches.append(gl.launch)
+            keep.append(gl)
+            launches.append(gl.launch)
     weights_per_step = L * sum(shapes[nm][0] * shapes[nm][1] for nm in plan)
     return launches, nbytes, keep, weights_per_step
 

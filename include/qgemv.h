@@ -604,6 +604,32 @@ qg_status qg_qgemv_sep(const uint8_t* cls, const int8_t* rv, int64_t rv_ld, cons
                        int32_t skip_residual, float* y, int32_t* acc_out, void* stream);
 
 /*
+ * qg_qgemv_sep for 1..QG_MAX_GROUP matrices that read the same x, in one
+ * launch ([SEP] section 3.3: the launch overhead of many small operators is
+ * one reason measured speed-ups fall short of the bandwidth model; the
+ * projections of a layer that share an input, such as q, k, v, are one
+ * launch).  Matrix m holds the arrays and outputs of one qg_qgemv_sep call,
+ * with the same meaning and limits; k, x, xt and skip_residual are shared.
+ * Each y (and acc_out) is exactly what qg_qgemv_sep gives for that matrix
+ * alone: every row is computed by the same code in the same order.
+ * Outputs must not overlap one another or x.  QG_ERR_ARG for count outside
+ * 1..QG_MAX_GROUP; the other errors as qg_qgemv_sep, for the first matrix
+ * that fails (nothing is launched then).
+ */
+typedef struct qg_sep_matrix {
+    const uint8_t* cls;   /* [n][k/4] classes                              */
+    const int8_t* rv;     /* [n][rv_ld] residual codes (unused when skipping) */
+    int64_t rv_ld;
+    const float* alpha;   /* [n]                                           */
+    const float* s_r;     /* [n] (unused when skipping)                    */
+    int64_t n;
+    float* y;             /* [n] fp32 (out)                                */
+    int32_t* acc_out;     /* [2][n] int32 (out) or NULL                    */
+} qg_sep_matrix;
+qg_status qg_qgemv_sep_grouped(const qg_sep_matrix* m, int32_t count, int64_t k, const void* x, int32_t xt,
+                               int32_t skip_residual, void* stream);
+
+/*
  * MXFP4 block-scaled 4-bit floats for the format-separated prefill ([DQ]:
  * "format separation" runs the prefill on the accelerator's native low-bit
  * compute -- NVFP4 on the hardware it measures -- while decode keeps a

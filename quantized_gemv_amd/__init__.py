@@ -9,7 +9,7 @@ libqgemv.so; this package only marshals arguments (see _binding.py).
 """
 from ._binding import (QgError, QWeight, CWeight, EXPORTED, LIB_PATH, lib, status_str,
                        quantize_absmax, quantize_absmax_split, detect_outliers, gather_columns_bf16, quantize_ternary,
-                       split_sign_residual, split_sign_residual_zp, quantize_asym, quantize_q4k, SepWeight, sep_resid_ld, quantize_mxfp4, gemm_mxfp4, prefill_mxfp4, split_sep_threshold, qgemv_sep, pack, unpack, base3_row_bytes, pack_base3, unpack_base3, pack_tiles16, tiled16, qgemv, qgemv_grouped, qgemv_batch, qgemv_batch_grouped, batch_workspace_bytes, GroupLaunch, qgemv_launch_raw,
+                       split_sign_residual, split_sign_residual_zp, quantize_asym, quantize_q4k, SepWeight, sep_resid_ld, quantize_mxfp4, gemm_mxfp4, prefill_mxfp4, split_sep_threshold, qgemv_sep, qgemv_sep_grouped, SepGroupLaunch, CSepMatrix, pack, unpack, base3_row_bytes, pack_base3, unpack_base3, pack_tiles16, tiled16, qgemv, qgemv_grouped, qgemv_batch, qgemv_batch_grouped, batch_workspace_bytes, GroupLaunch, qgemv_launch_raw,
                        ChainStep, CChainStage, chain_plan_image, QG_CHAIN_MAX_STAGES, QG_CHAIN_MIN_K, QG_CHAIN_MAX_K,
                        QG_CHAIN_ERROR_OFFSET, QG_CHAIN_TIMEOUT_TICKS,
                        qgemm_w8a8_outlier, qgemm_w8a8, out_ld, QG_MAX_GROUP, QG_OUT_LD_ALIGN, QG_MAX_OUT_LD,

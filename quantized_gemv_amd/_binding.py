@@ -56,6 +56,11 @@ class CWeight(ctypes.Structure):
                 ("codes", _c_vp), ("resid", _c_vp), ("scale", _c_vp), ("scale2", _c_vp), ("zero", _c_vp)]
 
 
+class CSepMatrix(ctypes.Structure):
+    _fields_ = [("cls", _c_vp), ("rv", _c_vp), ("rv_ld", _c_i64), ("alpha", _c_vp), ("s_r", _c_vp), ("n", _c_i64),
+                ("y", _c_vp), ("acc_out", _c_vp)]
+
+
 class CChainStage(ctypes.Structure):
     _fields_ = [("count", _c_i32), ("dep", _c_i32), ("x", _c_vp), ("w", ctypes.POINTER(CWeight)),
                 ("y", ctypes.POINTER(_c_vp))]
@@ -97,6 +102,7 @@ _SIGS = {
                                         _c_vp]),
     "qg_qgemv_sep": (_c_i32, [_c_vp, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_i32, _c_vp,
                               _c_vp, _c_vp]),
+    "qg_qgemv_sep_grouped": (_c_i32, [ctypes.POINTER(CSepMatrix), _c_i32, _c_i64, _c_vp, _c_i32, _c_i32, _c_vp]),
     "qg_pack": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i32, _c_vp, _c_vp]),
     "qg_base3_row_bytes": (_c_i64, [_c_i64]),
     "qg_pack_base3": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp]),
@@ -527,6 +533,45 @@ def qgemv_sep(sw: SepWeight, x: torch.Tensor, skip_residual: bool = False, y: to
     _check(lib().qg_qgemv_sep(_p(sw.cls), _p(sw.rv), sw.ld, _p(sw.alpha), _p(sw.s_r), sw.n, sw.k, _p(x), _xt(x),
                               1 if skip_residual else 0, _p(y), _p(acc_out), _stream(x)), "qg_qgemv_sep")
     return y
+
+
+class SepGroupLaunch:
+    """Pre-marshalled arguments of one qg_qgemv_sep_grouped call: products of
+    1..QG_MAX_GROUP thresholded separated matrices on the same x (kept alive
+    by this object); launch() enqueues it on x's current stream."""
+
+    def __init__(self, weights: Sequence[SepWeight], x: torch.Tensor, ys: Sequence[torch.Tensor],
+                 skip_residual: bool = False, accs: Optional[Sequence[torch.Tensor]] = None):
+        _dev(x, "x", (torch.float32, torch.bfloat16))
+        n = len(weights)
+        if not 1 <= n <= QG_MAX_GROUP or len(ys) != n or (accs is not None and len(accs) != n):
+            raise ValueError("need 1..%d weights and as many outputs" % QG_MAX_GROUP)
+        for y in ys:
+            _dev(y, "y", torch.float32)
+        if accs is not None:
+            for a in accs:
+                if a is not None:
+                    _dev(a, "acc_out", torch.int32)
+        self.keep = (list(weights), x, list(ys), accs)
+        self.m = (CSepMatrix * n)(*[
+            CSepMatrix(_p(w.cls), _p(w.rv), w.ld, _p(w.alpha), _p(w.s_r), w.n, _p(y),
+                       None if accs is None or accs[i] is None else _p(accs[i]))
+            for i, (w, y) in enumerate(zip(weights, ys))])
+        self.n, self.k, self.x, self.xt = n, weights[0].k, x, _xt(x)
+        self.skip = 1 if skip_residual else 0
+
+    def launch(self):
+        _check(lib().qg_qgemv_sep_grouped(self.m, self.n, self.k, _p(self.x), self.xt, self.skip, _stream(self.x)),
+               "qg_qgemv_sep_grouped")
+
+
+def qgemv_sep_grouped(weights: Sequence[SepWeight], x: torch.Tensor, skip_residual: bool = False,
+                      accs: Optional[Sequence[torch.Tensor]] = None):
+    """Thresholded separated products on the same x in one launch
+    (qg_qgemv_sep_grouped). Returns [y] (fp32)."""
+    ys = [torch.empty(w.n, dtype=torch.float32, device=x.device) for w in weights]
+    SepGroupLaunch(weights, x, ys, skip_residual, accs).launch()
+    return ys
 
 
 def qgemv(w: QWeight, x: torch.Tensor, act_int8: bool, y_dtype=torch.float32, y: torch.Tensor = None,

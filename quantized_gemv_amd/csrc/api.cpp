@@ -108,7 +108,7 @@ const char* qg_status_str(qg_status s) {
     }
 }
 
-int32_t qg_abi_version(void) { return 20501; }
+int32_t qg_abi_version(void) { return 20600; }
 
 size_t qg_quantize_absmax_workspace_bytes(int64_t rows, int64_t cols, int32_t gran) {
     if (gran != QG_PER_TENSOR || rows < 1 || cols < 8) return 0;
@@ -234,31 +234,46 @@ qg_status qg_split_sep_threshold(const float* w, int64_t n, int64_t k, int32_t p
                                          cls, rv, rv_ld, alpha, s_r, as_stream(stream)));
 }
 
+static qg_status sep_args(const qg_sep_matrix& m, int64_t k, const void* x, int32_t xt, bool skip, qg::SepArgs* a) {
+    if (!m.cls || !m.alpha || !x || !m.y || (!skip && (!m.rv || !m.s_r))) return QG_ERR_NULLPTR;
+    const qg_status sh = check_sep_shape(m.n, k);
+    if (sh != QG_OK) return sh;
+    if (m.n >= ((int64_t)1 << 31)) return QG_ERR_SHAPE;
+    if (xt != QG_F32 && xt != QG_BF16) return QG_ERR_ARG;
+    if (!skip && (m.rv_ld < 16 || m.rv_ld > k || m.rv_ld % 16 != 0)) return QG_ERR_SHAPE;
+    if (!aligned16(m.cls) || !aligned16(x) || (!skip && !aligned16(m.rv))) return QG_ERR_ALIGN;
+    a->cls = m.cls;
+    a->rv = skip ? nullptr : m.rv;
+    a->ld = skip ? 16 : m.rv_ld;
+    a->alpha = m.alpha;
+    a->s_r = m.s_r;
+    a->n = m.n;
+    a->k = k;
+    a->x = x;
+    a->xt = xt;
+    a->skip = skip;
+    a->y = m.y;
+    a->acc_out = m.acc_out;
+    return QG_OK;
+}
+
 qg_status qg_qgemv_sep(const uint8_t* cls, const int8_t* rv, int64_t rv_ld, const float* alpha, const float* s_r,
                        int64_t n, int64_t k, const void* x, int32_t xt, int32_t skip_residual, float* y,
                        int32_t* acc_out, void* stream) {
-    const bool skip = skip_residual != 0;
-    if (!cls || !alpha || !x || !y || (!skip && (!rv || !s_r))) return QG_ERR_NULLPTR;
-    const qg_status sh = check_sep_shape(n, k);
-    if (sh != QG_OK) return sh;
-    if (n >= ((int64_t)1 << 31)) return QG_ERR_SHAPE;
-    if (xt != QG_F32 && xt != QG_BF16) return QG_ERR_ARG;
-    if (!skip && (rv_ld < 16 || rv_ld > k || rv_ld % 16 != 0)) return QG_ERR_SHAPE;
-    if (!aligned16(cls) || !aligned16(x) || (!skip && !aligned16(rv))) return QG_ERR_ALIGN;
-    qg::SepArgs a;
-    a.cls = cls;
-    a.rv = skip ? nullptr : rv;
-    a.ld = skip ? 16 : rv_ld;
-    a.alpha = alpha;
-    a.s_r = s_r;
-    a.n = n;
-    a.k = k;
-    a.x = x;
-    a.xt = xt;
-    a.skip = skip;
-    a.y = y;
-    a.acc_out = acc_out;
-    return from_hip(qg::launch_sep_qgemv(a, as_stream(stream)));
+    const qg_sep_matrix m{cls, rv, rv_ld, alpha, s_r, n, y, acc_out};
+    return qg_qgemv_sep_grouped(&m, 1, k, x, xt, skip_residual, stream);
+}
+
+qg_status qg_qgemv_sep_grouped(const qg_sep_matrix* m, int32_t count, int64_t k, const void* x, int32_t xt,
+                               int32_t skip_residual, void* stream) {
+    if (!m) return QG_ERR_NULLPTR;
+    if (count < 1 || count > QG_MAX_GROUP) return QG_ERR_ARG;
+    qg::SepArgs a[QG_MAX_GROUP];
+    for (int32_t i = 0; i < count; ++i) {
+        const qg_status st = sep_args(m[i], k, x, xt, skip_residual != 0, &a[i]);
+        if (st != QG_OK) return st;
+    }
+    return from_hip(qg::launch_sep_qgemv_group(a, count, as_stream(stream)));
 }
 
 size_t qg_ternary_workspace_bytes(int64_t n, int64_t k) {

@@ -104,6 +104,8 @@ struct SepArgs {
     int32_t* acc_out;
 };
 hipError_t launch_sep_qgemv(const SepArgs& a, hipStream_t st);
+// 1..kMaxGroupLaunch matrices sharing x, k, xt and skip in one launch
+hipError_t launch_sep_qgemv_group(const SepArgs* a, int count, hipStream_t st);
 
 // Weight-only int8 products for a batch of m tokens (x bf16 [m][k]); the
 // entries of one launch share k, m, x and yt.

@@ -274,8 +274,17 @@ __device__ __forceinline__ void transpose4x4(const u32x4& a, uint32_t t[4]) {
 // next item (its start: the running residual count; its length: the scan of
 // its classes) is known when it is requested, and only the 16-byte blocks it
 // covers are read.
-template <int XT, int U, bool SKIP, bool XPL>
-__global__ __launch_bounds__(kSepThreads) void sep_qgemv_kernel(SepParams p) {
+// The matrices of one launch (1, 3 or 8 slots, the fewest that fit): they
+// share x and K; matrix blockIdx.y takes workgroups blockIdx.x = 0, 1, ...
+// of rows_per_wg rows each, and workgroups past its rows exit at once.
+template <int MG>
+struct SepGroup {
+    SepParams mats[MG];
+};
+
+template <int XT, int U, bool SKIP, bool XPL, int MG>
+__global__ __launch_bounds__(kSepThreads) void sep_qgemv_kernel(SepGroup<MG> grp) {
+    const SepParams& p = grp.mats[blockIdx.y];
     // The kernel's only LDS is this dynamic block (so it starts at address 0
     // and byte offsets are addresses): 256 selectors | reduction scratch |
     // int8 x (zero-padded to Kp) | with XPL the same x 4x4-byte-transposed |
@@ -301,6 +310,7 @@ __global__ __launch_bounds__(kSepThreads) void sep_qgemv_kernel(SepParams p) {
     };
 
     const int row0 = (int)blockIdx.x * p.rows_per_wg;
+    if (row0 >= p.n) return;  // a smaller matrix of the group needs fewer workgroups (before any barrier)
     const int rows = min(p.rows_per_wg, p.n - row0);
     const int rowC = K / 4;  // class bytes per row
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.cls + (int64_t)row0 * rowC, (uint32_t)(rows * rowC));
@@ -633,34 +643,42 @@ __global__ __launch_bounds__(kSepThreads) void sep_qgemv_kernel(SepParams p) {
     asm volatile("" ::"v"(inflight));
 }
 
-template <int XT, int U, bool SKIP, bool XPL>
-static hipError_t run_sep(const SepArgs& a, hipStream_t st) {
-    const int K = (int)a.k;
+template <int XT, int U, bool SKIP, bool XPL, int MG>
+static hipError_t run_sep(const SepArgs* a, int count, hipStream_t st) {
+    const int K = (int)a[0].k;
     const int nsteps = (K + kSepStep - 1) / kSepStep;
     const size_t lds = kSepLdsHead + (size_t)nsteps * kSepStep * (XPL ? 2 : 1) + (SKIP ? 0 : (size_t)kSepWaves * U * kSepStage);
     const int cus = device_cu_count();
-    const int64_t N = a.n;
+    int64_t total = 0, ld_max = K / 4;
+    for (int i = 0; i < count; ++i) {
+        total += a[i].n;
+        if (a[i].ld > ld_max) ld_max = a[i].ld;
+    }
     const int64_t quantum = (int64_t)kSepWaves * U;
-    int64_t rpw = (N + 2 * cus - 1) / (2 * cus);  // about two workgroups per CU
+    int64_t rpw = (total + 2 * cus - 1) / (2 * cus);  // about two workgroups per CU over the whole launch
     rpw = (rpw + quantum - 1) / quantum * quantum;
     // buffer ranges stay below 2 GiB
-    const int64_t per_row = a.ld > K / 4 ? a.ld : K / 4;
-    const int64_t cap = (((int64_t)1 << 31) / per_row) / quantum * quantum;
+    const int64_t cap = (((int64_t)1 << 31) / ld_max) / quantum * quantum;
     if (rpw > cap) rpw = cap > quantum ? cap : quantum;
-    SepParams p;
-    p.cls = a.cls;
-    p.rv = a.rv;
-    p.alpha = a.alpha;
-    p.s_r = a.s_r;
-    p.x = a.x;
-    p.y = a.y;
-    p.acc_out = a.acc_out;
-    p.ld = a.ld;
-    p.n = (int32_t)N;
-    p.k = K;
-    p.rows_per_wg = (int32_t)rpw;
-    const int grid = (int)((N + rpw - 1) / rpw);
-    auto kern = sep_qgemv_kernel<XT, U, SKIP, XPL>;
+    SepGroup<MG> g;
+    int64_t gx = 1;
+    for (int i = 0; i < count; ++i) {
+        SepParams& p = g.mats[i];
+        p.cls = a[i].cls;
+        p.rv = a[i].rv;
+        p.alpha = a[i].alpha;
+        p.s_r = a[i].s_r;
+        p.x = a[i].x;
+        p.y = a[i].y;
+        p.acc_out = a[i].acc_out;
+        p.ld = a[i].ld;
+        p.n = (int32_t)a[i].n;
+        p.k = K;
+        p.rows_per_wg = (int32_t)rpw;
+        const int64_t wgs = (a[i].n + rpw - 1) / rpw;
+        if (wgs > gx) gx = wgs;
+    }
+    auto kern = sep_qgemv_kernel<XT, U, SKIP, XPL, MG>;
     if (lds > 64 * 1024) {
         static bool attr_set = false;  // per instantiation
         if (!attr_set) {
@@ -670,21 +688,32 @@ static hipError_t run_sep(const SepArgs& a, hipStream_t st) {
             attr_set = true;
         }
     }
-    kern<<<grid, kSepThreads, lds, st>>>(p);
+    kern<<<dim3((unsigned)gx, (unsigned)count), kSepThreads, lds, st>>>(g);
     return hipGetLastError();
 }
 
-hipError_t launch_sep_qgemv(const SepArgs& a, hipStream_t st) {
+template <int XT, int U, bool SKIP, bool XPL>
+static hipError_t run_sep_mg(const SepArgs* a, int count, hipStream_t st) {
+    if (count == 1) return run_sep<XT, U, SKIP, XPL, 1>(a, count, st);
+    if (count <= 3) return run_sep<XT, U, SKIP, XPL, 3>(a, count, st);
+    return run_sep<XT, U, SKIP, XPL, kMaxGroupLaunch>(a, count, st);
+}
+
+hipError_t launch_sep_qgemv_group(const SepArgs* a, int count, hipStream_t st) {
+    if (count < 1 || count > kMaxGroupLaunch) return hipErrorInvalidValue;
     // One row per item: at two rows the slices' LDS leaves room for only one
     // workgroup per CU, which measured slower on MI355X; the skip path has no
     // slices and takes two.  The transposed copy of x stays in LDS while
     // K <= 32768 (else it is formed in registers).
-    if (a.k <= 32768) {
-        if (a.xt == 0) return a.skip ? run_sep<0, 2, true, true>(a, st) : run_sep<0, 1, false, true>(a, st);
-        return a.skip ? run_sep<1, 2, true, true>(a, st) : run_sep<1, 1, false, true>(a, st);
+    const bool skip = a[0].skip;
+    if (a[0].k <= 32768) {
+        if (a[0].xt == 0) return skip ? run_sep_mg<0, 2, true, true>(a, count, st) : run_sep_mg<0, 1, false, true>(a, count, st);
+        return skip ? run_sep_mg<1, 2, true, true>(a, count, st) : run_sep_mg<1, 1, false, true>(a, count, st);
     }
-    if (a.xt == 0) return a.skip ? run_sep<0, 2, true, false>(a, st) : run_sep<0, 1, false, false>(a, st);
-    return a.skip ? run_sep<1, 2, true, false>(a, st) : run_sep<1, 1, false, false>(a, st);
+    if (a[0].xt == 0) return skip ? run_sep_mg<0, 2, true, false>(a, count, st) : run_sep_mg<0, 1, false, false>(a, count, st);
+    return skip ? run_sep_mg<1, 2, true, false>(a, count, st) : run_sep_mg<1, 1, false, false>(a, count, st);
 }
+
+hipError_t launch_sep_qgemv(const SepArgs& a, hipStream_t st) { return launch_sep_qgemv_group(&a, 1, st); }
 
 }  // namespace qg

@@ -49,7 +49,7 @@ def test_header_symbols_exported(qg):
     for name in decl:
         assert hasattr(l, name), name
     assert set(decl) == set(qg.EXPORTED)
-    assert qg.lib().qg_abi_version() == 20501
+    assert qg.lib().qg_abi_version() == 20600
     for st in range(0, 8):
         assert qg.status_str(st)
     # every status of the header has its own text
@@ -448,6 +448,24 @@ def test_validation_sep_threshold(qg):
     assert g(U, A, ld, A, A, 4, 1024, A, 0, 0, A, None, None) == 3
     assert g(A, U, ld, A, A, 4, 1024, A, 0, 0, A, None, None) == 3
     assert g(A, A, ld, A, A, 4, 1024, U, 1, 0, A, None, None) == 3
+    h = l.qg_qgemv_sep_grouped
+
+    def M(cls=A, rv=A, rv_ld=ld, n=4, y=A):
+        return qg.CSepMatrix(cls, rv, rv_ld, A, A, n, y, None)
+
+    def grp(*ms):
+        return (qg.CSepMatrix * len(ms))(*ms)
+    # (m, count, k, x, xt, skip, stream)
+    assert h(None, 1, 1024, A, 0, 0, None) == 1
+    assert h(grp(M()), 0, 1024, A, 0, 0, None) == 4                 # count below 1
+    assert h(grp(*[M()] * 9), 9, 1024, A, 0, 0, None) == 4          # count above QG_MAX_GROUP
+    assert h(grp(M(), M(y=None)), 2, 1024, A, 0, 0, None) == 1      # a later matrix fails: nothing launched
+    assert h(grp(M(), M(n=0)), 2, 1024, A, 0, 0, None) == 2
+    assert h(grp(M(), M(rv_ld=8)), 2, 1024, A, 0, 0, None) == 2
+    assert h(grp(M(), M(cls=U)), 2, 1024, A, 0, 0, None) == 3
+    assert h(grp(M(), M()), 2, 1000, A, 0, 0, None) == 2            # shared k not a multiple of 128
+    assert h(grp(M(), M()), 2, 1024, U, 1, 0, None) == 3            # shared x misaligned
+    assert h(grp(M(), M()), 2, 1024, A, 2, 0, None) == 4            # x dtype
 
 
 @needs_no_gpu

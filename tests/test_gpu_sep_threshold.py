@@ -156,3 +156,55 @@ def test_qgemv_sep_full(qg):
     y_ref = th.y_threshold(acc_b, acc_r, a, sr, s_x)
     assert oracle.normwise_error(host(y), y_ref) <= TOL_F32
     assert canaries_intact(y_full, n) and canaries_intact(acc_full, 2 * n)
+
+
+# Several matrices on the same x in one launch (qg_qgemv_sep_grouped): every
+# row is computed by the kernel code of a single launch, so each matrix's y
+# and int32 sums must equal its own qg_qgemv_sep call bit for bit, and the
+# oracle's ([SEP] section 3.3: projections sharing an input in one launch).
+@pytest.mark.parametrize("ns,k,x_bf16,skip", [
+    ((300, 64, 1000), 1152, False, False),
+    ((4096, 4096, 4096), 4096, True, False),     # q, k, v shapes: row groups from the LDS counter
+    ((1, 17, 33, 200, 5, 64, 9, 130), 1024, True, True),
+    ((8, 3), 65536, False, False),               # x transposed in registers (K > 32768)
+])
+def test_qgemv_sep_grouped(qg, ns, k, x_bf16, skip):
+    note("qgemv thresholded grouped %s k=%d bf16=%s skip=%s" % (ns, k, x_bf16, skip))
+    g = synth.rng(4242 + k)
+    x = synth.gaussian(g, (k,), 1.0)
+    if x_bf16:
+        xb = synth.to_bf16_bits(x)
+        x = synth.bf16_bits_to_f32(xb)
+        xd = dev_bf16(xb)
+    else:
+        xd = dev(x)
+    xq, s_x = oracle.quantize_absmax(x, per_row=False)
+    ld = max(th.resid_ld(k, 50), 16)
+    ws, refs, ys, accs, guards = [], [], [], [], []
+    for i, n in enumerate(ns):
+        w = _weights(n, k, 77 * i + n, special=(i == 0))
+        f, a, rq, sr = th.threshold_split(w, 80, 50)
+        plane, stream = th.pack_threshold(f, rq, ld)
+        ws.append(qg.SepWeight(dev(plane), dev(stream), dev(a), dev(sr), k))
+        refs.append((f, a, rq, sr))
+        y_full, y = guarded(n, torch.float32)
+        acc_full, acc = guarded(2 * n, torch.int32)
+        ys.append(y)
+        accs.append(acc)
+        guards.append((y_full, acc_full))
+    qg.SepGroupLaunch(ws, xd, ys, skip_residual=skip, accs=accs).launch()
+    for i, n in enumerate(ns):
+        f, a, rq, sr = refs[i]
+        acc_b, acc_r = th.int_products(f, rq, xq)
+        acc_h = host(accs[i])
+        assert np.array_equal(acc_h[:n], acc_b), "matrix %d" % i
+        assert np.array_equal(acc_h[n:], np.zeros(n, np.int64) if skip else acc_r), "matrix %d" % i
+        y_ref = th.y_threshold(acc_b, acc_r, a, sr, s_x, skip_residual=skip)
+        assert oracle.normwise_error(host(ys[i]), y_ref) <= TOL_F32, "matrix %d" % i
+        assert canaries_intact(guards[i][0], n) and canaries_intact(guards[i][1], 2 * n), "matrix %d" % i
+        # the same matrix alone
+        y1 = torch.empty(n, dtype=torch.float32, device="cuda")
+        a1 = torch.empty(2 * n, dtype=torch.int32, device="cuda")
+        qg.qgemv_sep(ws[i], xd, skip_residual=skip, y=y1, acc_out=a1)
+        assert np.array_equal(host(y1).view(np.uint32), host(ys[i]).view(np.uint32)), "matrix %d" % i
+        assert np.array_equal(host(a1), acc_h), "matrix %d" % i
