@@ -132,13 +132,12 @@ def test_qgemv_batch_grouped_qkv_16_tokens(qg):
         Ws.append(W)
         refs.append(w)
     ys = qg.qgemv_batch_grouped(Ws, xd, y_dtype=torch.float32)
-    rows = np.unique(np.concatenate([[0, 1, 4095], synth.rng(93).choice(4096, 61, replace=False)]))
     for W, y, w in zip(Ws, ys, refs):
         y1 = qg.qgemv_batch(W, xd, y_dtype=torch.float32)
         assert np.array_equal(host(y), host(y1))
-        q_ref, s_ref = oracle.quantize_absmax(np.ascontiguousarray(w[rows]), per_row=True)
+        q_ref, s_ref = oracle.quantize_absmax(w, per_row=True)  # every row
         y_ref = oracle.y_w8a16_batch(q_ref, s_ref, xb)
-        assert oracle.normwise_error(host(y)[:, rows], y_ref) <= TOL_F32
+        assert oracle.normwise_error(host(y), y_ref) <= TOL_F32
 
 
 def _workspace(qg, n, k, m):

@@ -190,8 +190,8 @@ def test_gemm_mxfp4(qg, m, k, n):
 
 def test_prefill_mxfp4_full_shape(qg):
     # the prefill workload: X 2048x4096 bf16 with 20 channels x50, W 4096x4096;
-    # rows of Y sampled for the fp64 reference
-    note("mxfp4 prefill 2048x4096x4096 (sampled rows)")
+    # every row of Y against the fp64 reference
+    note("mxfp4 prefill 2048x4096x4096 (every row)")
     wl = synth.prefill_outlier()
     xb, w = wl.tensors["x_bf16"], wl.tensors["w"]
     m, k = xb.shape
@@ -201,7 +201,6 @@ def test_prefill_mxfp4_full_shape(qg):
     pw, sw = mx.pack_mxfp4(cw, ew)
     assert np.array_equal(host(wc), pw) and np.array_equal(host(ws), sw)
     y = qg.prefill_mxfp4(dev_bf16(xb), wc, ws)
-    rows = np.unique(np.concatenate([[0, 1, m - 1], synth.rng(9).choice(m, 45, replace=False)]))
-    cx, ex = mx.quantize_mxfp4(synth.bf16_bits_to_f32(xb[rows]))
+    cx, ex = mx.quantize_mxfp4(synth.bf16_bits_to_f32(xb))
     y_ref = mx.gemm_mxfp4(cx, ex, cw, ew)
-    assert oracle.normwise_error(host(y)[rows], y_ref) <= TOL_F32
+    assert oracle.normwise_error(host(y), y_ref) <= TOL_F32  # a max-norm: one wrong row fails it

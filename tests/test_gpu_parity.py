@@ -6,8 +6,8 @@ accumulators; float outputs within the normwise tolerances of gpu_util
 oracle's fp64 reference computed from the oracle's own codes.
 
 Sizes: small shapes spanning several workgroups with ragged tails, the five
-workloads at full size (sampled rows where the oracle is too slow for every
-row), and edge cases (minimum / maximum K, single rows, zero inputs).
+workloads at full size with every row checked, and edge cases (minimum /
+maximum K, single rows, zero inputs).
 """
 import sys
 
