@@ -1,0 +1,192 @@
+"""GPU parity on seeded random shapes, every format of the product.
+
+The other GPU tests pin chosen shapes (tile and segment boundaries, the
+workload sizes).  Here each format runs on shapes drawn from a fixed seed:
+n log-uniform in [1, 20000], k a log-uniform multiple of the format's K
+quantum up to its maximum, so that row counts that are not multiples of any
+workgroup share meet K that is not a multiple of any item size.  Every case
+keeps the full bar of the shape-specific tests (it calls the same case
+functions): codes, scales and int32 sums bit-exact against the oracle, fp32
+outputs within 1e-5 normwise, bf16 outputs the RNE of the fp32 result, and
+canaries around every output intact.  The drawn shapes are in the test ids.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import TOL_F32, canaries_intact, check_bf16_output, dev, dev_bf16, guarded, host
+from test_gpu_base3 import _tern3_case
+from test_gpu_parity import _int8_weight, _sr_case, _ternary_case
+from test_gpu_sep_threshold import _product_case
+from test_gpu_zero_point import _zp_case
+
+pytestmark = pytest.mark.gpu
+
+_RNG = np.random.default_rng(20261204)
+
+
+def note(msg):
+    print("[case] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+def _draw(count, quantum=128, kmax=32768, max_elems=12_000_000, nmax=20000):
+    """count (n, k) pairs: n and k / quantum log-uniform, n * k capped so
+    that the oracle stays within seconds."""
+    out = []
+    while len(out) < count:
+        n = int(np.exp(_RNG.uniform(0.0, np.log(nmax))))
+        k = quantum * max(1, int(np.exp(_RNG.uniform(0.0, np.log(kmax // quantum)))))
+        if n * k <= max_elems:
+            out.append((n, k))
+    return out
+
+
+W8A8_SHAPES = _draw(16)
+W8A16_SHAPES = _draw(16)
+TERNARY_SHAPES = _draw(16)
+BASE3_SHAPES = _draw(12)
+SR_SHAPES = _draw(12, max_elems=6_000_000)
+ZP_SHAPES = _draw(10, max_elems=6_000_000)
+Q4_SHAPES = _draw(12, quantum=256)
+SEP_SHAPES = [(n, k, int(_RNG.integers(50, 101))) for n, k in _draw(10, kmax=65536, max_elems=6_000_000)]
+BATCH_SHAPES = [(n, k, int(_RNG.integers(1, 17))) for n, k in _draw(16, kmax=65536, max_elems=12_000_000)]
+GROUP_SHAPES = [(tuple(int(np.exp(_RNG.uniform(0.0, np.log(6000)))) for _ in range(int(_RNG.integers(2, 9)))),
+                 128 * int(_RNG.integers(1, 65))) for _ in range(6)]
+
+
+@pytest.fixture(scope="module")
+def qg():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import quantized_gemv_amd as q
+    q.lib()  # fails loudly if the HIP library is not built
+    return q
+
+
+@pytest.mark.parametrize("n,k", W8A8_SHAPES)
+def test_random_w8a8(qg, n, k):
+    note("random w8a8 %dx%d" % (n, k))
+    wl = synth.tiny_gemv(n=n, k=k, seed=n + k)
+    w, x = wl.tensors["w"], wl.tensors["x"]
+    W, wq, s_w = _int8_weight(qg, w)
+    wq_ref, sw_ref = oracle.quantize_absmax(w, per_row=True)
+    assert np.array_equal(host(wq), wq_ref) and np.array_equal(host(s_w), sw_ref)
+    xq_ref, sx_ref = oracle.quantize_absmax(x, per_row=False)
+    acc_ref = oracle.int_dot_exact(wq_ref, xq_ref)
+    acc_full, acc = guarded(n, torch.int32)
+    y_full, y = guarded(n, torch.float32)
+    qg.qgemv(W, dev(x), act_int8=True, y=y, acc_out=acc)
+    assert np.array_equal(host(acc), acc_ref.astype(np.int32))
+    assert oracle.normwise_error(host(y), oracle.y_w8a8(acc_ref, sw_ref, sx_ref)) <= TOL_F32
+    assert canaries_intact(acc_full, n) and canaries_intact(y_full, n)
+
+
+@pytest.mark.parametrize("n,k", W8A16_SHAPES)
+def test_random_w8a16(qg, n, k):
+    note("random w8a16 %dx%d" % (n, k))
+    wl = synth.decode_w8a16(n=n, k=k, seed=n + 2 * k)
+    w, xb = wl.tensors["w"], wl.tensors["x_bf16"]
+    W, wq, s_w = _int8_weight(qg, w)
+    wq_ref, sw_ref = oracle.quantize_absmax(w, per_row=True)
+    assert np.array_equal(host(wq), wq_ref) and np.array_equal(host(s_w), sw_ref)
+    y_ref = oracle.y_w8a16(wq_ref, sw_ref, xb)
+    y_full, y = guarded(n, torch.float32)
+    qg.qgemv(W, dev_bf16(xb), act_int8=False, y=y)
+    yb_full, yb = guarded(n, torch.bfloat16)
+    qg.qgemv(W, dev_bf16(xb), act_int8=False, y=yb)
+    assert oracle.normwise_error(host(y), y_ref) <= TOL_F32
+    check_bf16_output(host(yb), host(y), y_ref)
+    assert canaries_intact(y_full, n) and canaries_intact(yb_full, n)
+
+
+@pytest.mark.parametrize("n,k", TERNARY_SHAPES)
+def test_random_ternary(qg, n, k):
+    note("random ternary %dx%d" % (n, k))
+    _ternary_case(qg, n, k, seed=n + 3 * k)
+
+
+@pytest.mark.parametrize("n,k", BASE3_SHAPES)
+def test_random_ternary_base3(qg, n, k):
+    note("random ternary base-3 %dx%d" % (n, k))
+    _tern3_case(qg, n, k, seed=n + 5 * k)
+
+
+@pytest.mark.parametrize("n,k", SR_SHAPES)
+def test_random_sign_residual(qg, n, k):
+    note("random sign + residual %dx%d" % (n, k))
+    _sr_case(qg, n, k, seed=n + 7 * k)
+
+
+@pytest.mark.parametrize("n,k", ZP_SHAPES)
+def test_random_sign_residual_zp(qg, n, k):
+    note("random sign + zero-point residual %dx%d" % (n, k))
+    _zp_case(qg, n, k, seed=n + 11 * k)
+
+
+@pytest.mark.parametrize("n,k", Q4_SHAPES)
+def test_random_q4k(qg, n, k):
+    note("random q4k %dx%d" % (n, k))
+    import oracle.q4 as oq4
+    g = synth.rng(n + 13 * k)
+    w = synth.gaussian(g, (n, k), 0.02)
+    xb = synth.to_bf16_bits(synth.gaussian(g, (k,), 1.0))
+    codes, meta = qg.quantize_q4k(dev(w))
+    parts = oq4.quantize_q4k(w)
+    plane_ref, meta_ref = oq4.pack_q4k(*parts)
+    assert np.array_equal(host(codes), plane_ref) and np.array_equal(host(meta), meta_ref)
+    W = qg.QWeight(qg.QG_WFMT_Q4K, n, k, codes, None, resid=meta)
+    y_full, y = guarded(n, torch.float32)
+    qg.qgemv(W, dev_bf16(xb), act_int8=False, y=y)
+    assert oracle.normwise_error(host(y), oq4.y_q4k(*parts, xb)) <= TOL_F32
+    assert canaries_intact(y_full, n)
+
+
+@pytest.mark.parametrize("n,k,pb", SEP_SHAPES)
+def test_random_sep_threshold(qg, n, k, pb):
+    pz = pb // 2
+    note("random thresholded %dx%d pb=%d pz=%d" % (n, k, pb, pz))
+    _product_case(qg, n, k, pb, pz, x_bf16=bool((n + k) & 1), seed=n + 17 * k)
+
+
+@pytest.mark.parametrize("n,k,m", BATCH_SHAPES)
+def test_random_batch(qg, n, k, m):
+    note("random batch %dx%d m=%d" % (n, k, m))
+    g = synth.rng(n + 19 * k + m)
+    w = synth.gaussian(g, (n, k), 0.02)
+    xb = synth.to_bf16_bits(synth.gaussian(g, (m, k), 1.0))
+    W, wq, s_w = _int8_weight(qg, w)
+    q_ref, s_ref = oracle.quantize_absmax(w, per_row=True)
+    y_ref = oracle.y_w8a16_batch(q_ref, s_ref, xb)
+    for layout in ("row-major", "tiled"):
+        Wl = W if layout == "row-major" else qg.tiled16(W)
+        full = torch.empty(m * n + 128, dtype=torch.float32, device="cuda")
+        full.view(torch.uint8).fill_(0x5A)
+        y = full[64:64 + m * n].view(m, n)
+        qg.qgemv_batch(Wl, dev_bf16(xb), y=y)
+        assert oracle.normwise_error(host(y), y_ref) <= TOL_F32, layout
+        assert canaries_intact(full, m * n), layout
+
+
+@pytest.mark.parametrize("ns,k", GROUP_SHAPES)
+def test_random_grouped_w8a16(qg, ns, k):
+    # a grouped launch of 2..8 matrices of random heights equals its single
+    # launches bit for bit, and each matrix the oracle
+    note("random grouped w8a16 %s k=%d" % (ns, k))
+    g = synth.rng(sum(ns) + k)
+    xb = synth.to_bf16_bits(synth.gaussian(g, (k,), 1.0))
+    x = dev_bf16(xb)
+    Ws, refs = [], []
+    for n in ns:
+        w = synth.gaussian(g, (n, k), 0.02)
+        W, _, _ = _int8_weight(qg, w)
+        Ws.append(W)
+        refs.append(oracle.quantize_absmax(w, per_row=True))
+    ys = qg.qgemv_grouped(Ws, x, act_int8=False, y_dtype=torch.float32)
+    for W, y, (q_ref, s_ref) in zip(Ws, ys, refs):
+        y1 = qg.qgemv(W, x, act_int8=False, y_dtype=torch.float32)
+        assert np.array_equal(host(y).view(np.uint32), host(y1).view(np.uint32))
+        assert oracle.normwise_error(host(y), oracle.y_w8a16(q_ref, s_ref, xb)) <= TOL_F32
