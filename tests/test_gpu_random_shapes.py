@@ -190,3 +190,43 @@ def test_random_grouped_w8a16(qg, ns, k):
         y1 = qg.qgemv(W, x, act_int8=False, y_dtype=torch.float32)
         assert np.array_equal(host(y).view(np.uint32), host(y1).view(np.uint32))
         assert oracle.normwise_error(host(y), oracle.y_w8a16(q_ref, s_ref, xb)) <= TOL_F32
+
+
+def _draw_gemm(count, quantum, kmax, nmax=1500, max_ops=3_000_000_000):
+    out = []
+    while len(out) < count:
+        m = int(np.exp(_RNG.uniform(0.0, np.log(nmax))))
+        n = int(np.exp(_RNG.uniform(0.0, np.log(nmax))))
+        k = quantum * max(1, int(np.exp(_RNG.uniform(0.0, np.log(kmax // quantum)))))
+        if m * n * k <= max_ops:
+            out.append((m, k, n))
+    return out
+
+
+QGEMM_SHAPES = [(m, k, n, int(_RNG.integers(0, 41)) if _RNG.uniform() < 0.7 else 0)
+                for m, k, n in _draw_gemm(10, 128, 8192)]
+MX_SHAPES = _draw_gemm(10, 256, 8192)
+
+
+@pytest.mark.parametrize("m,k,n,n_out", QGEMM_SHAPES)
+def test_random_qgemm_outlier(qg, m, k, n, n_out):
+    # the W8A8 prefill with outlier channels: split, int32 sums, rescale and
+    # the bf16 outlier product (the fixed-shape case function)
+    from test_gpu_parity import _qgemm_case
+    n_out = min(n_out, k - 1)
+    note("random qgemm m=%d k=%d n=%d n_out=%d" % (m, k, n, n_out))
+    _qgemm_case(qg, m, k, n, n_out, seed=m + k + n)
+
+
+@pytest.mark.parametrize("m,k,n", MX_SHAPES)
+def test_random_gemm_mxfp4(qg, m, k, n):
+    import oracle.mx as mx
+    from test_gpu_mx import _guarded2 as mx_guarded, _operands
+    note("random mxfp4 gemm %dx%dx%d" % (m, k, n))
+    ca, ea, cb, eb = _operands(m, k, n, m * 3 + k + n)
+    pa, sa = mx.pack_mxfp4(ca, ea)
+    pb, sb = mx.pack_mxfp4(cb, eb)
+    full, y = mx_guarded(m, n)
+    qg.gemm_mxfp4(dev(pa), dev(sa), dev(pb), dev(sb), y=y)
+    assert oracle.normwise_error(host(y), mx.gemm_mxfp4(ca, ea, cb, eb)) <= TOL_F32
+    assert canaries_intact(full, m * n)
