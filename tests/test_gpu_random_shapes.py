@@ -230,3 +230,100 @@ def test_random_gemm_mxfp4(qg, m, k, n):
     qg.gemm_mxfp4(dev(pa), dev(sa), dev(pb), dev(sb), y=y)
     assert oracle.normwise_error(host(y), mx.gemm_mxfp4(ca, ea, cb, eb)) <= TOL_F32
     assert canaries_intact(full, m * n)
+
+
+# ------------------------------------------------------------ quantizers and packing
+def _draw_rc(count, quantum=8, cmax=262144, rmax=5000, max_elems=8_000_000):
+    out = []
+    while len(out) < count:
+        r = int(np.exp(_RNG.uniform(0.0, np.log(rmax))))
+        c = quantum * max(1, int(np.exp(_RNG.uniform(0.0, np.log(cmax // quantum)))))
+        if r * c <= max_elems:
+            out.append((r, c))
+    return out
+
+
+ABSMAX_SHAPES = [(r, c, bool(_RNG.integers(0, 2))) for r, c in _draw_rc(12)]
+TENSOR_SIZES = [8 * int(np.exp(_RNG.uniform(0.0, np.log(1_000_000)))) for _ in range(8)]
+ASYM_SHAPES = [(r, c, bool(_RNG.integers(0, 2))) for r, c in _draw_rc(8)]
+TERNQ_SHAPES = _draw_rc(8, quantum=4, cmax=65536)
+PACK_SHAPES = [(int(_RNG.integers(1, 3)), r, c) for r, c in _draw_rc(8, cmax=65536)]
+MXQ_SHAPES = [(r, c, bool(_RNG.integers(0, 2))) for r, c in _draw_rc(8, quantum=256)]
+DETECT_SHAPES = [(r, c, int(_RNG.integers(0, min(c, 256) + 1))) for r, c in _draw_rc(8, rmax=3000, max_elems=4_000_000)]
+
+
+def _maybe_bf16(x, bf16):
+    if bf16:
+        bits = synth.to_bf16_bits(x)
+        return synth.bf16_bits_to_f32(bits), dev_bf16(bits)
+    return x, dev(x)
+
+
+@pytest.mark.parametrize("rows,cols,bf16", ABSMAX_SHAPES)
+def test_random_absmax_per_row(qg, rows, cols, bf16):
+    note("random absmax per row %dx%d bf16=%s" % (rows, cols, bf16))
+    x, xd = _maybe_bf16(synth.gaussian(synth.rng(rows + cols), (rows, cols), 0.02), bf16)
+    q, s = qg.quantize_absmax(xd, per_row=True)
+    q_ref, s_ref = oracle.quantize_absmax(x, per_row=True)
+    assert np.array_equal(host(s), s_ref) and np.array_equal(host(q), q_ref)
+
+
+@pytest.mark.parametrize("n", TENSOR_SIZES)
+def test_random_absmax_per_tensor(qg, n):
+    note("random absmax per tensor n=%d" % n)
+    x = synth.gaussian(synth.rng(n), (n,), 1.0)
+    q, s = qg.quantize_absmax(dev(x), per_row=False)
+    q_ref, s_ref = oracle.quantize_absmax(x, per_row=False)
+    assert host(s)[0] == s_ref[0] and np.array_equal(host(q), q_ref)
+
+
+@pytest.mark.parametrize("rows,cols,bf16", ASYM_SHAPES)
+def test_random_asym(qg, rows, cols, bf16):
+    note("random asym %dx%d bf16=%s" % (rows, cols, bf16))
+    x0 = (synth.gaussian(synth.rng(rows * 3 + cols), (rows, cols), 1.0) + np.float32(0.4)).astype(np.float32)
+    x, xd = _maybe_bf16(x0, bf16)
+    q, s, z = qg.quantize_asym(xd)
+    q_ref, s_ref, z_ref = oracle.quantize_asym(x)
+    assert np.array_equal(host(s), s_ref)
+    assert np.array_equal(host(z).astype(np.int32), z_ref)
+    assert np.array_equal(host(q), q_ref)
+
+
+@pytest.mark.parametrize("n,k", TERNQ_SHAPES)
+def test_random_ternary_quantize(qg, n, k):
+    note("random ternary quantize %dx%d" % (n, k))
+    w = synth.laplace(synth.rng(n + k), (n, k), 0.02)
+    q, gamma = qg.quantize_ternary(dev(w))
+    q_ref, g_ref = oracle.ternary_absmean(w)
+    assert host(gamma)[0] == g_ref and np.array_equal(host(q), q_ref)
+
+
+@pytest.mark.parametrize("bits,n,k", PACK_SHAPES)
+def test_random_pack(qg, bits, n, k):
+    note("random pack bits=%d %dx%d" % (bits, n, k))
+    g = synth.rng(bits + n + k)
+    if bits == 2:
+        c = (g.integers(0, 3, size=(n, k)) - 1).astype(np.int8)
+    else:
+        c = np.where(g.random((n, k)) < 0.5, -1, 1).astype(np.int8)
+    p = qg.pack(dev(c), bits)
+    assert np.array_equal(host(p), oracle.pack(c, bits))
+    assert np.array_equal(host(qg.unpack(p, bits, k)), c)
+
+
+@pytest.mark.parametrize("rows,cols,bf16", MXQ_SHAPES)
+def test_random_mxfp4_quantize(qg, rows, cols, bf16):
+    import oracle.mx as mx
+    note("random mxfp4 quantize %dx%d bf16=%s" % (rows, cols, bf16))
+    x, xd = _maybe_bf16(synth.gaussian(synth.rng(rows + 5 * cols), (rows, cols), 1.0), bf16)
+    codes, scales = qg.quantize_mxfp4(xd)
+    p_ref, s_ref = mx.pack_mxfp4(*mx.quantize_mxfp4(x))
+    assert np.array_equal(host(scales), s_ref) and np.array_equal(host(codes), p_ref)
+
+
+@pytest.mark.parametrize("m,k,n_out", DETECT_SHAPES)
+def test_random_detect_outliers(qg, m, k, n_out):
+    note("random detect outliers m=%d k=%d n_out=%d" % (m, k, n_out))
+    xb = synth.to_bf16_bits(synth.gaussian(synth.rng(m + k + n_out), (m, k), 1.0))
+    idx = qg.detect_outliers(dev_bf16(xb), n_out)
+    assert np.array_equal(host(idx), oracle.detect_outlier_channels(xb, n_out))
