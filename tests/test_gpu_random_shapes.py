@@ -327,3 +327,39 @@ def test_random_detect_outliers(qg, m, k, n_out):
     xb = synth.to_bf16_bits(synth.gaussian(synth.rng(m + k + n_out), (m, k), 1.0))
     idx = qg.detect_outliers(dev_bf16(xb), n_out)
     assert np.array_equal(host(idx), oracle.detect_outlier_channels(xb, n_out))
+
+
+# ------------------------------------------------ K split with a workspace; thresholded split
+SPLITK_SHAPES = [(int(np.exp(_RNG.uniform(0.0, np.log(4096)))), 128 * int(_RNG.integers(64, 129)),
+                  int(_RNG.integers(2, 17))) for _ in range(8)]
+SEP_SPLIT_SHAPES = [(n, k, int(_RNG.integers(50, 101))) for n, k in _draw(6, kmax=65536, max_elems=4_000_000)]
+
+
+@pytest.mark.parametrize("n,k,m", SPLITK_SHAPES)
+def test_random_batch_splitk(qg, n, k, m):
+    # qg_qgemv_batch_ws (K split over workgroups through the caller's
+    # workspace) on random row counts and 8192 <= K <= 16384; twice, since
+    # the row-block counters must come back to zero
+    note("random batch split-K %dx%d m=%d" % (n, k, m))
+    g = synth.rng(n + 23 * k + m)
+    w = synth.gaussian(g, (n, k), 0.02)
+    xb = synth.to_bf16_bits(synth.gaussian(g, (m, k), 1.0))
+    W, _, _ = _int8_weight(qg, w)
+    q_ref, s_ref = oracle.quantize_absmax(w, per_row=True)
+    y_ref = oracle.y_w8a16_batch(q_ref, s_ref, xb)
+    need = qg.batch_workspace_bytes(n, k, m)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
+    xd = dev_bf16(xb)
+    y1 = host(qg.qgemv_batch(W, xd, y_dtype=torch.float32, ws=ws))
+    y2 = host(qg.qgemv_batch(W, xd, y_dtype=torch.float32, ws=ws))
+    assert oracle.normwise_error(y1, y_ref) <= TOL_F32
+    assert np.array_equal(y1, y2)
+
+
+@pytest.mark.parametrize("n,k,pb", SEP_SPLIT_SHAPES)
+def test_random_sep_split(qg, n, k, pb):
+    # the thresholded split on the GPU: classes, residual stream (with its
+    # zero tail), alpha and s_r against the oracle on every row
+    from test_gpu_sep_threshold import _check_split, _weights
+    note("random thresholded split %dx%d pb=%d" % (n, k, pb))
+    _check_split(qg, _weights(n, k, n + 29 * k), pb, pb // 2)
