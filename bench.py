@@ -448,6 +448,17 @@ def summarize_counters(order_json, dirs):
         for name, r in ks.items():
             md.append("| %s | `%s` | %d | " % (cfg, name[:80], r["dispatches"]) +
                       " | ".join(str(r.get(c, "")) for c in cols) + " |")
+    # the memory pipeline (address unit TA, data unit TD, vector L1 TCP, L2
+    # TCC), where those passes were taken: cycles and requests summed over
+    # the block instances, per dispatch
+    mem = sorted({c for ks in out["configs"].values() for r in ks.values() for c in r
+                  if c.split("_")[0] in ("TA", "TD", "TCP", "TCC") and c not in cols})
+    if mem:
+        md += ["", "Memory pipeline counters (summed over block instances, mean per dispatch):", "",
+               "| config | kernel | " + " | ".join(mem) + " |", "|---|---|" + "---|" * len(mem)]
+        for cfg, ks in out["configs"].items():
+            for name, r in ks.items():
+                md.append("| %s | `%s` | " % (cfg, name[:80]) + " | ".join(str(r.get(c, "")) for c in mem) + " |")
     with open(COUNTERS_FILE[:-5] + ".md", "w") as f:
         f.write("\n".join(md) + "\n")
     print("\n".join(md[:6]))
