@@ -256,8 +256,11 @@ def profile_workload(args):
     the separator launch (see mark()): two 256 MiB device copies (the
     calibration of FETCH_SIZE / WRITE_SIZE), then two runs of each kernel
     the bench reports: the W8A16 decode step, the prefill call, the MXFP4
-    GEMM, the thresholded, sign + residual, ternary and 4-bit products, the
-    small-batch step, and the ternary and sign + residual decode steps.
+    GEMM, the three W8A16 projection shapes alone, the thresholded (with and
+    without the residual), sign + residual (with and without zero-points),
+    ternary (2-bit and base 3) and 4-bit products, the small-batch steps at
+    16 and 4 tokens, and the ternary, sign + residual and thresholded decode
+    steps.
     Launches are eager (no graphs)."""
     import torch
     import quantized_gemv_amd as qg
@@ -287,8 +290,15 @@ def profile_workload(args):
     del src, dst
     h = build_headline(torch, qg, synth, dev, args.layers)
     twice("decode_step_w8a16", h["launches"])
+    # the three projection shapes alone (the first layer's copies)
+    for name, idx in (("decode_w8a16_attn_4096x4096", 0), ("decode_w8a16_ffn_up_11008x4096", 4),
+                      ("decode_w8a16_ffn_down_4096x11008", 6)):
+        W1 = h["weights"][idx][1]
+        y1 = torch.empty(W1.n, dtype=torch.bfloat16, device=dev)
+        twice(name, [lambda W1=W1, y1=y1: qg.qgemv(W1, h["xs"][W1.k], act_int8=False, y=y1)])
     tiled = tiled_weights(qg, h["weights"])
-    twice("small_batch_decode_step_m16", small_batch_launches(torch, qg, dev, tiled, 16))
+    for m in (16, 4):
+        twice("small_batch_decode_step_m%d" % m, small_batch_launches(torch, qg, dev, tiled, m))
     del h, tiled
     torch.cuda.empty_cache()
     full, _, _, _ = build_prefill(torch, qg, synth, dev, cur_stream)
@@ -307,7 +317,14 @@ def profile_workload(args):
     xs = torch.from_numpy(wl.tensors["x_bf16"]).to(dev).view(torch.bfloat16)
     sw = qg.split_sep_threshold(wdev, 80, 50)
     twice("sep_threshold_28672x8192", [lambda: qg.qgemv_sep(sw, xs)])
+    twice("sep_threshold_skip_residual_28672x8192", [lambda: qg.qgemv_sep(sw, xs, skip_residual=True)])
     del sw
+    sign, alpha, rq, s_r, z_r = qg.split_sign_residual_zp(wdev)
+    Wz = qg.QWeight(qg.QG_WFMT_SIGN1_RES8Z, 28672, 8192, qg.pack(sign, 1), alpha, resid=rq, scale2=s_r, zero=z_r)
+    del sign
+    twice("sign1_res8z_28672x8192", [lambda: qg.qgemv(Wz, xs, act_int8=False, y_dtype=torch.bfloat16)])
+    del Wz, rq
+    torch.cuda.empty_cache()
     sign, alpha, rq, s_r = qg.split_sign_residual(wdev)
     Wsr = qg.QWeight(qg.QG_WFMT_SIGN1_RES8, 28672, 8192, qg.pack(sign, 1), alpha, resid=rq, scale2=s_r)
     del sign, wdev
@@ -319,7 +336,9 @@ def profile_workload(args):
     Wt = qg.QWeight(qg.QG_WFMT_TERNARY2, 11008, 4096, qg.pack(q, 2), gamma)
     xt = torch.from_numpy(wl.tensors["x"]).to(dev)
     twice("ternary_11008x4096", [lambda: qg.qgemv(Wt, xt, act_int8=True)])
-    del q, Wt
+    W3 = qg.QWeight(qg.QG_WFMT_TERNARY3, 11008, 4096, qg.pack_base3(q), gamma)
+    twice("ternary_base3_11008x4096", [lambda: qg.qgemv(W3, xt, act_int8=True)])
+    del q, Wt, W3
     wl = synth.q4_decode()
     codes, meta = qg.quantize_q4k(torch.from_numpy(wl.tensors["w"]).to(dev))
     Wq4 = qg.QWeight(qg.QG_WFMT_Q4K, 11008, 4096, codes, None, resid=meta)
@@ -327,7 +346,7 @@ def profile_workload(args):
     twice("q4k_w4a16_11008x4096", [lambda: qg.qgemv(Wq4, xq4, act_int8=False, y_dtype=torch.bfloat16)])
     del codes, meta, Wq4
     torch.cuda.empty_cache()
-    for fmt in ("ternary2", "sign1_res8"):
+    for fmt in ("ternary2", "sign1_res8", "sep_threshold"):
         launches, _, keep, _ = build_format_step(torch, qg, synth, dev, args.layers, fmt)
         twice("decode_step_" + fmt, launches)
         del launches, keep
@@ -699,9 +718,10 @@ def main():
             if isinstance(rec, dict):
                 rec["rocprof"] = recorded_durations(name)
                 if "traffic" not in rec:
-                    key = {"prefill_mxfp4": "gemm_mxfp4", "small_batch_decode_step_m16": "qgemv_batch",
-                           "decode_step_sep_threshold": "sep_qgemv",
+                    key = {"prefill_mxfp4": "gemm_mxfp4", "decode_step_sep_threshold": "sep_qgemv",
                            "prefill_w8a8_outlier": "qgemm_w8a8"}.get(name, "qgemv_kernel")
+                    if name.startswith("small_batch"):
+                        key = "qgemv_batch"
                     rec["traffic"] = recorded_traffic(name, key)
     result["context"] = {
         "note": "figures quoted from the pages for context; not targets",
@@ -753,8 +773,7 @@ def bench_sep_threshold(torch, qg, synth, dev, rotate_count):
                      "bytes_per_weight": round(per / (n * k), 4), "residual_share": round(nres / (n * k), 4),
                      "weights_per_ns": round(n * k / sec / 1e9, 1), "rotating_copies": len(copies),
                      "algorithmic_bytes": per}
-        if not skip:
-            out[name]["traffic"] = recorded_traffic(name, "sep_qgemv")
+        out[name]["traffic"] = recorded_traffic(name, "sep_qgemv")
         log("%s: %.2f us, %.0f GB/s" % (name, sec * 1e6, per / sec / 1e9))
         del copies, t
         torch.cuda.empty_cache()
